@@ -1,0 +1,73 @@
+"""Pins for the seeded input generators (published SplitMix64 outputs, bf16 rounding)."""
+
+import json
+import math
+import os
+
+import numpy as np
+
+from workloads import (bf16_bits, bf16_from_bits, hash_u64, hash_uniform_f32, inject_draw,
+                       inject_threshold, mix64, preset, stream_key)
+from workloads.synth import GOLDEN, MASK64
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_splitmix64_published_outputs():
+    g = json.load(open(os.path.join(GOLD, "splitmix64_seed0.json")))
+    # The stream with key = initial state 0 yields mix64(0 + (i+1)*gamma) for i = 0, 1, 2.
+    z = hash_u64(g["state0"], 0, 3)
+    assert [f"{int(v):016x}" for v in z] == g["outputs_hex"]
+
+
+def test_stream_key_is_first_output_of_state():
+    s = (7 << 32) + 12345
+    assert stream_key(7, 12345) == int(mix64(np.array([(s + GOLDEN) & MASK64], np.uint64))[0])
+
+
+def test_bf16_rounding_cases():
+    g = json.load(open(os.path.join(GOLD, "bf16_rounding.json")))
+    for c in g["cases"]:
+        x = np.array([int(c["f32_bits"], 16)], dtype=np.uint32).view(np.float32)
+        assert f"{int(bf16_bits(x)[0]):04x}" == c["bf16_bits"]
+    # round trip of representable values is exact
+    v = bf16_from_bits(np.arange(0, 0x7f80, 97, dtype=np.uint16))
+    assert np.array_equal(bf16_from_bits(bf16_bits(v)), v)
+
+
+def test_hash_uniform_moments_and_range():
+    std = 0.02
+    v = hash_uniform_f32(stream_key(1, 2), 0, 200_000, std).astype(np.float64)
+    a = std * math.sqrt(3.0)
+    assert v.min() >= -a and v.max() <= a
+    assert abs(v.mean()) < 4 * std / math.sqrt(v.size)
+    assert abs(v.std() - std) < 0.01 * std
+    # the extremes of the 24-bit grid reach the ends of the interval
+    assert v.max() > 0.999 * a and v.min() < -0.999 * a
+
+
+def test_hash_slices_are_consistent():
+    key = stream_key(3, 99)
+    full = hash_u64(key, 0, 1000)
+    assert np.array_equal(full[300:700], hash_u64(key, 300, 400))
+
+
+def test_injection_frequency_matches_p():
+    n = 20000
+    for p in (0.0, 0.3, 0.7, 1.0):
+        thr = inject_threshold(p)
+        hits = sum(inject_draw(11, 0, pos, 1 + pos % 3) < thr for pos in range(n))
+        if p in (0.0, 1.0):
+            assert hits == int(p * n)
+        else:
+            sd = math.sqrt(n * p * (1 - p))
+            assert abs(hits - p * n) < 5 * sd
+
+
+def test_presets_parameter_counts():
+    # The 31B-class workload is "~30.5B params"; a tied LM head gives 30.535B.
+    assert abs(preset("31b").target_params() / 1e9 - 30.535) < 0.01
+    # E2B-shaped target: 1.252B with a tied head.
+    assert abs(preset("e2b").target_params() / 1e9 - 1.252) < 0.005
+    t = preset("tiny")
+    assert t.vocab == t.n_centroids * t.cluster_size

@@ -1,0 +1,222 @@
+/*
+ * libspecdec -- greedy speculative decoding with a multi-token-prediction (MTP) drafter on one
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * The step (sources are five web pages on Gemma 4's MTP drafters):
+ *   1. specdec_draft     -- a light drafter head reads the target's last hidden state and
+ *                           cross-attends to the target's own KV cache (it keeps no cache), then
+ *                           proposes K tokens autoregressively through a clustered output layer
+ *                           ("Accelerating Gemini Nano on Pixel with frozen multi-token
+ *                           prediction", sections "The 'late exit' strategy" and "Zero-copy
+ *                           architecture"; "Gemma 4's MTP drafter explained", section "What is
+ *                           different about Gemma 4's drafter?").
+ *   2. specdec_verify    -- the target runs one forward pass over the current token and the K
+ *                           drafts ("Gemma 4's MTP drafter explained", section "How does
+ *                           speculative decoding work?").
+ *   3. specdec_accept    -- drafts are accepted up to the first disagreement, the rest dropped,
+ *                           and the target's own token appended: 1..K+1 tokens per step (same
+ *                           section; "Accelerating Gemma 4 ...", section "How MTP works").
+ *   4. specdec_kv_commit -- the cache rolls back to the first mismatch: only the committed
+ *                           length moves; dead entries are overwritten by the next verify
+ *                           ("Accelerating Gemini Nano on Pixel ...", "The 'late exit' strategy").
+ *
+ * Conventions for every call:
+ *   - All device buffers are allocated and owned by the caller.  The library never allocates
+ *     or frees device memory and never synchronises the stream in the step calls; every step
+ *     call only enqueues kernels on `stream` (a hipStream_t passed as void*; NULL = default).
+ *   - Return value: SPECDEC_OK (0) or a negative SPECDEC_E_* code; on error nothing has been
+ *     enqueued unless the code is SPECDEC_E_HIP (a launch failed part-way).
+ *   - Kernels never write out of bounds.  Conditions only visible on the device (a cache slot
+ *     beyond max_ctx, an out-of-range token id, a NaN logit) set bits in a sticky device error
+ *     word read with specdec_read_device_error.
+ *   - One context serves one stream / host thread at a time.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SPECDEC_OK = 0,
+  SPECDEC_E_INVAL = -1,       /* null pointer, bad shape, B/K/rows beyond the configured maxima */
+  SPECDEC_E_CAPACITY = -2,    /* host-side bound on len + rows exceeds max_ctx */
+  SPECDEC_E_HIP = -3,         /* a HIP launch / runtime call failed */
+  SPECDEC_E_UNSUPPORTED = -4  /* configuration the kernels are not built for */
+};
+
+enum { SPECDEC_F32 = 0, SPECDEC_BF16 = 1 };
+enum { SPECDEC_HEAD_CLUSTERED = 0, SPECDEC_HEAD_FULL = 1 };
+#define SPECDEC_ACCEPT_COMMIT 1u
+
+/* Device error word bits. */
+enum { SPECDEC_DEVERR_CAPACITY = 1, SPECDEC_DEVERR_NAN = 2, SPECDEC_DEVERR_TOKEN = 4 };
+
+/* Packing kinds for specdec_pack_matrix. */
+enum {
+  SPECDEC_PACK_PLAIN = 0,   /* any projection */
+  SPECDEC_PACK_ROPE = 1,    /* rows are heads of head_dim whose rotary pairs (i, i+hd/2) are
+                               made adjacent: the fused q/k/v projection and the drafter's q */
+  SPECDEC_PACK_GATE_UP = 2  /* rows [0,F) gate and [F,2F) up, interleaved per 16-row tile */
+};
+
+typedef struct {
+  /* target decoder (pre-norm RMSNorm, RoPE, gated SiLU FFN, tied LM head) */
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  /* mixture of experts: n_experts == 0 means dense (MoE is reported as unsupported for now) */
+  int32_t n_experts, top_k, expert_ffn, shared_ffn;
+  /* drafter: d_layers layers of width d_dim, FFN d_ffn, n_centroids equal clusters of the
+     vocabulary, cross-attending to target layer kv_src_layer (-1 = last) */
+  int32_t d_layers, d_dim, d_ffn, n_centroids, kv_src_layer;
+  int32_t dtype;            /* SPECDEC_F32 | SPECDEC_BF16: weights, KV and GEMM inputs */
+  float rms_eps, rope_theta;
+  int32_t max_batch;        /* sequences per call */
+  int32_t max_draft;        /* largest K */
+  int32_t max_rows;         /* largest rows per sequence in one verify (>= max_draft + 1) */
+  int32_t max_ctx;          /* KV-cache positions per sequence */
+} specdec_config;
+
+/* Per-layer tensor slots of specdec_weights.layers (n_layers * SPECDEC_N_LAYER_TENSORS). */
+enum {
+  SPECDEC_LW_ATTN_NORM = 0, /* float [d_model] */
+  SPECDEC_LW_QKV = 1,       /* packed (ROPE) [Hq*hd + 2*Hkv*hd][d_model]: Wq rows, Wk rows, Wv rows */
+  SPECDEC_LW_O = 2,         /* packed [d_model][Hq*hd] */
+  SPECDEC_LW_FFN_NORM = 3,  /* float [d_model] */
+  SPECDEC_LW_GATE_UP = 4,   /* packed (GATE_UP) [2*ffn_dim][d_model] */
+  SPECDEC_LW_DOWN = 5,      /* packed [d_model][ffn_dim] */
+  SPECDEC_N_LAYER_TENSORS = 6
+};
+
+/* Per-layer tensor slots of specdec_weights.d_layers (d_layers * SPECDEC_N_DRAFT_TENSORS). */
+enum {
+  SPECDEC_DW_N1 = 0,        /* float [d_dim] */
+  SPECDEC_DW_Q = 1,         /* packed (ROPE) [Hq*hd][d_dim] */
+  SPECDEC_DW_O = 2,         /* packed [d_dim][Hq*hd] */
+  SPECDEC_DW_N2 = 3,        /* float [d_dim] */
+  SPECDEC_DW_GATE_UP = 4,   /* packed (GATE_UP) [2*d_ffn][d_dim] */
+  SPECDEC_DW_DOWN = 5,      /* packed [d_dim][d_ffn] */
+  SPECDEC_N_DRAFT_TENSORS = 6
+};
+
+/* Device pointers to the weights (dtype elements unless noted).  "packed" tensors are in the
+   streaming tile layout written by specdec_pack_matrix.  The pointer tables are copied at
+   create; the tensors themselves must outlive the context. */
+typedef struct {
+  const void* embed;             /* packed [vocab][d_model]; also the tied LM head */
+  const float* final_norm;       /* [d_model] */
+  const void* const* layers;     /* n_layers * SPECDEC_N_LAYER_TENSORS pointers */
+  const void* table;             /* packed [vocab][d_dim], cluster-major rows (tied drafter
+                                    input embedding and output table) */
+  const void* centroids;         /* packed [n_centroids][d_dim] */
+  const int32_t* row_vocab;      /* [vocab]: vocabulary id of table row r */
+  const int32_t* vocab_row;      /* [vocab]: table row of vocabulary id v */
+  const float* norm_h;           /* [d_model] drafter norm of the target hidden input */
+  const float* norm_e;           /* [d_dim]   drafter norm of the token embedding input */
+  const void* w_in;              /* packed [d_dim][d_model + d_dim] */
+  const void* const* d_layers;   /* d_layers * SPECDEC_N_DRAFT_TENSORS pointers */
+  const float* norm_f;           /* [d_dim] drafter final norm */
+  const void* w_back;            /* packed [d_model][d_dim]: drafter state -> next hidden input */
+} specdec_weights;
+
+typedef struct specdec_ctx specdec_ctx; /* host memory; owns no device memory */
+
+/* Bytes of device workspace a context with this configuration needs (0 if the config is
+   invalid).  Size = f(config) only. */
+size_t specdec_workspace_bytes(const specdec_config* cfg);
+
+/* Elements of the KV cache per tensor (K or V): n_layers*max_batch*n_kv_heads*max_ctx*head_dim.
+   Element (l, b, g, pos, c) sits at (((l*max_batch + b)*n_kv_heads + g)*max_ctx + pos)*head_dim + c. */
+size_t specdec_kv_elems(const specdec_config* cfg);
+
+/* Creates a context over caller-owned device memory:
+     kv_k, kv_v  [n_layers][max_batch][n_kv_heads][max_ctx][head_dim] dtype
+     len         int32 [max_batch]: committed KV length per sequence (device-resident state)
+     hid         float [max_batch][d_model]: the drafter's hidden input (the target's
+                 pre-final-norm residual of the last committed position)
+     workspace   specdec_workspace_bytes(cfg) bytes, 256-byte aligned
+   Enqueues one small kernel on `stream` that zeroes the workspace's arrival counters and the
+   device error word.  Errors: SPECDEC_E_INVAL (null pointers, shapes not multiples of the
+   tile: d_model, Hq*hd, ffn_dim, d_dim, d_ffn % 32; head_dim % 16, head_dim <= 256;
+   vocab % 64; vocab / n_centroids % 64; max_batch*max_rows <= 64; max_rows <= 64),
+   SPECDEC_E_UNSUPPORTED (n_experts > 0). */
+int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv_k, void* kv_v,
+                   int32_t* len, float* hid, void* workspace, size_t workspace_bytes,
+                   void* stream, specdec_ctx** out);
+int specdec_destroy(specdec_ctx* ctx);
+
+/* Draft K tokens per sequence.
+   Inputs: cur_tok int32 [B] (device): the current token c0 at position len[b], not yet in the
+   cache; hid (context state) and the target's layer-kv_src_layer cache, keys [0, len[b]).
+   Sub-step j = 1..K embeds c_{j-1}, runs the drafter at query position len[b]+j-1 and scores
+   the head: SPECDEC_HEAD_CLUSTERED scores the n_centroids centroids, keeps the k_c best
+   clusters (ties -> lower cluster id) and takes the argmax over their member tokens;
+   SPECDEC_HEAD_FULL scores the whole vocabulary (the fallback that drops the clusters).
+   Ties -> lower vocabulary id.  Output drafts int32 [B][K] (device).
+   Optional workload injection (tests and benchmarks; NULL = off): inject int32 [B][inj_stride]
+   (device); entry (len[b]+j)*K + (j-1) >= 0 replaces draft j after it was drafted (the drafter's
+   own token still feeds sub-step j+1).  Errors: SPECDEC_E_INVAL (B > max_batch, K < 1,
+   K > max_draft, k_c outside [1, n_centroids], null pointers). */
+int specdec_draft(specdec_ctx* ctx, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
+                  const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
+                  int64_t inj_stride, void* stream);
+
+/* Target forward over n_rows rows per sequence: tokens int32 [B][n_rows] (device) at positions
+   len[b] .. len[b]+n_rows-1.  Row i attends keys [0, len[b]+i].  Appends the rows' keys and
+   values to the cache tentatively (len is not changed).  Keeps per-row hidden states and LM-head
+   argmax partials in the workspace for specdec_accept / specdec_kv_commit.
+   Optional outputs (NULL = skip): logits float [B][n_rows][vocab], argmax int32 [B][n_rows].
+   Prefill is verify(n_rows = chunk) + kv_commit(chunk) per chunk.
+   Errors: SPECDEC_E_INVAL (B, n_rows out of range), SPECDEC_E_CAPACITY (the host-side upper
+   bound of len + n_rows exceeds max_ctx). */
+int specdec_verify(specdec_ctx* ctx, int32_t B, int32_t n_rows, const int32_t* tokens,
+                   float* logits, int32_t* argmax, void* stream);
+
+/* Acceptance after a verify of K+1 rows per sequence (tokens = [c0, d1..dK], the verify input).
+   One fused kernel per call: G[i] = argmax of row i (lowest id on ties); m = largest j <= K with
+   tokens[1..j] == G[0..j-1]; out_tokens[b] = tokens[1..m], G[m], then -1 padding (int32
+   [B][K+1]); n_emit[b] = m+1; next_tok[b] = G[m].  With SPECDEC_ACCEPT_COMMIT the same kernel
+   also commits: len[b] += m+1 and hid[b] = hidden of row m.  Any output pointer may be NULL.
+   Errors: SPECDEC_E_INVAL (K+1 != rows of the last verify, B != its batch). */
+int specdec_accept(specdec_ctx* ctx, int32_t B, int32_t K, const int32_t* tokens,
+                   int32_t* out_tokens, int32_t* n_emit, int32_t* next_tok, uint32_t flags,
+                   void* stream);
+
+/* Commit n_commit[b] (int32 [B], device, 1..rows of the last verify) rows: len[b] += n and
+   hid[b] = hidden of row n-1.  For prefill chunks and callers that decide acceptance
+   themselves.  Errors: SPECDEC_E_INVAL. */
+int specdec_kv_commit(specdec_ctx* ctx, int32_t B, const int32_t* n_commit, void* stream);
+
+/* Packs a logical row-major matrix src [n][kd] (device, dtype) into the streaming tile layout
+   dst (device, n*kd elements).  kind: SPECDEC_PACK_*; head_dim for ROPE; split_rows = F for
+   GATE_UP (n = 2F).  Requires n % 16 == 0, kd % 32 == 0.  Setup-time helper. */
+int specdec_pack_matrix(const void* src, void* dst, int32_t n, int32_t kd, int32_t dtype,
+                        int32_t kind, int32_t head_dim, int32_t split_rows, void* stream);
+
+/* Tightens the host-side bound on len after the caller has read len back (host values). */
+int specdec_set_len_bound(specdec_ctx* ctx, const int32_t* host_len, int32_t B);
+
+/* Reads (synchronously) and optionally clears the sticky device error word. */
+int specdec_read_device_error(specdec_ctx* ctx, int32_t* host_word, int32_t clear, void* stream);
+
+/* Per-launch timing of one kernel class, for roofline reporting: after specdec_profile_start,
+   every launch of that class is bracketed by HIP events on the launch stream (up to `capacity`
+   launches).  specdec_profile_read synchronises and returns the durations in ms.
+   Classes: 0 gate/up GEMM, 1 down GEMM, 2 qkv GEMM, 3 o GEMM, 4 attention, 5 LM head,
+   6 drafter head.  Not for use under graph capture. */
+int specdec_profile_start(specdec_ctx* ctx, int32_t kernel_class, int32_t capacity);
+int specdec_profile_read(specdec_ctx* ctx, float* ms_out, int32_t max, int32_t* n_out);
+
+/* Split-K factor the context uses for a class (tests / reports). */
+int specdec_query_split(specdec_ctx* ctx, int32_t kernel_class, int32_t* splits, int32_t* units);
+
+const char* specdec_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H */

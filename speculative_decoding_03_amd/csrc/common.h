@@ -1,0 +1,89 @@
+// Shared device helpers for the CDNA4 (gfx950) kernels of libspecdec.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specdec {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr int TILE_N = 16;       // rows of W (output features) per packed tile
+constexpr int TILE_K = 32;       // reduction elements per packed tile
+constexpr int TILE_ELEMS = 512;  // 16 x 32
+constexpr int LANE_ELEMS = 8;    // elements each lane holds of a tile
+
+// Storage element type tags.
+struct bf16_t { uint16_t v; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(p->v); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { p->v = f32_to_bf16(v); }
+};
+
+// Offset (in elements) of logical element (n, k) of a packed [N][Kd] matrix.
+// Tile (n/16, k/32) is 512 contiguous elements; inside it lane = ((k%32)/8)*16 + n%16 holds
+// elements k%8 = 0..7, which is the operand layout of the 16x16x32 bf16 MFMA.
+__host__ __device__ __forceinline__ size_t packed_offset(int n, int k, int nkb) {
+  const size_t tile = (size_t)(n >> 4) * (size_t)nkb + (size_t)(k >> 5);
+  const int lane = (((k & 31) >> 3) << 4) | (n & 15);
+  return tile * TILE_ELEMS + (size_t)lane * LANE_ELEMS + (k & 7);
+}
+
+// Device-scope fences / atomics for the split-K "last arriver" reduction.
+__device__ __forceinline__ void fence_device() { __threadfence(); }
+
+__device__ __forceinline__ int atomic_inc_device(int* p) {
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_store_zero(int* p) {
+  __hip_atomic_store(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lowest-index-wins argmax combine on (value, index) pairs.
+__device__ __forceinline__ void argmax_combine(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Error word bits raised by kernels (sticky until cleared by the host).
+enum : int { ERRBIT_CAPACITY = 1, ERRBIT_NAN = 2, ERRBIT_TOKEN = 4 };
+
+__device__ __forceinline__ void raise_error(int* err, int bit) {
+  if (err) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace specdec

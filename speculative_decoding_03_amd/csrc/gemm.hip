@@ -1,0 +1,426 @@
+// Weight-streaming skinny GEMM for the verify / decode / drafter rows (M <= 64).
+//
+// Y[M][N] = X[M][Kd] . W[N][Kd]^T with W in the packed tile layout: each wave streams whole
+// 1 KB tiles (bf16) with one 16-byte load per lane, so every weight byte is read from HBM
+// exactly once per call and every wave load is fully contiguous.  The rows of X are padded to
+// the 16-row MFMA tile; v_mfma_f32_16x16x32_bf16 (fp32: eight v_mfma_f32_16x16x4f32) does the
+// contraction.  The reduction axis is split S ways where S depends only on (N, Kd), and the
+// last split to arrive at a unit sums all partials in split order, so every output element is
+// produced by the same instruction sequence whatever M is: a verify row is bit-identical to the
+// same row computed alone in a decode step.
+//
+// Prologue: X is either a storage-typed activation or the fp32 residual stream normalised on
+// load (x * rowscale * normweight, the RMSNorm of the layer).  Epilogues: store / residual add
+// with the next RMSNorm's row scale, rotary embedding + KV-cache append, SiLU-gated product,
+// and per-unit argmax partials for the LM head.
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace specdec {
+
+namespace {
+
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16_t> {
+  u32x4 v;
+};
+template <> struct Frag<float> {
+  u32x4 v[2];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_w(Frag<T>& f, const T* W, size_t tile, int nkb, int kb,
+                                       int lane) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(
+      W + (tile * (size_t)nkb + (size_t)kb) * TILE_ELEMS + (size_t)lane * LANE_ELEMS);
+  if constexpr (sizeof(T) == 2) {
+    f.v = __builtin_nontemporal_load(p);
+  } else {
+    f.v[0] = __builtin_nontemporal_load(p);
+    f.v[1] = __builtin_nontemporal_load(p + 1);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void zero_frag(Frag<T>& f) {
+  if constexpr (sizeof(T) == 2) {
+    f.v = u32x4{0, 0, 0, 0};
+  } else {
+    f.v[0] = u32x4{0, 0, 0, 0};
+    f.v[1] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// X fragment of lane `lane` for k-block kb: row m = mt*16 + lane%16, k = kb*32 + (lane/16)*8.
+template <typename T, int XM>
+__device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int m, float rs, int kb,
+                                       int lane) {
+  if (m >= a.M) {
+    zero_frag(f);
+    return;
+  }
+  const int k = kb * TILE_K + ((lane >> 4) << 3);
+  if constexpr (XM == XM_ELEM) {
+    const u32x4* p =
+        reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.X) + (size_t)m * a.ldx + k);
+    if constexpr (sizeof(T) == 2) {
+      f.v = *p;
+    } else {
+      f.v[0] = p[0];
+      f.v[1] = p[1];
+    }
+  } else {
+    const float4* px = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.X) +
+                                                       (size_t)m * a.ldx + k);
+    const float4* pw = reinterpret_cast<const float4*>(a.xnorm + k);
+    float4 x0 = px[0], x1 = px[1], w0 = pw[0], w1 = pw[1];
+    float y[8] = {x0.x * rs * w0.x, x0.y * rs * w0.y, x0.z * rs * w0.z, x0.w * rs * w0.w,
+                  x1.x * rs * w1.x, x1.y * rs * w1.y, x1.z * rs * w1.z, x1.w * rs * w1.w};
+    if constexpr (sizeof(T) == 2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_bf16(y[2 * i]) | ((uint32_t)f32_to_bf16(y[2 * i + 1]) << 16);
+      f.v = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+      f.v[0] = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                     __float_as_uint(y[3])};
+      f.v[1] = u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
+                     __float_as_uint(y[7])};
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 mma(const Frag<T>& x, const Frag<T>& w, f32x4 acc) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.v),
+                                                   __builtin_bit_cast(bf16x8, w.v), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.v[h][e]),
+                                                   __uint_as_float(w.v[h][e]), acc, 0, 0, 0);
+    return acc;
+  }
+}
+
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 8, WAVE);
+  v += __shfl_xor(v, 4, WAVE);
+  v += __shfl_xor(v, 2, WAVE);
+  v += __shfl_xor(v, 1, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ void argmax16(float& v, int& i) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    float v2 = __shfl_xor(v, o, WAVE);
+    int i2 = __shfl_xor(i, o, WAVE);
+    argmax_combine(v, i, v2, i2);
+  }
+}
+
+// Row-scale of the next RMSNorm, computed by the last unit to finish (one wave).
+__device__ void finish_row_scale(const GemmArgs& a, int lane) {
+  for (int m = 0; m < a.M; ++m) {
+    float s = 0.f;
+    for (int t = lane; t < a.n_tiles; t += WAVE) s += a.ssq[(size_t)t * a.M + m];
+    s = wave_sum(s);
+    if (lane == 0) a.scale_out[m] = 1.0f / sqrtf(s / (float)a.scale_n + a.eps);
+  }
+}
+
+template <typename T, int MT, int NU, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
+                                         int tile0, int lane) {
+  const int c16 = lane & 15;
+  const int rgrp = (lane >> 4) << 2;
+  if constexpr (EPI == EPI_STORE) {
+    const int tile = tile0;
+    const int col = tile * TILE_N + c16;
+    float sq[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + rgrp + v;
+        sq[mt][v] = 0.f;
+        if (m < a.M) {
+          float* o = a.out + (size_t)m * a.ldo + col;
+          float y = acc[0][mt][v];
+          if (a.accumulate) y = *o + y;
+          *o = y;
+          sq[mt][v] = y * y;
+        }
+      }
+    if (a.ssq) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = mt * 16 + rgrp + v;
+          const float r = sum16(sq[mt][v]);
+          if (c16 == 0 && m < a.M) a.ssq[(size_t)tile * a.M + m] = r;
+        }
+      fence_device();
+      int old = 0;
+      if (lane == 0) old = atomic_inc_device(a.gcnt);
+      old = __shfl(old, 0, WAVE);
+      if (old == a.n_units - 1) {
+        fence_device();
+        finish_row_scale(a, lane);
+        if (lane == 0) atomic_store_zero(a.gcnt);
+      }
+    }
+  } else if constexpr (EPI == EPI_ROPE) {
+    const int col = tile0 * TILE_N + c16;
+    const int hh = col / a.hd;
+    const int p = col - hh * a.hd;
+    const int i = p >> 1;
+    const int second = p & 1;
+    const int dim = i + second * (a.hd >> 1);
+    const bool rot = hh < a.hq + a.hkv;
+    const double inv_freq = pow((double)a.theta, -2.0 * (double)i / (double)a.hd);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + rgrp + v;
+        const float val = acc[0][mt][v];
+        const float partner = __shfl_xor(val, 1, WAVE);
+        if (m < a.M) {
+          const int b = m / a.rows_per_seq;
+          const int row = m - b * a.rows_per_seq;
+          const int pos = a.len[b] + row + a.pos_off;
+          float y = val;
+          if (rot) {
+            double sn, cs;
+            sincos((double)pos * inv_freq, &sn, &cs);
+            const float c = (float)cs, s = (float)sn;
+            const float x1 = second ? partner : val;
+            const float x2 = second ? val : partner;
+            y = second ? (x2 * c + x1 * s) : (x1 * c - x2 * s);
+          }
+          if (hh < a.hq) {
+            a.qout[((size_t)m * a.hq + hh) * a.hd + dim] = y;
+          } else if (pos >= a.max_ctx || pos < 0) {
+            raise_error(a.err, ERRBIT_CAPACITY);
+          } else {
+            const bool isk = hh < a.hq + a.hkv;
+            const int g = isk ? hh - a.hq : hh - a.hq - a.hkv;
+            T* cache = reinterpret_cast<T*>(isk ? a.kcache : a.vcache);
+            Elem<T>::store(cache + (size_t)b * a.cache_b_stride +
+                               ((size_t)g * a.max_ctx + pos) * a.hd + dim,
+                           y);
+          }
+        }
+      }
+  } else if constexpr (EPI == EPI_SILU) {
+    const int f = (tile0 >> 1) * TILE_N + c16;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + rgrp + v;
+        if (m < a.M) {
+          const float g = acc[0][mt][v];
+          const float up = acc[1][mt][v];
+          const float h = g / (1.0f + expf(-g)) * up;
+          Elem<T>::store(reinterpret_cast<T*>(a.hout) + (size_t)m * a.ldh + f, h);
+        }
+      }
+  } else {  // EPI_ARGMAX
+    const int keep_row = a.unit_row ? a.unit_row[u] : -1;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + rgrp + v;
+        float best = -INFINITY;
+        int bidx = 0x7fffffff;
+        bool nan = false;
+#pragma unroll
+        for (int t = 0; t < NU; ++t) {
+          const int tile = tile0 + t;
+          if (tile < a.n_tiles) {
+            const int col = tile * TILE_N + c16;
+            const float y = acc[t][mt][v];
+            nan |= (y != y);
+            const int idx = a.idx_map ? a.idx_map[col] : col;
+            argmax_combine(best, bidx, y, idx);
+            if (a.logits && m < a.M) a.logits[(size_t)m * a.ld_logits + col] = y;
+          }
+        }
+        argmax16(best, bidx);
+        if (nan && m < a.M) raise_error(a.err, ERRBIT_NAN);
+        if (c16 == 0 && m < a.M && (keep_row < 0 || keep_row == m)) {
+          // listed units belong to one row each and are stored by unit index
+          const size_t slot = a.unit_row ? (size_t)u : (size_t)m * a.ld_amax + u;
+          a.amax_val[slot] = best;
+          a.amax_idx[slot] = bidx;
+        }
+      }
+  }
+}
+
+template <typename T, int MT, int NU, int XM, int EPI>
+__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wid = threadIdx.x >> 6;
+  const int split = blockIdx.x % a.S;
+  const int u = (blockIdx.x / a.S) * 4 + wid;
+  const int n_units = a.n_units_dev ? min(*a.n_units_dev, a.n_units) : a.n_units;
+  if (u >= n_units) return;
+  const int tile0 = a.unit_tile ? a.unit_tile[u] : u * NU;
+  const int kb0 = split * a.kb_per_split;
+  const int kb1 = min(a.nkb, kb0 + a.kb_per_split);
+  const T* W = reinterpret_cast<const T*>(a.W);
+
+  float rs[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + (lane & 15);
+    rs[mt] = (XM == XM_NORM && m < a.M) ? a.xscale[m] : 0.f;
+  }
+  bool tvalid[NU];
+#pragma unroll
+  for (int t = 0; t < NU; ++t) tvalid[t] = (tile0 + t) < a.n_tiles;
+
+  f32x4 acc[NU][MT];
+#pragma unroll
+  for (int t = 0; t < NU; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int U = (sizeof(T) == 2) ? 8 : 4;
+  int kb = kb0;
+  for (; kb + U <= kb1; kb += U) {
+    Frag<T> w[U][NU];
+    Frag<T> x[U][MT];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+      for (int t = 0; t < NU; ++t) {
+        if (tvalid[t]) load_w<T>(w[uu][t], W, (size_t)(tile0 + t), a.nkb, kb + uu, lane);
+        else zero_frag(w[uu][t]);
+      }
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        load_x<T, XM>(x[uu][mt], a, mt * 16 + (lane & 15), rs[mt], kb + uu, lane);
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+      for (int t = 0; t < NU; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[uu][mt], w[uu][t], acc[t][mt]);
+  }
+  for (; kb < kb1; ++kb) {
+    Frag<T> w[NU];
+    Frag<T> x[MT];
+#pragma unroll
+    for (int t = 0; t < NU; ++t) {
+      if (tvalid[t]) load_w<T>(w[t], W, (size_t)(tile0 + t), a.nkb, kb, lane);
+      else zero_frag(w[t]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) load_x<T, XM>(x[mt], a, mt * 16 + (lane & 15), rs[mt], kb, lane);
+#pragma unroll
+    for (int t = 0; t < NU; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[mt], w[t], acc[t][mt]);
+  }
+
+  if (a.S > 1) {
+    const int rgrp = (lane >> 4) << 2;
+    const size_t stride_s = (size_t)a.n_units * NU * a.M * TILE_N;
+#pragma unroll
+    for (int t = 0; t < NU; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = mt * 16 + rgrp + v;
+          if (m < a.M)
+            a.part[split * stride_s + (((size_t)u * NU + t) * a.M + m) * TILE_N + (lane & 15)] =
+                acc[t][mt][v];
+        }
+    fence_device();
+    int old = 0;
+    if (lane == 0) old = atomic_inc_device(a.cnt + u);
+    old = __shfl(old, 0, WAVE);
+    if (old != a.S - 1) return;
+    fence_device();
+#pragma unroll
+    for (int t = 0; t < NU; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = mt * 16 + rgrp + v;
+          float s = 0.f;
+          if (m < a.M) {
+            const float* p = a.part + (((size_t)u * NU + t) * a.M + m) * TILE_N + (lane & 15);
+            for (int sp = 0; sp < a.S; ++sp) s += __builtin_nontemporal_load(p + sp * stride_s);
+          }
+          acc[t][mt][v] = s;
+        }
+    if (lane == 0) atomic_store_zero(a.cnt + u);
+  }
+  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, lane);
+}
+
+template <typename T, int MT, int NU, int XM, int EPI>
+hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+  const int groups = (a.n_units + 3) / 4;
+  dim3 grid(groups * a.S), block(256);
+  hipLaunchKernelGGL((gemm_kernel<T, MT, NU, XM, EPI>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int MT>
+hipError_t dispatch_epi(int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
+  if (epi == EPI_STORE && NU == 1)
+    return xmode == XM_NORM ? launch_t<T, MT, 1, XM_NORM, EPI_STORE>(a, st)
+                            : launch_t<T, MT, 1, XM_ELEM, EPI_STORE>(a, st);
+  if (epi == EPI_ROPE && NU == 1)
+    return xmode == XM_NORM ? launch_t<T, MT, 1, XM_NORM, EPI_ROPE>(a, st)
+                            : launch_t<T, MT, 1, XM_ELEM, EPI_ROPE>(a, st);
+  if (epi == EPI_SILU && NU == 2)
+    return xmode == XM_NORM ? launch_t<T, MT, 2, XM_NORM, EPI_SILU>(a, st)
+                            : launch_t<T, MT, 2, XM_ELEM, EPI_SILU>(a, st);
+  if (epi == EPI_ARGMAX && NU == 4)
+    return xmode == XM_NORM ? launch_t<T, MT, 4, XM_NORM, EPI_ARGMAX>(a, st)
+                            : launch_t<T, MT, 4, XM_ELEM, EPI_ARGMAX>(a, st);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t dispatch_mt(int MT, int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
+  switch (MT) {
+    case 1: return dispatch_epi<T, 1>(NU, xmode, epi, a, st);
+    case 2: return dispatch_epi<T, 2>(NU, xmode, epi, a, st);
+    case 4: return dispatch_epi<T, 4>(NU, xmode, epi, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int dtype, int MT, int NU, int xmode, int epi, const GemmArgs& a,
+                       hipStream_t st) {
+  if (a.n_units <= 0) return hipSuccess;
+  return dtype == DT_BF16 ? dispatch_mt<bf16_t>(MT, NU, xmode, epi, a, st)
+                          : dispatch_mt<float>(MT, NU, xmode, epi, a, st);
+}
+
+}  // namespace specdec

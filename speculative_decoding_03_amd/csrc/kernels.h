@@ -1,0 +1,121 @@
+// Internal launcher interface between the C-ABI layer (specdec.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specdec {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+enum XMode { XM_ELEM = 0, XM_NORM = 1 };
+enum Epi { EPI_STORE = 0, EPI_ROPE = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
+
+// One skinny GEMM  Y[M][N] = X[M][Kd] . W[N][Kd]^T  over packed tiles, with a fused
+// X prologue and output epilogue.  Work unit = NU consecutive 16-row tiles (or a tile
+// listed in unit_tile); K is split S ways, S fixed by (N, Kd) only.
+struct GemmArgs {
+  // weights
+  const void* W = nullptr;
+  int nkb = 0;        // Kd / 32
+  int n_tiles = 0;    // tiles of the (stacked) matrix that exist
+  int n_units = 0;    // launch upper bound of work units
+  const int* unit_tile = nullptr;  // optional first tile of unit u
+  const int* unit_row = nullptr;   // optional: argmax keeps only this row of unit u
+  const int* n_units_dev = nullptr;  // optional device count of valid units
+  int S = 1, kb_per_split = 0;
+  int M = 0;
+  // X operand: XM_ELEM -> storage-typed [M][ldx]; XM_NORM -> fp32 [M][ldx] * xscale[m] * xnorm[k]
+  const void* X = nullptr;
+  int ldx = 0;
+  const float* xscale = nullptr;
+  const float* xnorm = nullptr;
+  // split-K scratch
+  float* part = nullptr;
+  int* cnt = nullptr;   // per-unit arrival counters (zero between launches)
+  int* gcnt = nullptr;  // whole-GEMM arrival counter (row-scale epilogue)
+  int* err = nullptr;
+  // EPI_STORE: out[m][col] (=|+=) y; optional row scale 1/sqrt(sum(out^2)/scale_n + eps)
+  float* out = nullptr;
+  int ldo = 0;
+  int accumulate = 0;
+  float* ssq = nullptr;        // [n_tiles][M] partial sums of squares
+  float* scale_out = nullptr;  // [M]
+  int scale_n = 0;
+  float eps = 0.f;
+  // EPI_ROPE: columns are heads of hd with rotary pairs interleaved; heads [0,hq) -> qout,
+  // [hq, hq+hkv) -> kcache, [hq+hkv, hq+2hkv) -> vcache at position len[b] + row + pos_off.
+  float* qout = nullptr;
+  void* kcache = nullptr;
+  void* vcache = nullptr;
+  const int* len = nullptr;
+  int rows_per_seq = 1;
+  int pos_off = 0;
+  int hq = 0, hkv = 0, hd = 0;
+  int max_ctx = 0;
+  int cache_b_stride = 0;  // elements between sequences in one layer's cache = hkv*max_ctx*hd
+  float theta = 10000.f;
+  // EPI_SILU: hout[m][f] = silu(gate) * up, gate/up tiles interleaved
+  void* hout = nullptr;
+  int ldh = 0;
+  // EPI_ARGMAX: per unit (value, index) of the row maximum, lowest index on ties
+  float* amax_val = nullptr;
+  int* amax_idx = nullptr;
+  int ld_amax = 0;
+  const int* idx_map = nullptr;  // optional column -> reported index
+  float* logits = nullptr;       // optional full fp32 output [M][ld_logits]
+  int ld_logits = 0;
+};
+
+hipError_t launch_gemm(int dtype, int MT, int NU, int xmode, int epi, const GemmArgs& a,
+                       hipStream_t st);
+
+// Grouped-query attention of `rows_per_seq` query rows per sequence over one layer's cache.
+// Row i of sequence b sees keys [0, len[b] + i + key_off).  Chunks of CH keys are reduced in
+// fixed absolute positions and combined (log-sum-exp) by the last chunk to finish.
+struct AttnArgs {
+  const float* q = nullptr;  // [B*R][hq][hd]
+  const void* kcache = nullptr;
+  const void* vcache = nullptr;
+  const int* len = nullptr;
+  void* out = nullptr;  // storage-typed [B*R][hq*hd]
+  float* part = nullptr;
+  int* cnt = nullptr;
+  int* err = nullptr;
+  int B = 0, R = 0, key_off = 0;
+  int hq = 0, hkv = 0, hd = 0;
+  int max_ctx = 0;
+  int cache_b_stride = 0;
+  int chunk = 256;
+  int n_chunks = 0;  // launch bound = ceil(max_ctx / chunk)
+  float scale = 0.f;
+};
+
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+
+// Misc kernels (misc.hip).
+hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
+                        float* x, float* ssq_unused, float* scale, float eps, int vocab, int* err,
+                        hipStream_t st);
+hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
+                         int B, int R, const int* tokens, int* out_tokens, int* n_emit,
+                         int* next_tok, int commit, int* len, float* hid, const float* X, int d,
+                         int* argmax_out, int* err, hipStream_t st);
+hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid, const float* X,
+                         int d, int* err, hipStream_t st);
+hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
+                              int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
+                              const float* norm_e, int d, int Dd, float eps, void* u, int B,
+                              int* err, hipStream_t st);
+hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int tiles_per_cluster,
+                                 int units_per_cluster, int* unit_tile, int* unit_row,
+                                 hipStream_t st);
+hipError_t launch_draft_finalize(const float* amax_val, const int* amax_idx, int ld_amax,
+                                 int parts_per_seq, int seq_offset, int B, int K, int j,
+                                 const int* len,
+                                 const int* inject, int inj_stride, int* drafts, int* dtok,
+                                 int* err, hipStream_t st);
+hipError_t launch_pack(int dtype, const void* src, void* dst, int N, int Kd, int kind, int hd,
+                       int split_rows, hipStream_t st);
+hipError_t launch_fill_i32(int* p, int v, size_t n, hipStream_t st);
+
+}  // namespace specdec

@@ -1,0 +1,347 @@
+// Small kernels of the step: embedding gather, fused argmax + acceptance + commit, KV commit,
+// drafter input, cluster selection, draft finalisation, weight packing.
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace specdec {
+
+namespace {
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
+  return s;
+}
+
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* rv, int* ri) {
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = __shfl_xor(v, o, WAVE);
+    const int i2 = __shfl_xor(i, o, WAVE);
+    argmax_combine(v, i, v2, i2);
+  }
+  __syncthreads();
+  if (lane == 0) { rv[wid] = v; ri[wid] = i; }
+  __syncthreads();
+  v = rv[0];
+  i = ri[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_combine(v, i, rv[w], ri[w]);
+}
+
+// x[m] = E[tokens[m]] (fp32 residual), scale[m] = 1/sqrt(mean(x^2) + eps).
+template <typename T>
+__global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, const int* tokens,
+                                                    float* x, float* scale, float eps, int vocab,
+                                                    int* err) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  int tok = tokens[m];
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) raise_error(err, ERRBIT_TOKEN);
+    tok = 0;
+  }
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    const float v = Elem<T>::load(E + packed_offset(tok, k, nkb));
+    x[(size_t)m * d + k] = v;
+    ss += v * v;
+  }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) scale[m] = 1.0f / sqrtf(ss / (float)d + eps);
+}
+
+// Per sequence: G[i] = argmax of row i over the LM-head partials; m = longest prefix with
+// tokens[i+1] == G[i]; emit tokens[1..m] and G[m]; optionally commit (len += m+1, hid = X[m]).
+__global__ void __launch_bounds__(256) accept_kernel(
+    const float* amax_val, const int* amax_idx, int n_parts, int ld_amax, int R,
+    const int* tokens, int* out_tokens, int* n_emit, int* next_tok, int commit, int* len,
+    float* hid, const float* X, int d, int* argmax_out, int* err) {
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  __shared__ int G[64];
+  __shared__ int m_sh;
+  const int b = blockIdx.x;
+  for (int i = 0; i < R; ++i) {
+    const int row = b * R + i;
+    float v = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int p = threadIdx.x; p < n_parts; p += blockDim.x)
+      argmax_combine(v, idx, amax_val[(size_t)row * ld_amax + p], amax_idx[(size_t)row * ld_amax + p]);
+    block_argmax(v, idx, rv, ri);
+    if (threadIdx.x == 0) {
+      G[i] = idx;
+      if (argmax_out) argmax_out[row] = idx;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int K = R - 1;
+    int m = 0;
+    if (tokens) {
+      while (m < K && tokens[b * R + m + 1] == G[m]) ++m;
+    }
+    if (out_tokens) {
+      for (int j = 0; j < m; ++j) out_tokens[b * R + j] = tokens[b * R + j + 1];
+      out_tokens[b * R + m] = G[m];
+      for (int j = m + 1; j < R; ++j) out_tokens[b * R + j] = -1;
+    }
+    if (n_emit) n_emit[b] = m + 1;
+    if (next_tok) next_tok[b] = G[m];
+    if (G[m] == 0x7fffffff) raise_error(err, ERRBIT_NAN);
+    m_sh = m;
+  }
+  __syncthreads();
+  if (commit) {
+    const int m = m_sh;
+    for (int k = threadIdx.x; k < d; k += blockDim.x)
+      hid[(size_t)b * d + k] = X[((size_t)b * R + m) * d + k];
+    if (threadIdx.x == 0) len[b] += m + 1;
+  }
+}
+
+__global__ void __launch_bounds__(256) commit_kernel(const int* n_commit, int R, int* len,
+                                                     float* hid, const float* X, int d, int* err) {
+  const int b = blockIdx.x;
+  const int n = n_commit[b];
+  if (n < 1 || n > R) {
+    if (threadIdx.x == 0) raise_error(err, ERRBIT_CAPACITY);
+    return;
+  }
+  for (int k = threadIdx.x; k < d; k += blockDim.x)
+    hid[(size_t)b * d + k] = X[((size_t)b * R + n - 1) * d + k];
+  if (threadIdx.x == 0) len[b] += n;
+}
+
+// u[b] = [ rms(h[b]) * norm_h ; rms(table[row(tok[b])]) * norm_e ] in the storage dtype.
+template <typename T>
+__global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const int* tok,
+                                                          const T* table, int nkb_table,
+                                                          const int* vocab_row, int vocab,
+                                                          const float* norm_h, const float* norm_e,
+                                                          int d, int Dd, float eps, T* u, int* err) {
+  __shared__ float red[4];
+  __shared__ float ebuf[1024];
+  const int b = blockIdx.x;
+  int c = tok[b];
+  if (c < 0 || c >= vocab) {
+    if (threadIdx.x == 0) raise_error(err, ERRBIT_TOKEN);
+    c = 0;
+  }
+  const int row = vocab_row[c];
+  float ssh = 0.f;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    const float v = h[(size_t)b * d + k];
+    ssh += v * v;
+  }
+  ssh = block_sum(ssh, red);
+  float sse = 0.f;
+  for (int k = threadIdx.x; k < Dd; k += blockDim.x) {
+    const float v = Elem<T>::load(table + packed_offset(row, k, nkb_table));
+    ebuf[k] = v;
+    sse += v * v;
+  }
+  sse = block_sum(sse, red);
+  const float rh = 1.0f / sqrtf(ssh / (float)d + eps);
+  const float re = 1.0f / sqrtf(sse / (float)Dd + eps);
+  T* ub = u + (size_t)b * (d + Dd);
+  for (int k = threadIdx.x; k < d; k += blockDim.x)
+    Elem<T>::store(ub + k, h[(size_t)b * d + k] * rh * norm_h[k]);
+  for (int k = threadIdx.x; k < Dd; k += blockDim.x)
+    Elem<T>::store(ub + d + k, ebuf[k] * re * norm_e[k]);
+}
+
+// Selects the k_c best clusters of z[b] (ties -> lower cluster id) and lists their tiles as
+// argmax units: selected cluster r of sequence b owns units (b*k_c + r)*upc .. +upc-1.
+__global__ void __launch_bounds__(256) cluster_select_kernel(const float* z, int Nc, int k_c,
+                                                             int tiles_per_cluster, int upc,
+                                                             int* unit_tile, int* unit_row) {
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int b = blockIdx.x;
+  const float* zb = z + (size_t)b * Nc;
+  const int tiles_per_unit = tiles_per_cluster / upc;
+  if (k_c == 1) {
+    float v = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int c = threadIdx.x; c < Nc; c += blockDim.x) argmax_combine(v, idx, zb[c], c);
+    block_argmax(v, idx, rv, ri);
+    if (threadIdx.x < upc) {
+      const int u = b * upc + threadIdx.x;
+      unit_tile[u] = idx * tiles_per_cluster + threadIdx.x * tiles_per_unit;
+      unit_row[u] = b;
+    }
+    return;
+  }
+  for (int c = threadIdx.x; c < Nc; c += blockDim.x) {
+    const float zc = zb[c];
+    int rank = 0;
+    for (int c2 = 0; c2 < Nc; ++c2) {
+      const float z2 = zb[c2];
+      rank += (z2 > zc) || (z2 == zc && c2 < c);
+    }
+    if (rank < k_c) {
+      for (int q = 0; q < upc; ++q) {
+        const int u = (b * k_c + rank) * upc + q;
+        unit_tile[u] = c * tiles_per_cluster + q * tiles_per_unit;
+        unit_row[u] = b;
+      }
+    }
+  }
+}
+
+// Reduces a sequence's head partials to the drafted token, records it as the next sub-step's
+// input, and applies the optional injected replacement for slot j at position len[b] + j.
+__global__ void __launch_bounds__(256) draft_finalize_kernel(
+    const float* amax_val, const int* amax_idx, int ld_amax, int parts_per_seq, int seq_offset,
+    int K, int j, const int* len, const int* inject, int inj_stride, int* drafts, int* dtok,
+    int* err) {
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int b = blockIdx.x;
+  const int u0 = b * seq_offset;
+  float v = -INFINITY;
+  int idx = 0x7fffffff;
+  for (int p = threadIdx.x; p < parts_per_seq; p += blockDim.x)
+    argmax_combine(v, idx, amax_val[(size_t)b * ld_amax + u0 + p], amax_idx[(size_t)b * ld_amax + u0 + p]);
+  block_argmax(v, idx, rv, ri);
+  if (threadIdx.x == 0) {
+    if (idx == 0x7fffffff) {
+      raise_error(err, ERRBIT_NAN);
+      idx = 0;
+    }
+    dtok[b] = idx;
+    int out = idx;
+    if (inject) {
+      const long long slot = (long long)(len[b] + j) * K + (j - 1);
+      if (slot >= 0 && slot < inj_stride) {
+        const int r = inject[(size_t)b * inj_stride + slot];
+        if (r >= 0) out = r;
+      }
+    }
+    drafts[b * K + (j - 1)] = out;
+  }
+}
+
+// dst (packed tiles) <- src (logical row-major [N][Kd]).
+//   kind 0: plain; kind 1: rotary heads of hd with pairs (i, i+hd/2) made adjacent;
+//   kind 2: gate rows [0, F) and up rows [F, 2F) interleaved tile by tile (F = split_rows).
+template <typename T>
+__global__ void pack_kernel(const T* src, T* dst, int N, int Kd, int kind, int hd, int F) {
+  const size_t total = (size_t)N * Kd;
+  const int nkb = Kd / TILE_K;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int n = (int)(e / Kd);
+    const int k = (int)(e - (size_t)n * Kd);
+    int sr = n;
+    if (kind == 1) {
+      const int head = n / hd, p = n - head * hd;
+      sr = head * hd + (p >> 1) + (p & 1) * (hd >> 1);
+    } else if (kind == 2) {
+      const int tile = n >> 4;
+      sr = (tile & 1) * F + (tile >> 1) * TILE_N + (n & 15);
+    }
+    dst[packed_offset(n, k, nkb)] = src[(size_t)sr * Kd + k];
+  }
+}
+
+__global__ void fill_i32_kernel(int* p, int v, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
+                        float* x, float*, float* scale, float eps, int vocab, int* err,
+                        hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st,
+                       (const bf16_t*)E, nkb, d, tokens, x, scale, eps, vocab, err);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, nkb, d,
+                       tokens, x, scale, eps, vocab, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
+                         int B, int R, const int* tokens, int* out_tokens, int* n_emit,
+                         int* next_tok, int commit, int* len, float* hid, const float* X, int d,
+                         int* argmax_out, int* err, hipStream_t st) {
+  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(256), 0, st, amax_val, amax_idx, n_parts,
+                     ld_amax, R, tokens, out_tokens, n_emit, next_tok, commit, len, hid, X, d,
+                     argmax_out, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid, const float* X,
+                         int d, int* err, hipStream_t st) {
+  hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(256), 0, st, n_commit, R, len, hid, X, d, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
+                              int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
+                              const float* norm_e, int d, int Dd, float eps, void* u, int B,
+                              int* err, hipStream_t st) {
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(draft_input_kernel<bf16_t>, dim3(B), dim3(256), 0, st, h, tok,
+                       (const bf16_t*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
+                       eps, (bf16_t*)u, err);
+  else
+    hipLaunchKernelGGL(draft_input_kernel<float>, dim3(B), dim3(256), 0, st, h, tok,
+                       (const float*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
+                       eps, (float*)u, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int tiles_per_cluster,
+                                 int units_per_cluster, int* unit_tile, int* unit_row,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(cluster_select_kernel, dim3(B), dim3(256), 0, st, z, Nc, k_c,
+                     tiles_per_cluster, units_per_cluster, unit_tile, unit_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_finalize(const float* amax_val, const int* amax_idx, int ld_amax,
+                                 int parts_per_seq, int seq_offset, int B, int K, int j,
+                                 const int* len, const int* inject, int inj_stride, int* drafts,
+                                 int* dtok, int* err, hipStream_t st) {
+  hipLaunchKernelGGL(draft_finalize_kernel, dim3(B), dim3(256), 0, st, amax_val, amax_idx,
+                     ld_amax, parts_per_seq, seq_offset, K, j, len, inject, inj_stride, drafts,
+                     dtok, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int dtype, const void* src, void* dst, int N, int Kd, int kind, int hd,
+                       int split_rows, hipStream_t st) {
+  const size_t total = (size_t)N * Kd;
+  const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(pack_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)src,
+                       (bf16_t*)dst, N, Kd, kind, hd, split_rows);
+  else
+    hipLaunchKernelGGL(pack_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)src,
+                       (float*)dst, N, Kd, kind, hd, split_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int* p, int v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace specdec

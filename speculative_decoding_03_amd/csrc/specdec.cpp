@@ -1,0 +1,681 @@
+// C-ABI layer of libspecdec: validation, workspace carving, split-K policy and the launch
+// sequences of draft / verify / accept / commit.  All device memory belongs to the caller.
+
+#include "../../include/specdec.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace specdec;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int TARGET_TASKS = 8192;  // wave-tasks per GEMM launch to fill 256 CUs
+constexpr int MIN_KB_PER_TASK = 8;  // 8 KB of bf16 weights per tile per task at least
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// One projection: packed weights plus its fixed split-K decomposition.
+struct Gemm {
+  const void* W = nullptr;
+  int N = 0, Kd = 0, nkb = 0, n_tiles = 0, NU = 1, n_units = 0, S = 1, kbps = 0;
+};
+
+Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
+  Gemm g;
+  g.W = W;
+  g.N = N;
+  g.Kd = Kd;
+  g.nkb = Kd / 32;
+  g.n_tiles = N / 16;
+  g.NU = NU;
+  g.n_units = cdiv(g.n_tiles, NU);
+  int S = 1;
+  if (allow_split) {
+    S = std::max(1, cdiv(TARGET_TASKS, g.n_units));
+    S = std::min(S, std::max(1, g.nkb / MIN_KB_PER_TASK));
+  }
+  g.kbps = cdiv(g.nkb, S);
+  g.S = cdiv(g.nkb, g.kbps);
+  return g;
+}
+
+size_t gemm_part_floats(const Gemm& g, int M) {
+  return g.S > 1 ? (size_t)g.S * g.n_units * g.NU * M * 16 : 0;
+}
+
+struct Layout {
+  size_t x, scale, q, o, h, ssq, part, cnt, gcnt, amax_v, amax_i, att_part, att_cnt, err;
+  size_t u, xd, scale_d, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
+  size_t total;
+};
+
+struct Dims {
+  int Mx, Bx, Rall_max, n_chunks, chunk, esz, parts;
+};
+
+}  // namespace
+
+struct specdec_ctx {
+  specdec_config cfg{};
+  Dims dm{};
+  Layout lay{};
+  char* ws = nullptr;
+  void* kv_k = nullptr;
+  void* kv_v = nullptr;
+  int* len = nullptr;
+  float* hid = nullptr;
+  // weights
+  const void* embed = nullptr;
+  const float* final_norm = nullptr;
+  std::vector<const void*> lw, dw;
+  specdec_weights w{};
+  // GEMMs
+  std::vector<Gemm> g_qkv, g_o, g_gu, g_down;
+  Gemm g_head, g_in, g_back, g_cent, g_table, g_clu;
+  std::vector<Gemm> g_dq, g_do, g_dgu, g_ddown;
+  // host-side bound on len
+  std::vector<int> len_hi;
+  int last_B = 0, last_R = 0;
+  // profiling
+  int prof_class = -1, prof_cap = 0, prof_n = 0;
+  std::vector<hipEvent_t> prof_ev;
+};
+
+namespace {
+
+bool valid_config(const specdec_config* c) {
+  if (!c) return false;
+  if (c->dtype != SPECDEC_F32 && c->dtype != SPECDEC_BF16) return false;
+  if (c->n_layers < 1 || c->d_model < 32 || c->n_q_heads < 1 || c->n_kv_heads < 1) return false;
+  if (c->n_q_heads % c->n_kv_heads) return false;
+  if (c->head_dim % 16 || c->head_dim > 256 || c->head_dim < 16) return false;
+  const int qd = c->n_q_heads * c->head_dim;
+  if (c->d_model % 32 || qd % 32 || c->ffn_dim % 32 || c->ffn_dim < 32) return false;
+  if (c->d_layers < 1 || c->d_dim % 32 || c->d_dim < 32 || c->d_dim > 1024) return false;
+  if (c->d_ffn % 32 || c->d_ffn < 32) return false;
+  if (c->vocab % 64 || c->vocab < 64 || c->n_centroids < 16 || c->n_centroids % 16) return false;
+  if (c->vocab % c->n_centroids || (c->vocab / c->n_centroids) % 64) return false;
+  if (c->max_batch < 1 || c->max_rows < 1 || c->max_rows > 64) return false;
+  if (c->max_batch * c->max_rows > 64) return false;
+  if (c->max_draft < 1 || c->max_draft + 1 > c->max_rows) return false;
+  if (c->max_ctx < c->max_rows + 1) return false;
+  if (c->kv_src_layer >= c->n_layers) return false;
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return false;
+  return true;
+}
+
+int attn_chunk(const specdec_config* c) {
+  // Fixed by the configuration (never by the number of rows), so chunk boundaries are the same
+  // for a verify row and a decode row.  Aim for a few hundred workgroups per layer.
+  int ch = 256;
+  const long long keys = (long long)c->max_ctx * c->n_kv_heads * c->max_batch;
+  while (ch > 64 && keys / ch < 256) ch >>= 1;
+  // score phase: head_dim must split into 8-element pieces across 256/ch threads per key
+  while (ch < 256 && (c->head_dim % (8 * (256 / ch)))) ch <<= 1;
+  return ch;
+}
+
+Dims make_dims(const specdec_config* c) {
+  Dims d;
+  d.Bx = c->max_batch;
+  d.Mx = c->max_batch * c->max_rows;
+  d.Rall_max = c->max_rows * (c->n_q_heads / c->n_kv_heads);
+  d.chunk = attn_chunk(c);
+  d.n_chunks = cdiv(c->max_ctx, d.chunk);
+  d.esz = c->dtype == SPECDEC_BF16 ? 2 : 4;
+  d.parts = c->vocab / 64;
+  return d;
+}
+
+Layout make_layout(const specdec_config* c, const Dims& dm, size_t part_floats, int max_units) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + std::max<size_t>(bytes, 4));
+    return o;
+  };
+  const int d = c->d_model, qd = c->n_q_heads * c->head_dim, Dd = c->d_dim;
+  L.x = take((size_t)dm.Mx * d * 4);
+  L.scale = take((size_t)dm.Mx * 4);
+  L.q = take((size_t)dm.Mx * qd * 4);
+  L.o = take((size_t)dm.Mx * qd * dm.esz);
+  L.h = take((size_t)dm.Mx * c->ffn_dim * dm.esz);
+  L.ssq = take((size_t)dm.Mx * std::max(d, Dd) / 16 * 4);
+  L.part = take(part_floats * 4);
+  L.cnt = take((size_t)max_units * 4);
+  L.gcnt = take(64);
+  L.amax_v = take((size_t)dm.Mx * dm.parts * 4);
+  L.amax_i = take((size_t)dm.Mx * dm.parts * 4);
+  L.att_part = take((size_t)dm.Bx * c->n_kv_heads * dm.n_chunks * dm.Rall_max * (c->head_dim + 2) * 4);
+  L.att_cnt = take((size_t)dm.Bx * c->n_kv_heads * 4);
+  L.err = take(64);
+  L.u = take((size_t)dm.Bx * (d + Dd) * dm.esz);
+  L.xd = take((size_t)dm.Bx * Dd * 4);
+  L.scale_d = take((size_t)dm.Bx * 4);
+  L.dh = take((size_t)dm.Bx * c->d_ffn * dm.esz);
+  L.hnext = take((size_t)dm.Bx * d * 4);
+  L.z = take((size_t)dm.Bx * c->n_centroids * 4);
+  L.utile = take((size_t)dm.parts * dm.Bx * 4);
+  L.urow = take((size_t)dm.Bx * dm.parts * 4);
+  L.dtok = take((size_t)dm.Bx * 4);
+  L.d_amax_v = take((size_t)dm.Bx * dm.parts * 4);  // [B][V/64] (full) or [B*k_c*upc] (clustered)
+  L.d_amax_i = take((size_t)dm.Bx * dm.parts * 4);
+  L.total = off;
+  return L;
+}
+
+void build_gemms(specdec_ctx* x) {
+  const specdec_config& c = x->cfg;
+  const int d = c.d_model, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  x->g_qkv.clear(); x->g_o.clear(); x->g_gu.clear(); x->g_down.clear();
+  x->g_dq.clear(); x->g_do.clear(); x->g_dgu.clear(); x->g_ddown.clear();
+  for (int l = 0; l < c.n_layers; ++l) {
+    const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
+    x->g_qkv.push_back(make_gemm(t ? t[SPECDEC_LW_QKV] : nullptr, qd + 2 * kvd, d, 1));
+    x->g_o.push_back(make_gemm(t ? t[SPECDEC_LW_O] : nullptr, d, qd, 1));
+    x->g_gu.push_back(make_gemm(t ? t[SPECDEC_LW_GATE_UP] : nullptr, 2 * c.ffn_dim, d, 2));
+    x->g_down.push_back(make_gemm(t ? t[SPECDEC_LW_DOWN] : nullptr, d, c.ffn_dim, 1));
+  }
+  x->g_head = make_gemm(x->embed, c.vocab, d, 4);
+  x->g_in = make_gemm(x->w.w_in, c.d_dim, d + c.d_dim, 1);
+  x->g_back = make_gemm(x->w.w_back, d, c.d_dim, 1);
+  x->g_cent = make_gemm(x->w.centroids, c.n_centroids, c.d_dim, 1);
+  x->g_table = make_gemm(x->w.table, c.vocab, c.d_dim, 4);
+  x->g_clu = make_gemm(x->w.table, c.vocab, c.d_dim, 4, false);
+  for (int l = 0; l < c.d_layers; ++l) {
+    const void* const* t = x->dw.data() + (size_t)l * SPECDEC_N_DRAFT_TENSORS;
+    x->g_dq.push_back(make_gemm(t[SPECDEC_DW_Q], qd, c.d_dim, 1));
+    x->g_do.push_back(make_gemm(t[SPECDEC_DW_O], c.d_dim, qd, 1));
+    x->g_dgu.push_back(make_gemm(t[SPECDEC_DW_GATE_UP], 2 * c.d_ffn, c.d_dim, 2));
+    x->g_ddown.push_back(make_gemm(t[SPECDEC_DW_DOWN], c.d_dim, c.d_ffn, 1));
+  }
+}
+
+// Sizing without weights: same shapes as build_gemms.
+void sizing(const specdec_config* c, const Dims& dm, size_t* part_floats, int* max_units) {
+  const int d = c->d_model, qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+  std::vector<Gemm> gs = {
+      make_gemm(nullptr, qd + 2 * kvd, d, 1), make_gemm(nullptr, d, qd, 1),
+      make_gemm(nullptr, 2 * c->ffn_dim, d, 2), make_gemm(nullptr, d, c->ffn_dim, 1),
+      make_gemm(nullptr, c->vocab, d, 4), make_gemm(nullptr, c->d_dim, d + c->d_dim, 1),
+      make_gemm(nullptr, d, c->d_dim, 1), make_gemm(nullptr, c->n_centroids, c->d_dim, 1),
+      make_gemm(nullptr, c->vocab, c->d_dim, 4), make_gemm(nullptr, qd, c->d_dim, 1),
+      make_gemm(nullptr, c->d_dim, qd, 1), make_gemm(nullptr, 2 * c->d_ffn, c->d_dim, 2),
+      make_gemm(nullptr, c->d_dim, c->d_ffn, 1)};
+  size_t pf = 0;
+  int mu = 0;
+  for (auto& g : gs) {
+    pf = std::max(pf, gemm_part_floats(g, dm.Mx));
+    mu = std::max(mu, g.n_units);
+  }
+  *part_floats = pf;
+  *max_units = mu;
+}
+
+template <typename P>
+P* at(specdec_ctx* x, size_t off) {
+  return reinterpret_cast<P*>(x->ws + off);
+}
+
+int mt_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+struct ProfScope {
+  specdec_ctx* x;
+  bool on;
+  hipStream_t st;
+  ProfScope(specdec_ctx* c, int cls, hipStream_t s) : x(c), on(false), st(s) {
+    if (cls >= 0 && x->prof_class == cls && x->prof_n < x->prof_cap) {
+      on = true;
+      (void)hipEventRecord(x->prof_ev[2 * x->prof_n], st);
+    }
+  }
+  ~ProfScope() {
+    if (on) {
+      (void)hipEventRecord(x->prof_ev[2 * x->prof_n + 1], st);
+      x->prof_n++;
+    }
+  }
+};
+
+GemmArgs base_args(specdec_ctx* x, const Gemm& g, int M) {
+  GemmArgs a;
+  a.W = g.W;
+  a.nkb = g.nkb;
+  a.n_tiles = g.n_tiles;
+  a.n_units = g.n_units;
+  a.S = g.S;
+  a.kb_per_split = g.kbps;
+  a.M = M;
+  a.part = at<float>(x, x->lay.part);
+  a.cnt = at<int>(x, x->lay.cnt);
+  a.gcnt = at<int>(x, x->lay.gcnt);
+  a.err = at<int>(x, x->lay.err);
+  a.eps = x->cfg.rms_eps;
+  return a;
+}
+
+#define HIP_TRY(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return SPECDEC_E_HIP; \
+  } while (0)
+
+int run(specdec_ctx* x, int cls, int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
+  ProfScope ps(x, cls, st);
+  HIP_TRY(launch_gemm(x->cfg.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, mt_for(a.M), NU, xmode,
+                      epi, a, st));
+  return SPECDEC_OK;
+}
+
+// x[m] (+)= y with the next RMSNorm's row scale.
+int gemm_resid(specdec_ctx* x, int cls, const Gemm& g, int M, int xmode, const void* X, int ldx,
+               const float* xs, const float* xn, float* out, int ldo, int accumulate,
+               float* scale_out, int scale_n, hipStream_t st) {
+  GemmArgs a = base_args(x, g, M);
+  a.X = X; a.ldx = ldx; a.xscale = xs; a.xnorm = xn;
+  a.out = out; a.ldo = ldo; a.accumulate = accumulate;
+  if (scale_out) {
+    a.ssq = at<float>(x, x->lay.ssq);
+    a.scale_out = scale_out;
+    a.scale_n = scale_n;
+  }
+  return run(x, cls, 1, xmode, EPI_STORE, a, st);
+}
+
+int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hipStream_t st) {
+  const specdec_config& c = x->cfg;
+  AttnArgs a;
+  const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
+  a.q = at<float>(x, x->lay.q);
+  a.kcache = (const char*)x->kv_k + per_layer * layer * x->dm.esz;
+  a.vcache = (const char*)x->kv_v + per_layer * layer * x->dm.esz;
+  a.len = x->len;
+  a.out = x->ws + x->lay.o;
+  a.part = at<float>(x, x->lay.att_part);
+  a.cnt = at<int>(x, x->lay.att_cnt);
+  a.err = at<int>(x, x->lay.err);
+  a.B = B; a.R = R; a.key_off = key_off;
+  a.hq = c.n_q_heads; a.hkv = c.n_kv_heads; a.hd = c.head_dim;
+  a.max_ctx = c.max_ctx;
+  a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
+  a.chunk = x->dm.chunk;
+  a.n_chunks = x->dm.n_chunks;
+  a.scale = 1.0f / std::sqrt((float)c.head_dim);
+  ProfScope ps(x, cls, st);
+  HIP_TRY(launch_attention(c.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, a, st));
+  return SPECDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t specdec_workspace_bytes(const specdec_config* cfg) {
+  if (!valid_config(cfg)) return 0;
+  Dims dm = make_dims(cfg);
+  size_t pf;
+  int mu;
+  sizing(cfg, dm, &pf, &mu);
+  return make_layout(cfg, dm, pf, mu).total;
+}
+
+size_t specdec_kv_elems(const specdec_config* c) {
+  if (!valid_config(c)) return 0;
+  return (size_t)c->n_layers * c->max_batch * c->n_kv_heads * c->max_ctx * c->head_dim;
+}
+
+int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv_k, void* kv_v,
+                   int32_t* len, float* hid, void* workspace, size_t workspace_bytes,
+                   void* stream, specdec_ctx** out) {
+  if (!out) return SPECDEC_E_INVAL;
+  *out = nullptr;
+  if (!valid_config(cfg) || !w || !kv_k || !kv_v || !len || !hid || !workspace)
+    return SPECDEC_E_INVAL;
+  if (cfg->n_experts > 0) return SPECDEC_E_UNSUPPORTED;
+  if (((uintptr_t)workspace) % ALIGN) return SPECDEC_E_INVAL;
+  if (!w->embed || !w->final_norm || !w->layers || !w->table || !w->centroids || !w->row_vocab ||
+      !w->vocab_row || !w->norm_h || !w->norm_e || !w->w_in || !w->d_layers || !w->norm_f ||
+      !w->w_back)
+    return SPECDEC_E_INVAL;
+  for (int i = 0; i < cfg->n_layers * SPECDEC_N_LAYER_TENSORS; ++i)
+    if (!w->layers[i]) return SPECDEC_E_INVAL;
+  for (int i = 0; i < cfg->d_layers * SPECDEC_N_DRAFT_TENSORS; ++i)
+    if (!w->d_layers[i]) return SPECDEC_E_INVAL;
+  if (workspace_bytes < specdec_workspace_bytes(cfg)) return SPECDEC_E_INVAL;
+
+  specdec_ctx* x = new (std::nothrow) specdec_ctx();
+  if (!x) return SPECDEC_E_INVAL;
+  x->cfg = *cfg;
+  if (x->cfg.kv_src_layer < 0) x->cfg.kv_src_layer = cfg->n_layers - 1;
+  x->dm = make_dims(cfg);
+  size_t pf;
+  int mu;
+  sizing(cfg, x->dm, &pf, &mu);
+  x->lay = make_layout(cfg, x->dm, pf, mu);
+  x->ws = reinterpret_cast<char*>(workspace);
+  x->kv_k = kv_k;
+  x->kv_v = kv_v;
+  x->len = len;
+  x->hid = hid;
+  x->w = *w;
+  x->embed = w->embed;
+  x->final_norm = w->final_norm;
+  x->lw.assign(w->layers, w->layers + (size_t)cfg->n_layers * SPECDEC_N_LAYER_TENSORS);
+  x->dw.assign(w->d_layers, w->d_layers + (size_t)cfg->d_layers * SPECDEC_N_DRAFT_TENSORS);
+  x->w.layers = nullptr;
+  x->w.d_layers = nullptr;
+  build_gemms(x);
+  x->len_hi.assign(cfg->max_batch, 0);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // zero the arrival counters and the error word
+  if (launch_fill_i32(at<int>(x, x->lay.cnt), 0, (size_t)mu, st) != hipSuccess ||
+      launch_fill_i32(at<int>(x, x->lay.gcnt), 0, 16, st) != hipSuccess ||
+      launch_fill_i32(at<int>(x, x->lay.att_cnt), 0, (size_t)x->dm.Bx * cfg->n_kv_heads, st) !=
+          hipSuccess ||
+      launch_fill_i32(at<int>(x, x->lay.err), 0, 16, st) != hipSuccess) {
+    delete x;
+    return SPECDEC_E_HIP;
+  }
+  *out = x;
+  return SPECDEC_OK;
+}
+
+int specdec_destroy(specdec_ctx* x) {
+  if (!x) return SPECDEC_E_INVAL;
+  for (auto e : x->prof_ev) (void)hipEventDestroy(e);
+  delete x;
+  return SPECDEC_OK;
+}
+
+int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, float* logits,
+                   int32_t* argmax, void* stream) {
+  if (!x || !tokens) return SPECDEC_E_INVAL;
+  const specdec_config& c = x->cfg;
+  if (B < 1 || B > c.max_batch || R < 1 || R > c.max_rows) return SPECDEC_E_INVAL;
+  for (int b = 0; b < B; ++b)
+    if (x->len_hi[b] + R > c.max_ctx) return SPECDEC_E_CAPACITY;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int M = B * R;
+  const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
+  const int dt = c.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32;
+  float* X = at<float>(x, x->lay.x);
+  float* scale = at<float>(x, x->lay.scale);
+  int* err = at<int>(x, x->lay.err);
+  HIP_TRY(launch_embed(dt, x->embed, x->g_head.nkb, d, tokens, M, X, nullptr, scale, c.rms_eps,
+                       c.vocab, err, st));
+  const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
+  int rc;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
+    {  // fused q/k/v projection + RoPE + KV append
+      GemmArgs a = base_args(x, x->g_qkv[l], M);
+      a.X = X; a.ldx = d; a.xscale = scale; a.xnorm = (const float*)t[SPECDEC_LW_ATTN_NORM];
+      a.qout = at<float>(x, x->lay.q);
+      a.kcache = (char*)x->kv_k + per_layer * l * x->dm.esz;
+      a.vcache = (char*)x->kv_v + per_layer * l * x->dm.esz;
+      a.len = x->len; a.rows_per_seq = R; a.pos_off = 0;
+      a.hq = c.n_q_heads; a.hkv = c.n_kv_heads; a.hd = c.head_dim;
+      a.max_ctx = c.max_ctx; a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
+      a.theta = c.rope_theta;
+      if ((rc = run(x, 2, 1, XM_NORM, EPI_ROPE, a, st))) return rc;
+    }
+    if ((rc = attention(x, l, B, R, 1, 4, st))) return rc;
+    if ((rc = gemm_resid(x, 3, x->g_o[l], M, XM_ELEM, x->ws + x->lay.o, qd, nullptr, nullptr, X,
+                         d, 1, scale, d, st)))
+      return rc;
+    {
+      GemmArgs a = base_args(x, x->g_gu[l], M);
+      a.X = X; a.ldx = d; a.xscale = scale; a.xnorm = (const float*)t[SPECDEC_LW_FFN_NORM];
+      a.hout = x->ws + x->lay.h; a.ldh = c.ffn_dim;
+      if ((rc = run(x, 0, 2, XM_NORM, EPI_SILU, a, st))) return rc;
+    }
+    if ((rc = gemm_resid(x, 1, x->g_down[l], M, XM_ELEM, x->ws + x->lay.h, c.ffn_dim, nullptr,
+                         nullptr, X, d, 1, scale, d, st)))
+      return rc;
+  }
+  {  // final norm + tied LM head with per-unit argmax partials
+    GemmArgs a = base_args(x, x->g_head, M);
+    a.X = X; a.ldx = d; a.xscale = scale; a.xnorm = x->final_norm;
+    a.amax_val = at<float>(x, x->lay.amax_v);
+    a.amax_idx = at<int>(x, x->lay.amax_i);
+    a.ld_amax = x->dm.parts;
+    a.logits = logits; a.ld_logits = c.vocab;
+    if ((rc = run(x, 5, 4, XM_NORM, EPI_ARGMAX, a, st))) return rc;
+  }
+  if (argmax) {
+    HIP_TRY(launch_accept(at<float>(x, x->lay.amax_v), at<int>(x, x->lay.amax_i), x->dm.parts,
+                          x->dm.parts, B, R, nullptr, nullptr, nullptr, nullptr, 0, x->len,
+                          x->hid, X, d, argmax, err, st));
+  }
+  x->last_B = B;
+  x->last_R = R;
+  return SPECDEC_OK;
+}
+
+int specdec_accept(specdec_ctx* x, int32_t B, int32_t K, const int32_t* tokens,
+                   int32_t* out_tokens, int32_t* n_emit, int32_t* next_tok, uint32_t flags,
+                   void* stream) {
+  if (!x || !tokens) return SPECDEC_E_INVAL;
+  if (B != x->last_B || K + 1 != x->last_R || K < 0) return SPECDEC_E_INVAL;
+  const bool commit = (flags & SPECDEC_ACCEPT_COMMIT) != 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(launch_accept(at<float>(x, x->lay.amax_v), at<int>(x, x->lay.amax_i), x->dm.parts,
+                        x->dm.parts, B, K + 1, tokens, out_tokens, n_emit, next_tok,
+                        commit ? 1 : 0, x->len, x->hid, at<float>(x, x->lay.x), x->cfg.d_model,
+                        nullptr, at<int>(x, x->lay.err), st));
+  if (commit)
+    for (int b = 0; b < B; ++b) x->len_hi[b] += K + 1;
+  return SPECDEC_OK;
+}
+
+int specdec_kv_commit(specdec_ctx* x, int32_t B, const int32_t* n_commit, void* stream) {
+  if (!x || !n_commit || B != x->last_B || B < 1) return SPECDEC_E_INVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(launch_commit(n_commit, B, x->last_R, x->len, x->hid, at<float>(x, x->lay.x),
+                        x->cfg.d_model, at<int>(x, x->lay.err), st));
+  for (int b = 0; b < B; ++b) x->len_hi[b] += x->last_R;
+  return SPECDEC_OK;
+}
+
+int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
+                  const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
+                  int64_t inj_stride, void* stream) {
+  if (!x || !cur_tok || !drafts) return SPECDEC_E_INVAL;
+  const specdec_config& c = x->cfg;
+  if (B < 1 || B > c.max_batch || K < 1 || K > c.max_draft) return SPECDEC_E_INVAL;
+  if (head_mode != SPECDEC_HEAD_CLUSTERED && head_mode != SPECDEC_HEAD_FULL) return SPECDEC_E_INVAL;
+  if (head_mode == SPECDEC_HEAD_CLUSTERED && (k_c < 1 || k_c > c.n_centroids)) return SPECDEC_E_INVAL;
+  if (inject && inj_stride < 1) return SPECDEC_E_INVAL;
+  for (int b = 0; b < B; ++b)
+    if (x->len_hi[b] > c.max_ctx) return SPECDEC_E_CAPACITY;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int dt = c.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32;
+  const int d = c.d_model, Dd = c.d_dim, qd = c.n_q_heads * c.head_dim;
+  const int S = c.vocab / c.n_centroids;           // tokens per cluster
+  const int tpc = S / 16, upc = S / 64;            // tiles / argmax units per cluster
+  float* xd = at<float>(x, x->lay.xd);
+  float* sd = at<float>(x, x->lay.scale_d);
+  float* hnext = at<float>(x, x->lay.hnext);
+  int* dtok = at<int>(x, x->lay.dtok);
+  int* err = at<int>(x, x->lay.err);
+  const int src = c.kv_src_layer;
+  int rc;
+  for (int j = 1; j <= K; ++j) {
+    const float* h = (j == 1) ? x->hid : hnext;
+    const int* tok = (j == 1) ? cur_tok : dtok;
+    HIP_TRY(launch_draft_input(dt, h, tok, x->w.table, x->g_table.nkb, x->w.vocab_row, c.vocab,
+                               x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u, B,
+                               err, st));
+    if ((rc = gemm_resid(x, -1, x->g_in, B, XM_ELEM, x->ws + x->lay.u, d + Dd, nullptr, nullptr,
+                         xd, Dd, 0, sd, Dd, st)))
+      return rc;
+    for (int l = 0; l < c.d_layers; ++l) {
+      const void* const* t = x->dw.data() + (size_t)l * SPECDEC_N_DRAFT_TENSORS;
+      {
+        GemmArgs a = base_args(x, x->g_dq[l], B);
+        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = (const float*)t[SPECDEC_DW_N1];
+        a.qout = at<float>(x, x->lay.q);
+        a.len = x->len; a.rows_per_seq = 1; a.pos_off = j - 1;
+        a.hq = c.n_q_heads; a.hkv = 0; a.hd = c.head_dim;
+        a.max_ctx = c.max_ctx; a.theta = c.rope_theta;
+        if ((rc = run(x, -1, 1, XM_NORM, EPI_ROPE, a, st))) return rc;
+      }
+      if ((rc = attention(x, src, B, 1, 0, -1, st))) return rc;
+      if ((rc = gemm_resid(x, -1, x->g_do[l], B, XM_ELEM, x->ws + x->lay.o, qd, nullptr, nullptr,
+                           xd, Dd, 1, sd, Dd, st)))
+        return rc;
+      {
+        GemmArgs a = base_args(x, x->g_dgu[l], B);
+        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = (const float*)t[SPECDEC_DW_N2];
+        a.hout = x->ws + x->lay.dh; a.ldh = c.d_ffn;
+        if ((rc = run(x, -1, 2, XM_NORM, EPI_SILU, a, st))) return rc;
+      }
+      if ((rc = gemm_resid(x, -1, x->g_ddown[l], B, XM_ELEM, x->ws + x->lay.dh, c.d_ffn, nullptr,
+                           nullptr, xd, Dd, 1, sd, Dd, st)))
+        return rc;
+    }
+    // next hidden input: W_back . rms(x)*n_f
+    if ((rc = gemm_resid(x, -1, x->g_back, B, XM_NORM, xd, Dd, sd, x->w.norm_f, hnext, d, 0,
+                         nullptr, 0, st)))
+      return rc;
+    int parts_per_seq, seq_off;
+    {
+      ProfScope ps(x, 6, st);
+      if (head_mode == SPECDEC_HEAD_FULL) {
+        GemmArgs a = base_args(x, x->g_table, B);
+        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = x->w.norm_f;
+        a.amax_val = at<float>(x, x->lay.d_amax_v);
+        a.amax_idx = at<int>(x, x->lay.d_amax_i);
+        a.ld_amax = x->dm.parts;
+        a.idx_map = x->w.row_vocab;
+        HIP_TRY(launch_gemm(dt, mt_for(B), 4, XM_NORM, EPI_ARGMAX, a, st));
+        parts_per_seq = x->dm.parts;
+        seq_off = 0;
+      } else {
+        GemmArgs zc = base_args(x, x->g_cent, B);
+        zc.X = xd; zc.ldx = Dd; zc.xscale = sd; zc.xnorm = x->w.norm_f;
+        zc.out = at<float>(x, x->lay.z); zc.ldo = c.n_centroids;
+        HIP_TRY(launch_gemm(dt, mt_for(B), 1, XM_NORM, EPI_STORE, zc, st));
+        HIP_TRY(launch_cluster_select(at<float>(x, x->lay.z), c.n_centroids, k_c, B, tpc, upc,
+                                      at<int>(x, x->lay.utile), at<int>(x, x->lay.urow), st));
+        GemmArgs a = base_args(x, x->g_clu, B);
+        a.n_units = B * k_c * upc;
+        a.unit_tile = at<int>(x, x->lay.utile);
+        a.unit_row = at<int>(x, x->lay.urow);
+        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = x->w.norm_f;
+        a.amax_val = at<float>(x, x->lay.d_amax_v);
+        a.amax_idx = at<int>(x, x->lay.d_amax_i);
+        a.ld_amax = x->dm.parts;
+        a.idx_map = x->w.row_vocab;
+        HIP_TRY(launch_gemm(dt, mt_for(B), 4, XM_NORM, EPI_ARGMAX, a, st));
+        parts_per_seq = k_c * upc;
+        seq_off = k_c * upc;
+      }
+      HIP_TRY(launch_draft_finalize(at<float>(x, x->lay.d_amax_v), at<int>(x, x->lay.d_amax_i),
+                                    head_mode == SPECDEC_HEAD_FULL ? x->dm.parts : 0,
+                                    parts_per_seq, seq_off, B, K, j, x->len, inject,
+                                    (int)std::min<int64_t>(inj_stride, 0x7fffffff), drafts, dtok,
+                                    err, st));
+    }
+  }
+  return SPECDEC_OK;
+}
+
+int specdec_pack_matrix(const void* src, void* dst, int32_t n, int32_t kd, int32_t dtype,
+                        int32_t kind, int32_t head_dim, int32_t split_rows, void* stream) {
+  if (!src || !dst || n < 16 || kd < 32 || n % 16 || kd % 32) return SPECDEC_E_INVAL;
+  if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_E_INVAL;
+  if (kind == SPECDEC_PACK_ROPE && (head_dim < 16 || head_dim % 16 || n % head_dim))
+    return SPECDEC_E_INVAL;
+  if (kind == SPECDEC_PACK_GATE_UP && (split_rows * 2 != n || split_rows % 16))
+    return SPECDEC_E_INVAL;
+  if (kind < 0 || kind > 2) return SPECDEC_E_INVAL;
+  HIP_TRY(launch_pack(dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, src, dst, n, kd, kind, head_dim,
+                      split_rows, reinterpret_cast<hipStream_t>(stream)));
+  return SPECDEC_OK;
+}
+
+int specdec_set_len_bound(specdec_ctx* x, const int32_t* host_len, int32_t B) {
+  if (!x || !host_len || B < 1 || B > x->cfg.max_batch) return SPECDEC_E_INVAL;
+  for (int b = 0; b < B; ++b) {
+    if (host_len[b] < 0) return SPECDEC_E_INVAL;
+    x->len_hi[b] = host_len[b];
+  }
+  return SPECDEC_OK;
+}
+
+int specdec_read_device_error(specdec_ctx* x, int32_t* host_word, int32_t clear, void* stream) {
+  if (!x || !host_word) return SPECDEC_E_INVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(hipMemcpyAsync(host_word, at<int>(x, x->lay.err), 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  if (clear) HIP_TRY(launch_fill_i32(at<int>(x, x->lay.err), 0, 1, st));
+  return SPECDEC_OK;
+}
+
+int specdec_profile_start(specdec_ctx* x, int32_t cls, int32_t capacity) {
+  if (!x || capacity < 0 || cls < -1 || cls > 6) return SPECDEC_E_INVAL;
+  for (auto e : x->prof_ev) (void)hipEventDestroy(e);
+  x->prof_ev.clear();
+  x->prof_class = -1;
+  x->prof_n = 0;
+  x->prof_ev.resize((size_t)2 * capacity);
+  for (auto& e : x->prof_ev) HIP_TRY(hipEventCreate(&e));
+  x->prof_class = cls;
+  x->prof_cap = capacity;
+  return SPECDEC_OK;
+}
+
+int specdec_profile_read(specdec_ctx* x, float* ms_out, int32_t max, int32_t* n_out) {
+  if (!x || !n_out) return SPECDEC_E_INVAL;
+  const int n = std::min(x->prof_n, max);
+  for (int i = 0; i < n; ++i) {
+    HIP_TRY(hipEventSynchronize(x->prof_ev[2 * i + 1]));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, x->prof_ev[2 * i], x->prof_ev[2 * i + 1]));
+    if (ms_out) ms_out[i] = ms;
+  }
+  *n_out = n;
+  x->prof_class = -1;
+  return SPECDEC_OK;
+}
+
+int specdec_query_split(specdec_ctx* x, int32_t cls, int32_t* splits, int32_t* units) {
+  if (!x || !splits || !units) return SPECDEC_E_INVAL;
+  const Gemm* g = nullptr;
+  switch (cls) {
+    case 0: g = &x->g_gu[0]; break;
+    case 1: g = &x->g_down[0]; break;
+    case 2: g = &x->g_qkv[0]; break;
+    case 3: g = &x->g_o[0]; break;
+    case 5: g = &x->g_head; break;
+    default: return SPECDEC_E_INVAL;
+  }
+  *splits = g->S;
+  *units = g->n_units;
+  return SPECDEC_OK;
+}
+
+const char* specdec_error_string(int code) {
+  switch (code) {
+    case SPECDEC_OK: return "ok";
+    case SPECDEC_E_INVAL: return "invalid argument";
+    case SPECDEC_E_CAPACITY: return "KV-cache capacity exceeded";
+    case SPECDEC_E_HIP: return "HIP launch failure";
+    case SPECDEC_E_UNSUPPORTED: return "unsupported configuration";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,278 @@
+"""Python binding of libspecdec: torch tensors supply device memory and streams, every step of
+the path runs in the library's HIP kernels.  No CPU fallback exists: constructing an Engine
+without the built library or without a GPU raises."""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _ffi as F
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+ABI_DT = {"bf16": F.BF16, "f32": F.F32}
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _s(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Shape:
+    """Model shape as the C ABI sees it."""
+    n_layers: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn_dim: int
+    vocab: int
+    d_layers: int
+    d_dim: int
+    d_ffn: int
+    n_centroids: int
+    kv_src_layer: int = -1
+    dtype: str = "bf16"
+    rms_eps: float = 1e-6
+    rope_theta: float = 10000.0
+    n_experts: int = 0
+    top_k: int = 0
+    expert_ffn: int = 0
+    shared_ffn: int = 0
+
+    @classmethod
+    def of(cls, cfg) -> "Shape":
+        names = cls.__dataclass_fields__.keys()
+        return cls(**{n: getattr(cfg, n) for n in names})
+
+    @property
+    def q_dim(self):
+        return self.n_q_heads * self.head_dim
+
+    @property
+    def kv_dim(self):
+        return self.n_kv_heads * self.head_dim
+
+
+def pack_matrix(src: torch.Tensor, n: int, kd: int, dtype: str, kind: int = F.PACK_PLAIN,
+                head_dim: int = 0, split_rows: int = 0, stream=None) -> torch.Tensor:
+    """Packs a logical row-major [n][kd] device matrix into the streaming tile layout."""
+    assert src.is_cuda and src.is_contiguous() and src.numel() == n * kd
+    dst = torch.empty(n * kd, dtype=src.dtype, device=src.device)
+    F.check(F.load().specdec_pack_matrix(_p(src), _p(dst), n, kd, ABI_DT[dtype], kind, head_dim,
+                                         split_rows, _s(stream)), "specdec_pack_matrix")
+    return dst
+
+
+class DeviceModel:
+    """Packed device weights for one target + drafter pair.
+
+    `source.get(name, layer, shape)` must return a logical row-major device tensor of the
+    storage dtype (fp32 for norm weights); names follow workloads.synth.TID.  The drafter table is
+    stored cluster-major: row r holds vocabulary id perm[r].
+    """
+
+    def __init__(self, shape: Shape, source, perm: torch.Tensor, centroids: torch.Tensor,
+                 device="cuda", stream=None):
+        self.shape = s = shape
+        self.device = device
+        dt = s.dtype
+        keep = self._keep = []
+
+        def k(t):
+            keep.append(t)
+            return t.data_ptr()
+
+        d, qd, kvd, F_ = s.d_model, s.q_dim, s.kv_dim, s.ffn_dim
+        self.layer_ptrs = (C.c_void_p * (s.n_layers * F.N_LAYER_TENSORS))()
+        for l in range(s.n_layers):
+            wq = source.get("wq", l, (qd, d))
+            wk = source.get("wk", l, (kvd, d))
+            wv = source.get("wv", l, (kvd, d))
+            qkv = torch.cat([wq, wk, wv], 0).contiguous()
+            del wq, wk, wv
+            base = l * F.N_LAYER_TENSORS
+            self.layer_ptrs[base + F.LW_QKV] = k(pack_matrix(qkv, qd + 2 * kvd, d, dt, F.PACK_ROPE, s.head_dim, stream=stream))
+            del qkv
+            self.layer_ptrs[base + F.LW_O] = k(pack_matrix(source.get("wo", l, (d, qd)), d, qd, dt, stream=stream))
+            gu = torch.cat([source.get("wg", l, (F_, d)), source.get("wu", l, (F_, d))], 0).contiguous()
+            self.layer_ptrs[base + F.LW_GATE_UP] = k(pack_matrix(gu, 2 * F_, d, dt, F.PACK_GATE_UP, split_rows=F_, stream=stream))
+            del gu
+            self.layer_ptrs[base + F.LW_DOWN] = k(pack_matrix(source.get("wd", l, (d, F_)), d, F_, dt, stream=stream))
+            self.layer_ptrs[base + F.LW_ATTN_NORM] = k(source.get("attn_norm", l, (d,)).float().contiguous())
+            self.layer_ptrs[base + F.LW_FFN_NORM] = k(source.get("ffn_norm", l, (d,)).float().contiguous())
+        self.embed = pack_matrix(source.get("embed", 0, (s.vocab, d)), s.vocab, d, dt, stream=stream)
+        self.final_norm = source.get("final_norm", 0, (d,)).float().contiguous()
+
+        D, Fd = s.d_dim, s.d_ffn
+        perm = perm.to(device=device, dtype=torch.int64)
+        table = source.get("table", 0, (s.vocab, D))
+        self.table = pack_matrix(table.index_select(0, perm).contiguous(), s.vocab, D, dt, stream=stream)
+        del table
+        self.row_vocab = perm.to(torch.int32).contiguous()
+        inv = torch.empty_like(perm)
+        inv[perm] = torch.arange(s.vocab, device=device, dtype=torch.int64)
+        self.vocab_row = inv.to(torch.int32).contiguous()
+        self.centroids = pack_matrix(centroids.to(device=device, dtype=TORCH_DT[dt]).contiguous(),
+                                     s.n_centroids, D, dt, stream=stream)
+        self.norm_h = source.get("norm_h", 0, (d,)).float().contiguous()
+        self.norm_e = source.get("norm_e", 0, (D,)).float().contiguous()
+        self.w_in = pack_matrix(source.get("w_in", 0, (D, d + D)), D, d + D, dt, stream=stream)
+        self.norm_f = source.get("d_nf", 0, (D,)).float().contiguous()
+        self.w_back = pack_matrix(source.get("w_back", 0, (d, D)), d, D, dt, stream=stream)
+        self.dlayer_ptrs = (C.c_void_p * (s.d_layers * F.N_DRAFT_TENSORS))()
+        for l in range(s.d_layers):
+            base = l * F.N_DRAFT_TENSORS
+            self.dlayer_ptrs[base + F.DW_N1] = k(source.get("d_n1", l, (D,)).float().contiguous())
+            self.dlayer_ptrs[base + F.DW_N2] = k(source.get("d_n2", l, (D,)).float().contiguous())
+            self.dlayer_ptrs[base + F.DW_Q] = k(pack_matrix(source.get("d_wq", l, (qd, D)), qd, D, dt, F.PACK_ROPE, s.head_dim, stream=stream))
+            self.dlayer_ptrs[base + F.DW_O] = k(pack_matrix(source.get("d_wo", l, (D, qd)), D, qd, dt, stream=stream))
+            gu = torch.cat([source.get("d_wg", l, (Fd, D)), source.get("d_wu", l, (Fd, D))], 0).contiguous()
+            self.dlayer_ptrs[base + F.DW_GATE_UP] = k(pack_matrix(gu, 2 * Fd, D, dt, F.PACK_GATE_UP, split_rows=Fd, stream=stream))
+            self.dlayer_ptrs[base + F.DW_DOWN] = k(pack_matrix(source.get("d_wd", l, (D, Fd)), D, Fd, dt, stream=stream))
+
+    def abi(self) -> F.Weights:
+        w = F.Weights()
+        w.embed = self.embed.data_ptr()
+        w.final_norm = self.final_norm.data_ptr()
+        w.layers = C.cast(self.layer_ptrs, C.POINTER(C.c_void_p))
+        w.table = self.table.data_ptr()
+        w.centroids = self.centroids.data_ptr()
+        w.row_vocab = self.row_vocab.data_ptr()
+        w.vocab_row = self.vocab_row.data_ptr()
+        w.norm_h = self.norm_h.data_ptr()
+        w.norm_e = self.norm_e.data_ptr()
+        w.w_in = self.w_in.data_ptr()
+        w.d_layers = C.cast(self.dlayer_ptrs, C.POINTER(C.c_void_p))
+        w.norm_f = self.norm_f.data_ptr()
+        w.w_back = self.w_back.data_ptr()
+        return w
+
+    def weight_bytes(self) -> int:
+        tot = sum(t.numel() * t.element_size() for t in self._keep)
+        for t in (self.embed, self.final_norm, self.table, self.centroids, self.w_in, self.w_back):
+            tot += t.numel() * t.element_size()
+        return tot
+
+
+class Engine:
+    """One libspecdec context plus the caller-owned device state it works on."""
+
+    def __init__(self, model: DeviceModel, max_batch: int, max_draft: int, max_rows: int,
+                 max_ctx: int, stream=None):
+        lib = F.load()
+        if not torch.cuda.is_available():
+            raise RuntimeError("libspecdec needs a ROCm GPU; no CPU path exists")
+        s = model.shape
+        self.model = model
+        self.shape = s
+        self.lib = lib
+        cfg = F.Config()
+        for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
+                  "n_experts", "top_k", "expert_ffn", "shared_ffn", "d_layers", "d_dim", "d_ffn",
+                  "n_centroids", "kv_src_layer"):
+            setattr(cfg, n, int(getattr(s, n)))
+        cfg.dtype = ABI_DT[s.dtype]
+        cfg.rms_eps = s.rms_eps
+        cfg.rope_theta = s.rope_theta
+        cfg.max_batch, cfg.max_draft, cfg.max_rows, cfg.max_ctx = max_batch, max_draft, max_rows, max_ctx
+        self.cfg = cfg
+        self.max_batch, self.max_draft, self.max_rows, self.max_ctx = max_batch, max_draft, max_rows, max_ctx
+        ws = lib.specdec_workspace_bytes(C.byref(cfg))
+        if ws == 0:
+            raise F.SpecdecError(F.E_INVAL, "specdec_workspace_bytes (invalid configuration)")
+        dev = model.device
+        kv = lib.specdec_kv_elems(C.byref(cfg))
+        self.kv_k = torch.zeros(kv, dtype=TORCH_DT[s.dtype], device=dev)
+        self.kv_v = torch.zeros(kv, dtype=TORCH_DT[s.dtype], device=dev)
+        self.len = torch.zeros(max_batch, dtype=torch.int32, device=dev)
+        self.hid = torch.zeros(max_batch, s.d_model, dtype=torch.float32, device=dev)
+        self._ws = torch.zeros(ws + 256, dtype=torch.uint8, device=dev)
+        off = (-self._ws.data_ptr()) % 256
+        self.ws_ptr = self._ws.data_ptr() + off
+        self.ws_bytes = ws
+        self._w = model.abi()
+        ctx = C.c_void_p()
+        F.check(lib.specdec_create(C.byref(cfg), C.byref(self._w), _p(self.kv_k), _p(self.kv_v),
+                                   _p(self.len), _p(self.hid), C.c_void_p(self.ws_ptr), ws,
+                                   _s(stream), C.byref(ctx)), "specdec_create")
+        self.ctx = ctx
+
+    # --- state helpers (setup / tests) ---
+    def kv_view(self):
+        s = self.shape
+        shp = (s.n_layers, self.max_batch, s.n_kv_heads, self.max_ctx, s.head_dim)
+        return self.kv_k.view(shp), self.kv_v.view(shp)
+
+    def set_len(self, values) -> None:
+        vals = [int(v) for v in values]
+        self.len[: len(vals)].copy_(torch.tensor(vals, dtype=torch.int32))
+        self.set_len_bound(vals)
+
+    def set_len_bound(self, values) -> None:
+        arr = (C.c_int32 * len(values))(*[int(v) for v in values])
+        F.check(self.lib.specdec_set_len_bound(self.ctx, arr, len(values)), "specdec_set_len_bound")
+
+    def device_error(self, clear: bool = True, stream=None) -> int:
+        w = C.c_int32()
+        F.check(self.lib.specdec_read_device_error(self.ctx, C.byref(w), int(clear), _s(stream)),
+                "specdec_read_device_error")
+        return int(w.value)
+
+    # --- the four step calls ---
+    def verify(self, tokens, logits=None, argmax=None, stream=None) -> None:
+        B, R = tokens.shape
+        F.check(self.lib.specdec_verify(self.ctx, B, R, _p(tokens), _p(logits), _p(argmax),
+                                        _s(stream)), "specdec_verify")
+
+    def accept(self, tokens, out_tokens=None, n_emit=None, next_tok=None, commit=True,
+               stream=None) -> None:
+        B, R = tokens.shape
+        F.check(self.lib.specdec_accept(self.ctx, B, R - 1, _p(tokens), _p(out_tokens), _p(n_emit),
+                                        _p(next_tok), F.ACCEPT_COMMIT if commit else 0, _s(stream)),
+                "specdec_accept")
+
+    def kv_commit(self, n_commit, stream=None) -> None:
+        F.check(self.lib.specdec_kv_commit(self.ctx, n_commit.shape[0], _p(n_commit), _s(stream)),
+                "specdec_kv_commit")
+
+    def draft(self, cur_tok, drafts, head_mode=F.HEAD_CLUSTERED, k_c=1, inject=None,
+              stream=None) -> None:
+        B, K = drafts.shape
+        stride = 0 if inject is None else inject.shape[1]
+        F.check(self.lib.specdec_draft(self.ctx, B, K, head_mode, k_c, _p(cur_tok), _p(drafts),
+                                       _p(inject), stride, _s(stream)), "specdec_draft")
+
+    # --- measurement helpers ---
+    def profile_start(self, kernel_class: int, capacity: int) -> None:
+        F.check(self.lib.specdec_profile_start(self.ctx, kernel_class, capacity), "specdec_profile_start")
+
+    def profile_read(self, max_n: int = 100000) -> list:
+        buf = (C.c_float * max_n)()
+        n = C.c_int32()
+        F.check(self.lib.specdec_profile_read(self.ctx, buf, max_n, C.byref(n)), "specdec_profile_read")
+        return [buf[i] for i in range(n.value)]
+
+    def query_split(self, kernel_class: int):
+        s, u = C.c_int32(), C.c_int32()
+        F.check(self.lib.specdec_query_split(self.ctx, kernel_class, C.byref(s), C.byref(u)),
+                "specdec_query_split")
+        return s.value, u.value
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None):
+            self.lib.specdec_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

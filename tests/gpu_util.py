@@ -1,0 +1,105 @@
+"""Helpers for the GPU parity tests: build an engine for a workload, run prefill / greedy / the
+speculative loop through the C ABI, and compare against the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import speculative_decoding_03_amd as SD
+from speculative_decoding_03_amd import engine as E
+from workloads import device as WD
+from workloads import synth as S
+
+
+def rel_err(a: np.ndarray, ref: np.ndarray) -> float:
+    """max |a - ref| / max |ref| (per row: caller passes one row)."""
+    return float(np.max(np.abs(a.astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def build_engine(cfg, max_ctx: int, max_rows: int = 16, max_batch: int = 1, source=None,
+                 weights_override=None):
+    src = source or WD.source_for(cfg)
+    if weights_override is not None:
+        src = weights_override(src)
+    perm, cent = WD.clusters(cfg)
+    model = E.DeviceModel(E.Shape.of(cfg), src, perm, cent)
+    eng = E.Engine(model, max_batch=max_batch, max_draft=max(cfg.draft_k, 1),
+                   max_rows=max(max_rows, cfg.draft_k + 1), max_ctx=max_ctx)
+    return eng
+
+
+def gpu_prefill(eng, prompt: np.ndarray, chunk: int = 16, want_logits: bool = True):
+    """verify(chunk) + kv_commit(chunk) over the prompt; returns (first token, logits rows)."""
+    dev = eng.kv_k.device
+    V = eng.shape.vocab
+    rows = []
+    am = None
+    for s in range(0, len(prompt), chunk):
+        part = prompt[s:s + chunk]
+        toks = torch.tensor(part, dtype=torch.int32, device=dev).view(1, -1)
+        lg = torch.empty(1, len(part), V, dtype=torch.float32, device=dev) if want_logits else None
+        am = torch.empty(1, len(part), dtype=torch.int32, device=dev)
+        eng.verify(toks, logits=lg, argmax=am)
+        eng.kv_commit(torch.tensor([len(part)], dtype=torch.int32, device=dev))
+        if want_logits:
+            rows.append(lg[0].cpu().numpy())
+    eng.set_len_bound([len(prompt)])
+    return int(am[0, -1].item()), (np.concatenate(rows) if want_logits else None)
+
+
+def gpu_greedy(eng, t0: int, n: int):
+    """Plain greedy decoding through verify(1 row) + accept(K=0, commit).  Returns n tokens
+    (t0 first), including each step's logits row."""
+    dev = eng.kv_k.device
+    toks = [int(t0)]
+    cur = torch.tensor([[t0]], dtype=torch.int32, device=dev)
+    nxt = torch.empty(1, dtype=torch.int32, device=dev)
+    while len(toks) < n:
+        eng.verify(cur)
+        eng.accept(cur, next_tok=nxt, commit=True)
+        cur = nxt.view(1, 1).clone()
+        toks.append(int(nxt.item()))
+    return toks
+
+
+def gpu_spec(eng, t0: int, n: int, K: int, inject_tab=None, head_mode=SD.HEAD_CLUSTERED, k_c=1):
+    """The speculative loop through the C ABI; returns (tokens, emitted per step)."""
+    dev = eng.kv_k.device
+    toks = [int(t0)]
+    cur = torch.tensor([t0], dtype=torch.int32, device=dev)
+    drafts = torch.empty(1, K, dtype=torch.int32, device=dev)
+    out = torch.empty(1, K + 1, dtype=torch.int32, device=dev)
+    n_emit = torch.empty(1, dtype=torch.int32, device=dev)
+    nxt = torch.empty(1, dtype=torch.int32, device=dev)
+    inj = None if inject_tab is None else torch.from_numpy(inject_tab.reshape(1, -1)).to(dev)
+    emitted = []
+    length = int(eng.len[0].item())
+    while len(toks) < n:
+        eng.draft(cur, drafts, head_mode=head_mode, k_c=k_c, inject=inj)
+        T = torch.cat([cur.view(1, 1), drafts], 1).contiguous()
+        eng.verify(T)
+        eng.accept(T, out_tokens=out, n_emit=n_emit, next_tok=nxt, commit=True)
+        e = int(n_emit.item())
+        toks.extend(out[0, :e].cpu().tolist())
+        emitted.append(e)
+        length += e
+        eng.set_len_bound([length])  # the host now knows the committed length exactly
+        cur = nxt.clone()
+    return toks[:n], emitted
+
+
+def snapshot(eng):
+    return eng.len.clone(), eng.hid.clone()
+
+
+def restore(eng, snap):
+    ln, hid = snap
+    eng.len.copy_(ln)
+    eng.hid.copy_(hid)
+    eng.set_len_bound(ln.cpu().tolist())
+
+
+def oracle_model(cfg):
+    return O.as_f64(S.target_weights(cfg)), O.as_f64(S.drafter_weights(cfg))

@@ -71,3 +71,19 @@ def test_presets_parameter_counts():
     assert abs(preset("e2b").target_params() / 1e9 - 1.252) < 0.005
     t = preset("tiny")
     assert t.vocab == t.n_centroids * t.cluster_size
+
+
+def test_inject_table_agrees_with_scalar_draws():
+    from workloads import inject_table
+    g = np.arange(100, 160, dtype=np.int64)
+    g[:5] = -1
+    tab = inject_table(g, 3, 0.6, 17, b=1).reshape(-1, 3)
+    thr = inject_threshold(0.6)
+    for pos in range(len(g)):
+        for j in (1, 2, 3):
+            want = g[pos] if (g[pos] >= 0 and inject_draw(17, 1, pos, j) < thr) else -1
+            assert tab[pos, j - 1] == want
+    full = inject_table(g, 2, 1.0, 3).reshape(-1, 2)
+    assert np.array_equal(full[5:, 0], g[5:]) and np.all(full[:5] == -1)
+    wrong = inject_table(g, 2, 0.0, 3, forced_wrong=True, vocab=150).reshape(-1, 2)
+    assert np.array_equal(wrong[5:, 1], (g[5:] + 1) % 150)

@@ -1,0 +1,88 @@
+// Device-side seeded fills for synthetic workloads (weights, KV caches, hidden states).
+//
+// Same counter-based generator as workloads/synth.py: element i of the stream with key k is the
+// (i+1)-th SplitMix64 output of state k (Steele, Lea and Flood, OOPSLA 2014; Stafford's Mix13
+// finaliser).  value = float32(2*u24 - (2^24-1)) * scale, u24 = top 24 bits; bf16 tensors round
+// that fp32 value to nearest-even.  Holds no part of the decoding method.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ float value_at(uint64_t key, uint64_t idx, float scale) {
+  const uint64_t z = mix64(key + (idx + 1ull) * 0x9E3779B97F4A7C15ull);
+  const int odd = (int)((z >> 40) * 2ull) - ((1 << 24) - 1);
+  return (float)odd * scale;
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__global__ void fill_uniform(void* dst, int64_t n, int bf16, uint64_t key, int64_t start,
+                             float scale) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float v = value_at(key, (uint64_t)(start + i), scale);
+    if (bf16) reinterpret_cast<uint16_t*>(dst)[i] = to_bf16(v);
+    else reinterpret_cast<float*>(dst)[i] = v;
+  }
+}
+
+// KV cache [L][Bc][Hkv][max_ctx][hd]: positions [0, ctx) of sequences [0, Bl) get the logical
+// element (((l*Bl + b)*Hkv + g)*ctx + pos)*hd + c of the stream.
+__global__ void fill_kv(void* dst, int L, int Bl, int Bc, int Hkv, int ctx, int max_ctx, int hd,
+                        int bf16, uint64_t key, float scale) {
+  const int64_t n = (int64_t)L * Bl * Hkv * ctx * hd;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i;
+    const int c = (int)(r % hd); r /= hd;
+    const int pos = (int)(r % ctx); r /= ctx;
+    const int g = (int)(r % Hkv); r /= Hkv;
+    const int b = (int)(r % Bl); r /= Bl;
+    const int l = (int)r;
+    const int64_t o = ((((int64_t)l * Bc + b) * Hkv + g) * max_ctx + pos) * hd + c;
+    const float v = value_at(key, (uint64_t)i, scale);
+    if (bf16) reinterpret_cast<uint16_t*>(dst)[o] = to_bf16(v);
+    else reinterpret_cast<float*>(dst)[o] = v;
+  }
+}
+
+int grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (int)(b < 65536 ? (b > 0 ? b : 1) : 65536);
+}
+
+}  // namespace
+
+extern "C" {
+
+int synth_fill_uniform(void* dst, int64_t n, int bf16, uint64_t key, int64_t start, float scale,
+                       void* stream) {
+  if (!dst || n < 0) return -1;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(fill_uniform, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, dst, n,
+                     bf16, key, start, scale);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int synth_fill_kv(void* dst, int L, int Bl, int Bc, int Hkv, int ctx, int max_ctx, int hd,
+                  int bf16, uint64_t key, float scale, void* stream) {
+  if (!dst || ctx > max_ctx || Bl > Bc) return -1;
+  const int64_t n = (int64_t)L * Bl * Hkv * ctx * hd;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(fill_kv, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, dst, L, Bl,
+                     Bc, Hkv, ctx, max_ctx, hd, bf16, key, scale);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // extern "C"

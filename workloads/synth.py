@@ -34,6 +34,7 @@ __all__ = [
     "norm_weight", "target_weights", "target_layer_weights", "drafter_weights",
     "cluster_perm", "centroids_from_table", "kv_init", "kv_rows", "state_init",
     "prompt_tokens", "inject_threshold", "inject_draw", "inject_key", "hash_scale",
+    "hash_u64_at", "inject_table",
 ]
 
 MASK64 = (1 << 64) - 1
@@ -69,6 +70,13 @@ def hash_u64(key: int, start: int, n: int) -> np.ndarray:
     idx = np.arange(start + 1, start + n + 1, dtype=np.uint64)
     with np.errstate(over="ignore"):
         return mix64(np.uint64(key) + idx * _G)
+
+
+def hash_u64_at(key: int, idx: np.ndarray) -> np.ndarray:
+    """Elements at arbitrary indices of the counter stream with key ``key``."""
+    i = np.asarray(idx, dtype=np.uint64) + np.uint64(1)
+    with np.errstate(over="ignore"):
+        return mix64(np.uint64(key) + i * _G)
 
 
 def hash_scale(std: float) -> np.float32:
@@ -281,6 +289,30 @@ def inject_threshold(p: float) -> int:
     """Replacement threshold on a 53-bit uniform integer: floor(p * 2^53), clamped to [0, 2^53]."""
     p = min(max(float(p), 0.0), 1.0)
     return int(math.floor(p * float(1 << 53)))
+
+
+def inject_table(greedy_seq: np.ndarray, K: int, p: float, seed: int, b: int = 0,
+                 forced_wrong: bool = False, vocab: int = 0, n_pos: int | None = None) -> np.ndarray:
+    """Replacement table for one sequence: entry pos*K + (j-1) is the token that replaces draft
+    slot j when it proposes absolute position pos, or -1.  greedy_seq[pos] is the target's own
+    greedy token at pos (-1 where unknown).  forced_wrong puts (greedy+1) mod V in every slot."""
+    n_pos = len(greedy_seq) if n_pos is None else n_pos
+    tab = np.full((n_pos, K), -1, dtype=np.int32)
+    g = np.full(n_pos, -1, dtype=np.int64)
+    g[: min(n_pos, len(greedy_seq))] = greedy_seq[:n_pos]
+    known = g >= 0
+    if forced_wrong:
+        for j in range(1, K + 1):
+            tab[known, j - 1] = (g[known] + 1) % vocab
+        return tab.reshape(-1)
+    thr = inject_threshold(p)
+    pos = np.arange(n_pos, dtype=np.int64)
+    key = inject_key(seed, b)
+    for j in range(1, K + 1):
+        u = hash_u64_at(key, pos * 64 + j) >> np.uint64(11)
+        hit = (u < np.uint64(thr)) & known if thr < (1 << 53) else known.copy()
+        tab[hit, j - 1] = g[hit]
+    return tab.reshape(-1)
 
 
 def inject_draw(seed: int, b: int, pos: int, j: int) -> int:

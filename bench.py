@@ -1,0 +1,317 @@
+"""Benchmark of the draft-verify-accept step of greedy speculative decoding on one MI355X.
+
+One step = draft K tokens (MTP drafter, clustered head) + verify K+1 rows + fused accept/commit,
+on seeded synthetic inputs: random-init bf16 weights of the named shapes, a synthetic committed
+KV cache of `ctx` positions, and drafts replaced by the target's own greedy token with
+probability p (the acceptance mix of the workload).  Inputs are resident in HBM before timing.
+
+Prints one JSON line.  Default workload: the 31B-class dense configuration (64 layers, d 5120,
+40/8 heads of 128, FFN 25600, vocab 262144; drafter 4 layers x 256 with 2048 centroids; ctx
+8192, K=3, batch 1, p=0.7).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "accepted tokens/s at B=1 (K=3); verify-step ms vs 1-token decode ms; HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_TEXT = {
+    "31b": "31B-class dense: 64 layers, d 5120, 40 q / 8 kv heads of 128, gated FFN 25600, vocab 262144, bf16 random-init (30.5B params, tied head); drafter 4 layers x 256 over the 5120-d backbone state, 2048 centroids x 128 tokens; ctx 8192, K=3, batch 1, drafts injected at p=0.7",
+    "e2b": "E2B-shaped: 24 layers, d 1536, 8 q / 1 kv heads of 256, gated FFN 6144, vocab 262144, bf16; drafter 4 x 256, 2048 centroids x 128; ctx 2048, K=3, batch 1, p=0.7",
+    "e4b": "E4B-shaped: 34 layers, d 2560, 8 q / 2 kv heads of 256, gated FFN 10240, vocab 262144, bf16; drafter 4 x 256, 2048 centroids; ctx 4096, K=4, batch 1, p=0.7",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, rows: int, keys: float) -> float:
+    """Bytes a verify (rows = K+1) or decode (rows = 1) step must move: all target weights once,
+    the KV of the visible keys per layer, the new rows' KV writes, the embedding rows."""
+    w = cfg.target_params() * 2
+    kv_read = cfg.n_layers * 2 * cfg.n_kv_heads * keys * cfg.head_dim * 2
+    kv_write = cfg.n_layers * 2 * cfg.n_kv_heads * rows * cfg.head_dim * 2
+    return w + kv_read + kv_write + rows * cfg.d_model * 2
+
+
+def draft_substep_bytes(cfg, keys: float, k_c: int = 1) -> float:
+    D, d, qd = cfg.d_dim, cfg.d_model, cfg.q_dim
+    per = D * qd * 2 + 3 * D * cfg.d_ffn
+    w = (D * (d + D) + cfg.d_layers * per + d * D + cfg.n_centroids * D) * 2
+    table = k_c * cfg.cluster_size * D * 2 + D * 2
+    kv = cfg.d_layers * 2 * cfg.n_kv_heads * keys * cfg.head_dim * 2
+    return w + table + kv
+
+
+def gate_up_bytes(cfg, M: int) -> float:
+    """Algorithmic bytes of one gate/up GEMM launch: the 2F x d bf16 weights once, the fp32
+    residual rows in, the bf16 gated product out."""
+    return 2 * cfg.ffn_dim * cfg.d_model * 2 + M * cfg.d_model * 4 + M * cfg.ffn_dim * 2
+
+
+def src_sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(name: str, launch_bytes: float):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{name}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        cur = src_sha(os.path.join(ROOT, "speculative_decoding_03_amd", "csrc", "gemm.hip"))
+        if d.get("kernel_src_sha") != cur:
+            return None
+        return float(d["hbm_bytes_per_dispatch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(cfg, tokens_per_step: float, K: int) -> dict:
+    """The oracle timed on the host's cores on a bounded sample of the same workload: one decoder
+    layer at full width over the K+1 verify rows with the full synthetic KV, the tied LM head over
+    a vocabulary slice, and one drafter sub-step with the clustered head; scaled to the full
+    verify step (x n_layers, x vocab/slice) plus K drafter sub-steps."""
+    import numpy as np
+
+    import oracle as O
+    from workloads import synth as S
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    t_gen = time.perf_counter()
+    lw = O.as_f64(S.target_layer_weights(cfg, 0))
+    ctx = cfg.ctx
+    cap = ctx + K + 2
+    Kl = np.zeros((cfg.n_kv_heads, cap, cfg.head_dim))
+    Vl = np.zeros_like(Kl)
+    for g in range(cfg.n_kv_heads):
+        Kl[g, :ctx] = S.kv_rows(cfg, "k", 0, 0, g, 0, ctx)
+        Vl[g, :ctx] = S.kv_rows(cfg, "v", 0, 0, g, 0, ctx)
+    slice_rows = 8192
+    E_slice = S.gen_rows(cfg, "embed", 0, cfg.d_model, 0, slice_rows).astype(np.float64)
+    hid, t0 = S.state_init(cfg)
+    x0 = hid[0].astype(np.float64)
+    gen_s = time.perf_counter() - t_gen
+
+    t = time.perf_counter()
+    x = x0
+    for i in range(K + 1):
+        x = O.decoder_layer_row(lw, cfg, Kl, Vl, x0, ctx + i)
+    t_layer = time.perf_counter() - t
+    t = time.perf_counter()
+    for i in range(K + 1):
+        _ = E_slice @ O.rmsnorm(x, np.ones(cfg.d_model), cfg.rms_eps)
+    t_head = (time.perf_counter() - t) * (cfg.vocab / slice_rows)
+    del lw
+    # drafter sub-step (all drafter layers attend the same synthetic layer: reuse Kl / Vl)
+    DW = O.as_f64(S.drafter_weights(cfg))
+
+    cache = O.KVCache([None] * cfg.n_layers, [None] * cfg.n_layers)
+    cache.K[cfg.src_layer] = Kl
+    cache.V[cfg.src_layer] = Vl
+    t = time.perf_counter()
+    O.drafter_substep(DW, cfg, cache, x0, int(t0[0]), ctx, ctx, "clustered", 1)
+    t_draft = time.perf_counter() - t
+    step_s = cfg.n_layers * t_layer + t_head + K * t_draft
+    return {
+        "value": round(tokens_per_step / step_s, 4),
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle on {int(cores)} threads: 1 of {cfg.n_layers} decoder layers "
+                   f"(full width, {ctx}-position KV) over the {K + 1} verify rows ({t_layer:.2f} s), "
+                   f"LM head on {slice_rows} of {cfg.vocab} vocab rows, 1 drafter sub-step "
+                   f"({t_draft:.2f} s); extrapolated to one full step = {step_s:.1f} s at "
+                   f"{tokens_per_step:.2f} tokens/step (input generation {gen_s:.1f} s not timed)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="31b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--head", default="clustered", choices=["clustered", "full"])
+    ap.add_argument("--k-c", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-profile", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the path is built and measured on a single MI355X "
+              f"(--gpus {args.gpus} was requested). Multi-GPU sharding is a design note, not built.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_03_amd as SD
+    from speculative_decoding_03_amd import engine as E
+    from workloads import device as WD
+    from workloads import inject_table, preset
+
+    cfg = preset(args.config)
+    if args.p is not None:
+        cfg = cfg.replace(p_inject=args.p)
+    K, W, N = cfg.draft_k, args.warmup, args.steps
+    head_mode = SD.HEAD_FULL if args.head == "full" else SD.HEAD_CLUSTERED
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    t_setup = time.perf_counter()
+    n_greedy = (W + N) * (K + 1) + K + 2
+    max_ctx = cfg.ctx + n_greedy + 64
+    log(f"setup {cfg.name}: weights on device ({cfg.target_params() / 1e9:.2f}B target params)")
+    perm, cent = WD.clusters(cfg)
+    model = E.DeviceModel(E.Shape.of(cfg), WD.DeviceSource(cfg), perm, cent)
+    eng = E.Engine(model, max_batch=1, max_draft=K, max_rows=max(16, K + 1), max_ctx=max_ctx)
+    WD.fill_kv(eng, cfg)
+    t0 = WD.start_state(eng, cfg)
+    hid0 = eng.hid.clone()
+    torch.cuda.synchronize()
+    log(f"setup done in {time.perf_counter() - t_setup:.1f} s")
+
+    def restore():
+        eng.hid.copy_(hid0)
+        eng.set_len([cfg.ctx])
+
+    # ---- plain greedy decoding (1-row verify + fused accept/commit): decode-step timing ----
+    cur = t0.view(1, 1).clone()
+    gbuf = torch.empty(n_greedy, dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_greedy + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n_greedy):
+        eng.verify(cur)
+        eng.accept(cur, out_tokens=gbuf[i:i + 1], next_tok=cur, commit=True)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    dec_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(W, n_greedy)]
+    greedy = [int(t0.item())] + gbuf.cpu().tolist()
+    assert eng.device_error() == 0, "device error during greedy decoding"
+    log(f"greedy: {n_greedy} decode steps, median {np.median(dec_ms):.3f} ms")
+
+    # ---- speculative loop ----
+    restore()
+    gseq = np.full(max_ctx, -1, dtype=np.int64)
+    gseq[cfg.ctx:cfg.ctx + len(greedy)] = greedy
+    tab = torch.from_numpy(inject_table(gseq, K, cfg.p_inject, cfg.inject_seed).reshape(1, -1)).to(dev)
+    T = torch.empty(1, K + 1, dtype=torch.int32, device=dev)
+    T[0, 0] = int(t0.item())
+    drafts = T[:, 1:]
+    outs = torch.full((W + N, K + 1), -1, dtype=torch.int32, device=dev)
+    n_emit = torch.zeros(W + N, dtype=torch.int32, device=dev)
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(W + N)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(W + N)]
+    e2 = [torch.cuda.Event(enable_timing=True) for _ in range(W + N)]
+
+    def step(i):
+        e0[i].record()
+        eng.draft(T[:, 0], drafts, head_mode=head_mode, k_c=args.k_c, inject=tab)
+        e1[i].record()
+        eng.verify(T)
+        eng.accept(T, out_tokens=outs[i:i + 1], n_emit=n_emit[i:i + 1], next_tok=T[:, 0], commit=True)
+        e2[i].record()
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    prof = not args.no_kernel_profile
+    if prof:
+        eng.profile_start(SD.ffi.PROF_GATE_UP, cfg.n_layers * N)
+    t_start = time.perf_counter()
+    for i in range(W, W + N):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gate_ms = eng.profile_read() if prof else []
+    assert eng.device_error() == 0, "device error during the speculative loop"
+
+    ne = n_emit.cpu().tolist()
+    ot = outs.cpu().tolist()
+    spec = [int(greedy[0])]
+    for i in range(W + N):
+        spec.extend(ot[i][: ne[i]])
+    same = spec[: len(spec)] == greedy[: len(spec)]
+    emitted = sum(ne[W:])
+    accepted = emitted - N
+    tok_s = emitted / wall
+    draft_ms = [e0[i].elapsed_time(e1[i]) for i in range(W, W + N)]
+    ver_ms = [e1[i].elapsed_time(e2[i]) for i in range(W, W + N)]
+    med = lambda v: float(np.median(v))  # noqa: E731
+    keys = cfg.ctx + (W + N) * 2.5 / 2 + K + 1
+    v_bytes = algorithmic_bytes(cfg, K + 1, keys)
+    d_bytes = algorithmic_bytes(cfg, 1, keys - K)
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": N,
+        "warmup": W,
+        "ms_per_step": round(1e3 * wall / N, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "batch": 1, "K": K, "ctx": cfg.ctx,
+                   "p_inject": cfg.p_inject, "head": f"{args.head} k_c={args.k_c}"},
+        "verify_ms": round(med(ver_ms), 4),
+        "decode_ms": round(med(dec_ms), 4),
+        "verify_over_decode": round(med(ver_ms) / med(dec_ms), 4),
+        "draft_ms": round(med(draft_ms), 4),
+        "verify_hbm_gbs": round(v_bytes / (med(ver_ms) * 1e-3) / 1e9, 1),
+        "decode_hbm_gbs": round(d_bytes / (med(dec_ms) * 1e-3) / 1e9, 1),
+        "verify_hbm_frac": round(v_bytes / (med(ver_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tokens_per_step": round(emitted / N, 4),
+        "accepted_over_proposed": round(accepted / (N * K), 4),
+        "spec_equals_greedy": bool(same),
+        "draft_substep_mb": round(draft_substep_bytes(cfg, keys) / 1e6, 2),
+    }
+    if gate_ms:
+        launch_ms = float(np.mean(gate_ms))
+        lb = gate_up_bytes(cfg, K + 1)
+        achieved = lb / (launch_ms * 1e-3) / 1e9
+        traffic = load_traffic(f"gemm_gate_up_{args.config}", lb)
+        res["roofline"] = {
+            "kernel": "gemm_kernel<bf16,MT=1,NU=2,XM_NORM,EPI_SILU> (FFN gate/up, verify M=4)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": lb,
+            "avg_launch_us": round(launch_ms * 1e3, 2),
+            "launches": len(gate_ms),
+        }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host cores, bounded sample)")
+        res["cpu_baseline"] = cpu_baseline(cfg, emitted / N, K)
+    eng.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -306,7 +306,7 @@ def head_clustered(table: np.ndarray, centroids: np.ndarray, perm: np.ndarray, s
 
 
 def drafter_substep(DW: dict, cfg, cache: KVCache, h: np.ndarray, c_prev: int, qpos: int,
-                    length: int, head_mode: str = "clustered", k_c: int = 1):
+                    length: int, head_mode: str = "clustered", k_c: int = 1, trace=None):
     """One drafter sub-step: returns (draft token, next hidden input).
 
     Readings: input x = W_in [rms(h)*n_h ; rms(table[c_prev])*n_e]; each drafter layer is
@@ -328,6 +328,8 @@ def drafter_substep(DW: dict, cfg, cache: KVCache, h: np.ndarray, c_prev: int, q
         b = rmsnorm(x, lw["n2"], cfg.rms_eps)
         x = x + dense_ffn(lw["wg"], lw["wu"], lw["wd"], b)
     s = rmsnorm(x, DW["norm_f"], cfg.rms_eps)
+    if trace is not None:
+        trace.append(s)
     if head_mode == "full":
         d = head_full(DW["table"], s)
     else:
@@ -336,14 +338,14 @@ def drafter_substep(DW: dict, cfg, cache: KVCache, h: np.ndarray, c_prev: int, q
 
 
 def draft(DW: dict, cfg, cache: KVCache, hid: np.ndarray, c0: int, length: int, K: int,
-          head_mode: str = "clustered", k_c: int = 1) -> list:
+          head_mode: str = "clustered", k_c: int = 1, trace=None) -> list:
     """Draft K tokens (O7).  Sub-step j (1..K) reads the token c_{j-1} at position length+j-1
     (c_0 is the current token, not yet in the cache) and proposes the token at length+j."""
     h = hid
     c = int(c0)
     out = []
     for j in range(1, K + 1):
-        c, h = drafter_substep(DW, cfg, cache, h, c, length + j - 1, length, head_mode, k_c)
+        c, h = drafter_substep(DW, cfg, cache, h, c, length + j - 1, length, head_mode, k_c, trace)
         out.append(c)
     return out
 

@@ -179,7 +179,7 @@ def main() -> int:
 
     t_setup = time.perf_counter()
     n_greedy = (W + N) * (K + 1) + K + 2
-    max_ctx = cfg.ctx + n_greedy + 64
+    max_ctx = (cfg.ctx + n_greedy + 64 + 7) // 8 * 8
     log(f"setup {cfg.name}: weights on device ({cfg.target_params() / 1e9:.2f}B target params)")
     perm, cent = WD.clusters(cfg)
     model = E.DeviceModel(E.Shape.of(cfg), WD.DeviceSource(cfg), perm, cent)

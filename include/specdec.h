@@ -129,7 +129,9 @@ typedef struct specdec_ctx specdec_ctx; /* host memory; owns no device memory */
 size_t specdec_workspace_bytes(const specdec_config* cfg);
 
 /* Elements of the KV cache per tensor (K or V): n_layers*max_batch*n_kv_heads*max_ctx*head_dim.
-   Element (l, b, g, pos, c) sits at (((l*max_batch + b)*n_kv_heads + g)*max_ctx + pos)*head_dim + c. */
+   K element (l, b, g, pos, c) sits at (((l*max_batch + b)*n_kv_heads + g)*max_ctx + pos)*head_dim + c;
+   V is stored transposed per head: (((l*max_batch + b)*n_kv_heads + g)*head_dim + c)*max_ctx + pos,
+   so that both attention operands stream along their reduction axis. */
 size_t specdec_kv_elems(const specdec_config* cfg);
 
 /* Creates a context over caller-owned device memory:
@@ -141,8 +143,9 @@ size_t specdec_kv_elems(const specdec_config* cfg);
    Enqueues one small kernel on `stream` that zeroes the workspace's arrival counters and the
    device error word.  Errors: SPECDEC_E_INVAL (null pointers, shapes not multiples of the
    tile: d_model, Hq*hd, ffn_dim, d_dim, d_ffn % 32; head_dim % 16, head_dim <= 256;
-   vocab % 64; vocab / n_centroids % 64; max_batch*max_rows <= 64; max_rows <= 64),
-   SPECDEC_E_UNSUPPORTED (n_experts > 0). */
+   vocab % 64; vocab / n_centroids % 64; n_centroids % 16; max_batch*max_rows <= 64;
+   max_rows <= 64; max_ctx % 8), SPECDEC_E_UNSUPPORTED (n_experts > 0, head_dim not one of
+   64, 128, 176, 256). */
 int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv_k, void* kv_v,
                    int32_t* len, float* hid, void* workspace, size_t workspace_bytes,
                    void* stream, specdec_ctx** out);

@@ -2,12 +2,14 @@
 // the new rows, full over the committed prefix) and for the drafter's cross-attention into the
 // target's cache (keys [0, len), no cache of its own).
 //
-// Grid: (chunk, kv head, sequence).  A workgroup loads one chunk of `chunk` keys of one KV head
-// once and serves every query vector that reads that head: all rows x all query heads of the
-// group.  Per chunk it writes the running max, the sum of exponentials and the unnormalised
-// value sum; the last chunk to arrive combines them in chunk order.  Chunk boundaries sit at
-// fixed absolute positions and every reduction has a fixed order, so a row's output does not
-// depend on how many other rows are in the call.
+// Grid: (chunk, kv head, sequence).  A workgroup of 4 waves loads one chunk of CH keys of one
+// KV head once and serves every query vector that reads that head (all rows x all query heads
+// of the group, 16 per MFMA tile).  Scores S = Q K^T and the value sum P V both run on the
+// 16x16x32 bf16 MFMA (fp32 storage: 16x16x4 fp32).  K is stored [pos][hd] and V transposed
+// [hd][pos], so both operands stream as 16-byte loads along their reduction axis.  Per chunk the
+// kernel leaves (row max, sum of exponentials, unnormalised value sum); attn_combine merges the
+// chunks in chunk order.  Chunk boundaries sit at fixed absolute positions and every reduction
+// has a fixed order, so a row's output does not depend on how many other rows are in the call.
 
 #include <math.h>
 
@@ -18,39 +20,28 @@ namespace specdec {
 
 namespace {
 
-constexpr int RB = 16;                 // query vectors per pass
-constexpr int LDS_F = RB * 256;        // floats per LDS buffer
-constexpr int COMB_LDS = LDS_F;        // (query vector, chunk) pairs per combine pass
+constexpr int NWAVE = 4;
 
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
-  if constexpr (sizeof(T) == 2) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  } else {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
+template <int HD> struct AttnShape {
+  static constexpr int CH = HD <= 128 ? 256 : 128;          // keys per chunk
+  static constexpr int DS = (HD + 31) / 32;                 // 32-wide head-dim steps (scores)
+  static constexpr int KB = CH / 16 / NWAVE;                // 16-key blocks per wave (scores)
+  static constexpr int DB = (HD / 16 + NWAVE - 1) / NWAVE;  // 16-wide head-dim blocks per wave
+  static constexpr int KS = CH / 32;                        // 32-key steps (values)
+};
 
-template <typename T>
+template <typename T, int HD, int QT>
 __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
-  const int chunk = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wid = t >> 6;
+  using SH = AttnShape<HD>;
+  constexpr int CH = SH::CH;
+  __shared__ T pbuf[QT * 16 * CH];
+  __shared__ float wred[NWAVE][QT * 16];
+  __shared__ float mrow[QT * 16], lrow[QT * 16];
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
   const int Rall = a.R * G;
-  const int CH = a.chunk;
-  const int hd = a.hd;
   const int len = a.len[b];
   const int end_max = len + a.R - 1 + a.key_off;  // keys [0, end_max) are read by some row
   if (end_max > a.max_ctx || len < 0) {
@@ -58,212 +49,251 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     return;
   }
   const int n_act = (end_max + CH - 1) / CH;
+  if (chunk >= n_act) return;
+  const int key0 = chunk * CH;
+  const T* Kc = reinterpret_cast<const T*>(a.kcache) + (size_t)b * a.cache_b_stride +
+                (size_t)g * a.max_ctx * HD;
+  const T* Vt = reinterpret_cast<const T*>(a.vcache) + (size_t)b * a.cache_b_stride +
+                (size_t)g * HD * a.max_ctx;
+  float* pbase = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * (HD + 2);
+
+  for (int q0 = 0; q0 < Rall; q0 += 16 * QT) {
+    // ---- scores ----
+    f32x4 s[QT][SH::KB];
+    {
+      Frag<T> kf[SH::KB][SH::DS];
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+#pragma unroll
+        for (int ds = 0; ds < SH::DS; ++ds) {
+          const int key = key0 + (w + kb * NWAVE) * 16 + c16;
+          const int d = ds * 32 + grp * 8;
+          if (key < end_max && d < HD) load_frag<T>(kf[kb][ds], Kc + (size_t)key * HD + d);
+          else zero_frag(kf[kb][ds]);
+        }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        Frag<T> qf[SH::DS];
+        const int qv = q0 + qt * 16 + c16;
+        const int row = qv / G;
+        const int h = g * G + (qv - row * G);
+        const float* qp = a.q + (((size_t)b * a.R + row) * a.hq + h) * HD;
+#pragma unroll
+        for (int ds = 0; ds < SH::DS; ++ds) {
+          const int d = ds * 32 + grp * 8;
+          if (qv < Rall && d < HD) {
+            const float4 x0 = *reinterpret_cast<const float4*>(qp + d);
+            const float4 x1 = *reinterpret_cast<const float4*>(qp + d + 4);
+            const float y[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            to_frag<T>(qf[ds], y);
+          } else {
+            zero_frag(qf[ds]);
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < SH::KB; ++kb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ds = 0; ds < SH::DS; ++ds) acc = mma<T>(qf[ds], kf[kb][ds], acc);
+          s[qt][kb] = acc;
+        }
+      }
+    }
+    // ---- value operand, loaded now so it streams in under the softmax ----
+    Frag<T> vf[SH::DB][SH::KS];
+#pragma unroll
+    for (int dbi = 0; dbi < SH::DB; ++dbi)
+#pragma unroll
+      for (int ks = 0; ks < SH::KS; ++ks) {
+        const int db = w + dbi * NWAVE;
+        const int kk = key0 + ks * 32 + grp * 8;
+        const T* p = Vt + (size_t)(db * 16 + c16) * a.max_ctx + kk;
+        if (db >= HD / 16 || kk >= end_max) {
+          zero_frag(vf[dbi][ks]);
+        } else if (kk + 8 <= end_max) {
+          load_frag<T>(vf[dbi][ks], p);
+        } else {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = (kk + e < end_max) ? Elem<T>::load(p + e) : 0.f;
+          to_frag<T>(vf[dbi][ks], y);
+        }
+      }
+    // ---- softmax statistics of the chunk (fixed order: lanes, then waves) ----
+    float M[QT][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int qv = q0 + qt * 16 + grp * 4 + v;
+        const int kend = len + qv / G + a.key_off;
+        float m = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < SH::KB; ++kb) {
+          const int key = key0 + (w + kb * NWAVE) * 16 + c16;
+          const float val = (qv < Rall && key < kend) ? s[qt][kb][v] * a.scale : -INFINITY;
+          s[qt][kb][v] = val;
+          m = fmaxf(m, val);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
+        if (c16 == 0) wred[w][qt * 16 + grp * 4 + v] = m;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = qt * 16 + grp * 4 + v;
+        M[qt][v] = fmaxf(fmaxf(wred[0][r], wred[1][r]), fmaxf(wred[2][r], wred[3][r]));
+      }
+    __syncthreads();
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float sum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < SH::KB; ++kb) {
+          const float val = s[qt][kb][v];
+          const float p = (val == -INFINITY) ? 0.f : expf(val - M[qt][v]);
+          const int kl = (w + kb * NWAVE) * 16 + c16;
+          Elem<T>::store(&pbuf[(qt * 16 + grp * 4 + v) * CH + kl], p);
+          sum += p;
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, WAVE);
+        if (c16 == 0) wred[w][qt * 16 + grp * 4 + v] = sum;
+      }
+    __syncthreads();
+    if (w == 0 && c16 == 0) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = qt * 16 + grp * 4 + v;
+          mrow[r] = M[qt][v];
+          lrow[r] = ((wred[0][r] + wred[1][r]) + wred[2][r]) + wred[3][r];
+        }
+    }
+    // ---- values: O[qv][d] = sum_key P[qv][key] V[key][d] ----
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int dbi = 0; dbi < SH::DB; ++dbi) {
+        const int db = w + dbi * NWAVE;
+        if (db >= HD / 16) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < SH::KS; ++ks) {
+          Frag<T> pf;
+          load_frag<T>(pf, &pbuf[(qt * 16 + c16) * CH + ks * 32 + grp * 8]);
+          acc = mma<T>(pf, vf[dbi][ks], acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int qv = q0 + qt * 16 + grp * 4 + v;
+          if (qv < Rall) pbase[(size_t)qv * (HD + 2) + db * 16 + c16] = acc[v];
+        }
+      }
+    }
+    __syncthreads();
+    if (t < QT * 16 && q0 + t < Rall) {
+      pbase[(size_t)(q0 + t) * (HD + 2) + HD] = mrow[t];
+      pbase[(size_t)(q0 + t) * (HD + 2) + HD + 1] = lrow[t];
+    }
+    __syncthreads();
+  }
+}
+
+// Combines the chunk partials of one query vector in chunk order:
+// o = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c,  M = max_c m_c.
+template <typename T>
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a) {
+  __shared__ float wts[4096];
+  __shared__ float ls[4096];
+  __shared__ float Linv;
+  const int qv = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int t = threadIdx.x;
+  const int G = a.hq / a.hkv;
+  const int Rall = a.R * G;
+  const int hd = a.hd;
+  const int len = a.len[b];
+  const int end_max = len + a.R - 1 + a.key_off;
+  if (end_max > a.max_ctx || len < 0) return;
+  const int n_act = (end_max + a.chunk - 1) / a.chunk;
+  const int row = qv / G, h = g * G + (qv - row * G);
+  T* out = reinterpret_cast<T*>(a.out) + ((size_t)b * a.R + row) * (a.hq * hd) + h * hd;
   if (n_act == 0) {
     // no visible key (drafter before any context): the attention output is defined as zero
-    if (chunk == 0) {
-      for (int idx = t; idx < Rall * hd; idx += 256) {
-        const int qv = idx / hd, d = idx - (idx / hd) * hd;
-        const int row = qv / G, h = g * G + (qv - (qv / G) * G);
-        Elem<T>::store(reinterpret_cast<T*>(a.out) + ((size_t)b * a.R + row) * (a.hq * hd) + h * hd + d, 0.f);
-      }
-    }
+    for (int d = t; d < hd; d += blockDim.x) Elem<T>::store(out + d, 0.f);
     return;
   }
-  if (chunk >= n_act) return;
-
-  __shared__ float qs[LDS_F];   // query block; combine: l_c
-  __shared__ float sc[LDS_F];   // scores / probabilities; value-part reduction; combine: weights
-  __shared__ float ms[RB], ls[RB];
-  __shared__ float lsum[RB];
-  __shared__ int last_flag;
-  float* ored = sc;
-
-  const T* Kc = reinterpret_cast<const T*>(a.kcache) + (size_t)b * a.cache_b_stride +
-                (size_t)g * a.max_ctx * hd;
-  const T* Vc = reinterpret_cast<const T*>(a.vcache) + (size_t)b * a.cache_b_stride +
-                (size_t)g * a.max_ctx * hd;
-  const int TPK = 256 / CH;      // threads per key in the score phase
-  const int kk = t / TPK;        // key within chunk
-  const int part = t - kk * TPK;
-  const int dpt = hd / TPK;      // dims per thread (multiple of 8)
-  const int j = chunk * CH + kk; // absolute key position
-  const int KP = hd <= 256 ? max(1, 256 / hd) : 1;  // key parts in the value phase
-  const int dv = t % hd;
-  const int kp = t / hd;
-  const int keys_per_kp = CH / KP;
-  float* part_base = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * (hd + 2);
-
-  for (int r0 = 0; r0 < Rall; r0 += RB) {
-    const int nr = min(RB, Rall - r0);
-    // stage the block's query vectors
-    for (int idx = t; idx < nr * hd; idx += 256) {
-      const int r = idx / hd, d = idx - (idx / hd) * hd;
-      const int qv = r0 + r;
-      const int row = qv / G, h = g * G + (qv - (qv / G) * G);
-      qs[r * hd + d] = a.q[(((size_t)b * a.R + row) * a.hq + h) * hd + d];
-    }
-    __syncthreads();
-    // scores
-    float s[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) s[r] = 0.f;
-    if (j < end_max) {
-      const T* kp_ = Kc + (size_t)j * hd + part * dpt;
-      for (int d0 = 0; d0 < dpt; d0 += 8) {
-        float kv[8];
-        load8<T>(kp_ + d0, kv);
-        const int dd = part * dpt + d0;
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          if (r < nr) {
-            const float4 qa = *reinterpret_cast<const float4*>(&qs[r * hd + dd]);
-            const float4 qb = *reinterpret_cast<const float4*>(&qs[r * hd + dd + 4]);
-            float acc = s[r];
-            acc = fmaf(qa.x, kv[0], acc); acc = fmaf(qa.y, kv[1], acc);
-            acc = fmaf(qa.z, kv[2], acc); acc = fmaf(qa.w, kv[3], acc);
-            acc = fmaf(qb.x, kv[4], acc); acc = fmaf(qb.y, kv[5], acc);
-            acc = fmaf(qb.z, kv[6], acc); acc = fmaf(qb.w, kv[7], acc);
-            s[r] = acc;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      for (int o = 1; o < TPK; o <<= 1) s[r] += __shfl_xor(s[r], o, WAVE);
-    }
-    if (part == 0) {
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (r < nr) {
-          const int row = (r0 + r) / G;
-          const int kend = len + row + a.key_off;
-          sc[r * CH + kk] = (j < kend) ? s[r] * a.scale : -INFINITY;
-        }
-      }
-    }
-    __syncthreads();
-    // softmax statistics per query vector (one wave per vector, fixed lane order)
-    for (int r = wid; r < nr; r += 4) {
-      float mx = -INFINITY;
-      for (int k = lane; k < CH; k += WAVE) mx = fmaxf(mx, sc[r * CH + k]);
-      mx = wave_max(mx);
-      float sum = 0.f;
-      for (int k = lane; k < CH; k += WAVE) {
-        const float v = sc[r * CH + k];
-        const float p = (mx == -INFINITY) ? 0.f : expf(v - mx);
-        sc[r * CH + k] = p;
-        sum += p;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) { ms[r] = mx; ls[r] = sum; }
-    }
-    __syncthreads();
-    // value accumulation
-    float o[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) o[r] = 0.f;
-    if (kp < KP && t < KP * hd) {
-      const int k0 = kp * keys_per_kp;
-      const int kmax = min(k0 + keys_per_kp, end_max - chunk * CH);
-      for (int k = k0; k < kmax; ++k) {
-        const float v = Elem<T>::load(Vc + (size_t)(chunk * CH + k) * hd + dv);
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-          if (r < nr) o[r] = fmaf(sc[r * CH + k], v, o[r]);
-      }
-    }
-    if (KP > 1) {
-      __syncthreads();
-      if (kp < KP && t < KP * hd) {
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-          if (r < nr) ored[(kp * RB + r) * hd + dv] = o[r];
-      }
-      __syncthreads();
-      if (t < hd) {
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          if (r < nr) {
-            float acc = ored[r * hd + t];
-            for (int p = 1; p < KP; ++p) acc += ored[(p * RB + r) * hd + t];
-            o[r] = acc;
-          }
-        }
-      }
-    }
-    if (t < hd) {
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-        if (r < nr) part_base[(size_t)(r0 + r) * (hd + 2) + t] = o[r];
-    }
-    if (t < nr) {
-      part_base[(size_t)(r0 + t) * (hd + 2) + hd] = ms[t];
-      part_base[(size_t)(r0 + t) * (hd + 2) + hd + 1] = ls[t];
-    }
-    __syncthreads();
+  const size_t cstride = (size_t)Rall * (hd + 2);
+  const float* pbase = a.part + ((size_t)b * a.hkv + g) * a.n_chunks * cstride + (size_t)qv * (hd + 2);
+  for (int c = t; c < n_act; c += blockDim.x) {
+    wts[c] = pbase[c * cstride + hd];
+    ls[c] = pbase[c * cstride + hd + 1];
   }
-
-  // last chunk to arrive combines
-  fence_device();
   __syncthreads();
   if (t == 0) {
-    const int old = atomic_inc_device(a.cnt + b * a.hkv + g);
-    last_flag = (old == n_act - 1);
+    float M = -INFINITY;
+    for (int c = 0; c < n_act; ++c) M = fmaxf(M, wts[c]);
+    float L = 0.f;
+    for (int c = 0; c < n_act; ++c) {
+      const float e = (wts[c] == -INFINITY) ? 0.f : expf(wts[c] - M);
+      wts[c] = e;
+      L += ls[c] * e;
+    }
+    Linv = 1.0f / L;
   }
   __syncthreads();
-  if (!last_flag) return;
-  fence_device();
-  float* w = sc;  // reuse: weights [qv][chunk]
-  const float* pbase = a.part + ((size_t)b * a.hkv + g) * a.n_chunks * (size_t)Rall * (hd + 2);
-  const size_t cstride = (size_t)Rall * (hd + 2);
-  const int QB = max(1, min(min(Rall, RB), COMB_LDS / n_act));
-  for (int q0 = 0; q0 < Rall; q0 += QB) {
-    const int nq = min(QB, Rall - q0);
-    for (int idx = t; idx < nq * n_act; idx += 256) {
-      const int qi = idx / n_act, c = idx - (idx / n_act) * n_act;
-      const float* p = pbase + c * cstride + (size_t)(q0 + qi) * (hd + 2) + hd;
-      w[qi * n_act + c] = __builtin_nontemporal_load(p);   // m_c
-      qs[qi * n_act + c] = __builtin_nontemporal_load(p + 1);  // l_c
-    }
-    __syncthreads();
-    if (t < nq) {
-      float M = -INFINITY;
-      for (int c = 0; c < n_act; ++c) M = fmaxf(M, w[t * n_act + c]);
-      float L = 0.f;
-      for (int c = 0; c < n_act; ++c) {
-        const float mc = w[t * n_act + c];
-        const float e = (mc == -INFINITY) ? 0.f : expf(mc - M);
-        w[t * n_act + c] = e;
-        L += qs[t * n_act + c] * e;
-      }
-      lsum[t] = L;
-    }
-    __syncthreads();
-    for (int idx = t; idx < nq * hd; idx += 256) {
-      const int qi = idx / hd, d = idx - (idx / hd) * hd;
-      float acc = 0.f;
-      for (int c = 0; c < n_act; ++c)
-        acc += w[qi * n_act + c] * __builtin_nontemporal_load(pbase + c * cstride + (size_t)(q0 + qi) * (hd + 2) + d);
-      const float val = acc / lsum[qi];
-      const int qv = q0 + qi;
-      const int row = qv / G, h = g * G + (qv - (qv / G) * G);
-      Elem<T>::store(reinterpret_cast<T*>(a.out) + ((size_t)b * a.R + row) * (a.hq * hd) + h * hd + d, val);
-    }
-    __syncthreads();
+  const float inv = Linv;
+  for (int d = t; d < hd; d += blockDim.x) {
+    float acc = 0.f;
+    for (int c = 0; c < n_act; ++c) acc += wts[c] * pbase[c * cstride + d];
+    Elem<T>::store(out + d, acc * inv);
   }
-  if (t == 0) atomic_store_zero(a.cnt + b * a.hkv + g);
+}
+
+template <typename T, int HD>
+hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
+  if (a.chunk != AttnShape<HD>::CH) return hipErrorInvalidValue;
+  dim3 grid(a.n_chunks, a.hkv, a.B), block(256);
+  const int Rall = a.R * (a.hq / a.hkv);
+  if (Rall <= 16)
+    hipLaunchKernelGGL((attn_kernel<T, HD, 1>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, HD, 2>), grid, block, 0, st, a);
+  dim3 cgrid(Rall, a.hkv, a.B), cblock(a.hd <= 128 ? 128 : 256);
+  hipLaunchKernelGGL(attn_combine_kernel<T>, cgrid, cblock, 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
+  switch (a.hd) {
+    case 64: return launch_hd<T, 64>(a, st);
+    case 128: return launch_hd<T, 128>(a, st);
+    case 176: return launch_hd<T, 176>(a, st);
+    case 256: return launch_hd<T, 256>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
+int attention_chunk(int head_dim) { return head_dim <= 128 ? 256 : 128; }
+
+bool attention_supported(int head_dim) {
+  return head_dim == 64 || head_dim == 128 || head_dim == 176 || head_dim == 256;
+}
+
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.n_chunks, a.hkv, a.B), block(256);
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(attn_kernel<bf16_t>, grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_kernel<float>, grid, block, 0, st, a);
-  return hipGetLastError();
+  if (a.n_chunks > 4096) return hipErrorInvalidValue;
+  return dtype == DT_BF16 ? launch_t<bf16_t>(a, st) : launch_t<float>(a, st);
 }
 
 }  // namespace specdec

@@ -79,6 +79,72 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// One lane's share of a 16x32 MFMA operand tile: 8 consecutive reduction elements of one row.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+  u32x4 v;
+};
+template <> struct Frag<float> {
+  u32x4 v[2];
+};
+
+template <typename T>
+__device__ __forceinline__ void zero_frag(Frag<T>& f) {
+  if constexpr (sizeof(T) == 2) {
+    f.v = u32x4{0, 0, 0, 0};
+  } else {
+    f.v[0] = u32x4{0, 0, 0, 0};
+    f.v[1] = u32x4{0, 0, 0, 0};
+  }
+}
+
+// 8 fp32 values -> fragment of the storage type (bf16: round to nearest even).
+template <typename T>
+__device__ __forceinline__ void to_frag(Frag<T>& f, const float (&y)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16(y[2 * i]) | ((uint32_t)f32_to_bf16(y[2 * i + 1]) << 16);
+    f.v = u32x4{w[0], w[1], w[2], w[3]};
+  } else {
+    f.v[0] = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                   __float_as_uint(y[3])};
+    f.v[1] = u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
+                   __float_as_uint(y[7])};
+  }
+}
+
+// 16-byte (bf16) / 32-byte (fp32) fragment load of 8 consecutive elements.
+template <typename T>
+__device__ __forceinline__ void load_frag(Frag<T>& f, const T* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  if constexpr (sizeof(T) == 2) {
+    f.v = *q;
+  } else {
+    f.v[0] = q[0];
+    f.v[1] = q[1];
+  }
+}
+
+// acc += A (16 rows x 32, lanes as Frag) . B^T (16 cols x 32): C[i][j], lane l holds rows
+// (l/16)*4 + 0..3 of column l%16.
+template <typename T>
+__device__ __forceinline__ f32x4 mma(const Frag<T>& a, const Frag<T>& b, f32x4 acc) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                   __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v[h][e]),
+                                                   __uint_as_float(b.v[h][e]), acc, 0, 0, 0);
+    return acc;
+  }
+}
+
 // Error word bits raised by kernels (sticky until cleared by the host).
 enum : int { ERRBIT_CAPACITY = 1, ERRBIT_NAN = 2, ERRBIT_TOKEN = 4 };
 

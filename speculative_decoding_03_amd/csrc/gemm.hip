@@ -4,15 +4,18 @@
 // 1 KB tiles (bf16) with one 16-byte load per lane, so every weight byte is read from HBM
 // exactly once per call and every wave load is fully contiguous.  The rows of X are padded to
 // the 16-row MFMA tile; v_mfma_f32_16x16x32_bf16 (fp32: eight v_mfma_f32_16x16x4f32) does the
-// contraction.  The reduction axis is split S ways where S depends only on (N, Kd), and the
-// last split to arrive at a unit sums all partials in split order, so every output element is
-// produced by the same instruction sequence whatever M is: a verify row is bit-identical to the
-// same row computed alone in a decode step.
+// contraction.
+//
+// Work split: a workgroup of NW waves owns UPW units (a unit = NU consecutive 16-row tiles, or a
+// listed tile); the reduction axis of each unit is split over KW = NW / UPW waves, and the KW
+// partial accumulators are summed through LDS in wave order.  KW depends only on (N, Kd), so a
+// verify row and the same row in a decode step go through the same instruction sequence and
+// come out bit-identical.  There is no communication between workgroups.
 //
 // Prologue: X is either a storage-typed activation or the fp32 residual stream normalised on
-// load (x * rowscale * normweight, the RMSNorm of the layer).  Epilogues: store / residual add
-// with the next RMSNorm's row scale, rotary embedding + KV-cache append, SiLU-gated product,
-// and per-unit argmax partials for the LM head.
+// load (x * rowscale * normweight: the layer's RMSNorm); the row scale is formed from per-tile
+// sums of squares left by the producer of x.  Epilogues: store / residual add (leaving those
+// sums of squares), rotary embedding + KV-cache append, SiLU-gated product, per-unit argmax.
 
 #include <math.h>
 
@@ -22,15 +25,6 @@
 namespace specdec {
 
 namespace {
-
-template <typename T> struct Frag;
-
-template <> struct Frag<bf16_t> {
-  u32x4 v;
-};
-template <> struct Frag<float> {
-  u32x4 v[2];
-};
 
 template <typename T>
 __device__ __forceinline__ void load_w(Frag<T>& f, const T* W, size_t tile, int nkb, int kb,
@@ -42,16 +36,6 @@ __device__ __forceinline__ void load_w(Frag<T>& f, const T* W, size_t tile, int 
   } else {
     f.v[0] = __builtin_nontemporal_load(p);
     f.v[1] = __builtin_nontemporal_load(p + 1);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void zero_frag(Frag<T>& f) {
-  if constexpr (sizeof(T) == 2) {
-    f.v = u32x4{0, 0, 0, 0};
-  } else {
-    f.v[0] = u32x4{0, 0, 0, 0};
-    f.v[1] = u32x4{0, 0, 0, 0};
   }
 }
 
@@ -78,36 +62,9 @@ __device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int m, flo
                                                        (size_t)m * a.ldx + k);
     const float4* pw = reinterpret_cast<const float4*>(a.xnorm + k);
     float4 x0 = px[0], x1 = px[1], w0 = pw[0], w1 = pw[1];
-    float y[8] = {x0.x * rs * w0.x, x0.y * rs * w0.y, x0.z * rs * w0.z, x0.w * rs * w0.w,
-                  x1.x * rs * w1.x, x1.y * rs * w1.y, x1.z * rs * w1.z, x1.w * rs * w1.w};
-    if constexpr (sizeof(T) == 2) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)f32_to_bf16(y[2 * i]) | ((uint32_t)f32_to_bf16(y[2 * i + 1]) << 16);
-      f.v = u32x4{w[0], w[1], w[2], w[3]};
-    } else {
-      f.v[0] = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
-                     __float_as_uint(y[3])};
-      f.v[1] = u32x4{__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
-                     __float_as_uint(y[7])};
-    }
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ f32x4 mma(const Frag<T>& x, const Frag<T>& w, f32x4 acc) {
-  if constexpr (sizeof(T) == 2) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.v),
-                                                   __builtin_bit_cast(bf16x8, w.v), acc, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.v[h][e]),
-                                                   __uint_as_float(w.v[h][e]), acc, 0, 0, 0);
-    return acc;
+    const float y[8] = {x0.x * rs * w0.x, x0.y * rs * w0.y, x0.z * rs * w0.z, x0.w * rs * w0.w,
+                        x1.x * rs * w1.x, x1.y * rs * w1.y, x1.z * rs * w1.z, x1.w * rs * w1.w};
+    to_frag<T>(f, y);
   }
 }
 
@@ -128,16 +85,6 @@ __device__ __forceinline__ void argmax16(float& v, int& i) {
   }
 }
 
-// Row-scale of the next RMSNorm, computed by the last unit to finish (one wave).
-__device__ void finish_row_scale(const GemmArgs& a, int lane) {
-  for (int m = 0; m < a.M; ++m) {
-    float s = 0.f;
-    for (int t = lane; t < a.n_tiles; t += WAVE) s += a.ssq[(size_t)t * a.M + m];
-    s = wave_sum(s);
-    if (lane == 0) a.scale_out[m] = 1.0f / sqrtf(s / (float)a.scale_n + a.eps);
-  }
-}
-
 template <typename T, int MT, int NU, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
                                          int tile0, int lane) {
@@ -146,40 +93,24 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
   if constexpr (EPI == EPI_STORE) {
     const int tile = tile0;
     const int col = tile * TILE_N + c16;
-    float sq[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = mt * 16 + rgrp + v;
-        sq[mt][v] = 0.f;
+        float sq = 0.f;
         if (m < a.M) {
           float* o = a.out + (size_t)m * a.ldo + col;
           float y = acc[0][mt][v];
           if (a.accumulate) y = *o + y;
           *o = y;
-          sq[mt][v] = y * y;
+          sq = y * y;
         }
-      }
-    if (a.ssq) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = mt * 16 + rgrp + v;
-          const float r = sum16(sq[mt][v]);
+        if (a.ssq) {
+          const float r = sum16(sq);
           if (c16 == 0 && m < a.M) a.ssq[(size_t)tile * a.M + m] = r;
         }
-      fence_device();
-      int old = 0;
-      if (lane == 0) old = atomic_inc_device(a.gcnt);
-      old = __shfl(old, 0, WAVE);
-      if (old == a.n_units - 1) {
-        fence_device();
-        finish_row_scale(a, lane);
-        if (lane == 0) atomic_store_zero(a.gcnt);
       }
-    }
   } else if constexpr (EPI == EPI_ROPE) {
     const int col = tile0 * TILE_N + c16;
     const int hh = col / a.hd;
@@ -214,12 +145,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           } else if (pos >= a.max_ctx || pos < 0) {
             raise_error(a.err, ERRBIT_CAPACITY);
           } else {
+            // K is stored [pos][hd], V transposed [hd][pos]
             const bool isk = hh < a.hq + a.hkv;
             const int g = isk ? hh - a.hq : hh - a.hq - a.hkv;
-            T* cache = reinterpret_cast<T*>(isk ? a.kcache : a.vcache);
-            Elem<T>::store(cache + (size_t)b * a.cache_b_stride +
-                               ((size_t)g * a.max_ctx + pos) * a.hd + dim,
-                           y);
+            T* cache = reinterpret_cast<T*>(isk ? a.kcache : a.vcache) + (size_t)b * a.cache_b_stride;
+            const size_t off = isk ? ((size_t)g * a.max_ctx + pos) * a.hd + dim
+                                   : ((size_t)g * a.hd + dim) * a.max_ctx + pos;
+            Elem<T>::store(cache + off, y);
           }
         }
       }
@@ -271,28 +203,49 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
   }
 }
 
-template <typename T, int MT, int NU, int XM, int EPI>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
+// U: k-blocks in flight per wave per step of the main loop.
+template <int NU, int MT> struct Unroll {
+  static constexpr int base = NU >= 2 ? 4 : 8;
+  static constexpr int U = base / MT > 1 ? base / MT : 1;
+};
+
+template <typename T, int MT, int NU, int XM, int EPI, int NW>
+__global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
+  __shared__ f32x4 red[NW * NU * 64];
+  __shared__ float rscale[64];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x >> 6;
-  const int split = blockIdx.x % a.S;
-  const int u = (blockIdx.x / a.S) * 4 + wid;
+  const int KW = a.KW;
+  const int ks = wid % KW;
+  const int u = blockIdx.x * (NW / KW) + wid / KW;
   const int n_units = a.n_units_dev ? min(*a.n_units_dev, a.n_units) : a.n_units;
-  if (u >= n_units) return;
-  const int tile0 = a.unit_tile ? a.unit_tile[u] : u * NU;
-  const int kb0 = split * a.kb_per_split;
+  const bool active = u < n_units;
+  const int tile0 = active ? (a.unit_tile ? a.unit_tile[u] : u * NU) : 0;
+  const int kb0 = ks * a.kb_per_split;
   const int kb1 = min(a.nkb, kb0 + a.kb_per_split);
   const T* W = reinterpret_cast<const T*>(a.W);
 
+  if constexpr (XM == XM_NORM) {
+    // row scale 1/sqrt(mean(x^2) + eps) from the producer's per-tile sums of squares
+    if (wid == 0) {
+      for (int m = 0; m < a.M; ++m) {
+        float s = 0.f;
+        for (int t = lane; t < a.n_ssq; t += WAVE) s += a.xssq[(size_t)t * a.M + m];
+        s = wave_sum(s);
+        if (lane == 0) rscale[m] = 1.0f / sqrtf(s / (float)a.scale_n + a.eps);
+      }
+    }
+    __syncthreads();
+  }
   float rs[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + (lane & 15);
-    rs[mt] = (XM == XM_NORM && m < a.M) ? a.xscale[m] : 0.f;
+    rs[mt] = (XM == XM_NORM && m < a.M) ? rscale[m] : 0.f;
   }
   bool tvalid[NU];
 #pragma unroll
-  for (int t = 0; t < NU; ++t) tvalid[t] = (tile0 + t) < a.n_tiles;
+  for (int t = 0; t < NU; ++t) tvalid[t] = active && (tile0 + t) < a.n_tiles;
 
   f32x4 acc[NU][MT];
 #pragma unroll
@@ -300,107 +253,104 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int U = (sizeof(T) == 2) ? 8 : 4;
-  int kb = kb0;
-  for (; kb + U <= kb1; kb += U) {
-    Frag<T> w[U][NU];
-    Frag<T> x[U][MT];
+  if (active) {
+    constexpr int U = Unroll<NU, MT>::U;
+    int kb = kb0;
+    for (; kb + U <= kb1; kb += U) {
+      Frag<T> w[U][NU];
+      Frag<T> x[U][MT];
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu)
+      for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+        for (int t = 0; t < NU; ++t) {
+          if (tvalid[t]) load_w<T>(w[uu][t], W, (size_t)(tile0 + t), a.nkb, kb + uu, lane);
+          else zero_frag(w[uu][t]);
+        }
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          load_x<T, XM>(x[uu][mt], a, mt * 16 + (lane & 15), rs[mt], kb + uu, lane);
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+        for (int t = 0; t < NU; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[uu][mt], w[uu][t], acc[t][mt]);
+    }
+    for (; kb < kb1; ++kb) {
+      Frag<T> w[NU];
+      Frag<T> x[MT];
 #pragma unroll
       for (int t = 0; t < NU; ++t) {
-        if (tvalid[t]) load_w<T>(w[uu][t], W, (size_t)(tile0 + t), a.nkb, kb + uu, lane);
-        else zero_frag(w[uu][t]);
+        if (tvalid[t]) load_w<T>(w[t], W, (size_t)(tile0 + t), a.nkb, kb, lane);
+        else zero_frag(w[t]);
       }
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        load_x<T, XM>(x[uu][mt], a, mt * 16 + (lane & 15), rs[mt], kb + uu, lane);
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu)
+      for (int mt = 0; mt < MT; ++mt) load_x<T, XM>(x[mt], a, mt * 16 + (lane & 15), rs[mt], kb, lane);
 #pragma unroll
       for (int t = 0; t < NU; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[uu][mt], w[uu][t], acc[t][mt]);
-  }
-  for (; kb < kb1; ++kb) {
-    Frag<T> w[NU];
-    Frag<T> x[MT];
-#pragma unroll
-    for (int t = 0; t < NU; ++t) {
-      if (tvalid[t]) load_w<T>(w[t], W, (size_t)(tile0 + t), a.nkb, kb, lane);
-      else zero_frag(w[t]);
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[mt], w[t], acc[t][mt]);
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) load_x<T, XM>(x[mt], a, mt * 16 + (lane & 15), rs[mt], kb, lane);
-#pragma unroll
-    for (int t = 0; t < NU; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[mt], w[t], acc[t][mt]);
   }
 
-  if (a.S > 1) {
-    const int rgrp = (lane >> 4) << 2;
-    const size_t stride_s = (size_t)a.n_units * NU * a.M * TILE_N;
+  if (KW > 1) {
+    // sum the KW partial accumulators of each unit in wave order, one M-tile at a time
 #pragma unroll
-    for (int t = 0; t < NU; ++t)
+    for (int mt = 0; mt < MT; ++mt) {
+      if (ks != 0) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int t = 0; t < NU; ++t) red[(wid * NU + t) * 64 + lane] = acc[t][mt];
+      }
+      __syncthreads();
+      if (ks == 0) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = mt * 16 + rgrp + v;
-          if (m < a.M)
-            a.part[split * stride_s + (((size_t)u * NU + t) * a.M + m) * TILE_N + (lane & 15)] =
-                acc[t][mt][v];
+        for (int t = 0; t < NU; ++t) {
+          f32x4 s = acc[t][mt];
+          for (int k2 = 1; k2 < KW; ++k2) s += red[((wid + k2) * NU + t) * 64 + lane];
+          acc[t][mt] = s;
         }
-    fence_device();
-    int old = 0;
-    if (lane == 0) old = atomic_inc_device(a.cnt + u);
-    old = __shfl(old, 0, WAVE);
-    if (old != a.S - 1) return;
-    fence_device();
-#pragma unroll
-    for (int t = 0; t < NU; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = mt * 16 + rgrp + v;
-          float s = 0.f;
-          if (m < a.M) {
-            const float* p = a.part + (((size_t)u * NU + t) * a.M + m) * TILE_N + (lane & 15);
-            for (int sp = 0; sp < a.S; ++sp) s += __builtin_nontemporal_load(p + sp * stride_s);
-          }
-          acc[t][mt][v] = s;
-        }
-    if (lane == 0) atomic_store_zero(a.cnt + u);
+      }
+      __syncthreads();
+    }
+    if (ks != 0) return;
   }
+  if (!active) return;
   epilogue<T, MT, NU, EPI>(a, acc, u, tile0, lane);
 }
 
-template <typename T, int MT, int NU, int XM, int EPI>
+template <typename T, int MT, int NU, int XM, int EPI, int NW>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
-  const int groups = (a.n_units + 3) / 4;
-  dim3 grid(groups * a.S), block(256);
-  hipLaunchKernelGGL((gemm_kernel<T, MT, NU, XM, EPI>), grid, block, 0, st, a);
+  const int upw = NW / a.KW;
+  dim3 grid((a.n_units + upw - 1) / upw), block(NW * 64);
+  hipLaunchKernelGGL((gemm_kernel<T, MT, NU, XM, EPI, NW>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T, int MT, int NU, int XM, int EPI>
+hipError_t launch_nw(const GemmArgs& a, hipStream_t st) {
+  if constexpr (NU < 4) {
+    if (a.NW == 16) return launch_t<T, MT, NU, XM, EPI, 16>(a, st);
+  }
+  if (a.NW == 8) return launch_t<T, MT, NU, XM, EPI, 8>(a, st);
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int MT>
 hipError_t dispatch_epi(int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
   if (epi == EPI_STORE && NU == 1)
-    return xmode == XM_NORM ? launch_t<T, MT, 1, XM_NORM, EPI_STORE>(a, st)
-                            : launch_t<T, MT, 1, XM_ELEM, EPI_STORE>(a, st);
+    return xmode == XM_NORM ? launch_nw<T, MT, 1, XM_NORM, EPI_STORE>(a, st)
+                            : launch_nw<T, MT, 1, XM_ELEM, EPI_STORE>(a, st);
   if (epi == EPI_ROPE && NU == 1)
-    return xmode == XM_NORM ? launch_t<T, MT, 1, XM_NORM, EPI_ROPE>(a, st)
-                            : launch_t<T, MT, 1, XM_ELEM, EPI_ROPE>(a, st);
+    return xmode == XM_NORM ? launch_nw<T, MT, 1, XM_NORM, EPI_ROPE>(a, st)
+                            : launch_nw<T, MT, 1, XM_ELEM, EPI_ROPE>(a, st);
   if (epi == EPI_SILU && NU == 2)
-    return xmode == XM_NORM ? launch_t<T, MT, 2, XM_NORM, EPI_SILU>(a, st)
-                            : launch_t<T, MT, 2, XM_ELEM, EPI_SILU>(a, st);
+    return xmode == XM_NORM ? launch_nw<T, MT, 2, XM_NORM, EPI_SILU>(a, st)
+                            : launch_nw<T, MT, 2, XM_ELEM, EPI_SILU>(a, st);
   if (epi == EPI_ARGMAX && NU == 4)
-    return xmode == XM_NORM ? launch_t<T, MT, 4, XM_NORM, EPI_ARGMAX>(a, st)
-                            : launch_t<T, MT, 4, XM_ELEM, EPI_ARGMAX>(a, st);
+    return xmode == XM_NORM ? launch_nw<T, MT, 4, XM_NORM, EPI_ARGMAX>(a, st)
+                            : launch_nw<T, MT, 4, XM_ELEM, EPI_ARGMAX>(a, st);
   return hipErrorInvalidValue;
 }
 
@@ -419,6 +369,7 @@ hipError_t dispatch_mt(int MT, int NU, int xmode, int epi, const GemmArgs& a, hi
 hipError_t launch_gemm(int dtype, int MT, int NU, int xmode, int epi, const GemmArgs& a,
                        hipStream_t st) {
   if (a.n_units <= 0) return hipSuccess;
+  if (a.KW < 1 || (a.NW != 8 && a.NW != 16) || a.NW % a.KW) return hipErrorInvalidValue;
   return dtype == DT_BF16 ? dispatch_mt<bf16_t>(MT, NU, xmode, epi, a, st)
                           : dispatch_mt<float>(MT, NU, xmode, epi, a, st);
 }

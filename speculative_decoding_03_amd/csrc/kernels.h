@@ -12,7 +12,8 @@ enum Epi { EPI_STORE = 0, EPI_ROPE = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
 
 // One skinny GEMM  Y[M][N] = X[M][Kd] . W[N][Kd]^T  over packed tiles, with a fused
 // X prologue and output epilogue.  Work unit = NU consecutive 16-row tiles (or a tile
-// listed in unit_tile); K is split S ways, S fixed by (N, Kd) only.
+// listed in unit_tile).  A workgroup of NW waves holds NW/KW units; each unit's reduction is
+// split over KW waves and summed through LDS.  KW is fixed by (N, Kd) only.
 struct GemmArgs {
   // weights
   const void* W = nullptr;
@@ -22,26 +23,23 @@ struct GemmArgs {
   const int* unit_tile = nullptr;  // optional first tile of unit u
   const int* unit_row = nullptr;   // optional: argmax keeps only this row of unit u
   const int* n_units_dev = nullptr;  // optional device count of valid units
-  int S = 1, kb_per_split = 0;
+  int KW = 1, NW = 8, kb_per_split = 0;
   int M = 0;
-  // X operand: XM_ELEM -> storage-typed [M][ldx]; XM_NORM -> fp32 [M][ldx] * xscale[m] * xnorm[k]
+  // X operand: XM_ELEM -> storage-typed [M][ldx]; XM_NORM -> fp32 [M][ldx] * rowscale[m] *
+  // xnorm[k] with rowscale = 1/sqrt(sum_t xssq[t][m] / scale_n + eps) over n_ssq tiles
   const void* X = nullptr;
   int ldx = 0;
-  const float* xscale = nullptr;
+  const float* xssq = nullptr;
+  int n_ssq = 0;
   const float* xnorm = nullptr;
-  // split-K scratch
-  float* part = nullptr;
-  int* cnt = nullptr;   // per-unit arrival counters (zero between launches)
-  int* gcnt = nullptr;  // whole-GEMM arrival counter (row-scale epilogue)
+  int scale_n = 0;
+  float eps = 0.f;
   int* err = nullptr;
-  // EPI_STORE: out[m][col] (=|+=) y; optional row scale 1/sqrt(sum(out^2)/scale_n + eps)
+  // EPI_STORE: out[m][col] (=|+=) y; optional per-tile sums of squares of the result
   float* out = nullptr;
   int ldo = 0;
   int accumulate = 0;
-  float* ssq = nullptr;        // [n_tiles][M] partial sums of squares
-  float* scale_out = nullptr;  // [M]
-  int scale_n = 0;
-  float eps = 0.f;
+  float* ssq = nullptr;        // [n_tiles][M]
   // EPI_ROPE: columns are heads of hd with rotary pairs interleaved; heads [0,hq) -> qout,
   // [hq, hq+hkv) -> kcache, [hq+hkv, hq+2hkv) -> vcache at position len[b] + row + pos_off.
   float* qout = nullptr;
@@ -69,9 +67,11 @@ struct GemmArgs {
 hipError_t launch_gemm(int dtype, int MT, int NU, int xmode, int epi, const GemmArgs& a,
                        hipStream_t st);
 
-// Grouped-query attention of `rows_per_seq` query rows per sequence over one layer's cache.
-// Row i of sequence b sees keys [0, len[b] + i + key_off).  Chunks of CH keys are reduced in
-// fixed absolute positions and combined (log-sum-exp) by the last chunk to finish.
+// Grouped-query attention of R query rows per sequence over one layer's cache: K [pos][hd],
+// V transposed [hd][pos].
+// Row i of sequence b sees keys [0, len[b] + i + key_off).  Chunks of CH keys at fixed absolute
+// positions leave (max, sum of exponentials, value sum) partials that a second kernel combines
+// in chunk order.
 struct AttnArgs {
   const float* q = nullptr;  // [B*R][hq][hd]
   const void* kcache = nullptr;
@@ -79,7 +79,6 @@ struct AttnArgs {
   const int* len = nullptr;
   void* out = nullptr;  // storage-typed [B*R][hq*hd]
   float* part = nullptr;
-  int* cnt = nullptr;
   int* err = nullptr;
   int B = 0, R = 0, key_off = 0;
   int hq = 0, hkv = 0, hd = 0;
@@ -91,11 +90,12 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+int attention_chunk(int head_dim);          // keys per chunk (fixed per head size)
+bool attention_supported(int head_dim);     // head sizes the attention kernel is built for
 
 // Misc kernels (misc.hip).
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
-                        float* x, float* ssq_unused, float* scale, float eps, int vocab, int* err,
-                        hipStream_t st);
+                        float* x, float* ssq, int vocab, int* err, hipStream_t st);
 hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
                          int B, int R, const int* tokens, int* out_tokens, int* n_emit,
                          int* next_tok, int commit, int* len, float* hid, const float* X, int d,
@@ -107,7 +107,7 @@ hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const v
                               const float* norm_e, int d, int Dd, float eps, void* u, int B,
                               int* err, hipStream_t st);
 hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int tiles_per_cluster,
-                                 int units_per_cluster, int* unit_tile, int* unit_row,
+                                 int units_per_cluster, int* unit_tile, int* unit_row, int* err,
                                  hipStream_t st);
 hipError_t launch_draft_finalize(const float* amax_val, const int* amax_idx, int ld_amax,
                                  int parts_per_seq, int seq_offset, int B, int K, int j,

@@ -37,26 +37,30 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* rv, int* r
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_combine(v, i, rv[w], ri[w]);
 }
 
-// x[m] = E[tokens[m]] (fp32 residual), scale[m] = 1/sqrt(mean(x^2) + eps).
+// x[m] = E[tokens[m]] (fp32 residual) and the per-16-column sums of squares of x[m], the input
+// of the first layer's RMSNorm row scale.
 template <typename T>
 __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, const int* tokens,
-                                                    float* x, float* scale, float eps, int vocab,
+                                                    int M, float* x, float* ssq, int vocab,
                                                     int* err) {
-  __shared__ float red[4];
+  extern __shared__ float sq[];
   const int m = blockIdx.x;
   int tok = tokens[m];
   if (tok < 0 || tok >= vocab) {
     if (threadIdx.x == 0) raise_error(err, ERRBIT_TOKEN);
     tok = 0;
   }
-  float ss = 0.f;
   for (int k = threadIdx.x; k < d; k += blockDim.x) {
     const float v = Elem<T>::load(E + packed_offset(tok, k, nkb));
     x[(size_t)m * d + k] = v;
-    ss += v * v;
+    sq[k] = v * v;
   }
-  ss = block_sum(ss, red);
-  if (threadIdx.x == 0) scale[m] = 1.0f / sqrtf(ss / (float)d + eps);
+  __syncthreads();
+  for (int t = threadIdx.x; t < d / TILE_N; t += blockDim.x) {
+    float s = 0.f;
+    for (int c = 0; c < TILE_N; ++c) s += sq[t * TILE_N + c];
+    ssq[(size_t)t * M + m] = s;
+  }
 }
 
 // Per sequence: G[i] = argmax of row i over the LM-head partials; m = longest prefix with
@@ -163,7 +167,8 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
 // argmax units: selected cluster r of sequence b owns units (b*k_c + r)*upc .. +upc-1.
 __global__ void __launch_bounds__(256) cluster_select_kernel(const float* z, int Nc, int k_c,
                                                              int tiles_per_cluster, int upc,
-                                                             int* unit_tile, int* unit_row) {
+                                                             int* unit_tile, int* unit_row,
+                                                             int* err) {
   __shared__ float rv[4];
   __shared__ int ri[4];
   const int b = blockIdx.x;
@@ -174,6 +179,10 @@ __global__ void __launch_bounds__(256) cluster_select_kernel(const float* z, int
     int idx = 0x7fffffff;
     for (int c = threadIdx.x; c < Nc; c += blockDim.x) argmax_combine(v, idx, zb[c], c);
     block_argmax(v, idx, rv, ri);
+    if (idx < 0 || idx >= Nc) {  // only when every score is NaN
+      if (threadIdx.x == 0) raise_error(err, ERRBIT_NAN);
+      idx = 0;
+    }
     if (threadIdx.x < upc) {
       const int u = b * upc + threadIdx.x;
       unit_tile[u] = idx * tiles_per_cluster + threadIdx.x * tiles_per_unit;
@@ -263,15 +272,15 @@ __global__ void fill_i32_kernel(int* p, int v, size_t n) {
 }  // namespace
 
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
-                        float* x, float*, float* scale, float eps, int vocab, int* err,
-                        hipStream_t st) {
+                        float* x, float* ssq, int vocab, int* err, hipStream_t st) {
   if (M <= 0) return hipSuccess;
+  const size_t lds = (size_t)d * sizeof(float);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st,
-                       (const bf16_t*)E, nkb, d, tokens, x, scale, eps, vocab, err);
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), lds, st,
+                       (const bf16_t*)E, nkb, d, tokens, M, x, ssq, vocab, err);
   else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, nkb, d,
-                       tokens, x, scale, eps, vocab, err);
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), lds, st, (const float*)E, nkb, d,
+                       tokens, M, x, ssq, vocab, err);
   return hipGetLastError();
 }
 
@@ -307,10 +316,10 @@ hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const v
 }
 
 hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int tiles_per_cluster,
-                                 int units_per_cluster, int* unit_tile, int* unit_row,
+                                 int units_per_cluster, int* unit_tile, int* unit_row, int* err,
                                  hipStream_t st) {
   hipLaunchKernelGGL(cluster_select_kernel, dim3(B), dim3(256), 0, st, z, Nc, k_c,
-                     tiles_per_cluster, units_per_cluster, unit_tile, unit_row);
+                     tiles_per_cluster, units_per_cluster, unit_tile, unit_row, err);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
-// C-ABI layer of libspecdec: validation, workspace carving, split-K policy and the launch
-// sequences of draft / verify / accept / commit.  All device memory belongs to the caller.
+// C-ABI layer of libspecdec: validation, workspace carving, the per-shape work split of every
+// projection, and the launch sequences of draft / verify / accept / commit.  All device memory
+// belongs to the caller; nothing here allocates, frees or synchronises on the step path.
 
 #include "../../include/specdec.h"
 
@@ -7,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -18,17 +20,28 @@ using namespace specdec;
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr int TARGET_TASKS = 8192;  // wave-tasks per GEMM launch to fill 256 CUs
-constexpr int MIN_KB_PER_TASK = 8;  // 8 KB of bf16 weights per tile per task at least
+constexpr int TARGET_WAVES = 8192;  // waves per projection launch: 32 per CU on 256 CUs
+constexpr int MIN_KB_PER_WAVE = 4;  // at least 4 KB of bf16 weights per tile per wave
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// One projection: packed weights plus its fixed split-K decomposition.
+int pow2_floor(int v) {
+  int p = 1;
+  while (p * 2 <= v) p *= 2;
+  return p;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s ? atoi(s) : dflt;
+}
+
+// One projection: packed weights plus its fixed work split (a function of N and Kd only).
 struct Gemm {
   const void* W = nullptr;
-  int N = 0, Kd = 0, nkb = 0, n_tiles = 0, NU = 1, n_units = 0, S = 1, kbps = 0;
+  int N = 0, Kd = 0, nkb = 0, n_tiles = 0, NU = 1, n_units = 0, KW = 1, NW = 8, kbps = 0;
 };
 
 Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
@@ -40,23 +53,21 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   g.n_tiles = N / 16;
   g.NU = NU;
   g.n_units = cdiv(g.n_tiles, NU);
-  int S = 1;
+  const int kw_cap = NU >= 4 ? 8 : 16;
+  int KW = 1;
   if (allow_split) {
-    S = std::max(1, cdiv(TARGET_TASKS, g.n_units));
-    S = std::min(S, std::max(1, g.nkb / MIN_KB_PER_TASK));
+    KW = std::min({kw_cap, std::max(1, g.nkb / MIN_KB_PER_WAVE), cdiv(TARGET_WAVES, g.n_units)});
+    KW = pow2_floor(std::max(1, std::min(KW, env_int("SPECDEC_MAX_KW", 16))));
   }
-  g.kbps = cdiv(g.nkb, S);
-  g.S = cdiv(g.nkb, g.kbps);
+  g.KW = KW;
+  g.NW = KW == 16 ? 16 : 8;
+  g.kbps = cdiv(g.nkb, KW);
   return g;
 }
 
-size_t gemm_part_floats(const Gemm& g, int M) {
-  return g.S > 1 ? (size_t)g.S * g.n_units * g.NU * M * 16 : 0;
-}
-
 struct Layout {
-  size_t x, scale, q, o, h, ssq, part, cnt, gcnt, amax_v, amax_i, att_part, att_cnt, err;
-  size_t u, xd, scale_d, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
+  size_t x, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err;
+  size_t u, xd, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
   size_t total;
 };
 
@@ -75,19 +86,13 @@ struct specdec_ctx {
   void* kv_v = nullptr;
   int* len = nullptr;
   float* hid = nullptr;
-  // weights
-  const void* embed = nullptr;
-  const float* final_norm = nullptr;
   std::vector<const void*> lw, dw;
   specdec_weights w{};
-  // GEMMs
   std::vector<Gemm> g_qkv, g_o, g_gu, g_down;
   Gemm g_head, g_in, g_back, g_cent, g_table, g_clu;
   std::vector<Gemm> g_dq, g_do, g_dgu, g_ddown;
-  // host-side bound on len
-  std::vector<int> len_hi;
+  std::vector<int> len_hi;  // host-side upper bound on len
   int last_B = 0, last_R = 0;
-  // profiling
   int prof_class = -1, prof_cap = 0, prof_n = 0;
   std::vector<hipEvent_t> prof_ev;
 };
@@ -109,21 +114,11 @@ bool valid_config(const specdec_config* c) {
   if (c->max_batch < 1 || c->max_rows < 1 || c->max_rows > 64) return false;
   if (c->max_batch * c->max_rows > 64) return false;
   if (c->max_draft < 1 || c->max_draft + 1 > c->max_rows) return false;
-  if (c->max_ctx < c->max_rows + 1) return false;
+  if (c->max_ctx < c->max_rows + 1 || c->max_ctx > (1 << 20) || c->max_ctx % 8) return false;
+  if (c->max_ctx / attention_chunk(c->head_dim) > 4096) return false;
   if (c->kv_src_layer >= c->n_layers) return false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return false;
   return true;
-}
-
-int attn_chunk(const specdec_config* c) {
-  // Fixed by the configuration (never by the number of rows), so chunk boundaries are the same
-  // for a verify row and a decode row.  Aim for a few hundred workgroups per layer.
-  int ch = 256;
-  const long long keys = (long long)c->max_ctx * c->n_kv_heads * c->max_batch;
-  while (ch > 64 && keys / ch < 256) ch >>= 1;
-  // score phase: head_dim must split into 8-element pieces across 256/ch threads per key
-  while (ch < 256 && (c->head_dim % (8 * (256 / ch)))) ch <<= 1;
-  return ch;
 }
 
 Dims make_dims(const specdec_config* c) {
@@ -131,14 +126,14 @@ Dims make_dims(const specdec_config* c) {
   d.Bx = c->max_batch;
   d.Mx = c->max_batch * c->max_rows;
   d.Rall_max = c->max_rows * (c->n_q_heads / c->n_kv_heads);
-  d.chunk = attn_chunk(c);
+  d.chunk = attention_chunk(c->head_dim);
   d.n_chunks = cdiv(c->max_ctx, d.chunk);
   d.esz = c->dtype == SPECDEC_BF16 ? 2 : 4;
   d.parts = c->vocab / 64;
   return d;
 }
 
-Layout make_layout(const specdec_config* c, const Dims& dm, size_t part_floats, int max_units) {
+Layout make_layout(const specdec_config* c, const Dims& dm) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -148,26 +143,21 @@ Layout make_layout(const specdec_config* c, const Dims& dm, size_t part_floats, 
   };
   const int d = c->d_model, qd = c->n_q_heads * c->head_dim, Dd = c->d_dim;
   L.x = take((size_t)dm.Mx * d * 4);
-  L.scale = take((size_t)dm.Mx * 4);
   L.q = take((size_t)dm.Mx * qd * 4);
   L.o = take((size_t)dm.Mx * qd * dm.esz);
   L.h = take((size_t)dm.Mx * c->ffn_dim * dm.esz);
-  L.ssq = take((size_t)dm.Mx * std::max(d, Dd) / 16 * 4);
-  L.part = take(part_floats * 4);
-  L.cnt = take((size_t)max_units * 4);
-  L.gcnt = take(64);
+  L.ssq = take((size_t)dm.Mx * (d / 16) * 4);
+  L.ssq_d = take((size_t)dm.Bx * (Dd / 16) * 4);
   L.amax_v = take((size_t)dm.Mx * dm.parts * 4);
   L.amax_i = take((size_t)dm.Mx * dm.parts * 4);
   L.att_part = take((size_t)dm.Bx * c->n_kv_heads * dm.n_chunks * dm.Rall_max * (c->head_dim + 2) * 4);
-  L.att_cnt = take((size_t)dm.Bx * c->n_kv_heads * 4);
   L.err = take(64);
   L.u = take((size_t)dm.Bx * (d + Dd) * dm.esz);
   L.xd = take((size_t)dm.Bx * Dd * 4);
-  L.scale_d = take((size_t)dm.Bx * 4);
   L.dh = take((size_t)dm.Bx * c->d_ffn * dm.esz);
   L.hnext = take((size_t)dm.Bx * d * 4);
   L.z = take((size_t)dm.Bx * c->n_centroids * 4);
-  L.utile = take((size_t)dm.parts * dm.Bx * 4);
+  L.utile = take((size_t)dm.Bx * dm.parts * 4);
   L.urow = take((size_t)dm.Bx * dm.parts * 4);
   L.dtok = take((size_t)dm.Bx * 4);
   L.d_amax_v = take((size_t)dm.Bx * dm.parts * 4);  // [B][V/64] (full) or [B*k_c*upc] (clustered)
@@ -183,12 +173,12 @@ void build_gemms(specdec_ctx* x) {
   x->g_dq.clear(); x->g_do.clear(); x->g_dgu.clear(); x->g_ddown.clear();
   for (int l = 0; l < c.n_layers; ++l) {
     const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
-    x->g_qkv.push_back(make_gemm(t ? t[SPECDEC_LW_QKV] : nullptr, qd + 2 * kvd, d, 1));
-    x->g_o.push_back(make_gemm(t ? t[SPECDEC_LW_O] : nullptr, d, qd, 1));
-    x->g_gu.push_back(make_gemm(t ? t[SPECDEC_LW_GATE_UP] : nullptr, 2 * c.ffn_dim, d, 2));
-    x->g_down.push_back(make_gemm(t ? t[SPECDEC_LW_DOWN] : nullptr, d, c.ffn_dim, 1));
+    x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, 1));
+    x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, 1));
+    x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * c.ffn_dim, d, 2));
+    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, c.ffn_dim, 1));
   }
-  x->g_head = make_gemm(x->embed, c.vocab, d, 4);
+  x->g_head = make_gemm(x->w.embed, c.vocab, d, 4);
   x->g_in = make_gemm(x->w.w_in, c.d_dim, d + c.d_dim, 1);
   x->g_back = make_gemm(x->w.w_back, d, c.d_dim, 1);
   x->g_cent = make_gemm(x->w.centroids, c.n_centroids, c.d_dim, 1);
@@ -203,33 +193,14 @@ void build_gemms(specdec_ctx* x) {
   }
 }
 
-// Sizing without weights: same shapes as build_gemms.
-void sizing(const specdec_config* c, const Dims& dm, size_t* part_floats, int* max_units) {
-  const int d = c->d_model, qd = c->n_q_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
-  std::vector<Gemm> gs = {
-      make_gemm(nullptr, qd + 2 * kvd, d, 1), make_gemm(nullptr, d, qd, 1),
-      make_gemm(nullptr, 2 * c->ffn_dim, d, 2), make_gemm(nullptr, d, c->ffn_dim, 1),
-      make_gemm(nullptr, c->vocab, d, 4), make_gemm(nullptr, c->d_dim, d + c->d_dim, 1),
-      make_gemm(nullptr, d, c->d_dim, 1), make_gemm(nullptr, c->n_centroids, c->d_dim, 1),
-      make_gemm(nullptr, c->vocab, c->d_dim, 4), make_gemm(nullptr, qd, c->d_dim, 1),
-      make_gemm(nullptr, c->d_dim, qd, 1), make_gemm(nullptr, 2 * c->d_ffn, c->d_dim, 2),
-      make_gemm(nullptr, c->d_dim, c->d_ffn, 1)};
-  size_t pf = 0;
-  int mu = 0;
-  for (auto& g : gs) {
-    pf = std::max(pf, gemm_part_floats(g, dm.Mx));
-    mu = std::max(mu, g.n_units);
-  }
-  *part_floats = pf;
-  *max_units = mu;
-}
-
 template <typename P>
 P* at(specdec_ctx* x, size_t off) {
   return reinterpret_cast<P*>(x->ws + off);
 }
 
 int mt_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+int dt_of(const specdec_ctx* x) { return x->cfg.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32; }
 
 struct ProfScope {
   specdec_ctx* x;
@@ -255,42 +226,34 @@ GemmArgs base_args(specdec_ctx* x, const Gemm& g, int M) {
   a.nkb = g.nkb;
   a.n_tiles = g.n_tiles;
   a.n_units = g.n_units;
-  a.S = g.S;
+  a.KW = g.KW;
+  a.NW = g.NW;
   a.kb_per_split = g.kbps;
   a.M = M;
-  a.part = at<float>(x, x->lay.part);
-  a.cnt = at<int>(x, x->lay.cnt);
-  a.gcnt = at<int>(x, x->lay.gcnt);
   a.err = at<int>(x, x->lay.err);
   a.eps = x->cfg.rms_eps;
   return a;
 }
 
-#define HIP_TRY(expr)                         \
-  do {                                        \
+// X prologue: the fp32 residual x normalised on load with the given norm weight.
+void norm_input(GemmArgs& a, const float* X, int ld, const float* ssq, int n, const float* w) {
+  a.X = X;
+  a.ldx = ld;
+  a.xssq = ssq;
+  a.n_ssq = n / 16;
+  a.scale_n = n;
+  a.xnorm = w;
+}
+
+#define HIP_TRY(expr)                               \
+  do {                                              \
     if ((expr) != hipSuccess) return SPECDEC_E_HIP; \
   } while (0)
 
 int run(specdec_ctx* x, int cls, int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
   ProfScope ps(x, cls, st);
-  HIP_TRY(launch_gemm(x->cfg.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, mt_for(a.M), NU, xmode,
-                      epi, a, st));
+  HIP_TRY(launch_gemm(dt_of(x), mt_for(a.M), NU, xmode, epi, a, st));
   return SPECDEC_OK;
-}
-
-// x[m] (+)= y with the next RMSNorm's row scale.
-int gemm_resid(specdec_ctx* x, int cls, const Gemm& g, int M, int xmode, const void* X, int ldx,
-               const float* xs, const float* xn, float* out, int ldo, int accumulate,
-               float* scale_out, int scale_n, hipStream_t st) {
-  GemmArgs a = base_args(x, g, M);
-  a.X = X; a.ldx = ldx; a.xscale = xs; a.xnorm = xn;
-  a.out = out; a.ldo = ldo; a.accumulate = accumulate;
-  if (scale_out) {
-    a.ssq = at<float>(x, x->lay.ssq);
-    a.scale_out = scale_out;
-    a.scale_n = scale_n;
-  }
-  return run(x, cls, 1, xmode, EPI_STORE, a, st);
 }
 
 int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hipStream_t st) {
@@ -303,17 +266,20 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
   a.len = x->len;
   a.out = x->ws + x->lay.o;
   a.part = at<float>(x, x->lay.att_part);
-  a.cnt = at<int>(x, x->lay.att_cnt);
   a.err = at<int>(x, x->lay.err);
-  a.B = B; a.R = R; a.key_off = key_off;
-  a.hq = c.n_q_heads; a.hkv = c.n_kv_heads; a.hd = c.head_dim;
+  a.B = B;
+  a.R = R;
+  a.key_off = key_off;
+  a.hq = c.n_q_heads;
+  a.hkv = c.n_kv_heads;
+  a.hd = c.head_dim;
   a.max_ctx = c.max_ctx;
   a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
   a.chunk = x->dm.chunk;
   a.n_chunks = x->dm.n_chunks;
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
   ProfScope ps(x, cls, st);
-  HIP_TRY(launch_attention(c.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, a, st));
+  HIP_TRY(launch_attention(dt_of(x), a, st));
   return SPECDEC_OK;
 }
 
@@ -323,11 +289,7 @@ extern "C" {
 
 size_t specdec_workspace_bytes(const specdec_config* cfg) {
   if (!valid_config(cfg)) return 0;
-  Dims dm = make_dims(cfg);
-  size_t pf;
-  int mu;
-  sizing(cfg, dm, &pf, &mu);
-  return make_layout(cfg, dm, pf, mu).total;
+  return make_layout(cfg, make_dims(cfg)).total;
 }
 
 size_t specdec_kv_elems(const specdec_config* c) {
@@ -342,7 +304,7 @@ int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv
   *out = nullptr;
   if (!valid_config(cfg) || !w || !kv_k || !kv_v || !len || !hid || !workspace)
     return SPECDEC_E_INVAL;
-  if (cfg->n_experts > 0) return SPECDEC_E_UNSUPPORTED;
+  if (cfg->n_experts > 0 || !attention_supported(cfg->head_dim)) return SPECDEC_E_UNSUPPORTED;
   if (((uintptr_t)workspace) % ALIGN) return SPECDEC_E_INVAL;
   if (!w->embed || !w->final_norm || !w->layers || !w->table || !w->centroids || !w->row_vocab ||
       !w->vocab_row || !w->norm_h || !w->norm_e || !w->w_in || !w->d_layers || !w->norm_f ||
@@ -359,31 +321,21 @@ int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv
   x->cfg = *cfg;
   if (x->cfg.kv_src_layer < 0) x->cfg.kv_src_layer = cfg->n_layers - 1;
   x->dm = make_dims(cfg);
-  size_t pf;
-  int mu;
-  sizing(cfg, x->dm, &pf, &mu);
-  x->lay = make_layout(cfg, x->dm, pf, mu);
+  x->lay = make_layout(cfg, x->dm);
   x->ws = reinterpret_cast<char*>(workspace);
   x->kv_k = kv_k;
   x->kv_v = kv_v;
   x->len = len;
   x->hid = hid;
   x->w = *w;
-  x->embed = w->embed;
-  x->final_norm = w->final_norm;
   x->lw.assign(w->layers, w->layers + (size_t)cfg->n_layers * SPECDEC_N_LAYER_TENSORS);
   x->dw.assign(w->d_layers, w->d_layers + (size_t)cfg->d_layers * SPECDEC_N_DRAFT_TENSORS);
   x->w.layers = nullptr;
   x->w.d_layers = nullptr;
   build_gemms(x);
   x->len_hi.assign(cfg->max_batch, 0);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // zero the arrival counters and the error word
-  if (launch_fill_i32(at<int>(x, x->lay.cnt), 0, (size_t)mu, st) != hipSuccess ||
-      launch_fill_i32(at<int>(x, x->lay.gcnt), 0, 16, st) != hipSuccess ||
-      launch_fill_i32(at<int>(x, x->lay.att_cnt), 0, (size_t)x->dm.Bx * cfg->n_kv_heads, st) !=
-          hipSuccess ||
-      launch_fill_i32(at<int>(x, x->lay.err), 0, 16, st) != hipSuccess) {
+  if (launch_fill_i32(at<int>(x, x->lay.err), 0, 16, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess) {
     delete x;
     return SPECDEC_E_HIP;
   }
@@ -408,49 +360,68 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int M = B * R;
   const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
-  const int dt = c.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32;
   float* X = at<float>(x, x->lay.x);
-  float* scale = at<float>(x, x->lay.scale);
+  float* ssq = at<float>(x, x->lay.ssq);
   int* err = at<int>(x, x->lay.err);
-  HIP_TRY(launch_embed(dt, x->embed, x->g_head.nkb, d, tokens, M, X, nullptr, scale, c.rms_eps,
-                       c.vocab, err, st));
+  HIP_TRY(launch_embed(dt_of(x), x->w.embed, x->g_head.nkb, d, tokens, M, X, ssq, c.vocab, err, st));
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
   int rc;
   for (int l = 0; l < c.n_layers; ++l) {
     const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
-    {  // fused q/k/v projection + RoPE + KV append
+    {  // fused q/k/v projection + RoPE + KV append (tentative: len is not moved)
       GemmArgs a = base_args(x, x->g_qkv[l], M);
-      a.X = X; a.ldx = d; a.xscale = scale; a.xnorm = (const float*)t[SPECDEC_LW_ATTN_NORM];
+      norm_input(a, X, d, ssq, d, (const float*)t[SPECDEC_LW_ATTN_NORM]);
       a.qout = at<float>(x, x->lay.q);
       a.kcache = (char*)x->kv_k + per_layer * l * x->dm.esz;
       a.vcache = (char*)x->kv_v + per_layer * l * x->dm.esz;
-      a.len = x->len; a.rows_per_seq = R; a.pos_off = 0;
-      a.hq = c.n_q_heads; a.hkv = c.n_kv_heads; a.hd = c.head_dim;
-      a.max_ctx = c.max_ctx; a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
+      a.len = x->len;
+      a.rows_per_seq = R;
+      a.pos_off = 0;
+      a.hq = c.n_q_heads;
+      a.hkv = c.n_kv_heads;
+      a.hd = c.head_dim;
+      a.max_ctx = c.max_ctx;
+      a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
       a.theta = c.rope_theta;
       if ((rc = run(x, 2, 1, XM_NORM, EPI_ROPE, a, st))) return rc;
     }
     if ((rc = attention(x, l, B, R, 1, 4, st))) return rc;
-    if ((rc = gemm_resid(x, 3, x->g_o[l], M, XM_ELEM, x->ws + x->lay.o, qd, nullptr, nullptr, X,
-                         d, 1, scale, d, st)))
-      return rc;
-    {
+    {  // output projection + residual
+      GemmArgs a = base_args(x, x->g_o[l], M);
+      a.X = x->ws + x->lay.o;
+      a.ldx = qd;
+      a.out = X;
+      a.ldo = d;
+      a.accumulate = 1;
+      a.ssq = ssq;
+      if ((rc = run(x, 3, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+    }
+    {  // gate/up projection + SiLU-gated product
       GemmArgs a = base_args(x, x->g_gu[l], M);
-      a.X = X; a.ldx = d; a.xscale = scale; a.xnorm = (const float*)t[SPECDEC_LW_FFN_NORM];
-      a.hout = x->ws + x->lay.h; a.ldh = c.ffn_dim;
+      norm_input(a, X, d, ssq, d, (const float*)t[SPECDEC_LW_FFN_NORM]);
+      a.hout = x->ws + x->lay.h;
+      a.ldh = c.ffn_dim;
       if ((rc = run(x, 0, 2, XM_NORM, EPI_SILU, a, st))) return rc;
     }
-    if ((rc = gemm_resid(x, 1, x->g_down[l], M, XM_ELEM, x->ws + x->lay.h, c.ffn_dim, nullptr,
-                         nullptr, X, d, 1, scale, d, st)))
-      return rc;
+    {  // down projection + residual
+      GemmArgs a = base_args(x, x->g_down[l], M);
+      a.X = x->ws + x->lay.h;
+      a.ldx = c.ffn_dim;
+      a.out = X;
+      a.ldo = d;
+      a.accumulate = 1;
+      a.ssq = ssq;
+      if ((rc = run(x, 1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+    }
   }
   {  // final norm + tied LM head with per-unit argmax partials
     GemmArgs a = base_args(x, x->g_head, M);
-    a.X = X; a.ldx = d; a.xscale = scale; a.xnorm = x->final_norm;
+    norm_input(a, X, d, ssq, d, x->w.final_norm);
     a.amax_val = at<float>(x, x->lay.amax_v);
     a.amax_idx = at<int>(x, x->lay.amax_i);
     a.ld_amax = x->dm.parts;
-    a.logits = logits; a.ld_logits = c.vocab;
+    a.logits = logits;
+    a.ld_logits = c.vocab;
     if ((rc = run(x, 5, 4, XM_NORM, EPI_ARGMAX, a, st))) return rc;
   }
   if (argmax) {
@@ -496,16 +467,16 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
   if (B < 1 || B > c.max_batch || K < 1 || K > c.max_draft) return SPECDEC_E_INVAL;
   if (head_mode != SPECDEC_HEAD_CLUSTERED && head_mode != SPECDEC_HEAD_FULL) return SPECDEC_E_INVAL;
   if (head_mode == SPECDEC_HEAD_CLUSTERED && (k_c < 1 || k_c > c.n_centroids)) return SPECDEC_E_INVAL;
-  if (inject && inj_stride < 1) return SPECDEC_E_INVAL;
+  if (inject && (inj_stride < 1 || inj_stride > 0x7fffffff)) return SPECDEC_E_INVAL;
   for (int b = 0; b < B; ++b)
     if (x->len_hi[b] > c.max_ctx) return SPECDEC_E_CAPACITY;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int dt = c.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32;
+  const int dt = dt_of(x);
   const int d = c.d_model, Dd = c.d_dim, qd = c.n_q_heads * c.head_dim;
-  const int S = c.vocab / c.n_centroids;           // tokens per cluster
-  const int tpc = S / 16, upc = S / 64;            // tiles / argmax units per cluster
+  const int S = c.vocab / c.n_centroids;  // tokens per cluster
+  const int tpc = S / 16, upc = S / 64;   // tiles / argmax units per cluster
   float* xd = at<float>(x, x->lay.xd);
-  float* sd = at<float>(x, x->lay.scale_d);
+  float* sd = at<float>(x, x->lay.ssq_d);
   float* hnext = at<float>(x, x->lay.hnext);
   int* dtok = at<int>(x, x->lay.dtok);
   int* err = at<int>(x, x->lay.err);
@@ -517,44 +488,74 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
     HIP_TRY(launch_draft_input(dt, h, tok, x->w.table, x->g_table.nkb, x->w.vocab_row, c.vocab,
                                x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u, B,
                                err, st));
-    if ((rc = gemm_resid(x, -1, x->g_in, B, XM_ELEM, x->ws + x->lay.u, d + Dd, nullptr, nullptr,
-                         xd, Dd, 0, sd, Dd, st)))
-      return rc;
+    {  // input projection of [rms(h); rms(e)]
+      GemmArgs a = base_args(x, x->g_in, B);
+      a.X = x->ws + x->lay.u;
+      a.ldx = d + Dd;
+      a.out = xd;
+      a.ldo = Dd;
+      a.ssq = sd;
+      if ((rc = run(x, -1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+    }
     for (int l = 0; l < c.d_layers; ++l) {
       const void* const* t = x->dw.data() + (size_t)l * SPECDEC_N_DRAFT_TENSORS;
-      {
+      {  // q projection + RoPE at len + j - 1
         GemmArgs a = base_args(x, x->g_dq[l], B);
-        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = (const float*)t[SPECDEC_DW_N1];
+        norm_input(a, xd, Dd, sd, Dd, (const float*)t[SPECDEC_DW_N1]);
         a.qout = at<float>(x, x->lay.q);
-        a.len = x->len; a.rows_per_seq = 1; a.pos_off = j - 1;
-        a.hq = c.n_q_heads; a.hkv = 0; a.hd = c.head_dim;
-        a.max_ctx = c.max_ctx; a.theta = c.rope_theta;
+        a.len = x->len;
+        a.rows_per_seq = 1;
+        a.pos_off = j - 1;
+        a.hq = c.n_q_heads;
+        a.hkv = 0;
+        a.hd = c.head_dim;
+        a.max_ctx = c.max_ctx;
+        a.theta = c.rope_theta;
         if ((rc = run(x, -1, 1, XM_NORM, EPI_ROPE, a, st))) return rc;
       }
+      // cross-attention into the target's cache, keys [0, len)
       if ((rc = attention(x, src, B, 1, 0, -1, st))) return rc;
-      if ((rc = gemm_resid(x, -1, x->g_do[l], B, XM_ELEM, x->ws + x->lay.o, qd, nullptr, nullptr,
-                           xd, Dd, 1, sd, Dd, st)))
-        return rc;
+      {
+        GemmArgs a = base_args(x, x->g_do[l], B);
+        a.X = x->ws + x->lay.o;
+        a.ldx = qd;
+        a.out = xd;
+        a.ldo = Dd;
+        a.accumulate = 1;
+        a.ssq = sd;
+        if ((rc = run(x, -1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+      }
       {
         GemmArgs a = base_args(x, x->g_dgu[l], B);
-        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = (const float*)t[SPECDEC_DW_N2];
-        a.hout = x->ws + x->lay.dh; a.ldh = c.d_ffn;
+        norm_input(a, xd, Dd, sd, Dd, (const float*)t[SPECDEC_DW_N2]);
+        a.hout = x->ws + x->lay.dh;
+        a.ldh = c.d_ffn;
         if ((rc = run(x, -1, 2, XM_NORM, EPI_SILU, a, st))) return rc;
       }
-      if ((rc = gemm_resid(x, -1, x->g_ddown[l], B, XM_ELEM, x->ws + x->lay.dh, c.d_ffn, nullptr,
-                           nullptr, xd, Dd, 1, sd, Dd, st)))
-        return rc;
+      {
+        GemmArgs a = base_args(x, x->g_ddown[l], B);
+        a.X = x->ws + x->lay.dh;
+        a.ldx = c.d_ffn;
+        a.out = xd;
+        a.ldo = Dd;
+        a.accumulate = 1;
+        a.ssq = sd;
+        if ((rc = run(x, -1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+      }
     }
-    // next hidden input: W_back . rms(x)*n_f
-    if ((rc = gemm_resid(x, -1, x->g_back, B, XM_NORM, xd, Dd, sd, x->w.norm_f, hnext, d, 0,
-                         nullptr, 0, st)))
-      return rc;
-    int parts_per_seq, seq_off;
+    {  // next hidden input: W_back . rms(x) * n_f
+      GemmArgs a = base_args(x, x->g_back, B);
+      norm_input(a, xd, Dd, sd, Dd, x->w.norm_f);
+      a.out = hnext;
+      a.ldo = d;
+      if ((rc = run(x, -1, 1, XM_NORM, EPI_STORE, a, st))) return rc;
+    }
+    int parts_per_seq, seq_off, ld;
     {
       ProfScope ps(x, 6, st);
       if (head_mode == SPECDEC_HEAD_FULL) {
         GemmArgs a = base_args(x, x->g_table, B);
-        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = x->w.norm_f;
+        norm_input(a, xd, Dd, sd, Dd, x->w.norm_f);
         a.amax_val = at<float>(x, x->lay.d_amax_v);
         a.amax_idx = at<int>(x, x->lay.d_amax_i);
         a.ld_amax = x->dm.parts;
@@ -562,31 +563,31 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         HIP_TRY(launch_gemm(dt, mt_for(B), 4, XM_NORM, EPI_ARGMAX, a, st));
         parts_per_seq = x->dm.parts;
         seq_off = 0;
+        ld = x->dm.parts;
       } else {
         GemmArgs zc = base_args(x, x->g_cent, B);
-        zc.X = xd; zc.ldx = Dd; zc.xscale = sd; zc.xnorm = x->w.norm_f;
-        zc.out = at<float>(x, x->lay.z); zc.ldo = c.n_centroids;
+        norm_input(zc, xd, Dd, sd, Dd, x->w.norm_f);
+        zc.out = at<float>(x, x->lay.z);
+        zc.ldo = c.n_centroids;
         HIP_TRY(launch_gemm(dt, mt_for(B), 1, XM_NORM, EPI_STORE, zc, st));
         HIP_TRY(launch_cluster_select(at<float>(x, x->lay.z), c.n_centroids, k_c, B, tpc, upc,
-                                      at<int>(x, x->lay.utile), at<int>(x, x->lay.urow), st));
+                                      at<int>(x, x->lay.utile), at<int>(x, x->lay.urow), err, st));
         GemmArgs a = base_args(x, x->g_clu, B);
         a.n_units = B * k_c * upc;
         a.unit_tile = at<int>(x, x->lay.utile);
         a.unit_row = at<int>(x, x->lay.urow);
-        a.X = xd; a.ldx = Dd; a.xscale = sd; a.xnorm = x->w.norm_f;
+        norm_input(a, xd, Dd, sd, Dd, x->w.norm_f);
         a.amax_val = at<float>(x, x->lay.d_amax_v);
         a.amax_idx = at<int>(x, x->lay.d_amax_i);
-        a.ld_amax = x->dm.parts;
         a.idx_map = x->w.row_vocab;
         HIP_TRY(launch_gemm(dt, mt_for(B), 4, XM_NORM, EPI_ARGMAX, a, st));
         parts_per_seq = k_c * upc;
         seq_off = k_c * upc;
+        ld = 0;  // listed units are stored by unit index
       }
-      HIP_TRY(launch_draft_finalize(at<float>(x, x->lay.d_amax_v), at<int>(x, x->lay.d_amax_i),
-                                    head_mode == SPECDEC_HEAD_FULL ? x->dm.parts : 0,
+      HIP_TRY(launch_draft_finalize(at<float>(x, x->lay.d_amax_v), at<int>(x, x->lay.d_amax_i), ld,
                                     parts_per_seq, seq_off, B, K, j, x->len, inject,
-                                    (int)std::min<int64_t>(inj_stride, 0x7fffffff), drafts, dtok,
-                                    err, st));
+                                    (int)inj_stride, drafts, dtok, err, st));
     }
   }
   return SPECDEC_OK;
@@ -596,11 +597,11 @@ int specdec_pack_matrix(const void* src, void* dst, int32_t n, int32_t kd, int32
                         int32_t kind, int32_t head_dim, int32_t split_rows, void* stream) {
   if (!src || !dst || n < 16 || kd < 32 || n % 16 || kd % 32) return SPECDEC_E_INVAL;
   if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_E_INVAL;
+  if (kind < 0 || kind > 2) return SPECDEC_E_INVAL;
   if (kind == SPECDEC_PACK_ROPE && (head_dim < 16 || head_dim % 16 || n % head_dim))
     return SPECDEC_E_INVAL;
   if (kind == SPECDEC_PACK_GATE_UP && (split_rows * 2 != n || split_rows % 16))
     return SPECDEC_E_INVAL;
-  if (kind < 0 || kind > 2) return SPECDEC_E_INVAL;
   HIP_TRY(launch_pack(dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, src, dst, n, kd, kind, head_dim,
                       split_rows, reinterpret_cast<hipStream_t>(stream)));
   return SPECDEC_OK;
@@ -630,10 +631,11 @@ int specdec_profile_start(specdec_ctx* x, int32_t cls, int32_t capacity) {
   x->prof_ev.clear();
   x->prof_class = -1;
   x->prof_n = 0;
+  x->prof_cap = 0;
   x->prof_ev.resize((size_t)2 * capacity);
   for (auto& e : x->prof_ev) HIP_TRY(hipEventCreate(&e));
-  x->prof_class = cls;
   x->prof_cap = capacity;
+  x->prof_class = cls;
   return SPECDEC_OK;
 }
 
@@ -662,7 +664,7 @@ int specdec_query_split(specdec_ctx* x, int32_t cls, int32_t* splits, int32_t* u
     case 5: g = &x->g_head; break;
     default: return SPECDEC_E_INVAL;
   }
-  *splits = g->S;
+  *splits = g->KW;
   *units = g->n_units;
   return SPECDEC_OK;
 }

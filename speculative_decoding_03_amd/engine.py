@@ -207,9 +207,11 @@ class Engine:
 
     # --- state helpers (setup / tests) ---
     def kv_view(self):
+        """K as [L][B][Hkv][max_ctx][hd] and V as [L][B][Hkv][hd][max_ctx]."""
         s = self.shape
         shp = (s.n_layers, self.max_batch, s.n_kv_heads, self.max_ctx, s.head_dim)
-        return self.kv_k.view(shp), self.kv_v.view(shp)
+        vshp = (s.n_layers, self.max_batch, s.n_kv_heads, s.head_dim, self.max_ctx)
+        return self.kv_k.view(shp), self.kv_v.view(vshp)
 
     def set_len(self, values) -> None:
         vals = [int(v) for v in values]

@@ -62,7 +62,7 @@ def oracle_logits_at(W, cfg, h, ids):
 @pytest.fixture(scope="module", params=sorted(CASES))
 def case(request):
     cfg = CASES[request.param]
-    max_ctx = cfg.ctx + 96
+    max_ctx = (cfg.ctx + 96 + 7) // 8 * 8
     eng = build_engine(cfg, max_ctx)
     WD.fill_kv(eng, cfg)
     t0 = WD.start_state(eng, cfg)

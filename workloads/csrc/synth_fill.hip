@@ -37,10 +37,10 @@ __global__ void fill_uniform(void* dst, int64_t n, int bf16, uint64_t key, int64
   }
 }
 
-// KV cache [L][Bc][Hkv][max_ctx][hd]: positions [0, ctx) of sequences [0, Bl) get the logical
-// element (((l*Bl + b)*Hkv + g)*ctx + pos)*hd + c of the stream.
+// KV cache: K [L][Bc][Hkv][max_ctx][hd], V transposed [L][Bc][Hkv][hd][max_ctx].  Positions
+// [0, ctx) of sequences [0, Bl) get the logical element (((l*Bl + b)*Hkv + g)*ctx + pos)*hd + c.
 __global__ void fill_kv(void* dst, int L, int Bl, int Bc, int Hkv, int ctx, int max_ctx, int hd,
-                        int bf16, uint64_t key, float scale) {
+                        int bf16, uint64_t key, float scale, int transposed) {
   const int64_t n = (int64_t)L * Bl * Hkv * ctx * hd;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -50,7 +50,8 @@ __global__ void fill_kv(void* dst, int L, int Bl, int Bc, int Hkv, int ctx, int 
     const int g = (int)(r % Hkv); r /= Hkv;
     const int b = (int)(r % Bl); r /= Bl;
     const int l = (int)r;
-    const int64_t o = ((((int64_t)l * Bc + b) * Hkv + g) * max_ctx + pos) * hd + c;
+    const int64_t head = ((int64_t)l * Bc + b) * Hkv + g;
+    const int64_t o = transposed ? (head * hd + c) * max_ctx + pos : (head * max_ctx + pos) * hd + c;
     const float v = value_at(key, (uint64_t)i, scale);
     if (bf16) reinterpret_cast<uint16_t*>(dst)[o] = to_bf16(v);
     else reinterpret_cast<float*>(dst)[o] = v;
@@ -76,12 +77,12 @@ int synth_fill_uniform(void* dst, int64_t n, int bf16, uint64_t key, int64_t sta
 }
 
 int synth_fill_kv(void* dst, int L, int Bl, int Bc, int Hkv, int ctx, int max_ctx, int hd,
-                  int bf16, uint64_t key, float scale, void* stream) {
+                  int bf16, uint64_t key, float scale, int transposed, void* stream) {
   if (!dst || ctx > max_ctx || Bl > Bc) return -1;
   const int64_t n = (int64_t)L * Bl * Hkv * ctx * hd;
   if (n == 0) return 0;
   hipLaunchKernelGGL(fill_kv, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, dst, L, Bl,
-                     Bc, Hkv, ctx, max_ctx, hd, bf16, key, scale);
+                     Bc, Hkv, ctx, max_ctx, hd, bf16, key, scale, transposed);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -48,7 +48,8 @@ def synth_lib():
         lib.synth_fill_uniform.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_uint64, C.c_int64,
                                            C.c_float, C.c_void_p]
         lib.synth_fill_kv.restype = C.c_int
-        lib.synth_fill_kv.argtypes = [C.c_void_p] + [C.c_int] * 8 + [C.c_uint64, C.c_float, C.c_void_p]
+        lib.synth_fill_kv.argtypes = [C.c_void_p] + [C.c_int] * 8 + [C.c_uint64, C.c_float, C.c_int,
+                                                                      C.c_void_p]
         _synth = lib
     return _synth
 
@@ -110,7 +111,8 @@ def clusters(cfg, device="cuda"):
 
 
 def fill_kv(engine, cfg) -> None:
-    """Synthetic committed KV of cfg.ctx positions for sequences [0, cfg.batch) (std 1)."""
+    """Synthetic committed KV of cfg.ctx positions for sequences [0, cfg.batch) (std 1); K is
+    stored [pos][hd] and V transposed [hd][pos], as the library lays the cache out."""
     bf16 = 1 if cfg.dtype == "bf16" else 0
     s = engine.shape
     for which, buf in (("kv_k", engine.kv_k), ("kv_v", engine.kv_v)):
@@ -118,7 +120,7 @@ def fill_kv(engine, cfg) -> None:
         rc = synth_lib().synth_fill_kv(C.c_void_p(buf.data_ptr()), s.n_layers, cfg.batch,
                                        engine.max_batch, s.n_kv_heads, cfg.ctx, engine.max_ctx,
                                        s.head_dim, bf16, C.c_uint64(key), float(S.hash_scale(1.0)),
-                                       _stream())
+                                       1 if which == "kv_v" else 0, _stream())
         if rc != 0:
             raise RuntimeError(f"synth_fill_kv failed ({rc})")
 

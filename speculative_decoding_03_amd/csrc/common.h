@@ -127,6 +127,24 @@ __device__ __forceinline__ void load_frag(Frag<T>& f, const T* p) {
   }
 }
 
+// The 8 values of a fragment as fp32.
+template <typename T>
+__device__ __forceinline__ void frag_values(const Frag<T>& f, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(f.v[i] << 16);
+      v[2 * i + 1] = __uint_as_float(f.v[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(f.v[0][i]);
+      v[4 + i] = __uint_as_float(f.v[1][i]);
+    }
+  }
+}
+
 // acc += A (16 rows x 32, lanes as Frag) . B^T (16 cols x 32): C[i][j], lane l holds rows
 // (l/16)*4 + 0..3 of column l%16.
 template <typename T>

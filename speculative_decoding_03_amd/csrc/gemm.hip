@@ -12,10 +12,12 @@
 // verify row and the same row in a decode step go through the same instruction sequence and
 // come out bit-identical.  There is no communication between workgroups.
 //
-// Prologue: X is either a storage-typed activation or the fp32 residual stream normalised on
-// load (x * rowscale * normweight: the layer's RMSNorm); the row scale is formed from per-tile
-// sums of squares left by the producer of x.  Epilogues: store / residual add (leaving those
-// sums of squares), rotary embedding + KV-cache append, SiLU-gated product, per-unit argmax.
+// RMSNorm without a pass of its own: rms(x) * w . W^T = s * ((x * w) . W^T) with the row scale
+// s = 1/sqrt(mean(x^2) + eps).  The producer of the residual x also writes x * w_next in the
+// storage type (w_next = the weight of the norm that reads x next) and per-16-column sums of
+// squares of x; the consumer streams that operand like any other and multiplies its fp32
+// results by s, formed in its epilogue from the sums of squares.  Epilogues: store / residual
+// add, rotary embedding + KV-cache append, SiLU-gated product, per-unit argmax.
 
 #include <math.h>
 
@@ -40,32 +42,14 @@ __device__ __forceinline__ void load_w(Frag<T>& f, const T* W, size_t tile, int 
 }
 
 // X fragment of lane `lane` for k-block kb: row m = mt*16 + lane%16, k = kb*32 + (lane/16)*8.
-template <typename T, int XM>
-__device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int m, float rs, int kb,
-                                       int lane) {
+template <typename T>
+__device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int m, int kb, int lane) {
   if (m >= a.M) {
     zero_frag(f);
     return;
   }
   const int k = kb * TILE_K + ((lane >> 4) << 3);
-  if constexpr (XM == XM_ELEM) {
-    const u32x4* p =
-        reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.X) + (size_t)m * a.ldx + k);
-    if constexpr (sizeof(T) == 2) {
-      f.v = *p;
-    } else {
-      f.v[0] = p[0];
-      f.v[1] = p[1];
-    }
-  } else {
-    const float4* px = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.X) +
-                                                       (size_t)m * a.ldx + k);
-    const float4* pw = reinterpret_cast<const float4*>(a.xnorm + k);
-    float4 x0 = px[0], x1 = px[1], w0 = pw[0], w1 = pw[1];
-    const float y[8] = {x0.x * rs * w0.x, x0.y * rs * w0.y, x0.z * rs * w0.z, x0.w * rs * w0.w,
-                        x1.x * rs * w1.x, x1.y * rs * w1.y, x1.z * rs * w1.z, x1.w * rs * w1.w};
-    to_frag<T>(f, y);
-  }
+  load_frag<T>(f, reinterpret_cast<const T*>(a.X) + (size_t)m * a.ldx + k);
 }
 
 __device__ __forceinline__ float sum16(float v) {
@@ -85,14 +69,43 @@ __device__ __forceinline__ void argmax16(float& v, int& i) {
   }
 }
 
+// Row scales 1/sqrt(sum_t yssq[t][m] / yscale_n + eps) for the rows this lane holds.  The sum
+// runs lane-strided then through a fixed butterfly, identically for every caller.
+template <int MT>
+__device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, float (&sc)[MT][4]) {
+  float mine = 1.f;
+  for (int m = 0; m < a.M; ++m) {
+    float s = 0.f;
+    for (int t = lane; t < a.n_yssq; t += WAVE) s += a.yssq[(size_t)t * a.M + m];
+    s = wave_sum(s);
+    if (lane == m) mine = 1.0f / sqrtf(s / (float)a.yscale_n + a.eps);
+  }
+  const int rgrp = (lane >> 4) << 2;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc[mt][v] = __shfl(mine, (mt * 16 + rgrp + v) & 63, WAVE);
+}
+
 template <typename T, int MT, int NU, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
                                          int tile0, int lane) {
   const int c16 = lane & 15;
   const int rgrp = (lane >> 4) << 2;
+  if (a.yssq) {
+    float sc[MT][4];
+    row_scales<MT>(a, lane, sc);
+#pragma unroll
+    for (int t = 0; t < NU; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][mt][v] *= sc[mt][v];
+  }
   if constexpr (EPI == EPI_STORE) {
     const int tile = tile0;
     const int col = tile * TILE_N + c16;
+    const float wn = a.xw_out ? a.xw_norm[col] : 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -105,6 +118,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           if (a.accumulate) y = *o + y;
           *o = y;
           sq = y * y;
+          if (a.xw_out) Elem<T>::store(reinterpret_cast<T*>(a.xw_out) + (size_t)m * a.ldo + col, y * wn);
         }
         if (a.ssq) {
           const float r = sum16(sq);
@@ -203,16 +217,24 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
   }
 }
 
-// U: k-blocks in flight per wave per step of the main loop.
+// U: k-blocks per register stage (two stages are in flight) for NU = 1 / 2 / 4 tiles per unit.
+#ifndef SPECDEC_GEMM_U1
+#define SPECDEC_GEMM_U1 4
+#endif
+#ifndef SPECDEC_GEMM_U2
+#define SPECDEC_GEMM_U2 2
+#endif
+#ifndef SPECDEC_GEMM_U4
+#define SPECDEC_GEMM_U4 2
+#endif
 template <int NU, int MT> struct Unroll {
-  static constexpr int base = NU >= 2 ? 4 : 8;
+  static constexpr int base = NU >= 4 ? SPECDEC_GEMM_U4 : (NU == 2 ? SPECDEC_GEMM_U2 : SPECDEC_GEMM_U1);
   static constexpr int U = base / MT > 1 ? base / MT : 1;
 };
 
-template <typename T, int MT, int NU, int XM, int EPI, int NW>
+template <typename T, int MT, int NU, int EPI, int NW>
 __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   __shared__ f32x4 red[NW * NU * 64];
-  __shared__ float rscale[64];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x >> 6;
   const int KW = a.KW;
@@ -225,24 +247,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   const int kb1 = min(a.nkb, kb0 + a.kb_per_split);
   const T* W = reinterpret_cast<const T*>(a.W);
 
-  if constexpr (XM == XM_NORM) {
-    // row scale 1/sqrt(mean(x^2) + eps) from the producer's per-tile sums of squares
-    if (wid == 0) {
-      for (int m = 0; m < a.M; ++m) {
-        float s = 0.f;
-        for (int t = lane; t < a.n_ssq; t += WAVE) s += a.xssq[(size_t)t * a.M + m];
-        s = wave_sum(s);
-        if (lane == 0) rscale[m] = 1.0f / sqrtf(s / (float)a.scale_n + a.eps);
-      }
-    }
-    __syncthreads();
-  }
-  float rs[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + (lane & 15);
-    rs[mt] = (XM == XM_NORM && m < a.M) ? rscale[m] : 0.f;
-  }
   bool tvalid[NU];
 #pragma unroll
   for (int t = 0; t < NU; ++t) tvalid[t] = active && (tile0 + t) < a.n_tiles;
@@ -255,29 +259,43 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
 
   if (active) {
     constexpr int U = Unroll<NU, MT>::U;
-    int kb = kb0;
-    for (; kb + U <= kb1; kb += U) {
-      Frag<T> w[U][NU];
-      Frag<T> x[U][MT];
+    // Two register stages: the loads of batch i+1 are in flight while batch i is multiplied.
+    Frag<T> w[2][U][NU];
+    Frag<T> x[2][U][MT];
+    auto load_batch = [&](int st, int kbase) {
 #pragma unroll
       for (int uu = 0; uu < U; ++uu)
 #pragma unroll
         for (int t = 0; t < NU; ++t) {
-          if (tvalid[t]) load_w<T>(w[uu][t], W, (size_t)(tile0 + t), a.nkb, kb + uu, lane);
-          else zero_frag(w[uu][t]);
+          if (tvalid[t]) load_w<T>(w[st][uu][t], W, (size_t)(tile0 + t), a.nkb, kbase + uu, lane);
+          else zero_frag(w[st][uu][t]);
         }
 #pragma unroll
       for (int uu = 0; uu < U; ++uu)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          load_x<T, XM>(x[uu][mt], a, mt * 16 + (lane & 15), rs[mt], kb + uu, lane);
+          load_x<T>(x[st][uu][mt], a, mt * 16 + (lane & 15), kbase + uu, lane);
+    };
+    auto mul_batch = [&](int st) {
 #pragma unroll
       for (int uu = 0; uu < U; ++uu)
 #pragma unroll
         for (int t = 0; t < NU; ++t)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[uu][mt], w[uu][t], acc[t][mt]);
+          for (int mt = 0; mt < MT; ++mt)
+            acc[t][mt] = mma<T>(x[st][uu][mt], w[st][uu][t], acc[t][mt]);
+    };
+    const int nb = (kb1 - kb0) / U;  // whole batches
+    if (nb > 0) load_batch(0, kb0);
+    for (int b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) load_batch(1, kb0 + (b + 1) * U);
+      mul_batch(0);
+      if (b + 1 < nb) {
+        if (b + 2 < nb) load_batch(0, kb0 + (b + 2) * U);
+        mul_batch(1);
+      }
     }
+    int kb = kb0 + nb * U;
     for (; kb < kb1; ++kb) {
       Frag<T> w[NU];
       Frag<T> x[MT];
@@ -287,7 +305,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
         else zero_frag(w[t]);
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) load_x<T, XM>(x[mt], a, mt * 16 + (lane & 15), rs[mt], kb, lane);
+      for (int mt = 0; mt < MT; ++mt) load_x<T>(x[mt], a, mt * 16 + (lane & 15), kb, lane);
 #pragma unroll
       for (int t = 0; t < NU; ++t)
 #pragma unroll
@@ -320,58 +338,51 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   epilogue<T, MT, NU, EPI>(a, acc, u, tile0, lane);
 }
 
-template <typename T, int MT, int NU, int XM, int EPI, int NW>
+template <typename T, int MT, int NU, int EPI, int NW>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
   const int upw = NW / a.KW;
   dim3 grid((a.n_units + upw - 1) / upw), block(NW * 64);
-  hipLaunchKernelGGL((gemm_kernel<T, MT, NU, XM, EPI, NW>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-template <typename T, int MT, int NU, int XM, int EPI>
+template <typename T, int MT, int NU, int EPI>
 hipError_t launch_nw(const GemmArgs& a, hipStream_t st) {
   if constexpr (NU < 4) {
-    if (a.NW == 16) return launch_t<T, MT, NU, XM, EPI, 16>(a, st);
+    if (a.NW == 16) return launch_t<T, MT, NU, EPI, 16>(a, st);
   }
-  if (a.NW == 8) return launch_t<T, MT, NU, XM, EPI, 8>(a, st);
+  if (a.NW == 8) return launch_t<T, MT, NU, EPI, 8>(a, st);
+  if (a.NW == 4) return launch_t<T, MT, NU, EPI, 4>(a, st);
   return hipErrorInvalidValue;
 }
 
 template <typename T, int MT>
-hipError_t dispatch_epi(int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
-  if (epi == EPI_STORE && NU == 1)
-    return xmode == XM_NORM ? launch_nw<T, MT, 1, XM_NORM, EPI_STORE>(a, st)
-                            : launch_nw<T, MT, 1, XM_ELEM, EPI_STORE>(a, st);
-  if (epi == EPI_ROPE && NU == 1)
-    return xmode == XM_NORM ? launch_nw<T, MT, 1, XM_NORM, EPI_ROPE>(a, st)
-                            : launch_nw<T, MT, 1, XM_ELEM, EPI_ROPE>(a, st);
-  if (epi == EPI_SILU && NU == 2)
-    return xmode == XM_NORM ? launch_nw<T, MT, 2, XM_NORM, EPI_SILU>(a, st)
-                            : launch_nw<T, MT, 2, XM_ELEM, EPI_SILU>(a, st);
-  if (epi == EPI_ARGMAX && NU == 4)
-    return xmode == XM_NORM ? launch_nw<T, MT, 4, XM_NORM, EPI_ARGMAX>(a, st)
-                            : launch_nw<T, MT, 4, XM_ELEM, EPI_ARGMAX>(a, st);
+hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st) {
+  if (epi == EPI_STORE && NU == 1) return launch_nw<T, MT, 1, EPI_STORE>(a, st);
+  if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE>(a, st);
+  if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU>(a, st);
+  if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX>(a, st);
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t dispatch_mt(int MT, int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
+hipError_t dispatch_mt(int MT, int NU, int epi, const GemmArgs& a, hipStream_t st) {
   switch (MT) {
-    case 1: return dispatch_epi<T, 1>(NU, xmode, epi, a, st);
-    case 2: return dispatch_epi<T, 2>(NU, xmode, epi, a, st);
-    case 4: return dispatch_epi<T, 4>(NU, xmode, epi, a, st);
+    case 1: return dispatch_epi<T, 1>(NU, epi, a, st);
+    case 2: return dispatch_epi<T, 2>(NU, epi, a, st);
+    case 4: return dispatch_epi<T, 4>(NU, epi, a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int dtype, int MT, int NU, int xmode, int epi, const GemmArgs& a,
-                       hipStream_t st) {
+hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st) {
   if (a.n_units <= 0) return hipSuccess;
-  if (a.KW < 1 || (a.NW != 8 && a.NW != 16) || a.NW % a.KW) return hipErrorInvalidValue;
-  return dtype == DT_BF16 ? dispatch_mt<bf16_t>(MT, NU, xmode, epi, a, st)
-                          : dispatch_mt<float>(MT, NU, xmode, epi, a, st);
+  if (a.KW < 1 || (a.NW != 4 && a.NW != 8 && a.NW != 16) || a.NW % a.KW) return hipErrorInvalidValue;
+  if (a.M > MT * 16) return hipErrorInvalidValue;
+  return dtype == DT_BF16 ? dispatch_mt<bf16_t>(MT, NU, epi, a, st)
+                          : dispatch_mt<float>(MT, NU, epi, a, st);
 }
 
 }  // namespace specdec

@@ -7,7 +7,6 @@
 namespace specdec {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
-enum XMode { XM_ELEM = 0, XM_NORM = 1 };
 enum Epi { EPI_STORE = 0, EPI_ROPE = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
 
 // One skinny GEMM  Y[M][N] = X[M][Kd] . W[N][Kd]^T  over packed tiles, with a fused
@@ -25,21 +24,24 @@ struct GemmArgs {
   const int* n_units_dev = nullptr;  // optional device count of valid units
   int KW = 1, NW = 8, kb_per_split = 0;
   int M = 0;
-  // X operand: XM_ELEM -> storage-typed [M][ldx]; XM_NORM -> fp32 [M][ldx] * rowscale[m] *
-  // xnorm[k] with rowscale = 1/sqrt(sum_t xssq[t][m] / scale_n + eps) over n_ssq tiles
+  // X operand: storage-typed [M][ldx]
   const void* X = nullptr;
   int ldx = 0;
-  const float* xssq = nullptr;
-  int n_ssq = 0;
-  const float* xnorm = nullptr;
-  int scale_n = 0;
+  // optional row scale of the results (an RMSNorm folded in): y *= 1/sqrt(sum_t yssq[t][m] /
+  // yscale_n + eps) over n_yssq tiles
+  const float* yssq = nullptr;
+  int n_yssq = 0;
+  int yscale_n = 0;
   float eps = 0.f;
   int* err = nullptr;
-  // EPI_STORE: out[m][col] (=|+=) y; optional per-tile sums of squares of the result
+  // EPI_STORE: out[m][col] (=|+=) y; optional per-tile sums of squares of the result and the
+  // result times the next norm's weight in the storage type (xw_out[m][col], ld = ldo)
   float* out = nullptr;
   int ldo = 0;
   int accumulate = 0;
   float* ssq = nullptr;        // [n_tiles][M]
+  void* xw_out = nullptr;
+  const float* xw_norm = nullptr;
   // EPI_ROPE: columns are heads of hd with rotary pairs interleaved; heads [0,hq) -> qout,
   // [hq, hq+hkv) -> kcache, [hq+hkv, hq+2hkv) -> vcache at position len[b] + row + pos_off.
   float* qout = nullptr;
@@ -64,8 +66,7 @@ struct GemmArgs {
   int ld_logits = 0;
 };
 
-hipError_t launch_gemm(int dtype, int MT, int NU, int xmode, int epi, const GemmArgs& a,
-                       hipStream_t st);
+hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st);
 
 // Grouped-query attention of R query rows per sequence over one layer's cache: K [pos][hd],
 // V transposed [hd][pos].
@@ -85,7 +86,8 @@ struct AttnArgs {
   int max_ctx = 0;
   int cache_b_stride = 0;
   int chunk = 256;
-  int n_chunks = 0;  // launch bound = ceil(max_ctx / chunk)
+  int n_chunks = 0;  // chunks per head in the partial buffer = ceil(max_ctx / chunk)
+  int n_launch = 0;  // chunks launched: covers the host-side bound on len + R - 1 + key_off
   float scale = 0.f;
 };
 
@@ -95,7 +97,8 @@ bool attention_supported(int head_dim);     // head sizes the attention kernel i
 
 // Misc kernels (misc.hip).
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
-                        float* x, float* ssq, int vocab, int* err, hipStream_t st);
+                        float* x, float* ssq, void* xw, const float* norm, int vocab, int* err,
+                        hipStream_t st);
 hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
                          int B, int R, const int* tokens, int* out_tokens, int* n_emit,
                          int* next_tok, int commit, int* len, float* hid, const float* X, int d,

@@ -37,12 +37,13 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* rv, int* r
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_combine(v, i, rv[w], ri[w]);
 }
 
-// x[m] = E[tokens[m]] (fp32 residual) and the per-16-column sums of squares of x[m], the input
-// of the first layer's RMSNorm row scale.
+// x[m] = E[tokens[m]] (fp32 residual), xw[m] = x[m] * norm (the first layer's attention-norm
+// weight, storage type) and the per-16-column sums of squares of x[m], from which the consumer
+// forms the RMSNorm row scale.
 template <typename T>
 __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, const int* tokens,
-                                                    int M, float* x, float* ssq, int vocab,
-                                                    int* err) {
+                                                    int M, float* x, float* ssq, T* xw,
+                                                    const float* norm, int vocab, int* err) {
   extern __shared__ float sq[];
   const int m = blockIdx.x;
   int tok = tokens[m];
@@ -50,10 +51,19 @@ __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, 
     if (threadIdx.x == 0) raise_error(err, ERRBIT_TOKEN);
     tok = 0;
   }
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float v = Elem<T>::load(E + packed_offset(tok, k, nkb));
-    x[(size_t)m * d + k] = v;
-    sq[k] = v * v;
+  // 8 consecutive elements of a row are contiguous in the packed layout: one 16-byte load each
+  for (int k8 = threadIdx.x * 8; k8 < d; k8 += blockDim.x * 8) {
+    Frag<T> f;
+    load_frag<T>(f, E + packed_offset(tok, k8, nkb));
+    float v[8];
+    frag_values<T>(f, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = k8 + e;
+      x[(size_t)m * d + k] = v[e];
+      Elem<T>::store(xw + (size_t)m * d + k, v[e] * norm[k]);
+      sq[k] = v[e] * v[e];
+    }
   }
   __syncthreads();
   for (int t = threadIdx.x; t < d / TILE_N; t += blockDim.x) {
@@ -65,12 +75,12 @@ __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, 
 
 // Per sequence: G[i] = argmax of row i over the LM-head partials; m = longest prefix with
 // tokens[i+1] == G[i]; emit tokens[1..m] and G[m]; optionally commit (len += m+1, hid = X[m]).
-__global__ void __launch_bounds__(256) accept_kernel(
+__global__ void __launch_bounds__(1024) accept_kernel(
     const float* amax_val, const int* amax_idx, int n_parts, int ld_amax, int R,
     const int* tokens, int* out_tokens, int* n_emit, int* next_tok, int commit, int* len,
     float* hid, const float* X, int d, int* argmax_out, int* err) {
-  __shared__ float rv[4];
-  __shared__ int ri[4];
+  __shared__ float rv[16];
+  __shared__ int ri[16];
   __shared__ int G[64];
   __shared__ int m_sh;
   const int b = blockIdx.x;
@@ -148,10 +158,16 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
   }
   ssh = block_sum(ssh, red);
   float sse = 0.f;
-  for (int k = threadIdx.x; k < Dd; k += blockDim.x) {
-    const float v = Elem<T>::load(table + packed_offset(row, k, nkb_table));
-    ebuf[k] = v;
-    sse += v * v;
+  for (int k8 = threadIdx.x * 8; k8 < Dd; k8 += blockDim.x * 8) {
+    Frag<T> f;
+    load_frag<T>(f, table + packed_offset(row, k8, nkb_table));
+    float v[8];
+    frag_values<T>(f, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ebuf[k8 + e] = v[e];
+      sse += v[e] * v[e];
+    }
   }
   sse = block_sum(sse, red);
   const float rh = 1.0f / sqrtf(ssh / (float)d + eps);
@@ -272,15 +288,16 @@ __global__ void fill_i32_kernel(int* p, int v, size_t n) {
 }  // namespace
 
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
-                        float* x, float* ssq, int vocab, int* err, hipStream_t st) {
+                        float* x, float* ssq, void* xw, const float* norm, int vocab, int* err,
+                        hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const size_t lds = (size_t)d * sizeof(float);
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), lds, st,
-                       (const bf16_t*)E, nkb, d, tokens, M, x, ssq, vocab, err);
+                       (const bf16_t*)E, nkb, d, tokens, M, x, ssq, (bf16_t*)xw, norm, vocab, err);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), lds, st, (const float*)E, nkb, d,
-                       tokens, M, x, ssq, vocab, err);
+                       tokens, M, x, ssq, (float*)xw, norm, vocab, err);
   return hipGetLastError();
 }
 
@@ -288,7 +305,7 @@ hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts
                          int B, int R, const int* tokens, int* out_tokens, int* n_emit,
                          int* next_tok, int commit, int* len, float* hid, const float* X, int d,
                          int* argmax_out, int* err, hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(256), 0, st, amax_val, amax_idx, n_parts,
+  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(1024), 0, st, amax_val, amax_idx, n_parts,
                      ld_amax, R, tokens, out_tokens, n_emit, next_tok, commit, len, hid, X, d,
                      argmax_out, err);
   return hipGetLastError();

@@ -20,8 +20,8 @@ using namespace specdec;
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr int TARGET_WAVES = 8192;  // waves per projection launch: 32 per CU on 256 CUs
-constexpr int MIN_KB_PER_WAVE = 4;  // at least 4 KB of bf16 weights per tile per wave
+constexpr int TARGET_WAVES = 2048;  // waves per projection launch (8 per CU on 256 CUs)
+constexpr int MIN_KB_PER_WAVE = 8;  // at least 8 KB of bf16 weights per tile per wave
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -53,10 +53,13 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   g.n_tiles = N / 16;
   g.NU = NU;
   g.n_units = cdiv(g.n_tiles, NU);
-  const int kw_cap = NU >= 4 ? 8 : 16;
+  // Measured on MI355X at the 31B shapes (M = 4): about TARGET_WAVES waves per launch, each
+  // streaming at least MIN_KB_PER_WAVE k-blocks, is best for one-tile units; the 4-tile argmax
+  // units (LM head, drafter table) stream best split 8 ways.
   int KW = 1;
   if (allow_split) {
-    KW = std::min({kw_cap, std::max(1, g.nkb / MIN_KB_PER_WAVE), cdiv(TARGET_WAVES, g.n_units)});
+    KW = NU >= 4 ? 8 : cdiv(TARGET_WAVES, g.n_units);
+    KW = std::min({KW, 16, std::max(1, g.nkb / MIN_KB_PER_WAVE)});
     KW = pow2_floor(std::max(1, std::min(KW, env_int("SPECDEC_MAX_KW", 16))));
   }
   g.KW = KW;
@@ -66,8 +69,8 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
 }
 
 struct Layout {
-  size_t x, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err;
-  size_t u, xd, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
+  size_t x, xw, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err;
+  size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
   size_t total;
 };
 
@@ -143,6 +146,7 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   };
   const int d = c->d_model, qd = c->n_q_heads * c->head_dim, Dd = c->d_dim;
   L.x = take((size_t)dm.Mx * d * 4);
+  L.xw = take((size_t)dm.Mx * d * dm.esz);
   L.q = take((size_t)dm.Mx * qd * 4);
   L.o = take((size_t)dm.Mx * qd * dm.esz);
   L.h = take((size_t)dm.Mx * c->ffn_dim * dm.esz);
@@ -154,6 +158,7 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.err = take(64);
   L.u = take((size_t)dm.Bx * (d + Dd) * dm.esz);
   L.xd = take((size_t)dm.Bx * Dd * 4);
+  L.xdw = take((size_t)dm.Bx * Dd * dm.esz);
   L.dh = take((size_t)dm.Bx * c->d_ffn * dm.esz);
   L.hnext = take((size_t)dm.Bx * d * 4);
   L.z = take((size_t)dm.Bx * c->n_centroids * 4);
@@ -235,14 +240,25 @@ GemmArgs base_args(specdec_ctx* x, const Gemm& g, int M) {
   return a;
 }
 
-// X prologue: the fp32 residual x normalised on load with the given norm weight.
-void norm_input(GemmArgs& a, const float* X, int ld, const float* ssq, int n, const float* w) {
-  a.X = X;
+// Normalised input: X = x * w in the storage type (written by the producer of x), results
+// scaled by the RMSNorm row scale formed from the producer's per-tile sums of squares.
+void norm_input(GemmArgs& a, const void* xw, int ld, const float* ssq, int n) {
+  a.X = xw;
   a.ldx = ld;
-  a.xssq = ssq;
-  a.n_ssq = n / 16;
-  a.scale_n = n;
-  a.xnorm = w;
+  a.yssq = ssq;
+  a.n_yssq = n / 16;
+  a.yscale_n = n;
+}
+
+// Residual update x (+)= y that also leaves y's sums of squares and y * w_next.
+void resid_output(GemmArgs& a, float* x, int ld, int accumulate, float* ssq, void* xw,
+                  const float* w_next) {
+  a.out = x;
+  a.ldo = ld;
+  a.accumulate = accumulate;
+  a.ssq = ssq;
+  a.xw_out = xw;
+  a.xw_norm = w_next;
 }
 
 #define HIP_TRY(expr)                               \
@@ -250,9 +266,9 @@ void norm_input(GemmArgs& a, const float* X, int ld, const float* ssq, int n, co
     if ((expr) != hipSuccess) return SPECDEC_E_HIP; \
   } while (0)
 
-int run(specdec_ctx* x, int cls, int NU, int xmode, int epi, const GemmArgs& a, hipStream_t st) {
+int run(specdec_ctx* x, int cls, int NU, int epi, const GemmArgs& a, hipStream_t st) {
   ProfScope ps(x, cls, st);
-  HIP_TRY(launch_gemm(dt_of(x), mt_for(a.M), NU, xmode, epi, a, st));
+  HIP_TRY(launch_gemm(dt_of(x), mt_for(a.M), NU, epi, a, st));
   return SPECDEC_OK;
 }
 
@@ -277,6 +293,10 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
   a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
   a.chunk = x->dm.chunk;
   a.n_chunks = x->dm.n_chunks;
+  int hi = 0;  // chunks that can hold a visible key, from the host-side bound on len
+  for (int b = 0; b < B; ++b) hi = std::max(hi, x->len_hi[b]);
+  a.n_launch = std::min(x->dm.n_chunks, std::max(1, cdiv(std::min(hi + R - 1 + key_off, c.max_ctx),
+                                                          x->dm.chunk)));
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
   ProfScope ps(x, cls, st);
   HIP_TRY(launch_attention(dt_of(x), a, st));
@@ -361,16 +381,18 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
   const int M = B * R;
   const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
   float* X = at<float>(x, x->lay.x);
+  void* XW = x->ws + x->lay.xw;
   float* ssq = at<float>(x, x->lay.ssq);
   int* err = at<int>(x, x->lay.err);
-  HIP_TRY(launch_embed(dt_of(x), x->w.embed, x->g_head.nkb, d, tokens, M, X, ssq, c.vocab, err, st));
+  auto lw = [&](int l, int slot) { return (const float*)x->lw[(size_t)l * SPECDEC_N_LAYER_TENSORS + slot]; };
+  HIP_TRY(launch_embed(dt_of(x), x->w.embed, x->g_head.nkb, d, tokens, M, X, ssq, XW,
+                       lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st));
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
   int rc;
   for (int l = 0; l < c.n_layers; ++l) {
-    const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
     {  // fused q/k/v projection + RoPE + KV append (tentative: len is not moved)
       GemmArgs a = base_args(x, x->g_qkv[l], M);
-      norm_input(a, X, d, ssq, d, (const float*)t[SPECDEC_LW_ATTN_NORM]);
+      norm_input(a, XW, d, ssq, d);
       a.qout = at<float>(x, x->lay.q);
       a.kcache = (char*)x->kv_k + per_layer * l * x->dm.esz;
       a.vcache = (char*)x->kv_v + per_layer * l * x->dm.esz;
@@ -383,46 +405,41 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
       a.max_ctx = c.max_ctx;
       a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
       a.theta = c.rope_theta;
-      if ((rc = run(x, 2, 1, XM_NORM, EPI_ROPE, a, st))) return rc;
+      if ((rc = run(x, 2, 1, EPI_ROPE, a, st))) return rc;
     }
     if ((rc = attention(x, l, B, R, 1, 4, st))) return rc;
-    {  // output projection + residual
+    {  // output projection + residual; leaves x * ffn_norm for the FFN
       GemmArgs a = base_args(x, x->g_o[l], M);
       a.X = x->ws + x->lay.o;
       a.ldx = qd;
-      a.out = X;
-      a.ldo = d;
-      a.accumulate = 1;
-      a.ssq = ssq;
-      if ((rc = run(x, 3, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+      resid_output(a, X, d, 1, ssq, XW, lw(l, SPECDEC_LW_FFN_NORM));
+      if ((rc = run(x, 3, 1, EPI_STORE, a, st))) return rc;
     }
     {  // gate/up projection + SiLU-gated product
       GemmArgs a = base_args(x, x->g_gu[l], M);
-      norm_input(a, X, d, ssq, d, (const float*)t[SPECDEC_LW_FFN_NORM]);
+      norm_input(a, XW, d, ssq, d);
       a.hout = x->ws + x->lay.h;
       a.ldh = c.ffn_dim;
-      if ((rc = run(x, 0, 2, XM_NORM, EPI_SILU, a, st))) return rc;
+      if ((rc = run(x, 0, 2, EPI_SILU, a, st))) return rc;
     }
-    {  // down projection + residual
+    {  // down projection + residual; leaves x * (next attention norm | final norm)
       GemmArgs a = base_args(x, x->g_down[l], M);
       a.X = x->ws + x->lay.h;
       a.ldx = c.ffn_dim;
-      a.out = X;
-      a.ldo = d;
-      a.accumulate = 1;
-      a.ssq = ssq;
-      if ((rc = run(x, 1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+      const float* wn = l + 1 < c.n_layers ? lw(l + 1, SPECDEC_LW_ATTN_NORM) : x->w.final_norm;
+      resid_output(a, X, d, 1, ssq, XW, wn);
+      if ((rc = run(x, 1, 1, EPI_STORE, a, st))) return rc;
     }
   }
   {  // final norm + tied LM head with per-unit argmax partials
     GemmArgs a = base_args(x, x->g_head, M);
-    norm_input(a, X, d, ssq, d, x->w.final_norm);
+    norm_input(a, XW, d, ssq, d);
     a.amax_val = at<float>(x, x->lay.amax_v);
     a.amax_idx = at<int>(x, x->lay.amax_i);
     a.ld_amax = x->dm.parts;
     a.logits = logits;
     a.ld_logits = c.vocab;
-    if ((rc = run(x, 5, 4, XM_NORM, EPI_ARGMAX, a, st))) return rc;
+    if ((rc = run(x, 5, 4, EPI_ARGMAX, a, st))) return rc;
   }
   if (argmax) {
     HIP_TRY(launch_accept(at<float>(x, x->lay.amax_v), at<int>(x, x->lay.amax_i), x->dm.parts,
@@ -476,11 +493,13 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
   const int S = c.vocab / c.n_centroids;  // tokens per cluster
   const int tpc = S / 16, upc = S / 64;   // tiles / argmax units per cluster
   float* xd = at<float>(x, x->lay.xd);
+  void* xdw = x->ws + x->lay.xdw;
   float* sd = at<float>(x, x->lay.ssq_d);
   float* hnext = at<float>(x, x->lay.hnext);
   int* dtok = at<int>(x, x->lay.dtok);
   int* err = at<int>(x, x->lay.err);
   const int src = c.kv_src_layer;
+  auto dw = [&](int l, int slot) { return (const float*)x->dw[(size_t)l * SPECDEC_N_DRAFT_TENSORS + slot]; };
   int rc;
   for (int j = 1; j <= K; ++j) {
     const float* h = (j == 1) ? x->hid : hnext;
@@ -488,20 +507,17 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
     HIP_TRY(launch_draft_input(dt, h, tok, x->w.table, x->g_table.nkb, x->w.vocab_row, c.vocab,
                                x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u, B,
                                err, st));
-    {  // input projection of [rms(h); rms(e)]
+    {  // input projection of [rms(h); rms(e)]; leaves x * n1 of the first drafter layer
       GemmArgs a = base_args(x, x->g_in, B);
       a.X = x->ws + x->lay.u;
       a.ldx = d + Dd;
-      a.out = xd;
-      a.ldo = Dd;
-      a.ssq = sd;
-      if ((rc = run(x, -1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+      resid_output(a, xd, Dd, 0, sd, xdw, dw(0, SPECDEC_DW_N1));
+      if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
     }
     for (int l = 0; l < c.d_layers; ++l) {
-      const void* const* t = x->dw.data() + (size_t)l * SPECDEC_N_DRAFT_TENSORS;
       {  // q projection + RoPE at len + j - 1
         GemmArgs a = base_args(x, x->g_dq[l], B);
-        norm_input(a, xd, Dd, sd, Dd, (const float*)t[SPECDEC_DW_N1]);
+        norm_input(a, xdw, Dd, sd, Dd);
         a.qout = at<float>(x, x->lay.q);
         a.len = x->len;
         a.rows_per_seq = 1;
@@ -511,76 +527,71 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         a.hd = c.head_dim;
         a.max_ctx = c.max_ctx;
         a.theta = c.rope_theta;
-        if ((rc = run(x, -1, 1, XM_NORM, EPI_ROPE, a, st))) return rc;
+        if ((rc = run(x, -1, 1, EPI_ROPE, a, st))) return rc;
       }
       // cross-attention into the target's cache, keys [0, len)
       if ((rc = attention(x, src, B, 1, 0, -1, st))) return rc;
-      {
+      {  // o projection + residual; leaves x * n2
         GemmArgs a = base_args(x, x->g_do[l], B);
         a.X = x->ws + x->lay.o;
         a.ldx = qd;
-        a.out = xd;
-        a.ldo = Dd;
-        a.accumulate = 1;
-        a.ssq = sd;
-        if ((rc = run(x, -1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+        resid_output(a, xd, Dd, 1, sd, xdw, dw(l, SPECDEC_DW_N2));
+        if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
       }
       {
         GemmArgs a = base_args(x, x->g_dgu[l], B);
-        norm_input(a, xd, Dd, sd, Dd, (const float*)t[SPECDEC_DW_N2]);
+        norm_input(a, xdw, Dd, sd, Dd);
         a.hout = x->ws + x->lay.dh;
         a.ldh = c.d_ffn;
-        if ((rc = run(x, -1, 2, XM_NORM, EPI_SILU, a, st))) return rc;
+        if ((rc = run(x, -1, 2, EPI_SILU, a, st))) return rc;
       }
-      {
+      {  // down projection + residual; leaves x * (next n1 | n_f)
         GemmArgs a = base_args(x, x->g_ddown[l], B);
         a.X = x->ws + x->lay.dh;
         a.ldx = c.d_ffn;
-        a.out = xd;
-        a.ldo = Dd;
-        a.accumulate = 1;
-        a.ssq = sd;
-        if ((rc = run(x, -1, 1, XM_ELEM, EPI_STORE, a, st))) return rc;
+        const float* wn = l + 1 < c.d_layers ? dw(l + 1, SPECDEC_DW_N1) : x->w.norm_f;
+        resid_output(a, xd, Dd, 1, sd, xdw, wn);
+        if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
       }
     }
-    {  // next hidden input: W_back . rms(x) * n_f
+    {  // next hidden input: W_back . (rms(x) * n_f)
       GemmArgs a = base_args(x, x->g_back, B);
-      norm_input(a, xd, Dd, sd, Dd, x->w.norm_f);
+      norm_input(a, xdw, Dd, sd, Dd);
       a.out = hnext;
       a.ldo = d;
-      if ((rc = run(x, -1, 1, XM_NORM, EPI_STORE, a, st))) return rc;
+      if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
     }
     int parts_per_seq, seq_off, ld;
     {
       ProfScope ps(x, 6, st);
       if (head_mode == SPECDEC_HEAD_FULL) {
         GemmArgs a = base_args(x, x->g_table, B);
-        norm_input(a, xd, Dd, sd, Dd, x->w.norm_f);
+        norm_input(a, xdw, Dd, sd, Dd);
         a.amax_val = at<float>(x, x->lay.d_amax_v);
         a.amax_idx = at<int>(x, x->lay.d_amax_i);
         a.ld_amax = x->dm.parts;
         a.idx_map = x->w.row_vocab;
-        HIP_TRY(launch_gemm(dt, mt_for(B), 4, XM_NORM, EPI_ARGMAX, a, st));
+        HIP_TRY(launch_gemm(dt, mt_for(B), 4, EPI_ARGMAX, a, st));
         parts_per_seq = x->dm.parts;
         seq_off = 0;
         ld = x->dm.parts;
       } else {
         GemmArgs zc = base_args(x, x->g_cent, B);
-        norm_input(zc, xd, Dd, sd, Dd, x->w.norm_f);
+        norm_input(zc, xdw, Dd, sd, Dd);
         zc.out = at<float>(x, x->lay.z);
         zc.ldo = c.n_centroids;
-        HIP_TRY(launch_gemm(dt, mt_for(B), 1, XM_NORM, EPI_STORE, zc, st));
+        HIP_TRY(launch_gemm(dt, mt_for(B), 1, EPI_STORE, zc, st));
         HIP_TRY(launch_cluster_select(at<float>(x, x->lay.z), c.n_centroids, k_c, B, tpc, upc,
                                       at<int>(x, x->lay.utile), at<int>(x, x->lay.urow), err, st));
         GemmArgs a = base_args(x, x->g_clu, B);
         a.n_units = B * k_c * upc;
         a.unit_tile = at<int>(x, x->lay.utile);
         a.unit_row = at<int>(x, x->lay.urow);
-        norm_input(a, xd, Dd, sd, Dd, x->w.norm_f);
+        norm_input(a, xdw, Dd, sd, Dd);
         a.amax_val = at<float>(x, x->lay.d_amax_v);
         a.amax_idx = at<int>(x, x->lay.d_amax_i);
         a.idx_map = x->w.row_vocab;
-        HIP_TRY(launch_gemm(dt, mt_for(B), 4, XM_NORM, EPI_ARGMAX, a, st));
+        HIP_TRY(launch_gemm(dt, mt_for(B), 4, EPI_ARGMAX, a, st));
         parts_per_seq = k_c * upc;
         seq_off = k_c * upc;
         ld = 0;  // listed units are stored by unit index

@@ -55,9 +55,11 @@ def draft_substep_bytes(cfg, keys: float, k_c: int = 1) -> float:
 
 
 def gate_up_bytes(cfg, M: int) -> float:
-    """Algorithmic bytes of one gate/up GEMM launch: the 2F x d bf16 weights once, the fp32
-    residual rows in, the bf16 gated product out."""
-    return 2 * cfg.ffn_dim * cfg.d_model * 2 + M * cfg.d_model * 4 + M * cfg.ffn_dim * 2
+    """Algorithmic bytes of one gate/up GEMM launch: the 2F x d bf16 weights once, the M bf16
+    rows of x times the norm weight and their per-16-column fp32 sums of squares in, the M bf16
+    gated-product rows out."""
+    d, F = cfg.d_model, cfg.ffn_dim
+    return 2 * F * d * 2 + M * d * 2 + M * (d // 16) * 4 + M * F * 2
 
 
 def src_sha(path: str) -> str:
@@ -146,7 +148,7 @@ def cpu_baseline(cfg, tokens_per_step: float, K: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="31b", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--p", type=float, default=None)
@@ -293,8 +295,10 @@ def main() -> int:
         lb = gate_up_bytes(cfg, K + 1)
         achieved = lb / (launch_ms * 1e-3) / 1e9
         traffic = load_traffic(f"gemm_gate_up_{args.config}", lb)
+        kw, units, nw, groups = eng.query_split(0)
         res["roofline"] = {
-            "kernel": "gemm_kernel<bf16,MT=1,NU=2,XM_NORM,EPI_SILU> (FFN gate/up, verify M=4)",
+            "kernel": f"gemm_kernel<bf16, 1, 2, 2, {nw}> (FFN gate/up + SiLU product, verify "
+                      f"M={K + 1}, grid {groups * nw * 64} work-items, split-K {kw})",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -67,7 +67,9 @@ enum {
 typedef struct {
   /* target decoder (pre-norm RMSNorm, RoPE, gated SiLU FFN, tied LM head) */
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
-  /* mixture of experts: n_experts == 0 means dense (MoE is reported as unsupported for now) */
+  /* mixture of experts: n_experts == 0 means a dense FFN of ffn_dim; otherwise each layer's FFN
+     is the weighted sum of its top_k of n_experts gated experts of width expert_ffn plus a
+     shared gated FFN of width shared_ffn (ffn_dim unused) */
   int32_t n_experts, top_k, expert_ffn, shared_ffn;
   /* drafter: d_layers layers of width d_dim, FFN d_ffn, n_centroids equal clusters of the
      vocabulary, cross-attending to target layer kv_src_layer (-1 = last) */
@@ -86,9 +88,15 @@ enum {
   SPECDEC_LW_QKV = 1,       /* packed (ROPE) [Hq*hd + 2*Hkv*hd][d_model]: Wq rows, Wk rows, Wv rows */
   SPECDEC_LW_O = 2,         /* packed [d_model][Hq*hd] */
   SPECDEC_LW_FFN_NORM = 3,  /* float [d_model] */
-  SPECDEC_LW_GATE_UP = 4,   /* packed (GATE_UP) [2*ffn_dim][d_model] */
-  SPECDEC_LW_DOWN = 5,      /* packed [d_model][ffn_dim] */
-  SPECDEC_N_LAYER_TENSORS = 6
+  SPECDEC_LW_GATE_UP = 4,   /* packed (GATE_UP) [2*F][d_model], F = ffn_dim (dense) or
+                               shared_ffn (the shared FFN of a mixture-of-experts layer) */
+  SPECDEC_LW_DOWN = 5,      /* packed [d_model][F] */
+  /* mixture-of-experts layers only (NULL for a dense model): */
+  SPECDEC_LW_ROUTER = 6,    /* packed [n_experts][d_model] */
+  SPECDEC_LW_EXP_GATE_UP = 7, /* n_experts packed (GATE_UP) [2*expert_ffn][d_model] matrices,
+                                 back to back in expert order */
+  SPECDEC_LW_EXP_DOWN = 8,  /* n_experts packed [d_model][expert_ffn] matrices, back to back */
+  SPECDEC_N_LAYER_TENSORS = 9
 };
 
 /* Per-layer tensor slots of specdec_weights.d_layers (d_layers * SPECDEC_N_DRAFT_TENSORS). */
@@ -142,10 +150,11 @@ size_t specdec_kv_elems(const specdec_config* cfg);
      workspace   specdec_workspace_bytes(cfg) bytes, 256-byte aligned
    Enqueues one small kernel on `stream` that zeroes the workspace's arrival counters and the
    device error word.  Errors: SPECDEC_E_INVAL (null pointers, shapes not multiples of the
-   tile: d_model, Hq*hd, ffn_dim, d_dim, d_ffn % 32; head_dim % 16, head_dim <= 256;
-   vocab % 64; vocab / n_centroids % 64; n_centroids % 16; max_batch*max_rows <= 64;
-   max_rows <= 64; max_ctx % 8), SPECDEC_E_UNSUPPORTED (n_experts > 0, head_dim not one of
-   64, 128, 176, 256). */
+   tile: d_model, Hq*hd, ffn_dim (dense), expert_ffn and shared_ffn (MoE), d_dim, d_ffn % 32;
+   head_dim % 16, head_dim <= 256; vocab % 64; vocab / n_centroids % 64; n_centroids % 16;
+   max_batch*max_rows <= 64; max_rows <= 64; max_ctx % 8; MoE: n_experts <= 256 and % 16,
+   1 <= top_k <= min(16, n_experts)), SPECDEC_E_UNSUPPORTED (head_dim not one of 64, 128,
+   176, 256). */
 int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv_k, void* kv_v,
                    int32_t* len, float* hid, void* workspace, size_t workspace_bytes,
                    void* stream, specdec_ctx** out);
@@ -195,7 +204,9 @@ int specdec_kv_commit(specdec_ctx* ctx, int32_t B, const int32_t* n_commit, void
 
 /* Packs a logical row-major matrix src [n][kd] (device, dtype) into the streaming tile layout
    dst (device, n*kd elements).  kind: SPECDEC_PACK_*; head_dim for ROPE; split_rows = F for
-   GATE_UP (n = 2F).  Requires n % 16 == 0, kd % 32 == 0.  Setup-time helper. */
+   GATE_UP: n = 2F, or n = G*2F for G stacked [2F][kd] matrices (experts: gate rows then up
+   rows each), packed group by group.  Requires n % 16 == 0, kd % 32 == 0.  A plain stack of G
+   [n/G][kd] matrices packs as one [n][kd] PLAIN matrix.  Setup-time helper. */
 int specdec_pack_matrix(const void* src, void* dst, int32_t n, int32_t kd, int32_t dtype,
                         int32_t kind, int32_t head_dim, int32_t split_rows, void* stream);
 
@@ -206,15 +217,20 @@ int specdec_set_len_bound(specdec_ctx* ctx, const int32_t* host_len, int32_t B);
 int specdec_read_device_error(specdec_ctx* ctx, int32_t* host_word, int32_t clear, void* stream);
 
 /* Per-launch timing of one kernel class, for roofline reporting: after specdec_profile_start,
-   every launch of that class is bracketed by HIP events on the launch stream (up to `capacity`
-   launches).  specdec_profile_read synchronises and returns the durations in ms.
+   every launch of that class is timed (up to `capacity` launches), a single-kernel GEMM launch by
+   HIP events attached to its own dispatch, the others by events recorded on the launch stream
+   around their kernels.  specdec_profile_read synchronises and returns the durations in ms.
    Classes: 0 gate/up GEMM, 1 down GEMM, 2 qkv GEMM, 3 o GEMM, 4 attention, 5 LM head,
-   6 drafter head.  Not for use under graph capture. */
+   6 drafter head, 7 routed-expert gate/up GEMM, 8 routed-expert down GEMM.  Not for use under
+   graph capture. */
 int specdec_profile_start(specdec_ctx* ctx, int32_t kernel_class, int32_t capacity);
 int specdec_profile_read(specdec_ctx* ctx, float* ms_out, int32_t max, int32_t* n_out);
 
-/* Split-K factor the context uses for a class (tests / reports). */
-int specdec_query_split(specdec_ctx* ctx, int32_t kernel_class, int32_t* splits, int32_t* units);
+/* Launch shape the context uses for a GEMM class (classes 0, 1, 2, 3, 5 above; tests and
+   reports; classes 7, 8 for a mixture-of-experts model): split-K factor, work units, waves per
+   workgroup and workgroups of one launch (for 7 and 8: the upper bound, all experts). */
+int specdec_query_split(specdec_ctx* ctx, int32_t kernel_class, int32_t* splits, int32_t* units,
+                        int32_t* waves, int32_t* groups);
 
 const char* specdec_error_string(int code);
 

@@ -26,6 +26,7 @@ from workloads import inject_draw, inject_threshold
 
 __all__ = [
     "as_f64", "rmsnorm", "silu", "rope", "attention", "dense_ffn", "moe_ffn", "moe_route",
+    "moe_route_margin",
     "KVCache", "decoder_layer_row", "target_row", "lm_head", "argmax_first", "top2_margin",
     "greedy_generate", "prefill", "verify", "accept", "commit", "head_full",
     "head_clustered", "drafter_substep", "draft", "inject", "spec_generate", "SpecStats",
@@ -113,10 +114,21 @@ def moe_route(router: np.ndarray, b: np.ndarray, top_k: int):
     return sel, w
 
 
-def moe_ffn(lw: dict, cfg, b: np.ndarray) -> np.ndarray:
+def moe_route_margin(router: np.ndarray, b: np.ndarray, top_k: int) -> float:
+    """Gap between the top_k-th largest router logit and the next one.  The expert choice is an
+    integer decided from floating-point logits: where this gap is within the logits' rounding
+    error, either choice is a correct result."""
+    r = np.sort(router @ b)[::-1]
+    return float(r[top_k - 1] - r[top_k]) if top_k < r.shape[0] else math.inf
+
+
+def moe_ffn(lw: dict, cfg, b: np.ndarray, trace: list | None = None) -> np.ndarray:
     """Mixture-of-experts FFN: sum over the top-k experts (ascending id) of w_e * FFN_e(b), plus a
     shared gated FFN that every token uses.  The pages say only that the 26B MoE has a batch-1
-    "routing challenge" ([digest] "Inside the MTP drafter"); routing details are a reading."""
+    "routing challenge" ([digest] "Inside the MTP drafter"); routing details are a reading.
+    `trace`, when given, receives the routing margin (moe_route_margin)."""
+    if trace is not None:
+        trace.append(moe_route_margin(lw["router"], b, cfg.top_k))
     sel, w = moe_route(lw["router"], b, cfg.top_k)
     y = np.zeros_like(b)
     for e, we in zip(sel, w):
@@ -156,8 +168,9 @@ class KVCache:
 
 
 def decoder_layer_row(lw: dict, cfg, Kl: np.ndarray, Vl: np.ndarray, x: np.ndarray,
-                      pos: int) -> np.ndarray:
-    """One decoder layer for one token at position pos.  Writes k, v at pos, attends keys [0, pos]."""
+                      pos: int, trace: list | None = None) -> np.ndarray:
+    """One decoder layer for one token at position pos.  Writes k, v at pos, attends keys [0, pos].
+    `trace` (mixture of experts only) receives the layer's routing margin."""
     hd = cfg.head_dim
     a = rmsnorm(x, lw["attn_norm"], cfg.rms_eps)
     q = (lw["wq"] @ a).reshape(cfg.n_q_heads, hd)
@@ -171,7 +184,7 @@ def decoder_layer_row(lw: dict, cfg, Kl: np.ndarray, Vl: np.ndarray, x: np.ndarr
     x = x + lw["wo"] @ o.reshape(-1)
     b = rmsnorm(x, lw["ffn_norm"], cfg.rms_eps)
     if cfg.is_moe:
-        return x + moe_ffn(lw, cfg, b)
+        return x + moe_ffn(lw, cfg, b, trace)
     return x + dense_ffn(lw["wg"], lw["wu"], lw["wd"], b)
 
 

@@ -14,9 +14,11 @@ HEAD_CLUSTERED, HEAD_FULL = 0, 1
 ACCEPT_COMMIT = 1
 DEVERR_CAPACITY, DEVERR_NAN, DEVERR_TOKEN = 1, 2, 4
 PACK_PLAIN, PACK_ROPE, PACK_GATE_UP = 0, 1, 2
-LW_ATTN_NORM, LW_QKV, LW_O, LW_FFN_NORM, LW_GATE_UP, LW_DOWN, N_LAYER_TENSORS = range(7)
+(LW_ATTN_NORM, LW_QKV, LW_O, LW_FFN_NORM, LW_GATE_UP, LW_DOWN, LW_ROUTER, LW_EXP_GATE_UP, LW_EXP_DOWN,
+ N_LAYER_TENSORS) = range(10)
 DW_N1, DW_Q, DW_O, DW_N2, DW_GATE_UP, DW_DOWN, N_DRAFT_TENSORS = range(7)
-PROF_GATE_UP, PROF_DOWN, PROF_QKV, PROF_O, PROF_ATTN, PROF_HEAD, PROF_DRAFT_HEAD = range(7)
+(PROF_GATE_UP, PROF_DOWN, PROF_QKV, PROF_O, PROF_ATTN, PROF_HEAD, PROF_DRAFT_HEAD, PROF_EXP_GATE_UP,
+ PROF_EXP_DOWN) = range(9)
 
 EXPORTS = [
     "specdec_workspace_bytes", "specdec_kv_elems", "specdec_create", "specdec_destroy",
@@ -72,7 +74,7 @@ def load(path: str = LIB_PATH):
         "specdec_read_device_error": (C.c_int, [vp, P(i32), i32, vp]),
         "specdec_profile_start": (C.c_int, [vp, i32, i32]),
         "specdec_profile_read": (C.c_int, [vp, P(C.c_float), i32, P(i32)]),
-        "specdec_query_split": (C.c_int, [vp, i32, P(i32), P(i32)]),
+        "specdec_query_split": (C.c_int, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
         "specdec_error_string": (C.c_char_p, [C.c_int]),
     }
     for name, (res, args) in sig.items():

@@ -21,6 +21,8 @@
 
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -41,15 +43,16 @@ __device__ __forceinline__ void load_w(Frag<T>& f, const T* W, size_t tile, int 
   }
 }
 
-// X fragment of lane `lane` for k-block kb: row m = mt*16 + lane%16, k = kb*32 + (lane/16)*8.
+// X fragment of lane `lane` for k-block kb: X row r (the row that local row mt*16 + lane%16
+// reads; -1 = none), k = kb*32 + (lane/16)*8.
 template <typename T>
-__device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int m, int kb, int lane) {
-  if (m >= a.M) {
+__device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int r, int kb, int lane) {
+  if (r < 0) {
     zero_frag(f);
     return;
   }
   const int k = kb * TILE_K + ((lane >> 4) << 3);
-  load_frag<T>(f, reinterpret_cast<const T*>(a.X) + (size_t)m * a.ldx + k);
+  load_frag<T>(f, reinterpret_cast<const T*>(a.X) + (size_t)r * a.ldx + k);
 }
 
 __device__ __forceinline__ float sum16(float v) {
@@ -69,32 +72,51 @@ __device__ __forceinline__ void argmax16(float& v, int& i) {
   }
 }
 
-// Row scales 1/sqrt(sum_t yssq[t][m] / yscale_n + eps) for the rows this lane holds.  The sum
-// runs lane-strided then through a fixed butterfly, identically for every caller.
+// Row scales 1/sqrt(sum_t yssq[t][r] / yscale_n + eps) for the rows this lane holds (r = the X
+// row a local row reads: xr[mt] holds it for local row mt*16 + lane%16).  The sum runs
+// lane-strided then through a fixed butterfly, identically for every caller.
 template <int MT>
-__device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, float (&sc)[MT][4]) {
+__device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const int (&xr)[MT],
+                                           float (&sc)[MT][4]) {
   float mine = 1.f;
-  for (int m = 0; m < a.M; ++m) {
-    float s = 0.f;
-    for (int t = lane; t < a.n_yssq; t += WAVE) s += a.yssq[(size_t)t * a.M + m];
-    s = wave_sum(s);
-    if (lane == m) mine = 1.0f / sqrtf(s / (float)a.yscale_n + a.eps);
+  // up to 16 rows at a time, all their loads independent; per row the same order as one row alone
+  for (int m0 = 0; m0 < a.M; m0 += 16) {
+    const int nr = min(16, a.M - m0);
+    float s[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    for (int t = lane; t < a.n_yssq; t += WAVE) {
+      const float* p = a.yssq + (size_t)t * a.M + m0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r < nr) s[r] += p[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r < nr) {
+        const float v = wave_sum(s[r]);
+        if (lane == m0 + r) mine = 1.0f / sqrtf(v / (float)a.yscale_n + a.eps);
+      }
+    }
   }
   const int rgrp = (lane >> 4) << 2;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sc[mt][v] = __shfl(mine, (mt * 16 + rgrp + v) & 63, WAVE);
+    for (int v = 0; v < 4; ++v) {
+      const int r = __shfl(xr[mt], rgrp + v, WAVE);
+      sc[mt][v] = __shfl(mine, r < 0 ? 0 : (r & 63), WAVE);
+    }
 }
 
 template <typename T, int MT, int NU, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
-                                         int tile0, int lane) {
+                                         int tile0, int grp, const int (&xr)[MT], int lane) {
   const int c16 = lane & 15;
   const int rgrp = (lane >> 4) << 2;
   if (a.yssq) {
     float sc[MT][4];
-    row_scales<MT>(a, lane, sc);
+    row_scales<MT>(a, lane, xr, sc);
 #pragma unroll
     for (int t = 0; t < NU; ++t)
 #pragma unroll
@@ -115,6 +137,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
         if (m < a.M) {
           float* o = a.out + (size_t)m * a.ldo + col;
           float y = acc[0][mt][v];
+          if (a.addend) {
+            const float* ad = a.addend + (size_t)m * a.add_n * a.ldo + col;
+            float t = ad[0];
+            for (int k = 1; k < a.add_n; ++k) t += ad[(size_t)k * a.ldo];
+            y = t + y;
+          }
           if (a.accumulate) y = *o + y;
           *o = y;
           sq = y * y;
@@ -167,6 +195,26 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
                                    : ((size_t)g * a.hd + dim) * a.max_ctx + pos;
             Elem<T>::store(cache + off, y);
           }
+        }
+      }
+  } else if constexpr (EPI == EPI_SILU_G || EPI == EPI_STORE_G) {
+    const int lt = tile0 - grp * a.tiles_per_group;  // tile within the group's matrix
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + rgrp + v;
+        if (m >= a.M) continue;
+        const int orow = a.orow_map[(size_t)grp * a.M + m];
+        if (orow < 0) continue;
+        if constexpr (EPI == EPI_SILU_G) {
+          const float g = acc[0][mt][v];
+          const float up = acc[1][mt][v];
+          const float h = g / (1.0f + expf(-g)) * up;
+          Elem<T>::store(reinterpret_cast<T*>(a.hout) + (size_t)orow * a.ldh + (lt >> 1) * TILE_N + c16, h);
+        } else {
+          a.out[(size_t)orow * a.ldo + lt * TILE_N + c16] =
+              acc[0][mt][v] * a.orow_wt[(size_t)grp * a.M + m];
         }
       }
   } else if constexpr (EPI == EPI_SILU) {
@@ -237,12 +285,32 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   __shared__ f32x4 red[NW * NU * 64];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x >> 6;
+  constexpr bool GROUPED = EPI == EPI_SILU_G || EPI == EPI_STORE_G;
   const int KW = a.KW;
   const int ks = wid % KW;
   const int u = blockIdx.x * (NW / KW) + wid / KW;
-  const int n_units = a.n_units_dev ? min(*a.n_units_dev, a.n_units) : a.n_units;
+  int n_units = a.n_units;
+  if constexpr (GROUPED) n_units = min(n_units, a.n_groups_dev[0] * a.units_per_group);
+  else if (a.n_units_dev) n_units = min(*a.n_units_dev, n_units);
   const bool active = u < n_units;
-  const int tile0 = active ? (a.unit_tile ? a.unit_tile[u] : u * NU) : 0;
+  int tile0 = 0, grp = 0;
+  if (active) {
+    if constexpr (GROUPED) {
+      const int gi = u / a.units_per_group;
+      grp = a.group_list[gi];
+      tile0 = grp * a.tiles_per_group + (u - gi * a.units_per_group) * NU;
+    } else {
+      tile0 = a.unit_tile ? a.unit_tile[u] : u * NU;
+    }
+  }
+  // X row read by local row mt*16 + lane%16 (-1: none)
+  int xr[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + (lane & 15);
+    if constexpr (GROUPED) xr[mt] = (active && m < a.M) ? a.xrow_map[(size_t)grp * a.M + m] : -1;
+    else xr[mt] = m < a.M ? m : -1;
+  }
   const int kb0 = ks * a.kb_per_split;
   const int kb1 = min(a.nkb, kb0 + a.kb_per_split);
   const T* W = reinterpret_cast<const T*>(a.W);
@@ -274,7 +342,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
       for (int uu = 0; uu < U; ++uu)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          load_x<T>(x[st][uu][mt], a, mt * 16 + (lane & 15), kbase + uu, lane);
+          load_x<T>(x[st][uu][mt], a, xr[mt], kbase + uu, lane);
     };
     auto mul_batch = [&](int st) {
 #pragma unroll
@@ -305,7 +373,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
         else zero_frag(w[t]);
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) load_x<T>(x[mt], a, mt * 16 + (lane & 15), kb, lane);
+      for (int mt = 0; mt < MT; ++mt) load_x<T>(x[mt], a, xr[mt], kb, lane);
 #pragma unroll
       for (int t = 0; t < NU; ++t)
 #pragma unroll
@@ -335,54 +403,63 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     if (ks != 0) return;
   }
   if (!active) return;
-  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, lane);
+  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, lane);
 }
 
 template <typename T, int MT, int NU, int EPI, int NW>
-hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   const int upw = NW / a.KW;
   dim3 grid((a.n_units + upw - 1) / upw), block(NW * 64);
-  hipLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW>), grid, block, 0, st, a);
+  if (tm)
+    hipExtLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW>), grid, block, 0, st, tm->start,
+                          tm->stop, 0, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int MT, int NU, int EPI>
-hipError_t launch_nw(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_nw(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   if constexpr (NU < 4) {
-    if (a.NW == 16) return launch_t<T, MT, NU, EPI, 16>(a, st);
+    if (a.NW == 16) return launch_t<T, MT, NU, EPI, 16>(a, st, tm);
   }
-  if (a.NW == 8) return launch_t<T, MT, NU, EPI, 8>(a, st);
-  if (a.NW == 4) return launch_t<T, MT, NU, EPI, 4>(a, st);
+  if (a.NW == 8) return launch_t<T, MT, NU, EPI, 8>(a, st, tm);
+  if (a.NW == 4) return launch_t<T, MT, NU, EPI, 4>(a, st, tm);
   return hipErrorInvalidValue;
 }
 
 template <typename T, int MT>
-hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st) {
-  if (epi == EPI_STORE && NU == 1) return launch_nw<T, MT, 1, EPI_STORE>(a, st);
-  if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE>(a, st);
-  if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU>(a, st);
-  if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX>(a, st);
+hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st,
+                       const LaunchTiming* tm) {
+  if (epi == EPI_STORE && NU == 1) return launch_nw<T, MT, 1, EPI_STORE>(a, st, tm);
+  if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE>(a, st, tm);
+  if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU>(a, st, tm);
+  if (epi == EPI_SILU_G && NU == 2) return launch_nw<T, MT, 2, EPI_SILU_G>(a, st, tm);
+  if (epi == EPI_STORE_G && NU == 1) return launch_nw<T, MT, 1, EPI_STORE_G>(a, st, tm);
+  if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX>(a, st, tm);
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t dispatch_mt(int MT, int NU, int epi, const GemmArgs& a, hipStream_t st) {
+hipError_t dispatch_mt(int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
+                       const LaunchTiming* tm) {
   switch (MT) {
-    case 1: return dispatch_epi<T, 1>(NU, epi, a, st);
-    case 2: return dispatch_epi<T, 2>(NU, epi, a, st);
-    case 4: return dispatch_epi<T, 4>(NU, epi, a, st);
+    case 1: return dispatch_epi<T, 1>(NU, epi, a, st, tm);
+    case 2: return dispatch_epi<T, 2>(NU, epi, a, st, tm);
+    case 4: return dispatch_epi<T, 4>(NU, epi, a, st, tm);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
+                       const LaunchTiming* tm) {
   if (a.n_units <= 0) return hipSuccess;
   if (a.KW < 1 || (a.NW != 4 && a.NW != 8 && a.NW != 16) || a.NW % a.KW) return hipErrorInvalidValue;
   if (a.M > MT * 16) return hipErrorInvalidValue;
-  return dtype == DT_BF16 ? dispatch_mt<bf16_t>(MT, NU, epi, a, st)
-                          : dispatch_mt<float>(MT, NU, epi, a, st);
+  return dtype == DT_BF16 ? dispatch_mt<bf16_t>(MT, NU, epi, a, st, tm)
+                          : dispatch_mt<float>(MT, NU, epi, a, st, tm);
 }
 
 }  // namespace specdec

@@ -7,7 +7,16 @@
 namespace specdec {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
-enum Epi { EPI_STORE = 0, EPI_ROPE = 1, EPI_SILU = 2, EPI_ARGMAX = 3 };
+enum Epi {
+  EPI_STORE = 0,
+  EPI_ROPE = 1,
+  EPI_SILU = 2,
+  EPI_ARGMAX = 3,
+  // grouped (mixture-of-experts) variants: a stacked weight of groups of tiles_per_group tiles,
+  // only the listed groups computed, rows gathered and scattered through per-group row maps
+  EPI_SILU_G = 4,
+  EPI_STORE_G = 5
+};
 
 // One skinny GEMM  Y[M][N] = X[M][Kd] . W[N][Kd]^T  over packed tiles, with a fused
 // X prologue and output epilogue.  Work unit = NU consecutive 16-row tiles (or a tile
@@ -24,6 +33,17 @@ struct GemmArgs {
   const int* n_units_dev = nullptr;  // optional device count of valid units
   int KW = 1, NW = 8, kb_per_split = 0;
   int M = 0;
+  // grouped launches (EPI_*_G): unit u computes group g = group_list[u / units_per_group]
+  // (n_groups_dev[0] groups are listed), tiles g*tiles_per_group + (u % units_per_group)*NU.
+  // Local row m < M of group g reads X row xrow_map[g*M + m] (-1: empty row) and writes output
+  // row orow_map[g*M + m] (-1: skipped); EPI_STORE_G scales by orow_wt[g*M + m].
+  const int* group_list = nullptr;
+  const int* n_groups_dev = nullptr;
+  int units_per_group = 0;
+  int tiles_per_group = 0;
+  const int* xrow_map = nullptr;
+  const int* orow_map = nullptr;
+  const float* orow_wt = nullptr;
   // X operand: storage-typed [M][ldx]
   const void* X = nullptr;
   int ldx = 0;
@@ -40,6 +60,9 @@ struct GemmArgs {
   int ldo = 0;
   int accumulate = 0;
   float* ssq = nullptr;        // [n_tiles][M]
+  // optional addend rows: y = (sum_{k < add_n} addend[(m*add_n + k)*ldo + col]) + y, k ascending
+  const float* addend = nullptr;
+  int add_n = 0;
   void* xw_out = nullptr;
   const float* xw_norm = nullptr;
   // EPI_ROPE: columns are heads of hd with rotary pairs interleaved; heads [0,hq) -> qout,
@@ -66,7 +89,14 @@ struct GemmArgs {
   int ld_logits = 0;
 };
 
-hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st);
+// Optional events attached to the kernel's own dispatch (start and end of its execution on the
+// device, without the gaps between launches).
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
+                       const LaunchTiming* tm = nullptr);
 
 // Grouped-query attention of R query rows per sequence over one layer's cache: K [pos][hd],
 // V transposed [hd][pos].
@@ -109,6 +139,14 @@ hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const v
                               int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
                               const float* norm_e, int d, int Dd, float eps, void* u, int B,
                               int* err, hipStream_t st);
+// Mixture-of-experts routing of M rows over E experts (logits [M][E]): the top_k experts of
+// each row (ties -> lower id), softmax weights over them, and the per-expert row maps of the
+// grouped GEMMs: for expert e and its i-th routed row m (ascending m), xrow[e*M+i] = m,
+// orow[e*M+i] = m*top_k + r (r = rank of e among the row's experts in ascending id) and
+// wt[e*M+i] = its weight; -1 beyond the expert's count.  group_list = experts with at least one
+// row, ascending, n_groups[0] of them.
+hipError_t launch_moe_route(const float* logits, int M, int E, int top_k, int* xrow, int* orow,
+                            float* wt, int* group_list, int* n_groups, int* err, hipStream_t st);
 hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int tiles_per_cluster,
                                  int units_per_cluster, int* unit_tile, int* unit_row, int* err,
                                  hipStream_t st);

@@ -223,6 +223,113 @@ __global__ void __launch_bounds__(256) cluster_select_kernel(const float* z, int
   }
 }
 
+// Mixture-of-experts routing (one workgroup): per row, the top_k router logits by repeated
+// wave argmax (ties -> lower expert id) and their softmax weights; then, per expert, the rows
+// routed to it in ascending row order, and the ascending list of experts that received a row.
+constexpr int MOE_MAX_M = 64, MOE_MAX_E = 256, MOE_MAX_K = 16;
+
+__global__ void __launch_bounds__(256) moe_route_kernel(const float* logits, int M, int E,
+                                                        int top_k, int* xrow, int* orow,
+                                                        float* wt, int* group_list,
+                                                        int* n_groups, int* err) {
+  __shared__ int sel[MOE_MAX_M][MOE_MAX_K];
+  __shared__ float selw[MOE_MAX_M][MOE_MAX_K];
+  __shared__ int cnt[MOE_MAX_E];
+  __shared__ int wtot[4];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wid = threadIdx.x >> 6;
+  for (int m = wid; m < M; m += 4) {
+    const float* r = logits + (size_t)m * E;
+    float v[MOE_MAX_E / WAVE];
+    int id[MOE_MAX_E / WAVE];
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_E / WAVE; ++j) {
+      const int e = lane + WAVE * j;
+      v[j] = -INFINITY;
+      id[j] = 0x7fffffff;
+      if (e < E) {
+        const float x = r[e];
+        nan |= (x != x);
+        v[j] = (x != x) ? -INFINITY : x;
+        id[j] = e;
+      }
+    }
+    if (nan) raise_error(err, ERRBIT_NAN);
+    float sv[MOE_MAX_K];
+    int si[MOE_MAX_K];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k) {
+      sv[k] = 0.f;
+      si[k] = 0x7fffffff;
+      if (k < top_k) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_E / WAVE; ++j) argmax_combine(bv, bi, v[j], id[j]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const float v2 = __shfl_xor(bv, o, WAVE);
+          const int i2 = __shfl_xor(bi, o, WAVE);
+          argmax_combine(bv, bi, v2, i2);
+        }
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_E / WAVE; ++j)
+          if (id[j] == bi) {
+            v[j] = -INFINITY;
+            id[j] = 0x7fffffff;
+          }
+        sv[k] = bv;
+        si[k] = bi;
+      }
+    }
+    if (lane == 0) {
+      // ascending expert id: the rank of each selected id among the selected ones
+#pragma unroll
+      for (int k = 0; k < MOE_MAX_K; ++k) {
+        if (k < top_k) {
+          int rank = 0;
+#pragma unroll
+          for (int k2 = 0; k2 < MOE_MAX_K; ++k2) rank += (k2 < top_k && si[k2] < si[k]);
+          sel[m][rank] = si[k];
+          selw[m][rank] = expf(sv[k] - sv[0]);  // sv[0] is the largest selected logit
+        }
+      }
+      float sum = 0.f;
+      for (int k = 0; k < top_k; ++k) sum += selw[m][k];
+      for (int k = 0; k < top_k; ++k) selw[m][k] = selw[m][k] / sum;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+    for (int m = 0; m < M; ++m)
+      for (int k = 0; k < top_k; ++k)
+        if (sel[m][k] == e) {
+          xrow[(size_t)e * M + c] = m;
+          orow[(size_t)e * M + c] = m * top_k + k;
+          wt[(size_t)e * M + c] = selw[m][k];
+          ++c;
+        }
+    for (int i = c; i < M; ++i) {
+      xrow[(size_t)e * M + i] = -1;
+      orow[(size_t)e * M + i] = -1;
+      wt[(size_t)e * M + i] = 0.f;
+    }
+    cnt[e] = c;
+  }
+  __syncthreads();
+  const int e = threadIdx.x;
+  const bool used = e < E && cnt[e] > 0;
+  const unsigned long long mask = __ballot(used);
+  if (lane == 0) wtot[wid] = __popcll(mask);
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wid; ++w) off += wtot[w];
+  if (used) group_list[off + __popcll(mask & ((1ull << lane) - 1ull))] = e;
+  if (threadIdx.x == 0) n_groups[0] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+}
+
 // Reduces a sequence's head partials to the drafted token, records it as the next sub-step's
 // input, and applies the optional injected replacement for slot j at position len[b] + j.
 __global__ void __launch_bounds__(256) draft_finalize_kernel(
@@ -258,7 +365,8 @@ __global__ void __launch_bounds__(256) draft_finalize_kernel(
 
 // dst (packed tiles) <- src (logical row-major [N][Kd]).
 //   kind 0: plain; kind 1: rotary heads of hd with pairs (i, i+hd/2) made adjacent;
-//   kind 2: gate rows [0, F) and up rows [F, 2F) interleaved tile by tile (F = split_rows).
+//   kind 2: gate rows [0, F) and up rows [F, 2F) interleaved tile by tile (F = split_rows), in
+//   each group of 2F rows (N a multiple of 2F: stacked expert matrices).
 template <typename T>
 __global__ void pack_kernel(const T* src, T* dst, int N, int Kd, int kind, int hd, int F) {
   const size_t total = (size_t)N * Kd;
@@ -272,8 +380,9 @@ __global__ void pack_kernel(const T* src, T* dst, int N, int Kd, int kind, int h
       const int head = n / hd, p = n - head * hd;
       sr = head * hd + (p >> 1) + (p & 1) * (hd >> 1);
     } else if (kind == 2) {
-      const int tile = n >> 4;
-      sr = (tile & 1) * F + (tile >> 1) * TILE_N + (n & 15);
+      const int g = n / (2 * F), nl = n - g * 2 * F;
+      const int tile = nl >> 4;
+      sr = g * 2 * F + (tile & 1) * F + (tile >> 1) * TILE_N + (nl & 15);
     }
     dst[packed_offset(n, k, nkb)] = src[(size_t)sr * Kd + k];
   }
@@ -337,6 +446,16 @@ hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int til
                                  hipStream_t st) {
   hipLaunchKernelGGL(cluster_select_kernel, dim3(B), dim3(256), 0, st, z, Nc, k_c,
                      tiles_per_cluster, units_per_cluster, unit_tile, unit_row, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_route(const float* logits, int M, int E, int top_k, int* xrow, int* orow,
+                            float* wt, int* group_list, int* n_groups, int* err, hipStream_t st) {
+  if (M < 1 || M > MOE_MAX_M || E < 1 || E > MOE_MAX_E || top_k < 1 || top_k > MOE_MAX_K ||
+      top_k > E)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(256), 0, st, logits, M, E, top_k, xrow, orow,
+                     wt, group_list, n_groups, err);
   return hipGetLastError();
 }
 

@@ -42,7 +42,18 @@ int env_int(const char* name, int dflt) {
 struct Gemm {
   const void* W = nullptr;
   int N = 0, Kd = 0, nkb = 0, n_tiles = 0, NU = 1, n_units = 0, KW = 1, NW = 8, kbps = 0;
+  int tpg = 0, upg = 0;  // grouped (stacked experts): tiles and units per group
 };
+
+// Split-K factor of a projection with `units` work units of NU tiles over nkb k-blocks.  Measured
+// on MI355X at the 31B shapes (M = 4): about TARGET_WAVES waves per launch, each streaming at
+// least MIN_KB_PER_WAVE k-blocks, is best for one-tile units; the 4-tile argmax units (LM head,
+// drafter table) stream best split 8 ways.
+int split_for(int units, int nkb, int NU) {
+  int KW = NU >= 4 ? 8 : cdiv(TARGET_WAVES, units);
+  KW = std::min({KW, 16, std::max(1, nkb / MIN_KB_PER_WAVE)});
+  return pow2_floor(std::max(1, std::min(KW, env_int("SPECDEC_MAX_KW", 16))));
+}
 
 Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   Gemm g;
@@ -53,23 +64,35 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   g.n_tiles = N / 16;
   g.NU = NU;
   g.n_units = cdiv(g.n_tiles, NU);
-  // Measured on MI355X at the 31B shapes (M = 4): about TARGET_WAVES waves per launch, each
-  // streaming at least MIN_KB_PER_WAVE k-blocks, is best for one-tile units; the 4-tile argmax
-  // units (LM head, drafter table) stream best split 8 ways.
-  int KW = 1;
-  if (allow_split) {
-    KW = NU >= 4 ? 8 : cdiv(TARGET_WAVES, g.n_units);
-    KW = std::min({KW, 16, std::max(1, g.nkb / MIN_KB_PER_WAVE)});
-    KW = pow2_floor(std::max(1, std::min(KW, env_int("SPECDEC_MAX_KW", 16))));
-  }
-  g.KW = KW;
-  g.NW = KW == 16 ? 16 : 8;
-  g.kbps = cdiv(g.nkb, KW);
+  g.KW = allow_split ? split_for(g.n_units, g.nkb, NU) : 1;
+  g.NW = g.KW == 16 ? 16 : 8;
+  g.kbps = cdiv(g.nkb, g.KW);
+  return g;
+}
+
+// A stacked weight of E groups (experts) of N x Kd each, of which a launch computes only the
+// routed ones.  The split is sized for the top_k groups of one row, fixed per shape so that a
+// row's result does not depend on how many other rows share the launch.
+Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
+  Gemm g;
+  g.W = W;
+  g.N = N;
+  g.Kd = Kd;
+  g.nkb = Kd / 32;
+  g.tpg = N / 16;
+  g.upg = g.tpg / NU;
+  g.n_tiles = E * g.tpg;
+  g.NU = NU;
+  g.n_units = E * g.upg;
+  g.KW = split_for(top_k * g.upg, g.nkb, NU);
+  g.NW = g.KW == 16 ? 16 : 8;
+  g.kbps = cdiv(g.nkb, g.KW);
   return g;
 }
 
 struct Layout {
   size_t x, xw, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err;
+  size_t rlog, e_xrow, e_orow, e_wt, e_groups, e_ngroups, e_h, e_y;
   size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
   size_t total;
 };
@@ -92,6 +115,7 @@ struct specdec_ctx {
   std::vector<const void*> lw, dw;
   specdec_weights w{};
   std::vector<Gemm> g_qkv, g_o, g_gu, g_down;
+  std::vector<Gemm> g_router, g_egu, g_edown;  // mixture of experts
   Gemm g_head, g_in, g_back, g_cent, g_table, g_clu;
   std::vector<Gemm> g_dq, g_do, g_dgu, g_ddown;
   std::vector<int> len_hi;  // host-side upper bound on len
@@ -102,14 +126,24 @@ struct specdec_ctx {
 
 namespace {
 
+// Width of the dense gated FFN: the FFN itself, or the shared FFN of a mixture-of-experts layer.
+int ffn_width(const specdec_config* c) { return c->n_experts > 0 ? c->shared_ffn : c->ffn_dim; }
+
 bool valid_config(const specdec_config* c) {
   if (!c) return false;
+  if (c->n_experts < 0) return false;
+  if (c->n_experts > 0) {
+    if (c->n_experts > 256 || c->n_experts % 16 || c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return false;
+    if (c->expert_ffn % 32 || c->expert_ffn < 32 || c->shared_ffn % 32 || c->shared_ffn < 32)
+      return false;
+  }
   if (c->dtype != SPECDEC_F32 && c->dtype != SPECDEC_BF16) return false;
   if (c->n_layers < 1 || c->d_model < 32 || c->n_q_heads < 1 || c->n_kv_heads < 1) return false;
   if (c->n_q_heads % c->n_kv_heads) return false;
   if (c->head_dim % 16 || c->head_dim > 256 || c->head_dim < 16) return false;
   const int qd = c->n_q_heads * c->head_dim;
-  if (c->d_model % 32 || qd % 32 || c->ffn_dim % 32 || c->ffn_dim < 32) return false;
+  if (c->d_model % 32 || qd % 32) return false;
+  if (c->n_experts == 0 && (c->ffn_dim % 32 || c->ffn_dim < 32)) return false;
   if (c->d_layers < 1 || c->d_dim % 32 || c->d_dim < 32 || c->d_dim > 1024) return false;
   if (c->d_ffn % 32 || c->d_ffn < 32) return false;
   if (c->vocab % 64 || c->vocab < 64 || c->n_centroids < 16 || c->n_centroids % 16) return false;
@@ -149,7 +183,7 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.xw = take((size_t)dm.Mx * d * dm.esz);
   L.q = take((size_t)dm.Mx * qd * 4);
   L.o = take((size_t)dm.Mx * qd * dm.esz);
-  L.h = take((size_t)dm.Mx * c->ffn_dim * dm.esz);
+  L.h = take((size_t)dm.Mx * ffn_width(c) * dm.esz);
   L.ssq = take((size_t)dm.Mx * (d / 16) * 4);
   L.ssq_d = take((size_t)dm.Bx * (Dd / 16) * 4);
   L.amax_v = take((size_t)dm.Mx * dm.parts * 4);
@@ -167,6 +201,15 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.dtok = take((size_t)dm.Bx * 4);
   L.d_amax_v = take((size_t)dm.Bx * dm.parts * 4);  // [B][V/64] (full) or [B*k_c*upc] (clustered)
   L.d_amax_i = take((size_t)dm.Bx * dm.parts * 4);
+  const size_t E = c->n_experts, slots = (size_t)dm.Mx * c->top_k;
+  L.rlog = take((size_t)dm.Mx * E * 4);
+  L.e_xrow = take(E * dm.Mx * 4);
+  L.e_orow = take(E * dm.Mx * 4);
+  L.e_wt = take(E * dm.Mx * 4);
+  L.e_groups = take(E * 4);
+  L.e_ngroups = take(4);
+  L.e_h = take(slots * c->expert_ffn * dm.esz);
+  L.e_y = take(slots * d * 4);
   L.total = off;
   return L;
 }
@@ -174,14 +217,23 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
 void build_gemms(specdec_ctx* x) {
   const specdec_config& c = x->cfg;
   const int d = c.d_model, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  const int Fw = ffn_width(&c);
   x->g_qkv.clear(); x->g_o.clear(); x->g_gu.clear(); x->g_down.clear();
+  x->g_router.clear(); x->g_egu.clear(); x->g_edown.clear();
   x->g_dq.clear(); x->g_do.clear(); x->g_dgu.clear(); x->g_ddown.clear();
   for (int l = 0; l < c.n_layers; ++l) {
     const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
     x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, 1));
     x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, 1));
-    x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * c.ffn_dim, d, 2));
-    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, c.ffn_dim, 1));
+    x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * Fw, d, 2));
+    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, Fw, 1));
+    if (c.n_experts > 0) {
+      x->g_router.push_back(make_gemm(t[SPECDEC_LW_ROUTER], c.n_experts, d, 1));
+      x->g_egu.push_back(make_grouped_gemm(t[SPECDEC_LW_EXP_GATE_UP], 2 * c.expert_ffn, d, 2,
+                                           c.n_experts, c.top_k));
+      x->g_edown.push_back(make_grouped_gemm(t[SPECDEC_LW_EXP_DOWN], d, c.expert_ffn, 1,
+                                             c.n_experts, c.top_k));
+    }
   }
   x->g_head = make_gemm(x->w.embed, c.vocab, d, 4);
   x->g_in = make_gemm(x->w.w_in, c.d_dim, d + c.d_dim, 1);
@@ -207,19 +259,27 @@ int mt_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 int dt_of(const specdec_ctx* x) { return x->cfg.dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32; }
 
+// Times one launch of the profiled class.  A single-kernel launch takes the events attached to
+// its own dispatch (timing()); otherwise the scope records stream events around the launches.
 struct ProfScope {
   specdec_ctx* x;
-  bool on;
+  bool on, attached = false;
   hipStream_t st;
-  ProfScope(specdec_ctx* c, int cls, hipStream_t s) : x(c), on(false), st(s) {
+  LaunchTiming tm;
+  ProfScope(specdec_ctx* c, int cls, hipStream_t s, bool single_kernel = false)
+      : x(c), on(false), st(s) {
     if (cls >= 0 && x->prof_class == cls && x->prof_n < x->prof_cap) {
       on = true;
-      (void)hipEventRecord(x->prof_ev[2 * x->prof_n], st);
+      attached = single_kernel;
+      tm.start = x->prof_ev[2 * x->prof_n];
+      tm.stop = x->prof_ev[2 * x->prof_n + 1];
+      if (!attached) (void)hipEventRecord(tm.start, st);
     }
   }
+  const LaunchTiming* timing() const { return on && attached ? &tm : nullptr; }
   ~ProfScope() {
     if (on) {
-      (void)hipEventRecord(x->prof_ev[2 * x->prof_n + 1], st);
+      if (!attached) (void)hipEventRecord(tm.stop, st);
       x->prof_n++;
     }
   }
@@ -267,8 +327,69 @@ void resid_output(GemmArgs& a, float* x, int ld, int accumulate, float* ssq, voi
   } while (0)
 
 int run(specdec_ctx* x, int cls, int NU, int epi, const GemmArgs& a, hipStream_t st) {
-  ProfScope ps(x, cls, st);
-  HIP_TRY(launch_gemm(dt_of(x), mt_for(a.M), NU, epi, a, st));
+  ProfScope ps(x, cls, st, a.n_units > 0);
+  HIP_TRY(launch_gemm(dt_of(x), mt_for(a.M), NU, epi, a, st, ps.timing()));
+  return SPECDEC_OK;
+}
+
+// Routed experts of one mixture-of-experts layer over the M rows of x * ffn_norm (XW, with the
+// row scales from ssq): router logits, top-k routing, then the gate/up and down projections of
+// only the routed experts over their gathered rows.  Leaves w_e * FFN_e(row) in e_y at slot
+// row*top_k + rank (rank = the expert's place among the row's experts in ascending id).
+int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
+  const specdec_config& c = x->cfg;
+  const int d = c.d_model, E = c.n_experts;
+  void* XW = x->ws + x->lay.xw;
+  float* ssq = at<float>(x, x->lay.ssq);
+  int* xrow = at<int>(x, x->lay.e_xrow);
+  int* orow = at<int>(x, x->lay.e_orow);
+  float* wt = at<float>(x, x->lay.e_wt);
+  int* groups = at<int>(x, x->lay.e_groups);
+  int* ngroups = at<int>(x, x->lay.e_ngroups);
+  int rc;
+  {  // router logits [M][E] of the normalised rows
+    GemmArgs a = base_args(x, x->g_router[l], M);
+    norm_input(a, XW, d, ssq, d);
+    a.out = at<float>(x, x->lay.rlog);
+    a.ldo = E;
+    if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
+  }
+  HIP_TRY(launch_moe_route(at<float>(x, x->lay.rlog), M, E, c.top_k, xrow, orow, wt, groups,
+                           ngroups, at<int>(x, x->lay.err), st));
+  // at most min(E, M*top_k) experts are routed to
+  const int max_groups = std::min(E, M * c.top_k);
+  {  // gate/up of the routed experts over their rows -> SiLU product at the row's slot
+    const Gemm& g = x->g_egu[l];
+    GemmArgs a = base_args(x, g, M);
+    a.n_units = max_groups * g.upg;
+    norm_input(a, XW, d, ssq, d);
+    a.group_list = groups;
+    a.n_groups_dev = ngroups;
+    a.units_per_group = g.upg;
+    a.tiles_per_group = g.tpg;
+    a.xrow_map = xrow;
+    a.orow_map = orow;
+    a.hout = x->ws + x->lay.e_h;
+    a.ldh = c.expert_ffn;
+    if ((rc = run(x, 7, 2, EPI_SILU_G, a, st))) return rc;
+  }
+  {  // down of the routed experts, scaled by the routing weight, stored at the row's slot
+    const Gemm& g = x->g_edown[l];
+    GemmArgs a = base_args(x, g, M);
+    a.n_units = max_groups * g.upg;
+    a.X = x->ws + x->lay.e_h;
+    a.ldx = c.expert_ffn;
+    a.group_list = groups;
+    a.n_groups_dev = ngroups;
+    a.units_per_group = g.upg;
+    a.tiles_per_group = g.tpg;
+    a.xrow_map = orow;  // the slot rows the gate/up step wrote
+    a.orow_map = orow;
+    a.orow_wt = wt;
+    a.out = at<float>(x, x->lay.e_y);
+    a.ldo = d;
+    if ((rc = run(x, 8, 1, EPI_STORE_G, a, st))) return rc;
+  }
   return SPECDEC_OK;
 }
 
@@ -324,14 +445,16 @@ int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv
   *out = nullptr;
   if (!valid_config(cfg) || !w || !kv_k || !kv_v || !len || !hid || !workspace)
     return SPECDEC_E_INVAL;
-  if (cfg->n_experts > 0 || !attention_supported(cfg->head_dim)) return SPECDEC_E_UNSUPPORTED;
+  if (!attention_supported(cfg->head_dim)) return SPECDEC_E_UNSUPPORTED;
   if (((uintptr_t)workspace) % ALIGN) return SPECDEC_E_INVAL;
   if (!w->embed || !w->final_norm || !w->layers || !w->table || !w->centroids || !w->row_vocab ||
       !w->vocab_row || !w->norm_h || !w->norm_e || !w->w_in || !w->d_layers || !w->norm_f ||
       !w->w_back)
     return SPECDEC_E_INVAL;
-  for (int i = 0; i < cfg->n_layers * SPECDEC_N_LAYER_TENSORS; ++i)
-    if (!w->layers[i]) return SPECDEC_E_INVAL;
+  const int slots_used = cfg->n_experts > 0 ? SPECDEC_N_LAYER_TENSORS : SPECDEC_LW_ROUTER;
+  for (int l = 0; l < cfg->n_layers; ++l)
+    for (int i = 0; i < slots_used; ++i)
+      if (!w->layers[(size_t)l * SPECDEC_N_LAYER_TENSORS + i]) return SPECDEC_E_INVAL;
   for (int i = 0; i < cfg->d_layers * SPECDEC_N_DRAFT_TENSORS; ++i)
     if (!w->d_layers[i]) return SPECDEC_E_INVAL;
   if (workspace_bytes < specdec_workspace_bytes(cfg)) return SPECDEC_E_INVAL;
@@ -415,19 +538,26 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
       resid_output(a, X, d, 1, ssq, XW, lw(l, SPECDEC_LW_FFN_NORM));
       if ((rc = run(x, 3, 1, EPI_STORE, a, st))) return rc;
     }
-    {  // gate/up projection + SiLU-gated product
+    if (c.n_experts > 0 && (rc = routed_experts(x, l, M, st))) return rc;
+    const int Fw = ffn_width(&c);
+    {  // gate/up projection + SiLU-gated product (the shared FFN of an MoE layer)
       GemmArgs a = base_args(x, x->g_gu[l], M);
       norm_input(a, XW, d, ssq, d);
       a.hout = x->ws + x->lay.h;
-      a.ldh = c.ffn_dim;
+      a.ldh = Fw;
       if ((rc = run(x, 0, 2, EPI_SILU, a, st))) return rc;
     }
-    {  // down projection + residual; leaves x * (next attention norm | final norm)
+    {  // down projection + residual (+ the routed experts' weighted outputs, ascending expert
+       // id); leaves x * (next attention norm | final norm)
       GemmArgs a = base_args(x, x->g_down[l], M);
       a.X = x->ws + x->lay.h;
-      a.ldx = c.ffn_dim;
+      a.ldx = Fw;
       const float* wn = l + 1 < c.n_layers ? lw(l + 1, SPECDEC_LW_ATTN_NORM) : x->w.final_norm;
       resid_output(a, X, d, 1, ssq, XW, wn);
+      if (c.n_experts > 0) {
+        a.addend = at<float>(x, x->lay.e_y);
+        a.add_n = c.top_k;
+      }
       if ((rc = run(x, 1, 1, EPI_STORE, a, st))) return rc;
     }
   }
@@ -611,7 +741,7 @@ int specdec_pack_matrix(const void* src, void* dst, int32_t n, int32_t kd, int32
   if (kind < 0 || kind > 2) return SPECDEC_E_INVAL;
   if (kind == SPECDEC_PACK_ROPE && (head_dim < 16 || head_dim % 16 || n % head_dim))
     return SPECDEC_E_INVAL;
-  if (kind == SPECDEC_PACK_GATE_UP && (split_rows * 2 != n || split_rows % 16))
+  if (kind == SPECDEC_PACK_GATE_UP && (split_rows < 16 || split_rows % 16 || n % (2 * split_rows)))
     return SPECDEC_E_INVAL;
   HIP_TRY(launch_pack(dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, src, dst, n, kd, kind, head_dim,
                       split_rows, reinterpret_cast<hipStream_t>(stream)));
@@ -664,8 +794,9 @@ int specdec_profile_read(specdec_ctx* x, float* ms_out, int32_t max, int32_t* n_
   return SPECDEC_OK;
 }
 
-int specdec_query_split(specdec_ctx* x, int32_t cls, int32_t* splits, int32_t* units) {
-  if (!x || !splits || !units) return SPECDEC_E_INVAL;
+int specdec_query_split(specdec_ctx* x, int32_t cls, int32_t* splits, int32_t* units,
+                        int32_t* waves, int32_t* groups) {
+  if (!x || !splits || !units || !waves || !groups) return SPECDEC_E_INVAL;
   const Gemm* g = nullptr;
   switch (cls) {
     case 0: g = &x->g_gu[0]; break;
@@ -673,10 +804,14 @@ int specdec_query_split(specdec_ctx* x, int32_t cls, int32_t* splits, int32_t* u
     case 2: g = &x->g_qkv[0]; break;
     case 3: g = &x->g_o[0]; break;
     case 5: g = &x->g_head; break;
+    case 7: if (x->g_egu.empty()) return SPECDEC_E_INVAL; g = &x->g_egu[0]; break;
+    case 8: if (x->g_edown.empty()) return SPECDEC_E_INVAL; g = &x->g_edown[0]; break;
     default: return SPECDEC_E_INVAL;
   }
   *splits = g->KW;
   *units = g->n_units;
+  *waves = g->NW;
+  *groups = cdiv(g->n_units, g->NW / g->KW);
   return SPECDEC_OK;
 }
 

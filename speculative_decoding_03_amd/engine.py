@@ -102,10 +102,21 @@ class DeviceModel:
             self.layer_ptrs[base + F.LW_QKV] = k(pack_matrix(qkv, qd + 2 * kvd, d, dt, F.PACK_ROPE, s.head_dim, stream=stream))
             del qkv
             self.layer_ptrs[base + F.LW_O] = k(pack_matrix(source.get("wo", l, (d, qd)), d, qd, dt, stream=stream))
-            gu = torch.cat([source.get("wg", l, (F_, d)), source.get("wu", l, (F_, d))], 0).contiguous()
-            self.layer_ptrs[base + F.LW_GATE_UP] = k(pack_matrix(gu, 2 * F_, d, dt, F.PACK_GATE_UP, split_rows=F_, stream=stream))
+            if s.n_experts > 0:
+                # shared FFN in the dense slots; router and the stacked experts in their own
+                E, Fe, Fs = s.n_experts, s.expert_ffn, s.shared_ffn
+                names = ("sh_wg", "sh_wu", "sh_wd")
+                self.layer_ptrs[base + F.LW_ROUTER] = k(pack_matrix(source.get("router", l, (E, d)), E, d, dt, stream=stream))
+                egu = torch.cat([source.get("exp_wg", l, (E, Fe, d)), source.get("exp_wu", l, (E, Fe, d))], 1).contiguous()
+                self.layer_ptrs[base + F.LW_EXP_GATE_UP] = k(pack_matrix(egu.view(-1), E * 2 * Fe, d, dt, F.PACK_GATE_UP, split_rows=Fe, stream=stream))
+                del egu
+                self.layer_ptrs[base + F.LW_EXP_DOWN] = k(pack_matrix(source.get("exp_wd", l, (E, d, Fe)).view(-1), E * d, Fe, dt, stream=stream))
+            else:
+                Fs, names = F_, ("wg", "wu", "wd")
+            gu = torch.cat([source.get(names[0], l, (Fs, d)), source.get(names[1], l, (Fs, d))], 0).contiguous()
+            self.layer_ptrs[base + F.LW_GATE_UP] = k(pack_matrix(gu, 2 * Fs, d, dt, F.PACK_GATE_UP, split_rows=Fs, stream=stream))
             del gu
-            self.layer_ptrs[base + F.LW_DOWN] = k(pack_matrix(source.get("wd", l, (d, F_)), d, F_, dt, stream=stream))
+            self.layer_ptrs[base + F.LW_DOWN] = k(pack_matrix(source.get(names[2], l, (d, Fs)), d, Fs, dt, stream=stream))
             self.layer_ptrs[base + F.LW_ATTN_NORM] = k(source.get("attn_norm", l, (d,)).float().contiguous())
             self.layer_ptrs[base + F.LW_FFN_NORM] = k(source.get("ffn_norm", l, (d,)).float().contiguous())
         self.embed = pack_matrix(source.get("embed", 0, (s.vocab, d)), s.vocab, d, dt, stream=stream)
@@ -263,10 +274,11 @@ class Engine:
         return [buf[i] for i in range(n.value)]
 
     def query_split(self, kernel_class: int):
-        s, u = C.c_int32(), C.c_int32()
-        F.check(self.lib.specdec_query_split(self.ctx, kernel_class, C.byref(s), C.byref(u)),
-                "specdec_query_split")
-        return s.value, u.value
+        """(split-K factor, work units, waves per workgroup, workgroups) of one launch."""
+        s, u, w, g = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int32()
+        F.check(self.lib.specdec_query_split(self.ctx, kernel_class, C.byref(s), C.byref(u),
+                                             C.byref(w), C.byref(g)), "specdec_query_split")
+        return s.value, u.value, w.value, g.value
 
     def close(self) -> None:
         if getattr(self, "ctx", None):

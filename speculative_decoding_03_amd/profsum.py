@@ -1,0 +1,196 @@
+"""Summaries of rocprofv3 output: per-kernel time statistics and HBM traffic per dispatch.
+
+HBM traffic comes from two counter passes (FETCH_SIZE, then WRITE_SIZE, both in KiB per
+dispatch).  Each is scaled by what the same counter reads for a plain device copy of known size
+(``copy`` below), so that the figure is in real bytes.
+
+  python -m speculative_decoding_03_amd.profsum copy [--mib 1024] [--reps 4]
+      runs the plain copy that calibrates the counters (profile it under rocprofv3 --pmc)
+  python -m speculative_decoding_03_amd.profsum stats DIR --cmd CMD [--match S --last N] -o OUT
+      kernel time table from DIR/*kernel_stats.csv (+ the last N dispatches of kernels whose
+      name contains S, from DIR/*kernel_trace.csv)
+  python -m speculative_decoding_03_amd.profsum traffic --fetch D --write D --copy-fetch D
+      --copy-write D --match S --last N --algorithmic BYTES --src FILE --cmd CMD -o OUT
+      per-dispatch HBM bytes of the matching kernel, written as JSON
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+
+def _one(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, f"*{suffix}")))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def short_name(n: str) -> str:
+    n = n.replace("void ", "").replace("specdec::", "").replace("(anonymous namespace)::", "")
+    n = n.replace("bf16_t", "bf16")
+    m = re.match(r"([\w:]+)(<[^()]*>)?", n)
+    return (m.group(1) + (m.group(2) or "")) if m else n
+
+
+def _rows(path: str):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _grid(r) -> int:
+    g = r.get("Grid_Size_X", r.get("Grid_Size", "0"))
+    return int(float(g))
+
+
+def trace_durations(d: str, match: str, grid: int = 0):
+    """Durations (ns) of the dispatches whose kernel name contains `match` (and whose grid has
+    `grid` work-items, when given), in dispatch order."""
+    rows = [r for r in _rows(_one(d, "kernel_trace.csv")) if match in short_name(r["Kernel_Name"])
+            and (not grid or _grid(r) == grid)]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+
+
+def counter_values(d: str, counter: str, match: str | None, grid: int = 0):
+    """Per-dispatch value of `counter` for kernels whose short name contains `match` (all
+    kernels when None) and whose grid has `grid` work-items (when given), in dispatch order,
+    with the kernel names."""
+    out = []
+    for r in _rows(_one(d, "counter_collection.csv")):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = short_name(r["Kernel_Name"])
+        if match is not None and match not in name:
+            continue
+        if grid and _grid(r) != grid:
+            continue
+        out.append((int(r["Dispatch_Id"]), name, float(r["Counter_Value"])))
+    out.sort()
+    return out
+
+
+def cmd_copy(a) -> int:
+    import torch
+
+    n = a.mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(a.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": a.reps}))
+    return 0
+
+
+def cmd_stats(a) -> int:
+    rows = _rows(_one(a.dir, "kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel statistics", "", f"command: {a.cmd}", ""]
+    lines.append(f"{'kernel':<58} {'calls':>7} {'avg us':>10} {'min us':>9} {'max us':>9} {'time %':>7}")
+    for r in rows[: a.top]:
+        lines.append(f"{short_name(r['Name'])[:58]:<58} {r['Calls']:>7} "
+                     f"{float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>9.2f} "
+                     f"{float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>7.2f}")
+    if a.match:
+        dur = trace_durations(a.dir, a.match, a.grid)
+        sel = dur[-a.last:] if a.last else dur
+        if sel:
+            lines += ["", f"dispatches of '{a.match}' (grid {a.grid or 'any'}): {len(dur)}; "
+                      f"last {len(sel)} (the timed "
+                      f"region): avg {sum(sel) / len(sel) / 1e3:.2f} us, "
+                      f"min {min(sel) / 1e3:.2f} us, max {max(sel) / 1e3:.2f} us"]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        open(a.out, "w").write(text)
+    sys.stdout.write(text)
+    return 0
+
+
+def _copy_factor(d: str, counter: str, known: float):
+    vals = counter_values(d, counter, None)
+    if not vals:
+        raise SystemExit(f"no {counter} values under {d}")
+    # the calibration copy is the dispatch with the largest count
+    big = max(v for _, _, v in vals)
+    hits = [v for _, _, v in vals if v >= 0.5 * big]
+    kib = sum(hits) / len(hits)
+    name = [n for _, n, v in vals if v == big][0]
+    return known / (kib * 1024.0), kib, name
+
+
+def cmd_traffic(a) -> int:
+    known = a.copy_mib * (1 << 20)
+    ff, fkib, fname = _copy_factor(a.copy_fetch, "FETCH_SIZE", known)
+    fw, wkib, wname = _copy_factor(a.copy_write, "WRITE_SIZE", known)
+    fv = [v for _, _, v in counter_values(a.fetch, "FETCH_SIZE", a.match, a.grid)]
+    wv = [v for _, _, v in counter_values(a.write, "WRITE_SIZE", a.match, a.grid)]
+    if a.last:
+        fv, wv = fv[-a.last:], wv[-a.last:]
+    if not fv or not wv:
+        raise SystemExit(f"no counter values for '{a.match}'")
+    fetch = sum(fv) / len(fv) * 1024.0 * ff
+    write = sum(wv) / len(wv) * 1024.0 * fw
+    res = {
+        "kernel": a.match,
+        "grid_work_items": a.grid or None,
+        "command": a.cmd,
+        "kernel_src": a.src,
+        "kernel_src_sha": hashlib.sha256(open(a.src, "rb").read()).hexdigest()[:16],
+        "dispatches": {"fetch": len(fv), "write": len(wv)},
+        "fetch_kib_per_dispatch_raw": round(sum(fv) / len(fv), 2),
+        "write_kib_per_dispatch_raw": round(sum(wv) / len(wv), 2),
+        "copy_calibration": {"bytes": known, "kernel": fname, "fetch_kib": round(fkib, 1),
+                             "write_kib": round(wkib, 1), "fetch_scale": round(ff, 5),
+                             "write_scale": round(fw, 5)},
+        "hbm_fetch_bytes_per_dispatch": round(fetch),
+        "hbm_write_bytes_per_dispatch": round(write),
+        "hbm_bytes_per_dispatch": round(fetch + write),
+        "algorithmic_bytes_per_dispatch": a.algorithmic,
+        "traffic_over_algorithmic": round((fetch + write) / a.algorithmic, 4) if a.algorithmic else None,
+    }
+    text = json.dumps(res, indent=1)
+    if a.out:
+        open(a.out, "w").write(text + "\n")
+    print(text)
+    return 0
+
+
+def main(argv=None) -> int:
+    p = argparse.ArgumentParser(prog="profsum")
+    sp = p.add_subparsers(dest="what", required=True)
+    c = sp.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    c.add_argument("--reps", type=int, default=4)
+    s = sp.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--match")
+    s.add_argument("--last", type=int, default=0)
+    s.add_argument("--grid", type=int, default=0)
+    s.add_argument("--top", type=int, default=24)
+    s.add_argument("-o", "--out")
+    t = sp.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-mib", type=int, default=1024)
+    t.add_argument("--match", required=True)
+    t.add_argument("--last", type=int, default=0)
+    t.add_argument("--grid", type=int, default=0)
+    t.add_argument("--algorithmic", type=float, default=0.0)
+    t.add_argument("--src", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("-o", "--out")
+    a = p.parse_args(argv)
+    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,5 +1,6 @@
-"""GPU parity on the tiny fp32 workload (2 layers, d=256, vocab 4096, drafter d=128 with 64
-centroids of 64 tokens; prompt 64 ids; 64 generated tokens; K=3), through the C ABI.
+"""GPU parity on the tiny fp32 workloads (2 layers, d=256, vocab 4096, drafter d=128 with 64
+centroids of 64 tokens; prompt 64 ids; 64 generated tokens; K=3), through the C ABI: the dense
+target and its mixture-of-experts twin (16 experts of FFN 128, top-4, shared FFN 256).
 
 Tolerance: logits within a max relative error of 1e-4 (fp32); tokens must match wherever the
 oracle's top-2 logit margin exceeds 0.05; acceptance and indexing bit-exact given logits."""
@@ -27,9 +28,10 @@ MAX_CTX = 256
 TOL = 1e-4
 
 
-@pytest.fixture(scope="module")
-def tiny():
+@pytest.fixture(scope="module", params=["tiny", "tiny-moe"])
+def tiny(request):
     """GPU engine after prefill, plus the oracle's state after the same prefill."""
+    CFG = preset(request.param)
     eng = build_engine(CFG, MAX_CTX)
     prompt = prompt_tokens(CFG)[0]
     t0, logits = gpu_prefill(eng, prompt)
@@ -45,12 +47,14 @@ def tiny():
     K = CFG.draft_k
     greedy, margins = O.greedy_generate(W, CFG, cache.copy(), ref_t0, len(prompt), n + K + 2,
                                         record_margins=True)
-    return dict(eng=eng, t0=t0, logits=logits, ref_rows=np.array(ref_rows), ref_t0=ref_t0,
+    yield dict(cfg=CFG, eng=eng, t0=t0, logits=logits, ref_rows=np.array(ref_rows), ref_t0=ref_t0,
                 W=W, DW=DW, cache=cache, hid=hidden, length=len(prompt), greedy=greedy,
                 margins=margins, snap=snapshot(eng))
+    eng.close()
 
 
 def test_prefill_logits_match_oracle(tiny):
+    CFG = tiny["cfg"]
     errs = [rel_err(tiny["logits"][i], tiny["ref_rows"][i]) for i in range(len(tiny["ref_rows"]))]
     assert max(errs) < TOL, f"max rel err {max(errs):.3e}"
     assert tiny["t0"] == tiny["ref_t0"]
@@ -70,6 +74,7 @@ def _check_tokens(gpu_toks, ref_toks, margins, n):
 
 
 def test_gpu_greedy_matches_oracle(tiny):
+    CFG = tiny["cfg"]
     eng = tiny["eng"]
     restore(eng, tiny["snap"])
     n = CFG.gen_tokens
@@ -81,6 +86,7 @@ def test_gpu_greedy_matches_oracle(tiny):
 
 @pytest.mark.parametrize("p", [0.0, 0.6, 1.0, "wrong"])
 def test_gpu_spec_equals_gpu_greedy(tiny, p):
+    CFG = tiny["cfg"]
     eng = tiny["eng"]
     n, K = CFG.gen_tokens, CFG.draft_k
     restore(eng, tiny["snap"])
@@ -106,6 +112,7 @@ def test_gpu_spec_equals_gpu_greedy(tiny, p):
 
 @pytest.mark.parametrize("mode,k_c", [("clustered", 1), ("clustered", 3), ("clustered", 64), ("full", 0)])
 def test_drafter_matches_oracle(tiny, mode, k_c):
+    CFG = tiny["cfg"]
     eng = tiny["eng"]
     restore(eng, tiny["snap"])
     K = CFG.draft_k
@@ -122,6 +129,7 @@ def test_drafter_matches_oracle(tiny, mode, k_c):
 
 
 def test_accept_bit_exact_all_patterns(tiny):
+    CFG = tiny["cfg"]
     eng = tiny["eng"]
     K = CFG.draft_k
     dev = eng.kv_k.device
@@ -190,6 +198,7 @@ def test_argmax_ties_pick_lowest_id():
 
 
 def test_error_paths(tiny):
+    CFG = tiny["cfg"]
     eng = tiny["eng"]
     dev = eng.kv_k.device
     restore(eng, tiny["snap"])

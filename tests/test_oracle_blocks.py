@@ -125,6 +125,29 @@ def test_moe_routing_special_cases():
     assert np.allclose(O.moe_ffn(lw, cfg, b), O.dense_ffn(lw["exp_wg"][0], lw["exp_wu"][0], lw["exp_wd"][0], b))
 
 
+def test_moe_route_margin_and_convex_mixture():
+    d = 6
+    router = np.zeros((5, d)); router[:, 0] = [0.1, 2.0, -1.0, 1.5, 0.3]
+    assert np.isclose(O.moe_route_margin(router, np.eye(d)[0], 2), 1.5 - 0.3)
+    assert O.moe_route_margin(router, np.eye(d)[0], 5) == np.inf
+    # identical experts: the routing weights sum to one, so the mixture equals one expert's FFN
+    # (plus the shared FFN) whatever the router says
+    from workloads import ModelConfig
+    rng = np.random.default_rng(9)
+    cfg = ModelConfig(name="m", n_layers=1, d_model=d, n_q_heads=1, n_kv_heads=1, head_dim=2,
+                      ffn_dim=0, vocab=4, n_experts=5, top_k=3, expert_ffn=4, shared_ffn=3)
+    wg, wu, wd = rng.normal(size=(4, d)), rng.normal(size=(4, d)), rng.normal(size=(d, 4))
+    sg, su, sd = rng.normal(size=(3, d)), rng.normal(size=(3, d)), rng.normal(size=(d, 3))
+    lw = {"router": rng.normal(size=(5, d)), "exp_wg": np.stack([wg] * 5),
+          "exp_wu": np.stack([wu] * 5), "exp_wd": np.stack([wd] * 5),
+          "sh_wg": sg, "sh_wu": su, "sh_wd": sd}
+    b = rng.normal(size=d)
+    tr = []
+    y = O.moe_ffn(lw, cfg, b, trace=tr)
+    assert np.allclose(y, O.dense_ffn(wg, wu, wd, b) + O.dense_ffn(sg, su, sd, b))
+    assert len(tr) == 1 and tr[0] == O.moe_route_margin(lw["router"], b, 3)
+
+
 def test_argmax_first_ties_and_nan():
     assert O.argmax_first(np.array([1.0, 3.0, 3.0, 2.0])) == 1
     assert O.argmax_first(np.array([5.0, 5.0])) == 0

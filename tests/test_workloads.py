@@ -87,3 +87,16 @@ def test_inject_table_agrees_with_scalar_draws():
     assert np.array_equal(full[5:, 0], g[5:]) and np.all(full[:5] == -1)
     wrong = inject_table(g, 2, 0.0, 3, forced_wrong=True, vocab=150).reshape(-1, 2)
     assert np.array_equal(wrong[5:, 1], (g[5:] + 1) % 150)
+
+
+def test_expert_stack_slices_equal_the_whole_tensor():
+    from workloads import preset
+    from workloads import synth as S
+    from workloads.synth import ExpertStack
+    for cfg in (preset("tiny-moe"), preset("tiny-moe", init="hash", dtype="bf16", seed=3)):
+        E, Fe, d = cfg.n_experts, cfg.expert_ffn, cfg.d_model
+        whole = S.gen_tensor(cfg, "exp_wd", 1, (E, d, Fe))
+        st = ExpertStack(cfg, "exp_wd", 1, (E, d, Fe))
+        for e in (0, 5, E - 1):
+            assert np.array_equal(st[e], whole[e])
+        assert len(st) == E

@@ -111,6 +111,13 @@ PRESETS = {
         ffn_dim=1024, vocab=4096, d_layers=1, d_dim=128, d_ffn=512, n_centroids=64,
         dtype="f32", init="normal", seed=0, prompt_len=64, gen_tokens=64, draft_k=3,
         p_inject=0.6),
+    # The tiny configuration's mixture-of-experts twin: each layer's FFN is the softmax-weighted
+    # sum of its top-4 of 16 gated experts of width 128 plus a shared gated FFN of 256.
+    "tiny-moe": ModelConfig(
+        name="tiny-moe", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+        ffn_dim=0, vocab=4096, n_experts=16, top_k=4, expert_ffn=128, shared_ffn=256,
+        d_layers=1, d_dim=128, d_ffn=512, n_centroids=64, dtype="f32", init="normal", seed=8,
+        prompt_len=64, gen_tokens=64, draft_k=3, p_inject=0.6),
     # E2B-shaped
     "e2b": ModelConfig(
         name="e2b", n_layers=24, d_model=1536, n_q_heads=8, n_kv_heads=1, head_dim=256,

@@ -34,7 +34,7 @@ __all__ = [
     "norm_weight", "target_weights", "target_layer_weights", "drafter_weights",
     "cluster_perm", "centroids_from_table", "kv_init", "kv_rows", "state_init",
     "prompt_tokens", "inject_threshold", "inject_draw", "inject_key", "hash_scale",
-    "hash_u64_at", "inject_table",
+    "hash_u64_at", "inject_table", "ExpertStack",
 ]
 
 MASK64 = (1 << 64) - 1
@@ -151,6 +151,34 @@ def gen_tensor(cfg, name: str, layer: int, shape, std: float | None = None) -> n
     return v.reshape(shape)
 
 
+class ExpertStack:
+    """A stacked [E][rows][cols] expert weight whose slices are generated on first use: with the
+    hash generator each slice is its own range of the tensor's counter stream (identical to the
+    slice of the whole tensor); with the normal generator the whole tensor is drawn once.
+    Indexing by expert id returns that expert's [rows][cols] fp32 array."""
+
+    def __init__(self, cfg, name: str, layer: int, shape):
+        self.cfg, self.name, self.layer, self.shape = cfg, name, layer, tuple(shape)
+        self._full = None
+        self._cache = {}
+
+    def __len__(self) -> int:
+        return self.shape[0]
+
+    def __getitem__(self, e) -> np.ndarray:
+        e = int(e)
+        if not 0 <= e < self.shape[0]:
+            raise IndexError(e)
+        if self.cfg.init != "hash":
+            if self._full is None:
+                self._full = gen_tensor(self.cfg, self.name, self.layer, self.shape)
+            return self._full[e]
+        if e not in self._cache:
+            _, r, c = self.shape
+            self._cache[e] = gen_rows(self.cfg, self.name, self.layer, c, e * r, r)
+        return self._cache[e]
+
+
 def norm_weight(cfg, name: str, layer: int, n: int) -> np.ndarray:
     """RMSNorm weight: exactly 1, or 1 + jitter*U(-1, 1) when the workload asks for jitter."""
     if cfg.norm_jitter == 0.0:
@@ -173,9 +201,9 @@ def target_layer_weights(cfg, l: int) -> dict:
     if cfg.is_moe:
         E, Fe, Fs = cfg.n_experts, cfg.expert_ffn, cfg.shared_ffn
         w["router"] = gen_tensor(cfg, "router", l, (E, d))
-        w["exp_wg"] = gen_tensor(cfg, "exp_wg", l, (E, Fe, d))
-        w["exp_wu"] = gen_tensor(cfg, "exp_wu", l, (E, Fe, d))
-        w["exp_wd"] = gen_tensor(cfg, "exp_wd", l, (E, d, Fe))
+        w["exp_wg"] = ExpertStack(cfg, "exp_wg", l, (E, Fe, d))
+        w["exp_wu"] = ExpertStack(cfg, "exp_wu", l, (E, Fe, d))
+        w["exp_wd"] = ExpertStack(cfg, "exp_wd", l, (E, d, Fe))
         w["sh_wg"] = gen_tensor(cfg, "sh_wg", l, (Fs, d))
         w["sh_wu"] = gen_tensor(cfg, "sh_wu", l, (Fs, d))
         w["sh_wd"] = gen_tensor(cfg, "sh_wd", l, (d, Fs))

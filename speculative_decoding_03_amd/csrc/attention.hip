@@ -2,14 +2,13 @@
 // the new rows, full over the committed prefix) and for the drafter's cross-attention into the
 // target's cache (keys [0, len), no cache of its own).
 //
-// Grid: (chunk, kv head, sequence).  A workgroup of 4 waves loads one chunk of CH keys of one
-// KV head once and serves every query vector that reads that head (all rows x all query heads
-// of the group, 16 per MFMA tile).  Scores S = Q K^T and the value sum P V both run on the
-// 16x16x32 bf16 MFMA (fp32 storage: 16x16x4 fp32).  K is stored [pos][hd] and V transposed
-// [hd][pos], so both operands stream as 16-byte loads along their reduction axis.  Per chunk the
-// kernel leaves (row max, sum of exponentials, unnormalised value sum); attn_combine merges the
-// chunks in chunk order.  Chunk boundaries sit at fixed absolute positions and every reduction
-// has a fixed order, so a row's output does not depend on how many other rows are in the call.
+// Split over keys (flash-decoding): grid (chunk, kv head, sequence); a workgroup of four waves
+// takes one chunk of CH keys, each wave a contiguous quarter, and serves every query vector
+// that reads that KV head (all rows x the group's query heads).  K is stored [pos][hd] and V
+// transposed [hd][pos], so both MFMA operands stream as 16-byte loads.  Per chunk the kernel
+// leaves (row max, sum of exponentials, unnormalised value sum); attn_combine merges the chunks
+// in chunk order.  Chunk boundaries sit at fixed absolute positions and every reduction has a
+// fixed order, so a row's output does not depend on how many other rows are in the call.
 
 #include <math.h>
 #include <stdlib.h>
@@ -23,192 +22,202 @@ namespace {
 
 constexpr int NWAVE = 4;
 
-template <int HD, int CH_> struct AttnShape {
-  static constexpr int CH = CH_;                            // keys per chunk
-  static constexpr int DS = (HD + 31) / 32;                 // 32-wide head-dim steps (scores)
-  static constexpr int KB = CH / 16 / NWAVE;                // 16-key blocks per wave (scores)
-  static constexpr int DB = (HD / 16 + NWAVE - 1) / NWAVE;  // 16-wide head-dim blocks per wave
-  static constexpr int KS = CH / 32;                        // 32-key steps (values)
+// Keys per wave: two 32-key blocks for head sizes up to 128, one above (register budget).
+template <int HD> struct AttnShape {
+  static constexpr int KPW = HD <= 128 ? 64 : 32;  // keys per wave
+  static constexpr int CH = KPW * NWAVE;            // keys per workgroup = one partial
+  static constexpr int NB = KPW / 32;               // 32-key blocks per wave
+  static constexpr int DS = (HD + 31) / 32;         // 32-wide head-dim steps (scores)
+  static constexpr int DT = HD / 16;                // 16-row head-dim tiles (value sum)
+  static constexpr int PST = HD + 4;                // partial row: o[HD], m, l, 2 pad
 };
 
-template <typename T, int HD, int QT, int CH_>
+// One workgroup = CH consecutive keys of one KV head of one sequence; wave w owns keys
+// [chunk*CH + w*KPW, +KPW), which it loads once into registers.  Then, for each 16-vector tile of
+// the group's query vectors (rows x query heads of the KV head), per wave:
+//   S^T = K Q^T on MFMA (A = key rows, B = query vectors, k = head dim).  Key tile pairs map C
+//   row i to key 8*(i/4) + i%4 (+4 in the second tile of the pair), so a lane's eight scores of
+//   a query column are eight consecutive keys;
+//   masked softmax statistics over the wave's keys per query column (max, then the sum of
+//   exponentials; lanes combined by a fixed butterfly);
+//   O^T = V^T P^T on MFMA with P^T taken straight from the score registers (bf16) and V^T read
+//   from the transposed cache as 16-byte runs of the same eight keys.
+// The four waves then merge through LDS (common max, rescale, sum in wave order) and wave 0
+// writes the chunk's partial (o, m, l).  Keys that no row may see are never loaded.
+template <typename T, int HD>
 __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
-  using SH = AttnShape<HD, CH_>;
-  constexpr int CH = SH::CH;
-  __shared__ T pbuf[QT * 16 * CH];
-  __shared__ float wred[NWAVE][QT * 16];
-  __shared__ float mrow[QT * 16], lrow[QT * 16];
+  using SH = AttnShape<HD>;
+  constexpr int NB = SH::NB, DS = SH::DS, DT = SH::DT, KPW = SH::KPW, CH = SH::CH;
+  __shared__ __align__(16) float xch[NWAVE - 1][16][SH::PST];
+  __shared__ float mw[NWAVE][16], lw[NWAVE][16];
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
   const int Rall = a.R * G;
-  const int key0 = chunk * CH;
-  const T* Kc = reinterpret_cast<const T*>(a.kcache) + (size_t)b * a.cache_b_stride +
-                (size_t)g * a.max_ctx * HD;
-  const T* Vt = reinterpret_cast<const T*>(a.vcache) + (size_t)b * a.cache_b_stride +
-                (size_t)g * HD * a.max_ctx;
-  float* pbase = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * (HD + 2);
 
   const int len = a.len[b];
   const int end_max = len + a.R - 1 + a.key_off;  // keys [0, end_max) are read by some row
   if (end_max > a.max_ctx || len < 0) {
-    if (chunk == 0 && g == 0 && t == 0) raise_error(a.err, ERRBIT_CAPACITY);
+    if (chunk == 0 && g == 0 && threadIdx.x == 0) raise_error(a.err, ERRBIT_CAPACITY);
     return;
   }
-  const int n_act = (end_max + CH - 1) / CH;
-  if (chunk >= n_act) return;
+  if (chunk * CH >= end_max) return;  // uniform over the workgroup
+  const int kw0 = chunk * CH + w * KPW;
+  const T* Kc = reinterpret_cast<const T*>(a.kcache) + (size_t)b * a.cache_b_stride +
+                (size_t)g * a.max_ctx * HD;
+  const T* Vt = reinterpret_cast<const T*>(a.vcache) + (size_t)b * a.cache_b_stride +
+                (size_t)g * HD * a.max_ctx;
 
-  // The chunk's keys and values are loaded once, up front, and serve every query tile; values
-  // of positions no row may see are zeroed (they may hold anything, even NaN).
-  Frag<T> kf[SH::KB][SH::DS];
+  // ---- the wave's keys (K rows) and values (V^T runs) ----
+  Frag<T> kf[NB][2][DS];
 #pragma unroll
-  for (int kb = 0; kb < SH::KB; ++kb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int ds = 0; ds < SH::DS; ++ds) {
-      const int key = key0 + (w + kb * NWAVE) * 16 + c16;
-      const int d = ds * 32 + grp * 8;
-      if (key < end_max && d < HD) load_frag<T>(kf[kb][ds], Kc + (size_t)key * HD + d);
-      else zero_frag(kf[kb][ds]);
+    for (int h = 0; h < 2; ++h) {
+      const int key = kw0 + nb * 32 + 8 * (c16 >> 2) + 4 * h + (c16 & 3);
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const int d = ds * 32 + grp * 8;
+        if (key < end_max && d < HD) load_frag<T>(kf[nb][h][ds], Kc + (size_t)key * HD + d);
+        else zero_frag(kf[nb][h][ds]);
+      }
     }
-  Frag<T> vf[SH::DB][SH::KS];
+  Frag<T> vf[NB][DT];
 #pragma unroll
-  for (int dbi = 0; dbi < SH::DB; ++dbi)
+  for (int nb = 0; nb < NB; ++nb) {
+    const int kk = kw0 + nb * 32 + grp * 8;
 #pragma unroll
-    for (int ks = 0; ks < SH::KS; ++ks) {
-      const int db = w + dbi * NWAVE;
-      const int kk = key0 + ks * 32 + grp * 8;
-      const T* p = Vt + (size_t)(db * 16 + c16) * a.max_ctx + kk;
-      if (db >= HD / 16 || kk >= end_max) {
-        zero_frag(vf[dbi][ks]);
+    for (int dt = 0; dt < DT; ++dt) {
+      const T* p = Vt + (size_t)(dt * 16 + c16) * a.max_ctx + kk;
+      if (kk >= end_max) {
+        zero_frag(vf[nb][dt]);
       } else if (kk + 8 <= end_max) {
-        load_frag<T>(vf[dbi][ks], p);
-      } else {
+        load_frag<T>(vf[nb][dt], p);
+      } else {  // ragged end: values past end_max may hold anything, even NaN
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = (kk + e < end_max) ? Elem<T>::load(p + e) : 0.f;
-        to_frag<T>(vf[dbi][ks], y);
+        to_frag<T>(vf[nb][dt], y);
       }
     }
-  auto load_q = [&](Frag<T> (&qf)[QT][SH::DS], int q0) {
+  }
+
+  float* pbase = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * SH::PST;
+  for (int q0 = 0; q0 < Rall; q0 += 16) {
+    const int qv = q0 + c16;  // this lane's query column
+    const int row = qv / G;
+    Frag<T> qf[DS];
+    {
+      const float* qp = a.q + (((size_t)b * a.R + row) * a.hq + g * G + (qv - row * G)) * HD;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int qv = q0 + qt * 16 + c16;
-      const int row = qv / G;
-      const int h = g * G + (qv - row * G);
-      const float* qp = a.q + (((size_t)b * a.R + row) * a.hq + h) * HD;
-#pragma unroll
-      for (int ds = 0; ds < SH::DS; ++ds) {
+      for (int ds = 0; ds < DS; ++ds) {
         const int d = ds * 32 + grp * 8;
         if (qv < Rall && d < HD) {
           const float4 x0 = *reinterpret_cast<const float4*>(qp + d);
           const float4 x1 = *reinterpret_cast<const float4*>(qp + d + 4);
           const float y[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          to_frag<T>(qf[qt][ds], y);
+          to_frag<T>(qf[ds], y);
         } else {
-          zero_frag(qf[qt][ds]);
+          zero_frag(qf[ds]);
         }
       }
     }
-  };
-  Frag<T> qf[QT][SH::DS];
 
-  for (int q0 = 0; q0 < Rall; q0 += 16 * QT) {
-    load_q(qf, q0);
-    // ---- scores ----
-    f32x4 s[QT][SH::KB];
+    // ---- scores, masked, and the softmax statistics of the wave's keys ----
+    f32x4 s[NB][2];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb) {
+      for (int h = 0; h < 2; ++h) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < SH::DS; ++ds) acc = mma<T>(qf[qt][ds], kf[kb][ds], acc);
-        s[qt][kb] = acc;
+        for (int ds = 0; ds < DS; ++ds) acc = mma<T>(kf[nb][h][ds], qf[ds], acc);
+        s[nb][h] = acc;
       }
-    }
-    // ---- softmax statistics of the chunk (fixed order: lanes, then waves) ----
-    float M[QT][4];
+    const int kend = qv < Rall ? len + row + a.key_off : 0;  // keys [0, kend) are visible
+    float m = -INFINITY;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int qv = q0 + qt * 16 + grp * 4 + v;
-        const int kend = len + qv / G + a.key_off;
-        float m = -INFINITY;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int kb = 0; kb < SH::KB; ++kb) {
-          const int key = key0 + (w + kb * NWAVE) * 16 + c16;
-          const float val = (qv < Rall && key < kend) ? s[qt][kb][v] * a.scale : -INFINITY;
-          s[qt][kb][v] = val;
+        for (int v = 0; v < 4; ++v) {
+          const int key = kw0 + nb * 32 + 8 * grp + 4 * h + v;
+          const float val = key < kend ? s[nb][h][v] * a.scale : -INFINITY;
+          s[nb][h][v] = val;
           m = fmaxf(m, val);
         }
+    m = fmaxf(m, __shfl_xor(m, 16, WAVE));
+    m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+    float l = 0.f;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, WAVE));
-        if (c16 == 0) wred[w][qt * 16 + grp * 4 + v] = m;
-      }
-    __syncthreads();
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = qt * 16 + grp * 4 + v;
-        M[qt][v] = fmaxf(fmaxf(wred[0][r], wred[1][r]), fmaxf(wred[2][r], wred[3][r]));
-      }
-    __syncthreads();
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float sum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < SH::KB; ++kb) {
-          const float val = s[qt][kb][v];
-          const float p = (val == -INFINITY) ? 0.f : expf(val - M[qt][v]);
-          const int kl = (w + kb * NWAVE) * 16 + c16;
-          Elem<T>::store(&pbuf[(qt * 16 + grp * 4 + v) * CH + kl], p);
-          sum += p;
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, WAVE);
-        if (c16 == 0) wred[w][qt * 16 + grp * 4 + v] = sum;
-      }
-    __syncthreads();
-    if (w == 0 && c16 == 0) {
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int r = qt * 16 + grp * 4 + v;
-          mrow[r] = M[qt][v];
-          lrow[r] = ((wred[0][r] + wred[1][r]) + wred[2][r]) + wred[3][r];
+          const float val = s[nb][h][v];
+          const float p = val == -INFINITY ? 0.f : expf(val - m);
+          s[nb][h][v] = p;
+          l += p;
         }
+    l += __shfl_xor(l, 16, WAVE);
+    l += __shfl_xor(l, 32, WAVE);
+
+    // ---- value sum O^T[d][q] = sum_key V^T[d][key] P^T[key][q] ----
+    Frag<T> pf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = s[nb][j >> 2][j & 3];
+      to_frag<T>(pf[nb], y);
     }
-    // ---- values: O[qv][d] = sum_key P[qv][key] V[key][d] ----
+    f32x4 o[DT];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dbi = 0; dbi < SH::DB; ++dbi) {
-        const int db = w + dbi * NWAVE;
-        if (db >= HD / 16) continue;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < SH::KS; ++ks) {
-          Frag<T> pf;
-          load_frag<T>(pf, &pbuf[(qt * 16 + c16) * CH + ks * 32 + grp * 8]);
-          acc = mma<T>(pf, vf[dbi][ks], acc);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int qv = q0 + qt * 16 + grp * 4 + v;
-          if (qv < Rall) pbase[(size_t)qv * (HD + 2) + db * 16 + c16] = acc[v];
-        }
-      }
+      for (int nb = 0; nb < NB; ++nb) acc = mma<T>(vf[nb][dt], pf[nb], acc);
+      o[dt] = acc;
+    }
+
+    // ---- merge the four waves: common max, rescale, sum in wave order ----
+    if (grp == 0) {
+      mw[w][c16] = m;
+      lw[w][c16] = l;
     }
     __syncthreads();
-    if (t < QT * 16 && q0 + t < Rall) {
-      pbase[(size_t)(q0 + t) * (HD + 2) + HD] = mrow[t];
-      pbase[(size_t)(q0 + t) * (HD + 2) + HD + 1] = lrow[t];
+    float M = mw[0][c16];
+#pragma unroll
+    for (int u = 1; u < NWAVE; ++u) M = fmaxf(M, mw[u][c16]);
+    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    if (w > 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(&xch[w - 1][c16][dt * 16 + 4 * grp]) = o[dt] * f;
+    }
+    __syncthreads();
+    if (w == 0) {
+      float L = 0.f;
+#pragma unroll
+      for (int u = 0; u < NWAVE; ++u) {
+        const float mu = mw[u][c16];
+        L += mu == -INFINITY ? 0.f : lw[u][c16] * expf(mu - M);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        f32x4 y = o[dt] * f;
+#pragma unroll
+        for (int u = 0; u < NWAVE - 1; ++u)
+          y += *reinterpret_cast<const f32x4*>(&xch[u][c16][dt * 16 + 4 * grp]);
+        if (qv < Rall) *reinterpret_cast<f32x4*>(pbase + (size_t)qv * SH::PST + dt * 16 + 4 * grp) = y;
+      }
+      if (grp == 0 && qv < Rall) {
+        pbase[(size_t)qv * SH::PST + HD] = M;
+        pbase[(size_t)qv * SH::PST + HD + 1] = L;
+      }
     }
     __syncthreads();
   }
@@ -248,8 +257,9 @@ __global__ void __launch_bounds__(1024) attn_combine_kernel(AttnArgs a) {
     for (int d = t; d < hd; d += blockDim.x) Elem<T>::store(out + d, 0.f);
     return;
   }
-  const size_t cstride = (size_t)Rall * (hd + 2);
-  const float* pbase = a.part + ((size_t)b * a.hkv + g) * a.n_chunks * cstride + (size_t)qv * (hd + 2);
+  const int pst = hd + 4;  // partial row: o[hd], m, l, 2 pad
+  const size_t cstride = (size_t)Rall * pst;
+  const float* pbase = a.part + ((size_t)b * a.hkv + g) * a.n_chunks * cstride + (size_t)qv * pst;
   // chunk max over (m_c): per-thread stripes, then waves in order
   float mx = -INFINITY;
   for (int c = t; c < n_act; c += blockDim.x) {
@@ -297,27 +307,12 @@ __global__ void __launch_bounds__(1024) attn_combine_kernel(AttnArgs a) {
   }
 }
 
-template <typename T, int HD, int CH>
-void launch_ch(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.n_launch, a.hkv, a.B), block(256);
-  const int Rall = a.R * (a.hq / a.hkv);
-  if (Rall <= 16)
-    hipLaunchKernelGGL((attn_kernel<T, HD, 1, CH>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<T, HD, 2, CH>), grid, block, 0, st, a);
-}
-
 template <typename T, int HD>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
-  if constexpr (HD <= 128) {
-    if (a.chunk == 256) launch_ch<T, HD, 256>(a, st);
-    else if (a.chunk == 128) launch_ch<T, HD, 128>(a, st);
-    else return hipErrorInvalidValue;
-  } else {
-    if (a.chunk != 128) return hipErrorInvalidValue;
-    launch_ch<T, HD, 128>(a, st);
-  }
+  if (a.chunk != AttnShape<HD>::CH) return hipErrorInvalidValue;
   const int Rall = a.R * (a.hq / a.hkv);
+  dim3 grid(a.n_launch, a.hkv, a.B), block(NWAVE * WAVE);
+  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, block, 0, st, a);
   dim3 cgrid(Rall, a.hkv, a.B), cblock(1024);
   hipLaunchKernelGGL(attn_combine_kernel<T>, cgrid, cblock, 0, st, a);
   return hipGetLastError();
@@ -336,14 +331,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int attention_chunk(int head_dim) {
-  static const int forced = [] {
-    const char* e = getenv("SPECDEC_ATTN_CHUNK");
-    return e ? atoi(e) : 0;
-  }();
-  if (head_dim <= 128 && (forced == 128 || forced == 256)) return forced;
-  return 128;
-}
+int attention_chunk(int head_dim) { return head_dim <= 128 ? AttnShape<128>::CH : AttnShape<256>::CH; }
 
 bool attention_supported(int head_dim) {
   return head_dim == 64 || head_dim == 128 || head_dim == 176 || head_dim == 256;

@@ -175,9 +175,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           const int pos = a.len[b] + row + a.pos_off;
           float y = val;
           if (rot) {
-            double sn, cs;
-            sincos((double)pos * inv_freq, &sn, &cs);
-            const float c = (float)cs, s = (float)sn;
+            // angle reduced to [-pi, pi] in double, then sine and cosine in fp32
+            const double ang = (double)pos * inv_freq;
+            const double turns = rint(ang * (0.5 / M_PI));
+            const float r = (float)fma(-turns, 2.0 * M_PI, ang);
+            float s, c;
+            sincosf(r, &s, &c);
             const float x1 = second ? partner : val;
             const float x2 = second ? val : partner;
             y = second ? (x2 * c + x1 * s) : (x1 * c - x2 * s);

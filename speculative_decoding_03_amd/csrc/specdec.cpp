@@ -19,9 +19,15 @@ using namespace specdec;
 
 namespace {
 
+#ifndef SPECDEC_TARGET_WAVES
+#define SPECDEC_TARGET_WAVES 2048
+#endif
+#ifndef SPECDEC_MIN_KB_PER_WAVE
+#define SPECDEC_MIN_KB_PER_WAVE 8
+#endif
 constexpr size_t ALIGN = 256;
-constexpr int TARGET_WAVES = 2048;  // waves per projection launch (8 per CU on 256 CUs)
-constexpr int MIN_KB_PER_WAVE = 8;  // at least 8 KB of bf16 weights per tile per wave
+constexpr int TARGET_WAVES = SPECDEC_TARGET_WAVES;        // waves per projection launch
+constexpr int MIN_KB_PER_WAVE = SPECDEC_MIN_KB_PER_WAVE;  // k-blocks each wave streams at least
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -55,6 +61,15 @@ int split_for(int units, int nkb, int NU) {
   return pow2_floor(std::max(1, std::min(KW, env_int("SPECDEC_MAX_KW", 16))));
 }
 
+#ifndef SPECDEC_NW_POLICY
+#define SPECDEC_NW_POLICY 0
+#endif
+// Waves per workgroup for a split-K factor KW (a workgroup holds NW / KW whole units).
+int waves_for(int KW) {
+  if (SPECDEC_NW_POLICY == 1) return std::max(KW, 4);
+  return KW == 16 ? 16 : 8;
+}
+
 Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   Gemm g;
   g.W = W;
@@ -65,7 +80,13 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   g.NU = NU;
   g.n_units = cdiv(g.n_tiles, NU);
   g.KW = allow_split ? split_for(g.n_units, g.nkb, NU) : 1;
-  g.NW = g.KW == 16 ? 16 : 8;
+  g.NW = waves_for(g.KW);
+  if (allow_split && NU == 2 && g.n_units >= 4 * TARGET_WAVES / 8) {
+    // wide gated projections: one unit per workgroup, split four ways (measured on MI355X at
+    // the 31B gate/up shape: the small workgroups balance over the CUs as they retire)
+    g.KW = std::min(4, std::max(1, pow2_floor(g.nkb / MIN_KB_PER_WAVE)));
+    g.NW = 4;
+  }
   g.kbps = cdiv(g.nkb, g.KW);
   return g;
 }
@@ -85,7 +106,7 @@ Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
   g.NU = NU;
   g.n_units = E * g.upg;
   g.KW = split_for(top_k * g.upg, g.nkb, NU);
-  g.NW = g.KW == 16 ? 16 : 8;
+  g.NW = waves_for(g.KW);
   g.kbps = cdiv(g.nkb, g.KW);
   return g;
 }
@@ -188,7 +209,8 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.ssq_d = take((size_t)dm.Bx * (Dd / 16) * 4);
   L.amax_v = take((size_t)dm.Mx * dm.parts * 4);
   L.amax_i = take((size_t)dm.Mx * dm.parts * 4);
-  L.att_part = take((size_t)dm.Bx * c->n_kv_heads * dm.n_chunks * dm.Rall_max * (c->head_dim + 2) * 4);
+  // attention chunk partials: per (sequence, kv head, chunk) Rall rows of (o[hd], m, l, 2 pad)
+  L.att_part = take((size_t)dm.Bx * c->n_kv_heads * dm.n_chunks * dm.Rall_max * (c->head_dim + 4) * 4);
   L.err = take(64);
   L.u = take((size_t)dm.Bx * (d + Dd) * dm.esz);
   L.xd = take((size_t)dm.Bx * Dd * 4);

@@ -9,6 +9,8 @@ dispatch).  Each is scaled by what the same counter reads for a plain device cop
   python -m speculative_decoding_03_amd.profsum stats DIR --cmd CMD [--match S --last N] -o OUT
       kernel time table from DIR/*kernel_stats.csv (+ the last N dispatches of kernels whose
       name contains S, from DIR/*kernel_trace.csv)
+  python -m speculative_decoding_03_amd.profsum step DIR --index I --cmd CMD -o OUT
+      kernels of the I-th target pass (embed to accept) of DIR/*kernel_trace.csv
   python -m speculative_decoding_03_amd.profsum traffic --fetch D --write D --copy-fetch D
       --copy-write D --match S --last N --algorithmic BYTES --src FILE --cmd CMD -o OUT
       per-dispatch HBM bytes of the matching kernel, written as JSON
@@ -104,9 +106,43 @@ def cmd_stats(a) -> int:
         sel = dur[-a.last:] if a.last else dur
         if sel:
             lines += ["", f"dispatches of '{a.match}' (grid {a.grid or 'any'}): {len(dur)}; "
-                      f"last {len(sel)} (the timed "
-                      f"region): avg {sum(sel) / len(sel) / 1e3:.2f} us, "
+                      f"the last {len(sel)}: avg {sum(sel) / len(sel) / 1e3:.2f} us, "
                       f"min {min(sel) / 1e3:.2f} us, max {max(sel) / 1e3:.2f} us"]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        open(a.out, "w").write(text)
+    sys.stdout.write(text)
+    return 0
+
+
+def cmd_step(a) -> int:
+    """Kernels of one target pass (embed_kernel through accept_kernel), grouped by kernel and grid,
+    with the gaps between consecutive kernels."""
+    rows = _rows(_one(a.dir, "kernel_trace.csv"))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    starts = [i for i, r in enumerate(rows) if "embed_kernel" in r["Kernel_Name"]]
+    s = starts[a.index]
+    e = next(i for i in range(s, len(rows)) if "accept_kernel" in rows[i]["Kernel_Name"])
+    agg, order = {}, []
+    gaps = 0
+    for i in range(s, e + 1):
+        r = rows[i]
+        k = (short_name(r["Kernel_Name"]), _grid(r))
+        if k not in agg:
+            agg[k] = [0, 0]
+            order.append(k)
+        agg[k][0] += 1
+        agg[k][1] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if i > s:
+            gaps += max(0, int(r["Start_Timestamp"]) - int(rows[i - 1]["End_Timestamp"]))
+    span = int(rows[e]["End_Timestamp"]) - int(rows[s]["Start_Timestamp"])
+    lines = ["# one target pass from a rocprofv3 kernel trace", "", f"command: {a.cmd}", "",
+             f"pass {a.index} of {len(starts)}: span {span / 1e3:.1f} us, {e - s + 1} kernels, "
+             f"gaps between kernels {gaps / 1e3:.1f} us", "",
+             f"{'kernel':<40} {'grid':>9} {'calls':>6} {'total us':>10} {'avg us':>8}"]
+    for k in sorted(order, key=lambda k: -agg[k][1]):
+        n, t = agg[k]
+        lines.append(f"{k[0][:40]:<40} {k[1]:>9} {n:>6} {t / 1e3:>10.1f} {t / n / 1e3:>8.2f}")
     text = "\n".join(lines) + "\n"
     if a.out:
         open(a.out, "w").write(text)
@@ -177,6 +213,11 @@ def main(argv=None) -> int:
     s.add_argument("--grid", type=int, default=0)
     s.add_argument("--top", type=int, default=24)
     s.add_argument("-o", "--out")
+    st = sp.add_parser("step")
+    st.add_argument("dir")
+    st.add_argument("--index", type=int, default=-1)
+    st.add_argument("--cmd", required=True)
+    st.add_argument("-o", "--out")
     t = sp.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -189,7 +230,7 @@ def main(argv=None) -> int:
     t.add_argument("--cmd", required=True)
     t.add_argument("-o", "--out")
     a = p.parse_args(argv)
-    return {"copy": cmd_copy, "stats": cmd_stats, "traffic": cmd_traffic}[a.what](a)
+    return {"copy": cmd_copy, "stats": cmd_stats, "step": cmd_step, "traffic": cmd_traffic}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -7,7 +7,7 @@ probability p (the acceptance mix of the workload).  Inputs are resident in HBM 
 
 Prints one JSON line.  Default workload: the 31B-class dense configuration (64 layers, d 5120,
 40/8 heads of 128, FFN 25600, vocab 262144; drafter 4 layers x 256 with 2048 centroids; ctx
-8192, K=3, batch 1, p=0.7).
+8192, K=3, batch 1, p=0.7).  --config e2b | e4b | moe and --batch B run the other workloads.
 """
 
 from __future__ import annotations
@@ -26,9 +26,10 @@ sys.path.insert(0, ROOT)
 METRIC = "accepted tokens/s at B=1 (K=3); verify-step ms vs 1-token decode ms; HBM GB/s"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD_TEXT = {
-    "31b": "31B-class dense: 64 layers, d 5120, 40 q / 8 kv heads of 128, gated FFN 25600, vocab 262144, bf16 random-init (30.5B params, tied head); drafter 4 layers x 256 over the 5120-d backbone state, 2048 centroids x 128 tokens; ctx 8192, K=3, batch 1, drafts injected at p=0.7",
-    "e2b": "E2B-shaped: 24 layers, d 1536, 8 q / 1 kv heads of 256, gated FFN 6144, vocab 262144, bf16; drafter 4 x 256, 2048 centroids x 128; ctx 2048, K=3, batch 1, p=0.7",
-    "e4b": "E4B-shaped: 34 layers, d 2560, 8 q / 2 kv heads of 256, gated FFN 10240, vocab 262144, bf16; drafter 4 x 256, 2048 centroids; ctx 4096, K=4, batch 1, p=0.7",
+    "31b": "31B-class dense: 64 layers, d 5120, 40 q / 8 kv heads of 128, gated FFN 25600, vocab 262144, bf16 random-init (30.5B params, tied head); drafter 4 layers x 256 over the 5120-d backbone state, 2048 centroids x 128 tokens; ctx 8192, K=3, drafts injected at p=0.7",
+    "e2b": "E2B-shaped: 24 layers, d 1536, 8 q / 1 kv heads of 256, gated FFN 6144, vocab 262144, bf16; drafter 4 x 256, 2048 centroids x 128; ctx 2048, K=3, p=0.7",
+    "e4b": "E4B-shaped: 34 layers, d 2560, 8 q / 2 kv heads of 256, gated FFN 10240, vocab 262144, bf16; drafter 4 x 256, 2048 centroids; ctx 4096, K=4, p=0.7",
+    "moe": "26B-class MoE: 30 layers, d 2816, 16 q / 4 kv heads of 176, 128 experts top-8 of FFN 1408 + shared FFN 5632, vocab 262144, bf16 (48.45B params as listed); drafter 4 x 256, 2048 centroids; ctx 4096, K=3, p=0.7",
 }
 
 
@@ -36,29 +37,45 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(cfg, rows: int, keys: float) -> float:
-    """Bytes a verify (rows = K+1) or decode (rows = 1) step must move: all target weights once,
-    the KV of the visible keys per layer, the new rows' KV writes, the embedding rows."""
-    w = cfg.target_params() * 2
-    kv_read = cfg.n_layers * 2 * cfg.n_kv_heads * keys * cfg.head_dim * 2
-    kv_write = cfg.n_layers * 2 * cfg.n_kv_heads * rows * cfg.head_dim * 2
-    return w + kv_read + kv_write + rows * cfg.d_model * 2
+def expert_bytes(cfg) -> int:
+    """Bytes of one routed expert's gate, up and down matrices (bf16)."""
+    return 3 * cfg.d_model * cfg.expert_ffn * 2
 
 
-def draft_substep_bytes(cfg, keys: float, k_c: int = 1) -> float:
+def weight_bytes(cfg, experts_touched: float = 0.0) -> float:
+    """Target weight bytes a pass must read: every dense weight once; for a mixture of experts,
+    the router and shared FFN of every layer plus the experts the pass's rows were routed to
+    (experts_touched, summed over layers)."""
+    if not cfg.is_moe:
+        return cfg.target_params() * 2
+    all_experts = cfg.n_layers * cfg.n_experts * expert_bytes(cfg)
+    return cfg.target_params() * 2 - all_experts + experts_touched * expert_bytes(cfg)
+
+
+def algorithmic_bytes(cfg, B: int, rows: int, keys: float, experts_touched: float = 0.0) -> float:
+    """Bytes a verify (rows = K+1) or decode (rows = 1) pass over B sequences must move: the
+    target weights once, per sequence and layer the KV of the visible keys and the new rows' KV
+    writes, and the embedding rows."""
+    kv_read = B * cfg.n_layers * 2 * cfg.n_kv_heads * keys * cfg.head_dim * 2
+    kv_write = B * cfg.n_layers * 2 * cfg.n_kv_heads * rows * cfg.head_dim * 2
+    return weight_bytes(cfg, experts_touched) + kv_read + kv_write + B * rows * cfg.d_model * 2
+
+
+def draft_substep_bytes(cfg, B: int, keys: float, k_c: int = 1) -> float:
     D, d, qd = cfg.d_dim, cfg.d_model, cfg.q_dim
     per = D * qd * 2 + 3 * D * cfg.d_ffn
     w = (D * (d + D) + cfg.d_layers * per + d * D + cfg.n_centroids * D) * 2
-    table = k_c * cfg.cluster_size * D * 2 + D * 2
-    kv = cfg.d_layers * 2 * cfg.n_kv_heads * keys * cfg.head_dim * 2
+    table = B * (k_c * cfg.cluster_size * D * 2 + D * 2)
+    kv = B * cfg.d_layers * 2 * cfg.n_kv_heads * keys * cfg.head_dim * 2
     return w + table + kv
 
 
 def gate_up_bytes(cfg, M: int) -> float:
-    """Algorithmic bytes of one gate/up GEMM launch: the 2F x d bf16 weights once, the M bf16
-    rows of x times the norm weight and their per-16-column fp32 sums of squares in, the M bf16
-    gated-product rows out."""
-    d, F = cfg.d_model, cfg.ffn_dim
+    """Algorithmic bytes of one gate/up GEMM launch (the dense FFN, or the shared FFN of a
+    mixture-of-experts layer): the 2F x d bf16 weights once, the M bf16 rows of x times the norm
+    weight and their per-16-column fp32 sums of squares in, the M bf16 gated-product rows out."""
+    d = cfg.d_model
+    F = cfg.shared_ffn if cfg.is_moe else cfg.ffn_dim
     return 2 * F * d * 2 + M * d * 2 + M * (d // 16) * 4 + M * F * 2
 
 
@@ -82,11 +99,12 @@ def load_traffic(name: str, launch_bytes: float):
         return None
 
 
-def cpu_baseline(cfg, tokens_per_step: float, K: int) -> dict:
-    """The oracle timed on the host's cores on a bounded sample of the same workload: one decoder
-    layer at full width over the K+1 verify rows with the full synthetic KV, the tied LM head over
-    a vocabulary slice, and one drafter sub-step with the clustered head; scaled to the full
-    verify step (x n_layers, x vocab/slice) plus K drafter sub-steps."""
+def cpu_baseline(cfg, tokens_per_step: float, K: int, B: int) -> dict:
+    """The oracle, as it stands, timed on the host's cores on a bounded sample of the same
+    workload, for one sequence: the K+1 verify rows through all decoder layers at full width
+    against the full synthetic KV (every layer with layer 0's weights: the same shapes, so the
+    same work), the tied LM head over a vocabulary slice (scaled to the full vocabulary), and
+    the K drafter sub-steps with the clustered head.  B sequences cost B times one."""
     import numpy as np
 
     import oracle as O
@@ -106,42 +124,50 @@ def cpu_baseline(cfg, tokens_per_step: float, K: int) -> dict:
     for g in range(cfg.n_kv_heads):
         Kl[g, :ctx] = S.kv_rows(cfg, "k", 0, 0, g, 0, ctx)
         Vl[g, :ctx] = S.kv_rows(cfg, "v", 0, 0, g, 0, ctx)
-    slice_rows = 8192
+    slice_rows = 32768
     E_slice = S.gen_rows(cfg, "embed", 0, cfg.d_model, 0, slice_rows).astype(np.float64)
+    fnorm = S.norm_weight(cfg, "final_norm", 0, cfg.d_model).astype(np.float64)
     hid, t0 = S.state_init(cfg)
     x0 = hid[0].astype(np.float64)
+    DW = O.as_f64(S.drafter_weights(cfg))
+    if cfg.is_moe:  # generate the experts the sample routes to outside the timed region
+        for i in range(K + 1):
+            O.decoder_layer_row(lw, cfg, Kl, Vl, x0, ctx + i)
     gen_s = time.perf_counter() - t_gen
 
     t = time.perf_counter()
-    x = x0
+    H = []
     for i in range(K + 1):
-        x = O.decoder_layer_row(lw, cfg, Kl, Vl, x0, ctx + i)
-    t_layer = time.perf_counter() - t
+        x = x0
+        for _ in range(cfg.n_layers):
+            x = O.decoder_layer_row(lw, cfg, Kl, Vl, x, ctx + i)
+        H.append(x)
+    t_layers = time.perf_counter() - t
     t = time.perf_counter()
-    for i in range(K + 1):
-        _ = E_slice @ O.rmsnorm(x, np.ones(cfg.d_model), cfg.rms_eps)
-    t_head = (time.perf_counter() - t) * (cfg.vocab / slice_rows)
-    del lw
-    # drafter sub-step (all drafter layers attend the same synthetic layer: reuse Kl / Vl)
-    DW = O.as_f64(S.drafter_weights(cfg))
-
+    for x in H:
+        _ = E_slice @ O.rmsnorm(x, fnorm, cfg.rms_eps)
+    t_head_slice = time.perf_counter() - t
+    t_head = t_head_slice * (cfg.vocab / slice_rows)
     cache = O.KVCache([None] * cfg.n_layers, [None] * cfg.n_layers)
     cache.K[cfg.src_layer] = Kl
     cache.V[cfg.src_layer] = Vl
     t = time.perf_counter()
-    O.drafter_substep(DW, cfg, cache, x0, int(t0[0]), ctx, ctx, "clustered", 1)
+    O.draft(DW, cfg, cache, x0, int(t0[0]), ctx, K, head_mode="clustered", k_c=1)
     t_draft = time.perf_counter() - t
-    step_s = cfg.n_layers * t_layer + t_head + K * t_draft
+    step_s = t_layers + t_head + t_draft
+    timed = t_layers + t_head_slice + t_draft
     return {
-        "value": round(tokens_per_step / step_s, 4),
+        "value": round(B * tokens_per_step / (B * step_s), 4),
         "unit": "tokens/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle on {int(cores)} threads: 1 of {cfg.n_layers} decoder layers "
-                   f"(full width, {ctx}-position KV) over the {K + 1} verify rows ({t_layer:.2f} s), "
-                   f"LM head on {slice_rows} of {cfg.vocab} vocab rows, 1 drafter sub-step "
-                   f"({t_draft:.2f} s); extrapolated to one full step = {step_s:.1f} s at "
-                   f"{tokens_per_step:.2f} tokens/step (input generation {gen_s:.1f} s not timed)"),
+        "sample": (f"float64 numpy oracle on {int(cores)} threads, one sequence: the {K + 1} verify "
+                   f"rows through all {cfg.n_layers} layers at full width over the {ctx}-position "
+                   f"KV, each layer with layer 0's weights ({t_layers:.1f} s); the tied LM head on "
+                   f"{slice_rows} of {cfg.vocab} vocabulary rows ({t_head_slice:.1f} s, scaled to "
+                   f"{t_head:.1f} s); {K} drafter sub-steps ({t_draft:.1f} s).  {timed:.1f} s timed, "
+                   f"one step = {step_s:.1f} s at {tokens_per_step:.2f} tokens/step; input "
+                   f"generation {gen_s:.1f} s not timed"),
     }
 
 
@@ -151,6 +177,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="31b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--batch", type=int, default=1, help="independent sequences per step")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--head", default="clustered", choices=["clustered", "full"])
     ap.add_argument("--k-c", type=int, default=1)
@@ -171,104 +198,120 @@ def main() -> int:
     from workloads import device as WD
     from workloads import inject_table, preset
 
-    cfg = preset(args.config)
+    B = args.batch
+    cfg = preset(args.config, batch=B)
     if args.p is not None:
         cfg = cfg.replace(p_inject=args.p)
     K, W, N = cfg.draft_k, args.warmup, args.steps
     # steps after the timed region whose gate/up launches are timed one by one (events attached
     # to the dispatches add gaps between kernels, so they stay out of the timed region)
     P = 0 if args.no_kernel_profile else min(N, 8)
+    S_all = W + N + P
     head_mode = SD.HEAD_FULL if args.head == "full" else SD.HEAD_CLUSTERED
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
     t_setup = time.perf_counter()
-    n_greedy = (W + N + P) * (K + 1) + K + 2
+    n_greedy = S_all * (K + 1) + K + 2
     max_ctx = (cfg.ctx + n_greedy + 64 + 7) // 8 * 8
-    log(f"setup {cfg.name}: weights on device ({cfg.target_params() / 1e9:.2f}B target params)")
+    log(f"setup {cfg.name}: weights on device ({cfg.target_params() / 1e9:.2f}B target params), B={B}")
     perm, cent = WD.clusters(cfg)
     model = E.DeviceModel(E.Shape.of(cfg), WD.DeviceSource(cfg), perm, cent)
-    eng = E.Engine(model, max_batch=1, max_draft=K, max_rows=max(16, K + 1), max_ctx=max_ctx)
+    eng = E.Engine(model, max_batch=B, max_draft=K, max_rows=max(16 // B, K + 1), max_ctx=max_ctx)
     WD.fill_kv(eng, cfg)
-    t0 = WD.start_state(eng, cfg)
+    t0 = WD.start_state(eng, cfg)  # [B] int32
     hid0 = eng.hid.clone()
     torch.cuda.synchronize()
     log(f"setup done in {time.perf_counter() - t_setup:.1f} s")
 
     def restore():
         eng.hid.copy_(hid0)
-        eng.set_len([cfg.ctx])
+        eng.set_len([cfg.ctx] * B)
 
     # ---- plain greedy decoding (1-row verify + fused accept/commit): decode-step timing ----
-    cur = t0.view(1, 1).clone()
-    gbuf = torch.empty(n_greedy, dtype=torch.int32, device=dev)
+    cur = t0.clone().view(B, 1)
+    gbuf = torch.empty(n_greedy, B, dtype=torch.int32, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_greedy + 1)]
     torch.cuda.synchronize()
+    if cfg.is_moe:
+        eng.moe_usage_start()
     ev[0].record()
     for i in range(n_greedy):
         eng.verify(cur)
-        eng.accept(cur, out_tokens=gbuf[i:i + 1], next_tok=cur, commit=True)
+        eng.accept(cur, out_tokens=gbuf[i].view(B, 1), next_tok=cur, commit=True)
         ev[i + 1].record()
     torch.cuda.synchronize()
+    dec_experts = sum(eng.moe_usage_read()) / n_greedy if cfg.is_moe else 0.0
     dec_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(W, n_greedy)]
-    greedy = [int(t0.item())] + gbuf.cpu().tolist()
+    g_host = gbuf.cpu().numpy()
+    greedy = [[int(t0[b].item())] + g_host[:, b].tolist() for b in range(B)]
     assert eng.device_error() == 0, "device error during greedy decoding"
     log(f"greedy: {n_greedy} decode steps, median {np.median(dec_ms):.3f} ms")
 
-    # ---- speculative loop ----
+    # ---- speculative loop: draft -> verify -> accept + commit, B sequences per step ----
     restore()
-    gseq = np.full(max_ctx, -1, dtype=np.int64)
-    gseq[cfg.ctx:cfg.ctx + len(greedy)] = greedy
-    tab = torch.from_numpy(inject_table(gseq, K, cfg.p_inject, cfg.inject_seed).reshape(1, -1)).to(dev)
-    T = torch.empty(1, K + 1, dtype=torch.int32, device=dev)
-    T[0, 0] = int(t0.item())
-    drafts = T[:, 1:]
-    S = W + N + P
-    outs = torch.full((S, K + 1), -1, dtype=torch.int32, device=dev)
-    n_emit = torch.zeros(S, dtype=torch.int32, device=dev)
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
-    e2 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+    tabs = []
+    for b in range(B):
+        gseq = np.full(max_ctx, -1, dtype=np.int64)
+        gseq[cfg.ctx:cfg.ctx + len(greedy[b])] = greedy[b]
+        tabs.append(inject_table(gseq, K, cfg.p_inject, cfg.inject_seed, b=b))
+    tab = torch.from_numpy(np.stack(tabs)).to(dev)
+    cur = t0.clone()                    # current token per sequence
+    drafts = torch.empty(B, K, dtype=torch.int32, device=dev)
+    T = torch.empty(B, K + 1, dtype=torch.int32, device=dev)  # verify rows, written by the draft
+    outs = torch.full((S_all, B, K + 1), -1, dtype=torch.int32, device=dev)
+    n_emit = torch.zeros(S_all, B, dtype=torch.int32, device=dev)
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(S_all)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(S_all)]
+    e2 = [torch.cuda.Event(enable_timing=True) for _ in range(S_all)]
 
     def step(i):
         e0[i].record()
-        eng.draft(T[:, 0], drafts, head_mode=head_mode, k_c=args.k_c, inject=tab)
+        eng.draft(cur, drafts, head_mode=head_mode, k_c=args.k_c, inject=tab, verify_tokens=T)
         e1[i].record()
         eng.verify(T)
-        eng.accept(T, out_tokens=outs[i:i + 1], n_emit=n_emit[i:i + 1], next_tok=T[:, 0], commit=True)
+        eng.accept(T, out_tokens=outs[i], n_emit=n_emit[i], next_tok=cur, commit=True)
         e2[i].record()
 
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+    if cfg.is_moe:
+        eng.moe_usage_start()
     t_start = time.perf_counter()
     for i in range(W, W + N):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    ver_experts = sum(eng.moe_usage_read()) / N if cfg.is_moe else 0.0
     gate_ms = []
     if P:
         eng.profile_start(SD.ffi.PROF_GATE_UP, cfg.n_layers * P)
-        for i in range(W + N, S):
+        for i in range(W + N, S_all):
             step(i)
         gate_ms = eng.profile_read()
     assert eng.device_error() == 0, "device error during the speculative loop"
 
-    ne = n_emit.cpu().tolist()
-    ot = outs.cpu().tolist()
-    spec = [int(greedy[0])]
-    for i in range(S):
-        spec.extend(ot[i][: ne[i]])
-    same = spec[: len(spec)] == greedy[: len(spec)]
-    emitted = sum(ne[W:W + N])
-    accepted = emitted - N
+    ne = n_emit.cpu().numpy()
+    ot = outs.cpu().numpy()
+    same = True
+    for b in range(B):
+        spec = [int(t0[b].item())]
+        for i in range(S_all):
+            spec.extend(ot[i, b, : ne[i, b]].tolist())
+        same &= spec == greedy[b][: len(spec)]
+    emitted = int(ne[W:W + N].sum())
+    accepted = emitted - N * B
     tok_s = emitted / wall
     draft_ms = [e0[i].elapsed_time(e1[i]) for i in range(W, W + N)]
     ver_ms = [e1[i].elapsed_time(e2[i]) for i in range(W, W + N)]
     med = lambda v: float(np.median(v))  # noqa: E731
-    keys = cfg.ctx + (W + N) * 2.5 / 2 + K + 1
-    v_bytes = algorithmic_bytes(cfg, K + 1, keys)
-    d_bytes = algorithmic_bytes(cfg, 1, keys - K)
+    # visible keys of a timed verify: committed length at the step's start + K + 1, averaged
+    start_len = cfg.ctx + np.cumsum(np.concatenate([np.zeros((1, B)), ne[:-1]]), axis=0)
+    keys_v = float(start_len[W:W + N].mean()) + K + 1
+    keys_d = cfg.ctx + n_greedy / 2 + 1
+    v_bytes = algorithmic_bytes(cfg, B, K + 1, keys_v, ver_experts)
+    d_bytes = algorithmic_bytes(cfg, B, 1, keys_d, dec_experts)
     res = {
         "metric": METRIC,
         "value": round(tok_s, 3),
@@ -282,7 +325,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "batch": 1, "K": K, "ctx": cfg.ctx,
+        "config": {"workload": WORKLOAD_TEXT[args.config], "batch": B, "K": K, "ctx": cfg.ctx,
                    "p_inject": cfg.p_inject, "head": f"{args.head} k_c={args.k_c}"},
         "verify_ms": round(med(ver_ms), 4),
         "decode_ms": round(med(dec_ms), 4),
@@ -291,20 +334,29 @@ def main() -> int:
         "verify_hbm_gbs": round(v_bytes / (med(ver_ms) * 1e-3) / 1e9, 1),
         "decode_hbm_gbs": round(d_bytes / (med(dec_ms) * 1e-3) / 1e9, 1),
         "verify_hbm_frac": round(v_bytes / (med(ver_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "tokens_per_step": round(emitted / N, 4),
-        "accepted_over_proposed": round(accepted / (N * K), 4),
+        "verify_bytes": round(v_bytes),
+        "decode_bytes": round(d_bytes),
+        "tokens_per_step": round(emitted / (N * B), 4),
+        "accepted_over_proposed": round(accepted / (N * B * K), 4),
         "spec_equals_greedy": bool(same),
-        "draft_substep_mb": round(draft_substep_bytes(cfg, keys) / 1e6, 2),
+        "draft_substep_mb": round(draft_substep_bytes(cfg, B, keys_v) / 1e6, 2),
     }
+    if cfg.is_moe:
+        res["moe"] = {"experts_read_per_verify": round(ver_experts, 1),
+                      "experts_read_per_decode": round(dec_experts, 1),
+                      "experts_per_layer": cfg.n_experts, "layers": cfg.n_layers}
     if gate_ms:
         launch_ms = float(np.mean(gate_ms))
-        lb = gate_up_bytes(cfg, K + 1)
+        M = B * (K + 1)
+        lb = gate_up_bytes(cfg, M)
         achieved = lb / (launch_ms * 1e-3) / 1e9
-        traffic = load_traffic(f"gemm_gate_up_{args.config}", lb)
+        traffic = load_traffic(f"gemm_gate_up_{args.config}" + (f"_b{B}" if B > 1 else ""), lb)
         kw, units, nw, groups = eng.query_split(0)
+        what = "shared-FFN gate/up" if cfg.is_moe else "FFN gate/up"
         res["roofline"] = {
-            "kernel": f"gemm_kernel<bf16, 1, 2, 2, {nw}> (FFN gate/up + SiLU product, verify "
-                      f"M={K + 1}, grid {groups * nw * 64} work-items, split-K {kw})",
+            "kernel": f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}> "
+                      f"({what} + SiLU product, verify M={M}, grid {groups * nw * 64} work-items, "
+                      f"split-K {kw})",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -319,7 +371,7 @@ def main() -> int:
         }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores, bounded sample)")
-        res["cpu_baseline"] = cpu_baseline(cfg, emitted / N, K)
+        res["cpu_baseline"] = cpu_baseline(cfg, emitted / (N * B), K, B)
     eng.close()
     print(json.dumps(res), flush=True)
     return 0

@@ -170,11 +170,14 @@ int specdec_destroy(specdec_ctx* ctx);
    Ties -> lower vocabulary id.  Output drafts int32 [B][K] (device).
    Optional workload injection (tests and benchmarks; NULL = off): inject int32 [B][inj_stride]
    (device); entry (len[b]+j)*K + (j-1) >= 0 replaces draft j after it was drafted (the drafter's
-   own token still feeds sub-step j+1).  Errors: SPECDEC_E_INVAL (B > max_batch, K < 1,
-   K > max_draft, k_c outside [1, n_centroids], null pointers). */
+   own token still feeds sub-step j+1).  Optional verify_tokens int32 [B][K+1] (device; NULL =
+   skip) receives the next verify's input rows [c0, d1..dK] (drafts after injection), so a batch
+   goes from draft to verify without a copy; it may overlap cur_tok at column 0.
+   Errors: SPECDEC_E_INVAL (B > max_batch, K < 1, K > max_draft, k_c outside [1, n_centroids],
+   null pointers). */
 int specdec_draft(specdec_ctx* ctx, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
                   const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
-                  int64_t inj_stride, void* stream);
+                  int64_t inj_stride, int32_t* verify_tokens, void* stream);
 
 /* Target forward over n_rows rows per sequence: tokens int32 [B][n_rows] (device) at positions
    len[b] .. len[b]+n_rows-1.  Row i attends keys [0, len[b]+i].  Appends the rows' keys and
@@ -225,6 +228,14 @@ int specdec_read_device_error(specdec_ctx* ctx, int32_t* host_word, int32_t clea
    graph capture. */
 int specdec_profile_start(specdec_ctx* ctx, int32_t kernel_class, int32_t capacity);
 int specdec_profile_read(specdec_ctx* ctx, float* ms_out, int32_t max, int32_t* n_out);
+
+/* Mixture-of-experts measurement: specdec_moe_usage_start zeroes per-layer counters (enqueued on
+   `stream`) and from then on each verify adds, per layer, the number of distinct experts its rows
+   were routed to (the experts whose weights it read).  specdec_moe_usage_read synchronises
+   `stream`, copies the n_layers counters to host memory and stops counting.  Errors:
+   SPECDEC_E_INVAL for a dense model or null pointers. */
+int specdec_moe_usage_start(specdec_ctx* ctx, void* stream);
+int specdec_moe_usage_read(specdec_ctx* ctx, int32_t* per_layer, void* stream);
 
 /* Launch shape the context uses for a GEMM class (classes 0, 1, 2, 3, 5 above; tests and
    reports; classes 7, 8 for a mixture-of-experts model): split-K factor, work units, waves per

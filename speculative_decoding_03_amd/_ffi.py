@@ -25,6 +25,7 @@ EXPORTS = [
     "specdec_draft", "specdec_verify", "specdec_accept", "specdec_kv_commit",
     "specdec_pack_matrix", "specdec_set_len_bound", "specdec_read_device_error",
     "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
+    "specdec_moe_usage_start", "specdec_moe_usage_read",
 ]
 
 
@@ -65,7 +66,9 @@ def load(path: str = LIB_PATH):
         "specdec_kv_elems": (sz, [P(Config)]),
         "specdec_create": (C.c_int, [P(Config), P(Weights), vp, vp, vp, vp, vp, sz, vp, P(vp)]),
         "specdec_destroy": (C.c_int, [vp]),
-        "specdec_draft": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, i64, vp]),
+        "specdec_draft": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp]),
+        "specdec_moe_usage_start": (C.c_int, [vp, vp]),
+        "specdec_moe_usage_read": (C.c_int, [vp, P(i32), vp]),
         "specdec_verify": (C.c_int, [vp, i32, i32, vp, vp, vp, vp]),
         "specdec_accept": (C.c_int, [vp, i32, i32, vp, vp, vp, vp, u32, vp]),
         "specdec_kv_commit": (C.c_int, [vp, i32, vp, vp]),

@@ -144,9 +144,10 @@ hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const v
 // grouped GEMMs: for expert e and its i-th routed row m (ascending m), xrow[e*M+i] = m,
 // orow[e*M+i] = m*top_k + r (r = rank of e among the row's experts in ascending id) and
 // wt[e*M+i] = its weight; -1 beyond the expert's count.  group_list = experts with at least one
-// row, ascending, n_groups[0] of them.
+// row, ascending, n_groups[0] of them.  usage (optional): += n_groups.
 hipError_t launch_moe_route(const float* logits, int M, int E, int top_k, int* xrow, int* orow,
-                            float* wt, int* group_list, int* n_groups, int* err, hipStream_t st);
+                            float* wt, int* group_list, int* n_groups, int* usage, int* err,
+                            hipStream_t st);
 hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int tiles_per_cluster,
                                  int units_per_cluster, int* unit_tile, int* unit_row, int* err,
                                  hipStream_t st);
@@ -154,7 +155,7 @@ hipError_t launch_draft_finalize(const float* amax_val, const int* amax_idx, int
                                  int parts_per_seq, int seq_offset, int B, int K, int j,
                                  const int* len,
                                  const int* inject, int inj_stride, int* drafts, int* dtok,
-                                 int* err, hipStream_t st);
+                                 const int* cur_tok, int* vtok, int* err, hipStream_t st);
 hipError_t launch_pack(int dtype, const void* src, void* dst, int N, int Kd, int kind, int hd,
                        int split_rows, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int v, size_t n, hipStream_t st);

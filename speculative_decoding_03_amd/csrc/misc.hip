@@ -231,7 +231,7 @@ constexpr int MOE_MAX_M = 64, MOE_MAX_E = 256, MOE_MAX_K = 16;
 __global__ void __launch_bounds__(256) moe_route_kernel(const float* logits, int M, int E,
                                                         int top_k, int* xrow, int* orow,
                                                         float* wt, int* group_list,
-                                                        int* n_groups, int* err) {
+                                                        int* n_groups, int* usage, int* err) {
   __shared__ int sel[MOE_MAX_M][MOE_MAX_K];
   __shared__ float selw[MOE_MAX_M][MOE_MAX_K];
   __shared__ int cnt[MOE_MAX_E];
@@ -327,7 +327,11 @@ __global__ void __launch_bounds__(256) moe_route_kernel(const float* logits, int
   int off = 0;
   for (int w = 0; w < wid; ++w) off += wtot[w];
   if (used) group_list[off + __popcll(mask & ((1ull << lane) - 1ull))] = e;
-  if (threadIdx.x == 0) n_groups[0] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  if (threadIdx.x == 0) {
+    const int ng = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    n_groups[0] = ng;
+    if (usage) usage[0] += ng;  // one writer: the launches of a layer are ordered on the stream
+  }
 }
 
 // Reduces a sequence's head partials to the drafted token, records it as the next sub-step's
@@ -335,7 +339,7 @@ __global__ void __launch_bounds__(256) moe_route_kernel(const float* logits, int
 __global__ void __launch_bounds__(256) draft_finalize_kernel(
     const float* amax_val, const int* amax_idx, int ld_amax, int parts_per_seq, int seq_offset,
     int K, int j, const int* len, const int* inject, int inj_stride, int* drafts, int* dtok,
-    int* err) {
+    const int* cur_tok, int* vtok, int* err) {
   __shared__ float rv[4];
   __shared__ int ri[4];
   const int b = blockIdx.x;
@@ -360,6 +364,10 @@ __global__ void __launch_bounds__(256) draft_finalize_kernel(
       }
     }
     drafts[b * K + (j - 1)] = out;
+    if (vtok) {  // the verify input row [c0, d1..dK]
+      if (j == 1) vtok[b * (K + 1)] = cur_tok[b];
+      vtok[b * (K + 1) + j] = out;
+    }
   }
 }
 
@@ -450,22 +458,24 @@ hipError_t launch_cluster_select(const float* z, int Nc, int k_c, int B, int til
 }
 
 hipError_t launch_moe_route(const float* logits, int M, int E, int top_k, int* xrow, int* orow,
-                            float* wt, int* group_list, int* n_groups, int* err, hipStream_t st) {
+                            float* wt, int* group_list, int* n_groups, int* usage, int* err,
+                            hipStream_t st) {
   if (M < 1 || M > MOE_MAX_M || E < 1 || E > MOE_MAX_E || top_k < 1 || top_k > MOE_MAX_K ||
       top_k > E)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(256), 0, st, logits, M, E, top_k, xrow, orow,
-                     wt, group_list, n_groups, err);
+                     wt, group_list, n_groups, usage, err);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_finalize(const float* amax_val, const int* amax_idx, int ld_amax,
                                  int parts_per_seq, int seq_offset, int B, int K, int j,
                                  const int* len, const int* inject, int inj_stride, int* drafts,
-                                 int* dtok, int* err, hipStream_t st) {
+                                 int* dtok, const int* cur_tok, int* vtok, int* err,
+                                 hipStream_t st) {
   hipLaunchKernelGGL(draft_finalize_kernel, dim3(B), dim3(256), 0, st, amax_val, amax_idx,
                      ld_amax, parts_per_seq, seq_offset, K, j, len, inject, inj_stride, drafts,
-                     dtok, err);
+                     dtok, cur_tok, vtok, err);
   return hipGetLastError();
 }
 

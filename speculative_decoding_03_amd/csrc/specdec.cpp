@@ -113,7 +113,7 @@ Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
 
 struct Layout {
   size_t x, xw, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err;
-  size_t rlog, e_xrow, e_orow, e_wt, e_groups, e_ngroups, e_h, e_y;
+  size_t rlog, e_xrow, e_orow, e_wt, e_groups, e_ngroups, e_h, e_y, e_usage;
   size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
   size_t total;
 };
@@ -142,6 +142,7 @@ struct specdec_ctx {
   std::vector<int> len_hi;  // host-side upper bound on len
   int last_B = 0, last_R = 0;
   int prof_class = -1, prof_cap = 0, prof_n = 0;
+  bool moe_usage_on = false;
   std::vector<hipEvent_t> prof_ev;
 };
 
@@ -232,6 +233,7 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.e_ngroups = take(4);
   L.e_h = take(slots * c->expert_ffn * dm.esz);
   L.e_y = take(slots * d * 4);
+  L.e_usage = take((size_t)c->n_layers * 4);  // experts routed to, summed per layer (measurement)
   L.total = off;
   return L;
 }
@@ -377,7 +379,8 @@ int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
     if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
   }
   HIP_TRY(launch_moe_route(at<float>(x, x->lay.rlog), M, E, c.top_k, xrow, orow, wt, groups,
-                           ngroups, at<int>(x, x->lay.err), st));
+                           ngroups, x->moe_usage_on ? at<int>(x, x->lay.e_usage) + l : nullptr,
+                           at<int>(x, x->lay.err), st));
   // at most min(E, M*top_k) experts are routed to
   const int max_groups = std::min(E, M * c.top_k);
   {  // gate/up of the routed experts over their rows -> SiLU product at the row's slot
@@ -630,7 +633,7 @@ int specdec_kv_commit(specdec_ctx* x, int32_t B, const int32_t* n_commit, void* 
 
 int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
                   const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
-                  int64_t inj_stride, void* stream) {
+                  int64_t inj_stride, int32_t* verify_tokens, void* stream) {
   if (!x || !cur_tok || !drafts) return SPECDEC_E_INVAL;
   const specdec_config& c = x->cfg;
   if (B < 1 || B > c.max_batch || K < 1 || K > c.max_draft) return SPECDEC_E_INVAL;
@@ -750,7 +753,8 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
       }
       HIP_TRY(launch_draft_finalize(at<float>(x, x->lay.d_amax_v), at<int>(x, x->lay.d_amax_i), ld,
                                     parts_per_seq, seq_off, B, K, j, x->len, inject,
-                                    (int)inj_stride, drafts, dtok, err, st));
+                                    (int)inj_stride, drafts, dtok, cur_tok, verify_tokens, err,
+                                    st));
     }
   }
   return SPECDEC_OK;
@@ -785,6 +789,24 @@ int specdec_read_device_error(specdec_ctx* x, int32_t* host_word, int32_t clear,
   HIP_TRY(hipMemcpyAsync(host_word, at<int>(x, x->lay.err), 4, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
   if (clear) HIP_TRY(launch_fill_i32(at<int>(x, x->lay.err), 0, 1, st));
+  return SPECDEC_OK;
+}
+
+int specdec_moe_usage_start(specdec_ctx* x, void* stream) {
+  if (!x || x->cfg.n_experts == 0) return SPECDEC_E_INVAL;
+  HIP_TRY(launch_fill_i32(at<int>(x, x->lay.e_usage), 0, (size_t)x->cfg.n_layers,
+                          reinterpret_cast<hipStream_t>(stream)));
+  x->moe_usage_on = true;
+  return SPECDEC_OK;
+}
+
+int specdec_moe_usage_read(specdec_ctx* x, int32_t* per_layer, void* stream) {
+  if (!x || !per_layer || x->cfg.n_experts == 0) return SPECDEC_E_INVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(hipMemcpyAsync(per_layer, at<int>(x, x->lay.e_usage), (size_t)x->cfg.n_layers * 4,
+                         hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  x->moe_usage_on = false;
   return SPECDEC_OK;
 }
 

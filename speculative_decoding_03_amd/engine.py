@@ -257,11 +257,26 @@ class Engine:
                 "specdec_kv_commit")
 
     def draft(self, cur_tok, drafts, head_mode=F.HEAD_CLUSTERED, k_c=1, inject=None,
-              stream=None) -> None:
+              verify_tokens=None, stream=None) -> None:
+        """Drafts [B][K] from cur_tok [B]; optionally also writes the verify input rows
+        verify_tokens [B][K+1] = [cur, d1..dK] (after injection)."""
         B, K = drafts.shape
+        if verify_tokens is not None:
+            assert verify_tokens.is_contiguous() and tuple(verify_tokens.shape) == (B, K + 1)
         stride = 0 if inject is None else inject.shape[1]
         F.check(self.lib.specdec_draft(self.ctx, B, K, head_mode, k_c, _p(cur_tok), _p(drafts),
-                                       _p(inject), stride, _s(stream)), "specdec_draft")
+                                       _p(inject), stride, _p(verify_tokens), _s(stream)),
+                "specdec_draft")
+
+    def moe_usage_start(self, stream=None) -> None:
+        F.check(self.lib.specdec_moe_usage_start(self.ctx, _s(stream)), "specdec_moe_usage_start")
+
+    def moe_usage_read(self, stream=None) -> list:
+        """Per layer, the summed number of distinct experts routed to since moe_usage_start."""
+        n = self.shape.n_layers
+        buf = (C.c_int32 * n)()
+        F.check(self.lib.specdec_moe_usage_read(self.ctx, buf, _s(stream)), "specdec_moe_usage_read")
+        return [buf[i] for i in range(n)]
 
     # --- measurement helpers ---
     def profile_start(self, kernel_class: int, capacity: int) -> None:

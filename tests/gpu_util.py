@@ -90,6 +90,64 @@ def gpu_spec(eng, t0: int, n: int, K: int, inject_tab=None, head_mode=SD.HEAD_CL
     return toks[:n], emitted
 
 
+def gpu_prefill_batch(eng, prompts: np.ndarray, chunk: int = 16):
+    """verify(chunk) + kv_commit(chunk) over B equal-length prompts [B][L]; returns the first
+    generated token of each sequence."""
+    dev = eng.kv_k.device
+    B, L = prompts.shape
+    am = None
+    for s in range(0, L, chunk):
+        part = torch.tensor(prompts[:, s:s + chunk], dtype=torch.int32, device=dev).contiguous()
+        am = torch.empty(B, part.shape[1], dtype=torch.int32, device=dev)
+        eng.verify(part, argmax=am)
+        eng.kv_commit(torch.full((B,), part.shape[1], dtype=torch.int32, device=dev))
+    eng.set_len_bound([L] * B)
+    return am[:, -1].cpu().tolist()
+
+
+def gpu_greedy_batch(eng, t0s, n: int):
+    """Plain greedy decoding of B sequences at once (verify of one row each + accept)."""
+    dev = eng.kv_k.device
+    B = len(t0s)
+    cur = torch.tensor(t0s, dtype=torch.int32, device=dev).view(B, 1)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    toks = [[int(t)] for t in t0s]
+    while len(toks[0]) < n:
+        eng.verify(cur)
+        eng.accept(cur, next_tok=nxt, commit=True)
+        cur = nxt.view(B, 1).clone()
+        for b, t in enumerate(nxt.cpu().tolist()):
+            toks[b].append(t)
+    return toks
+
+
+def gpu_spec_batch(eng, t0s, n: int, K: int, inject_tabs: np.ndarray):
+    """The speculative loop over B sequences at once, the draft writing the verify rows."""
+    dev = eng.kv_k.device
+    B = len(t0s)
+    cur = torch.tensor(t0s, dtype=torch.int32, device=dev)
+    drafts = torch.empty(B, K, dtype=torch.int32, device=dev)
+    T = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    out = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    n_emit = torch.empty(B, dtype=torch.int32, device=dev)
+    inj = torch.from_numpy(np.ascontiguousarray(inject_tabs)).to(dev)
+    toks = [[int(t)] for t in t0s]
+    lengths = eng.len[:B].cpu().tolist()
+    emitted = []
+    while min(len(t) for t in toks) < n:
+        eng.draft(cur, drafts, inject=inj, verify_tokens=T)
+        eng.verify(T)
+        eng.accept(T, out_tokens=out, n_emit=n_emit, next_tok=cur, commit=True)
+        e = n_emit.cpu().tolist()
+        o = out.cpu().tolist()
+        for b in range(B):
+            toks[b].extend(o[b][: e[b]])
+            lengths[b] += e[b]
+        emitted.append(e)
+        eng.set_len_bound(lengths)
+    return [t[:n] for t in toks], emitted
+
+
 def snapshot(eng):
     return eng.len.clone(), eng.hid.clone()
 

@@ -1,0 +1,92 @@
+"""The C ABI without a GPU: the built library loads, exports every function include/specdec.h
+declares, and its host-only calls (workspace sizing and configuration checks, error strings)
+behave as documented.  No call here launches a kernel."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from speculative_decoding_03_amd import _ffi as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specdec.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(specdec_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(F.LIB_PATH):
+        pytest.fail(f"{F.LIB_PATH} is not built: run __graft_entry__.build()")
+    return F.load()
+
+
+def test_header_declares_the_step_calls():
+    names = declared_functions()
+    for n in ("specdec_draft", "specdec_verify", "specdec_accept", "specdec_kv_commit",
+              "specdec_create", "specdec_destroy", "specdec_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert sorted(F.EXPORTS) == names, "the binding's export list differs from the header"
+
+
+def _config(**kw):
+    c = F.Config()
+    base = dict(n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=1024,
+                vocab=4096, n_experts=0, top_k=0, expert_ffn=0, shared_ffn=0, d_layers=1,
+                d_dim=128, d_ffn=512, n_centroids=64, kv_src_layer=-1, dtype=F.F32,
+                max_batch=1, max_draft=3, max_rows=16, max_ctx=256)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(c, k, v)
+    c.rms_eps, c.rope_theta = 1e-6, 10000.0
+    return c
+
+
+def test_workspace_sizing_and_config_checks(lib):
+    ws = lib.specdec_workspace_bytes(C.byref(_config()))
+    assert ws > 0 and ws % 256 == 0
+    # grows with the batch and context
+    assert lib.specdec_workspace_bytes(C.byref(_config(max_batch=4, max_ctx=1024))) > ws
+    # KV elements: n_layers * max_batch * n_kv_heads * max_ctx * head_dim
+    assert lib.specdec_kv_elems(C.byref(_config())) == 2 * 1 * 2 * 256 * 64
+    bad = [dict(d_model=250), dict(head_dim=72 + 1), dict(n_q_heads=3), dict(vocab=4000),
+           dict(max_ctx=250), dict(max_rows=65), dict(max_batch=8, max_rows=16),
+           dict(max_draft=16, max_rows=16), dict(n_centroids=48), dict(dtype=7),
+           dict(n_experts=24, top_k=4, expert_ffn=128, shared_ffn=256, ffn_dim=0),
+           dict(n_experts=16, top_k=17, expert_ffn=128, shared_ffn=256, ffn_dim=0),
+           dict(n_experts=16, top_k=4, expert_ffn=100, shared_ffn=256, ffn_dim=0)]
+    for kw in bad:
+        assert lib.specdec_workspace_bytes(C.byref(_config(**kw))) == 0, kw
+    # a mixture-of-experts configuration is valid and needs its routing buffers
+    moe = _config(n_experts=16, top_k=4, expert_ffn=128, shared_ffn=256, ffn_dim=0)
+    assert lib.specdec_workspace_bytes(C.byref(moe)) > 0
+
+
+def test_error_strings(lib):
+    for code in (F.OK, F.E_INVAL, F.E_CAPACITY, F.E_HIP, F.E_UNSUPPORTED, -99):
+        s = lib.specdec_error_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.specdec_error_string(F.E_CAPACITY) != lib.specdec_error_string(F.E_INVAL)
+
+
+def test_null_handles_are_rejected(lib):
+    assert lib.specdec_destroy(None) == F.E_INVAL
+    assert lib.specdec_verify(None, 1, 1, None, None, None, None) == F.E_INVAL
+    assert lib.specdec_draft(None, 1, 1, 0, 1, None, None, None, 0, None, None) == F.E_INVAL
+    assert lib.specdec_accept(None, 1, 1, None, None, None, None, 0, None) == F.E_INVAL
+    assert lib.specdec_kv_commit(None, 1, None, None) == F.E_INVAL
+    out = C.c_void_p()
+    assert lib.specdec_create(None, None, None, None, None, None, None, 0, None, C.byref(out)) == F.E_INVAL
+    assert out.value is None

@@ -19,8 +19,9 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import oracle as O  # noqa: E402
 import speculative_decoding_03_amd as SD  # noqa: E402
-from gpu_util import (build_engine, gpu_greedy, gpu_prefill, gpu_spec, oracle_model, rel_err,  # noqa: E402
-                      restore, snapshot)
+from gpu_util import (build_engine, gpu_greedy, gpu_greedy_batch, gpu_prefill,  # noqa: E402
+                      gpu_prefill_batch, gpu_spec, gpu_spec_batch, oracle_model, rel_err, restore,
+                      snapshot)
 from workloads import inject_table, preset, prompt_tokens  # noqa: E402
 
 CFG = preset("tiny")
@@ -232,3 +233,36 @@ def test_error_paths(tiny):
     eng.verify(torch.tensor([[CFG.vocab + 5]], dtype=torch.int32, device=dev))
     assert eng.device_error(clear=True) & SD.ffi.DEVERR_TOKEN
     restore(eng, tiny["snap"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny-moe"])
+def test_batch_of_two_sequences(name):
+    """Two sequences in one call: each decodes exactly as it does alone (the path is
+    batch-invariant), and the batched speculative loop, with the draft writing the verify rows,
+    reproduces the batched greedy output."""
+    cfg = preset(name, batch=2)
+    n, K = 40, cfg.draft_k
+    prompts = prompt_tokens(cfg)
+    singles = []
+    for b in range(2):
+        e1 = build_engine(cfg.replace(batch=1), MAX_CTX)
+        t0 = gpu_prefill_batch(e1, prompts[b:b + 1])
+        singles.append(gpu_greedy_batch(e1, t0, n)[0])
+        e1.close()
+    eng = build_engine(cfg, MAX_CTX, max_batch=2)
+    t0s = gpu_prefill_batch(eng, prompts)
+    snap = snapshot(eng)
+    g2 = gpu_greedy_batch(eng, t0s, n + K + 2)
+    assert [g[:n] for g in g2] == singles
+    L = prompts.shape[1]
+    tabs = []
+    for b in range(2):
+        gseq = np.full(MAX_CTX, -1, dtype=np.int64)
+        gseq[L:L + len(g2[b])] = g2[b]
+        tabs.append(inject_table(gseq, K, 0.6, cfg.inject_seed, b=b))
+    restore(eng, snap)
+    toks, emitted = gpu_spec_batch(eng, t0s, n, K, np.stack(tabs))
+    assert toks == [g[:n] for g in g2]
+    assert all(1 <= e <= K + 1 for step in emitted for e in step)
+    assert eng.device_error() == 0
+    eng.close()

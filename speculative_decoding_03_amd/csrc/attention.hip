@@ -251,10 +251,13 @@ __global__ void __launch_bounds__(1024) attn_combine_kernel(AttnArgs a) {
     return;
   }
   const int row = qv / G, h = g * G + (qv - row * G);
-  T* out = reinterpret_cast<T*>(a.out) + ((size_t)b * a.R + row) * (a.hq * hd) + h * hd;
+  // output element d of this query vector: row b*R + row, column h*hd + d of the O input
+  T* const out = reinterpret_cast<T*>(a.out);
+  const int orow = b * a.R + row, ocol = h * hd, ld = a.hq * hd;
   if (n_act == 0) {
     // no visible key (drafter before any context): the attention output is defined as zero
-    for (int d = t; d < hd; d += blockDim.x) Elem<T>::store(out + d, 0.f);
+    for (int d = t; d < hd; d += blockDim.x)
+      Elem<T>::store(out + x_offset(a.out_qx, orow, ocol + d, ld), 0.f);
     return;
   }
   const int pst = hd + 4;  // partial row: o[hd], m, l, 2 pad
@@ -303,7 +306,7 @@ __global__ void __launch_bounds__(1024) attn_combine_kernel(AttnArgs a) {
   if (t < hd) {
     float o = psum[t];
     for (int q = 1; q < P; ++q) o += psum[q * hd + t];
-    Elem<T>::store(out + t, o * Linv);
+    Elem<T>::store(out + x_offset(a.out_qx, orow, ocol + t, ld), o * Linv);
   }
 }
 

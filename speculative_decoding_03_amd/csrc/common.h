@@ -79,6 +79,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Activation layout for at most 4 rows ("quad"): the reduction axis in blocks of 128 (four
+// k-blocks of 32), 512 elements per block; element (r, k) sits in lane kg*16 + j*4 + r of its
+// block, 8 consecutive elements per lane (kg = (k % 32) / 8, j = (k / 32) % 4).  One wave load
+// of a block holds four k-blocks; the operand fragment of k-block j (lane kg*16 + r holding row
+// r) is the block shifted down by 4j lanes within each row of 16 lanes.
+__host__ __device__ inline size_t qx_offset(int r, int k) {
+  return (size_t)(k >> 7) * 512 + (size_t)(((((k >> 3) & 3) << 4) + (((k >> 5) & 3) << 2) + r) << 3) +
+         (size_t)(k & 7);
+}
+// element (r, k) of an activation matrix with row stride ld, row-major or quad
+__host__ __device__ inline size_t x_offset(int qx, int r, int k, int ld) {
+  return qx ? qx_offset(r, k) : (size_t)r * ld + k;
+}
+
 // One lane's share of a 16x32 MFMA operand tile: 8 consecutive reduction elements of one row.
 template <typename T> struct Frag;
 template <> struct Frag<bf16_t> {

@@ -21,6 +21,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -52,7 +54,40 @@ __device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int r, int
     return;
   }
   const int k = kb * TILE_K + ((lane >> 4) << 3);
-  load_frag<T>(f, reinterpret_cast<const T*>(a.X) + (size_t)r * a.ldx + k);
+  load_frag<T>(f, reinterpret_cast<const T*>(a.X) + x_offset(a.x_qx, r, k, a.ldx));
+}
+
+// Fragment of k-block J of a quad block q (X in the quad layout, one wave load per block): lane
+// kg*16 + r takes lane kg*16 + 4J + r of its row of 16 (DPP row shift).  Lanes whose row is not
+// 0..3 of k-block J feed only output rows >= 4, which no epilogue stores.
+template <int J, typename T>
+__device__ __forceinline__ void quad_frag(Frag<T>& f, const Frag<T>& q) {
+  if constexpr (J == 0) {
+    f = q;
+  } else {
+    constexpr int ctrl = 0x100 + 4 * J;  // row_shl:4J
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f.v[i] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)q.v[i], ctrl, 0xF, 0xF, true);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          f.v[h][i] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)q.v[h][i], ctrl, 0xF, 0xF, true);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void quad_frag_rt(Frag<T>& f, const Frag<T>& q, int j) {
+  switch (j) {
+    case 0: quad_frag<0>(f, q); break;
+    case 1: quad_frag<1>(f, q); break;
+    case 2: quad_frag<2>(f, q); break;
+    default: quad_frag<3>(f, q); break;
+  }
 }
 
 __device__ __forceinline__ float sum16(float v) {
@@ -72,15 +107,47 @@ __device__ __forceinline__ void argmax16(float& v, int& i) {
   }
 }
 
+// Row-scale partial sums of up to 4 rows with n_yssq <= 64 * RS_J, loaded into registers after the
+// main loop and before the split-K reduction, so that their latency overlaps its barriers.
+constexpr int RS_J = 5;
+struct RowScaleLoads {
+  float v[RS_J][4];
+  bool fast;
+};
+
+__device__ __forceinline__ void row_scale_load(const GemmArgs& a, int lane, RowScaleLoads& rs) {
+  rs.fast = a.yssq && a.M <= 4 && a.n_yssq <= WAVE * RS_J;
+  if (!rs.fast) return;
+#pragma unroll
+  for (int j = 0; j < RS_J; ++j) {
+    const int t = lane + WAVE * j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rs.v[j][r] = (t < a.n_yssq && r < a.M) ? a.yssq[(size_t)t * a.M + r] : 0.f;
+  }
+}
+
 // Row scales 1/sqrt(sum_t yssq[t][r] / yscale_n + eps) for the rows this lane holds (r = the X
 // row a local row reads: xr[mt] holds it for local row mt*16 + lane%16).  The sum runs
 // lane-strided then through a fixed butterfly, identically for every caller.
 template <int MT>
 __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const int (&xr)[MT],
-                                           float (&sc)[MT][4]) {
+                                           const RowScaleLoads& rs, float (&sc)[MT][4]) {
   float mine = 1.f;
-  // up to 16 rows at a time, all their loads independent; per row the same order as one row alone
-  for (int m0 = 0; m0 < a.M; m0 += 16) {
+  if (rs.fast) {
+    // per row the partials are added in ascending order, as below
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < RS_J; ++j) s += rs.v[j][r];
+      if (r < a.M) {
+        const float w = wave_sum(s);
+        if (lane == r) mine = 1.0f / sqrtf(w / (float)a.yscale_n + a.eps);
+      }
+    }
+  }
+  // otherwise up to 16 rows at a time, all their loads independent
+  for (int m0 = 0; !rs.fast && m0 < a.M; m0 += 16) {
     const int nr = min(16, a.M - m0);
     float s[16];
 #pragma unroll
@@ -111,12 +178,13 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const in
 
 template <typename T, int MT, int NU, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
-                                         int tile0, int grp, const int (&xr)[MT], int lane) {
+                                         int tile0, int grp, const int (&xr)[MT],
+                                         const RowScaleLoads& rs, int lane) {
   const int c16 = lane & 15;
   const int rgrp = (lane >> 4) << 2;
   if (a.yssq) {
     float sc[MT][4];
-    row_scales<MT>(a, lane, xr, sc);
+    row_scales<MT>(a, lane, xr, rs, sc);
 #pragma unroll
     for (int t = 0; t < NU; ++t)
 #pragma unroll
@@ -146,7 +214,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           if (a.accumulate) y = *o + y;
           *o = y;
           sq = y * y;
-          if (a.xw_out) Elem<T>::store(reinterpret_cast<T*>(a.xw_out) + (size_t)m * a.ldo + col, y * wn);
+          if (a.xw_out)
+            Elem<T>::store(reinterpret_cast<T*>(a.xw_out) + x_offset(a.out_qx, m, col, a.ldo), y * wn);
         }
         if (a.ssq) {
           const float r = sum16(sq);
@@ -231,7 +300,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           const float g = acc[0][mt][v];
           const float up = acc[1][mt][v];
           const float h = g / (1.0f + expf(-g)) * up;
-          Elem<T>::store(reinterpret_cast<T*>(a.hout) + (size_t)m * a.ldh + f, h);
+          Elem<T>::store(reinterpret_cast<T*>(a.hout) + x_offset(a.out_qx, m, f, a.ldh), h);
         }
       }
   } else {  // EPI_ARGMAX
@@ -328,7 +397,73 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (active) {
+  bool quad_done = false;
+  if constexpr (MT == 1 && !GROUPED) {
+    if (active && a.x_qx) {
+      // X in the quad layout (at most 4 rows): one wave load per four k-blocks, shared by the
+      // batch's k-blocks through DPP row shifts.  kb0 is a multiple of 4.
+      constexpr int U = NU >= 4 ? 2 : 4;  // k-blocks per batch: a whole or half quad block
+      Frag<T> w[2][U][NU];
+      Frag<T> xq[2];
+      const T* Xq = reinterpret_cast<const T*>(a.X) + (size_t)lane * 8;
+      auto load_batch = [&](int st, int kbase) {
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+          for (int t = 0; t < NU; ++t) {
+            if (tvalid[t]) load_w<T>(w[st][uu][t], W, (size_t)(tile0 + t), a.nkb, kbase + uu, lane);
+            else zero_frag(w[st][uu][t]);
+          }
+        load_frag<T>(xq[st], Xq + (size_t)(kbase >> 2) * 512);
+      };
+      auto mul_at = [&](auto j0c, int st) {
+        constexpr int J0 = decltype(j0c)::value;
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          Frag<T> xf;
+          if constexpr (J0 + 0 == 0) {
+            if (uu == 0) quad_frag<0>(xf, xq[st]);
+            else if (uu == 1) quad_frag<1>(xf, xq[st]);
+            else if (uu == 2) quad_frag<2>(xf, xq[st]);
+            else quad_frag<3>(xf, xq[st]);
+          } else {
+            if (uu == 0) quad_frag<2>(xf, xq[st]);
+            else quad_frag<3>(xf, xq[st]);
+          }
+#pragma unroll
+          for (int t = 0; t < NU; ++t) acc[t][0] = mma<T>(xf, w[st][uu][t], acc[t][0]);
+        }
+      };
+      auto mul_batch = [&](int st, int kbase) {
+        if (U == 4 || (kbase & 2) == 0) mul_at(std::integral_constant<int, 0>{}, st);
+        else mul_at(std::integral_constant<int, 2>{}, st);
+      };
+      const int nb = (kb1 - kb0) / U;
+      if (nb > 0) load_batch(0, kb0);
+      for (int b = 0; b < nb; b += 2) {
+        if (b + 1 < nb) load_batch(1, kb0 + (b + 1) * U);
+        mul_batch(0, kb0 + b * U);
+        if (b + 1 < nb) {
+          if (b + 2 < nb) load_batch(0, kb0 + (b + 2) * U);
+          mul_batch(1, kb0 + (b + 1) * U);
+        }
+      }
+      for (int kb = kb0 + nb * U; kb < kb1; ++kb) {
+        Frag<T> wt[NU], q, xf;
+#pragma unroll
+        for (int t = 0; t < NU; ++t) {
+          if (tvalid[t]) load_w<T>(wt[t], W, (size_t)(tile0 + t), a.nkb, kb, lane);
+          else zero_frag(wt[t]);
+        }
+        load_frag<T>(q, Xq + (size_t)(kb >> 2) * 512);
+        quad_frag_rt<T>(xf, q, kb & 3);
+#pragma unroll
+        for (int t = 0; t < NU; ++t) acc[t][0] = mma<T>(xf, wt[t], acc[t][0]);
+      }
+      quad_done = true;
+    }
+  }
+  if (active && !quad_done) {
     constexpr int U = Unroll<NU, MT>::U;
     // Two register stages: the loads of batch i+1 are in flight while batch i is multiplied.
     Frag<T> w[2][U][NU];
@@ -384,6 +519,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     }
   }
 
+  RowScaleLoads rs;
+  rs.fast = false;
+  if (active && ks == 0) row_scale_load(a, lane, rs);
   if (KW > 1) {
     // sum the KW partial accumulators of each unit in wave order, one M-tile at a time
 #pragma unroll
@@ -406,7 +544,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     if (ks != 0) return;
   }
   if (!active) return;
-  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, lane);
+  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, rs, lane);
 }
 
 template <typename T, int MT, int NU, int EPI, int NW>

@@ -44,9 +44,11 @@ struct GemmArgs {
   const int* xrow_map = nullptr;
   const int* orow_map = nullptr;
   const float* orow_wt = nullptr;
-  // X operand: storage-typed [M][ldx]
+  // X operand: storage-typed [M][ldx], or the quad layout (x_qx, M <= 4; see qx_offset)
   const void* X = nullptr;
   int ldx = 0;
+  int x_qx = 0;
+  int out_qx = 0;  // xw_out / hout written in the quad layout (M <= 4)
   // optional row scale of the results (an RMSNorm folded in): y *= 1/sqrt(sum_t yssq[t][m] /
   // yscale_n + eps) over n_yssq tiles
   const float* yssq = nullptr;
@@ -108,7 +110,8 @@ struct AttnArgs {
   const void* kcache = nullptr;
   const void* vcache = nullptr;
   const int* len = nullptr;
-  void* out = nullptr;  // storage-typed [B*R][hq*hd]
+  void* out = nullptr;  // storage-typed [B*R][hq*hd], row-major or the quad layout (out_qx)
+  int out_qx = 0;
   float* part = nullptr;
   int* err = nullptr;
   int B = 0, R = 0, key_off = 0;
@@ -127,8 +130,8 @@ bool attention_supported(int head_dim);     // head sizes the attention kernel i
 
 // Misc kernels (misc.hip).
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
-                        float* x, float* ssq, void* xw, const float* norm, int vocab, int* err,
-                        hipStream_t st);
+                        float* x, float* ssq, void* xw, int xw_qx, const float* norm, int vocab,
+                        int* err, hipStream_t st);
 hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
                          int B, int R, const int* tokens, int* out_tokens, int* n_emit,
                          int* next_tok, int commit, int* len, float* hid, const float* X, int d,
@@ -137,8 +140,8 @@ hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid
                          int d, int* err, hipStream_t st);
 hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
                               int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
-                              const float* norm_e, int d, int Dd, float eps, void* u, int B,
-                              int* err, hipStream_t st);
+                              const float* norm_e, int d, int Dd, float eps, void* u, int u_qx,
+                              int B, int* err, hipStream_t st);
 // Mixture-of-experts routing of M rows over E experts (logits [M][E]): the top_k experts of
 // each row (ties -> lower id), softmax weights over them, and the per-expert row maps of the
 // grouped GEMMs: for expert e and its i-th routed row m (ascending m), xrow[e*M+i] = m,

@@ -38,11 +38,11 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* rv, int* r
 }
 
 // x[m] = E[tokens[m]] (fp32 residual), xw[m] = x[m] * norm (the first layer's attention-norm
-// weight, storage type) and the per-16-column sums of squares of x[m], from which the consumer
-// forms the RMSNorm row scale.
+// weight, storage type; row-major or the quad layout) and the per-16-column sums of squares of
+// x[m], from which the consumer forms the RMSNorm row scale.
 template <typename T>
 __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, const int* tokens,
-                                                    int M, float* x, float* ssq, T* xw,
+                                                    int M, float* x, float* ssq, T* xw, int xw_qx,
                                                     const float* norm, int vocab, int* err) {
   extern __shared__ float sq[];
   const int m = blockIdx.x;
@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, 
     for (int e = 0; e < 8; ++e) {
       const int k = k8 + e;
       x[(size_t)m * d + k] = v[e];
-      Elem<T>::store(xw + (size_t)m * d + k, v[e] * norm[k]);
+      Elem<T>::store(xw + x_offset(xw_qx, m, k, d), v[e] * norm[k]);
       sq[k] = v[e] * v[e];
     }
   }
@@ -141,7 +141,8 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
                                                           const T* table, int nkb_table,
                                                           const int* vocab_row, int vocab,
                                                           const float* norm_h, const float* norm_e,
-                                                          int d, int Dd, float eps, T* u, int* err) {
+                                                          int d, int Dd, float eps, T* u, int u_qx,
+                                                          int* err) {
   __shared__ float red[4];
   __shared__ float ebuf[1024];
   const int b = blockIdx.x;
@@ -172,11 +173,10 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
   sse = block_sum(sse, red);
   const float rh = 1.0f / sqrtf(ssh / (float)d + eps);
   const float re = 1.0f / sqrtf(sse / (float)Dd + eps);
-  T* ub = u + (size_t)b * (d + Dd);
   for (int k = threadIdx.x; k < d; k += blockDim.x)
-    Elem<T>::store(ub + k, h[(size_t)b * d + k] * rh * norm_h[k]);
+    Elem<T>::store(u + x_offset(u_qx, b, k, d + Dd), h[(size_t)b * d + k] * rh * norm_h[k]);
   for (int k = threadIdx.x; k < Dd; k += blockDim.x)
-    Elem<T>::store(ub + d + k, ebuf[k] * re * norm_e[k]);
+    Elem<T>::store(u + x_offset(u_qx, b, d + k, d + Dd), ebuf[k] * re * norm_e[k]);
 }
 
 // Selects the k_c best clusters of z[b] (ties -> lower cluster id) and lists their tiles as
@@ -405,16 +405,17 @@ __global__ void fill_i32_kernel(int* p, int v, size_t n) {
 }  // namespace
 
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
-                        float* x, float* ssq, void* xw, const float* norm, int vocab, int* err,
-                        hipStream_t st) {
+                        float* x, float* ssq, void* xw, int xw_qx, const float* norm, int vocab,
+                        int* err, hipStream_t st) {
   if (M <= 0) return hipSuccess;
+  if (xw_qx && M > 4) return hipErrorInvalidValue;
   const size_t lds = (size_t)d * sizeof(float);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), lds, st,
-                       (const bf16_t*)E, nkb, d, tokens, M, x, ssq, (bf16_t*)xw, norm, vocab, err);
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), lds, st, (const bf16_t*)E, nkb,
+                       d, tokens, M, x, ssq, (bf16_t*)xw, xw_qx, norm, vocab, err);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), lds, st, (const float*)E, nkb, d,
-                       tokens, M, x, ssq, (float*)xw, norm, vocab, err);
+                       tokens, M, x, ssq, (float*)xw, xw_qx, norm, vocab, err);
   return hipGetLastError();
 }
 
@@ -436,16 +437,17 @@ hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid
 
 hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
                               int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
-                              const float* norm_e, int d, int Dd, float eps, void* u, int B,
-                              int* err, hipStream_t st) {
+                              const float* norm_e, int d, int Dd, float eps, void* u, int u_qx,
+                              int B, int* err, hipStream_t st) {
+  if (u_qx && B > 4) return hipErrorInvalidValue;
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(draft_input_kernel<bf16_t>, dim3(B), dim3(256), 0, st, h, tok,
                        (const bf16_t*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
-                       eps, (bf16_t*)u, err);
+                       eps, (bf16_t*)u, u_qx, err);
   else
     hipLaunchKernelGGL(draft_input_kernel<float>, dim3(B), dim3(256), 0, st, h, tok,
                        (const float*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
-                       eps, (float*)u, err);
+                       eps, (float*)u, u_qx, err);
   return hipGetLastError();
 }
 

@@ -33,6 +33,10 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// k-blocks per split rounded up to whole quad blocks (four k-blocks), so that every split of an
+// operand in the quad layout starts on a block
+int round_up4(int v) { return (v + 3) / 4 * 4; }
+
 int pow2_floor(int v) {
   int p = 1;
   while (p * 2 <= v) p *= 2;
@@ -87,7 +91,7 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
     g.KW = std::min(4, std::max(1, pow2_floor(g.nkb / MIN_KB_PER_WAVE)));
     g.NW = 4;
   }
-  g.kbps = cdiv(g.nkb, g.KW);
+  g.kbps = round_up4(cdiv(g.nkb, g.KW));
   return g;
 }
 
@@ -107,7 +111,7 @@ Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
   g.n_units = E * g.upg;
   g.KW = split_for(top_k * g.upg, g.nkb, NU);
   g.NW = waves_for(g.KW);
-  g.kbps = cdiv(g.nkb, g.KW);
+  g.kbps = round_up4(cdiv(g.nkb, g.KW));
   return g;
 }
 
@@ -202,10 +206,12 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   };
   const int d = c->d_model, qd = c->n_q_heads * c->head_dim, Dd = c->d_dim;
   L.x = take((size_t)dm.Mx * d * 4);
-  L.xw = take((size_t)dm.Mx * d * dm.esz);
+  // GEMM operands (row-major [rows][K], or the quad layout when a call has at most 4 rows)
+  auto xbuf = [&](size_t K) { return take((size_t)std::max(dm.Mx, 4) * ((K + 127) / 128 * 128) * dm.esz); };
+  L.xw = xbuf(d);
   L.q = take((size_t)dm.Mx * qd * 4);
-  L.o = take((size_t)dm.Mx * qd * dm.esz);
-  L.h = take((size_t)dm.Mx * ffn_width(c) * dm.esz);
+  L.o = xbuf(qd);
+  L.h = xbuf(ffn_width(c));
   L.ssq = take((size_t)dm.Mx * (d / 16) * 4);
   L.ssq_d = take((size_t)dm.Bx * (Dd / 16) * 4);
   L.amax_v = take((size_t)dm.Mx * dm.parts * 4);
@@ -213,10 +219,10 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   // attention chunk partials: per (sequence, kv head, chunk) Rall rows of (o[hd], m, l, 2 pad)
   L.att_part = take((size_t)dm.Bx * c->n_kv_heads * dm.n_chunks * dm.Rall_max * (c->head_dim + 4) * 4);
   L.err = take(64);
-  L.u = take((size_t)dm.Bx * (d + Dd) * dm.esz);
+  L.u = xbuf(d + Dd);
   L.xd = take((size_t)dm.Bx * Dd * 4);
-  L.xdw = take((size_t)dm.Bx * Dd * dm.esz);
-  L.dh = take((size_t)dm.Bx * c->d_ffn * dm.esz);
+  L.xdw = xbuf(Dd);
+  L.dh = xbuf(c->d_ffn);
   L.hnext = take((size_t)dm.Bx * d * 4);
   L.z = take((size_t)dm.Bx * c->n_centroids * 4);
   L.utile = take((size_t)dm.Bx * dm.parts * 4);
@@ -319,6 +325,7 @@ GemmArgs base_args(specdec_ctx* x, const Gemm& g, int M) {
   a.NW = g.NW;
   a.kb_per_split = g.kbps;
   a.M = M;
+  a.x_qx = a.out_qx = M <= 4;  // activations of calls with at most 4 rows use the quad layout
   a.err = at<int>(x, x->lay.err);
   a.eps = x->cfg.rms_eps;
   return a;
@@ -394,8 +401,9 @@ int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
     a.tiles_per_group = g.tpg;
     a.xrow_map = xrow;
     a.orow_map = orow;
-    a.hout = x->ws + x->lay.e_h;
+    a.hout = x->ws + x->lay.e_h;  // slot rows: row-major
     a.ldh = c.expert_ffn;
+    a.out_qx = 0;
     if ((rc = run(x, 7, 2, EPI_SILU_G, a, st))) return rc;
   }
   {  // down of the routed experts, scaled by the routing weight, stored at the row's slot
@@ -404,6 +412,7 @@ int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
     a.n_units = max_groups * g.upg;
     a.X = x->ws + x->lay.e_h;
     a.ldx = c.expert_ffn;
+    a.x_qx = 0;
     a.group_list = groups;
     a.n_groups_dev = ngroups;
     a.units_per_group = g.upg;
@@ -427,6 +436,7 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
   a.vcache = (const char*)x->kv_v + per_layer * layer * x->dm.esz;
   a.len = x->len;
   a.out = x->ws + x->lay.o;
+  a.out_qx = B * R <= 4;  // the O projection's operand, in the quad layout for up to 4 rows
   a.part = at<float>(x, x->lay.att_part);
   a.err = at<int>(x, x->lay.err);
   a.B = B;
@@ -533,7 +543,7 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
   float* ssq = at<float>(x, x->lay.ssq);
   int* err = at<int>(x, x->lay.err);
   auto lw = [&](int l, int slot) { return (const float*)x->lw[(size_t)l * SPECDEC_N_LAYER_TENSORS + slot]; };
-  HIP_TRY(launch_embed(dt_of(x), x->w.embed, x->g_head.nkb, d, tokens, M, X, ssq, XW,
+  HIP_TRY(launch_embed(dt_of(x), x->w.embed, x->g_head.nkb, d, tokens, M, X, ssq, XW, M <= 4,
                        lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st));
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
   int rc;
@@ -660,8 +670,8 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
     const float* h = (j == 1) ? x->hid : hnext;
     const int* tok = (j == 1) ? cur_tok : dtok;
     HIP_TRY(launch_draft_input(dt, h, tok, x->w.table, x->g_table.nkb, x->w.vocab_row, c.vocab,
-                               x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u, B,
-                               err, st));
+                               x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u,
+                               B <= 4, B, err, st));
     {  // input projection of [rms(h); rms(e)]; leaves x * n1 of the first drafter layer
       GemmArgs a = base_args(x, x->g_in, B);
       a.X = x->ws + x->lay.u;

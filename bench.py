@@ -83,16 +83,19 @@ def src_sha(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(name: str, launch_bytes: float):
+def load_traffic(name: str, kernel: str, grid: int, launch_bytes: float):
     """HBM traffic of the dominant kernel from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source with the same instantiation, grid and algorithmic bytes;
+    else None."""
     p = os.path.join(ROOT, "profiles", f"{name}.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
         cur = src_sha(os.path.join(ROOT, "speculative_decoding_03_amd", "csrc", "gemm.hip"))
-        if d.get("kernel_src_sha") != cur:
+        if (d.get("kernel_src_sha") != cur or d.get("kernel") != kernel
+                or d.get("grid_work_items") != grid
+                or d.get("algorithmic_bytes_per_dispatch") != launch_bytes):
             return None
         return float(d["hbm_bytes_per_dispatch"])
     except Exception:
@@ -350,12 +353,14 @@ def main() -> int:
         M = B * (K + 1)
         lb = gate_up_bytes(cfg, M)
         achieved = lb / (launch_ms * 1e-3) / 1e9
-        traffic = load_traffic(f"gemm_gate_up_{args.config}" + (f"_b{B}" if B > 1 else ""), lb)
         kw, units, nw, groups = eng.query_split(0)
+        kname = f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}>"
+        grid = groups * nw * 64
+        traffic = load_traffic(f"gemm_gate_up_{args.config}" + (f"_b{B}" if B > 1 else ""),
+                               kname, grid, lb)
         what = "shared-FFN gate/up" if cfg.is_moe else "FFN gate/up"
         res["roofline"] = {
-            "kernel": f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}> "
-                      f"({what} + SiLU product, verify M={M}, grid {groups * nw * 64} work-items, "
+            "kernel": f"{kname} ({what} + SiLU product, verify M={M}, grid {grid} work-items, "
                       f"split-K {kw})",
             "bound": "hbm",
             "achieved": round(achieved, 1),

@@ -22,15 +22,31 @@ namespace {
 
 constexpr int NWAVE = 4;
 
-// Keys per wave: two 32-key blocks for head sizes up to 128, one above (register budget).
+// Keys per wave: one 32-key block (measured on MI355X at the 31B shape: more workgroups and
+// two waves per SIMD beat two blocks per wave at one wave per SIMD).
 template <int HD> struct AttnShape {
-  static constexpr int KPW = HD <= 128 ? 64 : 32;  // keys per wave
+  static constexpr int KPW = 32;  // keys per wave (one block: registers for 2 waves per SIMD)
   static constexpr int CH = KPW * NWAVE;            // keys per workgroup = one partial
   static constexpr int NB = KPW / 32;               // 32-key blocks per wave
   static constexpr int DS = (HD + 31) / 32;         // 32-wide head-dim steps (scores)
   static constexpr int DT = HD / 16;                // 16-row head-dim tiles (value sum)
   static constexpr int PST = HD + 4;                // partial row: o[HD], m, l, 2 pad
 };
+
+// Zeroes the elements of a fragment from index n on (its 8 elements are consecutive keys).
+template <typename T>
+__device__ __forceinline__ void keep_first(Frag<T>& f, int n) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.v[i] &= (2 * i < n ? 0x0000ffffu : 0u) | (2 * i + 1 < n ? 0xffff0000u : 0u);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.v[h][i] = 4 * h + i < n ? f.v[h][i] : 0u;
+  }
+}
 
 // One workgroup = CH consecutive keys of one KV head of one sequence; wave w owns keys
 // [chunk*CH + w*KPW, +KPW), which it loads once into registers.  Then, for each 16-vector tile of
@@ -69,60 +85,53 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
   const T* Vt = reinterpret_cast<const T*>(a.vcache) + (size_t)b * a.cache_b_stride +
                 (size_t)g * HD * a.max_ctx;
 
-  // ---- the wave's keys (K rows) and values (V^T runs) ----
+  // ---- loads, without per-lane branches: K rows and the first query tile, then V^T runs ----
+  // Addresses are clamped into the cache.  What a clamped or out-of-reach load brings in is
+  // masked before use: scores of keys a row may not see become -inf, values past end_max zero.
   Frag<T> kf[NB][2][DS];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int key = kw0 + nb * 32 + 8 * (c16 >> 2) + 4 * h + (c16 & 3);
+      const int key = min(kw0 + nb * 32 + 8 * (c16 >> 2) + 4 * h + (c16 & 3), a.max_ctx - 1);
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
         const int d = ds * 32 + grp * 8;
-        if (key < end_max && d < HD) load_frag<T>(kf[nb][h][ds], Kc + (size_t)key * HD + d);
+        if (HD % 32 == 0 || d < HD) load_frag<T>(kf[nb][h][ds], Kc + (size_t)key * HD + d);
         else zero_frag(kf[nb][h][ds]);
       }
     }
+  // this lane's query column of tile q0 (columns past Rall load a valid row; their scores are
+  // masked to -inf), already in the storage type
+  Frag<T> qf[DS];
+  auto load_q = [&](int q0) {
+    const int qc = min(q0 + c16, Rall - 1);
+    const int row = qc / G;
+    const T* qp = reinterpret_cast<const T*>(a.q) +
+                  (((size_t)b * a.R + row) * a.hq + g * G + (qc - row * G)) * HD;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const int d = ds * 32 + grp * 8;
+      if (HD % 32 == 0 || d < HD) load_frag<T>(qf[ds], qp + d);
+      else zero_frag(qf[ds]);
+    }
+  };
+  load_q(0);
   Frag<T> vf[NB][DT];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int kk = kw0 + nb * 32 + grp * 8;
+    const int kk = min(kw0 + nb * 32 + grp * 8, a.max_ctx - 8);  // max_ctx is a multiple of 8
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const T* p = Vt + (size_t)(dt * 16 + c16) * a.max_ctx + kk;
-      if (kk >= end_max) {
-        zero_frag(vf[nb][dt]);
-      } else if (kk + 8 <= end_max) {
-        load_frag<T>(vf[nb][dt], p);
-      } else {  // ragged end: values past end_max may hold anything, even NaN
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (kk + e < end_max) ? Elem<T>::load(p + e) : 0.f;
-        to_frag<T>(vf[nb][dt], y);
-      }
-    }
+    for (int dt = 0; dt < DT; ++dt) load_frag<T>(vf[nb][dt], Vt + (size_t)(dt * 16 + c16) * a.max_ctx + kk);
   }
+  // every load above is issued before any instruction that waits for one of them
+  __builtin_amdgcn_sched_barrier(0);
+  const bool ragged = kw0 + KPW > end_max;  // the wave holds values past end_max (wave-uniform)
 
   float* pbase = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * SH::PST;
   for (int q0 = 0; q0 < Rall; q0 += 16) {
     const int qv = q0 + c16;  // this lane's query column
     const int row = qv / G;
-    Frag<T> qf[DS];
-    {
-      const float* qp = a.q + (((size_t)b * a.R + row) * a.hq + g * G + (qv - row * G)) * HD;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        const int d = ds * 32 + grp * 8;
-        if (qv < Rall && d < HD) {
-          const float4 x0 = *reinterpret_cast<const float4*>(qp + d);
-          const float4 x1 = *reinterpret_cast<const float4*>(qp + d + 4);
-          const float y[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          to_frag<T>(qf[ds], y);
-        } else {
-          zero_frag(qf[ds]);
-        }
-      }
-    }
 
     // ---- scores, masked, and the softmax statistics of the wave's keys ----
     f32x4 s[NB][2];
@@ -135,6 +144,8 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
         for (int ds = 0; ds < DS; ++ds) acc = mma<T>(kf[nb][h][ds], qf[ds], acc);
         s[nb][h] = acc;
       }
+    // the next tile's query vectors load while this tile finishes
+    if (q0 + 16 < Rall) load_q(q0 + 16);
     const int kend = qv < Rall ? len + row + a.key_off : 0;  // keys [0, kend) are visible
     float m = -INFINITY;
 #pragma unroll
@@ -166,6 +177,14 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     l += __shfl_xor(l, 32, WAVE);
 
     // ---- value sum O^T[d][q] = sum_key V^T[d][key] P^T[key][q] ----
+    if (q0 == 0 && ragged) {  // values past end_max may hold anything, even NaN: zero them
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int nv = end_max - (kw0 + nb * 32 + grp * 8);  // visible elements of the lane's run
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) keep_first(vf[nb][dt], nv);
+      }
+    }
     Frag<T> pf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {

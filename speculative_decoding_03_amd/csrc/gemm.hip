@@ -255,7 +255,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
             y = second ? (x2 * c + x1 * s) : (x1 * c - x2 * s);
           }
           if (hh < a.hq) {
-            a.qout[((size_t)m * a.hq + hh) * a.hd + dim] = y;
+            Elem<T>::store(reinterpret_cast<T*>(a.qout) + ((size_t)m * a.hq + hh) * a.hd + dim, y);
           } else if (pos >= a.max_ctx || pos < 0) {
             raise_error(a.err, ERRBIT_CAPACITY);
           } else {

@@ -69,7 +69,7 @@ struct GemmArgs {
   const float* xw_norm = nullptr;
   // EPI_ROPE: columns are heads of hd with rotary pairs interleaved; heads [0,hq) -> qout,
   // [hq, hq+hkv) -> kcache, [hq+hkv, hq+2hkv) -> vcache at position len[b] + row + pos_off.
-  float* qout = nullptr;
+  void* qout = nullptr;  // storage-typed [M][hq][hd] (the attention's MFMA operand)
   void* kcache = nullptr;
   void* vcache = nullptr;
   const int* len = nullptr;
@@ -106,7 +106,7 @@ hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hi
 // positions leave (max, sum of exponentials, value sum) partials that a second kernel combines
 // in chunk order.
 struct AttnArgs {
-  const float* q = nullptr;  // [B*R][hq][hd]
+  const void* q = nullptr;  // storage-typed [B*R][hq][hd]
   const void* kcache = nullptr;
   const void* vcache = nullptr;
   const int* len = nullptr;

@@ -86,10 +86,11 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   g.KW = allow_split ? split_for(g.n_units, g.nkb, NU) : 1;
   g.NW = waves_for(g.KW);
   if (allow_split && NU == 2 && g.n_units >= 4 * TARGET_WAVES / 8) {
-    // wide gated projections: one unit per workgroup, split four ways (measured on MI355X at
-    // the 31B gate/up shape: the small workgroups balance over the CUs as they retire)
-    g.KW = std::min(4, std::max(1, pow2_floor(g.nkb / MIN_KB_PER_WAVE)));
-    g.NW = 4;
+    // wide gated projections: one unit per workgroup, split up to eight ways (measured on
+    // MI355X at the 31B gate/up shape: the small workgroups balance over the CUs as they
+    // retire, and eight waves keep more loads in flight than four)
+    g.KW = std::min(8, std::max(1, pow2_floor(g.nkb / MIN_KB_PER_WAVE)));
+    g.NW = std::max(4, g.KW);
   }
   g.kbps = round_up4(cdiv(g.nkb, g.KW));
   return g;
@@ -431,7 +432,7 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
   const specdec_config& c = x->cfg;
   AttnArgs a;
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
-  a.q = at<float>(x, x->lay.q);
+  a.q = x->ws + x->lay.q;
   a.kcache = (const char*)x->kv_k + per_layer * layer * x->dm.esz;
   a.vcache = (const char*)x->kv_v + per_layer * layer * x->dm.esz;
   a.len = x->len;
@@ -551,7 +552,7 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
     {  // fused q/k/v projection + RoPE + KV append (tentative: len is not moved)
       GemmArgs a = base_args(x, x->g_qkv[l], M);
       norm_input(a, XW, d, ssq, d);
-      a.qout = at<float>(x, x->lay.q);
+      a.qout = x->ws + x->lay.q;
       a.kcache = (char*)x->kv_k + per_layer * l * x->dm.esz;
       a.vcache = (char*)x->kv_v + per_layer * l * x->dm.esz;
       a.len = x->len;
@@ -683,7 +684,7 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
       {  // q projection + RoPE at len + j - 1
         GemmArgs a = base_args(x, x->g_dq[l], B);
         norm_input(a, xdw, Dd, sd, Dd);
-        a.qout = at<float>(x, x->lay.q);
+        a.qout = x->ws + x->lay.q;
         a.len = x->len;
         a.rows_per_seq = 1;
         a.pos_off = j - 1;

@@ -6,8 +6,8 @@
 // takes one chunk of CH keys, each wave a contiguous quarter, and serves every query vector
 // that reads that KV head (all rows x the group's query heads).  K is stored [pos][hd] and V
 // transposed [hd][pos], so both MFMA operands stream as 16-byte loads.  Per chunk the kernel
-// leaves (row max, sum of exponentials, unnormalised value sum); attn_combine merges the chunks
-// in chunk order.  Chunk boundaries sit at fixed absolute positions and every reduction has a
+// leaves (row max in base-2 units, sum of exponentials, unnormalised value sum); attn_combine
+// merges the chunks in chunk order.  Chunk boundaries sit at fixed absolute positions and every reduction has a
 // fixed order, so a row's output does not depend on how many other rows are in the call.
 
 #include <math.h>
@@ -32,6 +32,33 @@ template <int HD> struct AttnShape {
   static constexpr int DT = HD / 16;                // 16-row head-dim tiles (value sum)
   static constexpr int PST = HD + 4;                // partial row: o[HD], m, l, 2 pad
 };
+
+// Waves per SIMD the register allocation must allow.  Three for 16-bit heads of up to 128: a
+// 31B-class layer at 8K context launches 65 chunks x 8 KV heads = 2080 waves, just over the
+// 2048 slots that two waves per SIMD give on 256 CUs, and the few left over would otherwise run
+// as a second round after the first has drained.  Larger heads keep the compiler's choice.
+template <typename T, int HD> constexpr int attn_occupancy() {
+  return sizeof(T) == 2 && HD <= 128 ? 3 : 1;
+}
+
+// 2^x on the hardware exponential (2^-inf = 0).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), on the gfx950
+// row-swap instructions: after a swap the pair (first, second) holds both rows' values in every
+// lane, in the same order, so every lane of a group ends with the same bits.
+__device__ __forceinline__ float rows_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Zeroes the elements of a fragment from index n on (its 8 elements are consecutive keys).
 template <typename T>
@@ -58,19 +85,22 @@ __device__ __forceinline__ void keep_first(Frag<T>& f, int n) {
 //   exponentials; lanes combined by a fixed butterfly);
 //   O^T = V^T P^T on MFMA with P^T taken straight from the score registers (bf16) and V^T read
 //   from the transposed cache as 16-byte runs of the same eight keys.
-// The four waves then merge through LDS (common max, rescale, sum in wave order) and wave 0
-// writes the chunk's partial (o, m, l).  Keys that no row may see are never loaded.
+// The four waves then merge through LDS (common max, rescale, sum in wave order), each wave
+// writing a quarter of the chunk's partial (o, m, l).  Exponentials are 2^x on the hardware
+// instruction, with scores scaled by scale * log2 e.  Keys that no row may see are never loaded.
 template <typename T, int HD>
-__global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_occupancy<T, HD>())))
+attn_kernel(AttnArgs a) {
   using SH = AttnShape<HD>;
   constexpr int NB = SH::NB, DS = SH::DS, DT = SH::DT, KPW = SH::KPW, CH = SH::CH;
-  __shared__ __align__(16) float xch[NWAVE - 1][16][SH::PST];
+  __shared__ __align__(16) float xch[NWAVE][16][SH::PST];
   __shared__ float mw[NWAVE][16], lw[NWAVE][16];
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
   const int Rall = a.R * G;
+  const float scale2 = a.scale * 1.44269504088896341f;  // softmax scale times log2 e
 
   const int len = a.len[b];
   const int end_max = len + a.R - 1 + a.key_off;  // keys [0, end_max) are read by some row
@@ -147,6 +177,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     // the next tile's query vectors load while this tile finishes
     if (q0 + 16 < Rall) load_q(q0 + 16);
     const int kend = qv < Rall ? len + row + a.key_off : 0;  // keys [0, kend) are visible
+    // scores in base-2 units (scale * log2 e folded in): exp(x - m) = exp2(x2 - m2)
     float m = -INFINITY;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -155,12 +186,13 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int key = kw0 + nb * 32 + 8 * grp + 4 * h + v;
-          const float val = key < kend ? s[nb][h][v] * a.scale : -INFINITY;
+          const float val = key < kend ? s[nb][h][v] * scale2 : -INFINITY;
           s[nb][h][v] = val;
           m = fmaxf(m, val);
         }
-    m = fmaxf(m, __shfl_xor(m, 16, WAVE));
-    m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+    m = rows_max(m);
+    // a column with no visible key keeps m = -inf; its exponentials are exp2(-inf) = 0
+    const float ms = m == -INFINITY ? 0.f : m;
     float l = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -168,13 +200,11 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float val = s[nb][h][v];
-          const float p = val == -INFINITY ? 0.f : expf(val - m);
+          const float p = exp2_hw(s[nb][h][v] - ms);
           s[nb][h][v] = p;
           l += p;
         }
-    l += __shfl_xor(l, 16, WAVE);
-    l += __shfl_xor(l, 32, WAVE);
+    l = rows_sum(l);
 
     // ---- value sum O^T[d][q] = sum_key V^T[d][key] P^T[key][q] ----
     if (q0 == 0 && ragged) {  // values past end_max may hold anything, even NaN: zero them
@@ -203,47 +233,46 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     }
 
     // ---- merge the four waves: common max, rescale, sum in wave order ----
+    // Every wave parks its statistics and unscaled sums in LDS; after one barrier wave w
+    // rescales and adds up head-dim tiles w, w+4, ... over the four waves (in wave order) and
+    // writes them to the partial.
     if (grp == 0) {
       mw[w][c16] = m;
       lw[w][c16] = l;
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(&xch[w][c16][dt * 16 + 4 * grp]) = o[dt];
     __syncthreads();
-    float M = mw[0][c16];
+    float mu[NWAVE], fu[NWAVE];
 #pragma unroll
-    for (int u = 1; u < NWAVE; ++u) M = fmaxf(M, mw[u][c16]);
-    const float f = m == -INFINITY ? 0.f : expf(m - M);
-    if (w > 0) {
+    for (int u = 0; u < NWAVE; ++u) mu[u] = mw[u][c16];
+    float M = mu[0];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4*>(&xch[w - 1][c16][dt * 16 + 4 * grp]) = o[dt] * f;
+    for (int u = 1; u < NWAVE; ++u) M = fmaxf(M, mu[u]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int u = 0; u < NWAVE; ++u) fu[u] = exp2_hw(mu[u] - Ms);  // 0 for a wave with no key
+#pragma unroll
+    for (int dt = w; dt < DT; dt += NWAVE) {
+      f32x4 y = *reinterpret_cast<const f32x4*>(&xch[0][c16][dt * 16 + 4 * grp]) * fu[0];
+#pragma unroll
+      for (int u = 1; u < NWAVE; ++u)
+        y += *reinterpret_cast<const f32x4*>(&xch[u][c16][dt * 16 + 4 * grp]) * fu[u];
+      if (qv < Rall) *reinterpret_cast<f32x4*>(pbase + (size_t)qv * SH::PST + dt * 16 + 4 * grp) = y;
     }
-    __syncthreads();
-    if (w == 0) {
+    if (w == 0 && grp == 0 && qv < Rall) {
       float L = 0.f;
 #pragma unroll
-      for (int u = 0; u < NWAVE; ++u) {
-        const float mu = mw[u][c16];
-        L += mu == -INFINITY ? 0.f : lw[u][c16] * expf(mu - M);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 y = o[dt] * f;
-#pragma unroll
-        for (int u = 0; u < NWAVE - 1; ++u)
-          y += *reinterpret_cast<const f32x4*>(&xch[u][c16][dt * 16 + 4 * grp]);
-        if (qv < Rall) *reinterpret_cast<f32x4*>(pbase + (size_t)qv * SH::PST + dt * 16 + 4 * grp) = y;
-      }
-      if (grp == 0 && qv < Rall) {
-        pbase[(size_t)qv * SH::PST + HD] = M;
-        pbase[(size_t)qv * SH::PST + HD + 1] = L;
-      }
+      for (int u = 0; u < NWAVE; ++u) L += lw[u][c16] * fu[u];
+      pbase[(size_t)qv * SH::PST + HD] = M;
+      pbase[(size_t)qv * SH::PST + HD + 1] = L;
     }
-    __syncthreads();
+    if (q0 + 16 < Rall) __syncthreads();  // the next tile reuses the LDS buffers
   }
 }
 
 // Combines the chunk partials of one query vector:
-// o = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c,  M = max_c m_c.
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c (maxima in base-2 units).
 // Thread (p, d) sums chunks p, p+P, p+2P, ... of column d (P = 1024 / hd parts), and the P part
 // sums are added in part order, so the result depends only on the chunk partials (a chunk whose
 // keys are all invisible to the row contributes exact zeros).
@@ -295,8 +324,9 @@ __global__ void __launch_bounds__(1024) attn_combine_kernel(AttnArgs a) {
   __syncthreads();
   float M = wmax[0];
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) M = fmaxf(M, wmax[w]);
+  const float Ms = M == -INFINITY ? 0.f : M;  // chunk maxima are in base-2 units
   for (int c = t; c < n_act; c += blockDim.x)
-    wts[c] = (wts[c] == -INFINITY) ? 0.f : expf(wts[c] - M);
+    wts[c] = exp2_hw(wts[c] - Ms);
   __syncthreads();
   if (t == 0) {
     float L = 0.f;

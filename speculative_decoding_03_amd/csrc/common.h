@@ -23,12 +23,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
+// fp32 -> bf16 with the gfx950 conversion instruction (round to nearest even; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 values -> packed bf16 pair (lo in bits 0-15), one conversion instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  const f2_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2_t));
 }
 
 template <typename T> struct Elem;
@@ -119,7 +124,7 @@ __device__ __forceinline__ void to_frag(Frag<T>& f, const float (&y)[8]) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16(y[2 * i]) | ((uint32_t)f32_to_bf16(y[2 * i + 1]) << 16);
+      w[i] = f32x2_to_bf16x2(y[2 * i], y[2 * i + 1]);
     f.v = u32x4{w[0], w[1], w[2], w[3]};
   } else {
     f.v[0] = u32x4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),

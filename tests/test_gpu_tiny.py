@@ -65,6 +65,22 @@ def test_prefill_logits_match_oracle(tiny):
     assert eng.device_error() == 0
 
 
+def test_prefill_in_calls_of_32_rows(tiny):
+    """Prefill in 32-row verify calls: 64 query vectors per KV head, more than the attention
+    kernel stages in LDS (32), so it reads each 16-vector tile's queries from global memory."""
+    CFG = tiny["cfg"]
+    eng = build_engine(CFG, MAX_CTX, max_rows=32)
+    try:
+        prompt = prompt_tokens(CFG)[0]
+        t0, logits = gpu_prefill(eng, prompt, chunk=32)
+        errs = [rel_err(logits[i], tiny["ref_rows"][i]) for i in range(len(tiny["ref_rows"]))]
+        assert max(errs) < TOL, f"max rel err {max(errs):.3e}"
+        assert t0 == tiny["ref_t0"]
+        assert eng.device_error() == 0
+    finally:
+        eng.close()
+
+
 def _check_tokens(gpu_toks, ref_toks, margins, n):
     """Tokens must match wherever the oracle's margin exceeds 0.05; stop at an allowed flip."""
     for i in range(1, n):

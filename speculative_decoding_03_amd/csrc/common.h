@@ -72,16 +72,48 @@ __device__ __forceinline__ void argmax_combine(float& v, int& i, float v2, int i
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Lane exchange inside each row of 16 lanes (DPP): quad permutations and the row mirrors.
+enum : int { DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL> __device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over each row of 16 lanes, in VALU lane exchanges: pairs, quads, half rows, rows.  Every
+// step adds two equal-sized groups symmetrically, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f32<DPP_XOR1>(v);
+  v += dpp_f32<DPP_XOR2>(v);
+  v += dpp_f32<DPP_HALF_MIRROR>(v);
+  v += dpp_f32<DPP_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_f32<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f32<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f32<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f32<DPP_MIRROR>(v));
   return v;
 }
 
+// Rows of 16 lanes combined on the gfx950 row-swap instructions: after a swap the pair holds both
+// rows' values in every lane, in the same order, so all lanes keep identical bits.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+  v = max16(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Activation layout for at most 4 rows ("quad"): the reduction axis in blocks of 128 (four

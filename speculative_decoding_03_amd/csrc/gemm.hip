@@ -90,21 +90,12 @@ __device__ __forceinline__ void quad_frag_rt(Frag<T>& f, const Frag<T>& q, int j
   }
 }
 
-__device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 8, WAVE);
-  v += __shfl_xor(v, 4, WAVE);
-  v += __shfl_xor(v, 2, WAVE);
-  v += __shfl_xor(v, 1, WAVE);
-  return v;
-}
-
+// (max, lowest index) over each row of 16 lanes, in the same exchange pattern as sum16.
 __device__ __forceinline__ void argmax16(float& v, int& i) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    float v2 = __shfl_xor(v, o, WAVE);
-    int i2 = __shfl_xor(i, o, WAVE);
-    argmax_combine(v, i, v2, i2);
-  }
+  argmax_combine(v, i, dpp_f32<DPP_XOR1>(v), dpp_i32<DPP_XOR1>(i));
+  argmax_combine(v, i, dpp_f32<DPP_XOR2>(v), dpp_i32<DPP_XOR2>(i));
+  argmax_combine(v, i, dpp_f32<DPP_HALF_MIRROR>(v), dpp_i32<DPP_HALF_MIRROR>(i));
+  argmax_combine(v, i, dpp_f32<DPP_MIRROR>(v), dpp_i32<DPP_MIRROR>(i));
 }
 
 // Row-scale partial sums of up to 4 rows with n_yssq <= 64 * RS_J, loaded into registers after the
@@ -114,6 +105,60 @@ struct RowScaleLoads {
   float v[RS_J][4];
   bool fast;
 };
+
+// Epilogue operands that do not depend on the products, read before the main loop so that their
+// latency hides behind it: the norm weight and current value of each stored element (EPI_STORE),
+// the rotary inverse frequency and the row positions (EPI_ROPE).
+template <int MT, int NU> struct EpiPre {
+  float wn[NU];
+  float res[NU][MT][4];
+  float2 cs[NU][MT][4];  // rotary (cos, sin) of the lane's pair at each row's position
+  int pos[MT][4];
+};
+
+template <int MT, int NU, int EPI>
+__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int lane,
+                                             EpiPre<MT, NU>& pre) {
+  const int c16 = lane & 15;
+  const int rgrp = (lane >> 4) << 2;
+  if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+    for (int t = 0; t < NU; ++t) {
+      const int col = min(tile0 + t, a.n_tiles - 1) * TILE_N + c16;
+      pre.wn[t] = a.xw_out ? a.xw_norm[col] : 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = mt * 16 + rgrp + v;
+          pre.res[t][mt][v] = (a.accumulate && m < a.M) ? a.out[(size_t)m * a.ldo + col] : 0.f;
+        }
+    }
+  } else if constexpr (EPI == EPI_ROPE) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt * 16 + rgrp + v;
+        const int b = m < a.M ? m / a.rows_per_seq : 0;
+        pre.pos[mt][v] = a.len[b] + (m - b * a.rows_per_seq) + a.pos_off;
+      }
+    const int half = a.hd >> 1;
+#pragma unroll
+    for (int t = 0; t < NU; ++t) {
+      const int col = min(tile0 + t, a.n_tiles - 1) * TILE_N + c16;
+      const int i = (col % a.hd) >> 1;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          // a position outside the cache reads row 0 or the last (the epilogue flags it)
+          const int pc = min(max(pre.pos[mt][v], 0), a.max_ctx - 1);
+          pre.cs[t][mt][v] = a.rope_cs[(size_t)pc * half + i];
+        }
+    }
+  }
+}
 
 __device__ __forceinline__ void row_scale_load(const GemmArgs& a, int lane, RowScaleLoads& rs) {
   rs.fast = a.yssq && a.M <= 4 && a.n_yssq <= WAVE * RS_J;
@@ -179,7 +224,7 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const in
 template <typename T, int MT, int NU, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
                                          int tile0, int grp, const int (&xr)[MT],
-                                         const RowScaleLoads& rs, int lane) {
+                                         const RowScaleLoads& rs, const EpiPre<MT, NU>& pre, int lane) {
   const int c16 = lane & 15;
   const int rgrp = (lane >> 4) << 2;
   if (a.yssq) {
@@ -193,82 +238,84 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
         for (int v = 0; v < 4; ++v) acc[t][mt][v] *= sc[mt][v];
   }
   if constexpr (EPI == EPI_STORE) {
-    const int tile = tile0;
-    const int col = tile * TILE_N + c16;
-    const float wn = a.xw_out ? a.xw_norm[col] : 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < NU; ++t) {
+      const int tile = tile0 + t;
+      if (tile >= a.n_tiles) break;  // wave-uniform
+      const int col = tile * TILE_N + c16;
+      const float wn = pre.wn[t];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = mt * 16 + rgrp + v;
-        float sq = 0.f;
-        if (m < a.M) {
-          float* o = a.out + (size_t)m * a.ldo + col;
-          float y = acc[0][mt][v];
-          if (a.addend) {
-            const float* ad = a.addend + (size_t)m * a.add_n * a.ldo + col;
-            float t = ad[0];
-            for (int k = 1; k < a.add_n; ++k) t += ad[(size_t)k * a.ldo];
-            y = t + y;
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = mt * 16 + rgrp + v;
+          float sq = 0.f;
+          if (m < a.M) {
+            float* o = a.out + (size_t)m * a.ldo + col;
+            float y = acc[t][mt][v];
+            if (a.addend) {
+              const float* ad = a.addend + (size_t)m * a.add_n * a.ldo + col;
+              float s = ad[0];
+              for (int k = 1; k < a.add_n; ++k) s += ad[(size_t)k * a.ldo];
+              y = s + y;
+            }
+            if (a.accumulate) y = pre.res[t][mt][v] + y;
+            *o = y;
+            sq = y * y;
+            if (a.xw_out)
+              Elem<T>::store(reinterpret_cast<T*>(a.xw_out) + x_offset(a.out_qx, m, col, a.ldo), y * wn);
           }
-          if (a.accumulate) y = *o + y;
-          *o = y;
-          sq = y * y;
-          if (a.xw_out)
-            Elem<T>::store(reinterpret_cast<T*>(a.xw_out) + x_offset(a.out_qx, m, col, a.ldo), y * wn);
+          if (a.ssq) {
+            const float r = sum16(sq);
+            if (c16 == 0 && m < a.M) a.ssq[(size_t)tile * a.M + m] = r;
+          }
         }
-        if (a.ssq) {
-          const float r = sum16(sq);
-          if (c16 == 0 && m < a.M) a.ssq[(size_t)tile * a.M + m] = r;
-        }
-      }
+    }
   } else if constexpr (EPI == EPI_ROPE) {
-    const int col = tile0 * TILE_N + c16;
-    const int hh = col / a.hd;
-    const int p = col - hh * a.hd;
-    const int i = p >> 1;
-    const int second = p & 1;
-    const int dim = i + second * (a.hd >> 1);
-    const bool rot = hh < a.hq + a.hkv;
-    const double inv_freq = pow((double)a.theta, -2.0 * (double)i / (double)a.hd);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int t = 0; t < NU; ++t) {
+      const int tile = tile0 + t;
+      if (tile >= a.n_tiles) break;  // wave-uniform
+      const int col = tile * TILE_N + c16;
+      const int hh = col / a.hd;
+      const int p = col - hh * a.hd;
+      const int i = p >> 1;
+      const int second = p & 1;
+      const int dim = i + second * (a.hd >> 1);
+      const bool rot = hh < a.hq + a.hkv;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = mt * 16 + rgrp + v;
-        const float val = acc[0][mt][v];
-        const float partner = __shfl_xor(val, 1, WAVE);
-        if (m < a.M) {
-          const int b = m / a.rows_per_seq;
-          const int row = m - b * a.rows_per_seq;
-          const int pos = a.len[b] + row + a.pos_off;
-          float y = val;
-          if (rot) {
-            // angle reduced to [-pi, pi] in double, then sine and cosine in fp32
-            const double ang = (double)pos * inv_freq;
-            const double turns = rint(ang * (0.5 / M_PI));
-            const float r = (float)fma(-turns, 2.0 * M_PI, ang);
-            float s, c;
-            sincosf(r, &s, &c);
-            const float x1 = second ? partner : val;
-            const float x2 = second ? val : partner;
-            y = second ? (x2 * c + x1 * s) : (x1 * c - x2 * s);
-          }
-          if (hh < a.hq) {
-            Elem<T>::store(reinterpret_cast<T*>(a.qout) + ((size_t)m * a.hq + hh) * a.hd + dim, y);
-          } else if (pos >= a.max_ctx || pos < 0) {
-            raise_error(a.err, ERRBIT_CAPACITY);
-          } else {
-            // K is stored [pos][hd], V transposed [hd][pos]
-            const bool isk = hh < a.hq + a.hkv;
-            const int g = isk ? hh - a.hq : hh - a.hq - a.hkv;
-            T* cache = reinterpret_cast<T*>(isk ? a.kcache : a.vcache) + (size_t)b * a.cache_b_stride;
-            const size_t off = isk ? ((size_t)g * a.max_ctx + pos) * a.hd + dim
-                                   : ((size_t)g * a.hd + dim) * a.max_ctx + pos;
-            Elem<T>::store(cache + off, y);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = mt * 16 + rgrp + v;
+          const float val = acc[t][mt][v];
+          const float partner = __shfl_xor(val, 1, WAVE);
+          if (m < a.M) {
+            const int b = m / a.rows_per_seq;
+            const int pos = pre.pos[mt][v];
+            float y = val;
+            if (rot) {
+              const float cs = pre.cs[t][mt][v].x, sn = pre.cs[t][mt][v].y;
+              const float x1 = second ? partner : val;
+              const float x2 = second ? val : partner;
+              y = second ? (x2 * cs + x1 * sn) : (x1 * cs - x2 * sn);
+            }
+            if (hh < a.hq) {
+              Elem<T>::store(reinterpret_cast<T*>(a.qout) + ((size_t)m * a.hq + hh) * a.hd + dim, y);
+            } else if (pos >= a.max_ctx || pos < 0) {
+              raise_error(a.err, ERRBIT_CAPACITY);
+            } else {
+              // K is stored [pos][hd], V transposed [hd][pos]
+              const bool isk = hh < a.hq + a.hkv;
+              const int g = isk ? hh - a.hq : hh - a.hq - a.hkv;
+              T* cache = reinterpret_cast<T*>(isk ? a.kcache : a.vcache) + (size_t)b * a.cache_b_stride;
+              const size_t off = isk ? ((size_t)g * a.max_ctx + pos) * a.hd + dim
+                                     : ((size_t)g * a.hd + dim) * a.max_ctx + pos;
+              Elem<T>::store(cache + off, y);
+            }
           }
         }
-      }
+    }
   } else if constexpr (EPI == EPI_SILU_G || EPI == EPI_STORE_G) {
     const int lt = tile0 - grp * a.tiles_per_group;  // tile within the group's matrix
 #pragma unroll
@@ -347,6 +394,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
 #ifndef SPECDEC_GEMM_U4
 #define SPECDEC_GEMM_U4 2
 #endif
+// Register stages of the quad-layout main loop (S - 1 batches in flight while one multiplies),
+// for NU = 1 / 2 / 4 tiles per unit.
+#ifndef SPECDEC_QSTAGES1
+#define SPECDEC_QSTAGES1 2
+#endif
+#ifndef SPECDEC_QSTAGES2
+#define SPECDEC_QSTAGES2 2
+#endif
+#ifndef SPECDEC_QSTAGES4
+#define SPECDEC_QSTAGES4 2
+#endif
+template <int NU> struct QuadStages {
+  static constexpr int S = NU >= 4 ? SPECDEC_QSTAGES4 : (NU == 2 ? SPECDEC_QSTAGES2 : SPECDEC_QSTAGES1);
+};
+
 template <int NU, int MT> struct Unroll {
   static constexpr int base = NU >= 4 ? SPECDEC_GEMM_U4 : (NU == 2 ? SPECDEC_GEMM_U2 : SPECDEC_GEMM_U1);
   static constexpr int U = base / MT > 1 ? base / MT : 1;
@@ -356,7 +418,9 @@ template <typename T, int MT, int NU, int EPI, int NW>
 __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   __shared__ f32x4 red[NW * NU * 64];
   const int lane = threadIdx.x & (WAVE - 1);
-  const int wid = threadIdx.x >> 6;
+  // wave index, wave-uniform (readfirstlane tells the compiler, so the split bounds and the
+  // main loop's trip count live in scalar registers and its branches are uniform)
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr bool GROUPED = EPI == EPI_SILU_G || EPI == EPI_STORE_G;
   const int KW = a.KW;
   const int ks = wid % KW;
@@ -397,23 +461,36 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // epilogue operands and row-scale partials, requested before the main loop (the wave that
+  // finishes each unit is the ks == 0 one)
+  EpiPre<MT, NU> pre;
+  RowScaleLoads rs;
+  rs.fast = false;
+  if (active && ks == 0) {
+    epi_prefetch<MT, NU, EPI>(a, tile0, lane, pre);
+    row_scale_load(a, lane, rs);
+  }
+
   bool quad_done = false;
   if constexpr (MT == 1 && !GROUPED) {
     if (active && a.x_qx) {
       // X in the quad layout (at most 4 rows): one wave load per four k-blocks, shared by the
       // batch's k-blocks through DPP row shifts.  kb0 is a multiple of 4.
+      // Loads are branch-free (a tile past n_tiles reads the last tile; its sums are never
+      // stored), so the compiler's wait counts are exact and S - 1 batches stay in flight.
       constexpr int U = NU >= 4 ? 2 : 4;  // k-blocks per batch: a whole or half quad block
-      Frag<T> w[2][U][NU];
-      Frag<T> xq[2];
+      constexpr int S = QuadStages<NU>::S;  // register stages, used as a ring
+      Frag<T> w[S][U][NU];
+      Frag<T> xq[S];
       const T* Xq = reinterpret_cast<const T*>(a.X) + (size_t)lane * 8;
+      size_t wt_tile[NU];
+#pragma unroll
+      for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);
       auto load_batch = [&](int st, int kbase) {
 #pragma unroll
         for (int uu = 0; uu < U; ++uu)
 #pragma unroll
-          for (int t = 0; t < NU; ++t) {
-            if (tvalid[t]) load_w<T>(w[st][uu][t], W, (size_t)(tile0 + t), a.nkb, kbase + uu, lane);
-            else zero_frag(w[st][uu][t]);
-          }
+          for (int t = 0; t < NU; ++t) load_w<T>(w[st][uu][t], W, wt_tile[t], a.nkb, kbase + uu, lane);
         load_frag<T>(xq[st], Xq + (size_t)(kbase >> 2) * 512);
       };
       auto mul_at = [&](auto j0c, int st) {
@@ -439,22 +516,36 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
         else mul_at(std::integral_constant<int, 2>{}, st);
       };
       const int nb = (kb1 - kb0) / U;
-      if (nb > 0) load_batch(0, kb0);
-      for (int b = 0; b < nb; b += 2) {
-        if (b + 1 < nb) load_batch(1, kb0 + (b + 1) * U);
-        mul_batch(0, kb0 + b * U);
-        if (b + 1 < nb) {
-          if (b + 2 < nb) load_batch(0, kb0 + (b + 2) * U);
-          mul_batch(1, kb0 + (b + 1) * U);
+      if (nb > 0) {
+        // Batch i of this wave sits in stage i % S.  Whole groups of S batches run in the loop,
+        // each step prefetching S - 1 batches ahead (past the last batch it reads the last one
+        // again; those stages are never multiplied); the r < S batches left over are already in
+        // flight when the loop ends.  No step leaves the pipeline early, so every prefetch is
+        // used on every path and stays where it is issued.
+        auto kb_at = [&](int i) { return kb0 + i * U; };
+        auto kb_of = [&](int i) { return kb_at(min(i, nb - 1)); };
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st) load_batch(st, kb_of(st));
+        const int G = nb / S;
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int st = 0; st < S; ++st) {
+            // the prefetch is issued before this step's products wait for their stage
+            load_batch((st + S - 1) % S, kb_of(g * S + st + S - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            mul_batch(st, kb_at(g * S + st));
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
+        const int r = nb - G * S;
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st)
+          if (st < r) mul_batch(st, kb_at(G * S + st));
       }
       for (int kb = kb0 + nb * U; kb < kb1; ++kb) {
         Frag<T> wt[NU], q, xf;
 #pragma unroll
-        for (int t = 0; t < NU; ++t) {
-          if (tvalid[t]) load_w<T>(wt[t], W, (size_t)(tile0 + t), a.nkb, kb, lane);
-          else zero_frag(wt[t]);
-        }
+        for (int t = 0; t < NU; ++t) load_w<T>(wt[t], W, wt_tile[t], a.nkb, kb, lane);
         load_frag<T>(q, Xq + (size_t)(kb >> 2) * 512);
         quad_frag_rt<T>(xf, q, kb & 3);
 #pragma unroll
@@ -519,9 +610,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     }
   }
 
-  RowScaleLoads rs;
-  rs.fast = false;
-  if (active && ks == 0) row_scale_load(a, lane, rs);
   if (KW > 1) {
     // sum the KW partial accumulators of each unit in wave order, one M-tile at a time
 #pragma unroll
@@ -544,7 +632,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     if (ks != 0) return;
   }
   if (!active) return;
-  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, rs, lane);
+  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, rs, pre, lane);
 }
 
 template <typename T, int MT, int NU, int EPI, int NW>
@@ -573,7 +661,9 @@ template <typename T, int MT>
 hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st,
                        const LaunchTiming* tm) {
   if (epi == EPI_STORE && NU == 1) return launch_nw<T, MT, 1, EPI_STORE>(a, st, tm);
+  if (epi == EPI_STORE && NU == 2) return launch_nw<T, MT, 2, EPI_STORE>(a, st, tm);
   if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE>(a, st, tm);
+  if (epi == EPI_ROPE && NU == 2) return launch_nw<T, MT, 2, EPI_ROPE>(a, st, tm);
   if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU>(a, st, tm);
   if (epi == EPI_SILU_G && NU == 2) return launch_nw<T, MT, 2, EPI_SILU_G>(a, st, tm);
   if (epi == EPI_STORE_G && NU == 1) return launch_nw<T, MT, 1, EPI_STORE_G>(a, st, tm);

@@ -23,6 +23,7 @@ enum Epi {
 // listed in unit_tile).  A workgroup of NW waves holds NW/KW units; each unit's reduction is
 // split over KW waves and summed through LDS.  KW is fixed by (N, Kd) only.
 struct GemmArgs {
+  int nu = 1;  // tiles per work unit (the kernel instantiation)
   // weights
   const void* W = nullptr;
   int nkb = 0;        // Kd / 32
@@ -79,6 +80,7 @@ struct GemmArgs {
   int max_ctx = 0;
   int cache_b_stride = 0;  // elements between sequences in one layer's cache = hkv*max_ctx*hd
   float theta = 10000.f;
+  const float2* rope_cs = nullptr;  // EPI_ROPE: [max_ctx][hd/2] (cos, sin) (launch_rope_table)
   // EPI_SILU: hout[m][f] = silu(gate) * up, gate/up tiles interleaved
   void* hout = nullptr;
   int ldh = 0;
@@ -162,5 +164,7 @@ hipError_t launch_draft_finalize(const float* amax_val, const int* amax_idx, int
 hipError_t launch_pack(int dtype, const void* src, void* dst, int N, int Kd, int kind, int hd,
                        int split_rows, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int v, size_t n, hipStream_t st);
+// t[pos][i] = (cos, sin) of pos * theta^(-2i/hd), pos < max_ctx, i < hd/2.
+hipError_t launch_rope_table(float2* t, int hd, int max_ctx, float theta, hipStream_t st);
 
 }  // namespace specdec

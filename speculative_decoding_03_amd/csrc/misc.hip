@@ -494,6 +494,30 @@ hipError_t launch_pack(int dtype, const void* src, void* dst, int N, int Kd, int
   return hipGetLastError();
 }
 
+// Rotary (cos, sin) of every position and pair: angle pos * theta^(-2i/hd) for i < hd/2, formed and
+// reduced to [-pi, pi] in fp64, then sine and cosine in fp32.  One table per context; the q/k
+// projection epilogues read it instead of evaluating the angle per element.
+__global__ void rope_table_kernel(float2* t, int hd, int max_ctx, float theta) {
+  const int half = hd / 2;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)max_ctx * half) return;
+  const int pos = (int)(idx / half), i = (int)(idx - (size_t)pos * half);
+  const double inv_freq = pow((double)theta, -2.0 * (double)i / (double)hd);
+  const double ang = (double)pos * inv_freq;
+  const double turns = rint(ang * (0.5 / M_PI));
+  const float r = (float)fma(-turns, 2.0 * M_PI, ang);
+  float sn, cs;
+  sincosf(r, &sn, &cs);
+  t[idx] = make_float2(cs, sn);
+}
+
+hipError_t launch_rope_table(float2* t, int hd, int max_ctx, float theta, hipStream_t st) {
+  const size_t n = (size_t)max_ctx * (hd / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, t, hd,
+                     max_ctx, theta);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_i32(int* p, int v, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);

@@ -27,7 +27,13 @@ namespace {
 #endif
 constexpr size_t ALIGN = 256;
 constexpr int TARGET_WAVES = SPECDEC_TARGET_WAVES;        // waves per projection launch
-constexpr int MIN_KB_PER_WAVE = SPECDEC_MIN_KB_PER_WAVE;  // k-blocks each wave streams at least
+constexpr int MIN_KB_PER_WAVE = SPECDEC_MIN_KB_PER_WAVE;
+// Tiles per unit of the target's q/k/v, o and down projections: two (measured on MI355X at the
+// 31B shapes: one activation load then serves twice the weight bytes).
+#ifndef SPECDEC_STORE_NU
+#define SPECDEC_STORE_NU 2
+#endif
+constexpr int STORE_NU = SPECDEC_STORE_NU;  // k-blocks each wave streams at least
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -74,7 +80,7 @@ int waves_for(int KW) {
   return KW == 16 ? 16 : 8;
 }
 
-Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
+Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true, bool gated = false) {
   Gemm g;
   g.W = W;
   g.N = N;
@@ -85,7 +91,7 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true) {
   g.n_units = cdiv(g.n_tiles, NU);
   g.KW = allow_split ? split_for(g.n_units, g.nkb, NU) : 1;
   g.NW = waves_for(g.KW);
-  if (allow_split && NU == 2 && g.n_units >= 4 * TARGET_WAVES / 8) {
+  if (allow_split && gated && g.n_units >= 4 * TARGET_WAVES / 8) {
     // wide gated projections: one unit per workgroup, split up to eight ways (measured on
     // MI355X at the 31B gate/up shape: the small workgroups balance over the CUs as they
     // retire, and eight waves keep more loads in flight than four)
@@ -117,7 +123,7 @@ Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
 }
 
 struct Layout {
-  size_t x, xw, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err;
+  size_t x, xw, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err, rope;
   size_t rlog, e_xrow, e_orow, e_wt, e_groups, e_ngroups, e_h, e_y, e_usage;
   size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
   size_t total;
@@ -220,6 +226,7 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   // attention chunk partials: per (sequence, kv head, chunk) Rall rows of (o[hd], m, l, 2 pad)
   L.att_part = take((size_t)dm.Bx * c->n_kv_heads * dm.n_chunks * dm.Rall_max * (c->head_dim + 4) * 4);
   L.err = take(64);
+  L.rope = take((size_t)c->max_ctx * (c->head_dim / 2) * 8);
   L.u = xbuf(d + Dd);
   L.xd = take((size_t)dm.Bx * Dd * 4);
   L.xdw = xbuf(Dd);
@@ -254,10 +261,10 @@ void build_gemms(specdec_ctx* x) {
   x->g_dq.clear(); x->g_do.clear(); x->g_dgu.clear(); x->g_ddown.clear();
   for (int l = 0; l < c.n_layers; ++l) {
     const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
-    x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, 1));
-    x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, 1));
-    x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * Fw, d, 2));
-    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, Fw, 1));
+    x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, STORE_NU));
+    x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, STORE_NU));
+    x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * Fw, d, 2, true, true));
+    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, Fw, STORE_NU));
     if (c.n_experts > 0) {
       x->g_router.push_back(make_gemm(t[SPECDEC_LW_ROUTER], c.n_experts, d, 1));
       x->g_egu.push_back(make_grouped_gemm(t[SPECDEC_LW_EXP_GATE_UP], 2 * c.expert_ffn, d, 2,
@@ -276,7 +283,7 @@ void build_gemms(specdec_ctx* x) {
     const void* const* t = x->dw.data() + (size_t)l * SPECDEC_N_DRAFT_TENSORS;
     x->g_dq.push_back(make_gemm(t[SPECDEC_DW_Q], qd, c.d_dim, 1));
     x->g_do.push_back(make_gemm(t[SPECDEC_DW_O], c.d_dim, qd, 1));
-    x->g_dgu.push_back(make_gemm(t[SPECDEC_DW_GATE_UP], 2 * c.d_ffn, c.d_dim, 2));
+    x->g_dgu.push_back(make_gemm(t[SPECDEC_DW_GATE_UP], 2 * c.d_ffn, c.d_dim, 2, true, true));
     x->g_ddown.push_back(make_gemm(t[SPECDEC_DW_DOWN], c.d_dim, c.d_ffn, 1));
   }
 }
@@ -319,6 +326,7 @@ struct ProfScope {
 GemmArgs base_args(specdec_ctx* x, const Gemm& g, int M) {
   GemmArgs a;
   a.W = g.W;
+  a.nu = g.NU;
   a.nkb = g.nkb;
   a.n_tiles = g.n_tiles;
   a.n_units = g.n_units;
@@ -358,9 +366,9 @@ void resid_output(GemmArgs& a, float* x, int ld, int accumulate, float* ssq, voi
     if ((expr) != hipSuccess) return SPECDEC_E_HIP; \
   } while (0)
 
-int run(specdec_ctx* x, int cls, int NU, int epi, const GemmArgs& a, hipStream_t st) {
+int run(specdec_ctx* x, int cls, int epi, const GemmArgs& a, hipStream_t st) {
   ProfScope ps(x, cls, st, a.n_units > 0);
-  HIP_TRY(launch_gemm(dt_of(x), mt_for(a.M), NU, epi, a, st, ps.timing()));
+  HIP_TRY(launch_gemm(dt_of(x), mt_for(a.M), a.nu, epi, a, st, ps.timing()));
   return SPECDEC_OK;
 }
 
@@ -384,7 +392,7 @@ int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
     norm_input(a, XW, d, ssq, d);
     a.out = at<float>(x, x->lay.rlog);
     a.ldo = E;
-    if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
+    if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
   }
   HIP_TRY(launch_moe_route(at<float>(x, x->lay.rlog), M, E, c.top_k, xrow, orow, wt, groups,
                            ngroups, x->moe_usage_on ? at<int>(x, x->lay.e_usage) + l : nullptr,
@@ -405,7 +413,7 @@ int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
     a.hout = x->ws + x->lay.e_h;  // slot rows: row-major
     a.ldh = c.expert_ffn;
     a.out_qx = 0;
-    if ((rc = run(x, 7, 2, EPI_SILU_G, a, st))) return rc;
+    if ((rc = run(x, 7, EPI_SILU_G, a, st))) return rc;
   }
   {  // down of the routed experts, scaled by the routing weight, stored at the row's slot
     const Gemm& g = x->g_edown[l];
@@ -423,7 +431,7 @@ int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
     a.orow_wt = wt;
     a.out = at<float>(x, x->lay.e_y);
     a.ldo = d;
-    if ((rc = run(x, 8, 1, EPI_STORE_G, a, st))) return rc;
+    if ((rc = run(x, 8, EPI_STORE_G, a, st))) return rc;
   }
   return SPECDEC_OK;
 }
@@ -514,7 +522,9 @@ int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv
   build_gemms(x);
   x->len_hi.assign(cfg->max_batch, 0);
   if (launch_fill_i32(at<int>(x, x->lay.err), 0, 16, reinterpret_cast<hipStream_t>(stream)) !=
-      hipSuccess) {
+          hipSuccess ||
+      launch_rope_table(at<float2>(x, x->lay.rope), cfg->head_dim, cfg->max_ctx, cfg->rope_theta,
+                        reinterpret_cast<hipStream_t>(stream)) != hipSuccess) {
     delete x;
     return SPECDEC_E_HIP;
   }
@@ -564,7 +574,8 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
       a.max_ctx = c.max_ctx;
       a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
       a.theta = c.rope_theta;
-      if ((rc = run(x, 2, 1, EPI_ROPE, a, st))) return rc;
+      a.rope_cs = at<float2>(x, x->lay.rope);
+      if ((rc = run(x, 2, EPI_ROPE, a, st))) return rc;
     }
     if ((rc = attention(x, l, B, R, 1, 4, st))) return rc;
     {  // output projection + residual; leaves x * ffn_norm for the FFN
@@ -572,7 +583,7 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
       a.X = x->ws + x->lay.o;
       a.ldx = qd;
       resid_output(a, X, d, 1, ssq, XW, lw(l, SPECDEC_LW_FFN_NORM));
-      if ((rc = run(x, 3, 1, EPI_STORE, a, st))) return rc;
+      if ((rc = run(x, 3, EPI_STORE, a, st))) return rc;
     }
     if (c.n_experts > 0 && (rc = routed_experts(x, l, M, st))) return rc;
     const int Fw = ffn_width(&c);
@@ -581,7 +592,7 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
       norm_input(a, XW, d, ssq, d);
       a.hout = x->ws + x->lay.h;
       a.ldh = Fw;
-      if ((rc = run(x, 0, 2, EPI_SILU, a, st))) return rc;
+      if ((rc = run(x, 0, EPI_SILU, a, st))) return rc;
     }
     {  // down projection + residual (+ the routed experts' weighted outputs, ascending expert
        // id); leaves x * (next attention norm | final norm)
@@ -594,7 +605,7 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
         a.addend = at<float>(x, x->lay.e_y);
         a.add_n = c.top_k;
       }
-      if ((rc = run(x, 1, 1, EPI_STORE, a, st))) return rc;
+      if ((rc = run(x, 1, EPI_STORE, a, st))) return rc;
     }
   }
   {  // final norm + tied LM head with per-unit argmax partials
@@ -605,7 +616,7 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
     a.ld_amax = x->dm.parts;
     a.logits = logits;
     a.ld_logits = c.vocab;
-    if ((rc = run(x, 5, 4, EPI_ARGMAX, a, st))) return rc;
+    if ((rc = run(x, 5, EPI_ARGMAX, a, st))) return rc;
   }
   if (argmax) {
     HIP_TRY(launch_accept(at<float>(x, x->lay.amax_v), at<int>(x, x->lay.amax_i), x->dm.parts,
@@ -678,7 +689,7 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
       a.X = x->ws + x->lay.u;
       a.ldx = d + Dd;
       resid_output(a, xd, Dd, 0, sd, xdw, dw(0, SPECDEC_DW_N1));
-      if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
+      if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
     }
     for (int l = 0; l < c.d_layers; ++l) {
       {  // q projection + RoPE at len + j - 1
@@ -693,7 +704,8 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         a.hd = c.head_dim;
         a.max_ctx = c.max_ctx;
         a.theta = c.rope_theta;
-        if ((rc = run(x, -1, 1, EPI_ROPE, a, st))) return rc;
+        a.rope_cs = at<float2>(x, x->lay.rope);
+        if ((rc = run(x, -1, EPI_ROPE, a, st))) return rc;
       }
       // cross-attention into the target's cache, keys [0, len)
       if ((rc = attention(x, src, B, 1, 0, -1, st))) return rc;
@@ -702,14 +714,14 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         a.X = x->ws + x->lay.o;
         a.ldx = qd;
         resid_output(a, xd, Dd, 1, sd, xdw, dw(l, SPECDEC_DW_N2));
-        if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
+        if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
       }
       {
         GemmArgs a = base_args(x, x->g_dgu[l], B);
         norm_input(a, xdw, Dd, sd, Dd);
         a.hout = x->ws + x->lay.dh;
         a.ldh = c.d_ffn;
-        if ((rc = run(x, -1, 2, EPI_SILU, a, st))) return rc;
+        if ((rc = run(x, -1, EPI_SILU, a, st))) return rc;
       }
       {  // down projection + residual; leaves x * (next n1 | n_f)
         GemmArgs a = base_args(x, x->g_ddown[l], B);
@@ -717,7 +729,7 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         a.ldx = c.d_ffn;
         const float* wn = l + 1 < c.d_layers ? dw(l + 1, SPECDEC_DW_N1) : x->w.norm_f;
         resid_output(a, xd, Dd, 1, sd, xdw, wn);
-        if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
+        if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
       }
     }
     {  // next hidden input: W_back . (rms(x) * n_f)
@@ -725,7 +737,7 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
       norm_input(a, xdw, Dd, sd, Dd);
       a.out = hnext;
       a.ldo = d;
-      if ((rc = run(x, -1, 1, EPI_STORE, a, st))) return rc;
+      if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
     }
     int parts_per_seq, seq_off, ld;
     {

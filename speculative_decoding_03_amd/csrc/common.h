@@ -108,6 +108,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// (max, lowest index) over each row of 16 lanes, in the same exchange pattern as sum16.
+__device__ __forceinline__ void argmax16(float& v, int& i) {
+  argmax_combine(v, i, dpp_f32<DPP_XOR1>(v), dpp_i32<DPP_XOR1>(i));
+  argmax_combine(v, i, dpp_f32<DPP_XOR2>(v), dpp_i32<DPP_XOR2>(i));
+  argmax_combine(v, i, dpp_f32<DPP_HALF_MIRROR>(v), dpp_i32<DPP_HALF_MIRROR>(i));
+  argmax_combine(v, i, dpp_f32<DPP_MIRROR>(v), dpp_i32<DPP_MIRROR>(i));
+}
+
+// (max, lowest index) over the wave; every lane ends with the same pair.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax16(v, i);
+  auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  auto ri = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
+  v = __uint_as_float(rv[0]);
+  i = (int)ri[0];
+  argmax_combine(v, i, __uint_as_float(rv[1]), (int)ri[1]);
+  rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  ri = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+  v = __uint_as_float(rv[0]);
+  i = (int)ri[0];
+  argmax_combine(v, i, __uint_as_float(rv[1]), (int)ri[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   v = max16(v);
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -45,18 +45,6 @@ __device__ __forceinline__ void load_w(Frag<T>& f, const T* W, size_t tile, int 
   }
 }
 
-// X fragment of lane `lane` for k-block kb: X row r (the row that local row mt*16 + lane%16
-// reads; -1 = none), k = kb*32 + (lane/16)*8.
-template <typename T>
-__device__ __forceinline__ void load_x(Frag<T>& f, const GemmArgs& a, int r, int kb, int lane) {
-  if (r < 0) {
-    zero_frag(f);
-    return;
-  }
-  const int k = kb * TILE_K + ((lane >> 4) << 3);
-  load_frag<T>(f, reinterpret_cast<const T*>(a.X) + x_offset(a.x_qx, r, k, a.ldx));
-}
-
 // Fragment of k-block J of a quad block q (X in the quad layout, one wave load per block): lane
 // kg*16 + r takes lane kg*16 + 4J + r of its row of 16 (DPP row shift).  Lanes whose row is not
 // 0..3 of k-block J feed only output rows >= 4, which no epilogue stores.
@@ -90,13 +78,6 @@ __device__ __forceinline__ void quad_frag_rt(Frag<T>& f, const Frag<T>& q, int j
   }
 }
 
-// (max, lowest index) over each row of 16 lanes, in the same exchange pattern as sum16.
-__device__ __forceinline__ void argmax16(float& v, int& i) {
-  argmax_combine(v, i, dpp_f32<DPP_XOR1>(v), dpp_i32<DPP_XOR1>(i));
-  argmax_combine(v, i, dpp_f32<DPP_XOR2>(v), dpp_i32<DPP_XOR2>(i));
-  argmax_combine(v, i, dpp_f32<DPP_HALF_MIRROR>(v), dpp_i32<DPP_HALF_MIRROR>(i));
-  argmax_combine(v, i, dpp_f32<DPP_MIRROR>(v), dpp_i32<DPP_MIRROR>(i));
-}
 
 // Row-scale partial sums of up to 4 rows with n_yssq <= 64 * RS_J, loaded into registers after the
 // main loop and before the split-K reduction, so that their latency overlaps its barriers.
@@ -289,7 +270,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
         for (int v = 0; v < 4; ++v) {
           const int m = mt * 16 + rgrp + v;
           const float val = acc[t][mt][v];
-          const float partner = __shfl_xor(val, 1, WAVE);
+          const float partner = dpp_f32<DPP_XOR1>(val);  // the other element of the rotary pair
           if (m < a.M) {
             const int b = m / a.rows_per_seq;
             const int pos = pre.pos[mt][v];
@@ -451,9 +432,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   const int kb1 = min(a.nkb, kb0 + a.kb_per_split);
   const T* W = reinterpret_cast<const T*>(a.W);
 
-  bool tvalid[NU];
-#pragma unroll
-  for (int t = 0; t < NU; ++t) tvalid[t] = active && (tile0 + t) < a.n_tiles;
 
   f32x4 acc[NU][MT];
 #pragma unroll
@@ -555,58 +533,81 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     }
   }
   if (active && !quad_done) {
+    // Row-major X: the same ring of register stages as above.  Loads are branch-free: a tile past
+    // the matrix reads the last one (its sums are never stored) and a row that does not exist reads
+    // row 0, zeroed by a per-lane select before its product.
     constexpr int U = Unroll<NU, MT>::U;
-    // Two register stages: the loads of batch i+1 are in flight while batch i is multiplied.
-    Frag<T> w[2][U][NU];
-    Frag<T> x[2][U][MT];
+    constexpr int S = 2;
+    Frag<T> w[S][U][NU];
+    Frag<T> x[S][U][MT];
+    size_t wt_tile[NU];
+#pragma unroll
+    for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);
+    int xrow[MT];
+    bool xok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      xok[mt] = xr[mt] >= 0;
+      xrow[mt] = xok[mt] ? xr[mt] : 0;
+    }
+    const T* Xb = reinterpret_cast<const T*>(a.X);
+    const int kl = (lane >> 4) << 3;
     auto load_batch = [&](int st, int kbase) {
 #pragma unroll
       for (int uu = 0; uu < U; ++uu)
 #pragma unroll
-        for (int t = 0; t < NU; ++t) {
-          if (tvalid[t]) load_w<T>(w[st][uu][t], W, (size_t)(tile0 + t), a.nkb, kbase + uu, lane);
-          else zero_frag(w[st][uu][t]);
-        }
+        for (int t = 0; t < NU; ++t) load_w<T>(w[st][uu][t], W, wt_tile[t], a.nkb, kbase + uu, lane);
 #pragma unroll
       for (int uu = 0; uu < U; ++uu)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          load_x<T>(x[st][uu][mt], a, xr[mt], kbase + uu, lane);
+          load_frag<T>(x[st][uu][mt], Xb + x_offset(a.x_qx, xrow[mt], (kbase + uu) * TILE_K + kl, a.ldx));
     };
     auto mul_batch = [&](int st) {
 #pragma unroll
       for (int uu = 0; uu < U; ++uu)
 #pragma unroll
-        for (int t = 0; t < NU; ++t)
+        for (int mt = 0; mt < MT; ++mt) {
+          Frag<T> xf = x[st][uu][mt];
+          if (!xok[mt]) zero_frag(xf);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[t][mt] = mma<T>(x[st][uu][mt], w[st][uu][t], acc[t][mt]);
+          for (int t = 0; t < NU; ++t) acc[t][mt] = mma<T>(xf, w[st][uu][t], acc[t][mt]);
+        }
     };
     const int nb = (kb1 - kb0) / U;  // whole batches
-    if (nb > 0) load_batch(0, kb0);
-    for (int b = 0; b < nb; b += 2) {
-      if (b + 1 < nb) load_batch(1, kb0 + (b + 1) * U);
-      mul_batch(0);
-      if (b + 1 < nb) {
-        if (b + 2 < nb) load_batch(0, kb0 + (b + 2) * U);
-        mul_batch(1);
+    if (nb > 0) {
+      auto kb_of = [&](int i) { return kb0 + min(i, nb - 1) * U; };
+#pragma unroll
+      for (int st = 0; st < S - 1; ++st) load_batch(st, kb_of(st));
+      const int G = nb / S;
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+          load_batch((st + S - 1) % S, kb_of(g * S + st + S - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          mul_batch(st);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      const int r = nb - G * S;
+#pragma unroll
+      for (int st = 0; st < S - 1; ++st)
+        if (st < r) mul_batch(st);
     }
-    int kb = kb0 + nb * U;
-    for (; kb < kb1; ++kb) {
-      Frag<T> w[NU];
-      Frag<T> x[MT];
+    for (int kb = kb0 + nb * U; kb < kb1; ++kb) {
+      Frag<T> wt[NU];
+      Frag<T> xt[MT];
 #pragma unroll
-      for (int t = 0; t < NU; ++t) {
-        if (tvalid[t]) load_w<T>(w[t], W, (size_t)(tile0 + t), a.nkb, kb, lane);
-        else zero_frag(w[t]);
+      for (int t = 0; t < NU; ++t) load_w<T>(wt[t], W, wt_tile[t], a.nkb, kb, lane);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        load_frag<T>(xt[mt], Xb + x_offset(a.x_qx, xrow[mt], kb * TILE_K + kl, a.ldx));
+        if (!xok[mt]) zero_frag(xt[mt]);
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) load_x<T>(x[mt], a, xr[mt], kb, lane);
 #pragma unroll
       for (int t = 0; t < NU; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(x[mt], w[t], acc[t][mt]);
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(xt[mt], wt[t], acc[t][mt]);
     }
   }
 

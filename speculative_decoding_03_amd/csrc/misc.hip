@@ -23,12 +23,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 __device__ __forceinline__ void block_argmax(float& v, int& i, float* rv, int* ri) {
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, WAVE);
-    const int i2 = __shfl_xor(i, o, WAVE);
-    argmax_combine(v, i, v2, i2);
-  }
+  wave_argmax(v, i);
   __syncthreads();
   if (lane == 0) { rv[wid] = v; ri[wid] = i; }
   __syncthreads();
@@ -228,17 +223,19 @@ __global__ void __launch_bounds__(256) cluster_select_kernel(const float* z, int
 // routed to it in ascending row order, and the ascending list of experts that received a row.
 constexpr int MOE_MAX_M = 64, MOE_MAX_E = 256, MOE_MAX_K = 16;
 
-__global__ void __launch_bounds__(256) moe_route_kernel(const float* logits, int M, int E,
+constexpr int MOE_ROUTE_WAVES = 16;
+
+__global__ void __launch_bounds__(MOE_ROUTE_WAVES * 64) moe_route_kernel(const float* logits, int M, int E,
                                                         int top_k, int* xrow, int* orow,
                                                         float* wt, int* group_list,
                                                         int* n_groups, int* usage, int* err) {
   __shared__ int sel[MOE_MAX_M][MOE_MAX_K];
   __shared__ float selw[MOE_MAX_M][MOE_MAX_K];
   __shared__ int cnt[MOE_MAX_E];
-  __shared__ int wtot[4];
+  __shared__ int wtot[MOE_ROUTE_WAVES];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x >> 6;
-  for (int m = wid; m < M; m += 4) {
+  for (int m = wid; m < M; m += MOE_ROUTE_WAVES) {
     const float* r = logits + (size_t)m * E;
     float v[MOE_MAX_E / WAVE];
     int id[MOE_MAX_E / WAVE];
@@ -267,12 +264,7 @@ __global__ void __launch_bounds__(256) moe_route_kernel(const float* logits, int
         int bi = 0x7fffffff;
 #pragma unroll
         for (int j = 0; j < MOE_MAX_E / WAVE; ++j) argmax_combine(bv, bi, v[j], id[j]);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const float v2 = __shfl_xor(bv, o, WAVE);
-          const int i2 = __shfl_xor(bi, o, WAVE);
-          argmax_combine(bv, bi, v2, i2);
-        }
+        wave_argmax(bv, bi);
 #pragma unroll
         for (int j = 0; j < MOE_MAX_E / WAVE; ++j)
           if (id[j] == bi) {
@@ -328,7 +320,8 @@ __global__ void __launch_bounds__(256) moe_route_kernel(const float* logits, int
   for (int w = 0; w < wid; ++w) off += wtot[w];
   if (used) group_list[off + __popcll(mask & ((1ull << lane) - 1ull))] = e;
   if (threadIdx.x == 0) {
-    const int ng = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    int ng = 0;
+    for (int w = 0; w < MOE_ROUTE_WAVES; ++w) ng += wtot[w];
     n_groups[0] = ng;
     if (usage) usage[0] += ng;  // one writer: the launches of a layer are ordered on the stream
   }
@@ -465,7 +458,7 @@ hipError_t launch_moe_route(const float* logits, int M, int E, int top_k, int* x
   if (M < 1 || M > MOE_MAX_M || E < 1 || E > MOE_MAX_E || top_k < 1 || top_k > MOE_MAX_K ||
       top_k > E)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(256), 0, st, logits, M, E, top_k, xrow, orow,
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(MOE_ROUTE_WAVES * 64), 0, st, logits, M, E, top_k, xrow, orow,
                      wt, group_list, n_groups, usage, err);
   return hipGetLastError();
 }

@@ -535,80 +535,90 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   if (active && !quad_done) {
     // Row-major X: the same ring of register stages as above.  Loads are branch-free: a tile past
     // the matrix reads the last one (its sums are never stored) and a row that does not exist reads
-    // row 0, zeroed by a per-lane select before its product.
-    constexpr int U = Unroll<NU, MT>::U;
-    constexpr int S = 2;
-    Frag<T> w[S][U][NU];
-    Frag<T> x[S][U][MT];
-    size_t wt_tile[NU];
+    // row 0, zeroed by a per-lane select before its product.  Only the leading M-tiles that hold a
+    // row run (a routed expert gathers a few of the call's rows: its later M-tiles stay zero and
+    // their rows are never stored).
+    auto row_major = [&](auto mtc) {
+      constexpr int ML = decltype(mtc)::value;
+      constexpr int U = Unroll<NU, MT>::U;
+      constexpr int S = 2;
+      Frag<T> w[S][U][NU];
+      Frag<T> x[S][U][ML];
+      size_t wt_tile[NU];
 #pragma unroll
-    for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);
-    int xrow[MT];
-    bool xok[MT];
+      for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);
+      int xrow[ML];
+      bool xok[ML];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      xok[mt] = xr[mt] >= 0;
-      xrow[mt] = xok[mt] ? xr[mt] : 0;
-    }
-    const T* Xb = reinterpret_cast<const T*>(a.X);
-    const int kl = (lane >> 4) << 3;
-    auto load_batch = [&](int st, int kbase) {
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-        for (int t = 0; t < NU; ++t) load_w<T>(w[st][uu][t], W, wt_tile[t], a.nkb, kbase + uu, lane);
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          load_frag<T>(x[st][uu][mt], Xb + x_offset(a.x_qx, xrow[mt], (kbase + uu) * TILE_K + kl, a.ldx));
-    };
-    auto mul_batch = [&](int st) {
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          Frag<T> xf = x[st][uu][mt];
-          if (!xok[mt]) zero_frag(xf);
-#pragma unroll
-          for (int t = 0; t < NU; ++t) acc[t][mt] = mma<T>(xf, w[st][uu][t], acc[t][mt]);
-        }
-    };
-    const int nb = (kb1 - kb0) / U;  // whole batches
-    if (nb > 0) {
-      auto kb_of = [&](int i) { return kb0 + min(i, nb - 1) * U; };
-#pragma unroll
-      for (int st = 0; st < S - 1; ++st) load_batch(st, kb_of(st));
-      const int G = nb / S;
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int st = 0; st < S; ++st) {
-          load_batch((st + S - 1) % S, kb_of(g * S + st + S - 1));
-          __builtin_amdgcn_sched_barrier(0);
-          mul_batch(st);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int mt = 0; mt < ML; ++mt) {
+        xok[mt] = xr[mt] >= 0;
+        xrow[mt] = xok[mt] ? xr[mt] : 0;
       }
-      const int r = nb - G * S;
+      const T* Xb = reinterpret_cast<const T*>(a.X);
+      const int kl = (lane >> 4) << 3;
+      auto load_batch = [&](int st, int kbase) {
 #pragma unroll
-      for (int st = 0; st < S - 1; ++st)
-        if (st < r) mul_batch(st);
-    }
-    for (int kb = kb0 + nb * U; kb < kb1; ++kb) {
-      Frag<T> wt[NU];
-      Frag<T> xt[MT];
+        for (int uu = 0; uu < U; ++uu)
 #pragma unroll
-      for (int t = 0; t < NU; ++t) load_w<T>(wt[t], W, wt_tile[t], a.nkb, kb, lane);
+          for (int t = 0; t < NU; ++t) load_w<T>(w[st][uu][t], W, wt_tile[t], a.nkb, kbase + uu, lane);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        load_frag<T>(xt[mt], Xb + x_offset(a.x_qx, xrow[mt], kb * TILE_K + kl, a.ldx));
-        if (!xok[mt]) zero_frag(xt[mt]);
+        for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+          for (int mt = 0; mt < ML; ++mt)
+            load_frag<T>(x[st][uu][mt], Xb + x_offset(a.x_qx, xrow[mt], (kbase + uu) * TILE_K + kl, a.ldx));
+      };
+      auto mul_batch = [&](int st) {
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+          for (int mt = 0; mt < ML; ++mt) {
+            Frag<T> xf = x[st][uu][mt];
+            if (!xok[mt]) zero_frag(xf);
+#pragma unroll
+            for (int t = 0; t < NU; ++t) acc[t][mt] = mma<T>(xf, w[st][uu][t], acc[t][mt]);
+          }
+      };
+      const int nb = (kb1 - kb0) / U;  // whole batches
+      if (nb > 0) {
+        auto kb_of = [&](int i) { return kb0 + min(i, nb - 1) * U; };
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st) load_batch(st, kb_of(st));
+        const int G = nb / S;
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int st = 0; st < S; ++st) {
+            load_batch((st + S - 1) % S, kb_of(g * S + st + S - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            mul_batch(st);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        const int r = nb - G * S;
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st)
+          if (st < r) mul_batch(st);
       }
+      for (int kb = kb0 + nb * U; kb < kb1; ++kb) {
+        Frag<T> wt[NU];
+        Frag<T> xt[ML];
 #pragma unroll
-      for (int t = 0; t < NU; ++t)
+        for (int t = 0; t < NU; ++t) load_w<T>(wt[t], W, wt_tile[t], a.nkb, kb, lane);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mma<T>(xt[mt], wt[t], acc[t][mt]);
-    }
+        for (int mt = 0; mt < ML; ++mt) {
+          load_frag<T>(xt[mt], Xb + x_offset(a.x_qx, xrow[mt], kb * TILE_K + kl, a.ldx));
+          if (!xok[mt]) zero_frag(xt[mt]);
+        }
+#pragma unroll
+        for (int t = 0; t < NU; ++t)
+#pragma unroll
+          for (int mt = 0; mt < ML; ++mt) acc[t][mt] = mma<T>(xt[mt], wt[t], acc[t][mt]);
+      }
+    };
+    bool later_rows = false;  // does any M-tile after the first hold a row (wave-uniform)?
+#pragma unroll
+    for (int mt = 1; mt < MT; ++mt) later_rows |= __ballot(xr[mt] >= 0) != 0ull;
+    if (MT == 1 || !later_rows) row_major(std::integral_constant<int, 1>{});
+    else row_major(std::integral_constant<int, MT>{});
   }
 
   if (KW > 1) {

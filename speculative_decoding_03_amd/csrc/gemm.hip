@@ -219,6 +219,45 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
         for (int v = 0; v < 4; ++v) acc[t][mt][v] *= sc[mt][v];
   }
   if constexpr (EPI == EPI_STORE) {
+    // addend: a fixed-order sum of add_n row slices, read JB slices at a time for all of the
+    // lane's elements (at most 16 values) so that the loads are in flight together
+    constexpr int JB = 16 / (NU * MT * 4) > 1 ? 16 / (NU * MT * 4) : 1;
+    float adds[NU][MT][4];
+    if (a.addend) {
+#pragma unroll
+      for (int t = 0; t < NU; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) adds[t][mt][v] = 0.f;
+      for (int k0 = 0; k0 < a.add_n; k0 += JB) {
+        float ld[JB][NU][MT][4];
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+#pragma unroll
+          for (int t = 0; t < NU; ++t)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int m = min(mt * 16 + rgrp + v, a.M - 1);
+                const int col = min(tile0 + t, a.n_tiles - 1) * TILE_N + c16;
+                const int k = min(k0 + j, a.add_n - 1);
+                ld[j][t][mt][v] = a.addend[((size_t)m * a.add_n + k) * a.ldo + col];
+              }
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+          if (k0 + j < a.add_n) {
+#pragma unroll
+            for (int t = 0; t < NU; ++t)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  adds[t][mt][v] = k0 + j == 0 ? ld[j][t][mt][v] : adds[t][mt][v] + ld[j][t][mt][v];
+          }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < NU; ++t) {
       const int tile = tile0 + t;
@@ -234,12 +273,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           if (m < a.M) {
             float* o = a.out + (size_t)m * a.ldo + col;
             float y = acc[t][mt][v];
-            if (a.addend) {
-              const float* ad = a.addend + (size_t)m * a.add_n * a.ldo + col;
-              float s = ad[0];
-              for (int k = 1; k < a.add_n; ++k) s += ad[(size_t)k * a.ldo];
-              y = s + y;
-            }
+            if (a.addend) y = adds[t][mt][v] + y;
             if (a.accumulate) y = pre.res[t][mt][v] + y;
             *o = y;
             sq = y * y;

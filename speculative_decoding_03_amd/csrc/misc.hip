@@ -74,21 +74,47 @@ __global__ void __launch_bounds__(1024) accept_kernel(
     const float* amax_val, const int* amax_idx, int n_parts, int ld_amax, int R,
     const int* tokens, int* out_tokens, int* n_emit, int* next_tok, int commit, int* len,
     float* hid, const float* X, int d, int* argmax_out, int* err) {
-  __shared__ float rv[16];
-  __shared__ int ri[16];
+  // rows are reduced RG at a time: every thread's partial loads of the group are in flight
+  // together, each wave reduces its share of every row, and after one barrier thread j combines
+  // row j over the waves in wave order
+  constexpr int RG = 8, NWV = 16;
+  __shared__ float rv[RG][NWV];
+  __shared__ int ri[RG][NWV];
   __shared__ int G[64];
   __shared__ int m_sh;
   const int b = blockIdx.x;
-  for (int i = 0; i < R; ++i) {
-    const int row = b * R + i;
-    float v = -INFINITY;
-    int idx = 0x7fffffff;
+  const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x >> 6;
+  for (int i0 = 0; i0 < R; i0 += RG) {
+    float v[RG];
+    int idx[RG];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      v[j] = -INFINITY;
+      idx[j] = 0x7fffffff;
+    }
     for (int p = threadIdx.x; p < n_parts; p += blockDim.x)
-      argmax_combine(v, idx, amax_val[(size_t)row * ld_amax + p], amax_idx[(size_t)row * ld_amax + p]);
-    block_argmax(v, idx, rv, ri);
-    if (threadIdx.x == 0) {
-      G[i] = idx;
-      if (argmax_out) argmax_out[row] = idx;
+#pragma unroll
+      for (int j = 0; j < RG; ++j)
+        if (i0 + j < R) {
+          const size_t o = (size_t)(b * R + i0 + j) * ld_amax + p;
+          argmax_combine(v[j], idx[j], amax_val[o], amax_idx[o]);
+        }
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      wave_argmax(v[j], idx[j]);
+      if (lane == 0) {
+        rv[j][wid] = v[j];
+        ri[j][wid] = idx[j];
+      }
+    }
+    __syncthreads();
+    const int j = threadIdx.x;
+    if (j < RG && i0 + j < R) {
+      float bv = rv[j][0];
+      int bi = ri[j][0];
+      for (int w = 1; w < (int)(blockDim.x >> 6); ++w) argmax_combine(bv, bi, rv[j][w], ri[j][w]);
+      G[i0 + j] = bi;
+      if (argmax_out) argmax_out[b * R + i0 + j] = bi;
     }
     __syncthreads();
   }

@@ -28,12 +28,11 @@ namespace {
 constexpr size_t ALIGN = 256;
 constexpr int TARGET_WAVES = SPECDEC_TARGET_WAVES;        // waves per projection launch
 constexpr int MIN_KB_PER_WAVE = SPECDEC_MIN_KB_PER_WAVE;
-// Tiles per unit of the target's q/k/v, o and down projections: two (measured on MI355X at the
-// 31B shapes: one activation load then serves twice the weight bytes).
-#ifndef SPECDEC_STORE_NU
-#define SPECDEC_STORE_NU 2
-#endif
-constexpr int STORE_NU = SPECDEC_STORE_NU;  // k-blocks each wave streams at least
+// Tiles per unit of the target's q/k/v, o and down projections: two when the projection has at
+// least 256 tiles (one activation load then serves twice the weight bytes), else one, which keeps
+// more workgroups on the CUs (measured on MI355X: two at the 31B shapes, one at the E2B, E4B and
+// MoE model widths).
+int store_nu(int N) { return N / 16 >= 256 ? 2 : 1; }  // k-blocks each wave streams at least
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -261,10 +260,10 @@ void build_gemms(specdec_ctx* x) {
   x->g_dq.clear(); x->g_do.clear(); x->g_dgu.clear(); x->g_ddown.clear();
   for (int l = 0; l < c.n_layers; ++l) {
     const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
-    x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, STORE_NU));
-    x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, STORE_NU));
+    x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, store_nu(qd + 2 * kvd)));
+    x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, store_nu(d)));
     x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * Fw, d, 2, true, true));
-    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, Fw, STORE_NU));
+    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, Fw, store_nu(d)));
     if (c.n_experts > 0) {
       x->g_router.push_back(make_gemm(t[SPECDEC_LW_ROUTER], c.n_experts, d, 1));
       x->g_egu.push_back(make_grouped_gemm(t[SPECDEC_LW_EXP_GATE_UP], 2 * c.expert_ffn, d, 2,

@@ -101,6 +101,7 @@ __global__ void __launch_bounds__(1024) accept_kernel(
         }
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
+      if (i0 + j >= R) break;  // uniform
       wave_argmax(v[j], idx[j]);
       if (lane == 0) {
         rv[j][wid] = v[j];

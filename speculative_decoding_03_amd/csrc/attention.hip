@@ -7,8 +7,11 @@
 // that reads that KV head (all rows x the group's query heads).  K is stored [pos][hd] and V
 // transposed [hd][pos], so both MFMA operands stream as 16-byte loads.  Per chunk the kernel
 // leaves (row max in base-2 units, sum of exponentials, unnormalised value sum); attn_combine
-// merges the chunks in chunk order.  Chunk boundaries sit at fixed absolute positions and every reduction has a
-// fixed order, so a row's output does not depend on how many other rows are in the call.
+// merges the chunks in chunk order.  The value sums are kept in the storage type (bf16 rounds
+// each chunk's sum once, well inside the bf16 path's error budget, and halves the partial
+// traffic); the maxima and sums of exponentials stay fp32.  Chunk boundaries sit at fixed
+// absolute positions and every reduction has a fixed order, so a row's output does not depend
+// on how many other rows are in the call.
 
 #include <math.h>
 #include <stdlib.h>
@@ -73,6 +76,23 @@ __device__ __forceinline__ void keep_first(Frag<T>& f, int n) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) f.v[h][i] = 4 * h + i < n ? f.v[h][i] : 0u;
   }
+}
+
+// A chunk partial row: the value sum o[HD] in the storage type at the start of the row, then
+// (m, l) in fp32 at float offset HD; rows are HD + 4 floats apart.
+template <typename T>
+__device__ __forceinline__ void store_part_o(float* row, int d0, const f32x4& y) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 pk = {f32x2_to_bf16x2(y[0], y[1]), f32x2_to_bf16x2(y[2], y[3])};
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(row) + d0) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(row + d0) = y;
+  }
+}
+template <typename T>
+__device__ __forceinline__ float load_part_o(const float* row, int d) {
+  if constexpr (sizeof(T) == 2) return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
+  else return row[d];
 }
 
 // One workgroup = CH consecutive keys of one KV head of one sequence; wave w owns keys
@@ -258,7 +278,7 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 1; u < NWAVE; ++u)
         y += *reinterpret_cast<const f32x4*>(&xch[u][c16][dt * 16 + 4 * grp]) * fu[u];
-      if (qv < Rall) *reinterpret_cast<f32x4*>(pbase + (size_t)qv * SH::PST + dt * 16 + 4 * grp) = y;
+      if (qv < Rall) store_part_o<T>(pbase + (size_t)qv * SH::PST, dt * 16 + 4 * grp, y);
     }
     if (w == 0 && grp == 0 && qv < Rall) {
       float L = 0.f;
@@ -339,16 +359,16 @@ __global__ void __launch_bounds__(1024) attn_combine_kernel(AttnArgs a) {
   if (p < P) {
     int c = p;
     for (; c + 3 * P < n_act; c += 4 * P) {
-      const float v0 = pbase[(size_t)c * cstride + d];
-      const float v1 = pbase[(size_t)(c + P) * cstride + d];
-      const float v2 = pbase[(size_t)(c + 2 * P) * cstride + d];
-      const float v3 = pbase[(size_t)(c + 3 * P) * cstride + d];
+      const float v0 = load_part_o<T>(pbase + (size_t)c * cstride, d);
+      const float v1 = load_part_o<T>(pbase + (size_t)(c + P) * cstride, d);
+      const float v2 = load_part_o<T>(pbase + (size_t)(c + 2 * P) * cstride, d);
+      const float v3 = load_part_o<T>(pbase + (size_t)(c + 3 * P) * cstride, d);
       acc += wts[c] * v0;
       acc += wts[c + P] * v1;
       acc += wts[c + 2 * P] * v2;
       acc += wts[c + 3 * P] * v3;
     }
-    for (; c < n_act; c += P) acc += wts[c] * pbase[(size_t)c * cstride + d];
+    for (; c < n_act; c += P) acc += wts[c] * load_part_o<T>(pbase + (size_t)c * cstride, d);
     psum[p * hd + d] = acc;
   }
   __syncthreads();

@@ -34,38 +34,47 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* rv, int* r
 
 // x[m] = E[tokens[m]] (fp32 residual), xw[m] = x[m] * norm (the first layer's attention-norm
 // weight, storage type; row-major or the quad layout) and the per-16-column sums of squares of
-// x[m], from which the consumer forms the RMSNorm row scale.
+// x[m], from which the consumer forms the RMSNorm row scale.  Grid (d / 8 / 256 rounded up, M):
+// each thread moves one run of 8 consecutive elements (contiguous in the packed table), and the
+// two threads of a 16-column tile (adjacent lanes) add their sums with one lane exchange.
 template <typename T>
 __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, const int* tokens,
                                                     int M, float* x, float* ssq, T* xw, int xw_qx,
                                                     const float* norm, int vocab, int* err) {
-  extern __shared__ float sq[];
-  const int m = blockIdx.x;
+  const int m = blockIdx.y;
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;  // run of 8 elements in the row
+  const int k8 = c * 8;
   int tok = tokens[m];
   if (tok < 0 || tok >= vocab) {
-    if (threadIdx.x == 0) raise_error(err, ERRBIT_TOKEN);
+    if (c == 0) raise_error(err, ERRBIT_TOKEN);
     tok = 0;
   }
-  // 8 consecutive elements of a row are contiguous in the packed layout: one 16-byte load each
-  for (int k8 = threadIdx.x * 8; k8 < d; k8 += blockDim.x * 8) {
+  float sq = 0.f;
+  if (k8 < d) {
     Frag<T> f;
     load_frag<T>(f, E + packed_offset(tok, k8, nkb));
-    float v[8];
+    float v[8], y[8];
     frag_values<T>(f, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int k = k8 + e;
-      x[(size_t)m * d + k] = v[e];
-      Elem<T>::store(xw + x_offset(xw_qx, m, k, d), v[e] * norm[k]);
-      sq[k] = v[e] * v[e];
+      y[e] = v[e] * norm[k8 + e];
+      sq += v[e] * v[e];
+    }
+    f32x4* xo = reinterpret_cast<f32x4*>(x + (size_t)m * d + k8);
+    xo[0] = f32x4{v[0], v[1], v[2], v[3]};
+    xo[1] = f32x4{v[4], v[5], v[6], v[7]};
+    Frag<T> o;
+    to_frag<T>(o, y);
+    u32x4* q = reinterpret_cast<u32x4*>(xw + x_offset(xw_qx, m, k8, d));
+    if constexpr (sizeof(T) == 2) {
+      q[0] = o.v;
+    } else {
+      q[0] = o.v[0];
+      q[1] = o.v[1];
     }
   }
-  __syncthreads();
-  for (int t = threadIdx.x; t < d / TILE_N; t += blockDim.x) {
-    float s = 0.f;
-    for (int c = 0; c < TILE_N; ++c) s += sq[t * TILE_N + c];
-    ssq[(size_t)t * M + m] = s;
-  }
+  const float tot = sq + dpp_f32<DPP_XOR1>(sq);  // runs 2t and 2t+1 form 16-column tile t
+  if (k8 < d && (c & 1) == 0) ssq[(size_t)(k8 / TILE_N) * M + m] = tot;
 }
 
 // Per sequence: G[i] = argmax of row i over the LM-head partials; m = longest prefix with
@@ -429,12 +438,13 @@ hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tok
                         int* err, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (xw_qx && M > 4) return hipErrorInvalidValue;
-  const size_t lds = (size_t)d * sizeof(float);
+  if (d % TILE_N) return hipErrorInvalidValue;
+  const dim3 grid((d / 8 + 255) / 256, M);
   if (dtype == DT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), lds, st, (const bf16_t*)E, nkb,
-                       d, tokens, M, x, ssq, (bf16_t*)xw, xw_qx, norm, vocab, err);
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)E, nkb, d,
+                       tokens, M, x, ssq, (bf16_t*)xw, xw_qx, norm, vocab, err);
   else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), lds, st, (const float*)E, nkb, d,
+    hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, st, (const float*)E, nkb, d,
                        tokens, M, x, ssq, (float*)xw, xw_qx, norm, vocab, err);
   return hipGetLastError();
 }

@@ -1,8 +1,9 @@
 """GPU parity of the bf16 path at real widths, through the C ABI.
 
-Depth-truncated E2B-shaped (2 layers), 31B-class (1 layer) and 26B-class mixture-of-experts
-(1 layer: 128 experts, top-8, shared FFN) targets keep the full width and the full
-262144-entry vocabulary; norm weights are jittered so a dropped norm weight shows;
+Depth-truncated E2B-shaped (2 layers), E4B-shaped (1 layer; K=4, so a verify call has five
+rows and its projections take the row-major activation path), 31B-class (1 layer) and 26B-class
+mixture-of-experts (1 layer: 128 experts, top-8, shared FFN) targets keep the full width and
+the full 262144-entry vocabulary; norm weights are jittered so a dropped norm weight shows;
 the synthetic KV spans several attention chunks plus a ragged tail.  The oracle computes the
 hidden rows exactly and the logits on a sample of vocabulary rows (the LM head is a per-row dot
 product, so a sampled row is exact).  Tolerances: max relative error 2e-2 on logits and hidden
@@ -33,6 +34,7 @@ MARGIN = 0.05
 
 CASES = {
     "e2b-L2": truncated("e2b", 2, ctx=700, norm_jitter=0.1, d_layers=2),
+    "e4b-L1": truncated("e4b", 1, ctx=530, norm_jitter=0.1, d_layers=2),
     "31b-L1": truncated("31b", 1, ctx=530, norm_jitter=0.1, d_layers=2),
     "moe-L1": truncated("moe", 1, ctx=530, norm_jitter=0.1, d_layers=2),
 }

@@ -33,6 +33,9 @@ struct GemmArgs {
   const int* unit_row = nullptr;   // optional: argmax keeps only this row of unit u
   const int* n_units_dev = nullptr;  // optional device count of valid units
   int KW = 1, NW = 8, kb_per_split = 0;
+  // weights read again soon that fit in the last-level cache (the drafter's): plain loads;
+  // otherwise (the target's, streamed once per step) non-temporal loads
+  int w_cached = 0;
   int M = 0;
   // grouped launches (EPI_*_G): unit u computes group g = group_list[u / units_per_group]
   // (n_groups_dev[0] groups are listed), tiles g*tiles_per_group + (u % units_per_group)*NU.

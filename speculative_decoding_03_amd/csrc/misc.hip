@@ -167,6 +167,8 @@ __global__ void __launch_bounds__(256) commit_kernel(const int* n_commit, int R,
 }
 
 // u[b] = [ rms(h[b]) * norm_h ; rms(table[row(tok[b])]) * norm_e ] in the storage dtype.
+// h is requested first, as 16-byte runs held in registers (when d <= 4 * HV * blockDim.x), so its
+// latency overlaps the token -> table-row lookup; both sums of squares share one block reduction.
 template <typename T>
 __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const int* tok,
                                                           const T* table, int nkb_table,
@@ -174,23 +176,29 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
                                                           const float* norm_h, const float* norm_e,
                                                           int d, int Dd, float eps, T* u, int u_qx,
                                                           int* err) {
-  __shared__ float red[4];
+  constexpr int HV = 8;
+  __shared__ float red[2][16];
   __shared__ float ebuf[1024];
-  const int b = blockIdx.x;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int lane = t & (WAVE - 1), wid = t >> 6;
+  const float* hb = h + (size_t)b * d;
+  const bool hreg = d % 4 == 0 && d <= 4 * HV * (int)blockDim.x;
+  f32x4 hv[HV];
+  if (hreg) {
+#pragma unroll
+    for (int i = 0; i < HV; ++i) {
+      const int k = (t + i * (int)blockDim.x) * 4;
+      hv[i] = k < d ? *reinterpret_cast<const f32x4*>(hb + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   int c = tok[b];
   if (c < 0 || c >= vocab) {
-    if (threadIdx.x == 0) raise_error(err, ERRBIT_TOKEN);
+    if (t == 0) raise_error(err, ERRBIT_TOKEN);
     c = 0;
   }
   const int row = vocab_row[c];
-  float ssh = 0.f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float v = h[(size_t)b * d + k];
-    ssh += v * v;
-  }
-  ssh = block_sum(ssh, red);
   float sse = 0.f;
-  for (int k8 = threadIdx.x * 8; k8 < Dd; k8 += blockDim.x * 8) {
+  for (int k8 = t * 8; k8 < Dd; k8 += blockDim.x * 8) {
     Frag<T> f;
     load_frag<T>(f, table + packed_offset(row, k8, nkb_table));
     float v[8];
@@ -201,12 +209,44 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
       sse += v[e] * v[e];
     }
   }
-  sse = block_sum(sse, red);
+  float ssh = 0.f;
+  if (hreg) {
+#pragma unroll
+    for (int i = 0; i < HV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ssh += hv[i][e] * hv[i][e];
+  } else {
+    for (int k = t; k < d; k += blockDim.x) ssh += hb[k] * hb[k];
+  }
+  ssh = wave_sum(ssh);
+  sse = wave_sum(sse);
+  if (lane == 0) {
+    red[0][wid] = ssh;
+    red[1][wid] = sse;
+  }
+  __syncthreads();
+  ssh = 0.f;
+  sse = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    ssh += red[0][w];
+    sse += red[1][w];
+  }
   const float rh = 1.0f / sqrtf(ssh / (float)d + eps);
   const float re = 1.0f / sqrtf(sse / (float)Dd + eps);
-  for (int k = threadIdx.x; k < d; k += blockDim.x)
-    Elem<T>::store(u + x_offset(u_qx, b, k, d + Dd), h[(size_t)b * d + k] * rh * norm_h[k]);
-  for (int k = threadIdx.x; k < Dd; k += blockDim.x)
+  if (hreg) {
+#pragma unroll
+    for (int i = 0; i < HV; ++i) {
+      const int k = (t + i * (int)blockDim.x) * 4;
+      if (k < d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Elem<T>::store(u + x_offset(u_qx, b, k + e, d + Dd), hv[i][e] * rh * norm_h[k + e]);
+    }
+  } else {
+    for (int k = t; k < d; k += blockDim.x)
+      Elem<T>::store(u + x_offset(u_qx, b, k, d + Dd), hb[k] * rh * norm_h[k]);
+  }
+  for (int k = t; k < Dd; k += blockDim.x)
     Elem<T>::store(u + x_offset(u_qx, b, d + k, d + Dd), ebuf[k] * re * norm_e[k]);
 }
 

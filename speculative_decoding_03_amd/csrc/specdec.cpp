@@ -58,6 +58,7 @@ struct Gemm {
   const void* W = nullptr;
   int N = 0, Kd = 0, nkb = 0, n_tiles = 0, NU = 1, n_units = 0, KW = 1, NW = 8, kbps = 0;
   int tpg = 0, upg = 0;  // grouped (stacked experts): tiles and units per group
+  bool cached = false;   // the drafter's weights: re-read every sub-step, kept in the caches
 };
 
 // Split-K factor of a projection with `units` work units of NU tiles over nkb k-blocks.  Measured
@@ -285,6 +286,11 @@ void build_gemms(specdec_ctx* x) {
     x->g_dgu.push_back(make_gemm(t[SPECDEC_DW_GATE_UP], 2 * c.d_ffn, c.d_dim, 2, true, true));
     x->g_ddown.push_back(make_gemm(t[SPECDEC_DW_DOWN], c.d_dim, c.d_ffn, 1));
   }
+  // the drafter's weights (about 170 MB at the 31B shape, the full table included) are read
+  // again in every sub-step and fit in the 256 MB last-level cache
+  for (Gemm* g : {&x->g_in, &x->g_back, &x->g_cent, &x->g_table, &x->g_clu}) g->cached = true;
+  for (auto* v : {&x->g_dq, &x->g_do, &x->g_dgu, &x->g_ddown})
+    for (Gemm& g : *v) g.cached = true;
 }
 
 template <typename P>
@@ -332,6 +338,7 @@ GemmArgs base_args(specdec_ctx* x, const Gemm& g, int M) {
   a.KW = g.KW;
   a.NW = g.NW;
   a.kb_per_split = g.kbps;
+  a.w_cached = g.cached ? 1 : 0;
   a.M = M;
   a.x_qx = a.out_qx = M <= 4;  // activations of calls with at most 4 rows use the quad layout
   a.err = at<int>(x, x->lay.err);

@@ -354,7 +354,7 @@ def main() -> int:
         lb = gate_up_bytes(cfg, M)
         achieved = lb / (launch_ms * 1e-3) / 1e9
         kw, units, nw, groups = eng.query_split(0)
-        kname = f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}>"
+        kname = f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}, false>"
         grid = groups * nw * 64
         traffic = load_traffic(f"gemm_gate_up_{args.config}" + (f"_b{B}" if B > 1 else ""),
                                kname, grid, lb)

@@ -334,6 +334,9 @@ def main() -> int:
         "decode_ms": round(med(dec_ms), 4),
         "verify_over_decode": round(med(ver_ms) / med(dec_ms), 4),
         "draft_ms": round(med(draft_ms), 4),
+        "p10_p90_ms": {"verify": [round(float(np.percentile(ver_ms, q)), 4) for q in (10, 90)],
+                       "decode": [round(float(np.percentile(dec_ms, q)), 4) for q in (10, 90)],
+                       "draft": [round(float(np.percentile(draft_ms, q)), 4) for q in (10, 90)]},
         "verify_hbm_gbs": round(v_bytes / (med(ver_ms) * 1e-3) / 1e9, 1),
         "decode_hbm_gbs": round(d_bytes / (med(dec_ms) * 1e-3) / 1e9, 1),
         "verify_hbm_frac": round(v_bytes / (med(ver_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -14,6 +14,11 @@ dispatch).  Each is scaled by what the same counter reads for a plain device cop
   python -m speculative_decoding_03_amd.profsum traffic --fetch D --write D --copy-fetch D
       --copy-write D --match S --last N --algorithmic BYTES --src FILE --cmd CMD -o OUT
       per-dispatch HBM bytes of the matching kernel, written as JSON
+  python -m speculative_decoding_03_amd.profsum pass --fetch D --write D --copy-fetch D
+      --copy-write D [--mfma D --cus N] --index I --algorithmic BYTES --cmd CMD -o OUT
+      HBM bytes of every target pass (embed to accept, all kernels) from counter passes taken
+      without a kernel filter, against the pass's algorithmic bytes; with --mfma (a pass of
+      SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE) also the MFMA busy fraction
 """
 
 from __future__ import annotations
@@ -199,6 +204,66 @@ def cmd_traffic(a) -> int:
     return 0
 
 
+def _passes(vals):
+    """Split (dispatch id, name, value) triples, in dispatch order, into target passes: an
+    embed_kernel dispatch through the next accept_kernel dispatch."""
+    out, cur = [], None
+    for t in vals:
+        if "embed_kernel" in t[1]:
+            cur = [t]
+        elif cur is not None:
+            cur.append(t)
+            if "accept_kernel" in t[1]:
+                out.append(cur)
+                cur = None
+    return out
+
+
+def cmd_pass(a) -> int:
+    known = a.copy_mib * (1 << 20)
+    ff, fkib, _ = _copy_factor(a.copy_fetch, "FETCH_SIZE", known)
+    fw, wkib, _ = _copy_factor(a.copy_write, "WRITE_SIZE", known)
+    fp = _passes(counter_values(a.fetch, "FETCH_SIZE", None))
+    wp = _passes(counter_values(a.write, "WRITE_SIZE", None))
+    n = min(len(fp), len(wp))
+    lines = ["# HBM traffic of whole target passes (rocprofv3 counters, all kernels)", "",
+             f"command: {a.cmd}", "",
+             f"counters scaled by a plain {a.copy_mib} MiB device copy: FETCH_SIZE x {ff:.5f}, "
+             f"WRITE_SIZE x {fw:.5f}", "",
+             f"{'pass':>5} {'kernels':>8} {'fetch GB':>10} {'write GB':>10} {'total GB':>10}"]
+    tot = []
+    for i in range(n):
+        f = sum(v for _, _, v in fp[i]) * 1024.0 * ff
+        w = sum(v for _, _, v in wp[i]) * 1024.0 * fw
+        tot.append((f, w))
+        lines.append(f"{i:>5} {len(fp[i]):>8} {f / 1e9:>10.3f} {w / 1e9:>10.3f} {(f + w) / 1e9:>10.3f}")
+    f, w = tot[a.index]
+    lines += ["", f"pass {a.index}: {(f + w) / 1e9:.3f} GB measured against {a.algorithmic / 1e9:.3f} GB "
+              f"algorithmic = {(f + w) / a.algorithmic:.4f}x"]
+    if a.mfma:
+        # SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs; the capacity of a dispatch is its
+        # duration x clock x SIMDs (durations under counter collection run long, so this is a
+        # lower bound of the busy fraction)
+        rows = [r for r in _rows(_one(a.mfma, "counter_collection.csv"))
+                if r.get("Counter_Name") == "SQ_VALU_MFMA_BUSY_CYCLES"]
+        trip = sorted((int(r["Dispatch_Id"]), short_name(r["Kernel_Name"]),
+                       (float(r["Counter_Value"]),
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))) for r in rows)
+        mp = _passes(trip)
+        if mp:
+            b = sum(v[0] for _, _, v in mp[a.index])
+            t = sum(v[1] for _, _, v in mp[a.index]) * 1e-9
+            cap = t * a.clock_ghz * 1e9 * a.cus * 4
+            lines += [f"pass {a.index}: MFMA busy {b:.4g} SIMD-cycles over {t * 1e3:.2f} ms of its "
+                      f"dispatches x {a.clock_ghz} GHz x {a.cus} CUs x 4 SIMDs = {b / cap:.4f} "
+                      f"of the MFMA capacity"]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        open(a.out, "w").write(text)
+    sys.stdout.write(text)
+    return 0
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(prog="profsum")
     sp = p.add_subparsers(dest="what", required=True)
@@ -229,8 +294,20 @@ def main(argv=None) -> int:
     t.add_argument("--src", required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("-o", "--out")
+    ps = sp.add_parser("pass")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        ps.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    ps.add_argument("--copy-mib", type=int, default=1024)
+    ps.add_argument("--mfma")
+    ps.add_argument("--cus", type=int, default=256)
+    ps.add_argument("--clock-ghz", type=float, default=2.4)
+    ps.add_argument("--index", type=int, default=-1)
+    ps.add_argument("--algorithmic", type=float, required=True)
+    ps.add_argument("--cmd", required=True)
+    ps.add_argument("-o", "--out")
     a = p.parse_args(argv)
-    return {"copy": cmd_copy, "stats": cmd_stats, "step": cmd_step, "traffic": cmd_traffic}[a.what](a)
+    return {"copy": cmd_copy, "stats": cmd_stats, "step": cmd_step, "traffic": cmd_traffic,
+            "pass": cmd_pass}[a.what](a)
 
 
 if __name__ == "__main__":

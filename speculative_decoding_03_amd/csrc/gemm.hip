@@ -99,6 +99,14 @@ struct RowScaleLoads {
   bool fast;
 };
 
+// Local row of element v of M-tile mt in a lane.  The MFMA leaves rows (lane/16)*4 + v of
+// column lane%16; with a single M-tile of at most 4 rows ("narrow") all rows sit in lanes 0-15,
+// so the epilogue first moves row r to lanes 16r..16r+15 and then handles element 0 only, with
+// every lane busy.  Elements that hold no row get an index past any M.
+__device__ __forceinline__ int local_row(bool narrow, int mt, int v, int lane) {
+  return narrow ? (v == 0 ? (lane >> 4) : (1 << 20)) : mt * 16 + ((lane >> 4) << 2) + v;
+}
+
 // Epilogue operands that do not depend on the products, read before the main loop so that their
 // latency hides behind it: the norm weight and current value of each stored element (EPI_STORE),
 // the rotary inverse frequency and the row positions (EPI_ROPE).
@@ -113,7 +121,7 @@ template <int MT, int NU, int EPI>
 __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int lane,
                                              EpiPre<MT, NU>& pre) {
   const int c16 = lane & 15;
-  const int rgrp = (lane >> 4) << 2;
+  const bool narrow = MT == 1 && a.M <= 4;
   if constexpr (EPI == EPI_STORE) {
 #pragma unroll
     for (int t = 0; t < NU; ++t) {
@@ -123,7 +131,7 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int l
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = mt * 16 + rgrp + v;
+          const int m = local_row(narrow, mt, v, lane);
           pre.res[t][mt][v] = (a.accumulate && m < a.M) ? a.out[(size_t)m * a.ldo + col] : 0.f;
         }
     }
@@ -132,7 +140,7 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int l
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = mt * 16 + rgrp + v;
+        const int m = local_row(narrow, mt, v, lane);
         const int b = m < a.M ? m / a.rows_per_seq : 0;
         pre.pos[mt][v] = a.len[b] + (m - b * a.rows_per_seq) + a.pos_off;
       }
@@ -204,12 +212,12 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const in
       }
     }
   }
-  const int rgrp = (lane >> 4) << 2;
+  const bool narrow = MT == 1 && a.M <= 4;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int r = __shfl(xr[mt], rgrp + v, WAVE);
+      const int r = __shfl(xr[mt], local_row(narrow, mt, v, lane) & 15, WAVE);
       sc[mt][v] = __shfl(mine, r < 0 ? 0 : (r & 63), WAVE);
     }
 }
@@ -219,7 +227,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
                                          int tile0, int grp, const int (&xr)[MT],
                                          const RowScaleLoads& rs, const EpiPre<MT, NU>& pre, int lane) {
   const int c16 = lane & 15;
-  const int rgrp = (lane >> 4) << 2;
+  const bool narrow = MT == 1 && a.M <= 4;
+  if (narrow) {
+    // row r of column c moves from element r of lane c to element 0 of lane 16r + c
+    const int src = lane & 15, r = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < NU; ++t) {
+      const float x0 = __shfl(acc[t][0][0], src, WAVE), x1 = __shfl(acc[t][0][1], src, WAVE);
+      const float x2 = __shfl(acc[t][0][2], src, WAVE), x3 = __shfl(acc[t][0][3], src, WAVE);
+      acc[t][0][0] = r == 0 ? x0 : (r == 1 ? x1 : (r == 2 ? x2 : x3));
+    }
+  }
   if (a.yssq) {
     float sc[MT][4];
     row_scales<MT>(a, lane, xr, rs, sc);
@@ -252,7 +270,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
-                const int m = min(mt * 16 + rgrp + v, a.M - 1);
+                const int m = min(local_row(narrow, mt, v, lane), a.M - 1);
                 const int col = min(tile0 + t, a.n_tiles - 1) * TILE_N + c16;
                 const int k = min(k0 + j, a.add_n - 1);
                 ld[j][t][mt][v] = a.addend[((size_t)m * a.add_n + k) * a.ldo + col];
@@ -280,7 +298,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = mt * 16 + rgrp + v;
+          if (narrow && v > 0) continue;  // uniform
+          const int m = local_row(narrow, mt, v, lane);
           float sq = 0.f;
           if (m < a.M) {
             float* o = a.out + (size_t)m * a.ldo + col;
@@ -314,7 +333,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = mt * 16 + rgrp + v;
+          if (narrow && v > 0) continue;  // uniform
+          const int m = local_row(narrow, mt, v, lane);
           const float val = acc[t][mt][v];
           const float partner = dpp_f32<DPP_XOR1>(val);  // the other element of the rotary pair
           if (m < a.M) {
@@ -349,7 +369,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = mt * 16 + rgrp + v;
+        if (narrow && v > 0) continue;  // uniform
+        const int m = local_row(narrow, mt, v, lane);
         if (m >= a.M) continue;
         const int orow = a.orow_map[(size_t)grp * a.M + m];
         if (orow < 0) continue;
@@ -369,7 +390,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = mt * 16 + rgrp + v;
+        if (narrow && v > 0) continue;  // uniform
+        const int m = local_row(narrow, mt, v, lane);
         if (m < a.M) {
           const float g = acc[0][mt][v];
           const float up = acc[1][mt][v];
@@ -383,7 +405,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = mt * 16 + rgrp + v;
+        if (narrow && v > 0) continue;  // uniform
+        const int m = local_row(narrow, mt, v, lane);
         float best = -INFINITY;
         int bidx = 0x7fffffff;
         bool nan = false;

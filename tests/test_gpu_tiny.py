@@ -127,6 +127,34 @@ def test_gpu_spec_equals_gpu_greedy(tiny, p):
     assert eng.device_error() == 0
 
 
+@pytest.mark.parametrize("name", ["tiny", "tiny-moe"])
+def test_spec_equals_greedy_at_every_draft_length(name):
+    """The draft length is a per-call knob: K = 1 (the smallest speculative step: one draft, two
+    verify rows), 2 and 5 (past the configured 3) reproduce the same GPU's greedy output, with
+    exactly K+1 tokens per step when every draft is the target's own token."""
+    cfg = preset(name)
+    kmax = 5
+    eng = build_engine(cfg.replace(draft_k=kmax), MAX_CTX)
+    prompt = prompt_tokens(cfg)[0]
+    t0, _ = gpu_prefill(eng, prompt, want_logits=False)
+    snap = snapshot(eng)
+    n = cfg.gen_tokens
+    ref = gpu_greedy(eng, t0, n + kmax + 2)
+    L = len(prompt)
+    gseq = np.full(MAX_CTX, -1, dtype=np.int64)
+    gseq[L:L + len(ref)] = ref
+    for K in (1, 2, 5):
+        for p in (0.6, 1.0):
+            restore(eng, snap)
+            toks, emitted = gpu_spec(eng, t0, n, K, inject_table(gseq, K, p, cfg.inject_seed))
+            assert toks == ref[:n], f"K={K} p={p}"
+            assert all(1 <= e <= K + 1 for e in emitted)
+            if p == 1.0:
+                assert all(e == K + 1 for e in emitted), f"K={K}"
+    assert eng.device_error() == 0
+    eng.close()
+
+
 @pytest.mark.parametrize("mode,k_c", [("clustered", 1), ("clustered", 3), ("clustered", 64), ("full", 0)])
 def test_drafter_matches_oracle(tiny, mode, k_c):
     CFG = tiny["cfg"]

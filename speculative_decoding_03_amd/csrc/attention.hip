@@ -153,8 +153,8 @@ attn_kernel(AttnArgs a) {
     }
   // this lane's query column of tile q0 (columns past Rall load a valid row; their scores are
   // masked to -inf), already in the storage type
-  Frag<T> qf[DS];
-  auto load_q = [&](int q0) {
+  Frag<T> qa[DS], qb[DS];
+  auto load_q = [&](int q0, Frag<T> (&qf)[DS]) {
     const int qc = min(q0 + c16, Rall - 1);
     const int row = qc / G;
     const T* qp = reinterpret_cast<const T*>(a.q) +
@@ -166,7 +166,8 @@ attn_kernel(AttnArgs a) {
       else zero_frag(qf[ds]);
     }
   };
-  load_q(0);
+  load_q(0, qa);
+  if (Rall > 16) load_q(16, qb);  // the second tile's query vectors are requested up front
   Frag<T> vf[NB][DT];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -179,7 +180,7 @@ attn_kernel(AttnArgs a) {
   const bool ragged = kw0 + KPW > end_max;  // the wave holds values past end_max (wave-uniform)
 
   float* pbase = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * SH::PST;
-  for (int q0 = 0; q0 < Rall; q0 += 16) {
+  auto tile = [&](int q0, Frag<T> (&qf)[DS]) {
     const int qv = q0 + c16;  // this lane's query column
     const int row = qv / G;
 
@@ -194,8 +195,8 @@ attn_kernel(AttnArgs a) {
         for (int ds = 0; ds < DS; ++ds) acc = mma<T>(kf[nb][h][ds], qf[ds], acc);
         s[nb][h] = acc;
       }
-    // the next tile's query vectors load while this tile finishes
-    if (q0 + 16 < Rall) load_q(q0 + 16);
+    // the tile after next reuses this tile's buffer once its scores are done
+    if (q0 + 32 < Rall) load_q(q0 + 32, qf);
     const int kend = qv < Rall ? len + row + a.key_off : 0;  // keys [0, kend) are visible
     // scores in base-2 units (scale * log2 e folded in): exp(x - m) = exp2(x2 - m2)
     float m = -INFINITY;
@@ -288,6 +289,10 @@ attn_kernel(AttnArgs a) {
       pbase[(size_t)qv * SH::PST + HD + 1] = L;
     }
     if (q0 + 16 < Rall) __syncthreads();  // the next tile reuses the LDS buffers
+  };
+  for (int q0 = 0; q0 < Rall; q0 += 32) {
+    tile(q0, qa);
+    if (q0 + 16 < Rall) tile(q0 + 16, qb);
   }
 }
 

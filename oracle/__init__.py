@@ -9,8 +9,10 @@ Python binding; both sides take their seeded inputs from ``workloads``.
 Every function here is pinned by a ``-m "not gpu"`` test against something
 other than itself (closed forms, textbook special cases, brute force, the
 invariants the pages state, an independent matrix-form forward).  The drafter
-layer numerics (``draft``) are pinned only by special cases and by
-self-consistency; there is no printed worked example on the pages.
+sub-step (``drafter_substep`` / ``draft``) is pinned by hand-worked closed
+forms on 2-wide weights and by an independent explicit-loop drafter, and each
+plausible wiring mistake planted into a copy of this source fails one of those
+pins (tests/test_oracle_drafter.py); the pages print no worked example.
 """
 
 from .model import *  # noqa: F401,F403

@@ -28,7 +28,8 @@ __all__ = [
     "as_f64", "rmsnorm", "silu", "rope", "attention", "dense_ffn", "moe_ffn", "moe_route",
     "moe_route_margin",
     "KVCache", "decoder_layer_row", "target_row", "lm_head", "argmax_first", "top2_margin",
-    "greedy_generate", "prefill", "verify", "accept", "commit", "head_full",
+    "greedy_generate", "prefill", "verify", "accept", "commit", "token_scores",
+    "centroid_scores", "head_full",
     "head_clustered", "drafter_substep", "draft", "inject", "spec_generate", "SpecStats",
 ]
 
@@ -295,9 +296,19 @@ def commit(cache: KVCache | None, length: int, n_rows: int, m: int, H, poison: b
 # full-vocabulary scoring (same [guide] section; [digest] "Inside the MTP drafter").
 # ---------------------------------------------------------------------------
 
+def token_scores(table: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Score of every token the table lists: table[t] . s."""
+    return table @ s
+
+
+def centroid_scores(centroids: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Score of every cluster: centroids[c] . s."""
+    return centroids @ s
+
+
 def head_full(table: np.ndarray, s: np.ndarray) -> int:
     """Full-vocabulary scoring: argmax over t of table[t] . s (lowest vocab id on ties)."""
-    return argmax_first(table @ s)
+    return argmax_first(token_scores(table, s))
 
 
 def head_clustered(table: np.ndarray, centroids: np.ndarray, perm: np.ndarray, s: np.ndarray,
@@ -308,10 +319,10 @@ def head_clustered(table: np.ndarray, centroids: np.ndarray, perm: np.ndarray, s
     equal size from a seeded permutation, centroid = member mean."""
     Nc = centroids.shape[0]
     S = table.shape[0] // Nc
-    z = centroids @ s
+    z = centroid_scores(centroids, s)
     sel = sorted(range(Nc), key=lambda c: (-z[c], c))[:k_c]
     cand = np.sort(np.concatenate([perm[c * S:(c + 1) * S] for c in sel]))
-    scores = table[cand] @ s
+    scores = token_scores(table[cand], s)
     if np.isnan(scores).any():
         raise FloatingPointError("NaN in drafter scores")
     best = int(np.argmax(scores))  # cand is sorted, so the first max is the lowest vocab id

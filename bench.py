@@ -92,7 +92,7 @@ def load_traffic(name: str, kernel: str, grid: int, launch_bytes: float):
         return None
     try:
         d = json.load(open(p))
-        cur = src_sha(os.path.join(ROOT, "speculative_decoding_03_amd", "csrc", "gemm.hip"))
+        cur = src_sha(os.path.join(ROOT, "speculative_decoding_03_amd", "csrc", "gemm_impl.h"))
         if (d.get("kernel_src_sha") != cur or d.get("kernel") != kernel
                 or d.get("grid_work_items") != grid
                 or d.get("algorithmic_bytes_per_dispatch") != launch_bytes):
@@ -186,6 +186,8 @@ def main() -> int:
     ap.add_argument("--k-c", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--no-p-sweep", dest="p_sweep", action="store_false")
+    ap.add_argument("--sweep-steps", type=int, default=40)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the path is built and measured on a single MI355X "
@@ -252,62 +254,134 @@ def main() -> int:
     log(f"greedy: {n_greedy} decode steps, median {np.median(dec_ms):.3f} ms")
 
     # ---- speculative loop: draft -> verify -> accept + commit, B sequences per step ----
-    restore()
-    tabs = []
-    for b in range(B):
-        gseq = np.full(max_ctx, -1, dtype=np.int64)
-        gseq[cfg.ctx:cfg.ctx + len(greedy[b])] = greedy[b]
-        tabs.append(inject_table(gseq, K, cfg.p_inject, cfg.inject_seed, b=b))
-    tab = torch.from_numpy(np.stack(tabs)).to(dev)
-    cur = t0.clone()                    # current token per sequence
-    drafts = torch.empty(B, K, dtype=torch.int32, device=dev)
-    T = torch.empty(B, K + 1, dtype=torch.int32, device=dev)  # verify rows, written by the draft
-    outs = torch.full((S_all, B, K + 1), -1, dtype=torch.int32, device=dev)
-    n_emit = torch.zeros(S_all, B, dtype=torch.int32, device=dev)
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(S_all)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(S_all)]
-    e2 = [torch.cuda.Event(enable_timing=True) for _ in range(S_all)]
+    def inject_tab(p):
+        tabs = []
+        for b in range(B):
+            gseq = np.full(max_ctx, -1, dtype=np.int64)
+            gseq[cfg.ctx:cfg.ctx + len(greedy[b])] = greedy[b]
+            tabs.append(inject_table(gseq, K, p, cfg.inject_seed, b=b))
+        return torch.from_numpy(np.stack(tabs)).to(dev)
 
-    def step(i):
-        e0[i].record()
-        eng.draft(cur, drafts, head_mode=head_mode, k_c=args.k_c, inject=tab, verify_tokens=T)
-        e1[i].record()
-        eng.verify(T)
-        eng.accept(T, out_tokens=outs[i], n_emit=n_emit[i], next_tok=cur, commit=True)
-        e2[i].record()
+    def spec_run(p, warm, steps, graph=False, prof_steps=0, moe=False):
+        """warm + steps (+ prof_steps) speculative steps at injection rate p.  Every step ends
+        with one pinned device-to-host copy of its emitted tokens and their count, which the host
+        reads one step later (the next step is already enqueued) to learn the committed length;
+        the host-side bound on it is then exact up to the one step in flight.  graph=True replays
+        one captured step (draft, verify, accept + commit) instead of enqueueing its kernels."""
+        restore()
+        tab = inject_tab(p)
+        S = warm + steps + prof_steps
+        cur = t0.clone()
+        drafts = torch.empty(B, K, dtype=torch.int32, device=dev)
+        T = torch.empty(B, K + 1, dtype=torch.int32, device=dev)  # verify rows, written by the draft
+        out_d = torch.full((B, K + 1), -1, dtype=torch.int32, device=dev)
+        ne_d = torch.zeros(B, dtype=torch.int32, device=dev)
+        out_h = torch.full((S, B, K + 1), -1, dtype=torch.int32).pin_memory()
+        ne_h = torch.zeros(S, B, dtype=torch.int32).pin_memory()
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+        e2 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+        done = [torch.cuda.Event() for _ in range(S)]
 
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    if cfg.is_moe:
-        eng.moe_usage_start()
-    t_start = time.perf_counter()
-    for i in range(W, W + N):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ver_experts = sum(eng.moe_usage_read()) / N if cfg.is_moe else 0.0
-    gate_ms = []
-    if P:
-        eng.profile_start(SD.ffi.PROF_GATE_UP, cfg.n_layers * P)
-        for i in range(W + N, S_all):
-            step(i)
-        gate_ms = eng.profile_read()
-    assert eng.device_error() == 0, "device error during the speculative loop"
+        def body():
+            eng.draft(cur, drafts, head_mode=head_mode, k_c=args.k_c, inject=tab, verify_tokens=T)
+            eng.verify(T)
+            eng.accept(T, out_tokens=out_d, n_emit=ne_d, next_tok=cur, commit=True)
 
-    ne = n_emit.cpu().numpy()
-    ot = outs.cpu().numpy()
-    same = True
-    for b in range(B):
-        spec = [int(t0[b].item())]
-        for i in range(S_all):
-            spec.extend(ot[i, b, : ne[i, b]].tolist())
-        same &= spec == greedy[b][: len(spec)]
-    emitted = int(ne[W:W + N].sum())
+        g = None
+        if graph:
+            # captured with the bound at its largest, so that the attention launches cover every
+            # chunk a later committed length can reach (the kernels check the device length)
+            eng.set_len_bound([max_ctx - (K + 1)] * B)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                body()
+            torch.cuda.synchronize()
+            restore()
+        known = [cfg.ctx] * B
+
+        def enqueue(i):
+            e0[i].record()
+            if graph:
+                g.replay()
+                e1[i].record()
+            else:
+                eng.set_len_bound([n + K + 1 for n in known])  # step i - 1 is still in flight
+                eng.draft(cur, drafts, head_mode=head_mode, k_c=args.k_c, inject=tab,
+                          verify_tokens=T)
+                e1[i].record()
+                eng.verify(T)
+                eng.accept(T, out_tokens=out_d, n_emit=ne_d, next_tok=cur, commit=True)
+            e2[i].record()
+            out_h[i].copy_(out_d, non_blocking=True)
+            ne_h[i].copy_(ne_d, non_blocking=True)
+            done[i].record()
+
+        def read(i):
+            done[i].synchronize()
+            for b in range(B):
+                known[b] += int(ne_h[i, b])
+
+        def run(lo, hi):
+            for i in range(lo, hi):
+                enqueue(i)
+                if i > lo:
+                    read(i - 1)
+            read(hi - 1)
+
+        run(0, warm)
+        torch.cuda.synchronize()
+        if moe:
+            eng.moe_usage_start()
+        t_start = time.perf_counter()
+        run(warm, warm + steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        experts = sum(eng.moe_usage_read()) / steps if moe else 0.0
+        gate = []
+        if prof_steps:
+            eng.profile_start(SD.ffi.PROF_GATE_UP, cfg.n_layers * prof_steps)
+            run(warm + steps, S)
+            gate = eng.profile_read()
+        assert eng.device_error() == 0, "device error during the speculative loop"
+        del g
+        ne, ot = ne_h.numpy().copy(), out_h.numpy().copy()
+        same = True
+        for b in range(B):
+            spec = [int(t0[b].item())]
+            for i in range(S):
+                spec.extend(ot[i, b, : ne[i, b]].tolist())
+            same &= spec == greedy[b][: len(spec)]
+        timed = range(warm, warm + steps)
+        return {"wall": wall, "ne": ne, "same": bool(same), "experts": experts, "gate_ms": gate,
+                "emitted": int(ne[warm:warm + steps].sum()),
+                "draft_ms": [e0[i].elapsed_time(e1[i]) for i in timed] if not graph else [],
+                "ver_ms": [e1[i].elapsed_time(e2[i]) for i in timed] if not graph else [],
+                "step_ms": [e0[i].elapsed_time(e2[i]) for i in timed]}
+
+    main = spec_run(cfg.p_inject, W, N, prof_steps=P, moe=cfg.is_moe)
+    wall, ne, same = main["wall"], main["ne"], main["same"]
+    ver_experts = main["experts"]
+    gate_ms = main["gate_ms"]
+    draft_ms, ver_ms = main["draft_ms"], main["ver_ms"]
+    log(f"speculative loop: {main['emitted'] / wall:.1f} tokens/s, spec == greedy: {same}")
+    # graph replay of the whole step, same workload
+    gr = spec_run(cfg.p_inject, W, N, graph=True)
+    log(f"graph replay: {gr['emitted'] / gr['wall']:.1f} tokens/s, spec == greedy: {gr['same']}")
+    # acceptance mix sweep: p = 0.81 and 0.89 reproduce the pages' tokens-per-pass figures
+    sweep = {}
+    if args.p_sweep:
+        for p in (0.0, 0.6, 0.7, 0.81, 0.89, 1.0):
+            r = spec_run(p, 2, args.sweep_steps)
+            sweep[str(p)] = {"tokens_per_s": round(r["emitted"] / r["wall"], 2),
+                             "tokens_per_step": round(r["emitted"] / (args.sweep_steps * B), 3),
+                             "ms_per_step": round(1e3 * r["wall"] / args.sweep_steps, 3),
+                             "spec_equals_greedy": r["same"]}
+        log("p sweep: " + ", ".join(f"{p}: {v['tokens_per_s']}" for p, v in sweep.items()))
+
+    emitted = main["emitted"]
     accepted = emitted - N * B
     tok_s = emitted / wall
-    draft_ms = [e0[i].elapsed_time(e1[i]) for i in range(W, W + N)]
-    ver_ms = [e1[i].elapsed_time(e2[i]) for i in range(W, W + N)]
     med = lambda v: float(np.median(v))  # noqa: E731
     # visible keys of a timed verify: committed length at the step's start + K + 1, averaged
     start_len = cfg.ctx + np.cumsum(np.concatenate([np.zeros((1, B)), ne[:-1]]), axis=0)
@@ -346,7 +420,16 @@ def main() -> int:
         "accepted_over_proposed": round(accepted / (N * B * K), 4),
         "spec_equals_greedy": bool(same),
         "draft_substep_mb": round(draft_substep_bytes(cfg, B, keys_v) / 1e6, 2),
+        "host_readback": "one pinned device-to-host copy of each step's tokens and count, read by "
+                         "the host one step later to learn the committed length",
+        "graph_replay": {"tokens_per_s": round(gr["emitted"] / gr["wall"], 3),
+                         "ms_per_step": round(1e3 * gr["wall"] / N, 4),
+                         "step_ms_median": round(med(gr["step_ms"]), 4),
+                         "eager_step_ms_median": round(med(main["step_ms"]), 4),
+                         "spec_equals_greedy": gr["same"]},
     }
+    if sweep:
+        res["p_sweep"] = sweep
     if cfg.is_moe:
         res["moe"] = {"experts_read_per_verify": round(ver_experts, 1),
                       "experts_read_per_decode": round(dec_experts, 1),

@@ -148,8 +148,8 @@ size_t specdec_kv_elems(const specdec_config* cfg);
      hid         float [max_batch][d_model]: the drafter's hidden input (the target's
                  pre-final-norm residual of the last committed position)
      workspace   specdec_workspace_bytes(cfg) bytes, 256-byte aligned
-   Enqueues one small kernel on `stream` that zeroes the workspace's arrival counters and the
-   device error word.  Errors: SPECDEC_E_INVAL (null pointers, shapes not multiples of the
+   Enqueues two small kernels on `stream`: one zeroes the device error word, one tabulates the
+   rotary (cos, sin) of every position in the workspace.  Errors: SPECDEC_E_INVAL (null pointers, shapes not multiples of the
    tile: d_model, Hq*hd, ffn_dim (dense), expert_ffn and shared_ffn (MoE), d_dim, d_ffn % 32;
    head_dim % 16, head_dim <= 256; vocab % 64; vocab / n_centroids % 64; n_centroids % 16;
    max_batch*max_rows <= 64; max_rows <= 64; max_ctx % 8; MoE: n_experts <= 256 and % 16,
@@ -174,10 +174,36 @@ int specdec_destroy(specdec_ctx* ctx);
    skip) receives the next verify's input rows [c0, d1..dK] (drafts after injection), so a batch
    goes from draft to verify without a copy; it may overlap cur_tok at column 0.
    Errors: SPECDEC_E_INVAL (B > max_batch, K < 1, K > max_draft, k_c outside [1, n_centroids],
-   null pointers). */
+   null pointers), SPECDEC_E_CAPACITY (the host-side bound of len + K exceeds max_ctx: the last
+   sub-step's query position len + K - 1 must be a cache slot). */
 int specdec_draft(specdec_ctx* ctx, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
                   const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
                   int64_t inj_stride, int32_t* verify_tokens, void* stream);
+
+/* What one drafting call can report besides its tokens, per sequence b and sub-step j (tests and
+   measurement; every pointer is device memory and may be NULL to skip that part):
+     state           float [B][K][d_dim]: the head's input s = rms(x) * norm_f of sub-step j
+     hidden          float [B][K][d_model]: the next sub-step's hidden input W_back . s
+     centroid_scores float [B][K][n_centroids]: the centroid scores C . s (clustered head only)
+     table_scores    float [B][K][vocab], by table row (cluster-major, row_vocab maps a row to
+                     its vocabulary id): only the rows the head scored are written (the members of
+                     the selected clusters, or every row for the full head); the caller fills the
+                     buffer first with a value it can tell apart (NaN)
+     raw_drafts      int32 [B][K]: the drafter's own token of sub-step j, before injection
+   The same kernels run with or without a trace; a trace only adds copies after them. */
+typedef struct {
+  float* state;
+  float* hidden;
+  float* centroid_scores;
+  float* table_scores;
+  int32_t* raw_drafts;
+} specdec_draft_trace;
+
+/* specdec_draft with an optional trace (NULL = none, which is specdec_draft). */
+int specdec_draft_traced(specdec_ctx* ctx, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
+                         const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
+                         int64_t inj_stride, int32_t* verify_tokens,
+                         const specdec_draft_trace* trace, void* stream);
 
 /* Target forward over n_rows rows per sequence: tokens int32 [B][n_rows] (device) at positions
    len[b] .. len[b]+n_rows-1.  Row i attends keys [0, len[b]+i].  Appends the rows' keys and

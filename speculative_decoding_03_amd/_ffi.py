@@ -22,7 +22,7 @@ DW_N1, DW_Q, DW_O, DW_N2, DW_GATE_UP, DW_DOWN, N_DRAFT_TENSORS = range(7)
 
 EXPORTS = [
     "specdec_workspace_bytes", "specdec_kv_elems", "specdec_create", "specdec_destroy",
-    "specdec_draft", "specdec_verify", "specdec_accept", "specdec_kv_commit",
+    "specdec_draft", "specdec_draft_traced", "specdec_verify", "specdec_accept", "specdec_kv_commit",
     "specdec_pack_matrix", "specdec_set_len_bound", "specdec_read_device_error",
     "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
     "specdec_moe_usage_start", "specdec_moe_usage_read",
@@ -48,6 +48,11 @@ class Weights(C.Structure):
     ]
 
 
+class DraftTrace(C.Structure):
+    _fields_ = [("state", C.c_void_p), ("hidden", C.c_void_p), ("centroid_scores", C.c_void_p),
+                ("table_scores", C.c_void_p), ("raw_drafts", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -67,6 +72,8 @@ def load(path: str = LIB_PATH):
         "specdec_create": (C.c_int, [P(Config), P(Weights), vp, vp, vp, vp, vp, sz, vp, P(vp)]),
         "specdec_destroy": (C.c_int, [vp]),
         "specdec_draft": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp]),
+        "specdec_draft_traced": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, i64, vp,
+                                           P(DraftTrace), vp]),
         "specdec_moe_usage_start": (C.c_int, [vp, vp]),
         "specdec_moe_usage_read": (C.c_int, [vp, P(i32), vp]),
         "specdec_verify": (C.c_int, [vp, i32, i32, vp, vp, vp, vp]),

@@ -21,7 +21,9 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
 
-SOURCES = ["gemm.hip", "attention.hip", "misc.hip", "specdec.cpp"]
+# the GEMM's (storage type, M-tile count) instantiations compile in translation units of their own
+SOURCES = ["gemm.hip", *[f"gemm_{t}_m{m}.hip" for t in ("bf16", "f32") for m in (1, 2, 4)],
+           "attention.hip", "misc.hip", "specdec.cpp"]
 LIB = os.path.join(HERE, "libspecdec.so")
 
 
@@ -41,7 +43,7 @@ def build_specdec(verbose: bool = True) -> str:
     os.makedirs(bdir, exist_ok=True)
     objs = []
     jobs = []
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 4, 16, len(SOURCES))) as ex:
         for s in SOURCES:
             src = os.path.join(CSRC, s)
             obj = os.path.join(bdir, s + ".o")

@@ -1,774 +1,25 @@
-// Weight-streaming skinny GEMM for the verify / decode / drafter rows (M <= 64).
-//
-// Y[M][N] = X[M][Kd] . W[N][Kd]^T with W in the packed tile layout: each wave streams whole
-// 1 KB tiles (bf16) with one 16-byte load per lane, so every weight byte is read from HBM
-// exactly once per call and every wave load is fully contiguous.  The rows of X are padded to
-// the 16-row MFMA tile; v_mfma_f32_16x16x32_bf16 (fp32: eight v_mfma_f32_16x16x4f32) does the
-// contraction.
-//
-// Work split: a workgroup of NW waves owns UPW units (a unit = NU consecutive 16-row tiles, or a
-// listed tile); the reduction axis of each unit is split over KW = NW / UPW waves, and the KW
-// partial accumulators are summed through LDS in wave order.  KW depends only on (N, Kd), so a
-// verify row and the same row in a decode step go through the same instruction sequence and
-// come out bit-identical.  There is no communication between workgroups.
-//
-// RMSNorm without a pass of its own: rms(x) * w . W^T = s * ((x * w) . W^T) with the row scale
-// s = 1/sqrt(mean(x^2) + eps).  The producer of the residual x also writes x * w_next in the
-// storage type (w_next = the weight of the norm that reads x next) and per-16-column sums of
-// squares of x; the consumer streams that operand like any other and multiplies its fp32
-// results by s, formed in its epilogue from the sums of squares.  Epilogues: store / residual
-// add, rotary embedding + KV-cache append, SiLU-gated product, per-unit argmax.
+// Entry point of the weight-streaming skinny GEMM (the kernel and its design: gemm_impl.h).
 
-#include <math.h>
-
-#include <type_traits>
-
-#include <hip/hip_ext.h>
-
-#include "common.h"
-#include "kernels.h"
+#include "gemm_impl.h"
 
 namespace specdec {
+namespace gemm_detail {
+// each instantiation lives in its own translation unit (gemm_<type>_m<MT>.hip)
+extern template hipError_t dispatch_epi<bf16_t, 1>(int, int, const GemmArgs&, hipStream_t,
+                                                    const LaunchTiming*);
+extern template hipError_t dispatch_epi<bf16_t, 2>(int, int, const GemmArgs&, hipStream_t,
+                                                    const LaunchTiming*);
+extern template hipError_t dispatch_epi<bf16_t, 4>(int, int, const GemmArgs&, hipStream_t,
+                                                    const LaunchTiming*);
+extern template hipError_t dispatch_epi<float, 1>(int, int, const GemmArgs&, hipStream_t,
+                                                    const LaunchTiming*);
+extern template hipError_t dispatch_epi<float, 2>(int, int, const GemmArgs&, hipStream_t,
+                                                    const LaunchTiming*);
+extern template hipError_t dispatch_epi<float, 4>(int, int, const GemmArgs&, hipStream_t,
+                                                    const LaunchTiming*);
+}  // namespace gemm_detail
 
-namespace {
-
-// One lane's 16 (bf16) or 32 (fp32) bytes of a weight tile.  WC: weights that are read again
-// soon and fit in the last-level cache (the drafter's, re-read every sub-step) use plain loads,
-// which leave them cached; the target's weights, streamed once per step, use non-temporal loads
-// (measured on MI355X: plain loads make the target's gate/up projection 11% slower and the
-// drafter's sub-steps 9% faster).
-template <typename T, bool WC>
-__device__ __forceinline__ void load_w(Frag<T>& f, const T* W, size_t tile, int nkb, int kb,
-                                       int lane) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(
-      W + (tile * (size_t)nkb + (size_t)kb) * TILE_ELEMS + (size_t)lane * LANE_ELEMS);
-  if constexpr (WC) {
-    if constexpr (sizeof(T) == 2) {
-      f.v = *p;
-    } else {
-      f.v[0] = p[0];
-      f.v[1] = p[1];
-    }
-  } else if constexpr (sizeof(T) == 2) {
-    f.v = __builtin_nontemporal_load(p);
-  } else {
-    f.v[0] = __builtin_nontemporal_load(p);
-    f.v[1] = __builtin_nontemporal_load(p + 1);
-  }
-}
-
-// Fragment of k-block J of a quad block q (X in the quad layout, one wave load per block): lane
-// kg*16 + r takes lane kg*16 + 4J + r of its row of 16 (DPP row shift).  Lanes whose row is not
-// 0..3 of k-block J feed only output rows >= 4, which no epilogue stores.
-template <int J, typename T>
-__device__ __forceinline__ void quad_frag(Frag<T>& f, const Frag<T>& q) {
-  if constexpr (J == 0) {
-    f = q;
-  } else {
-    constexpr int ctrl = 0x100 + 4 * J;  // row_shl:4J
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f.v[i] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)q.v[i], ctrl, 0xF, 0xF, true);
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          f.v[h][i] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)q.v[h][i], ctrl, 0xF, 0xF, true);
-    }
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void quad_frag_rt(Frag<T>& f, const Frag<T>& q, int j) {
-  switch (j) {
-    case 0: quad_frag<0>(f, q); break;
-    case 1: quad_frag<1>(f, q); break;
-    case 2: quad_frag<2>(f, q); break;
-    default: quad_frag<3>(f, q); break;
-  }
-}
-
-
-// Row-scale partial sums of up to 4 rows with n_yssq <= 64 * RS_J, loaded into registers after the
-// main loop and before the split-K reduction, so that their latency overlaps its barriers.
-constexpr int RS_J = 5;
-struct RowScaleLoads {
-  float v[RS_J][4];
-  bool fast;
-};
-
-// Local row of element v of M-tile mt in a lane.  The MFMA leaves rows (lane/16)*4 + v of
-// column lane%16; with a single M-tile of at most 4 rows ("narrow") all rows sit in lanes 0-15,
-// so the epilogue first moves row r to lanes 16r..16r+15 and then handles element 0 only, with
-// every lane busy.  Elements that hold no row get an index past any M.
-__device__ __forceinline__ int local_row(bool narrow, int mt, int v, int lane) {
-  return narrow ? (v == 0 ? (lane >> 4) : (1 << 20)) : mt * 16 + ((lane >> 4) << 2) + v;
-}
-
-// Epilogue operands that do not depend on the products, read before the main loop so that their
-// latency hides behind it: the norm weight and current value of each stored element (EPI_STORE),
-// the rotary inverse frequency and the row positions (EPI_ROPE).
-template <int MT, int NU> struct EpiPre {
-  float wn[NU];
-  float res[NU][MT][4];
-  float2 cs[NU][MT][4];  // rotary (cos, sin) of the lane's pair at each row's position
-  int pos[MT][4];
-};
-
-template <int MT, int NU, int EPI>
-__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int lane,
-                                             EpiPre<MT, NU>& pre) {
-  const int c16 = lane & 15;
-  const bool narrow = MT == 1 && a.M <= 4;
-  if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-    for (int t = 0; t < NU; ++t) {
-      const int col = min(tile0 + t, a.n_tiles - 1) * TILE_N + c16;
-      pre.wn[t] = a.xw_out ? a.xw_norm[col] : 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = local_row(narrow, mt, v, lane);
-          pre.res[t][mt][v] = (a.accumulate && m < a.M) ? a.out[(size_t)m * a.ldo + col] : 0.f;
-        }
-    }
-  } else if constexpr (EPI == EPI_ROPE) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = local_row(narrow, mt, v, lane);
-        const int b = m < a.M ? m / a.rows_per_seq : 0;
-        pre.pos[mt][v] = a.len[b] + (m - b * a.rows_per_seq) + a.pos_off;
-      }
-    const int half = a.hd >> 1;
-#pragma unroll
-    for (int t = 0; t < NU; ++t) {
-      const int col = min(tile0 + t, a.n_tiles - 1) * TILE_N + c16;
-      const int i = (col % a.hd) >> 1;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          // a position outside the cache reads row 0 or the last (the epilogue flags it)
-          const int pc = min(max(pre.pos[mt][v], 0), a.max_ctx - 1);
-          pre.cs[t][mt][v] = a.rope_cs[(size_t)pc * half + i];
-        }
-    }
-  }
-}
-
-__device__ __forceinline__ void row_scale_load(const GemmArgs& a, int lane, RowScaleLoads& rs) {
-  rs.fast = a.yssq && a.M <= 4 && a.n_yssq <= WAVE * RS_J;
-  if (!rs.fast) return;
-#pragma unroll
-  for (int j = 0; j < RS_J; ++j) {
-    const int t = lane + WAVE * j;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rs.v[j][r] = (t < a.n_yssq && r < a.M) ? a.yssq[(size_t)t * a.M + r] : 0.f;
-  }
-}
-
-// Row scales 1/sqrt(sum_t yssq[t][r] / yscale_n + eps) for the rows this lane holds (r = the X
-// row a local row reads: xr[mt] holds it for local row mt*16 + lane%16).  The sum runs
-// lane-strided then through a fixed butterfly, identically for every caller.
-template <int MT>
-__device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const int (&xr)[MT],
-                                           const RowScaleLoads& rs, float (&sc)[MT][4]) {
-  float mine = 1.f;
-  if (rs.fast) {
-    // per row the partials are added in ascending order, as below
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float s = 0.f;
-#pragma unroll
-      for (int j = 0; j < RS_J; ++j) s += rs.v[j][r];
-      if (r < a.M) {
-        const float w = wave_sum(s);
-        if (lane == r) mine = 1.0f / sqrtf(w / (float)a.yscale_n + a.eps);
-      }
-    }
-  }
-  // otherwise up to 16 rows at a time, all their loads independent
-  for (int m0 = 0; !rs.fast && m0 < a.M; m0 += 16) {
-    const int nr = min(16, a.M - m0);
-    float s[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    for (int t = lane; t < a.n_yssq; t += WAVE) {
-      const float* p = a.yssq + (size_t)t * a.M + m0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (r < nr) s[r] += p[r];
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < nr) {
-        const float v = wave_sum(s[r]);
-        if (lane == m0 + r) mine = 1.0f / sqrtf(v / (float)a.yscale_n + a.eps);
-      }
-    }
-  }
-  const bool narrow = MT == 1 && a.M <= 4;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = __shfl(xr[mt], local_row(narrow, mt, v, lane) & 15, WAVE);
-      sc[mt][v] = __shfl(mine, r < 0 ? 0 : (r & 63), WAVE);
-    }
-}
-
-template <typename T, int MT, int NU, int EPI>
-__device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
-                                         int tile0, int grp, const int (&xr)[MT],
-                                         const RowScaleLoads& rs, const EpiPre<MT, NU>& pre, int lane) {
-  const int c16 = lane & 15;
-  const bool narrow = MT == 1 && a.M <= 4;
-  if (narrow) {
-    // row r of column c moves from element r of lane c to element 0 of lane 16r + c
-    const int src = lane & 15, r = lane >> 4;
-#pragma unroll
-    for (int t = 0; t < NU; ++t) {
-      const float x0 = __shfl(acc[t][0][0], src, WAVE), x1 = __shfl(acc[t][0][1], src, WAVE);
-      const float x2 = __shfl(acc[t][0][2], src, WAVE), x3 = __shfl(acc[t][0][3], src, WAVE);
-      acc[t][0][0] = r == 0 ? x0 : (r == 1 ? x1 : (r == 2 ? x2 : x3));
-    }
-  }
-  if (a.yssq) {
-    float sc[MT][4];
-    row_scales<MT>(a, lane, xr, rs, sc);
-#pragma unroll
-    for (int t = 0; t < NU; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[t][mt][v] *= sc[mt][v];
-  }
-  if constexpr (EPI == EPI_STORE) {
-    // addend: a fixed-order sum of add_n row slices, read JB slices at a time for all of the
-    // lane's elements (at most 16 values) so that the loads are in flight together
-    constexpr int JB = 16 / (NU * MT * 4) > 1 ? 16 / (NU * MT * 4) : 1;
-    float adds[NU][MT][4];
-    if (a.addend) {
-#pragma unroll
-      for (int t = 0; t < NU; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) adds[t][mt][v] = 0.f;
-      for (int k0 = 0; k0 < a.add_n; k0 += JB) {
-        float ld[JB][NU][MT][4];
-#pragma unroll
-        for (int j = 0; j < JB; ++j)
-#pragma unroll
-          for (int t = 0; t < NU; ++t)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int m = min(local_row(narrow, mt, v, lane), a.M - 1);
-                const int col = min(tile0 + t, a.n_tiles - 1) * TILE_N + c16;
-                const int k = min(k0 + j, a.add_n - 1);
-                ld[j][t][mt][v] = a.addend[((size_t)m * a.add_n + k) * a.ldo + col];
-              }
-#pragma unroll
-        for (int j = 0; j < JB; ++j)
-          if (k0 + j < a.add_n) {
-#pragma unroll
-            for (int t = 0; t < NU; ++t)
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                  adds[t][mt][v] = k0 + j == 0 ? ld[j][t][mt][v] : adds[t][mt][v] + ld[j][t][mt][v];
-          }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < NU; ++t) {
-      const int tile = tile0 + t;
-      if (tile >= a.n_tiles) break;  // wave-uniform
-      const int col = tile * TILE_N + c16;
-      const float wn = pre.wn[t];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (narrow && v > 0) continue;  // uniform
-          const int m = local_row(narrow, mt, v, lane);
-          float sq = 0.f;
-          if (m < a.M) {
-            float* o = a.out + (size_t)m * a.ldo + col;
-            float y = acc[t][mt][v];
-            if (a.addend) y = adds[t][mt][v] + y;
-            if (a.accumulate) y = pre.res[t][mt][v] + y;
-            *o = y;
-            sq = y * y;
-            if (a.xw_out)
-              Elem<T>::store(reinterpret_cast<T*>(a.xw_out) + x_offset(a.out_qx, m, col, a.ldo), y * wn);
-          }
-          if (a.ssq) {
-            const float r = sum16(sq);
-            if (c16 == 0 && m < a.M) a.ssq[(size_t)tile * a.M + m] = r;
-          }
-        }
-    }
-  } else if constexpr (EPI == EPI_ROPE) {
-#pragma unroll
-    for (int t = 0; t < NU; ++t) {
-      const int tile = tile0 + t;
-      if (tile >= a.n_tiles) break;  // wave-uniform
-      const int col = tile * TILE_N + c16;
-      const int hh = col / a.hd;
-      const int p = col - hh * a.hd;
-      const int i = p >> 1;
-      const int second = p & 1;
-      const int dim = i + second * (a.hd >> 1);
-      const bool rot = hh < a.hq + a.hkv;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (narrow && v > 0) continue;  // uniform
-          const int m = local_row(narrow, mt, v, lane);
-          const float val = acc[t][mt][v];
-          const float partner = dpp_f32<DPP_XOR1>(val);  // the other element of the rotary pair
-          if (m < a.M) {
-            const int b = m / a.rows_per_seq;
-            const int pos = pre.pos[mt][v];
-            float y = val;
-            if (rot) {
-              const float cs = pre.cs[t][mt][v].x, sn = pre.cs[t][mt][v].y;
-              const float x1 = second ? partner : val;
-              const float x2 = second ? val : partner;
-              y = second ? (x2 * cs + x1 * sn) : (x1 * cs - x2 * sn);
-            }
-            if (hh < a.hq) {
-              Elem<T>::store(reinterpret_cast<T*>(a.qout) + ((size_t)m * a.hq + hh) * a.hd + dim, y);
-            } else if (pos >= a.max_ctx || pos < 0) {
-              raise_error(a.err, ERRBIT_CAPACITY);
-            } else {
-              // K is stored [pos][hd], V transposed [hd][pos]
-              const bool isk = hh < a.hq + a.hkv;
-              const int g = isk ? hh - a.hq : hh - a.hq - a.hkv;
-              T* cache = reinterpret_cast<T*>(isk ? a.kcache : a.vcache) + (size_t)b * a.cache_b_stride;
-              const size_t off = isk ? ((size_t)g * a.max_ctx + pos) * a.hd + dim
-                                     : ((size_t)g * a.hd + dim) * a.max_ctx + pos;
-              Elem<T>::store(cache + off, y);
-            }
-          }
-        }
-    }
-  } else if constexpr (EPI == EPI_SILU_G || EPI == EPI_STORE_G) {
-    const int lt = tile0 - grp * a.tiles_per_group;  // tile within the group's matrix
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (narrow && v > 0) continue;  // uniform
-        const int m = local_row(narrow, mt, v, lane);
-        if (m >= a.M) continue;
-        const int orow = a.orow_map[(size_t)grp * a.M + m];
-        if (orow < 0) continue;
-        if constexpr (EPI == EPI_SILU_G) {
-          const float g = acc[0][mt][v];
-          const float up = acc[1][mt][v];
-          const float h = g / (1.0f + expf(-g)) * up;
-          Elem<T>::store(reinterpret_cast<T*>(a.hout) + (size_t)orow * a.ldh + (lt >> 1) * TILE_N + c16, h);
-        } else {
-          a.out[(size_t)orow * a.ldo + lt * TILE_N + c16] =
-              acc[0][mt][v] * a.orow_wt[(size_t)grp * a.M + m];
-        }
-      }
-  } else if constexpr (EPI == EPI_SILU) {
-    const int f = (tile0 >> 1) * TILE_N + c16;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (narrow && v > 0) continue;  // uniform
-        const int m = local_row(narrow, mt, v, lane);
-        if (m < a.M) {
-          const float g = acc[0][mt][v];
-          const float up = acc[1][mt][v];
-          const float h = g / (1.0f + expf(-g)) * up;
-          Elem<T>::store(reinterpret_cast<T*>(a.hout) + x_offset(a.out_qx, m, f, a.ldh), h);
-        }
-      }
-  } else {  // EPI_ARGMAX
-    const int keep_row = a.unit_row ? a.unit_row[u] : -1;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (narrow && v > 0) continue;  // uniform
-        const int m = local_row(narrow, mt, v, lane);
-        float best = -INFINITY;
-        int bidx = 0x7fffffff;
-        bool nan = false;
-#pragma unroll
-        for (int t = 0; t < NU; ++t) {
-          const int tile = tile0 + t;
-          if (tile < a.n_tiles) {
-            const int col = tile * TILE_N + c16;
-            const float y = acc[t][mt][v];
-            nan |= (y != y);
-            const int idx = a.idx_map ? a.idx_map[col] : col;
-            argmax_combine(best, bidx, y, idx);
-            if (a.logits && m < a.M) a.logits[(size_t)m * a.ld_logits + col] = y;
-          }
-        }
-        argmax16(best, bidx);
-        if (nan && m < a.M) raise_error(a.err, ERRBIT_NAN);
-        if (c16 == 0 && m < a.M && (keep_row < 0 || keep_row == m)) {
-          // listed units belong to one row each and are stored by unit index
-          const size_t slot = a.unit_row ? (size_t)u : (size_t)m * a.ld_amax + u;
-          a.amax_val[slot] = best;
-          a.amax_idx[slot] = bidx;
-        }
-      }
-  }
-}
-
-// U: k-blocks per register stage (two stages are in flight) for NU = 1 / 2 / 4 tiles per unit.
-#ifndef SPECDEC_GEMM_U1
-#define SPECDEC_GEMM_U1 4
-#endif
-#ifndef SPECDEC_GEMM_U2
-#define SPECDEC_GEMM_U2 2
-#endif
-#ifndef SPECDEC_GEMM_U4
-#define SPECDEC_GEMM_U4 2
-#endif
-// Register stages of the quad-layout main loop (S - 1 batches in flight while one multiplies),
-// for NU = 1 / 2 / 4 tiles per unit.
-#ifndef SPECDEC_QSTAGES1
-#define SPECDEC_QSTAGES1 2
-#endif
-#ifndef SPECDEC_QSTAGES2
-#define SPECDEC_QSTAGES2 2
-#endif
-#ifndef SPECDEC_QSTAGES4
-#define SPECDEC_QSTAGES4 2
-#endif
-template <int NU> struct QuadStages {
-  static constexpr int S = NU >= 4 ? SPECDEC_QSTAGES4 : (NU == 2 ? SPECDEC_QSTAGES2 : SPECDEC_QSTAGES1);
-};
-
-template <int NU, int MT> struct Unroll {
-  static constexpr int base = NU >= 4 ? SPECDEC_GEMM_U4 : (NU == 2 ? SPECDEC_GEMM_U2 : SPECDEC_GEMM_U1);
-  static constexpr int U = base / MT > 1 ? base / MT : 1;
-};
-
-template <typename T, int MT, int NU, int EPI, int NW, bool WC>
-__global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
-  __shared__ f32x4 red[NW * NU * 64];
-  const int lane = threadIdx.x & (WAVE - 1);
-  // wave index, wave-uniform (readfirstlane tells the compiler, so the split bounds and the
-  // main loop's trip count live in scalar registers and its branches are uniform)
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr bool GROUPED = EPI == EPI_SILU_G || EPI == EPI_STORE_G;
-  const int KW = a.KW;
-  const int ks = wid % KW;
-  const int u = blockIdx.x * (NW / KW) + wid / KW;
-  int n_units = a.n_units;
-  if constexpr (GROUPED) n_units = min(n_units, a.n_groups_dev[0] * a.units_per_group);
-  else if (a.n_units_dev) n_units = min(*a.n_units_dev, n_units);
-  const bool active = u < n_units;
-  int tile0 = 0, grp = 0;
-  if (active) {
-    if constexpr (GROUPED) {
-      const int gi = u / a.units_per_group;
-      grp = a.group_list[gi];
-      tile0 = grp * a.tiles_per_group + (u - gi * a.units_per_group) * NU;
-    } else {
-      tile0 = a.unit_tile ? a.unit_tile[u] : u * NU;
-    }
-  }
-  // X row read by local row mt*16 + lane%16 (-1: none)
-  int xr[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + (lane & 15);
-    if constexpr (GROUPED) xr[mt] = (active && m < a.M) ? a.xrow_map[(size_t)grp * a.M + m] : -1;
-    else xr[mt] = m < a.M ? m : -1;
-  }
-  const int kb0 = ks * a.kb_per_split;
-  const int kb1 = min(a.nkb, kb0 + a.kb_per_split);
-  const T* W = reinterpret_cast<const T*>(a.W);
-
-
-  f32x4 acc[NU][MT];
-#pragma unroll
-  for (int t = 0; t < NU; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // epilogue operands and row-scale partials, requested before the main loop (the wave that
-  // finishes each unit is the ks == 0 one)
-  EpiPre<MT, NU> pre;
-  RowScaleLoads rs;
-  rs.fast = false;
-  if (active && ks == 0) {
-    epi_prefetch<MT, NU, EPI>(a, tile0, lane, pre);
-    row_scale_load(a, lane, rs);
-  }
-
-  bool quad_done = false;
-  if constexpr (MT == 1 && !GROUPED) {
-    if (active && a.x_qx) {
-      // X in the quad layout (at most 4 rows): one wave load per four k-blocks, shared by the
-      // batch's k-blocks through DPP row shifts.  kb0 is a multiple of 4.
-      // Loads are branch-free (a tile past n_tiles reads the last tile; its sums are never
-      // stored), so the compiler's wait counts are exact and S - 1 batches stay in flight.
-      constexpr int U = NU >= 4 ? 2 : 4;  // k-blocks per batch: a whole or half quad block
-      constexpr int S = QuadStages<NU>::S;  // register stages, used as a ring
-      Frag<T> w[S][U][NU];
-      Frag<T> xq[S];
-      const T* Xq = reinterpret_cast<const T*>(a.X) + (size_t)lane * 8;
-      size_t wt_tile[NU];
-#pragma unroll
-      for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);
-      auto load_batch = [&](int st, int kbase) {
-#pragma unroll
-        for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-          for (int t = 0; t < NU; ++t) load_w<T, WC>(w[st][uu][t], W, wt_tile[t], a.nkb, kbase + uu, lane);
-        load_frag<T>(xq[st], Xq + (size_t)(kbase >> 2) * 512);
-      };
-      auto mul_at = [&](auto j0c, int st) {
-        constexpr int J0 = decltype(j0c)::value;
-#pragma unroll
-        for (int uu = 0; uu < U; ++uu) {
-          Frag<T> xf;
-          if constexpr (J0 + 0 == 0) {
-            if (uu == 0) quad_frag<0>(xf, xq[st]);
-            else if (uu == 1) quad_frag<1>(xf, xq[st]);
-            else if (uu == 2) quad_frag<2>(xf, xq[st]);
-            else quad_frag<3>(xf, xq[st]);
-          } else {
-            if (uu == 0) quad_frag<2>(xf, xq[st]);
-            else quad_frag<3>(xf, xq[st]);
-          }
-#pragma unroll
-          for (int t = 0; t < NU; ++t) acc[t][0] = mma<T>(xf, w[st][uu][t], acc[t][0]);
-        }
-      };
-      auto mul_batch = [&](int st, int kbase) {
-        if (U == 4 || (kbase & 2) == 0) mul_at(std::integral_constant<int, 0>{}, st);
-        else mul_at(std::integral_constant<int, 2>{}, st);
-      };
-      const int nb = (kb1 - kb0) / U;
-      if (nb > 0) {
-        // Batch i of this wave sits in stage i % S.  Whole groups of S batches run in the loop,
-        // each step prefetching S - 1 batches ahead (past the last batch it reads the last one
-        // again; those stages are never multiplied); the r < S batches left over are already in
-        // flight when the loop ends.  No step leaves the pipeline early, so every prefetch is
-        // used on every path and stays where it is issued.
-        auto kb_at = [&](int i) { return kb0 + i * U; };
-        auto kb_of = [&](int i) { return kb_at(min(i, nb - 1)); };
-#pragma unroll
-        for (int st = 0; st < S - 1; ++st) load_batch(st, kb_of(st));
-        const int G = nb / S;
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-          for (int st = 0; st < S; ++st) {
-            // the prefetch is issued before this step's products wait for their stage
-            load_batch((st + S - 1) % S, kb_of(g * S + st + S - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            mul_batch(st, kb_at(g * S + st));
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        const int r = nb - G * S;
-#pragma unroll
-        for (int st = 0; st < S - 1; ++st)
-          if (st < r) mul_batch(st, kb_at(G * S + st));
-      }
-      for (int kb = kb0 + nb * U; kb < kb1; ++kb) {
-        Frag<T> wt[NU], q, xf;
-#pragma unroll
-        for (int t = 0; t < NU; ++t) load_w<T, WC>(wt[t], W, wt_tile[t], a.nkb, kb, lane);
-        load_frag<T>(q, Xq + (size_t)(kb >> 2) * 512);
-        quad_frag_rt<T>(xf, q, kb & 3);
-#pragma unroll
-        for (int t = 0; t < NU; ++t) acc[t][0] = mma<T>(xf, wt[t], acc[t][0]);
-      }
-      quad_done = true;
-    }
-  }
-  if (active && !quad_done) {
-    // Row-major X: the same ring of register stages as above.  Loads are branch-free: a tile past
-    // the matrix reads the last one (its sums are never stored) and a row that does not exist reads
-    // row 0, zeroed by a per-lane select before its product.  Only the leading M-tiles that hold a
-    // row run (a routed expert gathers a few of the call's rows: its later M-tiles stay zero and
-    // their rows are never stored).
-    auto row_major = [&](auto mtc) {
-      constexpr int ML = decltype(mtc)::value;
-      constexpr int U = Unroll<NU, MT>::U;
-      constexpr int S = 2;
-      Frag<T> w[S][U][NU];
-      Frag<T> x[S][U][ML];
-      size_t wt_tile[NU];
-#pragma unroll
-      for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);
-      int xrow[ML];
-      bool xok[ML];
-#pragma unroll
-      for (int mt = 0; mt < ML; ++mt) {
-        xok[mt] = xr[mt] >= 0;
-        xrow[mt] = xok[mt] ? xr[mt] : 0;
-      }
-      const T* Xb = reinterpret_cast<const T*>(a.X);
-      const int kl = (lane >> 4) << 3;
-      auto load_batch = [&](int st, int kbase) {
-#pragma unroll
-        for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-          for (int t = 0; t < NU; ++t) load_w<T, WC>(w[st][uu][t], W, wt_tile[t], a.nkb, kbase + uu, lane);
-#pragma unroll
-        for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-          for (int mt = 0; mt < ML; ++mt)
-            load_frag<T>(x[st][uu][mt], Xb + x_offset(a.x_qx, xrow[mt], (kbase + uu) * TILE_K + kl, a.ldx));
-      };
-      auto mul_batch = [&](int st) {
-#pragma unroll
-        for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-          for (int mt = 0; mt < ML; ++mt) {
-            Frag<T> xf = x[st][uu][mt];
-            if (!xok[mt]) zero_frag(xf);
-#pragma unroll
-            for (int t = 0; t < NU; ++t) acc[t][mt] = mma<T>(xf, w[st][uu][t], acc[t][mt]);
-          }
-      };
-      const int nb = (kb1 - kb0) / U;  // whole batches
-      if (nb > 0) {
-        auto kb_of = [&](int i) { return kb0 + min(i, nb - 1) * U; };
-#pragma unroll
-        for (int st = 0; st < S - 1; ++st) load_batch(st, kb_of(st));
-        const int G = nb / S;
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-          for (int st = 0; st < S; ++st) {
-            load_batch((st + S - 1) % S, kb_of(g * S + st + S - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            mul_batch(st);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        const int r = nb - G * S;
-#pragma unroll
-        for (int st = 0; st < S - 1; ++st)
-          if (st < r) mul_batch(st);
-      }
-      for (int kb = kb0 + nb * U; kb < kb1; ++kb) {
-        Frag<T> wt[NU];
-        Frag<T> xt[ML];
-#pragma unroll
-        for (int t = 0; t < NU; ++t) load_w<T, WC>(wt[t], W, wt_tile[t], a.nkb, kb, lane);
-#pragma unroll
-        for (int mt = 0; mt < ML; ++mt) {
-          load_frag<T>(xt[mt], Xb + x_offset(a.x_qx, xrow[mt], kb * TILE_K + kl, a.ldx));
-          if (!xok[mt]) zero_frag(xt[mt]);
-        }
-#pragma unroll
-        for (int t = 0; t < NU; ++t)
-#pragma unroll
-          for (int mt = 0; mt < ML; ++mt) acc[t][mt] = mma<T>(xt[mt], wt[t], acc[t][mt]);
-      }
-    };
-    bool later_rows = false;  // does any M-tile after the first hold a row (wave-uniform)?
-#pragma unroll
-    for (int mt = 1; mt < MT; ++mt) later_rows |= __ballot(xr[mt] >= 0) != 0ull;
-    if (MT == 1 || !later_rows) row_major(std::integral_constant<int, 1>{});
-    else row_major(std::integral_constant<int, MT>{});
-  }
-
-  if (KW > 1) {
-    // sum the KW partial accumulators of each unit in wave order, one M-tile at a time
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (ks != 0) {
-#pragma unroll
-        for (int t = 0; t < NU; ++t) red[(wid * NU + t) * 64 + lane] = acc[t][mt];
-      }
-      __syncthreads();
-      if (ks == 0) {
-#pragma unroll
-        for (int t = 0; t < NU; ++t) {
-          f32x4 s = acc[t][mt];
-          for (int k2 = 1; k2 < KW; ++k2) s += red[((wid + k2) * NU + t) * 64 + lane];
-          acc[t][mt] = s;
-        }
-      }
-      __syncthreads();
-    }
-    if (ks != 0) return;
-  }
-  if (!active) return;
-  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, rs, pre, lane);
-}
-
-template <typename T, int MT, int NU, int EPI, int NW, bool WC>
-hipError_t launch_wc(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
-  const int upw = NW / a.KW;
-  dim3 grid((a.n_units + upw - 1) / upw), block(NW * 64);
-  if (tm)
-    hipExtLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW, WC>), grid, block, 0, st, tm->start,
-                          tm->stop, 0, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW, WC>), grid, block, 0, st, a);
-  return hipGetLastError();
-}
-
-template <typename T, int MT, int NU, int EPI, int NW>
-hipError_t launch_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
-  return a.w_cached ? launch_wc<T, MT, NU, EPI, NW, true>(a, st, tm)
-                    : launch_wc<T, MT, NU, EPI, NW, false>(a, st, tm);
-}
-
-template <typename T, int MT, int NU, int EPI>
-hipError_t launch_nw(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
-  if constexpr (NU < 4) {
-    if (a.NW == 16) return launch_t<T, MT, NU, EPI, 16>(a, st, tm);
-  }
-  if (a.NW == 8) return launch_t<T, MT, NU, EPI, 8>(a, st, tm);
-  if (a.NW == 4) return launch_t<T, MT, NU, EPI, 4>(a, st, tm);
-  return hipErrorInvalidValue;
-}
-
-template <typename T, int MT>
-hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st,
-                       const LaunchTiming* tm) {
-  if (epi == EPI_STORE && NU == 1) return launch_nw<T, MT, 1, EPI_STORE>(a, st, tm);
-  if (epi == EPI_STORE && NU == 2) return launch_nw<T, MT, 2, EPI_STORE>(a, st, tm);
-  if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE>(a, st, tm);
-  if (epi == EPI_ROPE && NU == 2) return launch_nw<T, MT, 2, EPI_ROPE>(a, st, tm);
-  if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU>(a, st, tm);
-  if (epi == EPI_SILU_G && NU == 2) return launch_nw<T, MT, 2, EPI_SILU_G>(a, st, tm);
-  if (epi == EPI_STORE_G && NU == 1) return launch_nw<T, MT, 1, EPI_STORE_G>(a, st, tm);
-  if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX>(a, st, tm);
-  return hipErrorInvalidValue;
-}
-
-template <typename T>
-hipError_t dispatch_mt(int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
-                       const LaunchTiming* tm) {
-  switch (MT) {
-    case 1: return dispatch_epi<T, 1>(NU, epi, a, st, tm);
-    case 2: return dispatch_epi<T, 2>(NU, epi, a, st, tm);
-    case 4: return dispatch_epi<T, 4>(NU, epi, a, st, tm);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
+using gemm_detail::dispatch_mt;
 
 hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
                        const LaunchTiming* tm) {

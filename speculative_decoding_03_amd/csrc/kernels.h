@@ -164,6 +164,13 @@ hipError_t launch_draft_finalize(const float* amax_val, const int* amax_idx, int
                                  const int* len,
                                  const int* inject, int inj_stride, int* drafts, int* dtok,
                                  const int* cur_tok, int* vtok, int* err, hipStream_t st);
+// Drafter trace helpers (tests and measurement): s[b] = x[b] * rs(b) * norm into out[b*ld_out],
+// rs(b) = 1/sqrt(sum_t ssq[t][b] / n + eps) over n/16 tiles (the row scale the head's epilogue
+// forms); and a strided copy of rows of 32-bit words.
+hipError_t launch_trace_state(const float* x, const float* ssq, int B, int n, const float* norm,
+                              float eps, float* out, int ld_out, hipStream_t st);
+hipError_t launch_copy_rows(void* dst, int ld_dst, const void* src, int ld_src, int rows, int cols,
+                            hipStream_t st);
 hipError_t launch_pack(int dtype, const void* src, void* dst, int N, int Kd, int kind, int hd,
                        int split_rows, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int v, size_t n, hipStream_t st);

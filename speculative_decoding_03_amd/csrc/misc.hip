@@ -465,6 +465,28 @@ __global__ void pack_kernel(const T* src, T* dst, int N, int Kd, int kind, int h
   }
 }
 
+__global__ void __launch_bounds__(256) trace_state_kernel(const float* x, const float* ssq, int B,
+                                                          int n, const float* norm, float eps,
+                                                          float* out, int ld_out) {
+  __shared__ float rs;
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) {
+    float s = 0.f;
+    for (int t = 0; t < n / TILE_N; ++t) s += ssq[(size_t)t * B + b];
+    rs = 1.0f / sqrtf(s / (float)n + eps);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < n; k += blockDim.x)
+    out[(size_t)b * ld_out + k] = x[(size_t)b * n + k] * rs * norm[k];
+}
+
+__global__ void copy_rows_kernel(uint32_t* dst, int ld_dst, const uint32_t* src, int ld_src,
+                                 int cols) {
+  const int r = blockIdx.y;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < cols; c += gridDim.x * blockDim.x)
+    dst[(size_t)r * ld_dst + c] = src[(size_t)r * ld_src + c];
+}
+
 __global__ void fill_i32_kernel(int* p, int v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -585,6 +607,23 @@ hipError_t launch_rope_table(float2* t, int hd, int max_ctx, float theta, hipStr
   const size_t n = (size_t)max_ctx * (hd / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, t, hd,
                      max_ctx, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_trace_state(const float* x, const float* ssq, int B, int n, const float* norm,
+                              float eps, float* out, int ld_out, hipStream_t st) {
+  if (B < 1 || n % TILE_N) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(trace_state_kernel, dim3(B), dim3(256), 0, st, x, ssq, B, n, norm, eps, out,
+                     ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(void* dst, int ld_dst, const void* src, int ld_src, int rows, int cols,
+                            hipStream_t st) {
+  if (rows < 1 || cols < 1) return hipSuccess;
+  const int gx = (cols + 255) / 256 < 64 ? (cols + 255) / 256 : 64;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(gx, rows), dim3(256), 0, st, (uint32_t*)dst, ld_dst,
+                     (const uint32_t*)src, ld_src, cols);
   return hipGetLastError();
 }
 

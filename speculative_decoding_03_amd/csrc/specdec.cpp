@@ -19,20 +19,14 @@ using namespace specdec;
 
 namespace {
 
-#ifndef SPECDEC_TARGET_WAVES
-#define SPECDEC_TARGET_WAVES 2048
-#endif
-#ifndef SPECDEC_MIN_KB_PER_WAVE
-#define SPECDEC_MIN_KB_PER_WAVE 8
-#endif
 constexpr size_t ALIGN = 256;
-constexpr int TARGET_WAVES = SPECDEC_TARGET_WAVES;        // waves per projection launch
-constexpr int MIN_KB_PER_WAVE = SPECDEC_MIN_KB_PER_WAVE;
+constexpr int TARGET_WAVES = 2048;   // waves per projection launch
+constexpr int MIN_KB_PER_WAVE = 8;   // k-blocks each wave streams at least
 // Tiles per unit of the target's q/k/v, o and down projections: two when the projection has at
 // least 256 tiles (one activation load then serves twice the weight bytes), else one, which keeps
 // more workgroups on the CUs (measured on MI355X: two at the 31B shapes, one at the E2B, E4B and
 // MoE model widths).
-int store_nu(int N) { return N / 16 >= 256 ? 2 : 1; }  // k-blocks each wave streams at least
+int store_nu(int N) { return N / 16 >= 256 ? 2 : 1; }
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -46,11 +40,6 @@ int pow2_floor(int v) {
   int p = 1;
   while (p * 2 <= v) p *= 2;
   return p;
-}
-
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return s ? atoi(s) : dflt;
 }
 
 // One projection: packed weights plus its fixed work split (a function of N and Kd only).
@@ -68,17 +57,11 @@ struct Gemm {
 int split_for(int units, int nkb, int NU) {
   int KW = NU >= 4 ? 8 : cdiv(TARGET_WAVES, units);
   KW = std::min({KW, 16, std::max(1, nkb / MIN_KB_PER_WAVE)});
-  return pow2_floor(std::max(1, std::min(KW, env_int("SPECDEC_MAX_KW", 16))));
+  return pow2_floor(std::max(1, KW));
 }
 
-#ifndef SPECDEC_NW_POLICY
-#define SPECDEC_NW_POLICY 0
-#endif
 // Waves per workgroup for a split-K factor KW (a workgroup holds NW / KW whole units).
-int waves_for(int KW) {
-  if (SPECDEC_NW_POLICY == 1) return std::max(KW, 4);
-  return KW == 16 ? 16 : 8;
-}
+int waves_for(int KW) { return KW == 16 ? 16 : 8; }
 
 Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true, bool gated = false) {
   Gemm g;
@@ -662,14 +645,23 @@ int specdec_kv_commit(specdec_ctx* x, int32_t B, const int32_t* n_commit, void* 
 int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
                   const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
                   int64_t inj_stride, int32_t* verify_tokens, void* stream) {
+  return specdec_draft_traced(x, B, K, head_mode, k_c, cur_tok, drafts, inject, inj_stride,
+                              verify_tokens, nullptr, stream);
+}
+
+int specdec_draft_traced(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
+                         const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
+                         int64_t inj_stride, int32_t* verify_tokens,
+                         const specdec_draft_trace* trace, void* stream) {
   if (!x || !cur_tok || !drafts) return SPECDEC_E_INVAL;
   const specdec_config& c = x->cfg;
   if (B < 1 || B > c.max_batch || K < 1 || K > c.max_draft) return SPECDEC_E_INVAL;
   if (head_mode != SPECDEC_HEAD_CLUSTERED && head_mode != SPECDEC_HEAD_FULL) return SPECDEC_E_INVAL;
   if (head_mode == SPECDEC_HEAD_CLUSTERED && (k_c < 1 || k_c > c.n_centroids)) return SPECDEC_E_INVAL;
   if (inject && (inj_stride < 1 || inj_stride > 0x7fffffff)) return SPECDEC_E_INVAL;
+  // sub-step j queries at position len + j - 1: the last one, len + K - 1, must be a cache slot
   for (int b = 0; b < B; ++b)
-    if (x->len_hi[b] > c.max_ctx) return SPECDEC_E_CAPACITY;
+    if (x->len_hi[b] + K > c.max_ctx) return SPECDEC_E_CAPACITY;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int dt = dt_of(x);
   const int d = c.d_model, Dd = c.d_dim, qd = c.n_q_heads * c.head_dim;
@@ -745,6 +737,14 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
       a.ldo = d;
       if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
     }
+    if (trace && trace->state)
+      HIP_TRY(launch_trace_state(xd, sd, B, Dd, x->w.norm_f, c.rms_eps, trace->state + (size_t)(j - 1) * Dd,
+                                 K * Dd, st));
+    if (trace && trace->hidden)
+      HIP_TRY(launch_copy_rows(trace->hidden + (size_t)(j - 1) * d, K * d, hnext, d, B, d, st));
+    // the head's scores of sub-step j land at trace row b*K + j - 1, by table row
+    float* tscores = trace && trace->table_scores ? trace->table_scores + (size_t)(j - 1) * c.vocab : nullptr;
+    const int ld_tscores = K * c.vocab;
     int parts_per_seq, seq_off, ld;
     {
       ProfScope ps(x, 6, st);
@@ -755,6 +755,8 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         a.amax_idx = at<int>(x, x->lay.d_amax_i);
         a.ld_amax = x->dm.parts;
         a.idx_map = x->w.row_vocab;
+        a.logits = tscores;
+        a.ld_logits = ld_tscores;
         HIP_TRY(launch_gemm(dt, mt_for(B), 4, EPI_ARGMAX, a, st));
         parts_per_seq = x->dm.parts;
         seq_off = 0;
@@ -765,6 +767,9 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         zc.out = at<float>(x, x->lay.z);
         zc.ldo = c.n_centroids;
         HIP_TRY(launch_gemm(dt, mt_for(B), 1, EPI_STORE, zc, st));
+        if (trace && trace->centroid_scores)
+          HIP_TRY(launch_copy_rows(trace->centroid_scores + (size_t)(j - 1) * c.n_centroids,
+                                   K * c.n_centroids, zc.out, c.n_centroids, B, c.n_centroids, st));
         HIP_TRY(launch_cluster_select(at<float>(x, x->lay.z), c.n_centroids, k_c, B, tpc, upc,
                                       at<int>(x, x->lay.utile), at<int>(x, x->lay.urow), err, st));
         GemmArgs a = base_args(x, x->g_clu, B);
@@ -775,6 +780,8 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
         a.amax_val = at<float>(x, x->lay.d_amax_v);
         a.amax_idx = at<int>(x, x->lay.d_amax_i);
         a.idx_map = x->w.row_vocab;
+        a.logits = tscores;
+        a.ld_logits = ld_tscores;
         HIP_TRY(launch_gemm(dt, mt_for(B), 4, EPI_ARGMAX, a, st));
         parts_per_seq = k_c * upc;
         seq_off = k_c * upc;
@@ -785,6 +792,8 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
                                     (int)inj_stride, drafts, dtok, cur_tok, verify_tokens, err,
                                     st));
     }
+    if (trace && trace->raw_drafts)
+      HIP_TRY(launch_copy_rows(trace->raw_drafts + (j - 1), K, dtok, 1, B, 1, st));
   }
   return SPECDEC_OK;
 }
@@ -840,7 +849,7 @@ int specdec_moe_usage_read(specdec_ctx* x, int32_t* per_layer, void* stream) {
 }
 
 int specdec_profile_start(specdec_ctx* x, int32_t cls, int32_t capacity) {
-  if (!x || capacity < 0 || cls < -1 || cls > 6) return SPECDEC_E_INVAL;
+  if (!x || capacity < 0 || cls < -1 || cls > 8) return SPECDEC_E_INVAL;
   for (auto e : x->prof_ev) (void)hipEventDestroy(e);
   x->prof_ev.clear();
   x->prof_class = -1;

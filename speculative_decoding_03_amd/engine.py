@@ -257,16 +257,32 @@ class Engine:
                 "specdec_kv_commit")
 
     def draft(self, cur_tok, drafts, head_mode=F.HEAD_CLUSTERED, k_c=1, inject=None,
-              verify_tokens=None, stream=None) -> None:
+              verify_tokens=None, trace=None, stream=None) -> None:
         """Drafts [B][K] from cur_tok [B]; optionally also writes the verify input rows
-        verify_tokens [B][K+1] = [cur, d1..dK] (after injection)."""
+        verify_tokens [B][K+1] = [cur, d1..dK] (after injection).  `trace`, a dict with any of
+        the keys state [B][K][d_dim], hidden [B][K][d_model], centroid_scores [B][K][Nc],
+        table_scores [B][K][V] (float32) and raw_drafts [B][K] (int32), receives the drafter's
+        intermediate values (specdec_draft_traced)."""
         B, K = drafts.shape
         if verify_tokens is not None:
             assert verify_tokens.is_contiguous() and tuple(verify_tokens.shape) == (B, K + 1)
         stride = 0 if inject is None else inject.shape[1]
-        F.check(self.lib.specdec_draft(self.ctx, B, K, head_mode, k_c, _p(cur_tok), _p(drafts),
-                                       _p(inject), stride, _p(verify_tokens), _s(stream)),
-                "specdec_draft")
+        if trace is None:
+            F.check(self.lib.specdec_draft(self.ctx, B, K, head_mode, k_c, _p(cur_tok), _p(drafts),
+                                           _p(inject), stride, _p(verify_tokens), _s(stream)),
+                    "specdec_draft")
+            return
+        s = self.shape
+        widths = {"state": s.d_dim, "hidden": s.d_model, "centroid_scores": s.n_centroids,
+                  "table_scores": s.vocab, "raw_drafts": 1}
+        tr = F.DraftTrace()
+        for name, t in trace.items():
+            want = (torch.int32 if name == "raw_drafts" else torch.float32)
+            assert t.is_contiguous() and t.dtype == want and t.numel() == B * K * widths[name], name
+            setattr(tr, name, t.data_ptr())
+        F.check(self.lib.specdec_draft_traced(self.ctx, B, K, head_mode, k_c, _p(cur_tok),
+                                              _p(drafts), _p(inject), stride, _p(verify_tokens),
+                                              C.byref(tr), _s(stream)), "specdec_draft_traced")
 
     def moe_usage_start(self, stream=None) -> None:
         F.check(self.lib.specdec_moe_usage_start(self.ctx, _s(stream)), "specdec_moe_usage_start")

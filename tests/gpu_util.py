@@ -161,3 +161,103 @@ def restore(eng, snap):
 
 def oracle_model(cfg):
     return O.as_f64(S.target_weights(cfg)), O.as_f64(S.drafter_weights(cfg))
+
+
+def host_embedding(cfg) -> np.ndarray:
+    """The tied embedding / LM head [V][d] as float32 on the host, made by the device fill of the
+    seeded input generator (bit-identical to the host generator, spot-checked here)."""
+    t = WD.DeviceSource(cfg).get("embed", 0, (cfg.vocab, cfg.d_model))
+    E = t.float().cpu().numpy()
+    del t
+    for r in (0, 12345 % cfg.vocab, cfg.vocab - 1):
+        assert np.array_equal(E[r], S.gen_rows(cfg, "embed", 0, cfg.d_model, r, 1)[0])
+    return E
+
+
+def oracle_logits_full(cfg, W, E32, hs, chunk: int = 32768) -> np.ndarray:
+    """The oracle's LM head over the whole vocabulary for each hidden row in hs, applied to row
+    blocks of the embedding E32 (float32 values of the storage type)."""
+    out = np.empty((len(hs), cfg.vocab))
+    if len(hs) == 0:
+        return out
+    X = np.stack(hs)
+    for r0 in range(0, cfg.vocab, chunk):
+        blk = {"embed": E32[r0:r0 + chunk].astype(np.float64), "final_norm": W["final_norm"]}
+        out[:, r0:r0 + chunk] = O.lm_head(blk, cfg, X)
+    return out
+
+
+def drafter_trace_check(eng, cfg, DW, cache, hid, t0: int, length: int, K: int, mode: str,
+                        k_c: int, tol: float, margin: float = 0.05):
+    """Runs one traced draft of K sub-steps and checks every sub-step against the oracle,
+    teacher-forced on the GPU's own tokens (sub-step j of the oracle reads the token the GPU
+    drafted at j-1, so a legitimate near-tie flip does not end the comparison):
+
+    * the head's input s, the next hidden W_back s and (clustered) the centroid scores, element by
+      element within `tol` (max relative error);
+    * the clusters the GPU scored are exactly the k_c best of its own centroid scores (ties ->
+      lower cluster id), and its token is the argmax of its own scores over those members (ties
+      -> lower vocabulary id): bit-exact integer decisions taken from the GPU's values;
+    * the GPU's token scores within `tol` of the oracle's at every scored row;
+    * where the oracle's own choice differs, a near tie explains it: a cluster the GPU took over
+      the oracle's choice scores within tol * max|z| of the oracle's k_c-th best, or (same
+      clusters) the two tokens' oracle scores are within `margin`.
+
+    Returns the list of sub-steps at which the oracle's token differed (near ties)."""
+    dev = eng.kv_k.device
+    s = eng.shape
+    V, Nc, S = s.vocab, s.n_centroids, s.vocab // s.n_centroids
+    drafts = torch.empty(1, K, dtype=torch.int32, device=dev)
+    tr = {"state": torch.empty(1, K, s.d_dim, dtype=torch.float32, device=dev),
+          "hidden": torch.empty(1, K, s.d_model, dtype=torch.float32, device=dev),
+          "table_scores": torch.full((1, K, V), float("nan"), dtype=torch.float32, device=dev),
+          "raw_drafts": torch.empty(1, K, dtype=torch.int32, device=dev)}
+    if mode == "clustered":
+        tr["centroid_scores"] = torch.empty(1, K, Nc, dtype=torch.float32, device=dev)
+    hm = SD.HEAD_FULL if mode == "full" else SD.HEAD_CLUSTERED
+    eng.draft(torch.tensor([t0], dtype=torch.int32, device=dev), drafts, head_mode=hm, k_c=k_c,
+              trace=tr)
+    got = {k: v[0].cpu().numpy() for k, v in tr.items()}
+    raw = got["raw_drafts"].tolist()
+    assert drafts[0].cpu().tolist() == raw, "without injection the drafts are the drafter's own"
+    perm = np.asarray(DW["perm"])
+    h, c, flips = np.asarray(hid, np.float64), int(t0), []
+    for j in range(K):
+        st = []
+        d_ref, h_next = O.drafter_substep(DW, cfg, cache, h, c, length + j, length, mode, k_c, st)
+        s_ref = st[0]
+        assert rel_err(got["state"][j], s_ref) < tol, f"sub-step {j + 1}: head input s"
+        assert rel_err(got["hidden"][j], h_next) < tol, f"sub-step {j + 1}: next hidden"
+        sc = got["table_scores"][j]
+        rows = np.nonzero(~np.isnan(sc))[0]
+        if mode == "clustered":
+            gz = got["centroid_scores"][j]
+            z_ref = O.centroid_scores(DW["centroids"], s_ref)
+            assert rel_err(gz, z_ref) < tol, f"sub-step {j + 1}: centroid scores"
+            sel = sorted(range(Nc), key=lambda q: (-float(gz[q]), q))[:k_c]
+            want = np.sort(np.concatenate([np.arange(q * S, (q + 1) * S) for q in sel]))
+            assert np.array_equal(rows, want), f"sub-step {j + 1}: scored rows are not the GPU's best clusters"
+        else:
+            assert len(rows) == V, f"sub-step {j + 1}: the full head left rows unscored"
+        ids = perm[rows]  # table row r holds vocabulary id perm[r]
+        vals = sc[rows]
+        best = float(vals.max())
+        assert raw[j] == int(ids[vals == best].min()), f"sub-step {j + 1}: not the argmax of its own scores"
+        ref_sc = O.token_scores(DW["table"][ids], s_ref)
+        assert rel_err(vals, ref_sc) < tol, f"sub-step {j + 1}: token scores"
+        if d_ref != raw[j]:
+            flips.append(j + 1)
+            if mode == "clustered":
+                z_ref = O.centroid_scores(DW["centroids"], s_ref)
+                osel = sorted(range(Nc), key=lambda q: (-z_ref[q], q))[:k_c]
+                if set(osel) != set(sel):
+                    kth = float(np.sort(z_ref)[::-1][k_c - 1])
+                    delta = tol * float(np.max(np.abs(z_ref)))
+                    assert all(z_ref[q] >= kth - delta for q in sel), f"sub-step {j + 1}: cluster choice"
+                    h, c = h_next, raw[j]
+                    continue
+            full_ref = O.token_scores(DW["table"], s_ref)
+            assert full_ref[d_ref] - full_ref[raw[j]] <= margin, f"sub-step {j + 1}: token choice"
+        h, c = h_next, raw[j]
+    assert eng.device_error() == 0
+    return flips

@@ -5,11 +5,15 @@ serving case).  Each has its own committed length, so one launch mixes different
 and attention chunk counts.  Depth-truncated targets keep the full width and the full
 262144-entry vocabulary:
 * 31B-class at B=8: 32 verify rows, two 16-row MFMA tiles per projection on the row-major path;
-* 26B-class mixture-of-experts at B=4: 16 rows routed over 128 experts, top-8.
+* 26B-class mixture-of-experts at B=4 and B=8: 16 and 32 rows routed over 128 experts, top-8
+  (at B=8 the grouped expert GEMMs run two M-tiles);
+* a 64-row prefill call at the E2B width (four 16-row M-tiles per projection, 512 query vectors
+  per KV head in the attention).
 
-Every verify row's hidden state and sampled logits are compared with the oracle run on that
-row's own sequence alone, so a row that read another sequence's cache, length or routing would
-fail.  Tolerances and the margin rules are those of the single-sequence bf16 tests."""
+Every verify row's hidden state and its logits over the whole vocabulary are compared with the
+oracle run on that row's own sequence alone, so a row that read another sequence's cache,
+length or routing would fail.  Tolerances and the margin rules are those of the
+single-sequence bf16 tests."""
 
 import numpy as np
 import pytest
@@ -20,7 +24,8 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import oracle as O  # noqa: E402
-from gpu_util import build_engine, gpu_greedy_batch, gpu_spec_batch, rel_err  # noqa: E402
+from gpu_util import (build_engine, gpu_greedy_batch, gpu_spec_batch,  # noqa: E402
+                      host_embedding, oracle_logits_full, rel_err)
 from workloads import device as WD  # noqa: E402
 from workloads import inject_table, truncated  # noqa: E402
 from workloads import synth as S  # noqa: E402
@@ -32,6 +37,7 @@ ROUTE_MARGIN = 0.01
 CASES = {
     "31b-L1-B8": truncated("31b", 1, ctx=530, norm_jitter=0.1, d_layers=2, batch=8),
     "moe-L1-B4": truncated("moe", 1, ctx=530, norm_jitter=0.1, d_layers=2, batch=4),
+    "moe-L1-B8": truncated("moe", 1, ctx=530, norm_jitter=0.1, d_layers=2, batch=8),
 }
 # committed length of each sequence: ctx minus these (different chunk counts in one call)
 SHORTEN = [0, 37, 130, 3, 64, 129, 255, 1]
@@ -49,9 +55,6 @@ def oracle_rows(W, cfg, cache, tokens, length, margins):
     return H
 
 
-def oracle_logits_at(W, cfg, h, ids):
-    E = np.stack([S.gen_rows(cfg, "embed", 0, cfg.d_model, int(i), 1)[0] for i in ids]).astype(np.float64)
-    return E @ O.rmsnorm(h, W["final_norm"], cfg.rms_eps)
 
 
 @pytest.fixture(scope="module", params=sorted(CASES))
@@ -105,6 +108,10 @@ def test_batched_verify_rows_match_oracle(bcase):
     eng.verify(Tt, logits=logits, argmax=am)
     lg = logits.cpu().numpy()
     G = am.cpu().numpy()
+    E32 = host_embedding(cfg)
+    pairs = [(b, i) for b in range(B) for i in range(K + 1) if check[b][i]]
+    refs = dict(zip(pairs, oracle_logits_full(cfg, bcase["W"], E32, [H[b][i] for b, i in pairs])))
+    del E32
     for i in range(K + 1):
         # committing i+1 rows leaves each sequence's hidden row i in hid
         reset(bcase)
@@ -117,13 +124,11 @@ def test_batched_verify_rows_match_oracle(bcase):
                 continue
             assert rel_err(got[b], H[b][i]) < TOL, f"sequence {b} row {i}"
             assert G[b, i] == int(np.argmax(lg[b, i]))
-            top = np.argsort(-lg[b, i], kind="stable")[:16]
-            ids = np.unique(np.concatenate([rng.integers(0, cfg.vocab, 1024), top]))
-            ref = oracle_logits_at(bcase["W"], cfg, H[b][i], ids)
-            assert rel_err(lg[b, i][ids], ref) < TOL, f"sequence {b} row {i}"
-            rb = ids[int(np.argmax(ref))]
+            ref = refs[(b, i)]
+            assert rel_err(lg[b, i], ref) < TOL, f"sequence {b} row {i}: logits"
+            rb = O.argmax_first(ref)
             if rb != G[b, i]:
-                assert ref.max() - ref[list(ids).index(G[b, i])] <= MARGIN
+                assert ref[rb] - ref[G[b, i]] <= MARGIN, f"sequence {b} row {i}: argmax"
     assert eng.device_error() == 0
 
 
@@ -142,3 +147,46 @@ def test_batched_spec_equals_batched_greedy(bcase):
     assert toks == [s[:n] for s in g]
     assert all(1 <= e <= K + 1 for step in emitted for e in step)
     assert eng.device_error() == 0
+
+
+def test_prefill_call_of_64_rows_matches_oracle():
+    """One 64-row verify call (a prefill chunk) at the E2B width after 530 committed positions:
+    four 16-row M-tiles per projection and 64 x 8 query vectors per KV head.  Hidden rows at a
+    sample of positions, all 64 rows' argmax against the GPU's own logits, and the logits over
+    the whole vocabulary of the sampled rows against the oracle."""
+    cfg = truncated("e2b", 1, ctx=530, norm_jitter=0.1, d_layers=2)
+    R = 64
+    max_ctx = (cfg.ctx + R + 8 + 7) // 8 * 8
+    eng = build_engine(cfg, max_ctx, max_rows=R)
+    try:
+        WD.fill_kv(eng, cfg)
+        WD.start_state(eng, cfg)
+        W = O.as_f64({"final_norm": S.norm_weight(cfg, "final_norm", 0, cfg.d_model),
+                      "layers": [S.target_layer_weights(cfg, l) for l in range(cfg.n_layers)]})
+        k, v = S.kv_init(cfg)
+        cache = O.KVCache.from_synthetic(cfg, k[:, 0].astype(np.float64), v[:, 0].astype(np.float64),
+                                         max_ctx)
+        toks = [int(t) for t in np.random.default_rng(41).integers(0, cfg.vocab, R)]
+        H = oracle_rows(W, cfg, cache, toks, cfg.ctx, [])
+        dev = eng.kv_k.device
+        Tt = torch.tensor([toks], dtype=torch.int32, device=dev)
+        logits = torch.empty(1, R, cfg.vocab, dtype=torch.float32, device=dev)
+        am = torch.empty(1, R, dtype=torch.int32, device=dev)
+        eng.verify(Tt, logits=logits, argmax=am)
+        lg = logits[0].cpu().numpy()
+        G = am[0].cpu().numpy()
+        assert all(G[i] == int(np.argmax(lg[i])) for i in range(R))
+        sample = [0, 1, 17, 31, 32, 47, 48, 63]
+        refs = oracle_logits_full(cfg, W, host_embedding(cfg), [H[i] for i in sample])
+        for i, ref in zip(sample, refs):
+            eng.set_len([cfg.ctx])
+            eng.verify(Tt)
+            eng.kv_commit(torch.tensor([i + 1], dtype=torch.int32, device=dev))
+            assert rel_err(eng.hid[0].cpu().numpy(), H[i]) < TOL, f"row {i}: hidden"
+            assert rel_err(lg[i], ref) < TOL, f"row {i}: logits"
+            rb = O.argmax_first(ref)
+            if rb != G[i]:
+                assert ref[rb] - ref[G[i]] <= MARGIN, f"row {i}: argmax"
+        assert eng.device_error() == 0
+    finally:
+        eng.close()

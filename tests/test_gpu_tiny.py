@@ -19,9 +19,9 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import oracle as O  # noqa: E402
 import speculative_decoding_03_amd as SD  # noqa: E402
-from gpu_util import (build_engine, gpu_greedy, gpu_greedy_batch, gpu_prefill,  # noqa: E402
-                      gpu_prefill_batch, gpu_spec, gpu_spec_batch, oracle_model, rel_err, restore,
-                      snapshot)
+from gpu_util import (build_engine, drafter_trace_check, gpu_greedy, gpu_greedy_batch,  # noqa: E402
+                      gpu_prefill, gpu_prefill_batch, gpu_spec, gpu_spec_batch, oracle_model,
+                      rel_err, restore, snapshot)
 from workloads import inject_table, preset, prompt_tokens  # noqa: E402
 
 CFG = preset("tiny")
@@ -173,6 +173,131 @@ def test_drafter_matches_oracle(tiny, mode, k_c):
     assert eng.device_error() == 0
 
 
+@pytest.mark.parametrize("mode,k_c", [("clustered", 1), ("clustered", 3), ("full", 1)])
+def test_drafter_trace_matches_oracle(tiny, mode, k_c):
+    """The drafter's intermediate values of every sub-step (head input, next hidden, centroid
+    and token scores) against the oracle at the fp32 tolerance, and its integer choices from its
+    own scores; at fp32 no sub-step may need the near-tie allowance."""
+    CFG = tiny["cfg"]
+    restore(tiny["eng"], tiny["snap"])
+    flips = drafter_trace_check(tiny["eng"], CFG, tiny["DW"], tiny["cache"], tiny["hid"],
+                                tiny["ref_t0"], tiny["length"], CFG.draft_k, mode, k_c, TOL)
+    assert flips == []
+
+
+def _spec_steps(eng, cur, steps, K, inj):
+    """`steps` speculative steps from the current token tensor cur [1] (updated in place);
+    returns the emitted tokens."""
+    dev = eng.kv_k.device
+    drafts = torch.empty(1, K, dtype=torch.int32, device=dev)
+    T = torch.empty(1, K + 1, dtype=torch.int32, device=dev)
+    out = torch.empty(1, K + 1, dtype=torch.int32, device=dev)
+    n_emit = torch.empty(1, dtype=torch.int32, device=dev)
+    toks = []
+    for _ in range(steps):
+        eng.draft(cur, drafts, inject=inj, verify_tokens=T)
+        eng.verify(T)
+        eng.accept(T, out_tokens=out, n_emit=n_emit, next_tok=cur, commit=True)
+        e = int(n_emit.item())
+        toks.extend(out[0, :e].cpu().tolist())
+        eng.set_len_bound([int(eng.len[0].item())])
+    return toks
+
+
+def test_snapshot_restore_continues_bitwise(tiny):
+    """Snapshot the step state (KV cache, len, hid, next token) mid-generation, run other steps
+    that overwrite the cache past len and move len and hid, restore, and continue: the tokens,
+    len and hid equal those of an uninterrupted run bit for bit."""
+    CFG = tiny["cfg"]
+    eng = tiny["eng"]
+    K = CFG.draft_k
+    dev = eng.kv_k.device
+    restore(eng, tiny["snap"])
+    ref = gpu_greedy(eng, tiny["t0"], 64)
+    L = tiny["length"]
+    gseq = np.full(MAX_CTX, -1, dtype=np.int64)
+    gseq[L:L + len(ref)] = ref
+    inj = torch.from_numpy(inject_table(gseq, K, 0.6, CFG.inject_seed).reshape(1, -1)).to(dev)
+    restore(eng, tiny["snap"])
+    cur = torch.tensor([tiny["t0"]], dtype=torch.int32, device=dev)
+    a = _spec_steps(eng, cur, 12, K, inj)
+    end_len, end_hid = eng.len.clone(), eng.hid.clone()
+
+    restore(eng, tiny["snap"])
+    cur = torch.tensor([tiny["t0"]], dtype=torch.int32, device=dev)
+    b = _spec_steps(eng, cur, 5, K, inj)
+    snap = (eng.kv_k.clone(), eng.kv_v.clone(), eng.len.clone(), eng.hid.clone(), cur.clone())
+    other = torch.tensor([7], dtype=torch.int32, device=dev)
+    _spec_steps(eng, other, 3, K, None)  # different tokens: the cache past len is overwritten
+    assert not torch.equal(eng.len, snap[2])
+    eng.kv_k.copy_(snap[0])
+    eng.kv_v.copy_(snap[1])
+    eng.len.copy_(snap[2])
+    eng.hid.copy_(snap[3])
+    eng.set_len_bound(snap[2].cpu().tolist())
+    cur = snap[4].clone()
+    b += _spec_steps(eng, cur, 7, K, inj)
+    assert b == a
+    assert torch.equal(eng.len, end_len) and torch.equal(eng.hid, end_hid)
+    assert eng.device_error() == 0
+
+
+def test_rollback_poison_is_never_read(tiny):
+    """Dead cache slots after each rollback are filled with NaN in every layer; the speculative
+    output is unchanged and no NaN is flagged."""
+    CFG = tiny["cfg"]
+    eng = tiny["eng"]
+    K = CFG.draft_k
+    dev = eng.kv_k.device
+    restore(eng, tiny["snap"])
+    ref = gpu_greedy(eng, tiny["t0"], 48 + K + 2)
+    L = tiny["length"]
+    gseq = np.full(MAX_CTX, -1, dtype=np.int64)
+    gseq[L:L + len(ref)] = ref
+    inj = torch.from_numpy(inject_table(gseq, K, 0.6, CFG.inject_seed).reshape(1, -1)).to(dev)
+    restore(eng, tiny["snap"])
+    saved = (eng.kv_k.clone(), eng.kv_v.clone())  # the fixture's cache is shared
+    kv_k, kv_v = eng.kv_view()
+    cur = torch.tensor([tiny["t0"]], dtype=torch.int32, device=dev)
+    toks, length, rejected = [tiny["t0"]], L, 0
+    while len(toks) < 48:
+        toks += _spec_steps(eng, cur, 1, K, inj)
+        new_len = int(eng.len[0].item())
+        if new_len < length + K + 1:
+            rejected += 1
+            kv_k[:, 0, :, new_len:length + K + 1, :] = float("nan")
+            kv_v[:, 0, :, :, new_len:length + K + 1] = float("nan")
+        length = new_len
+    assert rejected > 0
+    assert toks[:48] == ref[:48]
+    assert eng.device_error() == 0
+    eng.kv_k.copy_(saved[0])
+    eng.kv_v.copy_(saved[1])
+
+
+def test_nan_norm_weight_raises_the_nan_bit():
+    """A NaN in the final norm weight makes every logit NaN: the step flags SPECDEC_DEVERR_NAN
+    (the kernels finish normally; nothing is read or written out of bounds)."""
+    class NanNorm:
+        def __init__(self, src):
+            self.src = src
+
+        def get(self, name, layer, shape):
+            t = self.src.get(name, layer, shape)
+            if name == "final_norm":
+                t[3] = float("nan")
+            return t
+
+    eng = build_engine(CFG, 64, weights_override=lambda s: NanNorm(s))
+    dev = eng.kv_k.device
+    am = torch.empty(1, 2, dtype=torch.int32, device=dev)
+    eng.verify(torch.tensor([[5, 9]], dtype=torch.int32, device=dev), argmax=am)
+    err = eng.device_error(clear=True)
+    assert err & SD.ffi.DEVERR_NAN
+    assert eng.device_error() == 0  # cleared
+    eng.close()
+
+
 def test_accept_bit_exact_all_patterns(tiny):
     CFG = tiny["cfg"]
     eng = tiny["eng"]
@@ -261,6 +386,15 @@ def test_error_paths(tiny):
     with pytest.raises(SD.SpecdecError) as e:
         eng.verify(torch.zeros(1, 4, dtype=torch.int32, device=dev))
     assert e.value.code == -2
+    # a draft's last query position len + K - 1 must be a cache slot
+    d = torch.empty(1, 3, dtype=torch.int32, device=dev)
+    with pytest.raises(SD.SpecdecError) as e:
+        eng.draft(torch.zeros(1, dtype=torch.int32, device=dev), d)
+    assert e.value.code == -2
+    eng.set_len_bound([MAX_CTX - 3])
+    eng.len.fill_(MAX_CTX - 3)
+    eng.draft(torch.zeros(1, dtype=torch.int32, device=dev), d)  # positions up to MAX_CTX - 1
+    assert eng.device_error(clear=True) == 0
     # device-side guard: len beyond the bound known to the host -> error bit, no write past max_ctx
     before_k = eng.kv_k.clone()
     eng.len.fill_(MAX_CTX - 2)

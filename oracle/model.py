@@ -190,9 +190,10 @@ def decoder_layer_row(lw: dict, cfg, Kl: np.ndarray, Vl: np.ndarray, x: np.ndarr
 
 
 def lm_head(W: dict, cfg, hidden: np.ndarray) -> np.ndarray:
-    """Tied output layer: logits = E . rmsnorm(hidden).  Reading: the LM head is tied to the
-    embedding (the 31B workload's ~30.5B parameter count only matches a tied head)."""
-    return W["embed"] @ rmsnorm(hidden, W["final_norm"], cfg.rms_eps)
+    """Tied output layer: logits = E . rmsnorm(hidden), for one hidden row [d] or a stack of
+    rows [n][d] (then [n][V]).  Reading: the LM head is tied to the embedding (the 31B workload's
+    ~30.5B parameter count only matches a tied head)."""
+    return rmsnorm(hidden, W["final_norm"], cfg.rms_eps) @ W["embed"].T
 
 
 def target_row(W: dict, cfg, cache: KVCache, tok: int, pos: int):

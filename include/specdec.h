@@ -158,6 +158,23 @@ size_t specdec_kv_elems(const specdec_config* cfg);
 int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv_k, void* kv_v,
                    int32_t* len, float* hid, void* workspace, size_t workspace_bytes,
                    void* stream, specdec_ctx** out);
+/* For callers that cannot allocate device memory (code under stream capture, serving loops or
+   harnesses that forbid hipMalloc): specdec_create with the workspace taken from a fixed array
+   of SPECDEC_STATIC_WORKSPACE_BYTES inside the library instead of a caller buffer.  Each GPU the
+   library runs on holds its own copy of the array until the process ends; its address is looked
+   up (hipGetSymbolAddress) on the first call on that GPU, with that GPU current.  This call
+   allocates nothing: the caller still owns kv_k, kv_v, len and hid, as for specdec_create.
+   Every context made by this call on one GPU shares that GPU's array, which keeps what the last
+   call left there: use one such context per GPU at a time (creating another takes the array
+   over), and calls on it that overlap on one GPU race.  Create zeroes the device error word and
+   writes the rotary table there, as specdec_create does in its workspace; every other part of
+   the workspace is written by a step before it is read.
+   Errors: those of specdec_create, and SPECDEC_E_CAPACITY when specdec_workspace_bytes(cfg)
+   exceeds SPECDEC_STATIC_WORKSPACE_BYTES (checked before any HIP call). */
+#define SPECDEC_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int specdec_create_static(const specdec_config* cfg, const specdec_weights* w, void* kv_k,
+                          void* kv_v, int32_t* len, float* hid, void* stream, specdec_ctx** out);
+
 int specdec_destroy(specdec_ctx* ctx);
 
 /* Draft K tokens per sequence.

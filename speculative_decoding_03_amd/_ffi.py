@@ -9,6 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspecdec.so")
 
 OK, E_INVAL, E_CAPACITY, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4
+STATIC_WORKSPACE_BYTES = 64 << 20  # SPECDEC_STATIC_WORKSPACE_BYTES
 F32, BF16 = 0, 1
 HEAD_CLUSTERED, HEAD_FULL = 0, 1
 ACCEPT_COMMIT = 1
@@ -21,7 +22,8 @@ DW_N1, DW_Q, DW_O, DW_N2, DW_GATE_UP, DW_DOWN, N_DRAFT_TENSORS = range(7)
  PROF_EXP_DOWN) = range(9)
 
 EXPORTS = [
-    "specdec_workspace_bytes", "specdec_kv_elems", "specdec_create", "specdec_destroy",
+    "specdec_workspace_bytes", "specdec_kv_elems", "specdec_create", "specdec_create_static",
+    "specdec_destroy",
     "specdec_draft", "specdec_draft_traced", "specdec_verify", "specdec_accept", "specdec_kv_commit",
     "specdec_pack_matrix", "specdec_set_len_bound", "specdec_read_device_error",
     "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
@@ -70,6 +72,7 @@ def load(path: str = LIB_PATH):
         "specdec_workspace_bytes": (sz, [P(Config)]),
         "specdec_kv_elems": (sz, [P(Config)]),
         "specdec_create": (C.c_int, [P(Config), P(Weights), vp, vp, vp, vp, vp, sz, vp, P(vp)]),
+        "specdec_create_static": (C.c_int, [P(Config), P(Weights), vp, vp, vp, vp, vp, P(vp)]),
         "specdec_destroy": (C.c_int, [vp]),
         "specdec_draft": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp]),
         "specdec_draft_traced": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, i64, vp,

@@ -10,12 +10,19 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "kernels.h"
 
 using namespace specdec;
+
+// Workspace of contexts made by specdec_create_static (callers that cannot allocate device
+// memory): one fixed array per GPU, held by the loaded library until the process ends.  Host
+// code never uses this name as an address: the per-device address comes from
+// hipGetSymbolAddress (static_workspace below).
+static __device__ __align__(256) unsigned char scratch[SPECDEC_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -457,6 +464,11 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
   return SPECDEC_OK;
 }
 
+int static_workspace(void** out);
+int create_on(const specdec_config* cfg, const specdec_weights* w, void* kv_k, void* kv_v,
+              int32_t* len, float* hid, void* workspace, size_t workspace_bytes, void* stream,
+              specdec_ctx** out);
+
 }  // namespace
 
 extern "C" {
@@ -478,6 +490,45 @@ int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv
   *out = nullptr;
   if (!valid_config(cfg) || !w || !kv_k || !kv_v || !len || !hid || !workspace)
     return SPECDEC_E_INVAL;
+  return create_on(cfg, w, kv_k, kv_v, len, hid, workspace, workspace_bytes, stream, out);
+}
+
+int specdec_create_static(const specdec_config* cfg, const specdec_weights* w, void* kv_k,
+                          void* kv_v, int32_t* len, float* hid, void* stream, specdec_ctx** out) {
+  if (!out) return SPECDEC_E_INVAL;
+  *out = nullptr;
+  if (!valid_config(cfg) || !w || !kv_k || !kv_v || !len || !hid) return SPECDEC_E_INVAL;
+  const size_t need = specdec_workspace_bytes(cfg);
+  if (need > SPECDEC_STATIC_WORKSPACE_BYTES) return SPECDEC_E_CAPACITY;
+  void* ws = nullptr;
+  const int rc = static_workspace(&ws);
+  if (rc != SPECDEC_OK) return rc;
+  return create_on(cfg, w, kv_k, kv_v, len, hid, ws, SPECDEC_STATIC_WORKSPACE_BYTES, stream, out);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Address of this GPU's copy of `scratch`, looked up once per device with that device current.
+int static_workspace(void** out) {
+  static std::mutex mu;
+  static void* addr[256] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return SPECDEC_E_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPECDEC_E_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return SPECDEC_OK;
+}
+
+int create_on(const specdec_config* cfg, const specdec_weights* w, void* kv_k, void* kv_v,
+              int32_t* len, float* hid, void* workspace, size_t workspace_bytes, void* stream,
+              specdec_ctx** out) {
   if (!attention_supported(cfg->head_dim)) return SPECDEC_E_UNSUPPORTED;
   if (((uintptr_t)workspace) % ALIGN) return SPECDEC_E_INVAL;
   if (!w->embed || !w->final_norm || !w->layers || !w->table || !w->centroids || !w->row_vocab ||
@@ -520,6 +571,10 @@ int specdec_create(const specdec_config* cfg, const specdec_weights* w, void* kv
   *out = x;
   return SPECDEC_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int specdec_destroy(specdec_ctx* x) {
   if (!x) return SPECDEC_E_INVAL;

@@ -177,7 +177,9 @@ class Engine:
     """One libspecdec context plus the caller-owned device state it works on."""
 
     def __init__(self, model: DeviceModel, max_batch: int, max_draft: int, max_rows: int,
-                 max_ctx: int, stream=None):
+                 max_ctx: int, stream=None, static_workspace: bool = False):
+        """static_workspace=True creates the context with specdec_create_static: the library's
+        own fixed workspace array instead of a caller buffer (one such context per GPU)."""
         lib = F.load()
         if not torch.cuda.is_available():
             raise RuntimeError("libspecdec needs a ROCm GPU; no CPU path exists")
@@ -205,15 +207,22 @@ class Engine:
         self.kv_v = torch.zeros(kv, dtype=TORCH_DT[s.dtype], device=dev)
         self.len = torch.zeros(max_batch, dtype=torch.int32, device=dev)
         self.hid = torch.zeros(max_batch, s.d_model, dtype=torch.float32, device=dev)
-        self._ws = torch.zeros(ws + 256, dtype=torch.uint8, device=dev)
-        off = (-self._ws.data_ptr()) % 256
-        self.ws_ptr = self._ws.data_ptr() + off
         self.ws_bytes = ws
         self._w = model.abi()
         ctx = C.c_void_p()
-        F.check(lib.specdec_create(C.byref(cfg), C.byref(self._w), _p(self.kv_k), _p(self.kv_v),
-                                   _p(self.len), _p(self.hid), C.c_void_p(self.ws_ptr), ws,
-                                   _s(stream), C.byref(ctx)), "specdec_create")
+        if static_workspace:
+            self._ws = None
+            F.check(lib.specdec_create_static(C.byref(cfg), C.byref(self._w), _p(self.kv_k),
+                                              _p(self.kv_v), _p(self.len), _p(self.hid),
+                                              _s(stream), C.byref(ctx)), "specdec_create_static")
+        else:
+            self._ws = torch.zeros(ws + 256, dtype=torch.uint8, device=dev)
+            off = (-self._ws.data_ptr()) % 256
+            self.ws_ptr = self._ws.data_ptr() + off
+            F.check(lib.specdec_create(C.byref(cfg), C.byref(self._w), _p(self.kv_k),
+                                       _p(self.kv_v), _p(self.len), _p(self.hid),
+                                       C.c_void_p(self.ws_ptr), ws, _s(stream), C.byref(ctx)),
+                    "specdec_create")
         self.ctx = ctx
 
     # --- state helpers (setup / tests) ---

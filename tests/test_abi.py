@@ -90,3 +90,17 @@ def test_null_handles_are_rejected(lib):
     out = C.c_void_p()
     assert lib.specdec_create(None, None, None, None, None, None, None, 0, None, C.byref(out)) == F.E_INVAL
     assert out.value is None
+
+
+def test_static_workspace_create_refuses_an_oversized_workspace(lib):
+    """specdec_create_static checks the configuration's workspace against its fixed array before
+    any HIP call: a 31B-class configuration at batch 8 (about 108 MiB) is refused."""
+    c = _config(n_layers=64, d_model=5120, n_q_heads=40, n_kv_heads=8, head_dim=128,
+                ffn_dim=25600, vocab=262144, d_layers=4, d_dim=256, d_ffn=1024, n_centroids=2048,
+                dtype=F.BF16, max_batch=8, max_draft=3, max_rows=8, max_ctx=9216)
+    assert lib.specdec_workspace_bytes(C.byref(c)) > F.STATIC_WORKSPACE_BYTES
+    w = F.Weights()
+    ctx = C.c_void_p()
+    one = C.c_void_p(256)
+    rc = lib.specdec_create_static(C.byref(c), C.byref(w), one, one, one, one, None, C.byref(ctx))
+    assert rc == F.E_CAPACITY and not ctx.value

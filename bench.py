@@ -187,6 +187,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
     ap.add_argument("--no-p-sweep", dest="p_sweep", action="store_false")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the graph-replay leg (kernel traces then end with the timed steps)")
     ap.add_argument("--sweep-steps", type=int, default=40)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -367,6 +369,8 @@ def main() -> int:
     log(f"speculative loop: {main['emitted'] / wall:.1f} tokens/s, spec == greedy: {same}")
     # graph replay of the whole step, same workload
     try:
+        if not args.graph:
+            raise RuntimeError("skipped (--no-graph)")
         gr = spec_run(cfg.p_inject, W, N, graph=True)
         log(f"graph replay: {gr['emitted'] / gr['wall']:.1f} tokens/s, spec == greedy: {gr['same']}")
     except Exception as e:  # reported, never the headline

@@ -89,11 +89,6 @@ __device__ __forceinline__ void store_part_o(float* row, int d0, const f32x4& y)
     *reinterpret_cast<f32x4*>(row + d0) = y;
   }
 }
-template <typename T>
-__device__ __forceinline__ float load_part_o(const float* row, int d) {
-  if constexpr (sizeof(T) == 2) return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
-  else return row[d];
-}
 
 // One workgroup = CH consecutive keys of one KV head of one sequence; wave w owns keys
 // [chunk*CH + w*KPW, +KPW), which it loads once into registers.  Then, for each 16-vector tile of
@@ -122,13 +117,10 @@ attn_kernel(AttnArgs a) {
   const int Rall = a.R * G;
   const float scale2 = a.scale * 1.44269504088896341f;  // softmax scale times log2 e
 
-  const int len = a.len[b];
-  const int end_max = len + a.R - 1 + a.key_off;  // keys [0, end_max) are read by some row
-  if (end_max > a.max_ctx || len < 0) {
-    if (chunk == 0 && g == 0 && threadIdx.x == 0) raise_error(a.err, ERRBIT_CAPACITY);
-    return;
-  }
-  if (chunk * CH >= end_max) return;  // uniform over the workgroup
+  // The committed length is requested first but waited for only after every cache and query
+  // load is in flight: no load address depends on it (each is clamped into the cache), so its
+  // latency overlaps theirs.  A chunk launched past the visible keys returns after its loads.
+  const int len_in = a.len[b];
   const int kw0 = chunk * CH + w * KPW;
   const T* Kc = reinterpret_cast<const T*>(a.kcache) + (size_t)b * a.cache_b_stride +
                 (size_t)g * a.max_ctx * HD;
@@ -177,6 +169,13 @@ attn_kernel(AttnArgs a) {
   }
   // every load above is issued before any instruction that waits for one of them
   __builtin_amdgcn_sched_barrier(0);
+  const int len = len_in;
+  const int end_max = len + a.R - 1 + a.key_off;  // keys [0, end_max) are read by some row
+  if (end_max > a.max_ctx || len < 0) {
+    if (chunk == 0 && g == 0 && threadIdx.x == 0) raise_error(a.err, ERRBIT_CAPACITY);
+    return;
+  }
+  if (chunk * CH >= end_max) return;  // uniform over the workgroup
   const bool ragged = kw0 + KPW > end_max;  // the wave holds values past end_max (wave-uniform)
 
   float* pbase = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * SH::PST;
@@ -296,91 +295,135 @@ attn_kernel(AttnArgs a) {
   }
 }
 
-// Combines the chunk partials of one query vector:
+// Combines the chunk partials of one query vector on one wave:
 // o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c (maxima in base-2 units).
-// Thread (p, d) sums chunks p, p+P, p+2P, ... of column d (P = 1024 / hd parts), and the P part
-// sums are added in part order, so the result depends only on the chunk partials (a chunk whose
-// keys are all invisible to the row contributes exact zeros).
-template <typename T>
-__global__ void __launch_bounds__(1024) attn_combine_kernel(AttnArgs a) {
-  __shared__ float wts[4096];
-  __shared__ float ls[4096];
-  __shared__ float psum[1024];
-  __shared__ float wmax[16];
-  __shared__ float Linv;
-  const int qv = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int t = threadIdx.x;
+// A partial row's value sum is read as 16-byte runs: lane (r, q) = (lane % RN, lane / RN) takes
+// run r of chunks q, q + QN, q + 2 QN, ... (QN = 64 / RN chunk groups).  Each lane requests a
+// batch of CB chunks (value run and (m, l)) before it uses any of them, keeps a running maximum
+// of its own chunks and rescales its sums when the maximum grows, then the QN groups are merged
+// through LDS in group order.  Chunk c always belongs to the same lane and batch, so the result
+// depends only on the row's own partials (a chunk whose keys the row cannot see has m = -inf and
+// adds exact zeros).
+template <typename T, int HD>
+__global__ void __launch_bounds__(WAVE) attn_combine_kernel(AttnArgs a) {
+  constexpr int EPR = 16 / (int)sizeof(T);  // elements per 16-byte run
+  constexpr int RN = HD / EPR;              // runs per partial row
+  constexpr int QN = WAVE / RN;             // chunk groups
+  // chunks per lane per batch: 96 chunks of 128 keys (12K context at head size 128) in one batch
+  constexpr int CB = 24;
+  static_assert(HD % EPR == 0 && RN <= WAVE && QN >= 1, "partial row does not fit a wave");
+  __shared__ __align__(16) float red[QN][HD];
+  __shared__ float lred[QN];
+  const int qv = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
   const int G = a.hq / a.hkv;
-  const int Rall = a.R * G;
-  const int hd = a.hd;
-  const int len = a.len[b];
-  const int end_max = len + a.R - 1 + a.key_off;
-  if (end_max > a.max_ctx || len < 0) return;
-  const int n_act = (end_max + a.chunk - 1) / a.chunk;
-  if (n_act > a.n_launch) {  // the device length is beyond the host-side bound
-    if (t == 0) raise_error(a.err, ERRBIT_CAPACITY);
-    return;
-  }
   const int row = qv / G, h = g * G + (qv - row * G);
-  // output element d of this query vector: row b*R + row, column h*hd + d of the O input
   T* const out = reinterpret_cast<T*>(a.out);
-  const int orow = b * a.R + row, ocol = h * hd, ld = a.hq * hd;
-  if (n_act == 0) {
-    // no visible key (drafter before any context): the attention output is defined as zero
-    for (int d = t; d < hd; d += blockDim.x)
-      Elem<T>::store(out + x_offset(a.out_qx, orow, ocol + d, ld), 0.f);
-    return;
-  }
-  const int pst = hd + 4;  // partial row: o[hd], m, l, 2 pad
-  const size_t cstride = (size_t)Rall * pst;
+  const int orow = b * a.R + row, ocol = h * HD, ld = a.hq * HD;
+  const int r = lane % RN, q = lane / RN;
+  const bool active = q < QN;
+  const int pst = HD + 4;  // partial row: o[HD] (storage type), then (m, l) fp32 at float HD
+  const size_t cstride = (size_t)a.R * G * pst;
   const float* pbase = a.part + ((size_t)b * a.hkv + g) * a.n_chunks * cstride + (size_t)qv * pst;
-  // chunk max over (m_c): per-thread stripes, then waves in order
-  float mx = -INFINITY;
-  for (int c = t; c < n_act; c += blockDim.x) {
-    const float2 ml = *reinterpret_cast<const float2*>(pbase + c * cstride + hd);
-    wts[c] = ml.x;
-    ls[c] = ml.y;
-    mx = fmaxf(mx, ml.x);
-  }
-  mx = wave_max(mx);
-  if ((t & 63) == 0) wmax[t >> 6] = mx;
-  __syncthreads();
-  float M = wmax[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) M = fmaxf(M, wmax[w]);
-  const float Ms = M == -INFINITY ? 0.f : M;  // chunk maxima are in base-2 units
-  for (int c = t; c < n_act; c += blockDim.x)
-    wts[c] = exp2_hw(wts[c] - Ms);
-  __syncthreads();
-  if (t == 0) {
-    float L = 0.f;
-    for (int c = 0; c < n_act; ++c) L += ls[c] * wts[c];
-    Linv = 1.0f / L;
-  }
-  const int P = blockDim.x / hd;  // chunk parts
-  const int p = t / hd, d = t - p * hd;
-  float acc = 0.f;
-  if (p < P) {
-    int c = p;
-    for (; c + 3 * P < n_act; c += 4 * P) {
-      const float v0 = load_part_o<T>(pbase + (size_t)c * cstride, d);
-      const float v1 = load_part_o<T>(pbase + (size_t)(c + P) * cstride, d);
-      const float v2 = load_part_o<T>(pbase + (size_t)(c + 2 * P) * cstride, d);
-      const float v3 = load_part_o<T>(pbase + (size_t)(c + 3 * P) * cstride, d);
-      acc += wts[c] * v0;
-      acc += wts[c + P] * v1;
-      acc += wts[c + 2 * P] * v2;
-      acc += wts[c + 3 * P] * v3;
+  // Batches cover the chunks the launch may have written (the host-side bound n_launch), so the
+  // first batch's loads are in flight before the committed length arrives; chunks past the
+  // row's visible ones (n_act) are loaded but never used.
+  const int len_in = a.len[b];
+  float mq = -INFINITY, lq = 0.f, acc[EPR];
+#pragma unroll
+  for (int e = 0; e < EPR; ++e) acc[e] = 0.f;
+  const int per_lane = (a.n_launch + QN - 1) / QN;  // chunks of the busiest group
+  int n_act = -1;
+  for (int k0 = 0; k0 < per_lane; k0 += CB) {
+    u32x4 ov[CB];
+    float2 ml[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      // a chunk past the launch reads chunk 0 again (in bounds) and is not used
+      const int c = q + QN * (k0 + k);
+      const float* rowp = pbase + (size_t)(active && c < a.n_launch ? c : 0) * cstride;
+      ov[k] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(rowp) + r * 16);
+      ml[k] = *reinterpret_cast<const float2*>(rowp + HD);
     }
-    for (; c < n_act; c += P) acc += wts[c] * load_part_o<T>(pbase + (size_t)c * cstride, d);
-    psum[p * hd + d] = acc;
+    if (n_act < 0) {
+      const int len = len_in;
+      const int end_max = len + a.R - 1 + a.key_off;
+      if (end_max > a.max_ctx || len < 0) return;
+      n_act = (end_max + a.chunk - 1) / a.chunk;
+      if (n_act > a.n_launch) {  // the device length is beyond the host-side bound
+        if (lane == 0) raise_error(a.err, ERRBIT_CAPACITY);
+        return;
+      }
+      if (n_act == 0) {
+        // no visible key (drafter before any context): the attention output is defined as zero
+        if (active && q == 0)
+          *reinterpret_cast<u32x4*>(out + x_offset(a.out_qx, orow, ocol + r * EPR, ld)) = u32x4{0, 0, 0, 0};
+        return;
+      }
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < CB; ++k)
+      if (active && q + QN * (k0 + k) < n_act) mb = fmaxf(mb, ml[k].x);
+    const float mn = fmaxf(mq, mb);
+    if (mn != mq) {  // the running maximum grew: rescale what this lane has summed
+      const float sc = exp2_hw(mq - mn);  // mq = -inf: sums are zero, 2^-inf = 0
+#pragma unroll
+      for (int e = 0; e < EPR; ++e) acc[e] *= sc;
+      lq *= sc;
+      mq = mn;
+    }
+    const float ms = mq == -INFINITY ? 0.f : mq;
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      if (!(active && q + QN * (k0 + k) < n_act)) continue;
+      const float w = exp2_hw(ml[k].x - ms);
+      lq += w * ml[k].y;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += w * __uint_as_float(ov[k][i] << 16);
+          acc[2 * i + 1] += w * __uint_as_float(ov[k][i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += w * __uint_as_float(ov[k][i]);
+      }
+    }
+  }
+  // merge the chunk groups in group order, each rescaled to the common maximum
+  const float M = wave_max(active ? mq : -INFINITY);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  const float f = exp2_hw(mq - Ms);  // a group that saw no key: 2^-inf = 0
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < EPR; ++e) red[q][r * EPR + e] = acc[e] * f;
+    if (r == 0) lred[q] = lq * f;
   }
   __syncthreads();
-  if (t < hd) {
-    float o = psum[t];
-    for (int q = 1; q < P; ++q) o += psum[q * hd + t];
-    Elem<T>::store(out + x_offset(a.out_qx, orow, ocol + t, ld), o * Linv);
+  if (active && q == 0) {
+    float L = lred[0];
+#pragma unroll
+    for (int u = 1; u < QN; ++u) L += lred[u];
+    const float inv = 1.0f / L;
+    float o[EPR];
+#pragma unroll
+    for (int e = 0; e < EPR; ++e) {
+      o[e] = red[0][r * EPR + e];
+#pragma unroll
+      for (int u = 1; u < QN; ++u) o[e] += red[u][r * EPR + e];
+      o[e] *= inv;
+    }
+    // the run's EPR elements are consecutive in the output (row-major or quad layout)
+    u32x4 pk;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = f32x2_to_bf16x2(o[2 * i], o[2 * i + 1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = __float_as_uint(o[i]);
+    }
+    *reinterpret_cast<u32x4*>(out + x_offset(a.out_qx, orow, ocol + r * EPR, ld)) = pk;
   }
 }
 
@@ -390,8 +433,8 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   const int Rall = a.R * (a.hq / a.hkv);
   dim3 grid(a.n_launch, a.hkv, a.B), block(NWAVE * WAVE);
   hipLaunchKernelGGL((attn_kernel<T, HD>), grid, block, 0, st, a);
-  dim3 cgrid(Rall, a.hkv, a.B), cblock(1024);
-  hipLaunchKernelGGL(attn_combine_kernel<T>, cgrid, cblock, 0, st, a);
+  dim3 cgrid(Rall, a.hkv, a.B), cblock(WAVE);
+  hipLaunchKernelGGL((attn_combine_kernel<T, HD>), cgrid, cblock, 0, st, a);
   return hipGetLastError();
 }
 

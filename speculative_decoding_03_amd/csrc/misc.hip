@@ -101,13 +101,37 @@ __global__ void __launch_bounds__(1024) accept_kernel(
       v[j] = -INFINITY;
       idx[j] = 0x7fffffff;
     }
-    for (int p = threadIdx.x; p < n_parts; p += blockDim.x)
+    if (n_parts % 4 == 0 && ld_amax % 4 == 0) {
+      // four consecutive partials per 16-byte load (rows start 16-byte aligned); with n_parts
+      // <= 4 * blockDim every row's loads are in flight together
+      for (int p = 4 * threadIdx.x; p < n_parts; p += 4 * blockDim.x) {
+        f32x4 pv[RG];
+        int4 pi[RG];
 #pragma unroll
-      for (int j = 0; j < RG; ++j)
-        if (i0 + j < R) {
-          const size_t o = (size_t)(b * R + i0 + j) * ld_amax + p;
-          argmax_combine(v[j], idx[j], amax_val[o], amax_idx[o]);
-        }
+        for (int j = 0; j < RG; ++j)
+          if (i0 + j < R) {
+            const size_t o = (size_t)(b * R + i0 + j) * ld_amax + p;
+            pv[j] = *reinterpret_cast<const f32x4*>(amax_val + o);
+            pi[j] = *reinterpret_cast<const int4*>(amax_idx + o);
+          }
+#pragma unroll
+        for (int j = 0; j < RG; ++j)
+          if (i0 + j < R) {
+            argmax_combine(v[j], idx[j], pv[j][0], pi[j].x);
+            argmax_combine(v[j], idx[j], pv[j][1], pi[j].y);
+            argmax_combine(v[j], idx[j], pv[j][2], pi[j].z);
+            argmax_combine(v[j], idx[j], pv[j][3], pi[j].w);
+          }
+      }
+    } else {
+      for (int p = threadIdx.x; p < n_parts; p += blockDim.x)
+#pragma unroll
+        for (int j = 0; j < RG; ++j)
+          if (i0 + j < R) {
+            const size_t o = (size_t)(b * R + i0 + j) * ld_amax + p;
+            argmax_combine(v[j], idx[j], amax_val[o], amax_idx[o]);
+          }
+    }
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
       if (i0 + j >= R) break;  // uniform

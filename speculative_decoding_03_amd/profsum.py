@@ -57,10 +57,24 @@ def _grid(r) -> int:
     return int(float(g))
 
 
+def trace_rows(d: str):
+    """Kernel dispatch rows of a rocprofv3 kernel trace: DIR/*kernel_trace.csv (--output-format
+    csv) or the kernels view of DIR/*results.db (the default SQLite output), with the csv
+    columns Kernel_Name, Dispatch_Id, Start_Timestamp, End_Timestamp and Grid_Size."""
+    csvs = sorted(glob.glob(os.path.join(d, "*kernel_trace.csv")))
+    if csvs:
+        return _rows(csvs[0])
+    import sqlite3
+    db = sqlite3.connect(_one(d, "results.db"))
+    q = "select name, dispatch_id, start, end, grid_x * grid_y * grid_z from kernels"
+    return [{"Kernel_Name": n, "Dispatch_Id": str(i), "Start_Timestamp": str(s),
+             "End_Timestamp": str(e), "Grid_Size": str(g)} for n, i, s, e, g in db.execute(q)]
+
+
 def trace_durations(d: str, match: str, grid: int = 0):
     """Durations (ns) of the dispatches whose kernel name contains `match` (and whose grid has
     `grid` work-items, when given), in dispatch order."""
-    rows = [r for r in _rows(_one(d, "kernel_trace.csv")) if match in short_name(r["Kernel_Name"])
+    rows = [r for r in trace_rows(d) if match in short_name(r["Kernel_Name"])
             and (not grid or _grid(r) == grid)]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
@@ -123,7 +137,7 @@ def cmd_stats(a) -> int:
 def cmd_step(a) -> int:
     """Kernels of one target pass (embed_kernel through accept_kernel), grouped by kernel and grid,
     with the gaps between consecutive kernels."""
-    rows = _rows(_one(a.dir, "kernel_trace.csv"))
+    rows = trace_rows(a.dir)
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     starts = [i for i, r in enumerate(rows) if "embed_kernel" in r["Kernel_Name"]]
     s = starts[a.index]

@@ -286,6 +286,38 @@ int specdec_moe_usage_read(specdec_ctx* ctx, int32_t* per_layer, void* stream);
 int specdec_query_split(specdec_ctx* ctx, int32_t kernel_class, int32_t* splits, int32_t* units,
                         int32_t* waves, int32_t* groups);
 
+/* Draft-length policy (host code, no device work): picks the next step's K from the running
+   acceptance and the measured step costs.  The pages give the best draft length as a property of
+   the hardware and the text (two drafted tokens on one consumer GPU, one on a slower one; more
+   gain on predictable text): "Gemma 4's MTP drafter explained", sections "Tip: start with two
+   drafted tokens" and "Why use a drafter?".
+   Acceptance: a step that drafted K and emitted n (n_emit) accepted m = n - 1 drafts, and saw a
+   disagreement iff m < K; the estimate is p = (A + a0) / (A + R + a0 + r0) with A, R the sums of
+   m and of [m < K] over past steps, each decayed by `decay` per step, and a0, r0 the prior
+   pseudo-counts.  Choice: the K in [k_min, k_max] maximising (1 + p + ... + p^K) /
+   (K * t_draft_ms + t_verify_ms + K * t_row_ms), the smallest K on a tie.  t_draft_ms is one
+   drafter sub-step, t_verify_ms a one-row verify (decode) step, t_row_ms each further row.
+   The struct is caller memory; init fills every field. */
+typedef struct {
+  int32_t k_min, k_max;
+  float decay, prior_accepted, prior_rejected;
+  float t_draft_ms, t_verify_ms, t_row_ms;
+  double accepted, rejected; /* decayed counts */
+} specdec_k_policy;
+
+/* Errors: SPECDEC_E_INVAL (k_min < 1, k_max < k_min, decay outside (0, 1], non-positive prior,
+   negative or non-finite times, t_verify_ms <= 0). */
+int specdec_k_policy_init(specdec_k_policy* pol, int32_t k_min, int32_t k_max, float decay,
+                          float prior_accepted, float prior_rejected, float t_draft_ms,
+                          float t_verify_ms, float t_row_ms);
+/* Records one step that drafted K per sequence: n_emit (host int32 [B]) as specdec_accept
+   returned it.  Errors: SPECDEC_E_INVAL (null, B < 1, K < 1, an n_emit outside [1, K+1]). */
+int specdec_k_policy_observe(specdec_k_policy* pol, int32_t K, const int32_t* n_emit, int32_t B);
+/* The current acceptance estimate p (-1 for a null policy). */
+double specdec_k_policy_acceptance(const specdec_k_policy* pol);
+/* The draft length for the next step (or SPECDEC_E_INVAL for a null policy). */
+int32_t specdec_k_policy_choose(const specdec_k_policy* pol);
+
 const char* specdec_error_string(int code);
 
 #ifdef __cplusplus

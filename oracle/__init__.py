@@ -16,3 +16,4 @@ pins (tests/test_oracle_drafter.py); the pages print no worked example.
 """
 
 from .model import *  # noqa: F401,F403
+from .policy import KPolicy, expected_tokens  # noqa: F401

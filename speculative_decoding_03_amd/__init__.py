@@ -11,7 +11,7 @@ from ._ffi import (ACCEPT_COMMIT, BF16, F32, HEAD_CLUSTERED, HEAD_FULL, SpecdecE
 
 def __getattr__(name):
     # the torch-based binding is imported lazily so that the ctypes layer loads without torch
-    if name in ("Engine", "DeviceModel", "Shape", "pack_matrix"):
+    if name in ("Engine", "DeviceModel", "Shape", "pack_matrix", "KPolicy"):
         from . import engine
         return getattr(engine, name)
     raise AttributeError(name)

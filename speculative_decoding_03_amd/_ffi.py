@@ -27,7 +27,8 @@ EXPORTS = [
     "specdec_draft", "specdec_draft_traced", "specdec_verify", "specdec_accept", "specdec_kv_commit",
     "specdec_pack_matrix", "specdec_set_len_bound", "specdec_read_device_error",
     "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
-    "specdec_moe_usage_start", "specdec_moe_usage_read",
+    "specdec_moe_usage_start", "specdec_moe_usage_read", "specdec_k_policy_init",
+    "specdec_k_policy_observe", "specdec_k_policy_acceptance", "specdec_k_policy_choose",
 ]
 
 
@@ -48,6 +49,13 @@ class Weights(C.Structure):
         ("w_in", C.c_void_p), ("d_layers", C.POINTER(C.c_void_p)), ("norm_f", C.c_void_p),
         ("w_back", C.c_void_p),
     ]
+
+
+class KPolicy(C.Structure):
+    _fields_ = [("k_min", C.c_int32), ("k_max", C.c_int32), ("decay", C.c_float),
+                ("prior_accepted", C.c_float), ("prior_rejected", C.c_float),
+                ("t_draft_ms", C.c_float), ("t_verify_ms", C.c_float), ("t_row_ms", C.c_float),
+                ("accepted", C.c_double), ("rejected", C.c_double)]
 
 
 class DraftTrace(C.Structure):
@@ -89,6 +97,11 @@ def load(path: str = LIB_PATH):
         "specdec_profile_read": (C.c_int, [vp, P(C.c_float), i32, P(i32)]),
         "specdec_query_split": (C.c_int, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
         "specdec_error_string": (C.c_char_p, [C.c_int]),
+        "specdec_k_policy_init": (C.c_int, [P(KPolicy), i32, i32, C.c_float, C.c_float, C.c_float,
+                                            C.c_float, C.c_float, C.c_float]),
+        "specdec_k_policy_observe": (C.c_int, [P(KPolicy), i32, P(i32), i32]),
+        "specdec_k_policy_acceptance": (C.c_double, [P(KPolicy)]),
+        "specdec_k_policy_choose": (C.c_int32, [P(KPolicy)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

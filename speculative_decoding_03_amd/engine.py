@@ -330,3 +330,30 @@ class Engine:
             self.close()
         except Exception:
             pass
+
+
+class KPolicy:
+    """The library's draft-length policy (specdec_k_policy_*): host code, no device work."""
+
+    def __init__(self, k_min: int, k_max: int, t_draft_ms: float, t_verify_ms: float,
+                 t_row_ms: float, decay: float = 0.9, prior_accepted: float = 1.0,
+                 prior_rejected: float = 1.0):
+        self.lib = F.load()
+        self.s = F.KPolicy()
+        F.check(self.lib.specdec_k_policy_init(C.byref(self.s), k_min, k_max, decay,
+                                               prior_accepted, prior_rejected, t_draft_ms,
+                                               t_verify_ms, t_row_ms), "specdec_k_policy_init")
+
+    def observe(self, K: int, n_emit) -> None:
+        arr = (C.c_int32 * len(n_emit))(*[int(n) for n in n_emit])
+        F.check(self.lib.specdec_k_policy_observe(C.byref(self.s), K, arr, len(n_emit)),
+                "specdec_k_policy_observe")
+
+    def acceptance(self) -> float:
+        return float(self.lib.specdec_k_policy_acceptance(C.byref(self.s)))
+
+    def choose(self) -> int:
+        k = int(self.lib.specdec_k_policy_choose(C.byref(self.s)))
+        if k < 0:
+            F.check(k, "specdec_k_policy_choose")
+        return k

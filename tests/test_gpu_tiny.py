@@ -155,6 +155,54 @@ def test_spec_equals_greedy_at_every_draft_length(name):
     eng.close()
 
 
+@pytest.mark.parametrize("p", [0.0, 0.6, 1.0])
+def test_adaptive_draft_length_reproduces_greedy(tiny, p):
+    """Speculative steps whose draft length the library's policy picks from the running
+    acceptance (K between 1 and 6, changing step to step) reproduce the same GPU's greedy
+    output; at p = 1 the policy climbs to the longest draft, at p = 0 it stays at the shortest."""
+    CFG = tiny["cfg"]
+    eng = build_engine(CFG.replace(draft_k=6), MAX_CTX)
+    try:
+        prompt = prompt_tokens(CFG)[0]
+        t0, _ = gpu_prefill(eng, prompt, want_logits=False)
+        n, kmax = 48, 6
+        L = len(prompt)
+        snap = snapshot(eng)
+        ref = gpu_greedy(eng, t0, n + kmax + 2)
+        restore(eng, snap)
+        gseq = np.full(MAX_CTX, -1, dtype=np.int64)
+        gseq[L:L + len(ref)] = ref
+        dev = eng.kv_k.device
+        tabs = {K: torch.from_numpy(inject_table(gseq, K, p, CFG.inject_seed).reshape(1, -1)).to(dev)
+                for K in range(1, kmax + 1)}
+        pol = SD.KPolicy(1, kmax, t_draft_ms=0.05, t_verify_ms=1.0, t_row_ms=0.02, decay=0.8)
+        cur = torch.tensor([t0], dtype=torch.int32, device=dev)
+        toks, ks = [t0], []
+        while len(toks) < n:
+            K = pol.choose()
+            ks.append(K)
+            drafts = torch.empty(1, K, dtype=torch.int32, device=dev)
+            T = torch.empty(1, K + 1, dtype=torch.int32, device=dev)
+            out = torch.empty(1, K + 1, dtype=torch.int32, device=dev)
+            n_emit = torch.empty(1, dtype=torch.int32, device=dev)
+            eng.draft(cur, drafts, inject=tabs[K], verify_tokens=T)
+            eng.verify(T)
+            eng.accept(T, out_tokens=out, n_emit=n_emit, next_tok=cur, commit=True)
+            e = int(n_emit.item())
+            pol.observe(K, [e])
+            toks.extend(out[0, :e].cpu().tolist())
+            eng.set_len_bound([int(eng.len[0].item())])
+        assert toks[:n] == ref[:n]
+        if p == 1.0:
+            assert ks[-1] == kmax
+        if p == 0.0:
+            assert ks[-1] == 1
+        assert len(set(ks)) > 1 or p == 0.0
+        assert eng.device_error() == 0
+    finally:
+        eng.close()
+
+
 @pytest.mark.parametrize("mode,k_c", [("clustered", 1), ("clustered", 3), ("clustered", 64), ("full", 0)])
 def test_drafter_matches_oracle(tiny, mode, k_c):
     CFG = tiny["cfg"]

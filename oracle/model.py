@@ -31,6 +31,8 @@ __all__ = [
     "greedy_generate", "prefill", "verify", "accept", "commit", "token_scores",
     "centroid_scores", "head_full",
     "head_clustered", "drafter_substep", "draft", "inject", "spec_generate", "SpecStats",
+    "tree_parents", "tree_path", "head_top", "draft_tree", "inject_tree", "verify_tree",
+    "accept_tree", "commit_tree", "spec_generate_tree",
 ]
 
 
@@ -425,6 +427,148 @@ def spec_generate(W: dict, DW: dict, cfg, cache: KVCache, t0: int, hid: np.ndarr
         toks.extend(out)
         st.steps += 1
         st.proposed += K
+        st.accepted += m
+        st.emitted_per_step.append(m + 1)
+    return toks[:n], st
+
+
+# ---------------------------------------------------------------------------
+# Token trees.  Standard speculative decoding bets on one future path; the Pixel
+# page's "Future directions" describe letting the drafter explore branching
+# possibilities in parallel so a long sequence is accepted more often when the
+# context is uncertain.  Reading: the first drafter sub-step's `width` best
+# tokens start `width` branches, each continued greedily for `depth` tokens;
+# the target scores every node as the next token after its root-to-node path;
+# acceptance follows, from the root, the child equal to the target's token.
+# ---------------------------------------------------------------------------
+
+def tree_parents(width: int, depth: int) -> list:
+    """Parent of every node of the width x depth branch tree, in node order: node 0 is the
+    root; node 1 + width*(j-1) + k is the j-th token of branch k."""
+    par = [-1]
+    for j in range(1, depth + 1):
+        for k in range(width):
+            par.append(0 if j == 1 else 1 + width * (j - 2) + k)
+    return par
+
+
+def tree_path(parent, i: int) -> list:
+    """Nodes from the root to node i (both included)."""
+    path = [i]
+    while parent[path[-1]] >= 0:
+        path.append(parent[path[-1]])
+    return path[::-1]
+
+
+def head_top(DW: dict, s: np.ndarray, width: int, head_mode: str = "clustered", k_c: int = 1) -> list:
+    """The `width` best tokens among those the head scores (the members of the k_c best clusters,
+    or every token), by score and then lower vocabulary id."""
+    table = DW["table"]
+    if head_mode == "full":
+        cand = np.arange(table.shape[0])
+    else:
+        Nc = DW["centroids"].shape[0]
+        S = table.shape[0] // Nc
+        z = centroid_scores(DW["centroids"], s)
+        sel = sorted(range(Nc), key=lambda c: (-z[c], c))[:k_c]
+        cand = np.concatenate([DW["perm"][c * S:(c + 1) * S] for c in sel])
+    sc = token_scores(table[cand], s)
+    if np.isnan(sc).any():
+        raise FloatingPointError("NaN in drafter scores")
+    order = sorted(range(len(cand)), key=lambda i: (-sc[i], int(cand[i])))
+    return [int(cand[i]) for i in order[:width]]
+
+
+def draft_tree(DW: dict, cfg, cache: KVCache, hid: np.ndarray, c0: int, length: int, width: int,
+               depth: int, head_mode: str = "clustered", k_c: int = 1) -> list:
+    """Tokens of every node of a width x depth tree draft, in node order (node 0 = c0)."""
+    st = []
+    _, h1 = drafter_substep(DW, cfg, cache, hid, c0, length, length, head_mode, k_c, st)
+    firsts = head_top(DW, st[0], width, head_mode, k_c)
+    toks = [int(c0)] + firsts
+    branches = [[t] for t in firsts]
+    hs = [h1] * width
+    for j in range(2, depth + 1):
+        for k in range(width):
+            d, hs[k] = drafter_substep(DW, cfg, cache, hs[k], branches[k][-1], length + j - 1,
+                                       length, head_mode, k_c)
+            branches[k].append(d)
+        toks.extend(branches[k][-1] for k in range(width))
+    return toks
+
+
+def inject_tree(tokens, parent, greedy_seq, length: int, p: float, seed: int, b: int = 0) -> list:
+    """Workload injection for a tree: the node at depth j in slot s = node - 1 becomes
+    greedy_seq[length + j] when its draw (the linear one with slot s + 1 for j) is below p."""
+    out = list(tokens)
+    thr = inject_threshold(p)
+    depth = [0] * len(parent)
+    for i in range(1, len(parent)):
+        depth[i] = depth[parent[i]] + 1
+        if inject_draw(seed, b, length + depth[i], i) < thr:
+            out[i] = int(greedy_seq[length + depth[i]])
+    return out
+
+
+def verify_tree(W: dict, cfg, cache: KVCache, length: int, tokens, parent):
+    """Every node of a tree scored by the target as plain decoding of its root-to-node path would
+    score it (the path's tokens at positions length, length + 1, ...).  Returns (G, H, logits)
+    per node; the cache is not changed."""
+    G, H, Ls = [], [], []
+    for i in range(len(tokens)):
+        c = cache.copy()
+        logits = hidden = None
+        for j, node in enumerate(tree_path(parent, i)):
+            logits, hidden = target_row(W, cfg, c, int(tokens[node]), length + j)
+        G.append(argmax_first(logits))
+        H.append(hidden)
+        Ls.append(logits)
+    return G, H, Ls
+
+
+def accept_tree(tokens, parent, G):
+    """The longest root path on which every node's token is the target's choice at its parent
+    (the tree's longest agreeing draft); among equally long paths the one with the lower node
+    index at the first place they differ.  Written as a search over every node's root path.
+    Returns (m, emitted = the path's tokens + [G at its last node], next, path nodes)."""
+    best = []
+    for i in range(len(tokens)):
+        path = tree_path(parent, i)
+        if all(int(tokens[path[j]]) == int(G[path[j - 1]]) for j in range(1, len(path))):
+            cand = path[1:]
+            if len(cand) > len(best) or (len(cand) == len(best) and cand < best):
+                best = cand
+    end = best[-1] if best else 0
+    out = [int(tokens[n]) for n in best] + [int(G[end])]
+    return len(best), out, int(G[end]), best
+
+
+def commit_tree(W: dict, cfg, cache: KVCache, length: int, tokens, nodes, H):
+    """The committed state after accepting a tree path: the root's and the path's keys and values
+    at positions length .. length + m (what plain decoding of those tokens writes), the length
+    grown by m + 1 and the hidden of the path's last node."""
+    for j, node in enumerate([0] + list(nodes)):
+        target_row(W, cfg, cache, int(tokens[node]), length + j)
+    return length + len(nodes) + 1, H[nodes[-1] if nodes else 0]
+
+
+def spec_generate_tree(W: dict, DW: dict, cfg, cache: KVCache, t0: int, hid: np.ndarray,
+                       length: int, n: int, width: int, depth: int, greedy_seq=None, p: float = 0.0,
+                       seed: int = 0, head_mode: str = "clustered", k_c: int = 1, b: int = 0):
+    """The speculative loop with tree drafts: draft_tree -> (inject) -> verify_tree -> accept_tree
+    -> commit, until n tokens (t0 first; the last step truncated)."""
+    parent = tree_parents(width, depth)
+    toks, cur, st = [int(t0)], int(t0), SpecStats()
+    while len(toks) < n:
+        T = draft_tree(DW, cfg, cache, hid, cur, length, width, depth, head_mode, k_c)
+        if greedy_seq is not None:
+            T = inject_tree(T, parent, greedy_seq, length, p, seed, b)
+        G, H, _ = verify_tree(W, cfg, cache, length, T, parent)
+        m, out, cur, nodes = accept_tree(T, parent, G)
+        length, hid = commit_tree(W, cfg, cache, length, T, nodes, H)
+        toks.extend(out)
+        st.steps += 1
+        st.proposed += depth
         st.accepted += m
         st.emitted_per_step.append(m + 1)
     return toks[:n], st

@@ -233,12 +233,62 @@ int specdec_draft_traced(specdec_ctx* ctx, int32_t B, int32_t K, int32_t head_mo
 int specdec_verify(specdec_ctx* ctx, int32_t B, int32_t n_rows, const int32_t* tokens,
                    float* logits, int32_t* argmax, void* stream);
 
+/* ---- Token trees: several drafted continuations verified in one target pass ----
+   Standard speculative decoding bets on one future path; the pages describe letting the drafter
+   explore branching possibilities in parallel so that a long sequence is accepted more often in
+   uncertain contexts ("Accelerating Gemini Nano on Pixel with frozen multi-token prediction",
+   section "Future directions").  A tree has n_nodes <= max_rows nodes in topological order given
+   by a host array parent[n_nodes]: parent[0] = -1 (the root: the current token, not yet in the
+   cache) and 0 <= parent[i] < i; the depth of a node (its parent's plus one) is at most
+   SPECDEC_TREE_MAX_DEPTH.  Node i of sequence b is the token at position len[b] + depth(i); during
+   the verify its key and value sit in cache slot len[b] + i, and it attends to the committed
+   prefix [0, len[b]) and the slots of its ancestors and itself. */
+#define SPECDEC_TREE_MAX_DEPTH 16
+#define SPECDEC_TREE_MAX_WIDTH 16
+
+/* Drafts a tree of `width` branches of `depth` tokens per sequence: the first sub-step's `width`
+   best tokens (highest score, then lower vocabulary id, among the tokens the head scores: the
+   members of the k_c selected clusters, or the whole vocabulary) start the branches; each branch
+   then continues greedily with its own tokens and hidden states (sub-step j of every branch reads
+   the same committed keys [0, len) and queries at position len + j - 1).  Output tree_tokens int32
+   [B][1 + width*depth] (device) in node order: node 0 = cur_tok, node 1 + width*(j-1) + k = the
+   j-th token of branch k, whose parent is node 1 + width*(j-2) + k (j >= 2) or the root (j = 1).
+   Optional injection (tests and benchmarks): entry (len[b] + j) * (width*depth) + (node - 1) of
+   inject [B][inj_stride], when >= 0, replaces the node's token after drafting (the branch
+   continues from its own token).  Errors: SPECDEC_E_INVAL (width or depth outside [1, 16],
+   1 + width*depth > max_rows, B*width > max_batch*max_rows, bad head arguments, null pointers),
+   SPECDEC_E_CAPACITY (the host-side bound of len + depth exceeds max_ctx). */
+int specdec_draft_tree(specdec_ctx* ctx, int32_t B, int32_t width, int32_t depth, int32_t head_mode,
+                       int32_t k_c, const int32_t* cur_tok, int32_t* tree_tokens,
+                       const int32_t* inject, int64_t inj_stride, void* stream);
+
+/* specdec_verify over the nodes of a tree: tokens int32 [B][n_nodes] (device), positions and
+   visibility as described above; logits / argmax as for specdec_verify, per node.  Errors:
+   SPECDEC_E_INVAL (a malformed tree, n_nodes > max_rows), SPECDEC_E_CAPACITY (host-side bound of
+   len + n_nodes exceeds max_ctx). */
+int specdec_verify_tree(specdec_ctx* ctx, int32_t B, int32_t n_nodes, const int32_t* parent,
+                        const int32_t* tokens, float* logits, int32_t* argmax, void* stream);
+
+/* Acceptance after specdec_verify_tree of the same tree: G[i] = argmax of node i (lowest id on
+   ties); the accepted path is the longest root path on which every node's token equals G at its
+   parent (among equally long ones, the lower node index at the first place they differ);
+   out_tokens[b] (int32 [B][out_ld], out_ld >= tree depth + 1) = the tokens of its m nodes, then
+   G at its last node, then -1; n_emit[b] = m + 1; next_tok[b] = G at
+   the last node.  With SPECDEC_ACCEPT_COMMIT also len[b] += m + 1, hid[b] = hidden of the last
+   node, and the path's cache entries are moved to slots len + 1 .. len + m (in every layer), so
+   the cache again holds exactly the accepted sequence.  Errors: SPECDEC_E_INVAL (a different
+   tree or batch than the last verify, out_ld too small, null pointers). */
+int specdec_accept_tree(specdec_ctx* ctx, int32_t B, int32_t n_nodes, const int32_t* parent,
+                        const int32_t* tokens, int32_t* out_tokens, int32_t out_ld,
+                        int32_t* n_emit, int32_t* next_tok, uint32_t flags, void* stream);
+
 /* Acceptance after a verify of K+1 rows per sequence (tokens = [c0, d1..dK], the verify input).
    One fused kernel per call: G[i] = argmax of row i (lowest id on ties); m = largest j <= K with
    tokens[1..j] == G[0..j-1]; out_tokens[b] = tokens[1..m], G[m], then -1 padding (int32
    [B][K+1]); n_emit[b] = m+1; next_tok[b] = G[m].  With SPECDEC_ACCEPT_COMMIT the same kernel
    also commits: len[b] += m+1 and hid[b] = hidden of row m.  Any output pointer may be NULL.
-   Errors: SPECDEC_E_INVAL (K+1 != rows of the last verify, B != its batch). */
+   Errors: SPECDEC_E_INVAL (K+1 != rows of the last verify, B != its batch, the last verify was a
+   tree's). */
 int specdec_accept(specdec_ctx* ctx, int32_t B, int32_t K, const int32_t* tokens,
                    int32_t* out_tokens, int32_t* n_emit, int32_t* next_tok, uint32_t flags,
                    void* stream);

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libspecdec.so")
 
 OK, E_INVAL, E_CAPACITY, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4
 STATIC_WORKSPACE_BYTES = 64 << 20  # SPECDEC_STATIC_WORKSPACE_BYTES
+TREE_MAX_DEPTH = TREE_MAX_WIDTH = 16
 F32, BF16 = 0, 1
 HEAD_CLUSTERED, HEAD_FULL = 0, 1
 ACCEPT_COMMIT = 1
@@ -24,7 +25,8 @@ DW_N1, DW_Q, DW_O, DW_N2, DW_GATE_UP, DW_DOWN, N_DRAFT_TENSORS = range(7)
 EXPORTS = [
     "specdec_workspace_bytes", "specdec_kv_elems", "specdec_create", "specdec_create_static",
     "specdec_destroy",
-    "specdec_draft", "specdec_draft_traced", "specdec_verify", "specdec_accept", "specdec_kv_commit",
+    "specdec_draft", "specdec_draft_traced", "specdec_draft_tree", "specdec_verify",
+    "specdec_verify_tree", "specdec_accept_tree", "specdec_accept", "specdec_kv_commit",
     "specdec_pack_matrix", "specdec_set_len_bound", "specdec_read_device_error",
     "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
     "specdec_moe_usage_start", "specdec_moe_usage_read", "specdec_k_policy_init",
@@ -88,6 +90,9 @@ def load(path: str = LIB_PATH):
         "specdec_moe_usage_start": (C.c_int, [vp, vp]),
         "specdec_moe_usage_read": (C.c_int, [vp, P(i32), vp]),
         "specdec_verify": (C.c_int, [vp, i32, i32, vp, vp, vp, vp]),
+        "specdec_draft_tree": (C.c_int, [vp, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp]),
+        "specdec_verify_tree": (C.c_int, [vp, i32, i32, P(i32), vp, vp, vp, vp]),
+        "specdec_accept_tree": (C.c_int, [vp, i32, i32, P(i32), vp, vp, i32, vp, vp, u32, vp]),
         "specdec_accept": (C.c_int, [vp, i32, i32, vp, vp, vp, vp, u32, vp]),
         "specdec_kv_commit": (C.c_int, [vp, i32, vp, vp]),
         "specdec_pack_matrix": (C.c_int, [vp, vp, i32, i32, i32, i32, i32, i32, vp]),

@@ -170,7 +170,7 @@ attn_kernel(AttnArgs a) {
   // every load above is issued before any instruction that waits for one of them
   __builtin_amdgcn_sched_barrier(0);
   const int len = len_in;
-  const int end_max = len + a.R - 1 + a.key_off;  // keys [0, end_max) are read by some row
+  const int end_max = attn_key_end(a.vis, len, a.R, a.key_off);  // keys some row may see
   if (end_max > a.max_ctx || len < 0) {
     if (chunk == 0 && g == 0 && threadIdx.x == 0) raise_error(a.err, ERRBIT_CAPACITY);
     return;
@@ -196,7 +196,10 @@ attn_kernel(AttnArgs a) {
       }
     // the tile after next reuses this tile's buffer once its scores are done
     if (q0 + 32 < Rall) load_q(q0 + 32, qf);
-    const int kend = qv < Rall ? len + row + a.key_off : 0;  // keys [0, kend) are visible
+    // keys [0, kend) are visible, and in a tree verify slot len + j for each bit j of tmask
+    const int kend = qv >= Rall ? 0 : (a.vis == VIS_CAUSAL ? len + row + a.key_off
+                                                           : (a.vis == VIS_FLAT ? len + a.key_off : len));
+    const uint64_t tmask = a.vis == VIS_TREE && qv < Rall ? a.tree_mask[row] : 0ull;
     // scores in base-2 units (scale * log2 e folded in): exp(x - m) = exp2(x2 - m2)
     float m = -INFINITY;
 #pragma unroll
@@ -206,7 +209,9 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int key = kw0 + nb * 32 + 8 * grp + 4 * h + v;
-          const float val = key < kend ? s[nb][h][v] * scale2 : -INFINITY;
+          const unsigned tj = (unsigned)(key - len);  // slot of a tree node (when < 64)
+          const bool vis = key < kend || (tj < 64u && ((tmask >> tj) & 1ull));
+          const float val = vis ? s[nb][h][v] * scale2 : -INFINITY;
           s[nb][h][v] = val;
           m = fmaxf(m, val);
         }
@@ -347,7 +352,7 @@ __global__ void __launch_bounds__(WAVE) attn_combine_kernel(AttnArgs a) {
     }
     if (n_act < 0) {
       const int len = len_in;
-      const int end_max = len + a.R - 1 + a.key_off;
+      const int end_max = attn_key_end(a.vis, len, a.R, a.key_off);
       if (end_max > a.max_ctx || len < 0) return;
       n_act = (end_max + a.chunk - 1) / a.chunk;
       if (n_act > a.n_launch) {  // the device length is beyond the host-side bound

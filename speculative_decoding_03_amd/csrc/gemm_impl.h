@@ -118,7 +118,8 @@ template <int MT, int NU> struct EpiPre {
   float wn[NU];
   float res[NU][MT][4];
   float2 cs[NU][MT][4];  // rotary (cos, sin) of the lane's pair at each row's position
-  int pos[MT][4];
+  int pos[MT][4];        // rotary position of each row
+  int slot[MT][4];       // its cache slot (the position, except for a tree verify's nodes)
 };
 
 template <int MT, int NU, int EPI>
@@ -146,7 +147,11 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int l
       for (int v = 0; v < 4; ++v) {
         const int m = local_row(narrow, mt, v, lane);
         const int b = m < a.M ? m / a.rows_per_seq : 0;
-        pre.pos[mt][v] = a.len[b] + (m - b * a.rows_per_seq) + a.pos_off;
+        const int r = m < a.M ? m - b * a.rows_per_seq : 0;  // row within its sequence
+        const int len = a.len[b];
+        pre.slot[mt][v] = len + r + a.pos_off;
+        pre.pos[mt][v] = a.pos_mode == POS_FLAT ? len + a.pos_off
+                         : (a.pos_mode == POS_TREE ? len + a.tree_depth[r & 63] : len + r + a.pos_off);
       }
     const int half = a.hd >> 1;
 #pragma unroll
@@ -343,7 +348,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           const float partner = dpp_f32<DPP_XOR1>(val);  // the other element of the rotary pair
           if (m < a.M) {
             const int b = m / a.rows_per_seq;
-            const int pos = pre.pos[mt][v];
+            const int pos = pre.pos[mt][v], slot = pre.slot[mt][v];
             float y = val;
             if (rot) {
               const float cs = pre.cs[t][mt][v].x, sn = pre.cs[t][mt][v].y;
@@ -357,15 +362,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
             }
             if (hh < a.hq) {
               Elem<T>::store(reinterpret_cast<T*>(a.qout) + ((size_t)m * a.hq + hh) * a.hd + dim, y);
-            } else if (pos >= a.max_ctx || pos < 0) {
-              // no cache slot: nothing is written
+            } else if (slot >= a.max_ctx || slot < 0) {
+              raise_error(a.err, ERRBIT_CAPACITY);  // no cache slot: nothing is written
             } else {
               // K is stored [pos][hd], V transposed [hd][pos]
               const bool isk = hh < a.hq + a.hkv;
               const int g = isk ? hh - a.hq : hh - a.hq - a.hkv;
               T* cache = reinterpret_cast<T*>(isk ? a.kcache : a.vcache) + (size_t)b * a.cache_b_stride;
-              const size_t off = isk ? ((size_t)g * a.max_ctx + pos) * a.hd + dim
-                                     : ((size_t)g * a.hd + dim) * a.max_ctx + pos;
+              const size_t off = isk ? ((size_t)g * a.max_ctx + slot) * a.hd + dim
+                                     : ((size_t)g * a.hd + dim) * a.max_ctx + slot;
               Elem<T>::store(cache + off, y);
             }
           }

@@ -84,6 +84,11 @@ struct GemmArgs {
   int cache_b_stride = 0;  // elements between sequences in one layer's cache = hkv*max_ctx*hd
   float theta = 10000.f;
   const float2* rope_cs = nullptr;  // EPI_ROPE: [max_ctx][hd/2] (cos, sin) (launch_rope_table)
+  // EPI_ROPE positions of row r of a sequence: POS_LINEAR len + r + pos_off (rotary angle and
+  // cache slot); POS_FLAT len + pos_off for every row (the drafter's branches, no cache write);
+  // POS_TREE angle at len + tree_depth[r], cache slot len + r (a tree verify's nodes)
+  int pos_mode = 0;
+  uint8_t tree_depth[64] = {};
   // EPI_SILU: hout[m][f] = silu(gate) * up, gate/up tiles interleaved
   void* hout = nullptr;
   int ldh = 0;
@@ -125,9 +130,22 @@ struct AttnArgs {
   int cache_b_stride = 0;
   int chunk = 256;
   int n_chunks = 0;  // chunks per head in the partial buffer = ceil(max_ctx / chunk)
-  int n_launch = 0;  // chunks launched: covers the host-side bound on len + R - 1 + key_off
+  int n_launch = 0;  // chunks launched: covers the host-side bound on the keys any row sees
   float scale = 0.f;
+  // Keys row i of a sequence sees: VIS_CAUSAL [0, len + i + key_off) (verify rows, the drafter's
+  // single row); VIS_FLAT [0, len + key_off) for every row (the drafter's branches of a tree
+  // draft); VIS_TREE [0, len) and slot len + j for every bit j of tree_mask[i] (a tree verify:
+  // node i sees its ancestors and itself, each at slot len + node index).
+  int vis = 0;
+  uint64_t tree_mask[64] = {};
 };
+enum { VIS_CAUSAL = 0, VIS_FLAT = 1, VIS_TREE = 2 };
+enum { POS_LINEAR = 0, POS_FLAT = 1, POS_TREE = 2 };
+
+// Keys [0, end) hold every key some row of the call may see.
+__host__ __device__ inline int attn_key_end(int vis, int len, int R, int key_off) {
+  return vis == VIS_FLAT ? len + key_off : (vis == VIS_TREE ? len + R : len + R - 1 + key_off);
+}
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 int attention_chunk(int head_dim);          // keys per chunk (fixed per head size)
@@ -146,7 +164,24 @@ hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid
 hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
                               int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
                               const float* norm_e, int d, int Dd, float eps, void* u, int u_qx,
-                              int B, int* err, hipStream_t st);
+                              int B, int* err, hipStream_t st, int h_div = 1);
+// Tree drafts (misc.hip): the first level's top-w tokens, the later levels' per-branch tokens,
+// the acceptance walk over a tree and the compaction of the accepted path's cache entries.
+hipError_t launch_tree_top(const float* scores, int vocab, const int* unit_tile, int units_per_seq,
+                           int rows_per_unit, const int* row_vocab, int B, int w, int D,
+                           const int* cur_tok, const int* len, const int* inject, int inj_stride,
+                           int* tree_tok, int* raw, int* err, hipStream_t st);
+hipError_t launch_tree_finalize(const float* amax_val, const int* amax_idx, int ld_amax, int parts,
+                                int seq_offset, int rows, int w, int D, int depth, const int* len,
+                                const int* inject, int inj_stride, int* tree_tok, int* raw,
+                                int* err, hipStream_t st);
+hipError_t launch_tree_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
+                              int B, int n_nodes, const int8_t* parent, const int* tokens,
+                              int* out_tokens, int out_ld, int* n_emit, int* next_tok, int commit,
+                              int* len, float* hid, const float* X, int d, int* path, int* err,
+                              hipStream_t st);
+hipError_t launch_kv_compact(int dtype, void* kc, void* vc, const int* path, int L, int B,
+                             int Bmax, int hkv, int hd, int max_ctx, hipStream_t st);
 // Mixture-of-experts routing of M rows over E experts (logits [M][E]): the top_k experts of
 // each row (ties -> lower id), softmax weights over them, and the per-expert row maps of the
 // grouped GEMMs: for expert e and its i-th routed row m (ascending m), xrow[e*M+i] = m,

@@ -199,13 +199,13 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
                                                           const int* vocab_row, int vocab,
                                                           const float* norm_h, const float* norm_e,
                                                           int d, int Dd, float eps, T* u, int u_qx,
-                                                          int* err) {
+                                                          int h_div, int* err) {
   constexpr int HV = 8;
   __shared__ float red[2][16];
   __shared__ float ebuf[1024];
   const int b = blockIdx.x, t = threadIdx.x;
   const int lane = t & (WAVE - 1), wid = t >> 6;
-  const float* hb = h + (size_t)b * d;
+  const float* hb = h + (size_t)(b / h_div) * d;  // h_div rows share one hidden input
   const bool hreg = d % 4 == 0 && d <= 4 * HV * (int)blockDim.x;
   f32x4 hv[HV];
   if (hreg) {
@@ -489,6 +489,227 @@ __global__ void pack_kernel(const T* src, T* dst, int N, int Kd, int kind, int h
   }
 }
 
+// ---- tree drafts ----
+
+// Inject-or-keep of one drafted tree node: the table entry (len + depth) * n_slots + slot, when
+// it lies in the table and is not -1, replaces the token shown to the verify.
+__device__ __forceinline__ int inject_node(const int* inject, int inj_stride, int b, int len,
+                                           int depth, int n_slots, int slot, int tok) {
+  if (!inject) return tok;
+  const long long e = (long long)(len + depth) * n_slots + slot;
+  if (e < 0 || e >= inj_stride) return tok;
+  const int r = inject[(size_t)b * inj_stride + e];
+  return r >= 0 ? r : tok;
+}
+
+// The first level of a tree draft: the w best tokens of sequence b among the rows the head scored
+// (scores[b][row], by table row): for the clustered head the units_per_seq listed units of
+// sequence b (unit_tile[b*units_per_seq + i] = first tile, rows_per_unit rows each), for the full
+// head (unit_tile null) every row.  Ranked by score, then lower vocabulary id.  Writes the tree's
+// root (the current token) and nodes 1..w (after injection), and the branches' raw tokens (the
+// next sub-step's inputs).
+__global__ void __launch_bounds__(1024) tree_top_kernel(
+    const float* scores, int vocab, const int* unit_tile, int units_per_seq, int rows_per_unit,
+    const int* row_vocab, int w, int D, const int* cur_tok, const int* len, const int* inject,
+    int inj_stride, int* tree_tok, int* raw, int* err) {
+  __shared__ float rv[16];
+  __shared__ int ri[16];
+  __shared__ int chosen[16];
+  const int b = blockIdx.x;
+  const int n_rows = unit_tile ? units_per_seq * rows_per_unit : vocab;
+  const float* sc = scores + (size_t)b * vocab;
+  const int n_nodes = 1 + w * D;
+  for (int k = 0; k < w; ++k) {
+    float v = -INFINITY;
+    int id = 0x7fffffff;
+    for (int i = threadIdx.x; i < n_rows; i += blockDim.x) {
+      const int row = unit_tile ? unit_tile[(size_t)b * units_per_seq + i / rows_per_unit] * TILE_N +
+                                      i % rows_per_unit
+                                : i;
+      const int vid = row_vocab[row];
+      bool taken = false;
+      for (int q = 0; q < k; ++q) taken |= chosen[q] == vid;
+      if (!taken) argmax_combine(v, id, sc[row], vid);
+    }
+    block_argmax(v, id, rv, ri);
+    if (threadIdx.x == 0) {
+      if (id == 0x7fffffff) {  // fewer candidates than branches, or every score NaN
+        raise_error(err, ERRBIT_NAN);
+        id = 0;
+      }
+      chosen[k] = id;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < w) {
+    const int k = threadIdx.x;
+    raw[b * w + k] = chosen[k];
+    tree_tok[(size_t)b * n_nodes + 1 + k] =
+        inject_node(inject, inj_stride, b, len[b], 1, w * D, k, chosen[k]);
+  }
+  if (threadIdx.x == 0) tree_tok[(size_t)b * n_nodes] = cur_tok[b];
+}
+
+// Levels 2..D of a tree draft: row r = (sequence b, branch k) reduces its head partials to its
+// token, which feeds the branch's next sub-step, and writes node 1 + w*(depth-1) + k.
+__global__ void __launch_bounds__(256) tree_finalize_kernel(
+    const float* amax_val, const int* amax_idx, int ld_amax, int parts, int seq_offset, int w,
+    int D, int depth, const int* len, const int* inject, int inj_stride, int* tree_tok, int* raw,
+    int* err) {
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int r = blockIdx.x;
+  const int b = r / w, k = r - b * w;
+  const int u0 = r * seq_offset;
+  float v = -INFINITY;
+  int idx = 0x7fffffff;
+  for (int p = threadIdx.x; p < parts; p += blockDim.x)
+    argmax_combine(v, idx, amax_val[(size_t)r * ld_amax + u0 + p], amax_idx[(size_t)r * ld_amax + u0 + p]);
+  block_argmax(v, idx, rv, ri);
+  if (threadIdx.x == 0) {
+    if (idx == 0x7fffffff) {
+      raise_error(err, ERRBIT_NAN);
+      idx = 0;
+    }
+    raw[r] = idx;
+    const int node = 1 + w * (depth - 1) + k;
+    tree_tok[(size_t)b * (1 + w * D) + node] =
+        inject_node(inject, inj_stride, b, len[b], depth, w * D, node - 1, idx);
+  }
+}
+
+// Acceptance over a token tree (nodes in topological order, parent[0] = -1): G[i] = argmax of
+// node i's row; the longest root path on which every node's token is G at its parent (among
+// equally long ones the lower node index at the first difference) is accepted; emit its tokens
+// and the target's token at its end.  With
+// commit: len += m + 1, hid = hidden of the path's last node, and the path's nodes are recorded
+// (path[b][0] = old length, path[b][1..m] = node indices) for the cache compaction.
+struct TreeShape {
+  int n;
+  int8_t parent[64];
+};
+constexpr int TREE_MAX_DEPTH = 16;  // longest accepted path the compaction moves
+
+__global__ void __launch_bounds__(1024) tree_accept_kernel(
+    const float* amax_val, const int* amax_idx, int n_parts, int ld_amax, TreeShape tr,
+    const int* tokens, int* out_tokens, int out_ld, int* n_emit, int* next_tok, int commit,
+    int* len, float* hid, const float* X, int d, int* path, int* err) {
+  constexpr int NWV = 16;
+  __shared__ float rv[NWV];
+  __shared__ int ri[NWV];
+  __shared__ int G[64];
+  __shared__ int endn, mm;
+  const int b = blockIdx.x, R = tr.n;
+  const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x >> 6;
+  for (int i = 0; i < R; ++i) {
+    float v = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int p = threadIdx.x; p < n_parts; p += blockDim.x) {
+      const size_t o = (size_t)(b * R + i) * ld_amax + p;
+      argmax_combine(v, idx, amax_val[o], amax_idx[o]);
+    }
+    wave_argmax(v, idx);
+    if (lane == 0) {
+      rv[wid] = v;
+      ri[wid] = idx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float bv = rv[0];
+      int bi = ri[0];
+      for (int w2 = 1; w2 < (int)(blockDim.x >> 6); ++w2) argmax_combine(bv, bi, rv[w2], ri[w2]);
+      G[i] = bi;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    // longest agreeing path below each node, children visited in ascending index so that the
+    // lowest-index child wins among equally long continuations (nodes are in topological order)
+    int8_t best_len[64], best_child[64];
+    for (int i = R - 1; i >= 0; --i) {
+      best_len[i] = 0;
+      best_child[i] = -1;
+      for (int c = i + 1; c < R; ++c)
+        if (tr.parent[c] == i && tokens[b * R + c] == G[i] && best_len[c] + 1 > best_len[i]) {
+          best_len[i] = (int8_t)(best_len[c] + 1);
+          best_child[i] = (int8_t)c;
+        }
+    }
+    int cur = 0, m = 0;
+    int nodes[64];
+    while (best_child[cur] >= 0) {
+      const int nxt = best_child[cur];
+      out_tokens[b * out_ld + m] = tokens[b * R + nxt];
+      nodes[m] = nxt;
+      ++m;
+      cur = nxt;
+    }
+    out_tokens[b * out_ld + m] = G[cur];
+    for (int j = m + 1; j < out_ld; ++j) out_tokens[b * out_ld + j] = -1;
+    if (n_emit) n_emit[b] = m + 1;
+    if (next_tok) next_tok[b] = G[cur];
+    if (G[cur] == 0x7fffffff) raise_error(err, ERRBIT_NAN);
+    if (commit) {
+      path[b * 65] = len[b];
+      path[b * 65 + 1] = m;
+      for (int j = 0; j < m; ++j) path[b * 65 + 2 + j] = nodes[j];
+    }
+    endn = cur;
+    mm = m;
+  }
+  __syncthreads();
+  if (commit) {
+    const int e = endn;
+    for (int k = threadIdx.x; k < d; k += blockDim.x)
+      hid[(size_t)b * d + k] = X[((size_t)b * R + e) * d + k];
+    if (threadIdx.x == 0) len[b] += mm + 1;
+  }
+}
+
+// Moves the cache entries of an accepted tree path to consecutive slots: for path node j (1..m,
+// at depth j) slot old_len + node_j -> old_len + j, in every layer, KV head and element.  Each
+// thread reads every move of its element before it writes any, so a slot that is both a source
+// and a destination is read first.  K is [pos][hd], V transposed [hd][pos].
+template <typename T>
+__global__ void __launch_bounds__(256) kv_compact_kernel(T* kc, T* vc, const int* path, int L,
+                                                         int Bmax, int hkv, int hd, int max_ctx) {
+  const int b = blockIdx.y;
+  const int m = path[b * 65 + 1];
+  if (m <= 0 || m > TREE_MAX_DEPTH) return;
+  const int len0 = path[b * 65];
+  // every source slot (and so every destination, which is lower) must lie in the cache; a length
+  // beyond it was already flagged by the verify's kernels, and nothing is moved
+  for (int j = 0; j < m; ++j) {
+    const int node = path[b * 65 + 2 + j];
+    if (len0 < 0 || node < j + 1 || len0 + node >= max_ctx) return;
+  }
+  const size_t per = (size_t)L * hkv * hd;  // elements of one sequence's moves per slot
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < per;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(e % hd);
+    const size_t lg = e / hd;  // layer * hkv + g
+    const int g = (int)(lg % hkv), l = (int)(lg / hkv);
+    const size_t head = (((size_t)l * Bmax + b) * hkv + g);
+    T* kh = kc + head * max_ctx * hd;
+    T* vh = vc + head * hd * max_ctx + (size_t)c * max_ctx;
+    T kv[TREE_MAX_DEPTH], vv[TREE_MAX_DEPTH];
+#pragma unroll
+    for (int j = 0; j < TREE_MAX_DEPTH; ++j)
+      if (j < m) {
+        const int src = len0 + path[b * 65 + 2 + j];
+        kv[j] = kh[(size_t)src * hd + c];
+        vv[j] = vh[src];
+      }
+#pragma unroll
+    for (int j = 0; j < TREE_MAX_DEPTH; ++j)
+      if (j < m) {
+        const int dst = len0 + 1 + j;
+        kh[(size_t)dst * hd + c] = kv[j];
+        vh[dst] = vv[j];
+      }
+  }
+}
+
 __global__ void __launch_bounds__(256) trace_state_kernel(const float* x, const float* ssq, int B,
                                                           int n, const float* norm, float eps,
                                                           float* out, int ld_out) {
@@ -554,16 +775,17 @@ hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid
 hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
                               int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
                               const float* norm_e, int d, int Dd, float eps, void* u, int u_qx,
-                              int B, int* err, hipStream_t st) {
+                              int B, int* err, hipStream_t st, int h_div) {
   if (u_qx && B > 4) return hipErrorInvalidValue;
+  if (h_div < 1) return hipErrorInvalidValue;
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(draft_input_kernel<bf16_t>, dim3(B), dim3(256), 0, st, h, tok,
                        (const bf16_t*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
-                       eps, (bf16_t*)u, u_qx, err);
+                       eps, (bf16_t*)u, u_qx, h_div, err);
   else
     hipLaunchKernelGGL(draft_input_kernel<float>, dim3(B), dim3(256), 0, st, h, tok,
                        (const float*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
-                       eps, (float*)u, u_qx, err);
+                       eps, (float*)u, u_qx, h_div, err);
   return hipGetLastError();
 }
 
@@ -631,6 +853,55 @@ hipError_t launch_rope_table(float2* t, int hd, int max_ctx, float theta, hipStr
   const size_t n = (size_t)max_ctx * (hd / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, t, hd,
                      max_ctx, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_top(const float* scores, int vocab, const int* unit_tile, int units_per_seq,
+                           int rows_per_unit, const int* row_vocab, int B, int w, int D,
+                           const int* cur_tok, const int* len, const int* inject, int inj_stride,
+                           int* tree_tok, int* raw, int* err, hipStream_t st) {
+  if (w < 1 || w > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tree_top_kernel, dim3(B), dim3(1024), 0, st, scores, vocab, unit_tile,
+                     units_per_seq, rows_per_unit, row_vocab, w, D, cur_tok, len, inject,
+                     inj_stride, tree_tok, raw, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_finalize(const float* amax_val, const int* amax_idx, int ld_amax, int parts,
+                                int seq_offset, int rows, int w, int D, int depth, const int* len,
+                                const int* inject, int inj_stride, int* tree_tok, int* raw,
+                                int* err, hipStream_t st) {
+  hipLaunchKernelGGL(tree_finalize_kernel, dim3(rows), dim3(256), 0, st, amax_val, amax_idx,
+                     ld_amax, parts, seq_offset, w, D, depth, len, inject, inj_stride, tree_tok,
+                     raw, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
+                              int B, int n_nodes, const int8_t* parent, const int* tokens,
+                              int* out_tokens, int out_ld, int* n_emit, int* next_tok, int commit,
+                              int* len, float* hid, const float* X, int d, int* path, int* err,
+                              hipStream_t st) {
+  if (n_nodes < 1 || n_nodes > 64) return hipErrorInvalidValue;
+  TreeShape tr{};
+  tr.n = n_nodes;
+  for (int i = 0; i < n_nodes; ++i) tr.parent[i] = parent[i];
+  hipLaunchKernelGGL(tree_accept_kernel, dim3(B), dim3(1024), 0, st, amax_val, amax_idx, n_parts,
+                     ld_amax, tr, tokens, out_tokens, out_ld, n_emit, next_tok, commit, len, hid,
+                     X, d, path, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_compact(int dtype, void* kc, void* vc, const int* path, int L, int B,
+                             int Bmax, int hkv, int hd, int max_ctx, hipStream_t st) {
+  const size_t per = (size_t)L * hkv * hd;
+  const int gx = (int)((per + 255) / 256 < 2048 ? (per + 255) / 256 : 2048);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(gx, B), dim3(256), 0, st, (bf16_t*)kc,
+                       (bf16_t*)vc, path, L, Bmax, hkv, hd, max_ctx);
+  else
+    hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(gx, B), dim3(256), 0, st, (float*)kc,
+                       (float*)vc, path, L, Bmax, hkv, hd, max_ctx);
   return hipGetLastError();
 }
 

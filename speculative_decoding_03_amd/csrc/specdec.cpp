@@ -115,7 +115,7 @@ Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
 struct Layout {
   size_t x, xw, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err, rope;
   size_t rlog, e_xrow, e_orow, e_wt, e_groups, e_ngroups, e_h, e_y, e_usage;
-  size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i;
+  size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i, tscore, path;
   size_t total;
 };
 
@@ -142,6 +142,8 @@ struct specdec_ctx {
   std::vector<Gemm> g_dq, g_do, g_dgu, g_ddown;
   std::vector<int> len_hi;  // host-side upper bound on len
   int last_B = 0, last_R = 0;
+  int last_tree_n = 0;           // node count of the last tree verify (0: a linear verify)
+  int8_t last_parent[64] = {};   // its shape
   int prof_class = -1, prof_cap = 0, prof_n = 0;
   bool moe_usage_on = false;
   std::vector<hipEvent_t> prof_ev;
@@ -210,7 +212,7 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.o = xbuf(qd);
   L.h = xbuf(ffn_width(c));
   L.ssq = take((size_t)dm.Mx * (d / 16) * 4);
-  L.ssq_d = take((size_t)dm.Bx * (Dd / 16) * 4);
+  L.ssq_d = take((size_t)dm.Mx * (Dd / 16) * 4);  // drafter rows: sequences x tree branches
   L.amax_v = take((size_t)dm.Mx * dm.parts * 4);
   L.amax_i = take((size_t)dm.Mx * dm.parts * 4);
   // attention chunk partials: per (sequence, kv head, chunk) Rall rows of (o[hd], m, l, 2 pad)
@@ -218,16 +220,18 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.err = take(64);
   L.rope = take((size_t)c->max_ctx * (c->head_dim / 2) * 8);
   L.u = xbuf(d + Dd);
-  L.xd = take((size_t)dm.Bx * Dd * 4);
+  L.xd = take((size_t)dm.Mx * Dd * 4);
   L.xdw = xbuf(Dd);
   L.dh = xbuf(c->d_ffn);
-  L.hnext = take((size_t)dm.Bx * d * 4);
-  L.z = take((size_t)dm.Bx * c->n_centroids * 4);
-  L.utile = take((size_t)dm.Bx * dm.parts * 4);
-  L.urow = take((size_t)dm.Bx * dm.parts * 4);
-  L.dtok = take((size_t)dm.Bx * 4);
-  L.d_amax_v = take((size_t)dm.Bx * dm.parts * 4);  // [B][V/64] (full) or [B*k_c*upc] (clustered)
-  L.d_amax_i = take((size_t)dm.Bx * dm.parts * 4);
+  L.hnext = take((size_t)dm.Mx * d * 4);
+  L.z = take((size_t)dm.Mx * c->n_centroids * 4);
+  L.utile = take((size_t)dm.Mx * dm.parts * 4);
+  L.urow = take((size_t)dm.Mx * dm.parts * 4);
+  L.dtok = take((size_t)dm.Mx * 4);
+  L.d_amax_v = take((size_t)dm.Mx * dm.parts * 4);  // [rows][V/64] (full) or [rows*k_c*upc] (clustered)
+  L.d_amax_i = take((size_t)dm.Mx * dm.parts * 4);
+  L.tscore = take((size_t)dm.Bx * c->vocab * 4);  // a tree draft's first-level scores, by table row
+  L.path = take((size_t)dm.Bx * 65 * 4);         // accepted tree paths for the cache compaction
   const size_t E = c->n_experts, slots = (size_t)dm.Mx * c->top_k;
   L.rlog = take((size_t)dm.Mx * E * 4);
   L.e_xrow = take(E * dm.Mx * 4);
@@ -432,7 +436,38 @@ int routed_experts(specdec_ctx* x, int l, int M, hipStream_t st) {
   return SPECDEC_OK;
 }
 
-int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hipStream_t st) {
+// A token tree as the kernels take it: node i (topological order, parent[0] = -1) sits at depth
+// depth[i] (its rotary position is len + depth) in cache slot len + i, and sees the committed
+// prefix and the slots of the nodes in mask[i] (its ancestors and itself).
+struct Tree {
+  int n = 0, max_depth = 0;
+  int8_t parent[64] = {};
+  uint8_t depth[64] = {};
+  uint64_t mask[64] = {};
+};
+
+// Builds a Tree from a host parent array; false unless parent[0] = -1, 0 <= parent[i] < i, n <= 64
+// and every depth <= max_depth_allowed.
+bool make_tree(const int32_t* parent, int n, int max_depth_allowed, Tree* t) {
+  if (!parent || n < 1 || n > 64 || parent[0] != -1) return false;
+  t->n = n;
+  t->max_depth = 0;
+  t->parent[0] = -1;
+  t->depth[0] = 0;
+  t->mask[0] = 1ull;
+  for (int i = 1; i < n; ++i) {
+    const int p = parent[i];
+    if (p < 0 || p >= i) return false;
+    t->parent[i] = (int8_t)p;
+    t->depth[i] = (uint8_t)(t->depth[p] + 1);
+    t->mask[i] = t->mask[p] | (1ull << i);
+    t->max_depth = std::max<int>(t->max_depth, t->depth[i]);
+  }
+  return t->max_depth <= max_depth_allowed;
+}
+
+int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hipStream_t st,
+              int vis = VIS_CAUSAL, const Tree* tree = nullptr) {
   const specdec_config& c = x->cfg;
   AttnArgs a;
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
@@ -456,9 +491,13 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
   a.n_chunks = x->dm.n_chunks;
   int hi = 0;  // chunks that can hold a visible key, from the host-side bound on len
   for (int b = 0; b < B; ++b) hi = std::max(hi, x->len_hi[b]);
-  a.n_launch = std::min(x->dm.n_chunks, std::max(1, cdiv(std::min(hi + R - 1 + key_off, c.max_ctx),
-                                                          x->dm.chunk)));
+  a.n_launch = std::min(x->dm.n_chunks, std::max(1, cdiv(std::min(attn_key_end(vis, hi, R, key_off),
+                                                                  c.max_ctx),
+                                                         x->dm.chunk)));
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
+  a.vis = vis;
+  if (tree)
+    for (int i = 0; i < tree->n; ++i) a.tree_mask[i] = tree->mask[i];
   ProfScope ps(x, cls, st);
   HIP_TRY(launch_attention(dt_of(x), a, st));
   return SPECDEC_OK;
@@ -583,14 +622,15 @@ int specdec_destroy(specdec_ctx* x) {
   return SPECDEC_OK;
 }
 
-int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, float* logits,
-                   int32_t* argmax, void* stream) {
-  if (!x || !tokens) return SPECDEC_E_INVAL;
+}  // extern "C"
+
+namespace {
+
+// The target's forward over R rows per sequence (validated by the caller): linear rows (row i at
+// position len + i, seeing keys up to its own slot) or the nodes of a token tree.
+int verify_impl(specdec_ctx* x, int B, int R, const int32_t* tokens, float* logits, int32_t* argmax,
+                const Tree* tree, hipStream_t st) {
   const specdec_config& c = x->cfg;
-  if (B < 1 || B > c.max_batch || R < 1 || R > c.max_rows) return SPECDEC_E_INVAL;
-  for (int b = 0; b < B; ++b)
-    if (x->len_hi[b] + R > c.max_ctx) return SPECDEC_E_CAPACITY;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int M = B * R;
   const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
   float* X = at<float>(x, x->lay.x);
@@ -619,9 +659,13 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
       a.cache_b_stride = c.n_kv_heads * c.max_ctx * c.head_dim;
       a.theta = c.rope_theta;
       a.rope_cs = at<float2>(x, x->lay.rope);
+      if (tree) {
+        a.pos_mode = POS_TREE;
+        for (int i = 0; i < tree->n; ++i) a.tree_depth[i] = tree->depth[i];
+      }
       if ((rc = run(x, 2, EPI_ROPE, a, st))) return rc;
     }
-    if ((rc = attention(x, l, B, R, 1, 4, st))) return rc;
+    if ((rc = attention(x, l, B, R, 1, 4, st, tree ? VIS_TREE : VIS_CAUSAL, tree))) return rc;
     {  // output projection + residual; leaves x * ffn_norm for the FFN
       GemmArgs a = base_args(x, x->g_o[l], M);
       a.X = x->ws + x->lay.o;
@@ -669,6 +713,62 @@ int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, 
   }
   x->last_B = B;
   x->last_R = R;
+  x->last_tree_n = tree ? tree->n : 0;
+  if (tree)
+    for (int i = 0; i < tree->n; ++i) x->last_parent[i] = tree->parent[i];
+  return SPECDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, float* logits,
+                   int32_t* argmax, void* stream) {
+  if (!x || !tokens) return SPECDEC_E_INVAL;
+  const specdec_config& c = x->cfg;
+  if (B < 1 || B > c.max_batch || R < 1 || R > c.max_rows) return SPECDEC_E_INVAL;
+  for (int b = 0; b < B; ++b)
+    if (x->len_hi[b] + R > c.max_ctx) return SPECDEC_E_CAPACITY;
+  return verify_impl(x, B, R, tokens, logits, argmax, nullptr, reinterpret_cast<hipStream_t>(stream));
+}
+
+int specdec_verify_tree(specdec_ctx* x, int32_t B, int32_t n_nodes, const int32_t* parent,
+                        const int32_t* tokens, float* logits, int32_t* argmax, void* stream) {
+  if (!x || !tokens || !parent) return SPECDEC_E_INVAL;
+  const specdec_config& c = x->cfg;
+  if (B < 1 || B > c.max_batch || n_nodes < 1 || n_nodes > c.max_rows) return SPECDEC_E_INVAL;
+  Tree t;
+  if (!make_tree(parent, n_nodes, SPECDEC_TREE_MAX_DEPTH, &t)) return SPECDEC_E_INVAL;
+  for (int b = 0; b < B; ++b)
+    if (x->len_hi[b] + n_nodes > c.max_ctx) return SPECDEC_E_CAPACITY;
+  return verify_impl(x, B, n_nodes, tokens, logits, argmax, &t, reinterpret_cast<hipStream_t>(stream));
+}
+
+int specdec_accept_tree(specdec_ctx* x, int32_t B, int32_t n_nodes, const int32_t* parent,
+                        const int32_t* tokens, int32_t* out_tokens, int32_t out_ld,
+                        int32_t* n_emit, int32_t* next_tok, uint32_t flags, void* stream) {
+  if (!x || !tokens || !parent || !out_tokens) return SPECDEC_E_INVAL;
+  if (B != x->last_B || n_nodes != x->last_tree_n || n_nodes != x->last_R) return SPECDEC_E_INVAL;
+  Tree t;
+  if (!make_tree(parent, n_nodes, SPECDEC_TREE_MAX_DEPTH, &t)) return SPECDEC_E_INVAL;
+  for (int i = 0; i < n_nodes; ++i)
+    if (t.parent[i] != x->last_parent[i]) return SPECDEC_E_INVAL;  // not the verified tree
+  if (out_ld < t.max_depth + 1) return SPECDEC_E_INVAL;
+  const bool commit = (flags & SPECDEC_ACCEPT_COMMIT) != 0;
+  const specdec_config& c = x->cfg;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int* path = at<int>(x, x->lay.path);
+  HIP_TRY(launch_tree_accept(at<float>(x, x->lay.amax_v), at<int>(x, x->lay.amax_i), x->dm.parts,
+                             x->dm.parts, B, n_nodes, t.parent, tokens, out_tokens, out_ld, n_emit,
+                             next_tok, commit ? 1 : 0, x->len, x->hid, at<float>(x, x->lay.x),
+                             c.d_model, path, at<int>(x, x->lay.err), st));
+  if (commit) {
+    // the accepted path's cache entries move to the slots after the committed prefix
+    HIP_TRY(launch_kv_compact(dt_of(x), x->kv_k, x->kv_v, path, c.n_layers, B, c.max_batch,
+                              c.n_kv_heads, c.head_dim, c.max_ctx, st));
+    for (int b = 0; b < B; ++b) x->len_hi[b] += t.max_depth + 1;
+  }
   return SPECDEC_OK;
 }
 
@@ -676,7 +776,7 @@ int specdec_accept(specdec_ctx* x, int32_t B, int32_t K, const int32_t* tokens,
                    int32_t* out_tokens, int32_t* n_emit, int32_t* next_tok, uint32_t flags,
                    void* stream) {
   if (!x || !tokens) return SPECDEC_E_INVAL;
-  if (B != x->last_B || K + 1 != x->last_R || K < 0) return SPECDEC_E_INVAL;
+  if (B != x->last_B || K + 1 != x->last_R || K < 0 || x->last_tree_n) return SPECDEC_E_INVAL;
   const bool commit = (flags & SPECDEC_ACCEPT_COMMIT) != 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   HIP_TRY(launch_accept(at<float>(x, x->lay.amax_v), at<int>(x, x->lay.amax_i), x->dm.parts,
@@ -689,7 +789,7 @@ int specdec_accept(specdec_ctx* x, int32_t B, int32_t K, const int32_t* tokens,
 }
 
 int specdec_kv_commit(specdec_ctx* x, int32_t B, const int32_t* n_commit, void* stream) {
-  if (!x || !n_commit || B != x->last_B || B < 1) return SPECDEC_E_INVAL;
+  if (!x || !n_commit || B != x->last_B || B < 1 || x->last_tree_n) return SPECDEC_E_INVAL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   HIP_TRY(launch_commit(n_commit, B, x->last_R, x->len, x->hid, at<float>(x, x->lay.x),
                         x->cfg.d_model, at<int>(x, x->lay.err), st));
@@ -704,6 +804,152 @@ int specdec_draft(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32
                               verify_tokens, nullptr, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// One drafter sub-step over `rows` rows, rps rows per sequence (a tree draft's branches; 1 for a
+// linear draft) sharing their sequence's cache and query position len + pos_off.  Row r reads
+// hidden input h[r / h_div] and token tok[r].  Leaves x * n_f and its sums of squares for the head
+// and the next hidden input W_back s in hnext[r].
+int drafter_body(specdec_ctx* x, int rows, int rps, const float* h, int h_div, const int* tok,
+                 int pos_off, hipStream_t st) {
+  const specdec_config& c = x->cfg;
+  const int d = c.d_model, Dd = c.d_dim, qd = c.n_q_heads * c.head_dim;
+  float* xd = at<float>(x, x->lay.xd);
+  void* xdw = x->ws + x->lay.xdw;
+  float* sd = at<float>(x, x->lay.ssq_d);
+  int* err = at<int>(x, x->lay.err);
+  auto dw = [&](int l, int slot) { return (const float*)x->dw[(size_t)l * SPECDEC_N_DRAFT_TENSORS + slot]; };
+  int rc;
+  HIP_TRY(launch_draft_input(dt_of(x), h, tok, x->w.table, x->g_table.nkb, x->w.vocab_row, c.vocab,
+                             x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u,
+                             rows <= 4, rows, err, st, h_div));
+  {  // input projection of [rms(h); rms(e)]; leaves x * n1 of the first drafter layer
+    GemmArgs a = base_args(x, x->g_in, rows);
+    a.X = x->ws + x->lay.u;
+    a.ldx = d + Dd;
+    resid_output(a, xd, Dd, 0, sd, xdw, dw(0, SPECDEC_DW_N1));
+    if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
+  }
+  for (int l = 0; l < c.d_layers; ++l) {
+    {  // q projection + RoPE at len + pos_off (every row of a sequence at the same position)
+      GemmArgs a = base_args(x, x->g_dq[l], rows);
+      norm_input(a, xdw, Dd, sd, Dd);
+      a.qout = x->ws + x->lay.q;
+      a.len = x->len;
+      a.rows_per_seq = rps;
+      a.pos_off = pos_off;
+      a.pos_mode = POS_FLAT;
+      a.hq = c.n_q_heads;
+      a.hkv = 0;
+      a.hd = c.head_dim;
+      a.max_ctx = c.max_ctx;
+      a.theta = c.rope_theta;
+      a.rope_cs = at<float2>(x, x->lay.rope);
+      if ((rc = run(x, -1, EPI_ROPE, a, st))) return rc;
+    }
+    // cross-attention into the target's cache, keys [0, len) for every row
+    if ((rc = attention(x, c.kv_src_layer, rows / rps, rps, 0, -1, st, VIS_FLAT))) return rc;
+    {  // o projection + residual; leaves x * n2
+      GemmArgs a = base_args(x, x->g_do[l], rows);
+      a.X = x->ws + x->lay.o;
+      a.ldx = qd;
+      resid_output(a, xd, Dd, 1, sd, xdw, dw(l, SPECDEC_DW_N2));
+      if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
+    }
+    {
+      GemmArgs a = base_args(x, x->g_dgu[l], rows);
+      norm_input(a, xdw, Dd, sd, Dd);
+      a.hout = x->ws + x->lay.dh;
+      a.ldh = c.d_ffn;
+      if ((rc = run(x, -1, EPI_SILU, a, st))) return rc;
+    }
+    {  // down projection + residual; leaves x * (next n1 | n_f)
+      GemmArgs a = base_args(x, x->g_ddown[l], rows);
+      a.X = x->ws + x->lay.dh;
+      a.ldx = c.d_ffn;
+      const float* wn = l + 1 < c.d_layers ? dw(l + 1, SPECDEC_DW_N1) : x->w.norm_f;
+      resid_output(a, xd, Dd, 1, sd, xdw, wn);
+      if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
+    }
+  }
+  {  // next hidden input: W_back . (rms(x) * n_f)
+    GemmArgs a = base_args(x, x->g_back, rows);
+    norm_input(a, xdw, Dd, sd, Dd);
+    a.out = at<float>(x, x->lay.hnext);
+    a.ldo = d;
+    if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
+  }
+  return SPECDEC_OK;
+}
+
+// Where a head's argmax partials sit: row r's parts are amax[r * ld + r * seq_off + p], p < parts.
+struct HeadParts {
+  int parts, seq_off, ld;
+};
+
+// The drafter's output layer over `rows` rows: SPECDEC_HEAD_FULL scores every table row,
+// SPECDEC_HEAD_CLUSTERED scores the centroids, selects k_c clusters per row and scores their
+// members.  Optional copies: the scores by table row (scores, row stride ld_scores) and the
+// centroid scores (zcopy, row stride ld_z).
+int drafter_head(specdec_ctx* x, int rows, int head_mode, int k_c, float* scores, int ld_scores,
+                 float* zcopy, int ld_z, HeadParts* hp, hipStream_t st) {
+  const specdec_config& c = x->cfg;
+  const int dt = dt_of(x), Dd = c.d_dim;
+  const int S = c.vocab / c.n_centroids;  // tokens per cluster
+  const int tpc = S / 16, upc = S / 64;   // tiles / argmax units per cluster
+  void* xdw = x->ws + x->lay.xdw;
+  float* sd = at<float>(x, x->lay.ssq_d);
+  ProfScope ps(x, 6, st);
+  if (head_mode == SPECDEC_HEAD_FULL) {
+    GemmArgs a = base_args(x, x->g_table, rows);
+    norm_input(a, xdw, Dd, sd, Dd);
+    a.amax_val = at<float>(x, x->lay.d_amax_v);
+    a.amax_idx = at<int>(x, x->lay.d_amax_i);
+    a.ld_amax = x->dm.parts;
+    a.idx_map = x->w.row_vocab;
+    a.logits = scores;
+    a.ld_logits = ld_scores;
+    HIP_TRY(launch_gemm(dt, mt_for(rows), 4, EPI_ARGMAX, a, st));
+    *hp = {x->dm.parts, 0, x->dm.parts};
+    return SPECDEC_OK;
+  }
+  GemmArgs zc = base_args(x, x->g_cent, rows);
+  norm_input(zc, xdw, Dd, sd, Dd);
+  zc.out = at<float>(x, x->lay.z);
+  zc.ldo = c.n_centroids;
+  HIP_TRY(launch_gemm(dt, mt_for(rows), 1, EPI_STORE, zc, st));
+  if (zcopy)
+    HIP_TRY(launch_copy_rows(zcopy, ld_z, zc.out, c.n_centroids, rows, c.n_centroids, st));
+  HIP_TRY(launch_cluster_select(at<float>(x, x->lay.z), c.n_centroids, k_c, rows, tpc, upc,
+                                at<int>(x, x->lay.utile), at<int>(x, x->lay.urow),
+                                at<int>(x, x->lay.err), st));
+  GemmArgs a = base_args(x, x->g_clu, rows);
+  a.n_units = rows * k_c * upc;
+  a.unit_tile = at<int>(x, x->lay.utile);
+  a.unit_row = at<int>(x, x->lay.urow);
+  norm_input(a, xdw, Dd, sd, Dd);
+  a.amax_val = at<float>(x, x->lay.d_amax_v);
+  a.amax_idx = at<int>(x, x->lay.d_amax_i);
+  a.idx_map = x->w.row_vocab;
+  a.logits = scores;
+  a.ld_logits = ld_scores;
+  HIP_TRY(launch_gemm(dt, mt_for(rows), 4, EPI_ARGMAX, a, st));
+  *hp = {k_c * upc, k_c * upc, 0};  // listed units are stored by unit index
+  return SPECDEC_OK;
+}
+
+int check_head(const specdec_config& c, int head_mode, int k_c) {
+  if (head_mode != SPECDEC_HEAD_CLUSTERED && head_mode != SPECDEC_HEAD_FULL) return SPECDEC_E_INVAL;
+  if (head_mode == SPECDEC_HEAD_CLUSTERED && (k_c < 1 || k_c > c.n_centroids)) return SPECDEC_E_INVAL;
+  return SPECDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int specdec_draft_traced(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode, int32_t k_c,
                          const int32_t* cur_tok, int32_t* drafts, const int32_t* inject,
                          int64_t inj_stride, int32_t* verify_tokens,
@@ -711,144 +957,80 @@ int specdec_draft_traced(specdec_ctx* x, int32_t B, int32_t K, int32_t head_mode
   if (!x || !cur_tok || !drafts) return SPECDEC_E_INVAL;
   const specdec_config& c = x->cfg;
   if (B < 1 || B > c.max_batch || K < 1 || K > c.max_draft) return SPECDEC_E_INVAL;
-  if (head_mode != SPECDEC_HEAD_CLUSTERED && head_mode != SPECDEC_HEAD_FULL) return SPECDEC_E_INVAL;
-  if (head_mode == SPECDEC_HEAD_CLUSTERED && (k_c < 1 || k_c > c.n_centroids)) return SPECDEC_E_INVAL;
+  if (check_head(c, head_mode, k_c)) return SPECDEC_E_INVAL;
   if (inject && (inj_stride < 1 || inj_stride > 0x7fffffff)) return SPECDEC_E_INVAL;
   // sub-step j queries at position len + j - 1: the last one, len + K - 1, must be a cache slot
   for (int b = 0; b < B; ++b)
     if (x->len_hi[b] + K > c.max_ctx) return SPECDEC_E_CAPACITY;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int dt = dt_of(x);
-  const int d = c.d_model, Dd = c.d_dim, qd = c.n_q_heads * c.head_dim;
-  const int S = c.vocab / c.n_centroids;  // tokens per cluster
-  const int tpc = S / 16, upc = S / 64;   // tiles / argmax units per cluster
-  float* xd = at<float>(x, x->lay.xd);
-  void* xdw = x->ws + x->lay.xdw;
-  float* sd = at<float>(x, x->lay.ssq_d);
+  const int d = c.d_model, Dd = c.d_dim;
   float* hnext = at<float>(x, x->lay.hnext);
   int* dtok = at<int>(x, x->lay.dtok);
-  int* err = at<int>(x, x->lay.err);
-  const int src = c.kv_src_layer;
-  auto dw = [&](int l, int slot) { return (const float*)x->dw[(size_t)l * SPECDEC_N_DRAFT_TENSORS + slot]; };
   int rc;
   for (int j = 1; j <= K; ++j) {
     const float* h = (j == 1) ? x->hid : hnext;
     const int* tok = (j == 1) ? cur_tok : dtok;
-    HIP_TRY(launch_draft_input(dt, h, tok, x->w.table, x->g_table.nkb, x->w.vocab_row, c.vocab,
-                               x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u,
-                               B <= 4, B, err, st));
-    {  // input projection of [rms(h); rms(e)]; leaves x * n1 of the first drafter layer
-      GemmArgs a = base_args(x, x->g_in, B);
-      a.X = x->ws + x->lay.u;
-      a.ldx = d + Dd;
-      resid_output(a, xd, Dd, 0, sd, xdw, dw(0, SPECDEC_DW_N1));
-      if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
-    }
-    for (int l = 0; l < c.d_layers; ++l) {
-      {  // q projection + RoPE at len + j - 1
-        GemmArgs a = base_args(x, x->g_dq[l], B);
-        norm_input(a, xdw, Dd, sd, Dd);
-        a.qout = x->ws + x->lay.q;
-        a.len = x->len;
-        a.rows_per_seq = 1;
-        a.pos_off = j - 1;
-        a.hq = c.n_q_heads;
-        a.hkv = 0;
-        a.hd = c.head_dim;
-        a.max_ctx = c.max_ctx;
-        a.theta = c.rope_theta;
-        a.rope_cs = at<float2>(x, x->lay.rope);
-        if ((rc = run(x, -1, EPI_ROPE, a, st))) return rc;
-      }
-      // cross-attention into the target's cache, keys [0, len)
-      if ((rc = attention(x, src, B, 1, 0, -1, st))) return rc;
-      {  // o projection + residual; leaves x * n2
-        GemmArgs a = base_args(x, x->g_do[l], B);
-        a.X = x->ws + x->lay.o;
-        a.ldx = qd;
-        resid_output(a, xd, Dd, 1, sd, xdw, dw(l, SPECDEC_DW_N2));
-        if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
-      }
-      {
-        GemmArgs a = base_args(x, x->g_dgu[l], B);
-        norm_input(a, xdw, Dd, sd, Dd);
-        a.hout = x->ws + x->lay.dh;
-        a.ldh = c.d_ffn;
-        if ((rc = run(x, -1, EPI_SILU, a, st))) return rc;
-      }
-      {  // down projection + residual; leaves x * (next n1 | n_f)
-        GemmArgs a = base_args(x, x->g_ddown[l], B);
-        a.X = x->ws + x->lay.dh;
-        a.ldx = c.d_ffn;
-        const float* wn = l + 1 < c.d_layers ? dw(l + 1, SPECDEC_DW_N1) : x->w.norm_f;
-        resid_output(a, xd, Dd, 1, sd, xdw, wn);
-        if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
-      }
-    }
-    {  // next hidden input: W_back . (rms(x) * n_f)
-      GemmArgs a = base_args(x, x->g_back, B);
-      norm_input(a, xdw, Dd, sd, Dd);
-      a.out = hnext;
-      a.ldo = d;
-      if ((rc = run(x, -1, EPI_STORE, a, st))) return rc;
-    }
+    if ((rc = drafter_body(x, B, 1, h, 1, tok, j - 1, st))) return rc;
     if (trace && trace->state)
-      HIP_TRY(launch_trace_state(xd, sd, B, Dd, x->w.norm_f, c.rms_eps, trace->state + (size_t)(j - 1) * Dd,
+      HIP_TRY(launch_trace_state(at<float>(x, x->lay.xd), at<float>(x, x->lay.ssq_d), B, Dd,
+                                 x->w.norm_f, c.rms_eps, trace->state + (size_t)(j - 1) * Dd,
                                  K * Dd, st));
     if (trace && trace->hidden)
       HIP_TRY(launch_copy_rows(trace->hidden + (size_t)(j - 1) * d, K * d, hnext, d, B, d, st));
     // the head's scores of sub-step j land at trace row b*K + j - 1, by table row
     float* tscores = trace && trace->table_scores ? trace->table_scores + (size_t)(j - 1) * c.vocab : nullptr;
-    const int ld_tscores = K * c.vocab;
-    int parts_per_seq, seq_off, ld;
-    {
-      ProfScope ps(x, 6, st);
-      if (head_mode == SPECDEC_HEAD_FULL) {
-        GemmArgs a = base_args(x, x->g_table, B);
-        norm_input(a, xdw, Dd, sd, Dd);
-        a.amax_val = at<float>(x, x->lay.d_amax_v);
-        a.amax_idx = at<int>(x, x->lay.d_amax_i);
-        a.ld_amax = x->dm.parts;
-        a.idx_map = x->w.row_vocab;
-        a.logits = tscores;
-        a.ld_logits = ld_tscores;
-        HIP_TRY(launch_gemm(dt, mt_for(B), 4, EPI_ARGMAX, a, st));
-        parts_per_seq = x->dm.parts;
-        seq_off = 0;
-        ld = x->dm.parts;
-      } else {
-        GemmArgs zc = base_args(x, x->g_cent, B);
-        norm_input(zc, xdw, Dd, sd, Dd);
-        zc.out = at<float>(x, x->lay.z);
-        zc.ldo = c.n_centroids;
-        HIP_TRY(launch_gemm(dt, mt_for(B), 1, EPI_STORE, zc, st));
-        if (trace && trace->centroid_scores)
-          HIP_TRY(launch_copy_rows(trace->centroid_scores + (size_t)(j - 1) * c.n_centroids,
-                                   K * c.n_centroids, zc.out, c.n_centroids, B, c.n_centroids, st));
-        HIP_TRY(launch_cluster_select(at<float>(x, x->lay.z), c.n_centroids, k_c, B, tpc, upc,
-                                      at<int>(x, x->lay.utile), at<int>(x, x->lay.urow), err, st));
-        GemmArgs a = base_args(x, x->g_clu, B);
-        a.n_units = B * k_c * upc;
-        a.unit_tile = at<int>(x, x->lay.utile);
-        a.unit_row = at<int>(x, x->lay.urow);
-        norm_input(a, xdw, Dd, sd, Dd);
-        a.amax_val = at<float>(x, x->lay.d_amax_v);
-        a.amax_idx = at<int>(x, x->lay.d_amax_i);
-        a.idx_map = x->w.row_vocab;
-        a.logits = tscores;
-        a.ld_logits = ld_tscores;
-        HIP_TRY(launch_gemm(dt, mt_for(B), 4, EPI_ARGMAX, a, st));
-        parts_per_seq = k_c * upc;
-        seq_off = k_c * upc;
-        ld = 0;  // listed units are stored by unit index
-      }
-      HIP_TRY(launch_draft_finalize(at<float>(x, x->lay.d_amax_v), at<int>(x, x->lay.d_amax_i), ld,
-                                    parts_per_seq, seq_off, B, K, j, x->len, inject,
-                                    (int)inj_stride, drafts, dtok, cur_tok, verify_tokens, err,
-                                    st));
-    }
+    float* zcopy = trace && trace->centroid_scores
+                       ? trace->centroid_scores + (size_t)(j - 1) * c.n_centroids : nullptr;
+    HeadParts hp;
+    if ((rc = drafter_head(x, B, head_mode, k_c, tscores, K * c.vocab, zcopy, K * c.n_centroids, &hp, st)))
+      return rc;
+    HIP_TRY(launch_draft_finalize(at<float>(x, x->lay.d_amax_v), at<int>(x, x->lay.d_amax_i), hp.ld,
+                                  hp.parts, hp.seq_off, B, K, j, x->len, inject, (int)inj_stride,
+                                  drafts, dtok, cur_tok, verify_tokens, at<int>(x, x->lay.err), st));
     if (trace && trace->raw_drafts)
       HIP_TRY(launch_copy_rows(trace->raw_drafts + (j - 1), K, dtok, 1, B, 1, st));
+  }
+  return SPECDEC_OK;
+}
+
+int specdec_draft_tree(specdec_ctx* x, int32_t B, int32_t width, int32_t depth, int32_t head_mode,
+                       int32_t k_c, const int32_t* cur_tok, int32_t* tree_tokens,
+                       const int32_t* inject, int64_t inj_stride, void* stream) {
+  if (!x || !cur_tok || !tree_tokens) return SPECDEC_E_INVAL;
+  const specdec_config& c = x->cfg;
+  const int n_nodes = 1 + width * depth;
+  if (B < 1 || B > c.max_batch || width < 1 || width > SPECDEC_TREE_MAX_WIDTH || depth < 1 ||
+      depth > SPECDEC_TREE_MAX_DEPTH || n_nodes > c.max_rows || B * width > x->dm.Mx)
+    return SPECDEC_E_INVAL;
+  if (check_head(c, head_mode, k_c)) return SPECDEC_E_INVAL;
+  if (head_mode == SPECDEC_HEAD_CLUSTERED && width > k_c * (c.vocab / c.n_centroids))
+    return SPECDEC_E_INVAL;
+  if (inject && (inj_stride < 1 || inj_stride > 0x7fffffff)) return SPECDEC_E_INVAL;
+  for (int b = 0; b < B; ++b)
+    if (x->len_hi[b] + depth > c.max_ctx) return SPECDEC_E_CAPACITY;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* hnext = at<float>(x, x->lay.hnext);
+  int* raw = at<int>(x, x->lay.dtok);
+  int* err = at<int>(x, x->lay.err);
+  int rc;
+  // level 1: one row per sequence; the w best tokens of its head start the branches
+  if ((rc = drafter_body(x, B, 1, x->hid, 1, cur_tok, 0, st))) return rc;
+  HeadParts hp;
+  float* scores = at<float>(x, x->lay.tscore);
+  if ((rc = drafter_head(x, B, head_mode, k_c, scores, c.vocab, nullptr, 0, &hp, st))) return rc;
+  const bool clu = head_mode == SPECDEC_HEAD_CLUSTERED;
+  HIP_TRY(launch_tree_top(scores, c.vocab, clu ? at<int>(x, x->lay.utile) : nullptr, hp.parts, 64,
+                          x->w.row_vocab, B, width, depth, cur_tok, x->len, inject, (int)inj_stride,
+                          tree_tokens, raw, err, st));
+  // levels 2..depth: every branch continues from its own token (the level-1 hidden input is
+  // shared by a sequence's branches)
+  for (int lv = 2; lv <= depth; ++lv) {
+    const int rows = B * width;
+    if ((rc = drafter_body(x, rows, width, hnext, lv == 2 ? width : 1, raw, lv - 1, st))) return rc;
+    if ((rc = drafter_head(x, rows, head_mode, k_c, nullptr, 0, nullptr, 0, &hp, st))) return rc;
+    HIP_TRY(launch_tree_finalize(at<float>(x, x->lay.d_amax_v), at<int>(x, x->lay.d_amax_i), hp.ld,
+                                 hp.parts, hp.seq_off, rows, width, depth, lv, x->len, inject,
+                                 (int)inj_stride, tree_tokens, raw, err, st));
   }
   return SPECDEC_OK;
 }

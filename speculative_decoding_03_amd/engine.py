@@ -293,6 +293,34 @@ class Engine:
                                               _p(drafts), _p(inject), stride, _p(verify_tokens),
                                               C.byref(tr), _s(stream)), "specdec_draft_traced")
 
+    # --- token trees ---
+    @staticmethod
+    def _parents(parent):
+        return (C.c_int32 * len(parent))(*[int(v) for v in parent])
+
+    def draft_tree(self, cur_tok, tree_tokens, width: int, depth: int, head_mode=F.HEAD_CLUSTERED,
+                   k_c=1, inject=None, stream=None) -> None:
+        """A width x depth tree draft into tree_tokens [B][1 + width*depth] (node order)."""
+        B = tree_tokens.shape[0]
+        assert tree_tokens.is_contiguous() and tree_tokens.shape[1] == 1 + width * depth
+        stride = 0 if inject is None else inject.shape[1]
+        F.check(self.lib.specdec_draft_tree(self.ctx, B, width, depth, head_mode, k_c, _p(cur_tok),
+                                            _p(tree_tokens), _p(inject), stride, _s(stream)),
+                "specdec_draft_tree")
+
+    def verify_tree(self, parent, tokens, logits=None, argmax=None, stream=None) -> None:
+        B, n = tokens.shape
+        F.check(self.lib.specdec_verify_tree(self.ctx, B, n, self._parents(parent), _p(tokens),
+                                             _p(logits), _p(argmax), _s(stream)), "specdec_verify_tree")
+
+    def accept_tree(self, parent, tokens, out_tokens, n_emit=None, next_tok=None, commit=True,
+                    stream=None) -> None:
+        B, n = tokens.shape
+        F.check(self.lib.specdec_accept_tree(self.ctx, B, n, self._parents(parent), _p(tokens),
+                                             _p(out_tokens), out_tokens.shape[1], _p(n_emit),
+                                             _p(next_tok), F.ACCEPT_COMMIT if commit else 0,
+                                             _s(stream)), "specdec_accept_tree")
+
     def moe_usage_start(self, stream=None) -> None:
         F.check(self.lib.specdec_moe_usage_start(self.ctx, _s(stream)), "specdec_moe_usage_start")
 

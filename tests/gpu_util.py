@@ -261,3 +261,30 @@ def drafter_trace_check(eng, cfg, DW, cache, hid, t0: int, length: int, K: int, 
         h, c = h_next, raw[j]
     assert eng.device_error() == 0
     return flips
+
+
+def gpu_spec_tree(eng, t0: int, n: int, width: int, depth: int, inject_tab=None,
+                  head_mode=SD.HEAD_CLUSTERED, k_c=1):
+    """The speculative loop with tree drafts through the C ABI; returns (tokens, emitted per
+    step)."""
+    dev = eng.kv_k.device
+    par = O.tree_parents(width, depth)
+    nn = len(par)
+    toks = [int(t0)]
+    cur = torch.tensor([t0], dtype=torch.int32, device=dev)
+    T = torch.empty(1, nn, dtype=torch.int32, device=dev)
+    out = torch.empty(1, depth + 1, dtype=torch.int32, device=dev)
+    n_emit = torch.empty(1, dtype=torch.int32, device=dev)
+    inj = None if inject_tab is None else torch.from_numpy(inject_tab.reshape(1, -1)).to(dev)
+    emitted = []
+    length = int(eng.len[0].item())
+    while len(toks) < n:
+        eng.draft_tree(cur, T, width, depth, head_mode=head_mode, k_c=k_c, inject=inj)
+        eng.verify_tree(par, T)
+        eng.accept_tree(par, T, out, n_emit=n_emit, next_tok=cur, commit=True)
+        e = int(n_emit.item())
+        toks.extend(out[0, :e].cpu().tolist())
+        emitted.append(e)
+        length += e
+        eng.set_len_bound([length])
+    return toks[:n], emitted

@@ -190,6 +190,9 @@ def main() -> int:
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the graph-replay leg (kernel traces then end with the timed steps)")
     ap.add_argument("--sweep-steps", type=int, default=40)
+    ap.add_argument("--no-tree", dest="tree", action="store_false", help="skip the tree-draft leg")
+    ap.add_argument("--no-adaptive", dest="adaptive", action="store_false",
+                    help="skip the adaptive draft-length leg")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the path is built and measured on a single MI355X "
@@ -219,12 +222,18 @@ def main() -> int:
     dev = torch.device("cuda:0")
 
     t_setup = time.perf_counter()
-    n_greedy = S_all * (K + 1) + K + 2
+    # greedy tokens the injection tables need: every step of the main loop at K+1 tokens, and of
+    # the sweep and adaptive legs at up to 7 tokens
+    n_greedy = max(S_all * (K + 1), (args.sweep_steps + 2) * (max(K, 6) + 1)) + max(K, 6) + 2
     max_ctx = (cfg.ctx + n_greedy + 64 + 7) // 8 * 8
     log(f"setup {cfg.name}: weights on device ({cfg.target_params() / 1e9:.2f}B target params), B={B}")
     perm, cent = WD.clusters(cfg)
     model = E.DeviceModel(E.Shape.of(cfg), WD.DeviceSource(cfg), perm, cent)
-    eng = E.Engine(model, max_batch=B, max_draft=K, max_rows=max(16 // B, K + 1), max_ctx=max_ctx)
+    KA = max(K, 6)  # longest draft the adaptive-length leg may choose
+    # verify rows per sequence: a linear step (K + 1, up to KA + 1 in the adaptive leg) or a tree
+    # of up to 3 branches (1 + 3K), within the 64 rows of a call
+    max_rows = min(64 // B, max(16 // B, KA + 1, 1 + 3 * K))
+    eng = E.Engine(model, max_batch=B, max_draft=KA, max_rows=max_rows, max_ctx=max_ctx)
     WD.fill_kv(eng, cfg)
     t0 = WD.start_state(eng, cfg)  # [B] int32
     hid0 = eng.hid.clone()
@@ -387,6 +396,188 @@ def main() -> int:
                              "spec_equals_greedy": r["same"]}
         log("p sweep: " + ", ".join(f"{p}: {v['tokens_per_s']}" for p, v in sweep.items()))
 
+    # draft length chosen per step by the library's policy from the running acceptance, with the
+    # costs measured above: one drafter sub-step, a one-row verify, and each further verify row
+    adaptive = {}
+    if args.adaptive:
+        t_sub = float(np.median(main["draft_ms"])) / K
+        t_dec = float(np.median(dec_ms))
+        t_row = max(0.0, (float(np.median(main["ver_ms"])) - t_dec) / K)
+        ktabs = {}
+
+        def adaptive_run(p, steps, warm=2):
+            restore()
+            for k in range(1, KA + 1):
+                tabs = []
+                for b in range(B):
+                    gseq = np.full(max_ctx, -1, dtype=np.int64)
+                    gseq[cfg.ctx:cfg.ctx + len(greedy[b])] = greedy[b]
+                    tabs.append(inject_table(gseq, k, p, cfg.inject_seed, b=b))
+                ktabs[k] = torch.from_numpy(np.stack(tabs)).to(dev)
+            pol = E.KPolicy(1, KA, t_draft_ms=t_sub, t_verify_ms=t_dec, t_row_ms=t_row, decay=0.9)
+            cur = t0.clone()
+            S = warm + steps
+            ne_h = torch.zeros(S, B, dtype=torch.int32).pin_memory()
+            out_h = torch.zeros(S, B, KA + 1, dtype=torch.int32).pin_memory()
+            done = [torch.cuda.Event() for _ in range(S)]
+            toks = [[int(t0[b].item())] for b in range(B)]
+            known = [cfg.ctx] * B
+            ks, emitted, t_start = [], 0, None
+            # one step stays in flight: step i's length is chosen from the steps up to i - 2,
+            # and step i - 1's counts are read while step i runs
+            def read(i):
+                done[i].synchronize()
+                ne = ne_h[i].tolist()
+                pol.observe(ks_all[i], ne)
+                for b in range(B):
+                    known[b] += ne[b]
+                    toks[b].extend(out_h[i, b, : ne[b]].tolist())
+                return sum(ne)
+            ks_all = []
+            for i in range(S):
+                if i == warm:
+                    if i > 0:
+                        read(i - 1)
+                    torch.cuda.synchronize()
+                    t_start = time.perf_counter()
+                k = pol.choose()
+                ks_all.append(k)
+                drafts = torch.empty(B, k, dtype=torch.int32, device=dev)
+                T = torch.empty(B, k + 1, dtype=torch.int32, device=dev)
+                out_d = torch.empty(B, k + 1, dtype=torch.int32, device=dev)
+                ne_d = torch.empty(B, dtype=torch.int32, device=dev)
+                eng.set_len_bound([n + KA + 1 for n in known])  # one step in flight
+                eng.draft(cur, drafts, head_mode=head_mode, k_c=args.k_c, inject=ktabs[k],
+                          verify_tokens=T)
+                eng.verify(T)
+                eng.accept(T, out_tokens=out_d, n_emit=ne_d, next_tok=cur, commit=True)
+                ne_h[i].copy_(ne_d, non_blocking=True)
+                out_h[i, :, : k + 1].copy_(out_d, non_blocking=True)
+                done[i].record()
+                if i > 0 and i != warm:
+                    e = read(i - 1)
+                    if i - 1 >= warm:
+                        emitted += e
+            emitted += read(S - 1)
+            ks = ks_all[warm:]
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t_start
+            same = all(toks[b] == greedy[b][: len(toks[b])] for b in range(B))
+            assert eng.device_error() == 0, "device error in the adaptive-length loop"
+            return {"tokens_per_s": round(emitted / wall, 2),
+                    "mean_K": round(float(np.mean(ks)), 2),
+                    "K_counts": {str(k): ks.count(k) for k in sorted(set(ks))},
+                    "final_acceptance_estimate": round(pol.acceptance(), 3),
+                    "spec_equals_greedy": bool(same)}
+
+        for p in (0.0, 0.7, 0.89, 1.0):
+            r = adaptive_run(p, args.sweep_steps)
+            if str(p) in sweep:
+                r["fixed_K_tokens_per_s"] = sweep[str(p)]["tokens_per_s"]
+            adaptive[str(p)] = r
+        log("adaptive K: " + ", ".join(f"{p}: {v['tokens_per_s']} (mean K {v['mean_K']})"
+                                       for p, v in adaptive.items()))
+    # token trees: width branches of depth K per step, verified in one pass of 1 + width*K rows
+    trees = {}
+    if args.tree:
+        def tree_run(p, width, steps, warm=2):
+            restore()
+            depth = K
+            par = E.tree_parents(width, depth)
+            nn = len(par)
+            tabs = []
+            for b in range(B):
+                gseq = np.full(max_ctx, -1, dtype=np.int64)
+                gseq[cfg.ctx:cfg.ctx + len(greedy[b])] = greedy[b]
+                tabs.append(inject_table(gseq, width * depth, p, cfg.inject_seed, b=b))
+            tab = torch.from_numpy(np.stack(tabs)).to(dev)
+            S = warm + steps
+            cur = t0.clone()
+            T = torch.empty(B, nn, dtype=torch.int32, device=dev)
+            out_d = torch.empty(B, depth + 1, dtype=torch.int32, device=dev)
+            ne_d = torch.empty(B, dtype=torch.int32, device=dev)
+            out_h = torch.zeros(S, B, depth + 1, dtype=torch.int32).pin_memory()
+            ne_h = torch.zeros(S, B, dtype=torch.int32).pin_memory()
+            e0 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+            e1 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+            e2 = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+            done = [torch.cuda.Event() for _ in range(S)]
+            known = [cfg.ctx] * B
+
+            def enqueue(i):
+                eng.set_len_bound([n + depth + 1 for n in known])  # step i - 1 still in flight
+                e0[i].record()
+                eng.draft_tree(cur, T, width, depth, head_mode=head_mode, k_c=args.k_c, inject=tab)
+                e1[i].record()
+                eng.verify_tree(par, T)
+                eng.accept_tree(par, T, out_d, n_emit=ne_d, next_tok=cur, commit=True)
+                e2[i].record()
+                out_h[i].copy_(out_d, non_blocking=True)
+                ne_h[i].copy_(ne_d, non_blocking=True)
+                done[i].record()
+
+            def read(i):
+                done[i].synchronize()
+                for b in range(B):
+                    known[b] += int(ne_h[i, b])
+
+            for i in range(warm):
+                enqueue(i)
+                read(i)
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for i in range(warm, S):
+                enqueue(i)
+                if i > warm:
+                    read(i - 1)
+            read(S - 1)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t_start
+            assert eng.device_error() == 0, "device error in the tree loop"
+            ne, ot = ne_h.numpy(), out_h.numpy()
+            same = True
+            for b in range(B):
+                seq = [int(t0[b].item())]
+                for i in range(S):
+                    seq.extend(ot[i, b, : ne[i, b]].tolist())
+                same &= seq == greedy[b][: len(seq)]
+            em = int(ne[warm:].sum())
+            timed = range(warm, S)
+            # steps whose output still follows the greedy reference: a tree node sits in cache slot
+            # len + index rather than len + depth, so the attention sums its keys in another order
+            # than decoding does, and after a near-tie flip the injected reference tokens no longer
+            # apply
+            agree, pos = 0, 1
+            for i in range(S):
+                e = int(ne[i, 0])
+                if ot[i, 0, :e].tolist() != greedy[0][pos:pos + e]:
+                    break
+                pos += e
+                agree = i + 1
+            step_ms = float(np.median([e0[i].elapsed_time(e2[i]) for i in timed]))
+            # expected tokens per step when every node independently holds the reference token
+            # with probability p: 1 + sum_j P(some branch agrees through depth j)
+            e_tree = 1.0 + sum(1.0 - (1.0 - p ** j) ** width for j in range(1, depth + 1))
+            ok = [int(ne[i].sum()) for i in range(warm, min(agree, S))]
+            return {"step_ms": round(step_ms, 4),
+                    "verify_ms": round(float(np.median([e1[i].elapsed_time(e2[i]) for i in timed])), 4),
+                    "draft_ms": round(float(np.median([e0[i].elapsed_time(e1[i]) for i in timed])), 4),
+                    "expected_tokens_per_step": round(e_tree, 3),
+                    "modelled_tokens_per_s": round(B * e_tree / (step_ms * 1e-3), 2),
+                    "measured_tokens_per_step_while_on_reference": round(float(np.mean(ok)) / B, 3) if ok else None,
+                    "steps_on_reference": max(0, agree - warm),
+                    "wall_tokens_per_s": round(em / wall, 2),
+                    "spec_equals_greedy": bool(same)}
+
+        for width in [w for w in (2, 3) if 1 + w * K <= max_rows]:
+            for p in (0.7, 0.89):
+                r = tree_run(p, width, args.sweep_steps)
+                if str(p) in sweep:
+                    r["linear_tokens_per_s"] = sweep[str(p)]["tokens_per_s"]
+                    r["linear_ms_per_step"] = sweep[str(p)]["ms_per_step"]
+                trees[f"width{width}_p{p}"] = r
+        log("trees (modelled tokens/s): " + ", ".join(f"{k}: {v['modelled_tokens_per_s']}"
+                                                      for k, v in trees.items()))
     emitted = main["emitted"]
     accepted = emitted - N * B
     tok_s = emitted / wall
@@ -439,6 +630,20 @@ def main() -> int:
     }
     if sweep:
         res["p_sweep"] = sweep
+    if trees:
+        res["tree_drafts"] = {"shape": f"width branches of depth {K} (1 + width*{K} verify rows)",
+                              "tokens_per_s": "modelled: the measured median step time and the "
+                                              "expected tokens per step of independent per-node "
+                                              "agreement p (output is exact up to rounding, so it "
+                                              "leaves the greedy reference at near-ties and the "
+                                              "injected reference stops applying)",
+                              "by_width_p": trees}
+    if adaptive:
+        res["adaptive_k"] = {"policy": "library draft-length policy: K in [1, %d] maximising expected "
+                                       "tokens per unit time from the decayed acceptance estimate "
+                                       "(decay 0.9) and the measured sub-step, decode and per-row "
+                                       "costs; per-step host readback" % KA,
+                             "by_p": adaptive}
     if cfg.is_moe:
         res["moe"] = {"experts_read_per_verify": round(ver_experts, 1),
                       "experts_read_per_decode": round(dec_experts, 1),

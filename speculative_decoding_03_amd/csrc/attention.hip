@@ -103,7 +103,7 @@ __device__ __forceinline__ void store_part_o(float* row, int d0, const f32x4& y)
 // The four waves then merge through LDS (common max, rescale, sum in wave order), each wave
 // writing a quarter of the chunk's partial (o, m, l).  Exponentials are 2^x on the hardware
 // instruction, with scores scaled by scale * log2 e.  Keys that no row may see are never loaded.
-template <typename T, int HD>
+template <typename T, int HD, bool TREE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_occupancy<T, HD>())))
 attn_kernel(AttnArgs a) {
   using SH = AttnShape<HD>;
@@ -199,7 +199,8 @@ attn_kernel(AttnArgs a) {
     // keys [0, kend) are visible, and in a tree verify slot len + j for each bit j of tmask
     const int kend = qv >= Rall ? 0 : (a.vis == VIS_CAUSAL ? len + row + a.key_off
                                                            : (a.vis == VIS_FLAT ? len + a.key_off : len));
-    const uint64_t tmask = a.vis == VIS_TREE && qv < Rall ? a.tree_mask[row] : 0ull;
+    uint64_t tmask = 0ull;
+    if constexpr (TREE) tmask = qv < Rall ? a.tree_mask[row] : 0ull;
     // scores in base-2 units (scale * log2 e folded in): exp(x - m) = exp2(x2 - m2)
     float m = -INFINITY;
 #pragma unroll
@@ -209,8 +210,11 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int key = kw0 + nb * 32 + 8 * grp + 4 * h + v;
-          const unsigned tj = (unsigned)(key - len);  // slot of a tree node (when < 64)
-          const bool vis = key < kend || (tj < 64u && ((tmask >> tj) & 1ull));
+          bool vis = key < kend;
+          if constexpr (TREE) {
+            const unsigned tj = (unsigned)(key - len);  // slot of a tree node (when < 64)
+            vis |= tj < 64u && ((tmask >> tj) & 1ull);
+          }
           const float val = vis ? s[nb][h][v] * scale2 : -INFINITY;
           s[nb][h][v] = val;
           m = fmaxf(m, val);
@@ -437,7 +441,12 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   if (a.chunk != AttnShape<HD>::CH) return hipErrorInvalidValue;
   const int Rall = a.R * (a.hq / a.hkv);
   dim3 grid(a.n_launch, a.hkv, a.B), block(NWAVE * WAVE);
-  hipLaunchKernelGGL((attn_kernel<T, HD>), grid, block, 0, st, a);
+  if (a.vis == VIS_TREE) {
+    if (!a.tree_mask) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<T, HD, true>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<T, HD, false>), grid, block, 0, st, a);
+  }
   dim3 cgrid(Rall, a.hkv, a.B), cblock(WAVE);
   hipLaunchKernelGGL((attn_combine_kernel<T, HD>), cgrid, cblock, 0, st, a);
   return hipGetLastError();

@@ -119,7 +119,6 @@ template <int MT, int NU> struct EpiPre {
   float res[NU][MT][4];
   float2 cs[NU][MT][4];  // rotary (cos, sin) of the lane's pair at each row's position
   int pos[MT][4];        // rotary position of each row
-  int slot[MT][4];       // its cache slot (the position, except for a tree verify's nodes)
 };
 
 template <int MT, int NU, int EPI>
@@ -148,10 +147,11 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int l
         const int m = local_row(narrow, mt, v, lane);
         const int b = m < a.M ? m / a.rows_per_seq : 0;
         const int r = m < a.M ? m - b * a.rows_per_seq : 0;  // row within its sequence
-        const int len = a.len[b];
-        pre.slot[mt][v] = len + r + a.pos_off;
-        pre.pos[mt][v] = a.pos_mode == POS_FLAT ? len + a.pos_off
-                         : (a.pos_mode == POS_TREE ? len + a.tree_depth[r & 63] : len + r + a.pos_off);
+        pre.pos[mt][v] = a.len[b] + r + a.pos_off;
+        // the other position rules (the mode is uniform over the launch): every row of a
+        // sequence at len + pos_off, or a tree node at len + its depth (r < rows <= 64)
+        if (a.pos_mode == POS_FLAT) pre.pos[mt][v] -= r;
+        else if (a.pos_mode == POS_TREE) pre.pos[mt][v] += (int)a.tree_depth[r] - r - a.pos_off;
       }
     const int half = a.hd >> 1;
 #pragma unroll
@@ -348,7 +348,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           const float partner = dpp_f32<DPP_XOR1>(val);  // the other element of the rotary pair
           if (m < a.M) {
             const int b = m / a.rows_per_seq;
-            const int pos = pre.pos[mt][v], slot = pre.slot[mt][v];
+            const int pos = pre.pos[mt][v];
+            // cache slot: the position, except for a tree node (slot len + node index)
+            const int slot = a.pos_mode == POS_TREE ? a.len[b] + (m - b * a.rows_per_seq) : pos;
             float y = val;
             if (rot) {
               const float cs = pre.cs[t][mt][v].x, sn = pre.cs[t][mt][v].y;

@@ -88,7 +88,7 @@ struct GemmArgs {
   // cache slot); POS_FLAT len + pos_off for every row (the drafter's branches, no cache write);
   // POS_TREE angle at len + tree_depth[r], cache slot len + r (a tree verify's nodes)
   int pos_mode = 0;
-  uint8_t tree_depth[64] = {};
+  const uint8_t* tree_depth = nullptr;  // POS_TREE: [rows per sequence] device (launch_tree_desc)
   // EPI_SILU: hout[m][f] = silu(gate) * up, gate/up tiles interleaved
   void* hout = nullptr;
   int ldh = 0;
@@ -137,7 +137,7 @@ struct AttnArgs {
   // draft); VIS_TREE [0, len) and slot len + j for every bit j of tree_mask[i] (a tree verify:
   // node i sees its ancestors and itself, each at slot len + node index).
   int vis = 0;
-  uint64_t tree_mask[64] = {};
+  const uint64_t* tree_mask = nullptr;  // VIS_TREE: [R] device (launch_tree_desc)
 };
 enum { VIS_CAUSAL = 0, VIS_FLAT = 1, VIS_TREE = 2 };
 enum { POS_LINEAR = 0, POS_FLAT = 1, POS_TREE = 2 };
@@ -180,6 +180,10 @@ hipError_t launch_tree_accept(const float* amax_val, const int* amax_idx, int n_
                               int* out_tokens, int out_ld, int* n_emit, int* next_tok, int commit,
                               int* len, float* hid, const float* X, int d, int* path, int* err,
                               hipStream_t st);
+// Writes a tree's per-node visibility masks (uint64 [n]) and depths (uint8 [n]) to device memory
+// for the verify's attention and rotary epilogue.
+hipError_t launch_tree_desc(int n, const uint64_t* mask, const uint8_t* depth, uint64_t* mask_out,
+                            uint8_t* depth_out, hipStream_t st);
 hipError_t launch_kv_compact(int dtype, void* kc, void* vc, const int* path, int L, int B,
                              int Bmax, int hkv, int hd, int max_ctx, hipStream_t st);
 // Mixture-of-experts routing of M rows over E experts (logits [M][E]): the top_k experts of

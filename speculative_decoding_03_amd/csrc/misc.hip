@@ -892,6 +892,33 @@ hipError_t launch_tree_accept(const float* amax_val, const int* amax_idx, int n_
   return hipGetLastError();
 }
 
+struct TreeDesc {
+  int n;
+  uint8_t depth[64];
+  uint64_t mask[64];
+};
+
+__global__ void tree_desc_kernel(TreeDesc t, uint64_t* mask_out, uint8_t* depth_out) {
+  const int i = threadIdx.x;
+  if (i < t.n) {
+    mask_out[i] = t.mask[i];
+    depth_out[i] = t.depth[i];
+  }
+}
+
+hipError_t launch_tree_desc(int n, const uint64_t* mask, const uint8_t* depth, uint64_t* mask_out,
+                            uint8_t* depth_out, hipStream_t st) {
+  if (n < 1 || n > 64) return hipErrorInvalidValue;
+  TreeDesc t{};
+  t.n = n;
+  for (int i = 0; i < n; ++i) {
+    t.mask[i] = mask[i];
+    t.depth[i] = depth[i];
+  }
+  hipLaunchKernelGGL(tree_desc_kernel, dim3(1), dim3(64), 0, st, t, mask_out, depth_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_compact(int dtype, void* kc, void* vc, const int* path, int L, int B,
                              int Bmax, int hkv, int hd, int max_ctx, hipStream_t st) {
   const size_t per = (size_t)L * hkv * hd;

@@ -116,6 +116,7 @@ struct Layout {
   size_t x, xw, q, o, h, ssq, ssq_d, amax_v, amax_i, att_part, err, rope;
   size_t rlog, e_xrow, e_orow, e_wt, e_groups, e_ngroups, e_h, e_y, e_usage;
   size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i, tscore, path;
+  size_t tree_mask, tree_depth;
   size_t total;
 };
 
@@ -232,6 +233,8 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.d_amax_i = take((size_t)dm.Mx * dm.parts * 4);
   L.tscore = take((size_t)dm.Bx * c->vocab * 4);  // a tree draft's first-level scores, by table row
   L.path = take((size_t)dm.Bx * 65 * 4);         // accepted tree paths for the cache compaction
+  L.tree_mask = take(64 * 8);                     // the verified tree: visibility masks
+  L.tree_depth = take(64);                        // and node depths
   const size_t E = c->n_experts, slots = (size_t)dm.Mx * c->top_k;
   L.rlog = take((size_t)dm.Mx * E * 4);
   L.e_xrow = take(E * dm.Mx * 4);
@@ -496,8 +499,7 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
                                                          x->dm.chunk)));
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
   a.vis = vis;
-  if (tree)
-    for (int i = 0; i < tree->n; ++i) a.tree_mask[i] = tree->mask[i];
+  if (tree) a.tree_mask = at<uint64_t>(x, x->lay.tree_mask);
   ProfScope ps(x, cls, st);
   HIP_TRY(launch_attention(dt_of(x), a, st));
   return SPECDEC_OK;
@@ -632,6 +634,9 @@ int verify_impl(specdec_ctx* x, int B, int R, const int32_t* tokens, float* logi
                 const Tree* tree, hipStream_t st) {
   const specdec_config& c = x->cfg;
   const int M = B * R;
+  if (tree)
+    HIP_TRY(launch_tree_desc(tree->n, tree->mask, tree->depth, at<uint64_t>(x, x->lay.tree_mask),
+                             at<uint8_t>(x, x->lay.tree_depth), st));
   const int d = c.d_model, qd = c.n_q_heads * c.head_dim;
   float* X = at<float>(x, x->lay.x);
   void* XW = x->ws + x->lay.xw;
@@ -661,7 +666,7 @@ int verify_impl(specdec_ctx* x, int B, int R, const int32_t* tokens, float* logi
       a.rope_cs = at<float2>(x, x->lay.rope);
       if (tree) {
         a.pos_mode = POS_TREE;
-        for (int i = 0; i < tree->n; ++i) a.tree_depth[i] = tree->depth[i];
+        a.tree_depth = at<uint8_t>(x, x->lay.tree_depth);
       }
       if ((rc = run(x, 2, EPI_ROPE, a, st))) return rc;
     }

@@ -360,6 +360,13 @@ class Engine:
             pass
 
 
+def tree_parents(width: int, depth: int) -> list:
+    """Parent of every node of the tree specdec_draft_tree writes (node order: the root, then
+    level by level, branch k at node 1 + width*(j-1) + k)."""
+    return [-1] + [0 if j == 1 else 1 + width * (j - 2) + k
+                   for j in range(1, depth + 1) for k in range(width)]
+
+
 class KPolicy:
     """The library's draft-length policy (specdec_k_policy_*): host code, no device work."""
 

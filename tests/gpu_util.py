@@ -64,6 +64,24 @@ def gpu_greedy(eng, t0: int, n: int):
     return toks
 
 
+def gpu_greedy_margins(eng, t0: int, n: int):
+    """gpu_greedy that also returns each step's top-2 logit margin (from the GPU's own logits)."""
+    dev = eng.kv_k.device
+    V = eng.shape.vocab
+    toks, margins = [int(t0)], []
+    cur = torch.tensor([[t0]], dtype=torch.int32, device=dev)
+    nxt = torch.empty(1, dtype=torch.int32, device=dev)
+    lg = torch.empty(1, 1, V, dtype=torch.float32, device=dev)
+    while len(toks) < n:
+        eng.verify(cur, logits=lg)
+        eng.accept(cur, next_tok=nxt, commit=True)
+        top2 = torch.topk(lg[0, 0], 2).values
+        margins.append(float(top2[0] - top2[1]))
+        cur = nxt.view(1, 1).clone()
+        toks.append(int(nxt.item()))
+    return toks, margins
+
+
 def gpu_spec(eng, t0: int, n: int, K: int, inject_tab=None, head_mode=SD.HEAD_CLUSTERED, k_c=1):
     """The speculative loop through the C ABI; returns (tokens, emitted per step)."""
     dev = eng.kv_k.device
@@ -268,7 +286,7 @@ def gpu_spec_tree(eng, t0: int, n: int, width: int, depth: int, inject_tab=None,
     """The speculative loop with tree drafts through the C ABI; returns (tokens, emitted per
     step)."""
     dev = eng.kv_k.device
-    par = O.tree_parents(width, depth)
+    par = E.tree_parents(width, depth)
     nn = len(par)
     toks = [int(t0)]
     cur = torch.tensor([t0], dtype=torch.int32, device=dev)

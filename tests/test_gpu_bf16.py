@@ -28,7 +28,8 @@ import ctypes as C  # noqa: E402
 import oracle as O  # noqa: E402
 import speculative_decoding_03_amd as SD  # noqa: E402
 from gpu_util import (build_engine, drafter_trace_check, gpu_greedy, gpu_spec,  # noqa: E402
-                      host_embedding, oracle_logits_full, rel_err, restore, snapshot)
+                      gpu_greedy_margins, gpu_spec_tree, host_embedding, oracle_logits_full,
+                      rel_err, restore, snapshot)
 from workloads import device as WD  # noqa: E402
 from workloads import inject_table, truncated  # noqa: E402
 from workloads import synth as S  # noqa: E402
@@ -242,3 +243,57 @@ def test_rollback_leaves_dead_slots_unread(case):
     assert eng.device_error() == 0
     eng.kv_k.copy_(saved[0])
     eng.kv_v.copy_(saved[1])
+
+
+def test_tree_verify_matches_oracle(case):
+    """A 2-branch x 3-token tree verified at the workload's width and context: every node's logits
+    over the whole vocabulary against the oracle's plain decoding of the node's root path; then
+    tree speculation follows greedy decoding up to near ties.  A tree node's key sits in cache
+    slot len + node index, not len + depth, so the attention adds the same keys in another order
+    than decoding does: the output is exact up to rounding, and a token may differ from the same
+    GPU's greedy token only where the greedy step's top-2 margin is within the tolerance."""
+    cfg, eng = case["cfg"], case["eng"]
+    restore(eng, case["snap"])
+    width, depth = 2, 3
+    par = O.tree_parents(width, depth)
+    g = gpu_greedy(eng, case["t0"], depth + 2)
+    restore(eng, case["snap"])
+    rng = np.random.default_rng(17)
+    # branch 1 holds the greedy tokens for two steps, everything else random
+    T = [case["t0"]] + [int(v) for v in rng.integers(0, cfg.vocab, width * depth)]
+    T[2], T[4] = g[1], g[2]
+    dev = eng.kv_k.device
+    Tt = torch.tensor([T], dtype=torch.int32, device=dev)
+    lg = torch.empty(1, len(T), cfg.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, len(T), dtype=torch.int32, device=dev)
+    eng.verify_tree(par, Tt, logits=lg, argmax=am)
+    got = lg[0].cpu().numpy()
+    H, check = [], []
+    for i in range(len(T)):
+        path = O.tree_path(par, i)
+        margins = []
+        h = oracle_rows(case["W"], cfg, case["cache"].copy(), [T[n] for n in path], cfg.ctx, margins)
+        H.append(h[-1])
+        check.append(min(margins) > ROUTE_MARGIN)
+    rows = [i for i in range(len(T)) if check[i]]
+    refs = oracle_full_logits(case, [H[i] for i in rows])
+    for i, ref in zip(rows, refs):
+        assert rel_err(got[i], ref) < TOL, f"node {i}: logits"
+        rb = O.argmax_first(ref)
+        if rb != int(am[0, i]):
+            assert ref[rb] - ref[int(am[0, i])] <= MARGIN, f"node {i}: argmax"
+    assert eng.device_error() == 0
+    # tree speculation equals greedy (the same GPU)
+    restore(eng, case["snap"])
+    n = 16
+    ref_g, margins = gpu_greedy_margins(eng, case["t0"], n + depth + 2)
+    restore(eng, case["snap"])
+    gseq = np.full(case["max_ctx"], -1, dtype=np.int64)
+    gseq[cfg.ctx:cfg.ctx + len(ref_g)] = ref_g
+    toks, emitted = gpu_spec_tree(eng, case["t0"], n, width, depth,
+                                  inject_table(gseq, width * depth, 0.6, cfg.inject_seed))
+    for i in range(1, n):
+        if toks[i] != ref_g[i]:
+            assert margins[i - 1] <= MARGIN, f"token {i} differs at greedy margin {margins[i - 1]:.4f}"
+            break
+    assert eng.device_error() == 0

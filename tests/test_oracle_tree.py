@@ -137,3 +137,10 @@ def test_tree_spec_equals_greedy(width, p):
     assert all(1 <= e <= depth + 1 for e in st.emitted_per_step)
     if p == 1.0:
         assert all(e == depth + 1 for e in st.emitted_per_step[:-1])
+
+
+def test_binding_tree_shape_is_the_oracle_shape():
+    from speculative_decoding_03_amd.engine import tree_parents
+    for w in (1, 2, 3, 4):
+        for d in (1, 2, 3, 5):
+            assert tree_parents(w, d) == O.tree_parents(w, d)

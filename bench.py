@@ -1,13 +1,15 @@
 """Benchmark of the draft-verify-accept step of greedy speculative decoding on one MI355X.
 
 One step = draft K tokens (MTP drafter, clustered head) + verify K+1 rows + fused accept/commit,
-on seeded synthetic inputs: random-init bf16 weights of the named shapes, a synthetic committed
+on seeded synthetic inputs: random-init bf16 weights of the named shapes (or, with --wformat q4,
+every matrix in 4-bit blocks with an fp16 step per 32 weights), a synthetic committed
 KV cache of `ctx` positions, and drafts replaced by the target's own greedy token with
 probability p (the acceptance mix of the workload).  Inputs are resident in HBM before timing.
 
 Prints one JSON line.  Default workload: the 31B-class dense configuration (64 layers, d 5120,
 40/8 heads of 128, FFN 25600, vocab 262144; drafter 4 layers x 256 with 2048 centroids; ctx
 8192, K=3, batch 1, p=0.7).  --config e2b | e4b | moe and --batch B run the other workloads.
+The default run ends with the same workload on 4-bit weights (a child process, "q4_weights").
 """
 
 from __future__ import annotations
@@ -37,9 +39,15 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def expert_bytes(cfg) -> int:
-    """Bytes of one routed expert's gate, up and down matrices (bf16)."""
-    return 3 * cfg.d_model * cfg.expert_ffn * 2
+def wb(cfg) -> float:
+    """Bytes per weight: bf16, or the 4-bit block format (half a byte per code plus an fp16 step
+    per 32 weights)."""
+    return 9 / 16 if cfg.weight_format == "q4" else 2.0
+
+
+def expert_bytes(cfg) -> float:
+    """Bytes of one routed expert's gate, up and down matrices."""
+    return 3 * cfg.d_model * cfg.expert_ffn * wb(cfg)
 
 
 def weight_bytes(cfg, experts_touched: float = 0.0) -> float:
@@ -47,9 +55,9 @@ def weight_bytes(cfg, experts_touched: float = 0.0) -> float:
     the router and shared FFN of every layer plus the experts the pass's rows were routed to
     (experts_touched, summed over layers)."""
     if not cfg.is_moe:
-        return cfg.target_params() * 2
+        return cfg.target_params() * wb(cfg)
     all_experts = cfg.n_layers * cfg.n_experts * expert_bytes(cfg)
-    return cfg.target_params() * 2 - all_experts + experts_touched * expert_bytes(cfg)
+    return cfg.target_params() * wb(cfg) - all_experts + experts_touched * expert_bytes(cfg)
 
 
 def algorithmic_bytes(cfg, B: int, rows: int, keys: float, experts_touched: float = 0.0) -> float:
@@ -64,19 +72,20 @@ def algorithmic_bytes(cfg, B: int, rows: int, keys: float, experts_touched: floa
 def draft_substep_bytes(cfg, B: int, keys: float, k_c: int = 1) -> float:
     D, d, qd = cfg.d_dim, cfg.d_model, cfg.q_dim
     per = D * qd * 2 + 3 * D * cfg.d_ffn
-    w = (D * (d + D) + cfg.d_layers * per + d * D + cfg.n_centroids * D) * 2
-    table = B * (k_c * cfg.cluster_size * D * 2 + D * 2)
+    w = (D * (d + D) + cfg.d_layers * per + d * D + cfg.n_centroids * D) * wb(cfg)
+    table = B * (k_c * cfg.cluster_size * D * wb(cfg) + D * wb(cfg))
     kv = B * cfg.d_layers * 2 * cfg.n_kv_heads * keys * cfg.head_dim * 2
     return w + table + kv
 
 
 def gate_up_bytes(cfg, M: int) -> float:
     """Algorithmic bytes of one gate/up GEMM launch (the dense FFN, or the shared FFN of a
-    mixture-of-experts layer): the 2F x d bf16 weights once, the M bf16 rows of x times the norm
-    weight and their per-16-column fp32 sums of squares in, the M bf16 gated-product rows out."""
+    mixture-of-experts layer): the 2F x d weights once (bf16 or 4-bit blocks), the M bf16 rows of
+    x times the norm weight and their per-16-column fp32 sums of squares in, the M bf16
+    gated-product rows out."""
     d = cfg.d_model
     F = cfg.shared_ffn if cfg.is_moe else cfg.ffn_dim
-    return 2 * F * d * 2 + M * d * 2 + M * (d // 16) * 4 + M * F * 2
+    return 2 * F * d * wb(cfg) + M * d * 2 + M * (d // 16) * 4 + M * F * 2
 
 
 def src_sha(path: str) -> str:
@@ -193,6 +202,10 @@ def main() -> int:
     ap.add_argument("--no-tree", dest="tree", action="store_false", help="skip the tree-draft leg")
     ap.add_argument("--no-adaptive", dest="adaptive", action="store_false",
                     help="skip the adaptive draft-length leg")
+    ap.add_argument("--wformat", default="dense", choices=["dense", "q4"],
+                    help="weights: bf16, or every matrix in 4-bit blocks with an fp16 step per 32")
+    ap.add_argument("--no-q4-leg", dest="q4_leg", action="store_false",
+                    help="skip the 4-bit-weight run of the same workload (a child process)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the path is built and measured on a single MI355X "
@@ -209,7 +222,7 @@ def main() -> int:
     from workloads import inject_table, preset
 
     B = args.batch
-    cfg = preset(args.config, batch=B)
+    cfg = preset(args.config, batch=B, weight_format=args.wformat)
     if args.p is not None:
         cfg = cfg.replace(p_inject=args.p)
     K, W, N = cfg.draft_k, args.warmup, args.steps
@@ -601,7 +614,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "batch": B, "K": K, "ctx": cfg.ctx,
+        "config": {"workload": WORKLOAD_TEXT[args.config] + (
+                       "; every weight matrix in 4-bit blocks (fp16 step per 32 weights)"
+                       if args.wformat == "q4" else ""),
+                   "batch": B, "K": K, "ctx": cfg.ctx, "weights": args.wformat,
                    "p_inject": cfg.p_inject, "head": f"{args.head} k_c={args.k_c}"},
         "verify_ms": round(med(ver_ms), 4),
         "decode_ms": round(med(dec_ms), 4),
@@ -654,10 +670,11 @@ def main() -> int:
         lb = gate_up_bytes(cfg, M)
         achieved = lb / (launch_ms * 1e-3) / 1e9
         kw, units, nw, groups = eng.query_split(0)
-        kname = f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}, false>"
+        q4 = "true" if args.wformat == "q4" else "false"
+        kname = f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}, false, {q4}>"
         grid = groups * nw * 64
-        traffic = load_traffic(f"gemm_gate_up_{args.config}" + (f"_b{B}" if B > 1 else ""),
-                               kname, grid, lb)
+        traffic = load_traffic(f"gemm_gate_up_{args.config}" + (f"_b{B}" if B > 1 else "")
+                               + ("_q4" if args.wformat == "q4" else ""), kname, grid, lb)
         what = "shared-FFN gate/up" if cfg.is_moe else "FFN gate/up"
         res["roofline"] = {
             "kernel": f"{kname} ({what} + SiLU product, verify M={M}, grid {grid} work-items, "
@@ -678,8 +695,38 @@ def main() -> int:
         log("cpu baseline (oracle on host cores, bounded sample)")
         res["cpu_baseline"] = cpu_baseline(cfg, emitted / (N * B), K, B)
     eng.close()
+    del eng, model
+    torch.cuda.empty_cache()
+    if args.q4_leg and args.wformat == "dense":
+        res["q4_weights"] = q4_leg(args)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def q4_leg(args) -> dict:
+    """The same workload with every weight matrix in 4-bit blocks, run as a child process (its
+    progress goes to stderr) with the headline's timing and kernel profile, without the sweeps."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config, "--batch",
+           str(args.batch), "--wformat", "q4", "--steps", str(min(args.steps, 100)), "--warmup",
+           str(args.warmup), "--head", args.head, "--k-c", str(args.k_c), "--no-cpu-baseline",
+           "--no-p-sweep", "--no-tree", "--no-adaptive", "--no-graph", "--no-q4-leg"]
+    if args.p is not None:
+        cmd += ["--p", str(args.p)]
+    log("4-bit weight leg: " + " ".join(cmd[2:]))
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        return {"error": f"exit status {r.returncode}"}
+    try:
+        d = json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:
+        return {"error": f"unreadable output: {e}"}
+    keep = ("value", "unit", "steps", "ms_per_step", "verify_ms", "decode_ms", "draft_ms",
+            "verify_over_decode", "verify_hbm_gbs", "verify_hbm_frac", "verify_bytes",
+            "tokens_per_step", "spec_equals_greedy", "roofline")
+    out = {k: d[k] for k in keep if k in d}
+    out["weights"] = "4-bit blocks: codes plus an fp16 step per 32 weights (0.5625 bytes/weight)"
+    return out
 
 
 if __name__ == "__main__":

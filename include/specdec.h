@@ -51,6 +51,7 @@ enum {
 
 enum { SPECDEC_F32 = 0, SPECDEC_BF16 = 1 };
 enum { SPECDEC_HEAD_CLUSTERED = 0, SPECDEC_HEAD_FULL = 1 };
+enum { SPECDEC_WF_DENSE = 0, SPECDEC_WF_Q4 = 1 };
 #define SPECDEC_ACCEPT_COMMIT 1u
 
 /* Device error word bits. */
@@ -80,6 +81,11 @@ typedef struct {
   int32_t max_draft;        /* largest K */
   int32_t max_rows;         /* largest rows per sequence in one verify (>= max_draft + 1) */
   int32_t max_ctx;          /* KV-cache positions per sequence */
+  int32_t weight_format;    /* SPECDEC_WF_DENSE: packed matrices hold dtype elements;
+                               SPECDEC_WF_Q4: every packed matrix (target, drafter, embedding,
+                               table, centroids) is in the 4-bit block format of
+                               specdec_pack_q4; needs dtype BF16 and every reduction width
+                               (d_model, Hq*hd, the FFN widths, d_dim, d_ffn) % 128 == 0 */
 } specdec_config;
 
 /* Per-layer tensor slots of specdec_weights.layers (n_layers * SPECDEC_N_LAYER_TENSORS). */
@@ -111,7 +117,8 @@ enum {
 };
 
 /* Device pointers to the weights (dtype elements unless noted).  "packed" tensors are in the
-   streaming tile layout written by specdec_pack_matrix.  The pointer tables are copied at
+   streaming tile layout written by specdec_pack_matrix (weight_format SPECDEC_WF_DENSE) or in
+   the 4-bit block format written by specdec_pack_q4 (SPECDEC_WF_Q4).  The pointer tables are copied at
    create; the tensors themselves must outlive the context. */
 typedef struct {
   const void* embed;             /* packed [vocab][d_model]; also the tied LM head */
@@ -305,6 +312,21 @@ int specdec_kv_commit(specdec_ctx* ctx, int32_t B, const int32_t* n_commit, void
    [n/G][kd] matrices packs as one [n][kd] PLAIN matrix.  Setup-time helper. */
 int specdec_pack_matrix(const void* src, void* dst, int32_t n, int32_t kd, int32_t dtype,
                         int32_t kind, int32_t head_dim, int32_t split_rows, void* stream);
+
+/* 4-bit block weights ("Gemma 4's MTP drafter explained", section "Step 1 -- repackaging the
+   QAT drafter": the QAT drafters and targets keep every 32-weight block of a matrix on a 4-bit
+   grid, stored as Q4_0).  Logical weight (row i, column k) = step[i][k/32] * (code[i][k] - 8),
+   code 0..15, step an IEEE fp16 value.
+   specdec_pack_q4 writes the matrix given by codes [n][kd] (device, one byte per code, only the
+   low 4 bits read) and steps [n][kd/32] (device, fp16 bit patterns) into dst (device,
+   specdec_q4_bytes(n, kd) = n*kd*9/16 bytes, 256-byte aligned), rows permuted by kind,
+   head_dim and split_rows exactly as specdec_pack_matrix does.  Requires n % 16 == 0,
+   kd % 128 == 0.  Layout (for reference; the library reads it): 1152-byte blocks per 16 rows x
+   128 columns, tile-major; a block holds 1024 bytes of codes (16 bytes per MFMA operand lane)
+   and then each row's four fp16 steps.  Setup-time helper; errors: SPECDEC_E_INVAL. */
+size_t specdec_q4_bytes(int32_t n, int32_t kd);
+int specdec_pack_q4(const uint8_t* codes, const uint16_t* steps, void* dst, int32_t n, int32_t kd,
+                    int32_t kind, int32_t head_dim, int32_t split_rows, void* stream);
 
 /* Tightens the host-side bound on len after the caller has read len back (host values). */
 int specdec_set_len_bound(specdec_ctx* ctx, const int32_t* host_len, int32_t B);

@@ -22,10 +22,10 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from workloads import inject_draw, inject_threshold
+from workloads import ExpertStack, Q4Codes, inject_draw, inject_threshold
 
 __all__ = [
-    "as_f64", "rmsnorm", "silu", "rope", "attention", "dense_ffn", "moe_ffn", "moe_route",
+    "as_f64", "q4_weights", "rmsnorm", "silu", "rope", "attention", "dense_ffn", "moe_ffn", "moe_route",
     "moe_route_margin",
     "KVCache", "decoder_layer_row", "target_row", "lm_head", "argmax_first", "top2_margin",
     "greedy_generate", "prefill", "verify", "accept", "commit", "token_scores",
@@ -36,12 +36,44 @@ __all__ = [
 ]
 
 
+def q4_weights(codes: np.ndarray, steps: np.ndarray) -> np.ndarray:
+    """Weights of a matrix stored in 4-bit blocks ([guide] "Step 1 -- repackaging the QAT
+    drafter": the QAT weights keep every 32-weight block of a matrix on a 4-bit grid, which is
+    Q4_0's own layout).  Reading of Q4_0: along each row, block j of 32 consecutive weights has
+    one fp16 step d_j and 4-bit codes q in 0..15, weight = d_j * (q - 8).  codes [..., K],
+    steps [..., K/32]; float64 result (exact: an fp16 value times a small integer)."""
+    q = np.asarray(codes)
+    d = np.asarray(steps, dtype=np.float16).astype(np.float64)
+    K = q.shape[-1]
+    assert K % 32 == 0 and d.shape == q.shape[:-1] + (K // 32,)
+    blocks = q.reshape(*q.shape[:-1], K // 32, 32).astype(np.float64) - 8.0
+    return (blocks * d[..., None]).reshape(q.shape)
+
+
+class _F64Stack:
+    """A lazily generated expert stack whose slices come out as float64 weights."""
+
+    def __init__(self, stack):
+        self.stack = stack
+
+    def __len__(self):
+        return len(self.stack)
+
+    def __getitem__(self, e):
+        return as_f64(self.stack[e])
+
+
 def as_f64(tree):
-    """Recursively convert the float arrays of a weight dict to float64 (integer arrays kept)."""
+    """Recursively convert the weights of a weight dict to float64 (integer arrays kept); 4-bit
+    tensors become their weights (q4_weights)."""
     if isinstance(tree, dict):
         return {k: as_f64(v) for k, v in tree.items()}
     if isinstance(tree, list):
         return [as_f64(v) for v in tree]
+    if isinstance(tree, Q4Codes):
+        return q4_weights(tree.codes, tree.steps)
+    if isinstance(tree, ExpertStack):
+        return _F64Stack(tree)
     if isinstance(tree, np.ndarray) and tree.dtype.kind == "f":
         return tree.astype(np.float64)
     return tree

@@ -13,6 +13,7 @@ STATIC_WORKSPACE_BYTES = 64 << 20  # SPECDEC_STATIC_WORKSPACE_BYTES
 TREE_MAX_DEPTH = TREE_MAX_WIDTH = 16
 F32, BF16 = 0, 1
 HEAD_CLUSTERED, HEAD_FULL = 0, 1
+WF_DENSE, WF_Q4 = 0, 1
 ACCEPT_COMMIT = 1
 DEVERR_CAPACITY, DEVERR_NAN, DEVERR_TOKEN = 1, 2, 4
 PACK_PLAIN, PACK_ROPE, PACK_GATE_UP = 0, 1, 2
@@ -27,7 +28,7 @@ EXPORTS = [
     "specdec_destroy",
     "specdec_draft", "specdec_draft_traced", "specdec_draft_tree", "specdec_verify",
     "specdec_verify_tree", "specdec_accept_tree", "specdec_accept", "specdec_kv_commit",
-    "specdec_pack_matrix", "specdec_set_len_bound", "specdec_read_device_error",
+    "specdec_pack_matrix", "specdec_q4_bytes", "specdec_pack_q4", "specdec_set_len_bound", "specdec_read_device_error",
     "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
     "specdec_moe_usage_start", "specdec_moe_usage_read", "specdec_k_policy_init",
     "specdec_k_policy_observe", "specdec_k_policy_acceptance", "specdec_k_policy_choose",
@@ -40,7 +41,8 @@ class Config(C.Structure):
         "n_experts", "top_k", "expert_ffn", "shared_ffn",
         "d_layers", "d_dim", "d_ffn", "n_centroids", "kv_src_layer", "dtype")] + [
         ("rms_eps", C.c_float), ("rope_theta", C.c_float)] + [
-        (n, C.c_int32) for n in ("max_batch", "max_draft", "max_rows", "max_ctx")]
+        (n, C.c_int32) for n in ("max_batch", "max_draft", "max_rows", "max_ctx",
+                                 "weight_format")]
 
 
 class Weights(C.Structure):
@@ -96,6 +98,8 @@ def load(path: str = LIB_PATH):
         "specdec_accept": (C.c_int, [vp, i32, i32, vp, vp, vp, vp, u32, vp]),
         "specdec_kv_commit": (C.c_int, [vp, i32, vp, vp]),
         "specdec_pack_matrix": (C.c_int, [vp, vp, i32, i32, i32, i32, i32, i32, vp]),
+        "specdec_q4_bytes": (sz, [i32, i32]),
+        "specdec_pack_q4": (C.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "specdec_set_len_bound": (C.c_int, [vp, P(i32), i32]),
         "specdec_read_device_error": (C.c_int, [vp, P(i32), i32, vp]),
         "specdec_profile_start": (C.c_int, [vp, i32, i32]),

@@ -22,7 +22,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
 
 # the GEMM's (storage type, M-tile count) instantiations compile in translation units of their own
-SOURCES = ["gemm.hip", *[f"gemm_{t}_m{m}.hip" for t in ("bf16", "f32") for m in (1, 2, 4)],
+SOURCES = ["gemm.hip", *[f"gemm_{t}_m{m}.hip" for t in ("bf16", "f32", "q4") for m in (1, 2, 4)],
            "attention.hip", "misc.hip", "specdec.cpp", "policy.cpp"]
 LIB = os.path.join(HERE, "libspecdec.so")
 

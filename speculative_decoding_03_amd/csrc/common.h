@@ -9,6 +9,7 @@ namespace specdec {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 constexpr int TILE_N = 16;       // rows of W (output features) per packed tile
@@ -54,6 +55,32 @@ __host__ __device__ __forceinline__ size_t packed_offset(int n, int k, int nkb) 
   const size_t tile = (size_t)(n >> 4) * (size_t)nkb + (size_t)(k >> 5);
   const int lane = (((k & 31) >> 3) << 4) | (n & 15);
   return tile * TILE_ELEMS + (size_t)lane * LANE_ELEMS + (k & 7);
+}
+
+// The 4-bit block weight format (one fp16 step per 32 reduction elements, 4-bit codes, weight =
+// step * (code - 8)): a 16-row tile and a group of 128 reduction elements take Q4_BLOCK_BYTES,
+// the codes first (lane kg*16 + r: 16 bytes, dword kb holding the 8 codes of row r at
+// k = kb*32 + kg*8 + 0..7: elements 0, 2, 4, 6 in bits 0-15, 1, 3, 5, 7 in bits 16-31, four bits
+// each from the lowest), then row r's four steps at Q4_CODE_BYTES + 8r.  Blocks are stored tile
+// by tile, each tile's k-groups in order.
+constexpr int Q4_GROUP_K = 128;
+constexpr int Q4_CODE_BYTES = 1024;
+constexpr int Q4_BLOCK_BYTES = 1152;
+
+__host__ __device__ inline size_t q4_block_offset(int n, int k, int nkb) {
+  return ((size_t)(n >> 4) * (size_t)(nkb >> 2) + (size_t)(k >> 7)) * Q4_BLOCK_BYTES;
+}
+
+// Weights (n, k0 .. k0+7) of a 4-bit block matrix as fp32 (exact: an fp16 step times a small
+// integer), k0 a multiple of 8.
+__device__ __forceinline__ void q4_run8(const uint8_t* W, int n, int k0, int nkb, float (&v)[8]) {
+  const uint8_t* blk = W + q4_block_offset(n, k0, nkb);
+  const int kb = (k0 >> 5) & 3, kg = (k0 >> 3) & 3, r = n & 15;
+  const uint32_t c = *reinterpret_cast<const uint32_t*>(blk + (kg * 16 + r) * 16 + kb * 4);
+  const uint16_t h = *reinterpret_cast<const uint16_t*>(blk + Q4_CODE_BYTES + r * 8 + kb * 2);
+  const float d = (float)__builtin_bit_cast(_Float16, h);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = d * (float)((int)((c >> ((e & 1) * 16 + (e >> 1) * 4)) & 15u) - 8);
 }
 
 // Device-scope fences / atomics for the split-K "last arriver" reduction.

@@ -3,6 +3,6 @@
 
 namespace specdec {
 namespace gemm_detail {
-template hipError_t dispatch_epi<float, 4>(int, int, const GemmArgs&, hipStream_t, const LaunchTiming*);
+template hipError_t dispatch_epi<float, 4, false>(int, int, const GemmArgs&, hipStream_t, const LaunchTiming*);
 }  // namespace gemm_detail
 }  // namespace specdec

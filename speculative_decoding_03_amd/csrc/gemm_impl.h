@@ -1,13 +1,15 @@
 // Weight-streaming skinny GEMM: the kernel template and its launch dispatch.  Each
-// (storage type, M-tile count) instantiation of dispatch_epi is compiled in a translation unit
-// of its own (gemm_<type>_m<MT>.hip) so that the instantiations build in parallel; gemm.hip
+// (weight format, M-tile count) instantiation of dispatch_epi is compiled in a translation unit
+// of its own (gemm_<format>_m<MT>.hip) so that the instantiations build in parallel; gemm.hip
 // holds the entry point.
 //
 // Y[M][N] = X[M][Kd] . W[N][Kd]^T with W in the packed tile layout: each wave streams whole
 // 1 KB tiles (bf16) with one 16-byte load per lane, so every weight byte is read from HBM
 // exactly once per call and every wave load is fully contiguous.  The rows of X are padded to
 // the 16-row MFMA tile; v_mfma_f32_16x16x32_bf16 (fp32: eight v_mfma_f32_16x16x4f32) does the
-// contraction.
+// contraction.  Weights may instead be in the 4-bit block format (one fp16 step per 32 weights):
+// 1152-byte blocks of a 16-row tile and 128 reduction elements, one 16-byte code load per lane
+// per block, expanded in registers to the same MFMA operand (q4_* below).
 //
 // Work split: a workgroup of NW waves owns UPW units (a unit = NU consecutive 16-row tiles, or a
 // listed tile); the reduction axis of each unit is split over KW = NW / UPW waves, and the KW
@@ -94,6 +96,203 @@ __device__ __forceinline__ void quad_frag_rt(Frag<T>& f, const Frag<T>& q, int j
   }
 }
 
+
+// ---- 4-bit block weights ----
+// A lane's share of one (tile, k-group) block: 16 bytes of codes (four k-blocks of its 8
+// elements) and the four fp16 steps of its row.  The code fragment of k-block j becomes the bf16
+// MFMA operand 128 + code exactly (the code ORed into the mantissa of 128.0); a second product
+// against the constant -136 gives the row sums of X times -136, which, fed in as the accumulator
+// input, leaves X . (code - 8), and the k-block's step multiplies that in fp32.  The offset product
+// depends only on X, so it is shared by every tile of the unit.
+struct Q4Frag {
+  u32x4 code;
+  u32x2 step;
+};
+
+template <bool WC>
+__device__ __forceinline__ void load_q4(Q4Frag& f, const uint8_t* W, size_t tile, int ngk, int g,
+                                        int lane) {
+  const uint8_t* blk = W + (tile * (size_t)ngk + (size_t)g) * Q4_BLOCK_BYTES;
+  const u32x4* pc = reinterpret_cast<const u32x4*>(blk + lane * 16);
+  const u32x2* ps = reinterpret_cast<const u32x2*>(blk + Q4_CODE_BYTES + (lane & 15) * 8);
+  if constexpr (WC) {
+    f.code = *pc;
+    f.step = *ps;
+  } else {
+    f.code = __builtin_nontemporal_load(pc);
+    f.step = __builtin_nontemporal_load(ps);
+  }
+}
+
+// The two constants of the expansion, held in registers (made opaque once per kernel) so that
+// each dword takes one v_and_or_b32 instead of an AND and an OR with literal operands.
+struct Q4Consts {
+  uint32_t mask, magic;
+};
+__device__ __forceinline__ Q4Consts q4_consts() {
+  Q4Consts k{0x000F000Fu, 0x43004300u};
+  asm volatile("" : "+s"(k.mask));
+  asm volatile("" : "+v"(k.magic));
+  return k;
+}
+
+__device__ __forceinline__ Frag<bf16_t> q4_operand(uint32_t c, const Q4Consts& k) {
+  Frag<bf16_t> f;
+  f.v = u32x4{(c & k.mask) | k.magic, ((c >> 4) & k.mask) | k.magic, ((c >> 8) & k.mask) | k.magic,
+              ((c >> 12) & k.mask) | k.magic};
+  return f;
+}
+
+__device__ __forceinline__ float q4_step(const Q4Frag& f, int j) {
+  const uint32_t w = f.step[j >> 1];
+  const uint16_t h = (j & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// X . (-136)^T: the accumulator input that turns X . (128 + code)^T into X . (code - 8)^T
+__device__ __forceinline__ f32x4 q4_offset(const Frag<bf16_t>& xf) {
+  Frag<bf16_t> m;
+  m.v = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+  return mma<bf16_t>(xf, m, f32x4{0.f, 0.f, 0.f, 0.f});
+}
+
+__device__ __forceinline__ void q4_block(f32x4& acc, const Frag<bf16_t>& xf, const Frag<bf16_t>& wf,
+                                         float d, const f32x4& off) {
+  const f32x4 t = mma<bf16_t>(xf, wf, off);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, t[i], acc[i]);
+}
+
+// The main loops over the k-groups [g0, g1) for 4-bit block weights: X in the quad layout (at
+// most 4 rows, one M-tile) or row-major (ML leading M-tiles).  The same ring of register stages
+// as the bf16 loops; per k-block the operations are the same in both, so a row's result does not
+// depend on the layout its call used.
+template <int NU, bool WC>
+__device__ __forceinline__ void q4_quad_loop(const GemmArgs& a, const size_t (&wt_tile)[NU], int g0,
+                                             int g1, int lane, f32x4 (&acc)[NU][1]) {
+  constexpr int GU = NU >= 2 ? 1 : 2;  // k-groups per batch
+  constexpr int S = 2;
+  const uint8_t* W = reinterpret_cast<const uint8_t*>(a.W);
+  const int ngk = a.nkb >> 2;
+  const bf16_t* Xq = reinterpret_cast<const bf16_t*>(a.X) + (size_t)lane * 8;
+  const Q4Consts kq = q4_consts();
+  Q4Frag w[S][GU][NU];
+  Frag<bf16_t> xq[S][GU];
+  auto load_batch = [&](int st, int gb) {
+#pragma unroll
+    for (int gu = 0; gu < GU; ++gu) {
+#pragma unroll
+      for (int t = 0; t < NU; ++t) load_q4<WC>(w[st][gu][t], W, wt_tile[t], ngk, gb + gu, lane);
+      load_frag<bf16_t>(xq[st][gu], Xq + (size_t)(gb + gu) * 512);
+    }
+  };
+  auto mul_group = [&](const Q4Frag (&wg)[NU], const Frag<bf16_t>& q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Frag<bf16_t> xf;
+      quad_frag_rt<bf16_t>(xf, q, j);
+      const f32x4 off = q4_offset(xf);
+#pragma unroll
+      for (int t = 0; t < NU; ++t) q4_block(acc[t][0], xf, q4_operand(wg[t].code[j], kq), q4_step(wg[t], j), off);
+    }
+  };
+  const int nb = max(0, (g1 - g0) / GU);
+  if (nb > 0) {
+    auto g_of = [&](int i) { return g0 + min(i, nb - 1) * GU; };
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) load_batch(st, g_of(st));
+    const int G = nb / S;
+    for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+      for (int st = 0; st < S; ++st) {
+        load_batch((st + S - 1) % S, g_of(gi * S + st + S - 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int gu = 0; gu < GU; ++gu) mul_group(w[st][gu], xq[st][gu]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const int r = nb - G * S;
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      if (st < r) {
+#pragma unroll
+        for (int gu = 0; gu < GU; ++gu) mul_group(w[st][gu], xq[st][gu]);
+      }
+  }
+  for (int g = g0 + nb * GU; g < g1; ++g) {
+    Q4Frag wt[NU];
+    Frag<bf16_t> q;
+#pragma unroll
+    for (int t = 0; t < NU; ++t) load_q4<WC>(wt[t], W, wt_tile[t], ngk, g, lane);
+    load_frag<bf16_t>(q, Xq + (size_t)g * 512);
+    mul_group(wt, q);
+  }
+}
+
+template <int ML, int NU, int MT, bool WC>
+__device__ __forceinline__ void q4_row_loop(const GemmArgs& a, const size_t (&wt_tile)[NU],
+                                            const int (&xr)[MT], int g0, int g1, int lane,
+                                            f32x4 (&acc)[NU][MT]) {
+  constexpr int S = 2;
+  const uint8_t* W = reinterpret_cast<const uint8_t*>(a.W);
+  const int ngk = a.nkb >> 2;
+  const bf16_t* Xb = reinterpret_cast<const bf16_t*>(a.X);
+  const int kl = (lane >> 4) << 3;
+  int xrow[ML];
+  bool xok[ML];
+#pragma unroll
+  for (int mt = 0; mt < ML; ++mt) {
+    xok[mt] = xr[mt] >= 0;
+    xrow[mt] = xok[mt] ? xr[mt] : 0;
+  }
+  const Q4Consts kq = q4_consts();
+  Q4Frag w[S][NU];
+  Frag<bf16_t> x[S][4][ML];
+  auto load_batch = [&](int st, int g) {
+#pragma unroll
+    for (int t = 0; t < NU; ++t) load_q4<WC>(w[st][t], W, wt_tile[t], ngk, g, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mt = 0; mt < ML; ++mt)
+        load_frag<bf16_t>(x[st][j][mt], Xb + x_offset(a.x_qx, xrow[mt], (4 * g + j) * TILE_K + kl, a.ldx));
+  };
+  auto mul_group = [&](const Q4Frag (&wg)[NU], Frag<bf16_t> (&xg)[4][ML]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 off[ML];
+#pragma unroll
+      for (int mt = 0; mt < ML; ++mt) {
+        if (!xok[mt]) zero_frag(xg[j][mt]);
+        off[mt] = q4_offset(xg[j][mt]);
+      }
+#pragma unroll
+      for (int t = 0; t < NU; ++t) {
+        const Frag<bf16_t> wf = q4_operand(wg[t].code[j], kq);
+        const float d = q4_step(wg[t], j);
+#pragma unroll
+        for (int mt = 0; mt < ML; ++mt) q4_block(acc[t][mt], xg[j][mt], wf, d, off[mt]);
+      }
+    }
+  };
+  const int nb = max(0, g1 - g0);
+  if (nb > 0) {
+    auto g_of = [&](int i) { return g0 + min(i, nb - 1); };
+    load_batch(0, g_of(0));
+    const int G = nb / S;
+    for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+      for (int st = 0; st < S; ++st) {
+        load_batch((st + 1) % S, g_of(gi * S + st + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        mul_group(w[st], x[st]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (nb - G * S > 0) mul_group(w[0], x[0]);
+  }
+}
 
 // Row-scale partial sums of up to 4 rows with n_yssq <= 64 * RS_J, loaded into registers after the
 // main loop and before the split-K reduction, so that their latency overlaps its barriers.
@@ -465,7 +664,7 @@ template <int NU, int MT> struct Unroll {
   static constexpr int U = base / MT > 1 ? base / MT : 1;
 };
 
-template <typename T, int MT, int NU, int EPI, int NW, bool WC>
+template <typename T, int MT, int NU, int EPI, int NW, bool WC, bool Q4>
 __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   __shared__ f32x4 red[NW * NU * 64];
   const int lane = threadIdx.x & (WAVE - 1);
@@ -519,8 +718,27 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     row_scale_load(a, lane, rs);
   }
 
-  bool quad_done = false;
-  if constexpr (MT == 1 && !GROUPED) {
+  if constexpr (Q4) {
+    if (active) {
+      size_t wt_tile[NU];
+#pragma unroll
+      for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);
+      const int g0 = kb0 >> 2, g1 = kb1 >> 2;
+      bool later_rows = false;  // does any M-tile after the first hold a row (wave-uniform)?
+#pragma unroll
+      for (int mt = 1; mt < MT; ++mt) later_rows |= __ballot(xr[mt] >= 0) != 0ull;
+      if constexpr (MT == 1 && !GROUPED) {
+        if (a.x_qx) q4_quad_loop<NU, WC>(a, wt_tile, g0, g1, lane, acc);
+        else q4_row_loop<1, NU, MT, WC>(a, wt_tile, xr, g0, g1, lane, acc);
+      } else if (MT == 1 || !later_rows) {
+        q4_row_loop<1, NU, MT, WC>(a, wt_tile, xr, g0, g1, lane, acc);
+      } else {
+        q4_row_loop<MT, NU, MT, WC>(a, wt_tile, xr, g0, g1, lane, acc);
+      }
+    }
+  }
+  bool quad_done = Q4;
+  if constexpr (MT == 1 && !GROUPED && !Q4) {
     if (active && a.x_qx) {
       // X in the quad layout (at most 4 rows): one wave load per four k-blocks, shared by the
       // batch's k-blocks through DPP row shifts.  kb0 is a multiple of 4.
@@ -602,7 +820,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
       quad_done = true;
     }
   }
-  if (active && !quad_done) {
+  if constexpr (!Q4) if (active && !quad_done) {
     // Row-major X: the same ring of register stages as above.  Loads are branch-free: a tile past
     // the matrix reads the last one (its sums are never stored) and a row that does not exist reads
     // row 0, zeroed by a per-lane select before its product.  Only the leading M-tiles that hold a
@@ -716,55 +934,56 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, rs, pre, lane);
 }
 
-template <typename T, int MT, int NU, int EPI, int NW, bool WC>
+template <typename T, int MT, int NU, int EPI, int NW, bool WC, bool Q4>
 hipError_t launch_wc(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   const int upw = NW / a.KW;
   dim3 grid((a.n_units + upw - 1) / upw), block(NW * 64);
   if (tm)
-    hipExtLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW, WC>), grid, block, 0, st, tm->start,
+    hipExtLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW, WC, Q4>), grid, block, 0, st, tm->start,
                           tm->stop, 0, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW, WC>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<T, MT, NU, EPI, NW, WC, Q4>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-template <typename T, int MT, int NU, int EPI, int NW>
+template <typename T, int MT, int NU, int EPI, int NW, bool Q4>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
-  return a.w_cached ? launch_wc<T, MT, NU, EPI, NW, true>(a, st, tm)
-                    : launch_wc<T, MT, NU, EPI, NW, false>(a, st, tm);
+  return a.w_cached ? launch_wc<T, MT, NU, EPI, NW, true, Q4>(a, st, tm)
+                    : launch_wc<T, MT, NU, EPI, NW, false, Q4>(a, st, tm);
 }
 
-template <typename T, int MT, int NU, int EPI>
+template <typename T, int MT, int NU, int EPI, bool Q4>
 hipError_t launch_nw(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   if constexpr (NU < 4) {
-    if (a.NW == 16) return launch_t<T, MT, NU, EPI, 16>(a, st, tm);
+    if (a.NW == 16) return launch_t<T, MT, NU, EPI, 16, Q4>(a, st, tm);
   }
-  if (a.NW == 8) return launch_t<T, MT, NU, EPI, 8>(a, st, tm);
-  if (a.NW == 4) return launch_t<T, MT, NU, EPI, 4>(a, st, tm);
+  if (a.NW == 8) return launch_t<T, MT, NU, EPI, 8, Q4>(a, st, tm);
+  if (a.NW == 4) return launch_t<T, MT, NU, EPI, 4, Q4>(a, st, tm);
   return hipErrorInvalidValue;
 }
 
-template <typename T, int MT>
+// Q4: 4-bit block weights (bf16 activations only)
+template <typename T, int MT, bool Q4>
 hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st,
                        const LaunchTiming* tm) {
-  if (epi == EPI_STORE && NU == 1) return launch_nw<T, MT, 1, EPI_STORE>(a, st, tm);
-  if (epi == EPI_STORE && NU == 2) return launch_nw<T, MT, 2, EPI_STORE>(a, st, tm);
-  if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE>(a, st, tm);
-  if (epi == EPI_ROPE && NU == 2) return launch_nw<T, MT, 2, EPI_ROPE>(a, st, tm);
-  if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU>(a, st, tm);
-  if (epi == EPI_SILU_G && NU == 2) return launch_nw<T, MT, 2, EPI_SILU_G>(a, st, tm);
-  if (epi == EPI_STORE_G && NU == 1) return launch_nw<T, MT, 1, EPI_STORE_G>(a, st, tm);
-  if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX>(a, st, tm);
+  if (epi == EPI_STORE && NU == 1) return launch_nw<T, MT, 1, EPI_STORE, Q4>(a, st, tm);
+  if (epi == EPI_STORE && NU == 2) return launch_nw<T, MT, 2, EPI_STORE, Q4>(a, st, tm);
+  if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE, Q4>(a, st, tm);
+  if (epi == EPI_ROPE && NU == 2) return launch_nw<T, MT, 2, EPI_ROPE, Q4>(a, st, tm);
+  if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU, Q4>(a, st, tm);
+  if (epi == EPI_SILU_G && NU == 2) return launch_nw<T, MT, 2, EPI_SILU_G, Q4>(a, st, tm);
+  if (epi == EPI_STORE_G && NU == 1) return launch_nw<T, MT, 1, EPI_STORE_G, Q4>(a, st, tm);
+  if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX, Q4>(a, st, tm);
   return hipErrorInvalidValue;
 }
 
-template <typename T>
+template <typename T, bool Q4>
 hipError_t dispatch_mt(int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
                        const LaunchTiming* tm) {
   switch (MT) {
-    case 1: return dispatch_epi<T, 1>(NU, epi, a, st, tm);
-    case 2: return dispatch_epi<T, 2>(NU, epi, a, st, tm);
-    case 4: return dispatch_epi<T, 4>(NU, epi, a, st, tm);
+    case 1: return dispatch_epi<T, 1, Q4>(NU, epi, a, st, tm);
+    case 2: return dispatch_epi<T, 2, Q4>(NU, epi, a, st, tm);
+    case 4: return dispatch_epi<T, 4, Q4>(NU, epi, a, st, tm);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,6 +36,8 @@ struct GemmArgs {
   // weights read again soon that fit in the last-level cache (the drafter's): plain loads;
   // otherwise (the target's, streamed once per step) non-temporal loads
   int w_cached = 0;
+  // weights in the 4-bit block format (common.h): bf16 activations only, nkb % 4 == 0
+  int wq4 = 0;
   int M = 0;
   // grouped launches (EPI_*_G): unit u computes group g = group_list[u / units_per_group]
   // (n_groups_dev[0] groups are listed), tiles g*tiles_per_group + (u % units_per_group)*NU.
@@ -110,6 +112,13 @@ struct LaunchTiming {
 hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
                        const LaunchTiming* tm = nullptr);
 
+// The 4-bit block weight format (common.h): a matrix [N][Kd] with N % 16 == 0 and
+// Kd % 128 == 0 takes q4_bytes(N, Kd) bytes.  launch_pack_q4 writes it from codes [N][Kd] (one
+// byte each, 0..15) and fp16 steps [N][Kd / 32], rows permuted by `kind` as launch_pack does.
+__host__ __device__ inline size_t q4_bytes(size_t N, size_t Kd) { return N * Kd / 2 + N * (Kd / 32) * 2; }
+hipError_t launch_pack_q4(const uint8_t* q, const uint16_t* steps, void* dst, int N, int Kd,
+                          int kind, int hd, int split_rows, hipStream_t st);
+
 // Grouped-query attention of R query rows per sequence over one layer's cache: K [pos][hd],
 // V transposed [hd][pos].
 // Row i of sequence b sees keys [0, len[b] + i + key_off).  Chunks of CH keys at fixed absolute
@@ -154,7 +163,7 @@ bool attention_supported(int head_dim);     // head sizes the attention kernel i
 // Misc kernels (misc.hip).
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
                         float* x, float* ssq, void* xw, int xw_qx, const float* norm, int vocab,
-                        int* err, hipStream_t st);
+                        int* err, hipStream_t st, int e_q4 = 0);
 hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts, int ld_amax,
                          int B, int R, const int* tokens, int* out_tokens, int* n_emit,
                          int* next_tok, int commit, int* len, float* hid, const float* X, int d,
@@ -164,7 +173,7 @@ hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid
 hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
                               int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
                               const float* norm_e, int d, int Dd, float eps, void* u, int u_qx,
-                              int B, int* err, hipStream_t st, int h_div = 1);
+                              int B, int* err, hipStream_t st, int h_div = 1, int t_q4 = 0);
 // Tree drafts (misc.hip): the first level's top-w tokens, the later levels' per-branch tokens,
 // the acceptance walk over a tree and the compaction of the accepted path's cache entries.
 hipError_t launch_tree_top(const float* scores, int vocab, const int* unit_tile, int units_per_seq,

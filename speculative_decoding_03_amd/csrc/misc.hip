@@ -37,8 +37,21 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* rv, int* r
 // x[m], from which the consumer forms the RMSNorm row scale.  Grid (d / 8 / 256 rounded up, M):
 // each thread moves one run of 8 consecutive elements (contiguous in the packed table), and the
 // two threads of a 16-column tile (adjacent lanes) add their sums with one lane exchange.
-template <typename T>
-__global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, const int* tokens,
+// One run of 8 consecutive weights of row n as fp32: dtype elements of a packed matrix, or the
+// 4-bit block format (Q4).
+template <typename T, bool Q4>
+__device__ __forceinline__ void row_run8(const void* W, int n, int k8, int nkb, float (&v)[8]) {
+  if constexpr (Q4) {
+    q4_run8(reinterpret_cast<const uint8_t*>(W), n, k8, nkb, v);
+  } else {
+    Frag<T> f;
+    load_frag<T>(f, reinterpret_cast<const T*>(W) + packed_offset(n, k8, nkb));
+    frag_values<T>(f, v);
+  }
+}
+
+template <typename T, bool Q4>
+__global__ void __launch_bounds__(256) embed_kernel(const void* E, int nkb, int d, const int* tokens,
                                                     int M, float* x, float* ssq, T* xw, int xw_qx,
                                                     const float* norm, int vocab, int* err) {
   const int m = blockIdx.y;
@@ -51,10 +64,8 @@ __global__ void __launch_bounds__(256) embed_kernel(const T* E, int nkb, int d, 
   }
   float sq = 0.f;
   if (k8 < d) {
-    Frag<T> f;
-    load_frag<T>(f, E + packed_offset(tok, k8, nkb));
     float v[8], y[8];
-    frag_values<T>(f, v);
+    row_run8<T, Q4>(E, tok, k8, nkb, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       y[e] = v[e] * norm[k8 + e];
@@ -193,9 +204,9 @@ __global__ void __launch_bounds__(256) commit_kernel(const int* n_commit, int R,
 // u[b] = [ rms(h[b]) * norm_h ; rms(table[row(tok[b])]) * norm_e ] in the storage dtype.
 // h is requested first, as 16-byte runs held in registers (when d <= 4 * HV * blockDim.x), so its
 // latency overlaps the token -> table-row lookup; both sums of squares share one block reduction.
-template <typename T>
+template <typename T, bool Q4>
 __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const int* tok,
-                                                          const T* table, int nkb_table,
+                                                          const void* table, int nkb_table,
                                                           const int* vocab_row, int vocab,
                                                           const float* norm_h, const float* norm_e,
                                                           int d, int Dd, float eps, T* u, int u_qx,
@@ -223,10 +234,8 @@ __global__ void __launch_bounds__(256) draft_input_kernel(const float* h, const 
   const int row = vocab_row[c];
   float sse = 0.f;
   for (int k8 = t * 8; k8 < Dd; k8 += blockDim.x * 8) {
-    Frag<T> f;
-    load_frag<T>(f, table + packed_offset(row, k8, nkb_table));
     float v[8];
-    frag_values<T>(f, v);
+    row_run8<T, Q4>(table, row, k8, nkb_table, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       ebuf[k8 + e] = v[e];
@@ -489,6 +498,40 @@ __global__ void pack_kernel(const T* src, T* dst, int N, int Kd, int kind, int h
   }
 }
 
+// 4-bit block matrix from codes [N][Kd] (bytes, low 4 bits used) and fp16 steps [N][Kd/32], rows
+// permuted as pack_kernel does.  One thread per (row, run of 8 codes): it writes the run's code
+// dword, and the first run of each 32-block also writes the block's step.
+__global__ void pack_q4_kernel(const uint8_t* q, const uint16_t* steps, uint8_t* dst, int N, int Kd,
+                               int kind, int hd, int F) {
+  const int runs = Kd / 8;
+  const size_t total = (size_t)N * runs;
+  const int nkb = Kd / TILE_K;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int n = (int)(e / runs);
+    const int k0 = (int)(e - (size_t)n * runs) * 8;
+    int sr = n;
+    if (kind == 1) {
+      const int head = n / hd, p = n - head * hd;
+      sr = head * hd + (p >> 1) + (p & 1) * (hd >> 1);
+    } else if (kind == 2) {
+      const int g = n / (2 * F), nl = n - g * 2 * F;
+      const int tile = nl >> 4;
+      sr = g * 2 * F + (tile & 1) * F + (tile >> 1) * TILE_N + (nl & 15);
+    }
+    const uint8_t* src = q + (size_t)sr * Kd + k0;
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c |= (uint32_t)(src[i] & 15u) << ((i & 1) * 16 + (i >> 1) * 4);
+    uint8_t* blk = dst + q4_block_offset(n, k0, nkb);
+    const int kb = (k0 >> 5) & 3, kg = (k0 >> 3) & 3, r = n & 15;
+    *reinterpret_cast<uint32_t*>(blk + (kg * 16 + r) * 16 + kb * 4) = c;
+    if (kg == 0)
+      *reinterpret_cast<uint16_t*>(blk + Q4_CODE_BYTES + r * 8 + kb * 2) =
+          steps[(size_t)sr * (Kd / 32) + (k0 >> 5)];
+  }
+}
+
 // ---- tree drafts ----
 
 // Inject-or-keep of one drafted tree node: the table entry (len + depth) * n_slots + slot, when
@@ -742,17 +785,21 @@ __global__ void fill_i32_kernel(int* p, int v, size_t n) {
 
 hipError_t launch_embed(int dtype, const void* E, int nkb, int d, const int* tokens, int M,
                         float* x, float* ssq, void* xw, int xw_qx, const float* norm, int vocab,
-                        int* err, hipStream_t st) {
+                        int* err, hipStream_t st, int e_q4) {
   if (M <= 0) return hipSuccess;
   if (xw_qx && M > 4) return hipErrorInvalidValue;
   if (d % TILE_N) return hipErrorInvalidValue;
+  if (e_q4 && (dtype != DT_BF16 || nkb % 4)) return hipErrorInvalidValue;
   const dim3 grid((d / 8 + 255) / 256, M);
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)E, nkb, d,
-                       tokens, M, x, ssq, (bf16_t*)xw, xw_qx, norm, vocab, err);
+  if (e_q4)
+    hipLaunchKernelGGL((embed_kernel<bf16_t, true>), grid, dim3(256), 0, st, E, nkb, d, tokens, M,
+                       x, ssq, (bf16_t*)xw, xw_qx, norm, vocab, err);
+  else if (dtype == DT_BF16)
+    hipLaunchKernelGGL((embed_kernel<bf16_t, false>), grid, dim3(256), 0, st, E, nkb, d, tokens, M,
+                       x, ssq, (bf16_t*)xw, xw_qx, norm, vocab, err);
   else
-    hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), 0, st, (const float*)E, nkb, d,
-                       tokens, M, x, ssq, (float*)xw, xw_qx, norm, vocab, err);
+    hipLaunchKernelGGL((embed_kernel<float, false>), grid, dim3(256), 0, st, E, nkb, d, tokens, M,
+                       x, ssq, (float*)xw, xw_qx, norm, vocab, err);
   return hipGetLastError();
 }
 
@@ -775,17 +822,22 @@ hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid
 hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,
                               int nkb_table, const int* vocab_row, int vocab, const float* norm_h,
                               const float* norm_e, int d, int Dd, float eps, void* u, int u_qx,
-                              int B, int* err, hipStream_t st, int h_div) {
+                              int B, int* err, hipStream_t st, int h_div, int t_q4) {
   if (u_qx && B > 4) return hipErrorInvalidValue;
   if (h_div < 1) return hipErrorInvalidValue;
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(draft_input_kernel<bf16_t>, dim3(B), dim3(256), 0, st, h, tok,
-                       (const bf16_t*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
-                       eps, (bf16_t*)u, u_qx, h_div, err);
+  if (t_q4 && (dtype != DT_BF16 || nkb_table % 4)) return hipErrorInvalidValue;
+  if (t_q4)
+    hipLaunchKernelGGL((draft_input_kernel<bf16_t, true>), dim3(B), dim3(256), 0, st, h, tok, table,
+                       nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd, eps, (bf16_t*)u, u_qx,
+                       h_div, err);
+  else if (dtype == DT_BF16)
+    hipLaunchKernelGGL((draft_input_kernel<bf16_t, false>), dim3(B), dim3(256), 0, st, h, tok,
+                       table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd, eps, (bf16_t*)u,
+                       u_qx, h_div, err);
   else
-    hipLaunchKernelGGL(draft_input_kernel<float>, dim3(B), dim3(256), 0, st, h, tok,
-                       (const float*)table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd,
-                       eps, (float*)u, u_qx, h_div, err);
+    hipLaunchKernelGGL((draft_input_kernel<float, false>), dim3(B), dim3(256), 0, st, h, tok,
+                       table, nkb_table, vocab_row, vocab, norm_h, norm_e, d, Dd, eps, (float*)u,
+                       u_qx, h_div, err);
   return hipGetLastError();
 }
 
@@ -829,6 +881,15 @@ hipError_t launch_pack(int dtype, const void* src, void* dst, int N, int Kd, int
   else
     hipLaunchKernelGGL(pack_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)src,
                        (float*)dst, N, Kd, kind, hd, split_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_q4(const uint8_t* q, const uint16_t* steps, void* dst, int N, int Kd,
+                          int kind, int hd, int split_rows, hipStream_t st) {
+  const size_t total = (size_t)N * (Kd / 8);
+  const int blocks = (int)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+  hipLaunchKernelGGL(pack_q4_kernel, dim3(blocks), dim3(256), 0, st, q, steps, (uint8_t*)dst, N, Kd,
+                     kind, hd, split_rows);
   return hipGetLastError();
 }
 

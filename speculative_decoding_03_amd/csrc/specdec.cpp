@@ -164,6 +164,15 @@ bool valid_config(const specdec_config* c) {
       return false;
   }
   if (c->dtype != SPECDEC_F32 && c->dtype != SPECDEC_BF16) return false;
+  if (c->weight_format != SPECDEC_WF_DENSE && c->weight_format != SPECDEC_WF_Q4) return false;
+  if (c->weight_format == SPECDEC_WF_Q4) {
+    // 4-bit blocks: bf16 activations, whole 128-element k-groups on every reduction axis
+    const int qd = c->n_q_heads * c->head_dim;
+    if (c->dtype != SPECDEC_BF16) return false;
+    for (int k : {c->d_model, qd, c->n_experts > 0 ? c->shared_ffn : c->ffn_dim, c->d_dim, c->d_ffn})
+      if (k % 128) return false;
+    if (c->n_experts > 0 && c->expert_ffn % 128) return false;
+  }
   if (c->n_layers < 1 || c->d_model < 32 || c->n_q_heads < 1 || c->n_kv_heads < 1) return false;
   if (c->n_q_heads % c->n_kv_heads) return false;
   if (c->head_dim % 16 || c->head_dim > 256 || c->head_dim < 16) return false;
@@ -336,6 +345,7 @@ GemmArgs base_args(specdec_ctx* x, const Gemm& g, int M) {
   a.NW = g.NW;
   a.kb_per_split = g.kbps;
   a.w_cached = g.cached ? 1 : 0;
+  a.wq4 = x->cfg.weight_format == SPECDEC_WF_Q4;
   a.M = M;
   a.x_qx = a.out_qx = M <= 4;  // activations of calls with at most 4 rows use the quad layout
   a.err = at<int>(x, x->lay.err);
@@ -644,7 +654,8 @@ int verify_impl(specdec_ctx* x, int B, int R, const int32_t* tokens, float* logi
   int* err = at<int>(x, x->lay.err);
   auto lw = [&](int l, int slot) { return (const float*)x->lw[(size_t)l * SPECDEC_N_LAYER_TENSORS + slot]; };
   HIP_TRY(launch_embed(dt_of(x), x->w.embed, x->g_head.nkb, d, tokens, M, X, ssq, XW, M <= 4,
-                       lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st));
+                       lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st,
+                       c.weight_format == SPECDEC_WF_Q4));
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
   int rc;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -829,7 +840,7 @@ int drafter_body(specdec_ctx* x, int rows, int rps, const float* h, int h_div, c
   int rc;
   HIP_TRY(launch_draft_input(dt_of(x), h, tok, x->w.table, x->g_table.nkb, x->w.vocab_row, c.vocab,
                              x->w.norm_h, x->w.norm_e, d, Dd, c.rms_eps, x->ws + x->lay.u,
-                             rows <= 4, rows, err, st, h_div));
+                             rows <= 4, rows, err, st, h_div, c.weight_format == SPECDEC_WF_Q4));
   {  // input projection of [rms(h); rms(e)]; leaves x * n1 of the first drafter layer
     GemmArgs a = base_args(x, x->g_in, rows);
     a.X = x->ws + x->lay.u;
@@ -1051,6 +1062,25 @@ int specdec_pack_matrix(const void* src, void* dst, int32_t n, int32_t kd, int32
     return SPECDEC_E_INVAL;
   HIP_TRY(launch_pack(dtype == SPECDEC_BF16 ? DT_BF16 : DT_F32, src, dst, n, kd, kind, head_dim,
                       split_rows, reinterpret_cast<hipStream_t>(stream)));
+  return SPECDEC_OK;
+}
+
+size_t specdec_q4_bytes(int32_t n, int32_t kd) {
+  if (n < 16 || kd < 128 || n % 16 || kd % 128) return 0;
+  return q4_bytes((size_t)n, (size_t)kd);
+}
+
+int specdec_pack_q4(const uint8_t* codes, const uint16_t* steps, void* dst, int32_t n, int32_t kd,
+                    int32_t kind, int32_t head_dim, int32_t split_rows, void* stream) {
+  if (!codes || !steps || !dst || n < 16 || kd < 128 || n % 16 || kd % 128) return SPECDEC_E_INVAL;
+  if (reinterpret_cast<uintptr_t>(dst) % 256) return SPECDEC_E_INVAL;
+  if (kind < 0 || kind > 2) return SPECDEC_E_INVAL;
+  if (kind == SPECDEC_PACK_ROPE && (head_dim < 16 || head_dim % 16 || n % head_dim))
+    return SPECDEC_E_INVAL;
+  if (kind == SPECDEC_PACK_GATE_UP && (split_rows < 16 || split_rows % 16 || n % (2 * split_rows)))
+    return SPECDEC_E_INVAL;
+  HIP_TRY(launch_pack_q4(codes, steps, dst, n, kd, kind, head_dim, split_rows,
+                         reinterpret_cast<hipStream_t>(stream)));
   return SPECDEC_OK;
 }
 

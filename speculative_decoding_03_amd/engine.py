@@ -46,6 +46,7 @@ class Shape:
     top_k: int = 0
     expert_ffn: int = 0
     shared_ffn: int = 0
+    weight_format: str = "dense"  # "dense" (dtype elements) or "q4" (4-bit blocks)
 
     @classmethod
     def of(cls, cfg) -> "Shape":
@@ -71,6 +72,50 @@ def pack_matrix(src: torch.Tensor, n: int, kd: int, dtype: str, kind: int = F.PA
     return dst
 
 
+def pack_q4(codes: torch.Tensor, steps: torch.Tensor, n: int, kd: int, kind: int = F.PACK_PLAIN,
+            head_dim: int = 0, split_rows: int = 0, stream=None) -> torch.Tensor:
+    """Packs a logical [n][kd] 4-bit matrix (codes uint8 [n][kd], steps float16 [n][kd/32], device)
+    into the library's 4-bit block format."""
+    assert codes.is_cuda and codes.is_contiguous() and codes.dtype == torch.uint8
+    assert steps.is_cuda and steps.is_contiguous() and steps.dtype == torch.float16
+    assert codes.numel() == n * kd and steps.numel() == n * (kd // 32)
+    nbytes = F.load().specdec_q4_bytes(n, kd)
+    if nbytes == 0:
+        raise ValueError(f"no 4-bit layout for [{n}][{kd}]")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    F.check(F.load().specdec_pack_q4(_p(codes), _p(steps), _p(dst), n, kd, kind, head_dim,
+                                     split_rows, _s(stream)), "specdec_pack_q4")
+    return dst
+
+
+class _Mats:
+    """Matrix plumbing for one weight format: a dense matrix is one tensor, a 4-bit one a
+    (codes, steps) pair whose parts are concatenated and reindexed together."""
+
+    def __init__(self, source, dtype: str, q4: bool, stream):
+        self.source, self.dtype, self.q4, self.stream = source, dtype, q4, stream
+
+    def get(self, name, layer, shape):
+        return self.source.get_q4(name, layer, shape) if self.q4 else self.source.get(name, layer, shape)
+
+    def cat(self, parts, dim=0):
+        if self.q4:
+            return (torch.cat([p[0] for p in parts], dim).contiguous(),
+                    torch.cat([p[1] for p in parts], dim).contiguous())
+        return torch.cat(parts, dim).contiguous()
+
+    def rows(self, m, index):
+        if self.q4:
+            return m[0].index_select(0, index).contiguous(), m[1].index_select(0, index).contiguous()
+        return m.index_select(0, index).contiguous()
+
+    def pack(self, m, n, kd, kind=F.PACK_PLAIN, head_dim=0, split_rows=0):
+        if self.q4:
+            return pack_q4(m[0].reshape(-1), m[1].reshape(-1), n, kd, kind, head_dim, split_rows,
+                           self.stream)
+        return pack_matrix(m.reshape(-1), n, kd, self.dtype, kind, head_dim, split_rows, self.stream)
+
+
 class DeviceModel:
     """Packed device weights for one target + drafter pair.
 
@@ -91,63 +136,67 @@ class DeviceModel:
             return t.data_ptr()
 
         d, qd, kvd, F_ = s.d_model, s.q_dim, s.kv_dim, s.ffn_dim
+        q4 = s.weight_format == "q4"
+        if s.weight_format not in ("dense", "q4"):
+            raise ValueError(f"weight_format {s.weight_format!r}")
+        mm = _Mats(source, dt, q4, stream)
+        get, cat, pack = mm.get, mm.cat, mm.pack
         self.layer_ptrs = (C.c_void_p * (s.n_layers * F.N_LAYER_TENSORS))()
         for l in range(s.n_layers):
-            wq = source.get("wq", l, (qd, d))
-            wk = source.get("wk", l, (kvd, d))
-            wv = source.get("wv", l, (kvd, d))
-            qkv = torch.cat([wq, wk, wv], 0).contiguous()
-            del wq, wk, wv
+            qkv = cat([get("wq", l, (qd, d)), get("wk", l, (kvd, d)), get("wv", l, (kvd, d))])
             base = l * F.N_LAYER_TENSORS
-            self.layer_ptrs[base + F.LW_QKV] = k(pack_matrix(qkv, qd + 2 * kvd, d, dt, F.PACK_ROPE, s.head_dim, stream=stream))
+            self.layer_ptrs[base + F.LW_QKV] = k(pack(qkv, qd + 2 * kvd, d, F.PACK_ROPE, s.head_dim))
             del qkv
-            self.layer_ptrs[base + F.LW_O] = k(pack_matrix(source.get("wo", l, (d, qd)), d, qd, dt, stream=stream))
+            self.layer_ptrs[base + F.LW_O] = k(pack(get("wo", l, (d, qd)), d, qd))
             if s.n_experts > 0:
                 # shared FFN in the dense slots; router and the stacked experts in their own
                 E, Fe, Fs = s.n_experts, s.expert_ffn, s.shared_ffn
                 names = ("sh_wg", "sh_wu", "sh_wd")
-                self.layer_ptrs[base + F.LW_ROUTER] = k(pack_matrix(source.get("router", l, (E, d)), E, d, dt, stream=stream))
-                egu = torch.cat([source.get("exp_wg", l, (E, Fe, d)), source.get("exp_wu", l, (E, Fe, d))], 1).contiguous()
-                self.layer_ptrs[base + F.LW_EXP_GATE_UP] = k(pack_matrix(egu.view(-1), E * 2 * Fe, d, dt, F.PACK_GATE_UP, split_rows=Fe, stream=stream))
+                self.layer_ptrs[base + F.LW_ROUTER] = k(pack(get("router", l, (E, d)), E, d))
+                egu = cat([get("exp_wg", l, (E, Fe, d)), get("exp_wu", l, (E, Fe, d))], 1)
+                self.layer_ptrs[base + F.LW_EXP_GATE_UP] = k(pack(egu, E * 2 * Fe, d, F.PACK_GATE_UP, split_rows=Fe))
                 del egu
-                self.layer_ptrs[base + F.LW_EXP_DOWN] = k(pack_matrix(source.get("exp_wd", l, (E, d, Fe)).view(-1), E * d, Fe, dt, stream=stream))
+                self.layer_ptrs[base + F.LW_EXP_DOWN] = k(pack(get("exp_wd", l, (E, d, Fe)), E * d, Fe))
             else:
                 Fs, names = F_, ("wg", "wu", "wd")
-            gu = torch.cat([source.get(names[0], l, (Fs, d)), source.get(names[1], l, (Fs, d))], 0).contiguous()
-            self.layer_ptrs[base + F.LW_GATE_UP] = k(pack_matrix(gu, 2 * Fs, d, dt, F.PACK_GATE_UP, split_rows=Fs, stream=stream))
+            gu = cat([get(names[0], l, (Fs, d)), get(names[1], l, (Fs, d))])
+            self.layer_ptrs[base + F.LW_GATE_UP] = k(pack(gu, 2 * Fs, d, F.PACK_GATE_UP, split_rows=Fs))
             del gu
-            self.layer_ptrs[base + F.LW_DOWN] = k(pack_matrix(source.get(names[2], l, (d, Fs)), d, Fs, dt, stream=stream))
+            self.layer_ptrs[base + F.LW_DOWN] = k(pack(get(names[2], l, (d, Fs)), d, Fs))
             self.layer_ptrs[base + F.LW_ATTN_NORM] = k(source.get("attn_norm", l, (d,)).float().contiguous())
             self.layer_ptrs[base + F.LW_FFN_NORM] = k(source.get("ffn_norm", l, (d,)).float().contiguous())
-        self.embed = pack_matrix(source.get("embed", 0, (s.vocab, d)), s.vocab, d, dt, stream=stream)
+        self.embed = pack(get("embed", 0, (s.vocab, d)), s.vocab, d)
         self.final_norm = source.get("final_norm", 0, (d,)).float().contiguous()
 
         D, Fd = s.d_dim, s.d_ffn
         perm = perm.to(device=device, dtype=torch.int64)
-        table = source.get("table", 0, (s.vocab, D))
-        self.table = pack_matrix(table.index_select(0, perm).contiguous(), s.vocab, D, dt, stream=stream)
+        table = get("table", 0, (s.vocab, D))
+        self.table = pack(mm.rows(table, perm), s.vocab, D)
         del table
         self.row_vocab = perm.to(torch.int32).contiguous()
         inv = torch.empty_like(perm)
         inv[perm] = torch.arange(s.vocab, device=device, dtype=torch.int64)
         self.vocab_row = inv.to(torch.int32).contiguous()
-        self.centroids = pack_matrix(centroids.to(device=device, dtype=TORCH_DT[dt]).contiguous(),
-                                     s.n_centroids, D, dt, stream=stream)
+        if q4:
+            self.centroids = pack(centroids, s.n_centroids, D)
+        else:
+            self.centroids = pack(centroids.to(device=device, dtype=TORCH_DT[dt]).contiguous(),
+                                  s.n_centroids, D)
         self.norm_h = source.get("norm_h", 0, (d,)).float().contiguous()
         self.norm_e = source.get("norm_e", 0, (D,)).float().contiguous()
-        self.w_in = pack_matrix(source.get("w_in", 0, (D, d + D)), D, d + D, dt, stream=stream)
+        self.w_in = pack(get("w_in", 0, (D, d + D)), D, d + D)
         self.norm_f = source.get("d_nf", 0, (D,)).float().contiguous()
-        self.w_back = pack_matrix(source.get("w_back", 0, (d, D)), d, D, dt, stream=stream)
+        self.w_back = pack(get("w_back", 0, (d, D)), d, D)
         self.dlayer_ptrs = (C.c_void_p * (s.d_layers * F.N_DRAFT_TENSORS))()
         for l in range(s.d_layers):
             base = l * F.N_DRAFT_TENSORS
             self.dlayer_ptrs[base + F.DW_N1] = k(source.get("d_n1", l, (D,)).float().contiguous())
             self.dlayer_ptrs[base + F.DW_N2] = k(source.get("d_n2", l, (D,)).float().contiguous())
-            self.dlayer_ptrs[base + F.DW_Q] = k(pack_matrix(source.get("d_wq", l, (qd, D)), qd, D, dt, F.PACK_ROPE, s.head_dim, stream=stream))
-            self.dlayer_ptrs[base + F.DW_O] = k(pack_matrix(source.get("d_wo", l, (D, qd)), D, qd, dt, stream=stream))
-            gu = torch.cat([source.get("d_wg", l, (Fd, D)), source.get("d_wu", l, (Fd, D))], 0).contiguous()
-            self.dlayer_ptrs[base + F.DW_GATE_UP] = k(pack_matrix(gu, 2 * Fd, D, dt, F.PACK_GATE_UP, split_rows=Fd, stream=stream))
-            self.dlayer_ptrs[base + F.DW_DOWN] = k(pack_matrix(source.get("d_wd", l, (D, Fd)), D, Fd, dt, stream=stream))
+            self.dlayer_ptrs[base + F.DW_Q] = k(pack(get("d_wq", l, (qd, D)), qd, D, F.PACK_ROPE, s.head_dim))
+            self.dlayer_ptrs[base + F.DW_O] = k(pack(get("d_wo", l, (D, qd)), D, qd))
+            gu = cat([get("d_wg", l, (Fd, D)), get("d_wu", l, (Fd, D))])
+            self.dlayer_ptrs[base + F.DW_GATE_UP] = k(pack(gu, 2 * Fd, D, F.PACK_GATE_UP, split_rows=Fd))
+            self.dlayer_ptrs[base + F.DW_DOWN] = k(pack(get("d_wd", l, (D, Fd)), D, Fd))
 
     def abi(self) -> F.Weights:
         w = F.Weights()
@@ -196,6 +245,7 @@ class Engine:
         cfg.rms_eps = s.rms_eps
         cfg.rope_theta = s.rope_theta
         cfg.max_batch, cfg.max_draft, cfg.max_rows, cfg.max_ctx = max_batch, max_draft, max_rows, max_ctx
+        cfg.weight_format = F.WF_Q4 if s.weight_format == "q4" else F.WF_DENSE
         self.cfg = cfg
         self.max_batch, self.max_draft, self.max_rows, self.max_ctx = max_batch, max_draft, max_rows, max_ctx
         ws = lib.specdec_workspace_bytes(C.byref(cfg))

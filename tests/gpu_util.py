@@ -183,12 +183,24 @@ def oracle_model(cfg):
 
 def host_embedding(cfg) -> np.ndarray:
     """The tied embedding / LM head [V][d] as float32 on the host, made by the device fill of the
-    seeded input generator (bit-identical to the host generator, spot-checked here)."""
-    t = WD.DeviceSource(cfg).get("embed", 0, (cfg.vocab, cfg.d_model))
-    E = t.float().cpu().numpy()
-    del t
+    seeded input generator (bit-identical to the host generator, spot-checked here).  4-bit
+    weights are turned into values by the oracle's q4_weights, in row blocks (exact in fp32)."""
+    src = WD.DeviceSource(cfg)
+    shape = (cfg.vocab, cfg.d_model)
+    if cfg.weight_format == "q4":
+        codes, steps = src.get_q4("embed", 0, shape)
+        E = np.empty(shape, dtype=np.float32)
+        for r0 in range(0, cfg.vocab, 16384):
+            c = codes[r0:r0 + 16384].cpu().numpy()
+            d = steps[r0:r0 + 16384].cpu().numpy()
+            E[r0:r0 + 16384] = O.q4_weights(c, d)
+        del codes, steps
+    else:
+        t = src.get("embed", 0, shape)
+        E = t.float().cpu().numpy()
+        del t
     for r in (0, 12345 % cfg.vocab, cfg.vocab - 1):
-        assert np.array_equal(E[r], S.gen_rows(cfg, "embed", 0, cfg.d_model, r, 1)[0])
+        assert np.array_equal(E[r], O.as_f64(S.gen_rows(cfg, "embed", 0, cfg.d_model, r, 1))[0])
     return E
 
 

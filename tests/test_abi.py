@@ -67,8 +67,18 @@ def test_workspace_sizing_and_config_checks(lib):
            dict(n_experts=24, top_k=4, expert_ffn=128, shared_ffn=256, ffn_dim=0),
            dict(n_experts=16, top_k=17, expert_ffn=128, shared_ffn=256, ffn_dim=0),
            dict(n_experts=16, top_k=4, expert_ffn=100, shared_ffn=256, ffn_dim=0)]
+    # 4-bit blocks need bf16 and whole 128-wide groups on every reduction axis
+    bad += [dict(weight_format=2), dict(weight_format=F.WF_Q4),
+            dict(weight_format=F.WF_Q4, dtype=F.BF16, d_dim=96),
+            dict(weight_format=F.WF_Q4, dtype=F.BF16, d_model=288)]
     for kw in bad:
         assert lib.specdec_workspace_bytes(C.byref(_config(**kw))) == 0, kw
+    assert lib.specdec_workspace_bytes(C.byref(_config(weight_format=F.WF_Q4, dtype=F.BF16))) > 0
+    # the 4-bit block format's size: n*kd/2 code bytes plus an fp16 step per 32 weights
+    assert lib.specdec_q4_bytes(16, 128) == 1152
+    assert lib.specdec_q4_bytes(5120, 25600) == 5120 * 25600 * 9 // 16
+    assert lib.specdec_q4_bytes(16, 96) == 0 and lib.specdec_q4_bytes(8, 128) == 0
+    assert lib.specdec_pack_q4(None, None, None, 16, 128, 0, 0, 0, None) == F.E_INVAL
     # a mixture-of-experts configuration is valid and needs its routing buffers
     moe = _config(n_experts=16, top_k=4, expert_ffn=128, shared_ffn=256, ffn_dim=0)
     assert lib.specdec_workspace_bytes(C.byref(moe)) > 0

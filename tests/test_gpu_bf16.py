@@ -5,7 +5,9 @@ rows and its projections take the row-major activation path), 31B-class (1 layer
 mixture-of-experts (1 layer: 128 experts, top-8, shared FFN) targets keep the full width and
 the full 262144-entry vocabulary, each at its workload's committed context (2048, 4096, 8192,
 4096 positions: 16 to 64 attention chunks, so the chunk combine runs its main loop), plus an
-E2B-shaped case at 700 positions whose drafter keys end inside a chunk.  Norm weights are
+E2B-shaped case at 700 positions whose drafter keys end inside a chunk.  The 31B, E2B and
+mixture-of-experts shapes run again with every weight matrix (embedding, table and centroids
+included) in 4-bit blocks; the oracle takes the blocks' exact weights.  Norm weights are
 jittered so a dropped norm weight shows.  The oracle computes the hidden rows exactly and the
 logits over the whole vocabulary (the embedding is the seeded input generator's, made on the
 device bit-identically to the host generator).  Tolerances: max relative error 2e-2 on logits,
@@ -43,6 +45,10 @@ CASES = {
     "e4b-L1": truncated("e4b", 1, norm_jitter=0.1, d_layers=2),
     "31b-L1": truncated("31b", 1, norm_jitter=0.1, d_layers=2),
     "moe-L1": truncated("moe", 1, norm_jitter=0.1, d_layers=2),
+    # every weight matrix in 4-bit blocks (one fp16 step per 32 weights)
+    "31b-L1-q4": truncated("31b", 1, norm_jitter=0.1, d_layers=2, weight_format="q4"),
+    "e2b-L2-q4": truncated("e2b", 2, norm_jitter=0.1, d_layers=2, weight_format="q4"),
+    "moe-L1-q4": truncated("moe", 1, norm_jitter=0.1, d_layers=2, weight_format="q4"),
 }
 ROUTE_MARGIN = 0.01
 
@@ -62,7 +68,7 @@ def oracle_rows(W, cfg, cache, tokens, length, margins=None):
     receives each row's smallest routing margin over the layers (inf for a dense model)."""
     H = []
     for i, tok in enumerate(tokens):
-        x = S.gen_rows(cfg, "embed", 0, cfg.d_model, int(tok), 1)[0].astype(np.float64)
+        x = O.as_f64(S.gen_rows(cfg, "embed", 0, cfg.d_model, int(tok), 1))[0]
         tr = []
         for l, lw in enumerate(W["layers"]):
             x = O.decoder_layer_row(lw, cfg, cache.K[l], cache.V[l], x, length + i, trace=tr)
@@ -105,8 +111,14 @@ def test_device_fill_matches_host_generator(case):
             got = kv[l, 0, g, : cfg.ctx].float().cpu().numpy()
             assert np.array_equal(got, ref)
     src = WD.DeviceSource(cfg)
-    t = src.get("wo", 0, (cfg.d_model, cfg.q_dim)).float().cpu().numpy()
-    assert np.array_equal(t, S.gen_tensor(cfg, "wo", 0, (cfg.d_model, cfg.q_dim)))
+    ref = S.gen_tensor(cfg, "wo", 0, (cfg.d_model, cfg.q_dim))
+    if cfg.weight_format == "q4":
+        codes, steps = src.get_q4("wo", 0, (cfg.d_model, cfg.q_dim))
+        assert np.array_equal(codes.cpu().numpy(), ref.codes)
+        assert np.array_equal(steps.cpu().numpy().view(np.uint16), ref.steps.view(np.uint16))
+    else:
+        t = src.get("wo", 0, (cfg.d_model, cfg.q_dim)).float().cpu().numpy()
+        assert np.array_equal(t, ref)
 
 
 def test_verify_rows_match_oracle(case):

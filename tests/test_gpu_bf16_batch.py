@@ -8,7 +8,8 @@ and attention chunk counts.  Depth-truncated targets keep the full width and the
 * 26B-class mixture-of-experts at B=4 and B=8: 16 and 32 rows routed over 128 experts, top-8
   (at B=8 the grouped expert GEMMs run two M-tiles);
 * a 64-row prefill call at the E2B width (four 16-row M-tiles per projection, 512 query vectors
-  per KV head in the attention).
+  per KV head in the attention);
+* the 31B-class B=8 case and the prefill call again with every weight matrix in 4-bit blocks.
 
 Every verify row's hidden state and its logits over the whole vocabulary are compared with the
 oracle run on that row's own sequence alone, so a row that read another sequence's cache,
@@ -38,6 +39,8 @@ CASES = {
     "31b-L1-B8": truncated("31b", 1, ctx=530, norm_jitter=0.1, d_layers=2, batch=8),
     "moe-L1-B4": truncated("moe", 1, ctx=530, norm_jitter=0.1, d_layers=2, batch=4),
     "moe-L1-B8": truncated("moe", 1, ctx=530, norm_jitter=0.1, d_layers=2, batch=8),
+    "31b-L1-B8-q4": truncated("31b", 1, ctx=530, norm_jitter=0.1, d_layers=2, batch=8,
+                              weight_format="q4"),
 }
 # committed length of each sequence: ctx minus these (different chunk counts in one call)
 SHORTEN = [0, 37, 130, 3, 64, 129, 255, 1]
@@ -46,7 +49,7 @@ SHORTEN = [0, 37, 130, 3, 64, 129, 255, 1]
 def oracle_rows(W, cfg, cache, tokens, length, margins):
     H = []
     for i, tok in enumerate(tokens):
-        x = S.gen_rows(cfg, "embed", 0, cfg.d_model, int(tok), 1)[0].astype(np.float64)
+        x = O.as_f64(S.gen_rows(cfg, "embed", 0, cfg.d_model, int(tok), 1))[0]
         tr = []
         for l, lw in enumerate(W["layers"]):
             x = O.decoder_layer_row(lw, cfg, cache.K[l], cache.V[l], x, length + i, trace=tr)
@@ -149,12 +152,13 @@ def test_batched_spec_equals_batched_greedy(bcase):
     assert eng.device_error() == 0
 
 
-def test_prefill_call_of_64_rows_matches_oracle():
+@pytest.mark.parametrize("wformat", ["dense", "q4"])
+def test_prefill_call_of_64_rows_matches_oracle(wformat):
     """One 64-row verify call (a prefill chunk) at the E2B width after 530 committed positions:
     four 16-row M-tiles per projection and 64 x 8 query vectors per KV head.  Hidden rows at a
     sample of positions, all 64 rows' argmax against the GPU's own logits, and the logits over
-    the whole vocabulary of the sampled rows against the oracle."""
-    cfg = truncated("e2b", 1, ctx=530, norm_jitter=0.1, d_layers=2)
+    the whole vocabulary of the sampled rows against the oracle; bf16 and 4-bit weights."""
+    cfg = truncated("e2b", 1, ctx=530, norm_jitter=0.1, d_layers=2, weight_format=wformat)
     R = 64
     max_ctx = (cfg.ctx + R + 8 + 7) // 8 * 8
     eng = build_engine(cfg, max_ctx, max_rows=R)

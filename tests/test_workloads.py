@@ -100,3 +100,32 @@ def test_expert_stack_slices_equal_the_whole_tensor():
         for e in (0, 5, E - 1):
             assert np.array_equal(st[e], whole[e])
         assert len(st) == E
+
+
+def test_q4_generator_codes_steps_and_slices():
+    """4-bit tensors as drawn: codes are the top 4 bits of the tensor's stream, steps fp16 values
+    on [2s/3, 4s/3) with s = std / sqrt(21.5), row slices equal the whole tensor's rows, and the
+    weights (through the oracle's q4_weights) have about the configured standard deviation."""
+    import oracle as O
+    from workloads import synth as S
+    from workloads.synth import ExpertStack
+    cfg = preset("tiny-moe", init="hash", dtype="bf16", seed=3, weight_format="q4")
+    q = S.gen_tensor(cfg, "wo", 0, (256, 512))
+    assert q.codes.dtype == np.uint8 and q.codes.shape == (256, 512)
+    assert q.steps.dtype == np.float16 and q.steps.shape == (256, 16)
+    z = hash_u64(stream_key(cfg.seed, S.tensor_id("wo", 0)), 0, 10)
+    assert q.codes.reshape(-1)[:10].tolist() == [int(v >> np.uint64(60)) for v in z]
+    s = cfg.weight_std / math.sqrt(21.5)
+    st = q.steps.astype(np.float64)
+    assert st.min() >= 2 * s / 3 * (1 - 1e-3) and st.max() <= 4 * s / 3 * (1 + 1e-3)
+    counts = np.bincount(q.codes.reshape(-1), minlength=16)
+    assert counts.min() > 0.9 * q.codes.size / 16
+    rows = S.gen_q4_rows(cfg, "wo", 0, 512, 37, 5)
+    assert np.array_equal(rows.codes, q.codes[37:42]) and np.array_equal(rows.steps, q.steps[37:42])
+    w = O.q4_weights(q.codes, q.steps)
+    assert abs(w.std() / cfg.weight_std - 1) < 0.05
+    E, Fe, d = cfg.n_experts, cfg.expert_ffn, cfg.d_model
+    whole = S.gen_tensor(cfg, "exp_wd", 1, (E, d, Fe))
+    st = ExpertStack(cfg, "exp_wd", 1, (E, d, Fe))
+    for e in (0, 5, E - 1):
+        assert np.array_equal(st[e].codes, whole.codes[e]) and np.array_equal(st[e].steps, whole.steps[e])

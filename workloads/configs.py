@@ -40,6 +40,9 @@ class ModelConfig:
     kv_src_layer: int = -1  # -1 means the target's last layer
     # numerics
     dtype: str = "bf16"  # storage dtype of weights / KV / GEMM inputs: "bf16" or "f32"
+    # "dense" (weights in dtype) or "q4" (every weight matrix in 32-element blocks of 4-bit codes
+    # and an fp16 step; bf16 activations)
+    weight_format: str = "dense"
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
     # weight generator: "normal" (numpy default_rng per tensor) or "hash" (counter hash, bf16)

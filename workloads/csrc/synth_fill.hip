@@ -3,9 +3,13 @@
 // Same counter-based generator as workloads/synth.py: element i of the stream with key k is the
 // (i+1)-th SplitMix64 output of state k (Steele, Lea and Flood, OOPSLA 2014; Stafford's Mix13
 // finaliser).  value = float32(2*u24 - (2^24-1)) * scale, u24 = top 24 bits; bf16 tensors round
-// that fp32 value to nearest-even.  Holds no part of the decoding method.
+// that fp32 value to nearest-even.  4-bit tensors are drawn as codes and steps (workloads/synth.py
+// describes both).  Holds no part of the decoding method.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+// every product is rounded to fp32 on its own, as on the host (no fused multiply-add)
+#pragma clang fp contract(off)
 
 namespace {
 
@@ -34,6 +38,26 @@ __global__ void fill_uniform(void* dst, int64_t n, int bf16, uint64_t key, int64
     const float v = value_at(key, (uint64_t)(start + i), scale);
     if (bf16) reinterpret_cast<uint16_t*>(dst)[i] = to_bf16(v);
     else reinterpret_cast<float*>(dst)[i] = v;
+  }
+}
+
+// 4-bit tensors as drawn: code i = top 4 bits of element start_q + i of stream key_q; step j =
+// fp16(float32(u23 + 2^23) * scale), u23 the top 23 bits of element start_d + j of stream key_d.
+__global__ void fill_q4(uint8_t* codes, int64_t n_codes, uint16_t* steps, int64_t n_steps,
+                        uint64_t key_q, int64_t start_q, uint64_t key_d, int64_t start_d,
+                        float scale) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_codes; i += stride) {
+    const uint64_t z = mix64(key_q + ((uint64_t)(start_q + i) + 1ull) * 0x9E3779B97F4A7C15ull);
+    codes[i] = (uint8_t)(z >> 60);
+  }
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_steps; i += stride) {
+    const uint64_t z = mix64(key_d + ((uint64_t)(start_d + i) + 1ull) * 0x9E3779B97F4A7C15ull);
+    float v = (float)((uint32_t)(z >> 41) + 8388608u) * scale;
+    // the product is rounded to fp32 before the fp16 conversion (the host's two roundings); the
+    // empty asm keeps the compiler from fusing both into one mixed-precision multiply
+    asm volatile("" : "+v"(v));
+    steps[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
   }
 }
 
@@ -73,6 +97,17 @@ int synth_fill_uniform(void* dst, int64_t n, int bf16, uint64_t key, int64_t sta
   if (n == 0) return 0;
   hipLaunchKernelGGL(fill_uniform, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, dst, n,
                      bf16, key, start, scale);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int synth_fill_q4(void* codes, int64_t n_codes, void* steps, int64_t n_steps, uint64_t key_q,
+                  int64_t start_q, uint64_t key_d, int64_t start_d, float scale, void* stream) {
+  if (!codes || !steps || n_codes < 0 || n_steps < 0) return -1;
+  const int64_t n = n_codes > n_steps ? n_codes : n_steps;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(fill_q4, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)codes, n_codes, (uint16_t*)steps, n_steps, key_q, start_q, key_d,
+                     start_d, scale);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -2,7 +2,8 @@
 
 ``HostSource`` uploads the host generator's arrays (small configurations, the tiny fp32 one);
 ``DeviceSource`` fills hash-initialised tensors directly on the GPU with libsynth.so, which is
-bit-identical to the host generator (large configurations).  Holds no part of the method.
+bit-identical to the host generator (large configurations).  ``get`` returns a dense tensor;
+``get_q4`` the codes and steps of a 4-bit one.  Holds no part of the method.
 """
 
 from __future__ import annotations
@@ -47,6 +48,9 @@ def synth_lib():
         lib.synth_fill_uniform.restype = C.c_int
         lib.synth_fill_uniform.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_uint64, C.c_int64,
                                            C.c_float, C.c_void_p]
+        lib.synth_fill_q4.restype = C.c_int
+        lib.synth_fill_q4.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_uint64,
+                                      C.c_int64, C.c_uint64, C.c_int64, C.c_float, C.c_void_p]
         lib.synth_fill_kv.restype = C.c_int
         lib.synth_fill_kv.argtypes = [C.c_void_p] + [C.c_int] * 8 + [C.c_uint64, C.c_float, C.c_int,
                                                                       C.c_void_p]
@@ -78,8 +82,15 @@ class HostSource:
         if name in NORMS:
             a = S.norm_weight(cfg, name, layer, shape[0])
             return torch.from_numpy(a).to(self.device)
+        assert cfg.weight_format == "dense", "4-bit weights come from get_q4"
         a = S.gen_tensor(cfg, name, layer, shape)
         return torch.from_numpy(a).to(device=self.device, dtype=TORCH_DT[cfg.dtype])
+
+    def get_q4(self, name, layer, shape):
+        """(codes uint8 [*shape], steps float16 [*shape[:-1], shape[-1] / 32]) on the device."""
+        q = S.gen_tensor(self.cfg, name, layer, shape)
+        return (torch.from_numpy(q.codes).to(self.device),
+                torch.from_numpy(q.steps).to(self.device))
 
 
 class DeviceSource:
@@ -93,8 +104,26 @@ class DeviceSource:
         cfg = self.cfg
         if name in NORMS:
             return torch.from_numpy(S.norm_weight(cfg, name, layer, shape[0])).to(self.device)
+        assert cfg.weight_format == "dense", "4-bit weights come from get_q4"
         t = torch.empty(shape, dtype=TORCH_DT[cfg.dtype], device=self.device)
         return fill_uniform(t, S.stream_key(cfg.seed, S.tensor_id(name, layer)), cfg.weight_std)
+
+    def get_q4(self, name, layer, shape, row_start: int = 0):
+        """(codes uint8 [*shape], steps float16 [*shape[:-1], shape[-1] / 32]) on the device; rows
+        row_start.. of the tensor when only a slice is wanted."""
+        cfg = self.cfg
+        K = shape[-1]
+        codes = torch.empty(shape, dtype=torch.uint8, device=self.device)
+        steps = torch.empty((*shape[:-1], K // 32), dtype=torch.float16, device=self.device)
+        tid = S.tensor_id(name, layer)
+        rc = synth_lib().synth_fill_q4(
+            C.c_void_p(codes.data_ptr()), codes.numel(), C.c_void_p(steps.data_ptr()), steps.numel(),
+            C.c_uint64(S.stream_key(cfg.seed, tid)), row_start * K,
+            C.c_uint64(S.stream_key(cfg.seed, tid + S.Q4_STEP_TID)), row_start * (K // 32),
+            float(S.q4_step_scale(cfg.weight_std)), _stream())
+        if rc != 0:
+            raise RuntimeError(f"synth_fill_q4 failed ({rc})")
+        return codes, steps
 
 
 def source_for(cfg, device="cuda"):
@@ -103,8 +132,12 @@ def source_for(cfg, device="cuda"):
 
 def clusters(cfg, device="cuda"):
     """(perm, centroids) for the drafter's clustered head.  Centroids are member means of the
-    host-generated table, which is bit-identical to the device one."""
+    host-generated table, which is bit-identical to the device one; 4-bit weights draw their own
+    centroids, returned as (codes, steps) device tensors."""
     perm = S.cluster_perm(cfg)
+    if cfg.weight_format == "q4":
+        return torch.from_numpy(perm).to(device), source_for(cfg, device).get_q4(
+            "centroids", 0, (cfg.n_centroids, cfg.d_dim))
     table = S.gen_tensor(cfg, "table", 0, (cfg.vocab, cfg.d_dim))
     cent = S.centroids_from_table(cfg, table, perm)
     return torch.from_numpy(perm).to(device), torch.from_numpy(cent).to(device)

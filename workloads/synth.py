@@ -17,6 +17,15 @@ Two generators are used:
   nearest-even.  The HIP fill in ``workloads/csrc/synth_fill.hip`` implements the
   same definition, so device-generated tensors are bit-identical to these.
 
+Weights in the 4-bit block format (``weight_format == "q4"``) are drawn as raw
+codes and steps, not values: code ``i`` of a tensor is the top 4 bits of element
+``i`` of its hash stream; the fp16 step of (row, 32-column block) ``j`` comes from
+the stream of tensor id + 2^19, as
+``float16(float32(u23 + 2^23) * float32(2*s / (3 * 2^23)))`` with ``u23`` the top 23
+bits and ``s = std / sqrt(21.5)`` (21.5 = mean of (code - 8)^2 over uniform codes):
+steps uniform on [2s/3, 4s/3).  The generators return them as ``Q4Codes``; turning
+codes into weights is left to the consumers.
+
 Draft injection (the workload's "replace drafts with the target's greedy token
 with probability p") draws ``U = hash >> 11`` (53 bits) per (sequence, absolute
 position, draft slot) and replaces iff ``U < floor(p * 2^53)``.
@@ -25,6 +34,7 @@ position, draft slot) and replaces iff ``U < floor(p * 2^53)``.
 from __future__ import annotations
 
 import math
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -32,9 +42,10 @@ __all__ = [
     "GOLDEN", "mix64", "stream_key", "hash_u64", "hash_uniform_f32", "bf16_round",
     "bf16_bits", "bf16_from_bits", "TID", "tensor_id", "gen_tensor", "gen_rows",
     "norm_weight", "target_weights", "target_layer_weights", "drafter_weights",
-    "cluster_perm", "centroids_from_table", "kv_init", "kv_rows", "state_init",
+    "cluster_perm", "centroids_from_table", "drafter_centroids", "kv_init", "kv_rows", "state_init",
     "prompt_tokens", "inject_threshold", "inject_draw", "inject_key", "hash_scale",
-    "hash_u64_at", "inject_table", "ExpertStack",
+    "hash_u64_at", "inject_table", "ExpertStack", "Q4Codes", "gen_q4_rows", "q4_step_scale",
+    "Q4_STEP_TID",
 ]
 
 MASK64 = (1 << 64) - 1
@@ -115,7 +126,7 @@ TID = {
     "sh_wg": 23, "sh_wu": 24, "sh_wd": 25,
     "table": 40, "norm_h": 41, "norm_e": 42, "w_in": 43,
     "d_n1": 44, "d_wq": 45, "d_wo": 46, "d_n2": 47, "d_wg": 48, "d_wu": 49, "d_wd": 50,
-    "d_nf": 51, "w_back": 52,
+    "d_nf": 51, "w_back": 52, "centroids": 53,
     "kv_k": 60, "kv_v": 61, "hid": 62, "tok": 63, "inject": 64,
 }
 
@@ -124,10 +135,51 @@ def tensor_id(name: str, layer: int = 0) -> int:
     return TID[name] * (1 << 20) + layer
 
 
+Q4_STEP_TID = 1 << 19  # the step stream of a 4-bit tensor: its tensor id + 2^19
+
+
+@dataclass
+class Q4Codes:
+    """A weight tensor in the 4-bit block format as drawn: codes [..., K] (uint8, 0..15) and one
+    fp16 step per 32 consecutive codes of a row, steps [..., K // 32] (float16)."""
+    codes: np.ndarray
+    steps: np.ndarray
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+    def __getitem__(self, idx) -> "Q4Codes":
+        """Rows (leading-axis index or slice) of the tensor."""
+        return Q4Codes(self.codes[idx], self.steps[idx])
+
+
+def q4_step_scale(std: float) -> np.float32:
+    return np.float32(2.0 * (std / math.sqrt(21.5)) / (3.0 * float(1 << 23)))
+
+
+def gen_q4_rows(cfg, name: str, layer: int, n_cols: int, row_start: int, n_rows: int,
+                std: float | None = None) -> Q4Codes:
+    """Rows ``row_start .. row_start+n_rows-1`` of a 4-bit [*, n_cols] tensor (codes, steps)."""
+    assert cfg.init == "hash" and n_cols % 32 == 0
+    std = cfg.weight_std if std is None else std
+    tid = tensor_id(name, layer)
+    z = hash_u64(stream_key(cfg.seed, tid), row_start * n_cols, n_rows * n_cols)
+    codes = (z >> np.uint64(60)).astype(np.uint8).reshape(n_rows, n_cols)
+    nb = n_cols // 32
+    zd = hash_u64(stream_key(cfg.seed, tid + Q4_STEP_TID), row_start * nb, n_rows * nb)
+    u23 = (zd >> np.uint64(41)).astype(np.int64) + (1 << 23)
+    steps = (u23.astype(np.float32) * q4_step_scale(std)).astype(np.float16).reshape(n_rows, nb)
+    return Q4Codes(codes, steps)
+
+
 def gen_rows(cfg, name: str, layer: int, n_cols: int, row_start: int, n_rows: int,
-             std: float | None = None) -> np.ndarray:
-    """Rows ``row_start .. row_start+n_rows-1`` of a hash-initialised [*, n_cols] tensor (fp32 values)."""
+             std: float | None = None):
+    """Rows ``row_start .. row_start+n_rows-1`` of a hash-initialised [*, n_cols] tensor (fp32
+    values; ``Q4Codes`` for 4-bit weights)."""
     assert cfg.init == "hash"
+    if cfg.weight_format == "q4":
+        return gen_q4_rows(cfg, name, layer, n_cols, row_start, n_rows, std)
     std = cfg.weight_std if std is None else std
     key = stream_key(cfg.seed, tensor_id(name, layer))
     v = hash_uniform_f32(key, row_start * n_cols, n_rows * n_cols, std)
@@ -136,8 +188,12 @@ def gen_rows(cfg, name: str, layer: int, n_cols: int, row_start: int, n_rows: in
     return v.reshape(n_rows, n_cols)
 
 
-def gen_tensor(cfg, name: str, layer: int, shape, std: float | None = None) -> np.ndarray:
-    """A weight tensor in logical row-major order, as fp32 values (bf16-representable for bf16)."""
+def gen_tensor(cfg, name: str, layer: int, shape, std: float | None = None):
+    """A weight tensor in logical row-major order, as fp32 values (bf16-representable for bf16);
+    ``Q4Codes`` of that shape for 4-bit weights."""
+    if cfg.weight_format == "q4":
+        q = gen_q4_rows(cfg, name, layer, shape[-1], 0, int(np.prod(shape[:-1])), std)
+        return Q4Codes(q.codes.reshape(shape), q.steps.reshape(*shape[:-1], shape[-1] // 32))
     std = cfg.weight_std if std is None else std
     n = int(np.prod(shape))
     if cfg.init == "normal":
@@ -155,7 +211,8 @@ class ExpertStack:
     """A stacked [E][rows][cols] expert weight whose slices are generated on first use: with the
     hash generator each slice is its own range of the tensor's counter stream (identical to the
     slice of the whole tensor); with the normal generator the whole tensor is drawn once.
-    Indexing by expert id returns that expert's [rows][cols] fp32 array."""
+    Indexing by expert id returns that expert's [rows][cols] fp32 array (``Q4Codes`` for 4-bit
+    weights)."""
 
     def __init__(self, cfg, name: str, layer: int, shape):
         self.cfg, self.name, self.layer, self.shape = cfg, name, layer, tuple(shape)
@@ -165,7 +222,7 @@ class ExpertStack:
     def __len__(self) -> int:
         return self.shape[0]
 
-    def __getitem__(self, e) -> np.ndarray:
+    def __getitem__(self, e):
         e = int(e)
         if not 0 <= e < self.shape[0]:
             raise IndexError(e)
@@ -238,6 +295,14 @@ def centroids_from_table(cfg, table: np.ndarray, perm: np.ndarray) -> np.ndarray
     return bf16_round(c) if cfg.dtype == "bf16" else c
 
 
+def drafter_centroids(cfg, table, perm):
+    """The clustered head's centroids: member means of the table for dense weights; for 4-bit
+    weights a drawn 4-bit tensor of their own (stream "centroids")."""
+    if cfg.weight_format == "q4":
+        return gen_tensor(cfg, "centroids", 0, (cfg.n_centroids, cfg.d_dim))
+    return centroids_from_table(cfg, table, perm)
+
+
 def drafter_weights(cfg) -> dict:
     D, d, Fd = cfg.d_dim, cfg.d_model, cfg.d_ffn
     table = gen_tensor(cfg, "table", 0, (cfg.vocab, D))
@@ -245,7 +310,7 @@ def drafter_weights(cfg) -> dict:
     w = {
         "table": table,
         "perm": perm,
-        "centroids": centroids_from_table(cfg, table, perm),
+        "centroids": drafter_centroids(cfg, table, perm),
         "norm_h": norm_weight(cfg, "norm_h", 0, d),
         "norm_e": norm_weight(cfg, "norm_e", 0, D),
         "w_in": gen_tensor(cfg, "w_in", 0, (D, d + D)),

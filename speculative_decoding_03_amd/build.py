@@ -25,6 +25,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 SOURCES = ["gemm.hip", *[f"gemm_{t}_m{m}.hip" for t in ("bf16", "f32", "q4") for m in (1, 2, 4)],
            "attention.hip", "misc.hip", "specdec.cpp", "policy.cpp"]
 LIB = os.path.join(HERE, "libspecdec.so")
+# The 4-bit weight kernels read every MFMA result with VALU instructions (the per-block step):
+# results in architectural VGPRs save a copy out of the accumulation registers per element
+# (the calls of at most 16 rows; the compiler fails on the wider instantiations with this form).
+FILE_FLAGS = {"gemm_q4_m1.hip": ("-mllvm", "-amdgpu-mfma-vgpr-form")}
 
 
 def _compile(src: str, obj: str, extra=()) -> None:
@@ -48,7 +52,7 @@ def build_specdec(verbose: bool = True) -> str:
             src = os.path.join(CSRC, s)
             obj = os.path.join(bdir, s + ".o")
             objs.append(obj)
-            jobs.append(ex.submit(_compile, src, obj))
+            jobs.append(ex.submit(_compile, src, obj, FILE_FLAGS.get(s, ())))
         for j in jobs:
             j.result()
     tmp = LIB + ".tmp"

@@ -156,9 +156,8 @@ __device__ __forceinline__ f32x4 q4_offset(const Frag<bf16_t>& xf) {
   return mma<bf16_t>(xf, m, f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
-__device__ __forceinline__ void q4_block(f32x4& acc, const Frag<bf16_t>& xf, const Frag<bf16_t>& wf,
-                                         float d, const f32x4& off) {
-  const f32x4 t = mma<bf16_t>(xf, wf, off);
+// acc += d * t, elementwise (the k-block's product t scaled by its step d)
+__device__ __forceinline__ void q4_scale_add(f32x4& acc, const f32x4& t, float d) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d, t[i], acc[i]);
 }
@@ -170,7 +169,9 @@ __device__ __forceinline__ void q4_block(f32x4& acc, const Frag<bf16_t>& xf, con
 template <int NU, bool WC>
 __device__ __forceinline__ void q4_quad_loop(const GemmArgs& a, const size_t (&wt_tile)[NU], int g0,
                                              int g1, int lane, f32x4 (&acc)[NU][1]) {
-  constexpr int GU = NU >= 2 ? 1 : 2;  // k-groups per batch
+  // k-groups per batch; two register stages (measured on MI355X at the 31B gate/up shape:
+  // deeper rings and larger batches gain nothing)
+  constexpr int GU = NU >= 2 ? 1 : 2;
   constexpr int S = 2;
   const uint8_t* W = reinterpret_cast<const uint8_t*>(a.W);
   const int ngk = a.nkb >> 2;
@@ -193,7 +194,8 @@ __device__ __forceinline__ void q4_quad_loop(const GemmArgs& a, const size_t (&w
       quad_frag_rt<bf16_t>(xf, q, j);
       const f32x4 off = q4_offset(xf);
 #pragma unroll
-      for (int t = 0; t < NU; ++t) q4_block(acc[t][0], xf, q4_operand(wg[t].code[j], kq), q4_step(wg[t], j), off);
+      for (int t = 0; t < NU; ++t)
+        q4_scale_add(acc[t][0], mma<bf16_t>(xf, q4_operand(wg[t].code[j], kq), off), q4_step(wg[t], j));
     }
   };
   const int nb = max(0, (g1 - g0) / GU);
@@ -272,7 +274,8 @@ __device__ __forceinline__ void q4_row_loop(const GemmArgs& a, const size_t (&wt
         const Frag<bf16_t> wf = q4_operand(wg[t].code[j], kq);
         const float d = q4_step(wg[t], j);
 #pragma unroll
-        for (int mt = 0; mt < ML; ++mt) q4_block(acc[t][mt], xg[j][mt], wf, d, off[mt]);
+        for (int mt = 0; mt < ML; ++mt)
+          q4_scale_add(acc[t][mt], mma<bf16_t>(xg[j][mt], wf, off[mt]), d);
       }
     }
   };

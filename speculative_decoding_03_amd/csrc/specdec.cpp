@@ -29,6 +29,10 @@ namespace {
 constexpr size_t ALIGN = 256;
 constexpr int TARGET_WAVES = 2048;   // waves per projection launch
 constexpr int MIN_KB_PER_WAVE = 8;   // k-blocks each wave streams at least
+// 4-bit weights carry 3.6x fewer bytes per k-block: each wave streams at least 16 (measured on
+// MI355X at the 31B shapes: 16 beats 8 and 32; wide gated projections split at most 4 ways)
+constexpr int MIN_KB_PER_WAVE_Q4 = 16;
+constexpr int GATED_MAX_KW_Q4 = 4;
 // Tiles per unit of the target's q/k/v, o and down projections: two when the projection has at
 // least 256 tiles (one activation load then serves twice the weight bytes), else one, which keeps
 // more workgroups on the CUs (measured on MI355X: two at the 31B shapes, one at the E2B, E4B and
@@ -61,16 +65,18 @@ struct Gemm {
 // on MI355X at the 31B shapes (M = 4): about TARGET_WAVES waves per launch, each streaming at
 // least MIN_KB_PER_WAVE k-blocks, is best for one-tile units; the 4-tile argmax units (LM head,
 // drafter table) stream best split 8 ways.
-int split_for(int units, int nkb, int NU) {
+int split_for(int units, int nkb, int NU, bool q4) {
+  const int mkb = q4 ? MIN_KB_PER_WAVE_Q4 : MIN_KB_PER_WAVE;
   int KW = NU >= 4 ? 8 : cdiv(TARGET_WAVES, units);
-  KW = std::min({KW, 16, std::max(1, nkb / MIN_KB_PER_WAVE)});
+  KW = std::min({KW, 16, std::max(1, nkb / mkb)});
   return pow2_floor(std::max(1, KW));
 }
 
 // Waves per workgroup for a split-K factor KW (a workgroup holds NW / KW whole units).
 int waves_for(int KW) { return KW == 16 ? 16 : 8; }
 
-Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true, bool gated = false) {
+Gemm make_gemm(const void* W, int N, int Kd, int NU, bool q4, bool allow_split = true,
+               bool gated = false) {
   Gemm g;
   g.W = W;
   g.N = N;
@@ -79,13 +85,14 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true, bo
   g.n_tiles = N / 16;
   g.NU = NU;
   g.n_units = cdiv(g.n_tiles, NU);
-  g.KW = allow_split ? split_for(g.n_units, g.nkb, NU) : 1;
+  g.KW = allow_split ? split_for(g.n_units, g.nkb, NU, q4) : 1;
   g.NW = waves_for(g.KW);
   if (allow_split && gated && g.n_units >= 4 * TARGET_WAVES / 8) {
     // wide gated projections: one unit per workgroup, split up to eight ways (measured on
     // MI355X at the 31B gate/up shape: the small workgroups balance over the CUs as they
     // retire, and eight waves keep more loads in flight than four)
-    g.KW = std::min(8, std::max(1, pow2_floor(g.nkb / MIN_KB_PER_WAVE)));
+    g.KW = std::min(q4 ? GATED_MAX_KW_Q4 : 8,
+                    std::max(1, pow2_floor(g.nkb / (q4 ? MIN_KB_PER_WAVE_Q4 : MIN_KB_PER_WAVE))));
     g.NW = std::max(4, g.KW);
   }
   g.kbps = round_up4(cdiv(g.nkb, g.KW));
@@ -95,7 +102,7 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool allow_split = true, bo
 // A stacked weight of E groups (experts) of N x Kd each, of which a launch computes only the
 // routed ones.  The split is sized for the top_k groups of one row, fixed per shape so that a
 // row's result does not depend on how many other rows share the launch.
-Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
+Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k, bool q4) {
   Gemm g;
   g.W = W;
   g.N = N;
@@ -106,7 +113,7 @@ Gemm make_grouped_gemm(const void* W, int N, int Kd, int NU, int E, int top_k) {
   g.n_tiles = E * g.tpg;
   g.NU = NU;
   g.n_units = E * g.upg;
-  g.KW = split_for(top_k * g.upg, g.nkb, NU);
+  g.KW = split_for(top_k * g.upg, g.nkb, NU, q4);
   g.NW = waves_for(g.KW);
   g.kbps = round_up4(cdiv(g.nkb, g.KW));
   return g;
@@ -262,35 +269,36 @@ void build_gemms(specdec_ctx* x) {
   const specdec_config& c = x->cfg;
   const int d = c.d_model, qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   const int Fw = ffn_width(&c);
+  const bool q4 = c.weight_format == SPECDEC_WF_Q4;
   x->g_qkv.clear(); x->g_o.clear(); x->g_gu.clear(); x->g_down.clear();
   x->g_router.clear(); x->g_egu.clear(); x->g_edown.clear();
   x->g_dq.clear(); x->g_do.clear(); x->g_dgu.clear(); x->g_ddown.clear();
   for (int l = 0; l < c.n_layers; ++l) {
     const void* const* t = x->lw.data() + (size_t)l * SPECDEC_N_LAYER_TENSORS;
-    x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, store_nu(qd + 2 * kvd)));
-    x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, store_nu(d)));
-    x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * Fw, d, 2, true, true));
-    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, Fw, store_nu(d)));
+    x->g_qkv.push_back(make_gemm(t[SPECDEC_LW_QKV], qd + 2 * kvd, d, store_nu(qd + 2 * kvd), q4));
+    x->g_o.push_back(make_gemm(t[SPECDEC_LW_O], d, qd, store_nu(d), q4));
+    x->g_gu.push_back(make_gemm(t[SPECDEC_LW_GATE_UP], 2 * Fw, d, 2, q4, true, true));
+    x->g_down.push_back(make_gemm(t[SPECDEC_LW_DOWN], d, Fw, store_nu(d), q4));
     if (c.n_experts > 0) {
-      x->g_router.push_back(make_gemm(t[SPECDEC_LW_ROUTER], c.n_experts, d, 1));
+      x->g_router.push_back(make_gemm(t[SPECDEC_LW_ROUTER], c.n_experts, d, 1, q4));
       x->g_egu.push_back(make_grouped_gemm(t[SPECDEC_LW_EXP_GATE_UP], 2 * c.expert_ffn, d, 2,
-                                           c.n_experts, c.top_k));
+                                           c.n_experts, c.top_k, q4));
       x->g_edown.push_back(make_grouped_gemm(t[SPECDEC_LW_EXP_DOWN], d, c.expert_ffn, 1,
-                                             c.n_experts, c.top_k));
+                                             c.n_experts, c.top_k, q4));
     }
   }
-  x->g_head = make_gemm(x->w.embed, c.vocab, d, 4);
-  x->g_in = make_gemm(x->w.w_in, c.d_dim, d + c.d_dim, 1);
-  x->g_back = make_gemm(x->w.w_back, d, c.d_dim, 1);
-  x->g_cent = make_gemm(x->w.centroids, c.n_centroids, c.d_dim, 1);
-  x->g_table = make_gemm(x->w.table, c.vocab, c.d_dim, 4);
-  x->g_clu = make_gemm(x->w.table, c.vocab, c.d_dim, 4, false);
+  x->g_head = make_gemm(x->w.embed, c.vocab, d, 4, q4);
+  x->g_in = make_gemm(x->w.w_in, c.d_dim, d + c.d_dim, 1, q4);
+  x->g_back = make_gemm(x->w.w_back, d, c.d_dim, 1, q4);
+  x->g_cent = make_gemm(x->w.centroids, c.n_centroids, c.d_dim, 1, q4);
+  x->g_table = make_gemm(x->w.table, c.vocab, c.d_dim, 4, q4);
+  x->g_clu = make_gemm(x->w.table, c.vocab, c.d_dim, 4, q4, false);
   for (int l = 0; l < c.d_layers; ++l) {
     const void* const* t = x->dw.data() + (size_t)l * SPECDEC_N_DRAFT_TENSORS;
-    x->g_dq.push_back(make_gemm(t[SPECDEC_DW_Q], qd, c.d_dim, 1));
-    x->g_do.push_back(make_gemm(t[SPECDEC_DW_O], c.d_dim, qd, 1));
-    x->g_dgu.push_back(make_gemm(t[SPECDEC_DW_GATE_UP], 2 * c.d_ffn, c.d_dim, 2, true, true));
-    x->g_ddown.push_back(make_gemm(t[SPECDEC_DW_DOWN], c.d_dim, c.d_ffn, 1));
+    x->g_dq.push_back(make_gemm(t[SPECDEC_DW_Q], qd, c.d_dim, 1, q4));
+    x->g_do.push_back(make_gemm(t[SPECDEC_DW_O], c.d_dim, qd, 1, q4));
+    x->g_dgu.push_back(make_gemm(t[SPECDEC_DW_GATE_UP], 2 * c.d_ffn, c.d_dim, 2, q4, true, true));
+    x->g_ddown.push_back(make_gemm(t[SPECDEC_DW_DOWN], c.d_dim, c.d_ffn, 1, q4));
   }
   // the drafter's weights (about 170 MB at the 31B shape, the full table included) are read
   // again in every sub-step and fit in the 256 MB last-level cache

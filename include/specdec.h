@@ -86,6 +86,11 @@ typedef struct {
                                table, centroids) is in the 4-bit block format of
                                specdec_pack_q4; needs dtype BF16 and every reduction width
                                (d_model, Hq*hd, the FFN widths, d_dim, d_ffn) % 128 == 0 */
+  int32_t max_prefill;      /* rows of the largest specdec_prefill call, 0..1024 (0: none).  Above
+                               0 it needs dtype BF16, dense weights, no experts and d_model,
+                               Hq*hd, ffn_dim % 64 == 0, and the workspace grows by the chunk's
+                               activations and attention partials
+                               (about n_kv_heads*max_ctx/chunk*max_prefill*Hq/Hkv*(hd+4)*4 B) */
 } specdec_config;
 
 /* Per-layer tensor slots of specdec_weights.layers (n_layers * SPECDEC_N_LAYER_TENSORS). */
@@ -299,6 +304,21 @@ int specdec_accept_tree(specdec_ctx* ctx, int32_t B, int32_t n_nodes, const int3
 int specdec_accept(specdec_ctx* ctx, int32_t B, int32_t K, const int32_t* tokens,
                    int32_t* out_tokens, int32_t* n_emit, int32_t* next_tok, uint32_t flags,
                    void* stream);
+
+/* Prompt prefill ("Gemma 4 MTP Drafter", section "How it works": the target first processes the
+   prompt and the context; "Accelerating Gemini Nano on Pixel ...", section "Zero-copy
+   architecture": the drafter then reads the target's cache and needs no prefill of its own).
+   Runs T tokens (int32 [T], device) of sequence b (0 <= b < max_batch) through the target at
+   positions len[b] .. len[b]+T-1, as one forward pass over the chunk (causal attention over the
+   committed prefix and the chunk's earlier rows), appends their K/V, and commits them:
+   len[b] += T, hid[b] = the pre-final-norm hidden state of the last row.  logits (fp32 [T][vocab],
+   device) and argmax (int32 [T], device; argmax[T-1] is the first generated token) are optional.
+   Uses the compute-bound prompt GEMM (weights read once per chunk, not once per row).  Cancels a
+   pending verify (its accept / kv_commit are refused afterwards).  Errors: SPECDEC_E_INVAL,
+   SPECDEC_E_CAPACITY (len[b] + T beyond max_ctx on the host-side bound), SPECDEC_E_UNSUPPORTED
+   (max_prefill == 0). */
+int specdec_prefill(specdec_ctx* ctx, int32_t b, int32_t T, const int32_t* tokens, float* logits,
+                    int32_t* argmax, void* stream);
 
 /* Commit n_commit[b] (int32 [B], device, 1..rows of the last verify) rows: len[b] += n and
    hid[b] = hidden of row n-1.  For prefill chunks and callers that decide acceptance

@@ -26,7 +26,7 @@ DW_N1, DW_Q, DW_O, DW_N2, DW_GATE_UP, DW_DOWN, N_DRAFT_TENSORS = range(7)
 EXPORTS = [
     "specdec_workspace_bytes", "specdec_kv_elems", "specdec_create", "specdec_create_static",
     "specdec_destroy",
-    "specdec_draft", "specdec_draft_traced", "specdec_draft_tree", "specdec_verify",
+    "specdec_draft", "specdec_draft_traced", "specdec_draft_tree", "specdec_verify", "specdec_prefill",
     "specdec_verify_tree", "specdec_accept_tree", "specdec_accept", "specdec_kv_commit",
     "specdec_pack_matrix", "specdec_q4_bytes", "specdec_pack_q4", "specdec_set_len_bound", "specdec_read_device_error",
     "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
@@ -42,7 +42,7 @@ class Config(C.Structure):
         "d_layers", "d_dim", "d_ffn", "n_centroids", "kv_src_layer", "dtype")] + [
         ("rms_eps", C.c_float), ("rope_theta", C.c_float)] + [
         (n, C.c_int32) for n in ("max_batch", "max_draft", "max_rows", "max_ctx",
-                                 "weight_format")]
+                                 "weight_format", "max_prefill")]
 
 
 class Weights(C.Structure):
@@ -92,6 +92,7 @@ def load(path: str = LIB_PATH):
         "specdec_moe_usage_start": (C.c_int, [vp, vp]),
         "specdec_moe_usage_read": (C.c_int, [vp, P(i32), vp]),
         "specdec_verify": (C.c_int, [vp, i32, i32, vp, vp, vp, vp]),
+        "specdec_prefill": (C.c_int, [vp, i32, i32, vp, vp, vp, vp]),
         "specdec_draft_tree": (C.c_int, [vp, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp]),
         "specdec_verify_tree": (C.c_int, [vp, i32, i32, P(i32), vp, vp, vp, vp]),
         "specdec_accept_tree": (C.c_int, [vp, i32, i32, P(i32), vp, vp, i32, vp, vp, u32, vp]),

@@ -23,7 +23,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 
 # the GEMM's (storage type, M-tile count) instantiations compile in translation units of their own
 SOURCES = ["gemm.hip", *[f"gemm_{t}_m{m}.hip" for t in ("bf16", "f32", "q4") for m in (1, 2, 4)],
-           "attention.hip", "misc.hip", "specdec.cpp", "policy.cpp"]
+           "gemm_mm.hip", "attention.hip", "misc.hip", "specdec.cpp", "policy.cpp"]
 LIB = os.path.join(HERE, "libspecdec.so")
 # The 4-bit weight kernels read every MFMA result with VALU instructions (the per-block step):
 # results in architectural VGPRs save a copy out of the accumulation registers per element

@@ -110,11 +110,16 @@ attn_kernel(AttnArgs a) {
   constexpr int NB = SH::NB, DS = SH::DS, DT = SH::DT, KPW = SH::KPW, CH = SH::CH;
   __shared__ __align__(16) float xch[NWAVE][16][SH::PST];
   __shared__ float mw[NWAVE][16], lw[NWAVE][16];
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
   const int Rall = a.R * G;
+  // query vectors [q_begin, q_end) of the group: all of them, or one block of q_block
+  const int nqb = a.q_block ? (Rall + a.q_block - 1) / a.q_block : 1;
+  const int b = blockIdx.z / nqb;
+  const int q_begin = a.q_block ? (blockIdx.z - b * nqb) * a.q_block : 0;
+  const int q_end = a.q_block ? min(Rall, q_begin + a.q_block) : Rall;
   const float scale2 = a.scale * 1.44269504088896341f;  // softmax scale times log2 e
 
   // The committed length is requested first but waited for only after every cache and query
@@ -158,8 +163,8 @@ attn_kernel(AttnArgs a) {
       else zero_frag(qf[ds]);
     }
   };
-  load_q(0, qa);
-  if (Rall > 16) load_q(16, qb);  // the second tile's query vectors are requested up front
+  load_q(q_begin, qa);
+  if (q_begin + 16 < q_end) load_q(q_begin + 16, qb);  // the second tile's, requested up front
   Frag<T> vf[NB][DT];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -179,9 +184,16 @@ attn_kernel(AttnArgs a) {
   const bool ragged = kw0 + KPW > end_max;  // the wave holds values past end_max (wave-uniform)
 
   float* pbase = a.part + (((size_t)b * a.hkv + g) * a.n_chunks + chunk) * (size_t)Rall * SH::PST;
+  bool v_clean = !ragged;  // values past end_max zeroed (done once, by the first tile that uses them)
   auto tile = [&](int q0, Frag<T> (&qf)[DS]) {
     const int qv = q0 + c16;  // this lane's query column
     const int row = qv / G;
+    // causal rows that all end before this chunk: no partial is needed (the combine reads a
+    // row's chunks only up to its own last key); uniform over the workgroup
+    if (a.vis == VIS_CAUSAL && chunk * CH >= len + min(q0 + 15, Rall - 1) / G + a.key_off) {
+      if (q0 + 32 < q_end) load_q(q0 + 32, qf);
+      return;
+    }
 
     // ---- scores, masked, and the softmax statistics of the wave's keys ----
     f32x4 s[NB][2];
@@ -195,7 +207,7 @@ attn_kernel(AttnArgs a) {
         s[nb][h] = acc;
       }
     // the tile after next reuses this tile's buffer once its scores are done
-    if (q0 + 32 < Rall) load_q(q0 + 32, qf);
+    if (q0 + 32 < q_end) load_q(q0 + 32, qf);
     // keys [0, kend) are visible, and in a tree verify slot len + j for each bit j of tmask
     const int kend = qv >= Rall ? 0 : (a.vis == VIS_CAUSAL ? len + row + a.key_off
                                                            : (a.vis == VIS_FLAT ? len + a.key_off : len));
@@ -236,13 +248,14 @@ attn_kernel(AttnArgs a) {
     l = rows_sum(l);
 
     // ---- value sum O^T[d][q] = sum_key V^T[d][key] P^T[key][q] ----
-    if (q0 == 0 && ragged) {  // values past end_max may hold anything, even NaN: zero them
+    if (!v_clean) {  // values past end_max may hold anything, even NaN: zero them
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int nv = end_max - (kw0 + nb * 32 + grp * 8);  // visible elements of the lane's run
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) keep_first(vf[nb][dt], nv);
       }
+      v_clean = true;
     }
     Frag<T> pf[NB];
 #pragma unroll
@@ -296,11 +309,11 @@ attn_kernel(AttnArgs a) {
       pbase[(size_t)qv * SH::PST + HD] = M;
       pbase[(size_t)qv * SH::PST + HD + 1] = L;
     }
-    if (q0 + 16 < Rall) __syncthreads();  // the next tile reuses the LDS buffers
+    if (q0 + 16 < q_end) __syncthreads();  // the next tile reuses the LDS buffers
   };
-  for (int q0 = 0; q0 < Rall; q0 += 32) {
+  for (int q0 = q_begin; q0 < q_end; q0 += 32) {
     tile(q0, qa);
-    if (q0 + 16 < Rall) tile(q0 + 16, qb);
+    if (q0 + 16 < q_end) tile(q0 + 16, qb);
   }
 }
 
@@ -358,11 +371,14 @@ __global__ void __launch_bounds__(WAVE) attn_combine_kernel(AttnArgs a) {
       const int len = len_in;
       const int end_max = attn_key_end(a.vis, len, a.R, a.key_off);
       if (end_max > a.max_ctx || len < 0) return;
-      n_act = (end_max + a.chunk - 1) / a.chunk;
-      if (n_act > a.n_launch) {  // the device length is beyond the host-side bound
+      if ((end_max + a.chunk - 1) / a.chunk > a.n_launch) {  // beyond the host-side bound
         if (lane == 0) raise_error(a.err, ERRBIT_CAPACITY);
         return;
       }
+      // the chunks that hold a key this row sees (a causal row ends at its own key; chunks
+      // after it, which only later rows see, contribute exact zeros and are not read)
+      const int row_end = a.vis == VIS_CAUSAL ? len + row + a.key_off : end_max;
+      n_act = (row_end + a.chunk - 1) / a.chunk;
       if (n_act == 0) {
         // no visible key (drafter before any context): the attention output is defined as zero
         if (active && q == 0)
@@ -440,7 +456,9 @@ template <typename T, int HD>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   if (a.chunk != AttnShape<HD>::CH) return hipErrorInvalidValue;
   const int Rall = a.R * (a.hq / a.hkv);
-  dim3 grid(a.n_launch, a.hkv, a.B), block(NWAVE * WAVE);
+  const int nqb = a.q_block ? (Rall + a.q_block - 1) / a.q_block : 1;
+  if (a.q_block % 0x20 || (a.q_block && a.vis == VIS_TREE)) return hipErrorInvalidValue;
+  dim3 grid(a.n_launch, a.hkv, a.B * nqb), block(NWAVE * WAVE);
   if (a.vis == VIS_TREE) {
     if (!a.tree_mask) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_kernel<T, HD, true>), grid, block, 0, st, a);

@@ -372,14 +372,17 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int l
   }
 }
 
+__device__ __forceinline__ int yssq_ld(const GemmArgs& a) { return a.ld_yssq ? a.ld_yssq : a.M; }
+
 __device__ __forceinline__ void row_scale_load(const GemmArgs& a, int lane, RowScaleLoads& rs) {
   rs.fast = a.yssq && a.M <= 4 && a.n_yssq <= WAVE * RS_J;
   if (!rs.fast) return;
+  const int ld = yssq_ld(a);
 #pragma unroll
   for (int j = 0; j < RS_J; ++j) {
     const int t = lane + WAVE * j;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rs.v[j][r] = (t < a.n_yssq && r < a.M) ? a.yssq[(size_t)t * a.M + r] : 0.f;
+    for (int r = 0; r < 4; ++r) rs.v[j][r] = (t < a.n_yssq && r < a.M) ? a.yssq[(size_t)t * ld + r] : 0.f;
   }
 }
 
@@ -410,7 +413,7 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const in
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
     for (int t = lane; t < a.n_yssq; t += WAVE) {
-      const float* p = a.yssq + (size_t)t * a.M + m0;
+      const float* p = a.yssq + (size_t)t * yssq_ld(a) + m0;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (r < nr) s[r] += p[r];
@@ -524,7 +527,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           }
           if (a.ssq) {
             const float r = sum16(sq);
-            if (c16 == 0 && m < a.M) a.ssq[(size_t)tile * a.M + m] = r;
+            if (c16 == 0 && m < a.M) a.ssq[(size_t)tile * (a.ld_ssq ? a.ld_ssq : a.M) + m] = r;
           }
         }
     }

@@ -1,0 +1,194 @@
+// Compute-bound GEMM for prompt chunks (prefill): Y[M][N] = X[M][Kd] . W[N][Kd]^T with M in the
+// hundreds, where every weight byte feeds M rows and the MFMA units, not HBM, set the pace.
+//
+// A workgroup of WM x WN waves computes a block of 64*WM rows x 64*WN columns; wave (wm, wn) owns
+// the 64 x 64 sub-block of four 16-row M-tiles and four 16-column tiles, held as the same
+// accumulator array the skinny kernel uses (acc[tile][M-tile]), so the skinny kernel's epilogues
+// (residual add + sums of squares + x * w_next, rotary + KV append, SiLU product, per-unit argmax)
+// apply unchanged to each wave's sub-block.  The reduction axis streams in stages of two k-blocks
+// (64 elements): every thread copies 16-byte runs of X rows and of packed weight tiles from
+// global memory into LDS, laid out in MFMA operand order (a fragment = 64 lanes x 16 bytes,
+// contiguous), so each wave reads its four X fragments and four weight fragments per k-block
+// with conflict-free 16-byte LDS reads and issues sixteen v_mfma_f32_16x16x32_bf16.  Two LDS
+// stages alternate: the next stage's global loads are in flight while the current one is
+// multiplied, and one barrier per stage separates writing a stage from reading it.  The
+// per-row, per-tile reduction order is fixed (k-blocks ascending), independent of M and of the
+// block shape.
+
+#include "gemm_impl.h"
+
+namespace specdec {
+namespace gemm_detail {
+
+constexpr int MM_KS = 2;  // k-blocks per LDS stage
+
+template <int EPI, int WM, int WN>
+__global__ void __launch_bounds__(WM * WN * 64) mm_kernel(GemmArgs a) {
+  constexpr int NTH = WM * WN * 64;
+  constexpr int BMT = 4 * WM;             // 16-row M-tiles per block
+  constexpr int BNT = 4 * WN;             // 16-column tiles per block
+  constexpr int A_FR = MM_KS * BMT;       // X fragments per stage
+  constexpr int B_FR = MM_KS * BNT;       // weight fragments per stage
+  constexpr int A_RUNS = A_FR * 64 / NTH;  // 16-byte runs each thread copies per stage
+  constexpr int B_RUNS = B_FR * 64 / NTH;
+  static_assert(A_FR * 64 % NTH == 0 && B_FR * 64 % NTH == 0, "stage does not split evenly");
+  __shared__ __align__(16) u32x4 sa[2][A_FR * 64];
+  __shared__ __align__(16) u32x4 sb[2][B_FR * 64];
+
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w % WM, wn = w / WM;
+  const int m_blk = blockIdx.y * 64 * WM, t_blk = blockIdx.x * BNT;
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
+  const bf16_t* W = reinterpret_cast<const bf16_t*>(a.W);
+  const int nkb = a.nkb, n_st = nkb / MM_KS;
+
+  // this thread's runs: X run i = tid + j*NTH is row i / (4*KS) of the block, 8 elements at
+  // k-block (i / 4) % KS, k-group i % 4; weight run i is lane i % 64 of fragment i / 64
+  // (k-block (i / 64) % KS of block tile (i / 64) / KS).  Rows past M and tiles past N read the
+  // last row / tile (their results are never stored).
+  const bf16_t* xsrc[A_RUNS];
+  int adst[A_RUNS];
+#pragma unroll
+  for (int j = 0; j < A_RUNS; ++j) {
+    const int i = tid + j * NTH;
+    const int row = i / (4 * MM_KS), kq = i % (4 * MM_KS);
+    const int kb = kq / 4, kg = kq % 4;
+    xsrc[j] = X + (size_t)min(m_blk + row, a.M - 1) * a.ldx + kb * TILE_K + kg * 8;
+    adst[j] = (kb * BMT + row / 16) * 64 + kg * 16 + row % 16;
+  }
+  const bf16_t* wsrc[B_RUNS];
+  int bdst[B_RUNS];
+#pragma unroll
+  for (int j = 0; j < B_RUNS; ++j) {
+    const int i = tid + j * NTH;
+    const int fr = i / 64, ln = i % 64;
+    const int kb = fr % MM_KS, t = fr / MM_KS;
+    wsrc[j] = W + ((size_t)min(t_blk + t, a.n_tiles - 1) * nkb + kb) * TILE_ELEMS + ln * LANE_ELEMS;
+    bdst[j] = (kb * BNT + t) * 64 + ln;
+  }
+  u32x4 ra[A_RUNS], rb[B_RUNS];
+  auto load_stage = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < A_RUNS; ++j) ra[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + s * MM_KS * TILE_K);
+#pragma unroll
+    for (int j = 0; j < B_RUNS; ++j)
+      rb[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)s * MM_KS * TILE_ELEMS));
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < A_RUNS; ++j) sa[buf][adst[j]] = ra[j];
+#pragma unroll
+    for (int j = 0; j < B_RUNS; ++j) sb[buf][bdst[j]] = rb[j];
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_st > 0) {
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int s = 0; s < n_st; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < n_st) load_stage(s + 1);  // in flight while this stage multiplies
+#pragma unroll
+      for (int kb = 0; kb < MM_KS; ++kb) {
+        Frag<bf16_t> xf[4], wf[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) xf[mt].v = sa[buf][(kb * BMT + wm * 4 + mt) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wf[t].v = sb[buf][(kb * BNT + wn * 4 + t) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mma<bf16_t>(xf[mt], wf[t], acc[t][mt]);
+      }
+      if (s + 1 < n_st) store_stage(buf ^ 1);  // the other stage was last read before the barrier
+      __syncthreads();
+    }
+  }
+
+  // ---- the skinny kernel's epilogue on this wave's 64 x 64 sub-block ----
+  const int m0 = m_blk + wm * 64, tile0 = t_blk + wn * 4;
+  if (m0 >= a.M || tile0 >= a.n_tiles) return;
+  GemmArgs e = a;
+  e.M = min(64, a.M - m0);
+  e.x_qx = e.out_qx = 0;
+  e.ld_yssq = a.M;
+  if (e.yssq) e.yssq = a.yssq + m0;
+  if constexpr (EPI == EPI_STORE) {
+    e.out = a.out + (size_t)m0 * a.ldo;
+    e.ld_ssq = a.M;
+    if (e.ssq) e.ssq = a.ssq + m0;
+    if (e.xw_out) e.xw_out = reinterpret_cast<bf16_t*>(a.xw_out) + (size_t)m0 * a.ldo;
+  } else if constexpr (EPI == EPI_ROPE) {
+    e.qout = reinterpret_cast<bf16_t*>(a.qout) + (size_t)m0 * a.hq * a.hd;
+    e.rows_per_seq = 1 << 30;  // one sequence
+    e.pos_off = a.pos_off + m0;
+  } else if constexpr (EPI == EPI_SILU) {
+    e.hout = reinterpret_cast<bf16_t*>(a.hout) + (size_t)m0 * a.ldh;
+  } else {
+    e.amax_val = a.amax_val + (size_t)m0 * a.ld_amax;
+    e.amax_idx = a.amax_idx + (size_t)m0 * a.ld_amax;
+    if (e.logits) e.logits = a.logits + (size_t)m0 * a.ld_logits;
+    e.unit_row = nullptr;
+  }
+  int xr[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = mt * 16 + (lane & 15);
+    xr[mt] = m < e.M ? m : -1;
+  }
+  RowScaleLoads rs;
+  rs.fast = false;
+  if constexpr (EPI == EPI_ARGMAX) {
+    // one argmax unit of 64 columns
+    EpiPre<4, 4> pre;
+    epilogue<bf16_t, 4, 4, EPI>(e, acc, tile0 >> 2, tile0, 0, xr, rs, pre, lane);
+  } else {
+    // two halves of two tiles each (for SiLU: a gate and an up tile), so that the epilogue's
+    // prefetched operands stay within the main loop's register budget
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int t0 = tile0 + 2 * hh;
+      if (t0 >= e.n_tiles) break;  // uniform
+      f32x4 (&part)[2][4] = *reinterpret_cast<f32x4 (*)[2][4]>(&acc[2 * hh][0]);
+      EpiPre<4, 2> pre;
+      epi_prefetch<4, 2, EPI>(e, t0, lane, pre);
+      epilogue<bf16_t, 4, 2, EPI>(e, part, t0 >> 1, t0, 0, xr, rs, pre, lane);
+    }
+  }
+}
+
+template <int EPI, int WM, int WN>
+hipError_t launch_mm_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
+  dim3 grid((a.n_tiles + 4 * WN - 1) / (4 * WN), (a.M + 64 * WM - 1) / (64 * WM)), block(WM * WN * 64);
+  if (tm)
+    hipExtLaunchKernelGGL((mm_kernel<EPI, WM, WN>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+  else
+    hipLaunchKernelGGL((mm_kernel<EPI, WM, WN>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace gemm_detail
+
+hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
+  using namespace gemm_detail;
+  if (a.M <= 0 || a.n_tiles <= 0) return hipSuccess;
+  if (a.nkb % MM_KS || a.wq4) return hipErrorInvalidValue;
+  if (epi == EPI_ARGMAX && a.n_tiles % 4) return hipErrorInvalidValue;  // whole 64-column units
+  if (epi == EPI_SILU && a.n_tiles % 2) return hipErrorInvalidValue;    // gate/up pairs
+  switch (epi) {
+    case EPI_STORE: return launch_mm_t<EPI_STORE, 2, 2>(a, st, tm);
+    case EPI_ROPE: return launch_mm_t<EPI_ROPE, 2, 2>(a, st, tm);
+    case EPI_SILU: return launch_mm_t<EPI_SILU, 2, 2>(a, st, tm);
+    case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 2, 2>(a, st, tm);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace specdec

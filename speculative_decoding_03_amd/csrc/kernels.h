@@ -67,7 +67,10 @@ struct GemmArgs {
   float* out = nullptr;
   int ldo = 0;
   int accumulate = 0;
-  float* ssq = nullptr;        // [n_tiles][M]
+  float* ssq = nullptr;        // [n_tiles][ld_ssq]
+  // row strides of ssq and yssq (0: M); a launch over a slice of a longer call's rows uses the
+  // call's row count
+  int ld_ssq = 0, ld_yssq = 0;
   // optional addend rows: y = (sum_{k < add_n} addend[(m*add_n + k)*ldo + col]) + y, k ascending
   const float* addend = nullptr;
   int add_n = 0;
@@ -112,6 +115,13 @@ struct LaunchTiming {
 hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
                        const LaunchTiming* tm = nullptr);
 
+// Compute-bound GEMM of a prompt chunk (gemm_mm.hip): bf16 weights in the packed tile layout,
+// row-major bf16 X of a.M rows (any count), nkb % 2 == 0; epilogues EPI_STORE, EPI_ROPE (one
+// sequence: rows at positions len[0] + pos_off + row), EPI_SILU and EPI_ARGMAX (units of 64
+// columns, slot row * ld_amax + unit) as in launch_gemm.  The unit fields (nu, n_units, KW, NW,
+// kb_per_split) are not used.
+hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm = nullptr);
+
 // The 4-bit block weight format (common.h): a matrix [N][Kd] with N % 16 == 0 and
 // Kd % 128 == 0 takes q4_bytes(N, Kd) bytes.  launch_pack_q4 writes it from codes [N][Kd] (one
 // byte each, 0..15) and fp16 steps [N][Kd / 32], rows permuted by `kind` as launch_pack does.
@@ -147,6 +157,9 @@ struct AttnArgs {
   // node i sees its ancestors and itself, each at slot len + node index).
   int vis = 0;
   const uint64_t* tree_mask = nullptr;  // VIS_TREE: [R] device (launch_tree_desc)
+  // query vectors per workgroup (a multiple of 32; 0: all R * hq / hkv of a sequence in each);
+  // a prompt chunk's hundreds of rows spread over more workgroups
+  int q_block = 0;
 };
 enum { VIS_CAUSAL = 0, VIS_FLAT = 1, VIS_TREE = 2 };
 enum { POS_LINEAR = 0, POS_FLAT = 1, POS_TREE = 2 };
@@ -168,6 +181,12 @@ hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts
                          int B, int R, const int* tokens, int* out_tokens, int* n_emit,
                          int* next_tok, int commit, int* len, float* hid, const float* X, int d,
                          int* argmax_out, int* err, hipStream_t st);
+// Prompt prefill (misc.hip): per-row argmax over LM-head partials [rows][ld]; commit of n rows
+// of one sequence (len += n, hid = the last row).
+hipError_t launch_rows_argmax(const float* amax_val, const int* amax_idx, int n_parts, int ld,
+                              int rows, int* out, hipStream_t st);
+hipError_t launch_commit_rows(int* len, float* hid, const float* xlast, int d, int n,
+                              hipStream_t st);
 hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid, const float* X,
                          int d, int* err, hipStream_t st);
 hipError_t launch_draft_input(int dtype, const float* h, const int* tok, const void* table,

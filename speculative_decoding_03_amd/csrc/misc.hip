@@ -201,6 +201,37 @@ __global__ void __launch_bounds__(256) commit_kernel(const int* n_commit, int R,
   if (threadIdx.x == 0) len[b] += n;
 }
 
+// Per row of a prompt chunk: argmax over its LM-head partials (lowest index on ties), one
+// workgroup per row.
+__global__ void __launch_bounds__(256) rows_argmax_kernel(const float* amax_val, const int* amax_idx,
+                                                          int n_parts, int ld, int* out) {
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x >> 6;
+  float v = -INFINITY;
+  int i = 0x7fffffff;
+  for (int p = threadIdx.x; p < n_parts; p += blockDim.x)
+    argmax_combine(v, i, amax_val[(size_t)row * ld + p], amax_idx[(size_t)row * ld + p]);
+  wave_argmax(v, i);
+  if (lane == 0) {
+    rv[wid] = v;
+    ri[wid] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) argmax_combine(v, i, rv[w], ri[w]);
+    out[row] = i;
+  }
+}
+
+// Commit of a prompt chunk of n rows of one sequence: len += n, hid = the chunk's last hidden row.
+__global__ void __launch_bounds__(256) commit_rows_kernel(int* len, float* hid, const float* xlast,
+                                                          int d, int n) {
+  for (int k = threadIdx.x; k < d; k += blockDim.x) hid[k] = xlast[k];
+  if (threadIdx.x == 0) *len += n;
+}
+
 // u[b] = [ rms(h[b]) * norm_h ; rms(table[row(tok[b])]) * norm_e ] in the storage dtype.
 // h is requested first, as 16-byte runs held in registers (when d <= 4 * HV * blockDim.x), so its
 // latency overlaps the token -> table-row lookup; both sums of squares share one block reduction.
@@ -816,6 +847,20 @@ hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts
 hipError_t launch_commit(const int* n_commit, int B, int R, int* len, float* hid, const float* X,
                          int d, int* err, hipStream_t st) {
   hipLaunchKernelGGL(commit_kernel, dim3(B), dim3(256), 0, st, n_commit, R, len, hid, X, d, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_argmax(const float* amax_val, const int* amax_idx, int n_parts, int ld,
+                              int rows, int* out, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_argmax_kernel, dim3(rows), dim3(256), 0, st, amax_val, amax_idx, n_parts,
+                     ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit_rows(int* len, float* hid, const float* xlast, int d, int n,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(commit_rows_kernel, dim3(1), dim3(256), 0, st, len, hid, xlast, d, n);
   return hipGetLastError();
 }
 

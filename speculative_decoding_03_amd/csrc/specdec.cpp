@@ -124,6 +124,8 @@ struct Layout {
   size_t rlog, e_xrow, e_orow, e_wt, e_groups, e_ngroups, e_h, e_y, e_usage;
   size_t u, xd, xdw, dh, hnext, z, utile, urow, dtok, d_amax_v, d_amax_i, tscore, path;
   size_t tree_mask, tree_depth;
+  // prompt prefill (max_prefill rows): activations, argmax partials and attention partials
+  size_t p_x, p_xw, p_ssq, p_q, p_o, p_h, p_amax_v, p_amax_i, p_part;
   size_t total;
 };
 
@@ -195,6 +197,14 @@ bool valid_config(const specdec_config* c) {
   if (c->max_draft < 1 || c->max_draft + 1 > c->max_rows) return false;
   if (c->max_ctx < c->max_rows + 1 || c->max_ctx > (1 << 20) || c->max_ctx % 8) return false;
   if (c->max_ctx / attention_chunk(c->head_dim) > 4096) return false;
+  if (c->max_prefill < 0 || c->max_prefill > 1024) return false;
+  if (c->max_prefill > 0) {
+    // the prompt GEMM: bf16 weights of a dense model, reduction widths in stages of 64
+    const int qd = c->n_q_heads * c->head_dim;
+    if (c->dtype != SPECDEC_BF16 || c->weight_format != SPECDEC_WF_DENSE || c->n_experts > 0)
+      return false;
+    if (c->d_model % 64 || qd % 64 || c->ffn_dim % 64) return false;
+  }
   if (c->kv_src_layer >= c->n_layers) return false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return false;
   return true;
@@ -261,6 +271,19 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.e_h = take(slots * c->expert_ffn * dm.esz);
   L.e_y = take(slots * d * 4);
   L.e_usage = take((size_t)c->n_layers * 4);  // experts routed to, summed per layer (measurement)
+  const size_t P = (size_t)c->max_prefill;
+  if (P > 0) {
+    const int G = c->n_q_heads / c->n_kv_heads;
+    L.p_x = take(P * d * 4);
+    L.p_xw = take(P * d * 2);
+    L.p_ssq = take(P * (d / 16) * 4);
+    L.p_q = take(P * qd * 2);
+    L.p_o = take(P * qd * 2);
+    L.p_h = take(P * c->ffn_dim * 2);
+    L.p_amax_v = take(P * dm.parts * 4);
+    L.p_amax_i = take(P * dm.parts * 4);
+    L.p_part = take((size_t)c->n_kv_heads * dm.n_chunks * P * G * (c->head_dim + 4) * 4);
+  }
   L.total = off;
   return L;
 }
@@ -743,9 +766,135 @@ int verify_impl(specdec_ctx* x, int B, int R, const int32_t* tokens, float* logi
   return SPECDEC_OK;
 }
 
+// The GEMM arguments of a prompt-chunk launch (launch_mm): the weights and the row count.
+GemmArgs mm_args(specdec_ctx* x, const Gemm& g, int M) {
+  GemmArgs a;
+  a.W = g.W;
+  a.nkb = g.nkb;
+  a.n_tiles = g.n_tiles;
+  a.M = M;
+  a.err = at<int>(x, x->lay.err);
+  a.eps = x->cfg.rms_eps;
+  return a;
+}
+
+// Prompt chunk of T rows of sequence b through the target (the same layer sequence as a verify),
+// on the compute-bound GEMM and the attention split over key chunks and query blocks, then the
+// commit of all T rows.
+int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* logits,
+                 int32_t* argmax, hipStream_t st) {
+  const specdec_config& c = x->cfg;
+  const int d = c.d_model, qd = c.n_q_heads * c.head_dim, Fw = c.ffn_dim;
+  float* X = at<float>(x, x->lay.p_x);
+  void* XW = x->ws + x->lay.p_xw;
+  float* ssq = at<float>(x, x->lay.p_ssq);
+  int* err = at<int>(x, x->lay.err);
+  int* len = x->len + b;
+  auto lw = [&](int l, int slot) { return (const float*)x->lw[(size_t)l * SPECDEC_N_LAYER_TENSORS + slot]; };
+  HIP_TRY(launch_embed(DT_BF16, x->w.embed, x->g_head.nkb, d, tokens, T, X, ssq, XW, 0,
+                       lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st));
+  const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
+  const size_t seq = (size_t)b * c.n_kv_heads * c.max_ctx * c.head_dim;  // sequence b's cache
+  const int n_launch = std::min(x->dm.n_chunks, cdiv(x->len_hi[b] + T, x->dm.chunk));
+  for (int l = 0; l < c.n_layers; ++l) {
+    void* kc = (char*)x->kv_k + (per_layer * l + seq) * 2;
+    void* vc = (char*)x->kv_v + (per_layer * l + seq) * 2;
+    {  // q/k/v projection + RoPE at positions len + row + K/V append
+      GemmArgs a = mm_args(x, x->g_qkv[l], T);
+      norm_input(a, XW, d, ssq, d);
+      a.qout = x->ws + x->lay.p_q;
+      a.kcache = kc;
+      a.vcache = vc;
+      a.len = len;
+      a.hq = c.n_q_heads;
+      a.hkv = c.n_kv_heads;
+      a.hd = c.head_dim;
+      a.max_ctx = c.max_ctx;
+      a.rope_cs = at<float2>(x, x->lay.rope);
+      HIP_TRY(launch_mm(EPI_ROPE, a, st));
+    }
+    {  // causal attention of the T rows over the committed prefix and the chunk
+      AttnArgs a;
+      a.q = x->ws + x->lay.p_q;
+      a.kcache = kc;
+      a.vcache = vc;
+      a.len = len;
+      a.out = x->ws + x->lay.p_o;
+      a.out_qx = 0;
+      a.part = at<float>(x, x->lay.p_part);
+      a.err = err;
+      a.B = 1;
+      a.R = T;
+      a.key_off = 1;
+      a.hq = c.n_q_heads;
+      a.hkv = c.n_kv_heads;
+      a.hd = c.head_dim;
+      a.max_ctx = c.max_ctx;
+      a.chunk = x->dm.chunk;
+      a.n_chunks = x->dm.n_chunks;
+      a.n_launch = n_launch;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      a.vis = VIS_CAUSAL;
+      a.q_block = 128;
+      HIP_TRY(launch_attention(DT_BF16, a, st));
+    }
+    {  // output projection + residual; leaves x * ffn_norm
+      GemmArgs a = mm_args(x, x->g_o[l], T);
+      a.X = x->ws + x->lay.p_o;
+      a.ldx = qd;
+      resid_output(a, X, d, 1, ssq, XW, lw(l, SPECDEC_LW_FFN_NORM));
+      HIP_TRY(launch_mm(EPI_STORE, a, st));
+    }
+    {  // gate/up + SiLU product
+      GemmArgs a = mm_args(x, x->g_gu[l], T);
+      norm_input(a, XW, d, ssq, d);
+      a.hout = x->ws + x->lay.p_h;
+      a.ldh = Fw;
+      HIP_TRY(launch_mm(EPI_SILU, a, st));
+    }
+    {  // down projection + residual; leaves x * (next attention norm | final norm)
+      GemmArgs a = mm_args(x, x->g_down[l], T);
+      a.X = x->ws + x->lay.p_h;
+      a.ldx = Fw;
+      const float* wn = l + 1 < c.n_layers ? lw(l + 1, SPECDEC_LW_ATTN_NORM) : x->w.final_norm;
+      resid_output(a, X, d, 1, ssq, XW, wn);
+      HIP_TRY(launch_mm(EPI_STORE, a, st));
+    }
+  }
+  {  // final norm + tied LM head: per-unit argmax partials (+ optional logits)
+    GemmArgs a = mm_args(x, x->g_head, T);
+    norm_input(a, XW, d, ssq, d);
+    a.amax_val = at<float>(x, x->lay.p_amax_v);
+    a.amax_idx = at<int>(x, x->lay.p_amax_i);
+    a.ld_amax = x->dm.parts;
+    a.logits = logits;
+    a.ld_logits = c.vocab;
+    HIP_TRY(launch_mm(EPI_ARGMAX, a, st));
+  }
+  if (argmax)
+    HIP_TRY(launch_rows_argmax(at<float>(x, x->lay.p_amax_v), at<int>(x, x->lay.p_amax_i),
+                               x->dm.parts, x->dm.parts, T, argmax, st));
+  HIP_TRY(launch_commit_rows(len, x->hid + (size_t)b * d, X + (size_t)(T - 1) * d, d, T, st));
+  x->len_hi[b] += T;
+  x->last_B = 0;  // a verify's rows can no longer be accepted or committed
+  x->last_R = 0;
+  x->last_tree_n = 0;
+  return SPECDEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int specdec_prefill(specdec_ctx* x, int32_t b, int32_t T, const int32_t* tokens, float* logits,
+                    int32_t* argmax, void* stream) {
+  if (!x || !tokens) return SPECDEC_E_INVAL;
+  const specdec_config& c = x->cfg;
+  if (c.max_prefill < 1) return SPECDEC_E_UNSUPPORTED;
+  if (b < 0 || b >= c.max_batch || T < 1 || T > c.max_prefill) return SPECDEC_E_INVAL;
+  if (x->len_hi[b] + T > c.max_ctx) return SPECDEC_E_CAPACITY;
+  return prefill_impl(x, b, T, tokens, logits, argmax, reinterpret_cast<hipStream_t>(stream));
+}
 
 int specdec_verify(specdec_ctx* x, int32_t B, int32_t R, const int32_t* tokens, float* logits,
                    int32_t* argmax, void* stream) {

@@ -226,7 +226,7 @@ class Engine:
     """One libspecdec context plus the caller-owned device state it works on."""
 
     def __init__(self, model: DeviceModel, max_batch: int, max_draft: int, max_rows: int,
-                 max_ctx: int, stream=None, static_workspace: bool = False):
+                 max_ctx: int, stream=None, static_workspace: bool = False, max_prefill: int = 0):
         """static_workspace=True creates the context with specdec_create_static: the library's
         own fixed workspace array instead of a caller buffer (one such context per GPU)."""
         lib = F.load()
@@ -246,6 +246,7 @@ class Engine:
         cfg.rope_theta = s.rope_theta
         cfg.max_batch, cfg.max_draft, cfg.max_rows, cfg.max_ctx = max_batch, max_draft, max_rows, max_ctx
         cfg.weight_format = F.WF_Q4 if s.weight_format == "q4" else F.WF_DENSE
+        cfg.max_prefill = max_prefill
         self.cfg = cfg
         self.max_batch, self.max_draft, self.max_rows, self.max_ctx = max_batch, max_draft, max_rows, max_ctx
         ws = lib.specdec_workspace_bytes(C.byref(cfg))
@@ -303,6 +304,13 @@ class Engine:
         B, R = tokens.shape
         F.check(self.lib.specdec_verify(self.ctx, B, R, _p(tokens), _p(logits), _p(argmax),
                                         _s(stream)), "specdec_verify")
+
+    def prefill(self, b: int, tokens, logits=None, argmax=None, stream=None) -> None:
+        """Runs the prompt chunk tokens (int32 [T], device) of sequence b through the target and
+        commits it (specdec_prefill)."""
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        F.check(self.lib.specdec_prefill(self.ctx, b, tokens.numel(), _p(tokens), _p(logits),
+                                         _p(argmax), _s(stream)), "specdec_prefill")
 
     def accept(self, tokens, out_tokens=None, n_emit=None, next_tok=None, commit=True,
                stream=None) -> None:

@@ -19,14 +19,15 @@ def rel_err(a: np.ndarray, ref: np.ndarray) -> float:
 
 
 def build_engine(cfg, max_ctx: int, max_rows: int = 16, max_batch: int = 1, source=None,
-                 weights_override=None):
+                 weights_override=None, max_prefill: int = 0):
     src = source or WD.source_for(cfg)
     if weights_override is not None:
         src = weights_override(src)
     perm, cent = WD.clusters(cfg)
     model = E.DeviceModel(E.Shape.of(cfg), src, perm, cent)
     eng = E.Engine(model, max_batch=max_batch, max_draft=max(cfg.draft_k, 1),
-                   max_rows=max(max_rows, cfg.draft_k + 1), max_ctx=max_ctx)
+                   max_rows=max(max_rows, cfg.draft_k + 1), max_ctx=max_ctx,
+                   max_prefill=max_prefill)
     return eng
 
 

@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "accepted tokens/s at B=1 (K=3); verify-step ms vs 1-token decode ms; HBM GB/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 WORKLOAD_TEXT = {
     "31b": "31B-class dense: 64 layers, d 5120, 40 q / 8 kv heads of 128, gated FFN 25600, vocab 262144, bf16 random-init (30.5B params, tied head); drafter 4 layers x 256 over the 5120-d backbone state, 2048 centroids x 128 tokens; ctx 8192, K=3, drafts injected at p=0.7",
     "e2b": "E2B-shaped: 24 layers, d 1536, 8 q / 1 kv heads of 256, gated FFN 6144, vocab 262144, bf16; drafter 4 x 256, 2048 centroids x 128; ctx 2048, K=3, p=0.7",
@@ -206,6 +207,10 @@ def main() -> int:
                     help="weights: bf16, or every matrix in 4-bit blocks with an fp16 step per 32")
     ap.add_argument("--no-q4-leg", dest="q4_leg", action="store_false",
                     help="skip the 4-bit-weight run of the same workload (a child process)")
+    ap.add_argument("--prefill-tokens", type=int, default=512,
+                    help="prompt chunk of the prefill leg (0: none; dense bf16 models only)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill leg (for profiling it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the path is built and measured on a single MI355X "
@@ -246,7 +251,10 @@ def main() -> int:
     # verify rows per sequence: a linear step (K + 1, up to KA + 1 in the adaptive leg) or a tree
     # of up to 3 branches (1 + 3K), within the 64 rows of a call
     max_rows = min(64 // B, max(16 // B, KA + 1, 1 + 3 * K))
-    eng = E.Engine(model, max_batch=B, max_draft=KA, max_rows=max_rows, max_ctx=max_ctx)
+    PT = args.prefill_tokens if (not cfg.is_moe and args.wformat == "dense") else 0
+    max_ctx = max(max_ctx, (cfg.ctx + PT + 7) // 8 * 8)
+    eng = E.Engine(model, max_batch=B, max_draft=KA, max_rows=max_rows, max_ctx=max_ctx,
+                   max_prefill=PT)
     WD.fill_kv(eng, cfg)
     t0 = WD.start_state(eng, cfg)  # [B] int32
     hid0 = eng.hid.clone()
@@ -256,6 +264,53 @@ def main() -> int:
     def restore():
         eng.hid.copy_(hid0)
         eng.set_len([cfg.ctx] * B)
+
+    def prefill_leg(runs: int = 5) -> dict:
+        """One prompt chunk of PT tokens of sequence 0 through the target at position ctx
+        (specdec_prefill: compute-bound GEMMs, chunk attention, commit), timed with HIP events
+        around the call, inputs resident; the median of `runs` after two warm-up calls."""
+        T = PT
+        toks = torch.from_numpy(np.random.default_rng(cfg.state_seed + 1)
+                                .integers(0, cfg.vocab, T).astype(np.int32)).to(dev)
+        am = torch.empty(T, dtype=torch.int32, device=dev)
+        ms = []
+        for i in range(2 + runs):
+            restore()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            eng.prefill(0, toks, argmax=am)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(e0.elapsed_time(e1))
+        assert eng.device_error() == 0, "device error during prefill"
+        restore()
+        d, qd, kvd = cfg.d_model, cfg.q_dim, cfg.kv_dim
+        per_layer = d * (qd + 2 * kvd) + qd * d + 3 * d * cfg.ffn_dim
+        gemm = 2.0 * T * (cfg.n_layers * per_layer + cfg.vocab * d)
+        keys = sum(cfg.ctx + r + 1 for r in range(T))
+        attn = 4.0 * cfg.n_layers * cfg.n_q_heads * cfg.head_dim * keys
+        t = float(np.median(ms)) * 1e-3
+        return {"tokens": T, "start_position": cfg.ctx, "ms": round(t * 1e3, 3),
+                "tokens_per_s": round(T / t, 1),
+                "tflops": round((gemm + attn) / t / 1e12, 1),
+                "mfma_frac": round((gemm + attn) / t / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                "flops": {"gemm": gemm, "attention": attn},
+                "what": "specdec_prefill of one sequence: embed, per layer q/k/v + RoPE + KV "
+                        "append, causal chunk attention, O, gate/up + SiLU, down (prompt GEMM), "
+                        "tied LM head with per-row argmax, commit; bf16 MFMA peak 2.5 PFLOP/s"}
+
+    if args.prefill_only:
+        if not PT:
+            log("no prefill leg for this configuration")
+            return 2
+        r = prefill_leg()
+        log(f"prefill: {r['tokens']} tokens in {r['ms']} ms, {r['tflops']} TFLOP/s")
+        print(json.dumps({"metric": "prefill TFLOP/s", "value": r["tflops"], "unit": "TFLOP/s",
+                          "config": {"workload": WORKLOAD_TEXT[args.config]}, "prefill": r}))
+        eng.close()
+        return 0
 
     # ---- plain greedy decoding (1-row verify + fused accept/commit): decode-step timing ----
     cur = t0.clone().view(B, 1)
@@ -691,6 +746,9 @@ def main() -> int:
             "launch_timing": f"HIP events attached to the dispatches; the gate/up launches of {P} "
                              f"speculative steps run after the timed region",
         }
+    if PT:
+        res["prefill"] = prefill_leg()
+        log(f"prefill: {PT} tokens in {res['prefill']['ms']} ms, {res['prefill']['tflops']} TFLOP/s")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores, bounded sample)")
         res["cpu_baseline"] = cpu_baseline(cfg, emitted / (N * B), K, B)

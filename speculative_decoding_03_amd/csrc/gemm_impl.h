@@ -436,7 +436,8 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const in
     }
 }
 
-template <typename T, int MT, int NU, int EPI>
+// ADDEND: compile the addend rows of EPI_STORE in (a launch that never has them leaves them out)
+template <typename T, int MT, int NU, int EPI, bool ADDEND = true>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
                                          int tile0, int grp, const int (&xr)[MT],
                                          const RowScaleLoads& rs, const EpiPre<MT, NU>& pre, int lane) {
@@ -467,7 +468,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
     // lane's elements (at most 16 values) so that the loads are in flight together
     constexpr int JB = 16 / (NU * MT * 4) > 1 ? 16 / (NU * MT * 4) : 1;
     float adds[NU][MT][4];
-    if (a.addend) {
+    const bool has_add = ADDEND && a.addend;
+    if (has_add) {
 #pragma unroll
       for (int t = 0; t < NU; ++t)
 #pragma unroll
@@ -518,7 +520,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
           if (m < a.M) {
             float* o = a.out + (size_t)m * a.ldo + col;
             float y = acc[t][mt][v];
-            if (a.addend) y = adds[t][mt][v] + y;
+            if (has_add) y = adds[t][mt][v] + y;
             if (a.accumulate) y = pre.res[t][mt][v] + y;
             *o = y;
             sq = y * y;

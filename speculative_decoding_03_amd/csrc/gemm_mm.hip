@@ -23,7 +23,7 @@ namespace gemm_detail {
 constexpr int MM_KS = 2;  // k-blocks per LDS stage
 
 template <int EPI, int WM, int WN>
-__global__ void __launch_bounds__(WM * WN * 64) mm_kernel(GemmArgs a) {
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) mm_kernel(GemmArgs a) {
   constexpr int NTH = WM * WN * 64;
   constexpr int BMT = 4 * WM;             // 16-row M-tiles per block
   constexpr int BNT = 4 * WN;             // 16-column tiles per block
@@ -43,19 +43,21 @@ __global__ void __launch_bounds__(WM * WN * 64) mm_kernel(GemmArgs a) {
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.W);
   const int nkb = a.nkb, n_st = nkb / MM_KS;
 
-  // this thread's runs: X run i = tid + j*NTH is row i / (4*KS) of the block, 8 elements at
-  // k-block (i / 4) % KS, k-group i % 4; weight run i is lane i % 64 of fragment i / 64
-  // (k-block (i / 64) % KS of block tile (i / 64) / KS).  Rows past M and tiles past N read the
-  // last row / tile (their results are never stored).
+  // this thread's runs: run i = tid + j*NTH is lane i % 64 of fragment i / 64, so a wave writes
+  // one whole fragment (64 consecutive 16-byte LDS slots, no bank conflict).  X fragment f is
+  // M-tile f % BMT at k-block f / BMT: lane kg*16 + r holds row r, elements kg*8 .. kg*8+7;
+  // weight fragment f is block tile f / KS at k-block f % KS.  Rows past M and tiles past N read
+  // the last row / tile (their results are never stored).
   const bf16_t* xsrc[A_RUNS];
   int adst[A_RUNS];
 #pragma unroll
   for (int j = 0; j < A_RUNS; ++j) {
     const int i = tid + j * NTH;
-    const int row = i / (4 * MM_KS), kq = i % (4 * MM_KS);
-    const int kb = kq / 4, kg = kq % 4;
-    xsrc[j] = X + (size_t)min(m_blk + row, a.M - 1) * a.ldx + kb * TILE_K + kg * 8;
-    adst[j] = (kb * BMT + row / 16) * 64 + kg * 16 + row % 16;
+    const int fr = i / 64, ln = i % 64;
+    const int kb = fr / BMT, mt = fr % BMT;
+    const int row = mt * 16 + (ln & 15);
+    xsrc[j] = X + (size_t)min(m_blk + row, a.M - 1) * a.ldx + kb * TILE_K + (ln >> 4) * 8;
+    adst[j] = fr * 64 + ln;
   }
   const bf16_t* wsrc[B_RUNS];
   int bdst[B_RUNS];
@@ -118,8 +120,23 @@ __global__ void __launch_bounds__(WM * WN * 64) mm_kernel(GemmArgs a) {
   GemmArgs e = a;
   e.M = min(64, a.M - m0);
   e.x_qx = e.out_qx = 0;
-  e.ld_yssq = a.M;
-  if (e.yssq) e.yssq = a.yssq + m0;
+  if (a.yssq) {
+    // RMSNorm row scales of the 64 rows, one row per lane: the partials [t][M] of a row are
+    // summed in t order with loads that are contiguous across the lanes
+    const int m = min(m0 + lane, a.M - 1);
+    float ss = 0.f;
+    for (int t = 0; t < a.n_yssq; ++t) ss += a.yssq[(size_t)t * a.M + m];
+    const float mine = 1.0f / sqrtf(ss / (float)a.yscale_n + a.eps);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sc = __shfl(mine, mt * 16 + ((lane >> 4) << 2) + v, WAVE);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t][mt][v] *= sc;
+      }
+    e.yssq = nullptr;
+  }
   if constexpr (EPI == EPI_STORE) {
     e.out = a.out + (size_t)m0 * a.ldo;
     e.ld_ssq = a.M;
@@ -148,7 +165,7 @@ __global__ void __launch_bounds__(WM * WN * 64) mm_kernel(GemmArgs a) {
   if constexpr (EPI == EPI_ARGMAX) {
     // one argmax unit of 64 columns
     EpiPre<4, 4> pre;
-    epilogue<bf16_t, 4, 4, EPI>(e, acc, tile0 >> 2, tile0, 0, xr, rs, pre, lane);
+    epilogue<bf16_t, 4, 4, EPI, false>(e, acc, tile0 >> 2, tile0, 0, xr, rs, pre, lane);
   } else {
     // two halves of two tiles each (for SiLU: a gate and an up tile), so that the epilogue's
     // prefetched operands stay within the main loop's register budget
@@ -159,7 +176,8 @@ __global__ void __launch_bounds__(WM * WN * 64) mm_kernel(GemmArgs a) {
       f32x4 (&part)[2][4] = *reinterpret_cast<f32x4 (*)[2][4]>(&acc[2 * hh][0]);
       EpiPre<4, 2> pre;
       epi_prefetch<4, 2, EPI>(e, t0, lane, pre);
-      epilogue<bf16_t, 4, 2, EPI>(e, part, t0 >> 1, t0, 0, xr, rs, pre, lane);
+      epilogue<bf16_t, 4, 2, EPI, false>(e, part, t0 >> 1, t0, 0, xr, rs, pre, lane);
+      __builtin_amdgcn_sched_barrier(0);  // the halves' registers do not overlap
     }
   }
 }
@@ -182,9 +200,15 @@ hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTim
   if (a.nkb % MM_KS || a.wq4) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX && a.n_tiles % 4) return hipErrorInvalidValue;  // whole 64-column units
   if (epi == EPI_SILU && a.n_tiles % 2) return hipErrorInvalidValue;    // gate/up pairs
+  // 128 x 128 blocks; a projection too narrow to give every CU a block takes 64 x 128 blocks of
+  // two waves instead (the model-width outputs: o and down)
+  const int blocks = ((a.n_tiles + 7) / 8) * ((a.M + 127) / 128);
+  const bool narrow = blocks < 256;
   switch (epi) {
-    case EPI_STORE: return launch_mm_t<EPI_STORE, 2, 2>(a, st, tm);
-    case EPI_ROPE: return launch_mm_t<EPI_ROPE, 2, 2>(a, st, tm);
+    case EPI_STORE:
+      return narrow ? launch_mm_t<EPI_STORE, 1, 2>(a, st, tm) : launch_mm_t<EPI_STORE, 2, 2>(a, st, tm);
+    case EPI_ROPE:
+      return narrow ? launch_mm_t<EPI_ROPE, 1, 2>(a, st, tm) : launch_mm_t<EPI_ROPE, 2, 2>(a, st, tm);
     case EPI_SILU: return launch_mm_t<EPI_SILU, 2, 2>(a, st, tm);
     case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 2, 2>(a, st, tm);
     default: return hipErrorInvalidValue;

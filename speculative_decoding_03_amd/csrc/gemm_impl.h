@@ -406,14 +406,34 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const in
       }
     }
   }
-  // otherwise up to 16 rows at a time, all their loads independent
+  // otherwise up to 16 rows at a time: the partials t = lane + 64j of the first RS_J values of j
+  // are all requested before any is added (one memory latency per 16 rows), then summed in the
+  // same order as above
   for (int m0 = 0; !rs.fast && m0 < a.M; m0 += 16) {
     const int nr = min(16, a.M - m0);
+    const int ld = yssq_ld(a);
     float s[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    for (int t = lane; t < a.n_yssq; t += WAVE) {
-      const float* p = a.yssq + (size_t)t * yssq_ld(a) + m0;
+    {
+      float v[RS_J][16];
+#pragma unroll
+      for (int j = 0; j < RS_J; ++j) {
+        const int t = min(lane + WAVE * j, a.n_yssq - 1);
+        const float* p = a.yssq + (size_t)t * ld + m0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[j][r] = p[min(r, nr - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < RS_J; ++j)
+        if (lane + WAVE * j < a.n_yssq) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r < nr) s[r] += v[j][r];
+        }
+    }
+    for (int t = lane + WAVE * RS_J; t < a.n_yssq; t += WAVE) {
+      const float* p = a.yssq + (size_t)t * ld + m0;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (r < nr) s[r] += p[r];

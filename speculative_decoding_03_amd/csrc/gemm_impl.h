@@ -297,12 +297,17 @@ __device__ __forceinline__ void q4_row_loop(const GemmArgs& a, const size_t (&wt
   }
 }
 
-// Row-scale partial sums of up to 4 rows with n_yssq <= 64 * RS_J, loaded into registers after the
-// main loop and before the split-K reduction, so that their latency overlaps its barriers.
-constexpr int RS_J = 5;
-struct RowScaleLoads {
-  float v[RS_J][4];
-  bool fast;
+// RMSNorm row scales 1/sqrt(sum_t yssq[t][r] / yscale_n + eps), from the sums of squares the
+// producer of X left per 16-column tile t.  Every wave of a unit sums the tiles of its own
+// reduction slice (tiles 2*kb0 .. 2*kb1, requested before its main loop): lane kg*16 + c adds
+// tiles t0 + kg, t0 + kg + 4, ... of row c (+16 per M-tile) in ascending order, the four lane
+// groups are added on the row swaps, and the unit's waves are added in wave order through LDS.
+// The order is the same for every call size and layout, so a row's scale never depends on the
+// call's other rows.
+constexpr int RSL = 10;  // partials per lane and 16-row group requested ahead of the main loop
+template <int MT> struct RowPart {
+  float v[MT][RSL];
+  int t0, t1;  // the wave's tile slice
 };
 
 // Local row of element v of M-tile mt in a lane.  The MFMA leaves rows (lane/16)*4 + v of
@@ -374,78 +379,48 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int tile0, int l
 
 __device__ __forceinline__ int yssq_ld(const GemmArgs& a) { return a.ld_yssq ? a.ld_yssq : a.M; }
 
-__device__ __forceinline__ void row_scale_load(const GemmArgs& a, int lane, RowScaleLoads& rs) {
-  rs.fast = a.yssq && a.M <= 4 && a.n_yssq <= WAVE * RS_J;
-  if (!rs.fast) return;
+template <int MT>
+__device__ __forceinline__ void rowpart_load(const GemmArgs& a, int lane, int kb0, int kb1,
+                                             RowPart<MT>& p) {
+  p.t0 = min(2 * kb0, a.n_yssq);
+  p.t1 = min(2 * kb1, a.n_yssq);
   const int ld = yssq_ld(a);
 #pragma unroll
-  for (int j = 0; j < RS_J; ++j) {
-    const int t = lane + WAVE * j;
+  for (int g = 0; g < MT; ++g) {
+    const int row = min(g * 16 + (lane & 15), a.M - 1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rs.v[j][r] = (t < a.n_yssq && r < a.M) ? a.yssq[(size_t)t * ld + r] : 0.f;
+    for (int i = 0; i < RSL; ++i) {
+      const int t = min(p.t0 + (lane >> 4) + 4 * i, a.n_yssq - 1);  // past the slice: not added
+      p.v[g][i] = a.yssq[(size_t)t * ld + row];
+    }
   }
 }
 
-// Row scales 1/sqrt(sum_t yssq[t][r] / yscale_n + eps) for the rows this lane holds (r = the X
-// row a local row reads: xr[mt] holds it for local row mt*16 + lane%16).  The sum runs
-// lane-strided then through a fixed butterfly, identically for every caller.
+// The wave's slice sums: part[g] for row g*16 + lane%16, identical in the four lanes of the row.
 template <int MT>
-__device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const int (&xr)[MT],
-                                           const RowScaleLoads& rs, float (&sc)[MT][4]) {
-  float mine = 1.f;
-  if (rs.fast) {
-    // per row the partials are added in ascending order, as below
+__device__ __forceinline__ void rowpart_sum(const GemmArgs& a, int lane, const RowPart<MT>& p,
+                                            float (&part)[MT]) {
+  const int ld = yssq_ld(a);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float s = 0.f;
+  for (int g = 0; g < MT; ++g) {
+    const int row = min(g * 16 + (lane & 15), a.M - 1);
+    float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < RS_J; ++j) s += rs.v[j][r];
-      if (r < a.M) {
-        const float w = wave_sum(s);
-        if (lane == r) mine = 1.0f / sqrtf(w / (float)a.yscale_n + a.eps);
-      }
-    }
+    for (int i = 0; i < RSL; ++i)
+      if (p.t0 + (lane >> 4) + 4 * i < p.t1) s += p.v[g][i];
+    for (int t = p.t0 + (lane >> 4) + 4 * RSL; t < p.t1; t += 4) s += a.yssq[(size_t)t * ld + row];
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    part[g] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  // otherwise up to 16 rows at a time: the partials t = lane + 64j of the first RS_J values of j
-  // are all requested before any is added (one memory latency per 16 rows), then summed in the
-  // same order as above
-  for (int m0 = 0; !rs.fast && m0 < a.M; m0 += 16) {
-    const int nr = min(16, a.M - m0);
-    const int ld = yssq_ld(a);
-    float s[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    {
-      float v[RS_J][16];
-#pragma unroll
-      for (int j = 0; j < RS_J; ++j) {
-        const int t = min(lane + WAVE * j, a.n_yssq - 1);
-        const float* p = a.yssq + (size_t)t * ld + m0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[j][r] = p[min(r, nr - 1)];
-      }
-#pragma unroll
-      for (int j = 0; j < RS_J; ++j)
-        if (lane + WAVE * j < a.n_yssq) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (r < nr) s[r] += v[j][r];
-        }
-    }
-    for (int t = lane + WAVE * RS_J; t < a.n_yssq; t += WAVE) {
-      const float* p = a.yssq + (size_t)t * ld + m0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (r < nr) s[r] += p[r];
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < nr) {
-        const float v = wave_sum(s[r]);
-        if (lane == m0 + r) mine = 1.0f / sqrtf(v / (float)a.yscale_n + a.eps);
-      }
-    }
-  }
+}
+
+// The scale of each element of the lane's results, from `mine` = the scale of X row `lane`
+// (r = the X row a local row reads: xr[mt] holds it for local row mt*16 + lane%16).
+template <int MT>
+__device__ __forceinline__ void row_scale_spread(const GemmArgs& a, int lane, const int (&xr)[MT],
+                                                 float mine, float (&sc)[MT][4]) {
   const bool narrow = MT == 1 && a.M <= 4;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -460,7 +435,7 @@ __device__ __forceinline__ void row_scales(const GemmArgs& a, int lane, const in
 template <typename T, int MT, int NU, int EPI, bool ADDEND = true>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT], int u,
                                          int tile0, int grp, const int (&xr)[MT],
-                                         const RowScaleLoads& rs, const EpiPre<MT, NU>& pre, int lane) {
+                                         float mine, const EpiPre<MT, NU>& pre, int lane) {
   const int c16 = lane & 15;
   const bool narrow = MT == 1 && a.M <= 4;
   if (narrow) {
@@ -475,7 +450,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
   }
   if (a.yssq) {
     float sc[MT][4];
-    row_scales<MT>(a, lane, xr, rs, sc);
+    row_scale_spread<MT>(a, lane, xr, mine, sc);
 #pragma unroll
     for (int t = 0; t < NU; ++t)
 #pragma unroll
@@ -695,6 +670,7 @@ template <int NU, int MT> struct Unroll {
 template <typename T, int MT, int NU, int EPI, int NW, bool WC, bool Q4>
 __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   __shared__ f32x4 red[NW * NU * 64];
+  __shared__ float rsum[NW][64];  // per wave: its slice of each row's sum of squares
   const int lane = threadIdx.x & (WAVE - 1);
   // wave index, wave-uniform (readfirstlane tells the compiler, so the split bounds and the
   // main loop's trip count live in scalar registers and its branches are uniform)
@@ -739,12 +715,11 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
   // epilogue operands and row-scale partials, requested before the main loop (the wave that
   // finishes each unit is the ks == 0 one)
   EpiPre<MT, NU> pre;
-  RowScaleLoads rs;
-  rs.fast = false;
-  if (active && ks == 0) {
-    epi_prefetch<MT, NU, EPI>(a, tile0, lane, pre);
-    row_scale_load(a, lane, rs);
-  }
+  if (active && ks == 0) epi_prefetch<MT, NU, EPI>(a, tile0, lane, pre);
+  // this wave's share of the RMSNorm row-scale sums (all waves of the unit)
+  const bool scaled = a.yssq != nullptr && active;  // wave-uniform
+  RowPart<MT> rp;
+  if (scaled) rowpart_load<MT>(a, lane, kb0, kb1, rp);
 
   if constexpr (Q4) {
     if (active) {
@@ -937,7 +912,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     else row_major(std::integral_constant<int, MT>{});
   }
 
+  float part[MT];
+  if (scaled) rowpart_sum<MT>(a, lane, rp, part);
+  float mine = 1.f;  // the RMSNorm scale of X row `lane`
+  auto finish_scale = [&](float total) { mine = 1.0f / sqrtf(total / (float)a.yscale_n + a.eps); };
   if (KW > 1) {
+    // the row-scale slices of the unit's waves, added in wave order after the first barrier
+    if (scaled && lane < 16) {
+#pragma unroll
+      for (int g = 0; g < MT; ++g) rsum[wid][g * 16 + lane] = part[g];
+    }
     // sum the KW partial accumulators of each unit in wave order, one M-tile at a time
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -957,9 +941,22 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
       __syncthreads();
     }
     if (ks != 0) return;
+    if (scaled) {
+      float total = rsum[wid][lane];
+      for (int k2 = 1; k2 < KW; ++k2) total += rsum[wid + k2][lane];
+      finish_scale(total);
+    }
+  } else if (scaled) {
+    // one wave: every lane of column c holds the sums of rows g*16 + c, so lane `lane` has row
+    // `lane` in part[lane / 16]
+    float total = part[0];
+#pragma unroll
+    for (int g = 1; g < MT; ++g)
+      if ((lane >> 4) == g) total = part[g];
+    finish_scale(total);
   }
   if (!active) return;
-  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, rs, pre, lane);
+  epilogue<T, MT, NU, EPI>(a, acc, u, tile0, grp, xr, mine, pre, lane);
 }
 
 template <typename T, int MT, int NU, int EPI, int NW, bool WC, bool Q4>

@@ -160,12 +160,10 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
     const int m = mt * 16 + (lane & 15);
     xr[mt] = m < e.M ? m : -1;
   }
-  RowScaleLoads rs;
-  rs.fast = false;
   if constexpr (EPI == EPI_ARGMAX) {
     // one argmax unit of 64 columns
     EpiPre<4, 4> pre;
-    epilogue<bf16_t, 4, 4, EPI, false>(e, acc, tile0 >> 2, tile0, 0, xr, rs, pre, lane);
+    epilogue<bf16_t, 4, 4, EPI, false>(e, acc, tile0 >> 2, tile0, 0, xr, 1.f, pre, lane);
   } else {
     // two halves of two tiles each (for SiLU: a gate and an up tile), so that the epilogue's
     // prefetched operands stay within the main loop's register budget
@@ -176,7 +174,7 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
       f32x4 (&part)[2][4] = *reinterpret_cast<f32x4 (*)[2][4]>(&acc[2 * hh][0]);
       EpiPre<4, 2> pre;
       epi_prefetch<4, 2, EPI>(e, t0, lane, pre);
-      epilogue<bf16_t, 4, 2, EPI, false>(e, part, t0 >> 1, t0, 0, xr, rs, pre, lane);
+      epilogue<bf16_t, 4, 2, EPI, false>(e, part, t0 >> 1, t0, 0, xr, 1.f, pre, lane);
       __builtin_amdgcn_sched_barrier(0);  // the halves' registers do not overlap
     }
   }

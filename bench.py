@@ -724,9 +724,9 @@ def main() -> int:
         M = B * (K + 1)
         lb = gate_up_bytes(cfg, M)
         achieved = lb / (launch_ms * 1e-3) / 1e9
-        kw, units, nw, groups = eng.query_split(0)
+        kw, nu, units, nw, groups = eng.query_launch(0, M)
         q4 = "true" if args.wformat == "q4" else "false"
-        kname = f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, 2, 2, {nw}, false, {q4}>"
+        kname = f"gemm_kernel<bf16, {1 if M <= 16 else (2 if M <= 32 else 4)}, {nu}, 2, {nw}, false, {q4}>"
         grid = groups * nw * 64
         traffic = load_traffic(f"gemm_gate_up_{args.config}" + (f"_b{B}" if B > 1 else "")
                                + ("_q4" if args.wformat == "q4" else ""), kname, grid, lb)

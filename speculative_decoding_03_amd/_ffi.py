@@ -29,7 +29,7 @@ EXPORTS = [
     "specdec_draft", "specdec_draft_traced", "specdec_draft_tree", "specdec_verify", "specdec_prefill",
     "specdec_verify_tree", "specdec_accept_tree", "specdec_accept", "specdec_kv_commit",
     "specdec_pack_matrix", "specdec_q4_bytes", "specdec_pack_q4", "specdec_set_len_bound", "specdec_read_device_error",
-    "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_error_string",
+    "specdec_profile_start", "specdec_profile_read", "specdec_query_split", "specdec_query_launch", "specdec_error_string",
     "specdec_moe_usage_start", "specdec_moe_usage_read", "specdec_k_policy_init",
     "specdec_k_policy_observe", "specdec_k_policy_acceptance", "specdec_k_policy_choose",
 ]
@@ -106,6 +106,7 @@ def load(path: str = LIB_PATH):
         "specdec_profile_start": (C.c_int, [vp, i32, i32]),
         "specdec_profile_read": (C.c_int, [vp, P(C.c_float), i32, P(i32)]),
         "specdec_query_split": (C.c_int, [vp, i32, P(i32), P(i32), P(i32), P(i32)]),
+        "specdec_query_launch": (C.c_int, [vp, i32, i32, P(i32), P(i32), P(i32), P(i32), P(i32)]),
         "specdec_error_string": (C.c_char_p, [C.c_int]),
         "specdec_k_policy_init": (C.c_int, [P(KPolicy), i32, i32, C.c_float, C.c_float, C.c_float,
                                             C.c_float, C.c_float, C.c_float]),

@@ -602,20 +602,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[NU][MT]
         }
       }
   } else if constexpr (EPI == EPI_SILU) {
-    const int f = (tile0 >> 1) * TILE_N + c16;
+    // tiles (2p, 2p+1) of the unit are the gate and up columns of product tile tile0/2 + p
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int p = 0; p < NU / 2; ++p) {
+      if (tile0 + 2 * p >= a.n_tiles) break;  // wave-uniform
+      const int f = ((tile0 >> 1) + p) * TILE_N + c16;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (narrow && v > 0) continue;  // uniform
-        const int m = local_row(narrow, mt, v, lane);
-        if (m < a.M) {
-          const float g = acc[0][mt][v];
-          const float up = acc[1][mt][v];
-          const float h = g / (1.0f + expf(-g)) * up;
-          Elem<T>::store(reinterpret_cast<T*>(a.hout) + x_offset(a.out_qx, m, f, a.ldh), h);
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (narrow && v > 0) continue;  // uniform
+          const int m = local_row(narrow, mt, v, lane);
+          if (m < a.M) {
+            const float g = acc[2 * p][mt][v];
+            const float up = acc[2 * p + 1][mt][v];
+            const float h = g / (1.0f + expf(-g)) * up;
+            Elem<T>::store(reinterpret_cast<T*>(a.hout) + x_offset(a.out_qx, m, f, a.ldh), h);
+          }
         }
-      }
+    }
   } else {  // EPI_ARGMAX
     const int keep_row = a.unit_row ? a.unit_row[u] : -1;
 #pragma unroll
@@ -996,6 +1001,9 @@ hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st,
   if (epi == EPI_ROPE && NU == 1) return launch_nw<T, MT, 1, EPI_ROPE, Q4>(a, st, tm);
   if (epi == EPI_ROPE && NU == 2) return launch_nw<T, MT, 2, EPI_ROPE, Q4>(a, st, tm);
   if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU, Q4>(a, st, tm);
+  // gated units of four gate/up pairs: bf16 calls of 17..32 rows
+  if constexpr (MT == 2 && !Q4 && sizeof(T) == 2)
+    if (epi == EPI_SILU && NU == 8) return launch_nw<T, MT, 8, EPI_SILU, Q4>(a, st, tm);
   if (epi == EPI_SILU_G && NU == 2) return launch_nw<T, MT, 2, EPI_SILU_G, Q4>(a, st, tm);
   if (epi == EPI_STORE_G && NU == 1) return launch_nw<T, MT, 1, EPI_STORE_G, Q4>(a, st, tm);
   if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX, Q4>(a, st, tm);

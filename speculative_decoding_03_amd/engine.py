@@ -406,6 +406,14 @@ class Engine:
                                              C.byref(w), C.byref(g)), "specdec_query_split")
         return s.value, u.value, w.value, g.value
 
+    def query_launch(self, kernel_class: int, rows: int):
+        """(split-K factor, tiles per unit, work units, waves per workgroup, workgroups) of one
+        launch of a call of `rows` rows."""
+        v = [C.c_int32() for _ in range(5)]
+        F.check(self.lib.specdec_query_launch(self.ctx, kernel_class, rows,
+                                              *[C.byref(x) for x in v]), "specdec_query_launch")
+        return tuple(x.value for x in v)
+
     def close(self) -> None:
         if getattr(self, "ctx", None):
             self.lib.specdec_destroy(self.ctx)

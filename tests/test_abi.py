@@ -105,6 +105,9 @@ def test_null_handles_are_rejected(lib):
     assert lib.specdec_accept(None, 1, 1, None, None, None, None, 0, None) == F.E_INVAL
     assert lib.specdec_kv_commit(None, 1, None, None) == F.E_INVAL
     assert lib.specdec_prefill(None, 0, 1, None, None, None, None) == F.E_INVAL
+    i = C.c_int32()
+    assert lib.specdec_query_split(None, 0, *[C.byref(i)] * 4) == F.E_INVAL
+    assert lib.specdec_query_launch(None, 0, 1, *[C.byref(i)] * 5) == F.E_INVAL
     out = C.c_void_p()
     assert lib.specdec_create(None, None, None, None, None, None, None, 0, None, C.byref(out)) == F.E_INVAL
     assert out.value is None

@@ -152,6 +152,21 @@ def test_batched_spec_equals_batched_greedy(bcase):
     assert eng.device_error() == 0
 
 
+def test_gated_units_of_the_batched_call(bcase):
+    """A call of 17..32 rows of the wide dense gate/up projection (31B width) takes units of four
+    gate/up pairs (so the verify test above runs them); calls of 16 rows or fewer, 4-bit weights
+    and the narrower shared FFN of the mixture-of-experts model keep units of one pair.  The
+    split-K is the same for every call size."""
+    cfg, eng = bcase["cfg"], bcase["eng"]
+    M = cfg.batch * (cfg.draft_k + 1)
+    kw, nu, units, nw, groups = eng.query_launch(0, M)
+    kw1, nu1, units1, nw1, groups1 = eng.query_launch(0, cfg.batch)
+    assert kw == kw1 and nu1 == 2
+    wide = 16 < M <= 32 and cfg.weight_format == "dense" and not cfg.is_moe
+    assert nu == (8 if wide else 2)
+    assert units * nu == units1 * nu1 and groups == units * kw // nw
+
+
 @pytest.mark.parametrize("wformat", ["dense", "q4"])
 def test_prefill_call_of_64_rows_matches_oracle(wformat):
     """One 64-row verify call (a prefill chunk) at the E2B width after 530 committed positions:

@@ -361,6 +361,9 @@ __global__ void __launch_bounds__(256) cluster_select_kernel(const float* z, int
 // Mixture-of-experts routing (one workgroup): per row, the top_k router logits by repeated
 // wave argmax (ties -> lower expert id) and their softmax weights; then, per expert, the rows
 // routed to it in ascending row order, and the ascending list of experts that received a row.
+// The per-expert lists come from a bit set of rows per expert: a (row, expert) pair's place in
+// its expert's list is the number of lower rows routed to that expert, so every pair writes its
+// own entry with no ordering between threads.
 constexpr int MOE_MAX_M = 64, MOE_MAX_E = 256, MOE_MAX_K = 16;
 
 constexpr int MOE_ROUTE_WAVES = 16;
@@ -371,10 +374,11 @@ __global__ void __launch_bounds__(MOE_ROUTE_WAVES * 64) moe_route_kernel(const f
                                                         int* n_groups, int* usage, int* err) {
   __shared__ int sel[MOE_MAX_M][MOE_MAX_K];
   __shared__ float selw[MOE_MAX_M][MOE_MAX_K];
-  __shared__ int cnt[MOE_MAX_E];
+  __shared__ unsigned long long rows_of[MOE_MAX_E];  // bit m: row m is routed to the expert
   __shared__ int wtot[MOE_ROUTE_WAVES];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) rows_of[e] = 0ull;
   for (int m = wid; m < M; m += MOE_ROUTE_WAVES) {
     const float* r = logits + (size_t)m * E;
     float v[MOE_MAX_E / WAVE];
@@ -433,26 +437,30 @@ __global__ void __launch_bounds__(MOE_ROUTE_WAVES * 64) moe_route_kernel(const f
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int m = 0; m < M; ++m)
-      for (int k = 0; k < top_k; ++k)
-        if (sel[m][k] == e) {
-          xrow[(size_t)e * M + c] = m;
-          orow[(size_t)e * M + c] = m * top_k + k;
-          wt[(size_t)e * M + c] = selw[m][k];
-          ++c;
-        }
-    for (int i = c; i < M; ++i) {
-      xrow[(size_t)e * M + i] = -1;
-      orow[(size_t)e * M + i] = -1;
-      wt[(size_t)e * M + i] = 0.f;
-    }
-    cnt[e] = c;
+  const int P = M * top_k;  // (row, rank) pairs, at most MOE_MAX_M * MOE_MAX_K = 1024
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    const int m = p / top_k;
+    atomicOr(&rows_of[sel[m][p - m * top_k]], 1ull << m);
   }
   __syncthreads();
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    const int m = p / top_k, k = p - m * top_k;
+    const int e = sel[m][k];
+    const int c = __popcll(rows_of[e] & ((1ull << m) - 1ull));  // lower rows of this expert
+    xrow[(size_t)e * M + c] = m;
+    orow[(size_t)e * M + c] = p;
+    wt[(size_t)e * M + c] = selw[m][k];
+  }
+  for (int q = threadIdx.x; q < E * M; q += blockDim.x) {
+    const int e = q / M;
+    if (q - e * M >= __popcll(rows_of[e])) {  // past the expert's rows
+      xrow[q] = -1;
+      orow[q] = -1;
+      wt[q] = 0.f;
+    }
+  }
   const int e = threadIdx.x;
-  const bool used = e < E && cnt[e] > 0;
+  const bool used = e < E && rows_of[e] != 0ull;
   const unsigned long long mask = __ballot(used);
   if (lane == 0) wtot[wid] = __popcll(mask);
   __syncthreads();

@@ -379,62 +379,90 @@ __global__ void __launch_bounds__(MOE_ROUTE_WAVES * 64) moe_route_kernel(const f
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += blockDim.x) rows_of[e] = 0ull;
-  for (int m = wid; m < M; m += MOE_ROUTE_WAVES) {
-    const float* r = logits + (size_t)m * E;
-    float v[MOE_MAX_E / WAVE];
-    int id[MOE_MAX_E / WAVE];
-    bool nan = false;
+  // Every logit of the wave's rows is requested before any is used (one memory round trip); a
+  // row or expert past the call reads a valid entry, masked below.
+  constexpr int RPW = MOE_MAX_M / MOE_ROUTE_WAVES;  // rows per wave
+  constexpr int EPL = MOE_MAX_E / WAVE;             // logits per lane and row
+  __shared__ float wsel[MOE_ROUTE_WAVES][MOE_MAX_K];
+  float lv[RPW][EPL];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_E / WAVE; ++j) {
-      const int e = lane + WAVE * j;
-      v[j] = -INFINITY;
-      id[j] = 0x7fffffff;
-      if (e < E) {
-        const float x = r[e];
-        nan |= (x != x);
-        v[j] = (x != x) ? -INFINITY : x;
-        id[j] = e;
-      }
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      lv[i][j] = logits[(size_t)min(wid + MOE_ROUTE_WAVES * i, M - 1) * E + min(lane + WAVE * j, E - 1)];
+  const unsigned long long below = (1ull << lane) - 1ull;  // lanes under this one
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int m = wid + MOE_ROUTE_WAVES * i;
+    if (m >= M) break;  // wave-uniform
+    // Selection of the top_k logits, larger first and the lower expert id on equal values, as
+    // one threshold: the top_k-th largest key of the order-preserving integer keys (NaN as -inf,
+    // -0 as +0), found bit by bit from the wave's counts; then the experts with equal keys are
+    // taken in ascending id up to top_k.  Expert e = lane + 64 j sits in slot j of its lane.
+    uint32_t key[EPL];
+    float v[EPL];
+    bool ok[EPL], nan = false;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const float x = lv[i][j];
+      ok[j] = lane + WAVE * j < E;
+      nan |= ok[j] && (x != x);
+      v[j] = x == x ? x + 0.0f : -INFINITY;  // + 0 turns -0 into +0
+      const uint32_t u = __float_as_uint(v[j]);
+      key[j] = ok[j] ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
     }
     if (nan) raise_error(err, ERRBIT_NAN);
-    float sv[MOE_MAX_K];
-    int si[MOE_MAX_K];
+    auto count_ge = [&](uint32_t t) {
+      int c = 0;
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_K; ++k) {
-      sv[k] = 0.f;
-      si[k] = 0x7fffffff;
-      if (k < top_k) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_E / WAVE; ++j) argmax_combine(bv, bi, v[j], id[j]);
-        wave_argmax(bv, bi);
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_E / WAVE; ++j)
-          if (id[j] == bi) {
-            v[j] = -INFINITY;
-            id[j] = 0x7fffffff;
-          }
-        sv[k] = bv;
-        si[k] = bi;
-      }
+      for (int j = 0; j < EPL; ++j) c += __popcll(__ballot(ok[j] && key[j] >= t));
+      return c;
+    };
+    uint32_t T = 0u;  // the largest threshold with at least top_k keys at or above it
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      if (count_ge(cand) >= top_k) T = cand;
     }
-    if (lane == 0) {
-      // ascending expert id: the rank of each selected id among the selected ones
+    int above = 0;
 #pragma unroll
-      for (int k = 0; k < MOE_MAX_K; ++k) {
-        if (k < top_k) {
-          int rank = 0;
+    for (int j = 0; j < EPL; ++j) above += __popcll(__ballot(ok[j] && key[j] > T));
+    const int need = top_k - above;  // experts with key == T taken, lowest ids first
+    bool pick[EPL];
+    int tie_before = 0;  // equal keys at lower expert ids
 #pragma unroll
-          for (int k2 = 0; k2 < MOE_MAX_K; ++k2) rank += (k2 < top_k && si[k2] < si[k]);
-          sel[m][rank] = si[k];
-          selw[m][rank] = expf(sv[k] - sv[0]);  // sv[0] is the largest selected logit
-        }
-      }
-      float sum = 0.f;
-      for (int k = 0; k < top_k; ++k) sum += selw[m][k];
-      for (int k = 0; k < top_k; ++k) selw[m][k] = selw[m][k] / sum;
+    for (int j = 0; j < EPL; ++j) {
+      const bool tie = ok[j] && key[j] == T;
+      const unsigned long long b = __ballot(tie);
+      pick[j] = (ok[j] && key[j] > T) || (tie && tie_before + __popcll(b & below) < need);
+      tie_before += __popcll(b);
     }
+    // the selected experts in ascending id (slot 0 lanes first): their rank is their place
+    float vmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) vmax = fmaxf(vmax, pick[j] ? v[j] : -INFINITY);
+    vmax = wave_max(vmax);  // the largest selected logit
+    int before = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const unsigned long long b = __ballot(pick[j]);
+      if (pick[j]) {
+        const int rank = before + __popcll(b & below);
+        const float w = expf(v[j] - vmax);
+        sel[m][rank] = lane + WAVE * j;
+        wsel[wid][rank] = w;
+      }
+      before += __popcll(b);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the weights' sum in rank order, then each weight divided by it
+    float sum = 0.f;
+    for (int k = 0; k < top_k; ++k) sum += wsel[wid][k];
+    if (lane < top_k) selw[m][lane] = wsel[wid][lane] / sum;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   __syncthreads();
   const int P = M * top_k;  // (row, rank) pairs, at most MOE_MAX_M * MOE_MAX_K = 1024

@@ -415,6 +415,48 @@ def test_argmax_ties_pick_lowest_id():
     eng.close()
 
 
+@pytest.mark.parametrize("pattern", ["all-zero", "copies-of-three"])
+def test_moe_routing_ties_pick_lowest_ids(pattern):
+    """Router weights whose logits tie exactly: all rows zero (every logit +-0, so the top-k are
+    the lowest ids, 0..3), or row e a copy of row e % 3 (three values, each repeated at ids
+    congruent mod 3: the top-k are the lowest ids holding the largest value, with the k-th pick
+    decided among equal logits).  The GPU must choose the experts the oracle chooses: the logits of
+    every prompt row match."""
+    cfg = preset("tiny-moe")
+    prompt = prompt_tokens(cfg)[0][:32]
+
+    def tie(r):  # a numpy array (oracle) or a device tensor (weight source)
+        r = r.clone() if hasattr(r, "clone") else np.array(r, copy=True)
+        if pattern == "all-zero":
+            r[:] = 0
+        else:
+            for e in range(r.shape[0]):
+                r[e] = r[e % 3]
+        return r
+
+    class Ties:
+        def __init__(self, src):
+            self.src = src
+
+        def get(self, name, layer, shape):
+            t = self.src.get(name, layer, shape)
+            return tie(t) if name == "router" else t
+
+    eng = build_engine(cfg, 64, weights_override=lambda s: Ties(s))
+    try:
+        t0, logits = gpu_prefill(eng, prompt)
+        W, _ = oracle_model(cfg)
+        for lw in W["layers"]:
+            lw["router"] = tie(lw["router"])
+        cache = O.KVCache.empty(cfg, 64)
+        for pos, tok in enumerate(prompt):
+            ref, _ = O.target_row(W, cfg, cache, int(tok), pos)
+            assert rel_err(logits[pos], ref) < TOL, f"row {pos}"
+        assert eng.device_error() == 0
+    finally:
+        eng.close()
+
+
 def test_error_paths(tiny):
     CFG = tiny["cfg"]
     eng = tiny["eng"]

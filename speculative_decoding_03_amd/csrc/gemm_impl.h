@@ -746,7 +746,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
     }
   }
   bool quad_done = Q4;
-  if constexpr (MT == 1 && !GROUPED && !Q4) {
+  if constexpr (MT == 1 && !Q4) {
     if (active && a.x_qx) {
       // X in the quad layout (at most 4 rows): one wave load per four k-blocks, shared by the
       // batch's k-blocks through DPP row shifts.  kb0 is a multiple of 4.
@@ -756,7 +756,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_kernel(GemmArgs a) {
       constexpr int S = QuadStages<NU>::S;  // register stages, used as a ring
       Frag<T> w[S][U][NU];
       Frag<T> xq[S];
-      const T* Xq = reinterpret_cast<const T*>(a.X) + (size_t)lane * 8;
+      int xl = lane;  // this lane's place in a quad block: row slot lane % 4
+      if constexpr (GROUPED) {
+        // a routed expert's rows are gathered: row slot r reads source row xrow_map[r] (a slot
+        // no row was routed to reads row 0; its output row is never stored)
+        const int src = __shfl(xr[0], lane & 3, WAVE);
+        xl = lane - (lane & 3) + max(src, 0);
+      }
+      const T* Xq = reinterpret_cast<const T*>(a.X) + (size_t)xl * 8;
       size_t wt_tile[NU];
 #pragma unroll
       for (int t = 0; t < NU; ++t) wt_tile[t] = (size_t)min(tile0 + t, a.n_tiles - 1);

@@ -10,8 +10,9 @@
 // global memory into LDS, laid out in MFMA operand order (a fragment = 64 lanes x 16 bytes,
 // contiguous), so each wave reads its four X fragments and four weight fragments per k-block
 // with conflict-free 16-byte LDS reads and issues sixteen v_mfma_f32_16x16x32_bf16.  Two LDS
-// stages alternate: the next stage's global loads are in flight while the current one is
-// multiplied, and one barrier per stage separates writing a stage from reading it.  The
+// stages alternate: the next D stages' global loads are in flight (a register ring) while the
+// current one is multiplied, and one barrier per stage separates writing a stage from reading it.
+// Wide projections take 256 x 256 blocks (16 waves), narrower ones 128 x 128 or 64 x 128.  The
 // per-row, per-tile reduction order is fixed (k-blocks ascending), independent of M and of the
 // block shape.
 
@@ -20,10 +21,9 @@
 namespace specdec {
 namespace gemm_detail {
 
-constexpr int MM_KS = 2;  // k-blocks per LDS stage
-
-template <int EPI, int WM, int WN>
-__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) mm_kernel(GemmArgs a) {
+template <int EPI, int WM, int WN, int KS, int D>
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4 > 2 ? WM * WN / 4 : 2))) mm_kernel(GemmArgs a) {
+  constexpr int MM_KS = KS;               // k-blocks per LDS stage
   constexpr int NTH = WM * WN * 64;
   constexpr int BMT = 4 * WM;             // 16-row M-tiles per block
   constexpr int BNT = 4 * WN;             // 16-column tiles per block
@@ -69,48 +69,61 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
     wsrc[j] = W + ((size_t)min(t_blk + t, a.n_tiles - 1) * nkb + kb) * TILE_ELEMS + ln * LANE_ELEMS;
     bdst[j] = (kb * BNT + t) * 64 + ln;
   }
-  u32x4 ra[A_RUNS], rb[B_RUNS];
-  auto load_stage = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < A_RUNS; ++j) ra[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + s * MM_KS * TILE_K);
-#pragma unroll
-    for (int j = 0; j < B_RUNS; ++j)
-      rb[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)s * MM_KS * TILE_ELEMS));
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < A_RUNS; ++j) sa[buf][adst[j]] = ra[j];
-#pragma unroll
-    for (int j = 0; j < B_RUNS; ++j) sb[buf][bdst[j]] = rb[j];
-  };
-
   f32x4 acc[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // D stages in flight in a register ring (slot = stage % D); a stage past the last one reads the
+  // last one again and is never stored
+  u32x4 ra[D][A_RUNS], rb[D][B_RUNS];
+  auto load_stage = [&](int slot, int st) {
+    const int s = min(st, n_st - 1);
+#pragma unroll
+    for (int j = 0; j < A_RUNS; ++j) ra[slot][j] = *reinterpret_cast<const u32x4*>(xsrc[j] + s * MM_KS * TILE_K);
+#pragma unroll
+    for (int j = 0; j < B_RUNS; ++j)
+      rb[slot][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)s * MM_KS * TILE_ELEMS));
+  };
+  auto store_stage = [&](int slot, int buf) {
+#pragma unroll
+    for (int j = 0; j < A_RUNS; ++j) sa[buf][adst[j]] = ra[slot][j];
+#pragma unroll
+    for (int j = 0; j < B_RUNS; ++j) sb[buf][bdst[j]] = rb[slot][j];
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kb = 0; kb < MM_KS; ++kb) {
+      Frag<bf16_t> xf[4], wf[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) xf[mt].v = sa[buf][(kb * BMT + wm * 4 + mt) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) wf[t].v = sb[buf][(kb * BNT + wn * 4 + t) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mma<bf16_t>(xf[mt], wf[t], acc[t][mt]);
+    }
+  };
+
   if (n_st > 0) {
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int s = 0; s < n_st; ++s) {
-      const int buf = s & 1;
-      if (s + 1 < n_st) load_stage(s + 1);  // in flight while this stage multiplies
 #pragma unroll
-      for (int kb = 0; kb < MM_KS; ++kb) {
-        Frag<bf16_t> xf[4], wf[4];
+    for (int d = 0; d < D; ++d) load_stage(d, d);
+    // Stage s: copied from its register slot into LDS buffer s % 2 (last read by stage s - 2,
+    // which every wave finished before the previous barrier), its slot refilled with stage
+    // s + D, one barrier, then multiplied.
+    for (int s0 = 0; s0 < n_st; s0 += D) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) xf[mt].v = sa[buf][(kb * BMT + wm * 4 + mt) * 64 + lane];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) wf[t].v = sb[buf][(kb * BNT + wn * 4 + t) * 64 + lane];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mma<bf16_t>(xf[mt], wf[t], acc[t][mt]);
+      for (int d = 0; d < D; ++d) {
+        const int s = s0 + d;
+        if (s < n_st) {  // uniform
+          store_stage(d, s & 1);
+          load_stage(d, s + D);
+          __syncthreads();
+          compute(s & 1);
+        }
       }
-      if (s + 1 < n_st) store_stage(buf ^ 1);  // the other stage was last read before the barrier
-      __syncthreads();
     }
   }
 
@@ -180,13 +193,14 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
   }
 }
 
-template <int EPI, int WM, int WN>
+template <int EPI, int WM, int WN, int KS = 2, int D = 1>
 hipError_t launch_mm_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
+  if (a.nkb % KS) return hipErrorInvalidValue;
   dim3 grid((a.n_tiles + 4 * WN - 1) / (4 * WN), (a.M + 64 * WM - 1) / (64 * WM)), block(WM * WN * 64);
   if (tm)
-    hipExtLaunchKernelGGL((mm_kernel<EPI, WM, WN>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+    hipExtLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D>), grid, block, 0, st, tm->start, tm->stop, 0, a);
   else
-    hipLaunchKernelGGL((mm_kernel<EPI, WM, WN>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -195,7 +209,7 @@ hipError_t launch_mm_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm
 hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   using namespace gemm_detail;
   if (a.M <= 0 || a.n_tiles <= 0) return hipSuccess;
-  if (a.nkb % MM_KS || a.wq4) return hipErrorInvalidValue;
+  if (a.nkb % 2 || a.wq4) return hipErrorInvalidValue;
   if (epi == EPI_ARGMAX && a.n_tiles % 4) return hipErrorInvalidValue;  // whole 64-column units
   if (epi == EPI_SILU && a.n_tiles % 2) return hipErrorInvalidValue;    // gate/up pairs
   // 128 x 128 blocks; a projection too narrow to give every CU a block takes 64 x 128 blocks of
@@ -207,8 +221,11 @@ hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTim
       return narrow ? launch_mm_t<EPI_STORE, 1, 2>(a, st, tm) : launch_mm_t<EPI_STORE, 2, 2>(a, st, tm);
     case EPI_ROPE:
       return narrow ? launch_mm_t<EPI_ROPE, 1, 2>(a, st, tm) : launch_mm_t<EPI_ROPE, 2, 2>(a, st, tm);
-    case EPI_SILU: return launch_mm_t<EPI_SILU, 2, 2>(a, st, tm);
-    case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 2, 2>(a, st, tm);
+    // the wide projections (gate/up, LM head): 256 x 256 blocks of 16 waves, half the LDS and L2
+    // bytes per product of 128 x 128 blocks (31B, 512 rows: prefill 303 -> 374 TFLOP/s; a
+    // register ring of 2 to 4 stages in flight instead of one gained nothing)
+    case EPI_SILU: return launch_mm_t<EPI_SILU, 4, 4>(a, st, tm);
+    case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 4, 4>(a, st, tm);
     default: return hipErrorInvalidValue;
   }
 }

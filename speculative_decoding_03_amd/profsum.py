@@ -14,6 +14,9 @@ dispatch).  Each is scaled by what the same counter reads for a plain device cop
   python -m speculative_decoding_03_amd.profsum traffic --fetch D --write D --copy-fetch D
       --copy-write D --match S --last N --algorithmic BYTES --src FILE --cmd CMD -o OUT
       per-dispatch HBM bytes of the matching kernel, written as JSON
+  python -m speculative_decoding_03_amd.profsum prefill DIR --config NAME --tokens T --cmd CMD
+      per-kernel time and TFLOP/s of the last prompt prefill call (embed to commit_rows) of
+      DIR/*kernel_trace.csv, with each kernel class's product count from the model's shapes
   python -m speculative_decoding_03_amd.profsum pass --fetch D --write D --copy-fetch D
       --copy-write D [--mfma D --cus N] --index I --algorithmic BYTES --cmd CMD -o OUT
       HBM bytes of every target pass (embed to accept, all kernels) from counter passes taken
@@ -169,6 +172,57 @@ def cmd_step(a) -> int:
     return 0
 
 
+def cmd_prefill(a) -> int:
+    """Kernels of the last prefill call (embed_kernel through commit_rows_kernel), with the
+    multiply-add count of each prompt-GEMM class and of the causal chunk attention (the chunk of T
+    rows starts after the configuration's context)."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from workloads import preset
+    cfg = preset(a.config)
+    T, L = a.tokens, cfg.n_layers
+    d, qd, kvd, F = cfg.d_model, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim
+    keys = sum(cfg.ctx + r + 1 for r in range(T))
+    flops = {  # by kernel name prefix and epilogue
+        "mm_kernel<1,": ("q/k/v + RoPE + KV append", 2.0 * T * L * d * (qd + 2 * kvd)),
+        "mm_kernel<0,": ("o + down (residual add)", 2.0 * T * L * (qd * d + F * d)),
+        "mm_kernel<2,": ("gate/up + SiLU product", 2.0 * T * L * d * 2 * F),
+        "mm_kernel<3,": ("tied LM head + argmax", 2.0 * T * d * cfg.vocab),
+        "attn_kernel": ("causal chunk attention", 4.0 * L * cfg.n_q_heads * cfg.head_dim * keys),
+    }
+    rows = trace_rows(a.dir)
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    s = [i for i, r in enumerate(rows) if "embed_kernel" in r["Kernel_Name"]][-1]
+    e = next(i for i in range(s, len(rows)) if "commit_rows_kernel" in rows[i]["Kernel_Name"])
+    agg, order = {}, []
+    for i in range(s, e + 1):
+        r = rows[i]
+        k = short_name(r["Kernel_Name"]).replace(" ", "")
+        if k not in agg:
+            agg[k] = [0, 0]
+            order.append(k)
+        agg[k][0] += 1
+        agg[k][1] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    span = (int(rows[e]["End_Timestamp"]) - int(rows[s]["Start_Timestamp"])) * 1e-9
+    total = sum(f for _, f in flops.values())
+    peak = a.peak_tflops
+    lines = [f"## {a.config}: {T} tokens at position {cfg.ctx}", "", f"command: {a.cmd}", "",
+             f"last call: span {span * 1e6:.1f} us, {total / 1e12:.2f} TFLOP of GEMM and attention "
+             f"work -> {total / span / 1e12:.1f} TFLOP/s ({100 * total / span / 1e12 / peak:.1f}% "
+             f"of the {peak / 1000:g} PFLOP/s dense bf16 MFMA peak)", "", "```",
+             f"{'kernel':<36} {'calls':>6} {'total us':>10} {'avg us':>9} {'TFLOP/s':>8}  what"]
+    for k in sorted(order, key=lambda k: -agg[k][1]):
+        n, t = agg[k]
+        what, f = next(((w, f) for pre, (w, f) in flops.items() if pre in k), ("", 0.0))
+        tf = f"{f / (t * 1e-9) / 1e12:8.1f}" if f else f"{'-':>8}"
+        lines.append(f"{k[:36]:<36} {n:>6} {t / 1e3:>10.1f} {t / n / 1e3:>9.2f} {tf}  {what}")
+    lines.append("```")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        open(a.out, "w").write(text)
+    sys.stdout.write(text)
+    return 0
+
+
 def _copy_factor(d: str, counter: str, known: float):
     vals = counter_values(d, counter, None)
     if not vals:
@@ -308,6 +362,13 @@ def main(argv=None) -> int:
     t.add_argument("--src", required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("-o", "--out")
+    pf = sp.add_parser("prefill")
+    pf.add_argument("dir")
+    pf.add_argument("--config", required=True)
+    pf.add_argument("--tokens", type=int, default=512)
+    pf.add_argument("--peak-tflops", type=float, default=2500.0)
+    pf.add_argument("--cmd", required=True)
+    pf.add_argument("-o", "--out")
     ps = sp.add_parser("pass")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         ps.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -321,7 +382,7 @@ def main(argv=None) -> int:
     ps.add_argument("-o", "--out")
     a = p.parse_args(argv)
     return {"copy": cmd_copy, "stats": cmd_stats, "step": cmd_step, "traffic": cmd_traffic,
-            "pass": cmd_pass}[a.what](a)
+            "pass": cmd_pass, "prefill": cmd_prefill}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -21,7 +21,17 @@
 namespace specdec {
 namespace gemm_detail {
 
-template <int EPI, int WM, int WN, int KS, int D>
+template <int EPI>
+__device__ void mm_finish(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int tile0, int lane);
+
+// The partial block of split z (k-range z of kpart_n) in MFMA accumulator order: wave w of block
+// (bx, by) holds 16 fragments (tile, M-tile) of 64 lanes x 4 floats, each a contiguous 1 KB.
+// Offset in floats of the wave's 16 x 64 x 4 floats.
+__device__ __forceinline__ size_t mm_part_offset(int z, int nblk, int blk, int nw, int w) {
+  return (((size_t)z * nblk + blk) * nw + w) * (16 * 64 * 4);
+}
+
+template <int EPI, int WM, int WN, int KS, int D, bool SPLIT>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4 > 2 ? WM * WN / 4 : 2))) mm_kernel(GemmArgs a) {
   constexpr int MM_KS = KS;               // k-blocks per LDS stage
   constexpr int NTH = WM * WN * 64;
@@ -41,7 +51,14 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
   const int m_blk = blockIdx.y * 64 * WM, t_blk = blockIdx.x * BNT;
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.X);
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.W);
-  const int nkb = a.nkb, n_st = nkb / MM_KS;
+  const int nkb = a.nkb;
+  // stages [st0, st0 + n_st) of the reduction: all of it, or split blockIdx.z of kpart_n
+  int st0 = 0, n_st = nkb / MM_KS;
+  if constexpr (SPLIT) {
+    const int z = blockIdx.z, tot = n_st;
+    st0 = (int)((long)tot * z / a.kpart_n);
+    n_st = (int)((long)tot * (z + 1) / a.kpart_n) - st0;
+  }
 
   // this thread's runs: run i = tid + j*NTH is lane i % 64 of fragment i / 64, so a wave writes
   // one whole fragment (64 consecutive 16-byte LDS slots, no bank conflict).  X fragment f is
@@ -79,7 +96,7 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
   // last one again and is never stored
   u32x4 ra[D][A_RUNS], rb[D][B_RUNS];
   auto load_stage = [&](int slot, int st) {
-    const int s = min(st, n_st - 1);
+    const int s = st0 + min(st, n_st - 1);
 #pragma unroll
     for (int j = 0; j < A_RUNS; ++j) ra[slot][j] = *reinterpret_cast<const u32x4*>(xsrc[j] + s * MM_KS * TILE_K);
 #pragma unroll
@@ -127,8 +144,46 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
     }
   }
 
-  // ---- the skinny kernel's epilogue on this wave's 64 x 64 sub-block ----
-  const int m0 = m_blk + wm * 64, tile0 = t_blk + wn * 4;
+  if constexpr (SPLIT) {
+    // this split's sums, for the reduction launch
+    float* dst = a.kpart + mm_part_offset(blockIdx.z, gridDim.x * gridDim.y,
+                                          blockIdx.y * gridDim.x + blockIdx.x, WM * WN, w);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        *reinterpret_cast<f32x4*>(dst + ((t * 4 + mt) * 64 + lane) * 4) = acc[t][mt];
+    return;
+  }
+  mm_finish<EPI>(a, acc, m_blk + wm * 64, t_blk + wn * 4, lane);
+}
+
+// Sums the kpart_n partial blocks of a split prompt GEMM in split order, then applies the
+// epilogue.  Workgroups of 4 waves (the epilogue's registers); block (x, y) of the split launch
+// is covered by workgroups (x, y, 0 .. WM*WN/4 - 1), wave w of the block by workgroup w / 4.
+template <int EPI, int WM, int WN>
+__global__ void __launch_bounds__(256) mm_reduce_kernel(GemmArgs a) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.z * 4 + (threadIdx.x >> 6));
+  const int wm = w % WM, wn = w / WM;
+  const int nblk = gridDim.x * gridDim.y, blk = blockIdx.y * gridDim.x + blockIdx.x;
+  f32x4 acc[4][4];
+  for (int z = 0; z < a.kpart_n; ++z) {
+    const float* src = a.kpart + mm_part_offset(z, nblk, blk, WM * WN, w);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + ((t * 4 + mt) * 64 + lane) * 4);
+        acc[t][mt] = z == 0 ? v : acc[t][mt] + v;
+      }
+  }
+  mm_finish<EPI>(a, acc, blockIdx.y * 64 * WM + wm * 64, blockIdx.x * 4 * WN + wn * 4, lane);
+}
+
+// ---- the skinny kernel's epilogue on one wave's 64 x 64 sub-block (rows m0.., tiles tile0..) ----
+template <int EPI>
+__device__ void mm_finish(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int tile0, int lane) {
   if (m0 >= a.M || tile0 >= a.n_tiles) return;
   GemmArgs e = a;
   e.M = min(64, a.M - m0);
@@ -197,19 +252,50 @@ template <int EPI, int WM, int WN, int KS = 2, int D = 1>
 hipError_t launch_mm_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   if (a.nkb % KS) return hipErrorInvalidValue;
   dim3 grid((a.n_tiles + 4 * WN - 1) / (4 * WN), (a.M + 64 * WM - 1) / (64 * WM)), block(WM * WN * 64);
+  if constexpr (WM * WN == 16) {
+    if (a.kpart_n > 1) {
+      // the reduction split over kpart_n workgroups per block, partials summed by a second launch
+      dim3 sgrid(grid.x, grid.y, a.kpart_n), rgrid(grid.x, grid.y, WM * WN / 4);
+      hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, true>), sgrid, block, 0, st, a);
+      if (tm)
+        hipExtLaunchKernelGGL((mm_reduce_kernel<EPI, WM, WN>), rgrid, dim3(256), 0, st, tm->start,
+                              tm->stop, 0, a);
+      else
+        hipLaunchKernelGGL((mm_reduce_kernel<EPI, WM, WN>), rgrid, dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.kpart_n > 1) return hipErrorInvalidValue;
   if (tm)
-    hipExtLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+    hipExtLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, false>), grid, block, 0, st, tm->start, tm->stop, 0, a);
   else
-    hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace gemm_detail
 
+size_t launch_mm_partial_floats(int n_tiles, int M, int kpart_n) {
+  // 256 x 256 blocks of 16 waves, each wave 16 fragments of 64 lanes x 4 floats
+  return kpart_n > 1 ? (size_t)kpart_n * ((n_tiles + 15) / 16) * ((M + 255) / 256) * 16 * 16 * 64 * 4 : 0;
+}
+
 hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   using namespace gemm_detail;
   if (a.M <= 0 || a.n_tiles <= 0) return hipSuccess;
   if (a.nkb % 2 || a.wq4) return hipErrorInvalidValue;
+  if (a.kpart_n > 1) {
+    // a projection too narrow for 256 x 256 blocks to fill the CUs: the same blocks with the
+    // reduction split kpart_n ways (at least one stage each), partials summed by a second launch
+    if (!a.kpart || a.kpart_n > a.nkb / 2) return hipErrorInvalidValue;
+    switch (epi) {
+      case EPI_STORE: return launch_mm_t<EPI_STORE, 4, 4>(a, st, tm);
+      case EPI_ROPE: return launch_mm_t<EPI_ROPE, 4, 4>(a, st, tm);
+      case EPI_SILU: return launch_mm_t<EPI_SILU, 4, 4>(a, st, tm);
+      case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 4, 4>(a, st, tm);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (epi == EPI_ARGMAX && a.n_tiles % 4) return hipErrorInvalidValue;  // whole 64-column units
   if (epi == EPI_SILU && a.n_tiles % 2) return hipErrorInvalidValue;    // gate/up pairs
   // 128 x 128 blocks; a projection too narrow to give every CU a block takes 64 x 128 blocks of

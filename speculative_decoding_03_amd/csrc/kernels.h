@@ -71,6 +71,10 @@ struct GemmArgs {
   // row strides of ssq and yssq (0: M); a launch over a slice of a longer call's rows uses the
   // call's row count
   int ld_ssq = 0, ld_yssq = 0;
+  // prompt GEMM (launch_mm) with its reduction split over kpart_n workgroups per block: fp32
+  // partial blocks in kpart (launch_mm_partial_floats), summed in split order by a second launch
+  float* kpart = nullptr;
+  int kpart_n = 1;
   // optional addend rows: y = (sum_{k < add_n} addend[(m*add_n + k)*ldo + col]) + y, k ascending
   const float* addend = nullptr;
   int add_n = 0;
@@ -119,8 +123,10 @@ hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hi
 // row-major bf16 X of a.M rows (any count), nkb % 2 == 0; epilogues EPI_STORE, EPI_ROPE (one
 // sequence: rows at positions len[0] + pos_off + row), EPI_SILU and EPI_ARGMAX (units of 64
 // columns, slot row * ld_amax + unit) as in launch_gemm.  The unit fields (nu, n_units, KW, NW,
-// kb_per_split) are not used.
+// kb_per_split) are not used.  With kpart_n > 1 the reduction is split
+// kpart_n ways over 256 x 256 blocks into a.kpart, which holds launch_mm_partial_floats floats.
 hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm = nullptr);
+size_t launch_mm_partial_floats(int n_tiles, int M, int kpart_n);
 
 // The 4-bit block weight format (common.h): a matrix [N][Kd] with N % 16 == 0 and
 // Kd % 128 == 0 takes q4_bytes(N, Kd) bytes.  launch_pack_q4 writes it from codes [N][Kd] (one

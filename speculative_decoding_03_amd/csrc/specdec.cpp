@@ -30,6 +30,7 @@ constexpr size_t ALIGN = 256;
 constexpr int TARGET_WAVES = 2048;   // waves per projection launch
 constexpr int MIN_KB_PER_WAVE = 8;   // k-blocks each wave streams at least
 constexpr int WIDE_NU = 8;            // tiles per gated unit in calls of 17..32 rows
+constexpr int MM_SPLIT_WGS = 240;     // workgroups of a prompt GEMM whose reduction is split
 constexpr int WIDE_MIN_UNITS = 400;   // ... when that leaves at least this many units
 // 4-bit weights carry 3.6x fewer bytes per k-block: each wave streams at least 16 (measured on
 // MI355X at the 31B shapes: 16 beats 8 and 32; wide gated projections split at most 4 ways)
@@ -303,7 +304,10 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
     L.p_h = take(P * c->ffn_dim * 2);
     L.p_amax_v = take(P * dm.parts * 4);
     L.p_amax_i = take(P * dm.parts * 4);
-    L.p_part = take((size_t)c->n_kv_heads * dm.n_chunks * P * G * (c->head_dim + 4) * 4);
+    // the chunk attention's partials, and (at other times of the layer) the prompt GEMM's split
+    // partial blocks: at most MM_SPLIT_WGS blocks of one split launch
+    L.p_part = take(std::max((size_t)c->n_kv_heads * dm.n_chunks * P * G * (c->head_dim + 4) * 4,
+                             launch_mm_partial_floats(16, 256, MM_SPLIT_WGS) * 4));
   }
   L.total = off;
   return L;
@@ -788,8 +792,22 @@ int verify_impl(specdec_ctx* x, int B, int R, const int32_t* tokens, float* logi
   return SPECDEC_OK;
 }
 
-// The GEMM arguments of a prompt-chunk launch (launch_mm): the weights and the row count.
-GemmArgs mm_args(specdec_ctx* x, const Gemm& g, int M) {
+// Ways the reduction of a prompt GEMM is split.  A projection whose 256 x 256 blocks leave most
+// CUs idle takes up to MM_SPLIT_WGS workgroups, each at least 8 k-blocks of the reduction, with
+// the fp32 partials (4 bytes per split and output) at most the weight bytes.  Measured on MI355X
+// at the 31B shapes, 512 rows: o + down 500 -> 231 us per layer including the summing launches.
+// The q/k/v projection is not split: the summing launch's rotary + K/V append epilogue, on few
+// waves, took as long as the split saved.
+int mm_split(const Gemm& g, int M, int epi) {
+  const int blocks = cdiv(g.n_tiles, 16) * cdiv(M, 256);
+  if (epi == EPI_ROPE || blocks >= MM_SPLIT_WGS / 4) return 1;
+  const int kn = std::min({MM_SPLIT_WGS / blocks, g.nkb / 8, 16 * g.nkb / M});
+  return kn >= 2 ? kn : 1;
+}
+
+// The GEMM arguments of a prompt-chunk launch (launch_mm): the weights, the row count and the
+// split of the reduction (partials in the attention partials' buffer, free outside attention).
+GemmArgs mm_args(specdec_ctx* x, const Gemm& g, int M, int epi) {
   GemmArgs a;
   a.W = g.W;
   a.nkb = g.nkb;
@@ -797,6 +815,8 @@ GemmArgs mm_args(specdec_ctx* x, const Gemm& g, int M) {
   a.M = M;
   a.err = at<int>(x, x->lay.err);
   a.eps = x->cfg.rms_eps;
+  a.kpart_n = mm_split(g, M, epi);
+  if (a.kpart_n > 1) a.kpart = at<float>(x, x->lay.p_part);
   return a;
 }
 
@@ -822,7 +842,7 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
     void* kc = (char*)x->kv_k + (per_layer * l + seq) * 2;
     void* vc = (char*)x->kv_v + (per_layer * l + seq) * 2;
     {  // q/k/v projection + RoPE at positions len + row + K/V append
-      GemmArgs a = mm_args(x, x->g_qkv[l], T);
+      GemmArgs a = mm_args(x, x->g_qkv[l], T, EPI_ROPE);
       norm_input(a, XW, d, ssq, d);
       a.qout = x->ws + x->lay.p_q;
       a.kcache = kc;
@@ -861,21 +881,21 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
       HIP_TRY(launch_attention(DT_BF16, a, st));
     }
     {  // output projection + residual; leaves x * ffn_norm
-      GemmArgs a = mm_args(x, x->g_o[l], T);
+      GemmArgs a = mm_args(x, x->g_o[l], T, EPI_STORE);
       a.X = x->ws + x->lay.p_o;
       a.ldx = qd;
       resid_output(a, X, d, 1, ssq, XW, lw(l, SPECDEC_LW_FFN_NORM));
       HIP_TRY(launch_mm(EPI_STORE, a, st));
     }
     {  // gate/up + SiLU product
-      GemmArgs a = mm_args(x, x->g_gu[l], T);
+      GemmArgs a = mm_args(x, x->g_gu[l], T, EPI_SILU);
       norm_input(a, XW, d, ssq, d);
       a.hout = x->ws + x->lay.p_h;
       a.ldh = Fw;
       HIP_TRY(launch_mm(EPI_SILU, a, st));
     }
     {  // down projection + residual; leaves x * (next attention norm | final norm)
-      GemmArgs a = mm_args(x, x->g_down[l], T);
+      GemmArgs a = mm_args(x, x->g_down[l], T, EPI_STORE);
       a.X = x->ws + x->lay.p_h;
       a.ldx = Fw;
       const float* wn = l + 1 < c.n_layers ? lw(l + 1, SPECDEC_LW_ATTN_NORM) : x->w.final_norm;
@@ -884,7 +904,7 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
     }
   }
   {  // final norm + tied LM head: per-unit argmax partials (+ optional logits)
-    GemmArgs a = mm_args(x, x->g_head, T);
+    GemmArgs a = mm_args(x, x->g_head, T, EPI_ARGMAX);
     norm_input(a, XW, d, ssq, d);
     a.amax_val = at<float>(x, x->lay.p_amax_v);
     a.amax_idx = at<int>(x, x->lay.p_amax_i);

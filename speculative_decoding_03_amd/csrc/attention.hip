@@ -115,11 +115,8 @@ attn_kernel(AttnArgs a) {
   const int c16 = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
   const int Rall = a.R * G;
-  // query vectors [q_begin, q_end) of the group: all of them, or one block of q_block
-  const int nqb = a.q_block ? (Rall + a.q_block - 1) / a.q_block : 1;
-  const int b = blockIdx.z / nqb;
-  const int q_begin = a.q_block ? (blockIdx.z - b * nqb) * a.q_block : 0;
-  const int q_end = a.q_block ? min(Rall, q_begin + a.q_block) : Rall;
+  const int b = blockIdx.z;
+  const int q_begin = 0, q_end = Rall;  // every query vector of the group
   const float scale2 = a.scale * 1.44269504088896341f;  // softmax scale times log2 e
 
   // The committed length is requested first but waited for only after every cache and query
@@ -452,13 +449,218 @@ __global__ void __launch_bounds__(WAVE) attn_combine_kernel(AttnArgs a) {
   }
 }
 
+// Prompt attention: the rows of a prompt chunk of one sequence (causal, over the committed prefix
+// and the chunk), bf16.  A workgroup of NWQ waves takes 16 * NWQ consecutive query vectors of one
+// KV head (rows x the group's query heads) and walks every key any of them sees in steps of KS
+// keys.  Each step's K rows and V^T runs are copied from the cache into LDS in MFMA operand order
+// (a fragment = 64 lanes x 16 bytes, one run per thread and fragment, conflict-free), with the
+// values of keys past the block's last visible key zeroed as they are stored; every wave then
+// multiplies its 16 query vectors against the step on MFMA (S^T = K Q^T, O^T += V^T P^T with P^T
+// taken from the score registers, as in attn_kernel) under an online softmax: the running
+// maximum in base-2 units, and the sums rescaled by 2^(m_old - m_new) when it grows.  The output
+// is normalised and stored directly.  With n_chunks > 1 the keys are split into n_chunks ranges
+// of `chunk` keys (grid z): each workgroup leaves a chunk partial of its range in attn_kernel's
+// format and attn_combine_kernel merges the ranges.  Two LDS stages alternate; the next step's
+// loads are in flight while the current one is multiplied.
+template <int HD, int NWQ, int QT>
+__global__ void __launch_bounds__(NWQ * 64) attn_prompt_kernel(AttnArgs a) {
+  using T = bf16_t;
+  constexpr int KS = HD <= 128 ? 64 : 32;  // keys per step
+  constexpr int NB = KS / 32;              // 32-key blocks per step
+  constexpr int DS = HD / 32, DT = HD / 16;
+  constexpr int KFR = NB * 2 * DS, VFR = NB * DT;  // K and V^T fragments per step
+  constexpr int NTH = NWQ * 64;
+  constexpr int KR = KFR * 64 / NTH, VR = VFR * 64 / NTH;  // runs per thread and step
+  static_assert(HD % 32 == 0 && KFR * 64 % NTH == 0 && VFR * 64 % NTH == 0, "step layout");
+  __shared__ __align__(16) u32x4 sk[2][KFR * 64];
+  __shared__ __align__(16) u32x4 sv[2][VFR * 64];
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.y;
+  const int G = a.hq / a.hkv;
+  const int Rall = a.R * G;
+  const int v_blk = blockIdx.x * 16 * NWQ * QT;
+  const float scale2 = a.scale * 1.44269504088896341f;
+  const int len = a.len[0];
+  // keys [0, kend_blk) hold every key a row of the block sees
+  const int row_last = (min(v_blk + 16 * NWQ * QT, Rall) - 1) / G;
+  const int kend_blk = len + row_last + a.key_off;
+  if (kend_blk > a.max_ctx || len < 0) {
+    if (blockIdx.x == 0 && g == 0 && tid == 0) raise_error(a.err, ERRBIT_CAPACITY);
+    return;
+  }
+  // this workgroup's key range
+  const int kr0 = blockIdx.z * a.chunk;
+  const int kr1 = a.n_chunks > 1 ? min(kend_blk, kr0 + a.chunk) : kend_blk;
+  if (kr0 >= kend_blk) return;  // no row of the block sees the range (the combine reads none)
+  const int n_steps = (kr1 - kr0 + KS - 1) / KS;
+  const T* Kc = reinterpret_cast<const T*>(a.kcache) + (size_t)g * a.max_ctx * HD;
+  const T* Vt = reinterpret_cast<const T*>(a.vcache) + (size_t)g * HD * a.max_ctx;
+
+  // this wave's QT tiles of 16 query vectors (a vector past Rall loads a valid one; it is
+  // never stored)
+  int qv[QT], qrow[QT], kend[QT];  // kend: keys the lane's query vector of tile t sees
+  Frag<T> qf[QT][DS];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    qv[t] = v_blk + 16 * (w * QT + t) + c16;
+    const int qc = min(qv[t], Rall - 1);
+    qrow[t] = qc / G;
+    kend[t] = len + qrow[t] + a.key_off;
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)qrow[t] * a.hq + g * G + (qc - qrow[t] * G)) * HD;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) load_frag<T>(qf[t][ds], qp + ds * 32 + grp * 8);
+  }
+
+  // the thread's runs of a step: run i = tid + j * NTH is lane i % 64 of fragment i / 64
+  u32x4 rk[KR], rv[VR];
+  auto load_step = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const int i = tid + j * NTH, f = i / 64, ln = i % 64;
+      const int nb = f / (2 * DS), h = (f / DS) % 2, ds = f % DS;
+      const int lc = ln & 15, lg = ln >> 4;
+      const int key = min(k0 + nb * 32 + 8 * (lc >> 2) + 4 * h + (lc & 3), a.max_ctx - 1);
+      rk[j] = *reinterpret_cast<const u32x4*>(Kc + (size_t)key * HD + ds * 32 + lg * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < VR; ++j) {
+      const int i = tid + j * NTH, f = i / 64, ln = i % 64;
+      const int nb = f / DT, dt = f % DT;
+      const int lc = ln & 15, lg = ln >> 4;
+      const int kk = min(k0 + nb * 32 + lg * 8, a.max_ctx - 8);  // max_ctx is a multiple of 8
+      rv[j] = *reinterpret_cast<const u32x4*>(Vt + (size_t)(dt * 16 + lc) * a.max_ctx + kk);
+    }
+  };
+  auto store_step = [&](int buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < KR; ++j) sk[buf][tid + j * NTH] = rk[j];
+#pragma unroll
+    for (int j = 0; j < VR; ++j) {
+      const int i = tid + j * NTH, f = i / 64, ln = i % 64;
+      const int nb = f / DT;
+      Frag<T> fr;
+      fr.v = rv[j];
+      keep_first(fr, kend_blk - (k0 + nb * 32 + (ln >> 4) * 8));  // values past the block's keys
+      sv[buf][i] = fr.v;
+    }
+  };
+
+  float m_run[QT], l_lane[QT];
+  f32x4 o[QT][DT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    m_run[t] = -INFINITY;
+    l_lane[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto compute = [&](int buf, int k0) {
+    float sc[QT][NB][8];
+    float mb[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) mb[t] = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 acc[QT];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          Frag<T> kf;
+          kf.v = sk[buf][((nb * 2 + h) * DS + ds) * 64 + lane];
+#pragma unroll
+          for (int t = 0; t < QT; ++t) acc[t] = mma<T>(kf, qf[t][ds], acc[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int key = k0 + nb * 32 + 8 * grp + 4 * h + v;
+            const float val = key < kend[t] ? acc[t][v] * scale2 : -INFINITY;
+            sc[t][nb][4 * h + v] = val;
+            mb[t] = fmaxf(mb[t], val);
+          }
+      }
+    float ms[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const float mn = fmaxf(m_run[t], rows_max(mb[t]));
+      ms[t] = mn == -INFINITY ? 0.f : mn;
+      const float alpha = exp2_hw(m_run[t] - ms[t]);  // m_run = -inf: 0 (nothing summed yet)
+      l_lane[t] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+      m_run[t] = mn;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      Frag<T> pf[QT];
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          y[j] = exp2_hw(sc[t][nb][j] - ms[t]);
+          l_lane[t] += y[j];
+        }
+        to_frag<T>(pf[t], y);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        Frag<T> vf;
+        vf.v = sv[buf][(nb * DT + dt) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) o[t][dt] = mma<T>(vf, pf[t], o[t][dt]);
+      }
+    }
+  };
+
+  load_step(kr0);
+  for (int s = 0; s < n_steps; ++s) {
+    const int k0 = kr0 + s * KS;
+    store_step(s & 1, k0);
+    if (s + 1 < n_steps) load_step(k0 + KS);
+    __syncthreads();
+    compute(s & 1, k0);
+  }
+
+  // normalise and store: lane (grp, c16) holds head-dim elements dt*16 + 4*grp .. +3 of its vector
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const float lsum = rows_sum(l_lane[t]);
+    if (qv[t] >= Rall) continue;
+    if (a.n_chunks > 1) {  // the range's partial: unnormalised sums, then (max, sum) in fp32
+      float* row = a.part + ((size_t)g * a.n_chunks + blockIdx.z) * (size_t)Rall * (HD + 4) +
+                   (size_t)qv[t] * (HD + 4);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store_part_o<T>(row, dt * 16 + 4 * grp, o[t][dt]);
+      if (grp == 0) {
+        row[HD] = m_run[t];
+        row[HD + 1] = lsum;
+      }
+    } else {
+      const float inv = 1.0f / lsum;
+      T* out = reinterpret_cast<T*>(a.out) + (size_t)qrow[t] * a.hq * HD +
+               (size_t)(g * G + (qv[t] - qrow[t] * G)) * HD;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint2 pk = {f32x2_to_bf16x2(o[t][dt][0] * inv, o[t][dt][1] * inv),
+                          f32x2_to_bf16x2(o[t][dt][2] * inv, o[t][dt][3] * inv)};
+        *reinterpret_cast<uint2*>(out + dt * 16 + 4 * grp) = pk;
+      }
+    }
+  }
+}
+
 template <typename T, int HD>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   if (a.chunk != AttnShape<HD>::CH) return hipErrorInvalidValue;
   const int Rall = a.R * (a.hq / a.hkv);
-  const int nqb = a.q_block ? (Rall + a.q_block - 1) / a.q_block : 1;
-  if (a.q_block % 0x20 || (a.q_block && a.vis == VIS_TREE)) return hipErrorInvalidValue;
-  dim3 grid(a.n_launch, a.hkv, a.B * nqb), block(NWAVE * WAVE);
+  dim3 grid(a.n_launch, a.hkv, a.B), block(NWAVE * WAVE);
   if (a.vis == VIS_TREE) {
     if (!a.tree_mask) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_kernel<T, HD, true>), grid, block, 0, st, a);
@@ -492,6 +694,46 @@ bool attention_supported(int head_dim) {
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   if (a.n_chunks > 4096 || a.n_launch < 1 || a.n_launch > a.n_chunks) return hipErrorInvalidValue;
   return dtype == DT_BF16 ? launch_t<bf16_t>(a, st) : launch_t<float>(a, st);
+}
+
+// query tiles per wave (measured on MI355X, 31B and E2B prompts of 512 rows: two tiles, which
+// share each LDS fragment read but need 223 registers, are 4-6% slower than one)
+constexpr int PROMPT_QT = 1;
+template <int HD>
+hipError_t launch_prompt_hd(const AttnArgs& a, int nwq, hipStream_t st) {
+  constexpr int QT = PROMPT_QT;
+  const int Rall = a.R * (a.hq / a.hkv);
+  dim3 grid((Rall + 16 * nwq * QT - 1) / (16 * nwq * QT), a.hkv, a.n_chunks > 1 ? a.n_chunks : 1);
+  if (nwq == 4) hipLaunchKernelGGL((attn_prompt_kernel<HD, 4, QT>), grid, dim3(256), 0, st, a);
+  else if (nwq == 2) hipLaunchKernelGGL((attn_prompt_kernel<HD, 2, QT>), grid, dim3(128), 0, st, a);
+  else return hipErrorInvalidValue;
+  if (a.n_chunks > 1) {
+    dim3 cgrid(Rall, a.hkv, 1);
+    hipLaunchKernelGGL((attn_combine_kernel<bf16_t, HD>), cgrid, dim3(WAVE), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+int attention_prompt_nwq(int R, int hq, int hkv) {
+  // 4-wave workgroups (64 * QT query vectors sharing each K/V step) unless that leaves fewer
+  // than 256 workgroups (a single KV head), then 2-wave ones
+  return (R * (hq / hkv) + 64 * PROMPT_QT - 1) / (64 * PROMPT_QT) * hkv >= 256 ? 4 : 2;
+}
+
+int attention_prompt_block(int R, int hq, int hkv) {
+  return 16 * PROMPT_QT * attention_prompt_nwq(R, hq, hkv);
+}
+
+hipError_t launch_attention_prompt(const AttnArgs& a, hipStream_t st) {
+  if (a.B != 1 || a.vis != VIS_CAUSAL || a.R < 1 || a.hq % a.hkv) return hipErrorInvalidValue;
+  if (a.n_chunks > 1 && (!a.part || a.chunk % 64 || a.n_launch != a.n_chunks)) return hipErrorInvalidValue;
+  const int nwq = attention_prompt_nwq(a.R, a.hq, a.hkv);
+  switch (a.hd) {
+    case 64: return launch_prompt_hd<64>(a, nwq, st);
+    case 128: return launch_prompt_hd<128>(a, nwq, st);
+    case 256: return launch_prompt_hd<256>(a, nwq, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace specdec

@@ -163,9 +163,6 @@ struct AttnArgs {
   // node i sees its ancestors and itself, each at slot len + node index).
   int vis = 0;
   const uint64_t* tree_mask = nullptr;  // VIS_TREE: [R] device (launch_tree_desc)
-  // query vectors per workgroup (a multiple of 32; 0: all R * hq / hkv of a sequence in each);
-  // a prompt chunk's hundreds of rows spread over more workgroups
-  int q_block = 0;
 };
 enum { VIS_CAUSAL = 0, VIS_FLAT = 1, VIS_TREE = 2 };
 enum { POS_LINEAR = 0, POS_FLAT = 1, POS_TREE = 2 };
@@ -176,6 +173,15 @@ __host__ __device__ inline int attn_key_end(int vis, int len, int R, int key_off
 }
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+// The rows of a prompt chunk of one sequence (B = 1, VIS_CAUSAL, bf16, head size 64, 128 or
+// 256): every row's attention over the committed prefix and the chunk, written to out
+// (row-major).  n_chunks <= 1: each workgroup walks all keys of its query vectors; n_chunks > 1
+// (= n_launch): the keys split into ranges of `chunk` keys (a multiple of 64, chunk * n_chunks
+// covering every key a row sees), partials in part ([hkv][n_chunks][R*hq/hkv][hd + 4] floats)
+// merged by the combine.
+hipError_t launch_attention_prompt(const AttnArgs& a, hipStream_t st);
+int attention_prompt_nwq(int R, int hq, int hkv);    // waves per prompt-attention workgroup
+int attention_prompt_block(int R, int hq, int hkv);  // query vectors per workgroup
 int attention_chunk(int head_dim);          // keys per chunk (fixed per head size)
 bool attention_supported(int head_dim);     // head sizes the attention kernel is built for
 

@@ -31,6 +31,10 @@ constexpr int TARGET_WAVES = 2048;   // waves per projection launch
 constexpr int MIN_KB_PER_WAVE = 8;   // k-blocks each wave streams at least
 constexpr int WIDE_NU = 8;            // tiles per gated unit in calls of 17..32 rows
 constexpr int MM_SPLIT_WGS = 240;     // workgroups of a prompt GEMM whose reduction is split
+// prompt attention: workgroups the key ranges aim at, and the most ranges (measured on MI355X,
+// 512-row prompts: 512 workgroups are 4% slower at the 31B shape, 2048 and 8 ranges no faster)
+constexpr int PROMPT_ATTN_WGS = 1024;
+constexpr int PROMPT_MAX_RANGES = 4;
 constexpr int WIDE_MIN_UNITS = 400;   // ... when that leaves at least this many units
 // 4-bit weights carry 3.6x fewer bytes per k-block: each wave streams at least 16 (measured on
 // MI355X at the 31B shapes: 16 beats 8 and 32; wide gated projections split at most 4 ways)
@@ -226,6 +230,8 @@ bool valid_config(const specdec_config* c) {
     if (c->dtype != SPECDEC_BF16 || c->weight_format != SPECDEC_WF_DENSE || c->n_experts > 0)
       return false;
     if (c->d_model % 64 || qd % 64 || c->ffn_dim % 64) return false;
+    // the prompt attention's head sizes
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return false;
   }
   if (c->kv_src_layer >= c->n_layers) return false;
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return false;
@@ -295,7 +301,6 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
   L.e_usage = take((size_t)c->n_layers * 4);  // experts routed to, summed per layer (measurement)
   const size_t P = (size_t)c->max_prefill;
   if (P > 0) {
-    const int G = c->n_q_heads / c->n_kv_heads;
     L.p_x = take(P * d * 4);
     L.p_xw = take(P * d * 2);
     L.p_ssq = take(P * (d / 16) * 4);
@@ -304,10 +309,11 @@ Layout make_layout(const specdec_config* c, const Dims& dm) {
     L.p_h = take(P * c->ffn_dim * 2);
     L.p_amax_v = take(P * dm.parts * 4);
     L.p_amax_i = take(P * dm.parts * 4);
-    // the chunk attention's partials, and (at other times of the layer) the prompt GEMM's split
-    // partial blocks: at most MM_SPLIT_WGS blocks of one split launch
-    L.p_part = take(std::max((size_t)c->n_kv_heads * dm.n_chunks * P * G * (c->head_dim + 4) * 4,
-                             launch_mm_partial_floats(16, 256, MM_SPLIT_WGS) * 4));
+    // the prompt GEMM's split partial blocks (at most MM_SPLIT_WGS blocks of one split launch)
+    // and, at other times of the layer, the prompt attention's key-range partials
+    const size_t G = (size_t)(c->n_q_heads / c->n_kv_heads);
+    L.p_part = take(std::max(launch_mm_partial_floats(16, 256, MM_SPLIT_WGS) * 4,
+                             (size_t)c->n_kv_heads * PROMPT_MAX_RANGES * P * G * (c->head_dim + 4) * 4));
   }
   L.total = off;
   return L;
@@ -837,7 +843,6 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
                        lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st));
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
   const size_t seq = (size_t)b * c.n_kv_heads * c.max_ctx * c.head_dim;  // sequence b's cache
-  const int n_launch = std::min(x->dm.n_chunks, cdiv(x->len_hi[b] + T, x->dm.chunk));
   for (int l = 0; l < c.n_layers; ++l) {
     void* kc = (char*)x->kv_k + (per_layer * l + seq) * 2;
     void* vc = (char*)x->kv_v + (per_layer * l + seq) * 2;
@@ -863,7 +868,6 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
       a.len = len;
       a.out = x->ws + x->lay.p_o;
       a.out_qx = 0;
-      a.part = at<float>(x, x->lay.p_part);
       a.err = err;
       a.B = 1;
       a.R = T;
@@ -872,13 +876,18 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
       a.hkv = c.n_kv_heads;
       a.hd = c.head_dim;
       a.max_ctx = c.max_ctx;
-      a.chunk = x->dm.chunk;
-      a.n_chunks = x->dm.n_chunks;
-      a.n_launch = n_launch;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
       a.vis = VIS_CAUSAL;
-      a.q_block = 128;
-      HIP_TRY(launch_attention(DT_BF16, a, st));
+      // split the keys into ranges (merged by the combine) when the query-vector blocks alone
+      // leave the CUs with few waves: about PROMPT_ATTN_WGS workgroups in all
+      const int G = c.n_q_heads / c.n_kv_heads;
+      const int blocks = cdiv(T * G, attention_prompt_block(T, c.n_q_heads, c.n_kv_heads)) * c.n_kv_heads;
+      const int kend = x->len_hi[b] + T;  // bound on the keys any row sees
+      const int ranges = std::max(1, std::min(PROMPT_MAX_RANGES, PROMPT_ATTN_WGS / blocks));
+      a.chunk = cdiv(cdiv(kend, ranges), 64) * 64;
+      a.n_chunks = a.n_launch = cdiv(kend, a.chunk);
+      if (a.n_chunks > 1) a.part = at<float>(x, x->lay.p_part);
+      HIP_TRY(launch_attention_prompt(a, st));
     }
     {  // output projection + residual; leaves x * ffn_norm
       GemmArgs a = mm_args(x, x->g_o[l], T, EPI_STORE);

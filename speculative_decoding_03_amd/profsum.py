@@ -187,6 +187,7 @@ def cmd_prefill(a) -> int:
         "mm_kernel<0,": ("o + down (residual add)", 2.0 * T * L * (qd * d + F * d)),
         "mm_kernel<2,": ("gate/up + SiLU product", 2.0 * T * L * d * 2 * F),
         "mm_kernel<3,": ("tied LM head + argmax", 2.0 * T * d * cfg.vocab),
+        "attn_prompt_kernel": ("causal prompt attention", 4.0 * L * cfg.n_q_heads * cfg.head_dim * keys),
         "attn_kernel": ("causal chunk attention", 4.0 * L * cfg.n_q_heads * cfg.head_dim * keys),
     }
     rows = trace_rows(a.dir)
@@ -203,7 +204,7 @@ def cmd_prefill(a) -> int:
         agg[k][0] += 1
         agg[k][1] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     span = (int(rows[e]["End_Timestamp"]) - int(rows[s]["Start_Timestamp"])) * 1e-9
-    total = sum(f for _, f in flops.values())
+    total = sum(f for k, (_, f) in flops.items() if k != "attn_kernel")  # attention once
     peak = a.peak_tflops
     lines = [f"## {a.config}: {T} tokens at position {cfg.ctx}", "", f"command: {a.cmd}", "",
              f"last call: span {span * 1e6:.1f} us, {total / 1e12:.2f} TFLOP of GEMM and attention "

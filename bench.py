@@ -207,6 +207,8 @@ def main() -> int:
                     help="weights: bf16, or every matrix in 4-bit blocks with an fp16 step per 32")
     ap.add_argument("--no-q4-leg", dest="q4_leg", action="store_false",
                     help="skip the 4-bit-weight run of the same workload (a child process)")
+    ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
+                    help="skip the streaming-read ceiling measured beside the roofline")
     ap.add_argument("--prefill-tokens", type=int, default=512,
                     help="prompt chunk of the prefill leg (0: none; dense bf16 models only)")
     ap.add_argument("--prefill-only", action="store_true",
@@ -746,6 +748,19 @@ def main() -> int:
             "launch_timing": f"HIP events attached to the dispatches; the gate/up launches of {P} "
                              f"speculative steps run after the timed region",
         }
+    if gate_ms and args.ceiling:
+        # a plain streaming read of the dominant launch's bytes beside its roofline: the bandwidth
+        # a weight stream of that size reaches on this GPU with no arithmetic at all
+        from workloads import device as WD
+        ceil = WD.stream_read_ceiling(int(res["roofline"]["algorithmic_bytes_per_launch"]))
+        best = max(ceil.values(), key=lambda r: r["gbs"])
+        res["streaming_ceiling"] = {
+            "what": "non-temporal 16-byte loads, one contiguous run per wave, 8 in flight per lane, "
+                    "over the dominant launch's bytes; by workgroups of 8 waves",
+            "by_workgroups": ceil, "best_gbs": best["gbs"],
+            "best_frac_of_peak": round(best["gbs"] / HBM_PEAK_GBS, 4),
+            "roofline_achieved_over_best": round(res["roofline"]["achieved"] / best["gbs"], 4)}
+        log(f"streaming ceiling: {best['gbs']} GB/s ({res['streaming_ceiling']['best_frac_of_peak']} of peak)")
     if PT:
         res["prefill"] = prefill_leg()
         log(f"prefill: {PT} tokens in {res['prefill']['ms']} ms, {res['prefill']['tflops']} TFLOP/s")
@@ -768,7 +783,7 @@ def q4_leg(args) -> dict:
     cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config, "--batch",
            str(args.batch), "--wformat", "q4", "--steps", str(min(args.steps, 100)), "--warmup",
            str(args.warmup), "--head", args.head, "--k-c", str(args.k_c), "--no-cpu-baseline",
-           "--no-p-sweep", "--no-tree", "--no-adaptive", "--no-graph", "--no-q4-leg"]
+           "--no-p-sweep", "--no-tree", "--no-adaptive", "--no-graph", "--no-q4-leg", "--no-ceiling"]
     if args.p is not None:
         cmd += ["--p", str(args.p)]
     log("4-bit weight leg: " + " ".join(cmd[2:]))

@@ -82,6 +82,26 @@ __global__ void fill_kv(void* dst, int L, int Bl, int Bc, int Hkv, int ctx, int 
   }
 }
 
+// Streaming-read ceiling (a measurement, not part of the method): n_wg workgroups of 8 waves read
+// a buffer once, each wave a contiguous run of per_wave16 16-byte units with non-temporal loads,
+// 8 in flight per lane (the access pattern of a weight stream).  The loaded words are folded into
+// one value that is stored only if it equals a constant, so the reads are not removed.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(512) stream_read(const u32x4_t* __restrict__ p, int64_t per_wave16,
+                                                   unsigned* sink) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const u32x4_t* base = p + ((int64_t)blockIdx.x * 8 + w) * per_wave16;
+  unsigned acc = 0;
+  for (int64_t i = 0; i + 64 * 8 <= per_wave16; i += 64 * 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(base + i + j * 64 + lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 int grid_for(int64_t n) {
   const int64_t b = (n + 255) / 256;
   return (int)(b < 65536 ? (b > 0 ? b : 1) : 65536);
@@ -118,6 +138,14 @@ int synth_fill_kv(void* dst, int L, int Bl, int Bc, int Hkv, int ctx, int max_ct
   if (n == 0) return 0;
   hipLaunchKernelGGL(fill_kv, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream, dst, L, Bl,
                      Bc, Hkv, ctx, max_ctx, hd, bf16, key, scale, transposed);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// Reads n_wg * 8 * per_wave16 16-byte units of src (per_wave16 a multiple of 512).
+int synth_stream_read(const void* src, int64_t per_wave16, int n_wg, void* sink, void* stream) {
+  if (!src || !sink || n_wg < 1 || per_wave16 < 512 || per_wave16 % 512) return -1;
+  hipLaunchKernelGGL(stream_read, dim3(n_wg), dim3(512), 0, (hipStream_t)stream,
+                     (const u32x4_t*)src, per_wave16, (unsigned*)sink);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

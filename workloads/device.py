@@ -54,8 +54,44 @@ def synth_lib():
         lib.synth_fill_kv.restype = C.c_int
         lib.synth_fill_kv.argtypes = [C.c_void_p] + [C.c_int] * 8 + [C.c_uint64, C.c_float, C.c_int,
                                                                       C.c_void_p]
+        lib.synth_stream_read.restype = C.c_int
+        lib.synth_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
         _synth = lib
     return _synth
+
+
+def stream_read_ceiling(nbytes: int, n_wgs=(160, 256, 1600), reps: int = 7) -> dict:
+    """Read bandwidth of a plain streaming kernel (non-temporal 16-byte loads, one contiguous run
+    per wave, 8 loads in flight per lane) over a buffer of about nbytes, for a few workgroup
+    counts: the ceiling a weight-streaming GEMM of that size can reach.  Median of reps timed
+    launches each, a 1 GiB read of another buffer between them (so nothing is served from the
+    caches)."""
+    dev = torch.device("cuda")
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    flush = torch.ones((1 << 30) // 2, dtype=torch.bfloat16, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    lib, st = synth_lib(), _stream()
+    out = {}
+    for nwg in n_wgs:
+        per = (nbytes // 16) // (nwg * 8) // 512 * 512
+        fper = ((1 << 30) // 16) // (2048 * 8) // 512 * 512
+        ms = []
+        for _ in range(reps):
+            if lib.synth_stream_read(C.c_void_p(flush.data_ptr()), fper, 2048, C.c_void_p(sink.data_ptr()), st):
+                raise RuntimeError("synth_stream_read failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if lib.synth_stream_read(C.c_void_p(buf.data_ptr()), per, nwg, C.c_void_p(sink.data_ptr()), st):
+                raise RuntimeError("synth_stream_read failed")
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        b = per * 16 * nwg * 8
+        out[str(nwg)] = {"bytes": b, "us": round(ms[len(ms) // 2] * 1e3, 2),
+                         "gbs": round(b / (ms[len(ms) // 2] * 1e-3) / 1e9, 1)}
+    del buf, flush
+    return out
 
 
 def _stream():

@@ -35,6 +35,7 @@ constexpr int MM_SPLIT_WGS = 240;     // workgroups of a prompt GEMM whose reduc
 // 512-row prompts: 512 workgroups are 4% slower at the 31B shape, 2048 and 8 ranges no faster)
 constexpr int PROMPT_ATTN_WGS = 1024;
 constexpr int PROMPT_MAX_RANGES = 4;
+constexpr int PROMPT_SPLIT_KEYS = 1024;
 constexpr int WIDE_MIN_UNITS = 400;   // ... when that leaves at least this many units
 // 4-bit weights carry 3.6x fewer bytes per k-block: each wave streams at least 16 (measured on
 // MI355X at the 31B shapes: 16 beats 8 and 32; wide gated projections split at most 4 ways)
@@ -879,11 +880,13 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
       a.vis = VIS_CAUSAL;
       // split the keys into ranges (merged by the combine) when the query-vector blocks alone
-      // leave the CUs with few waves: about PROMPT_ATTN_WGS workgroups in all
+      // leave the CUs with few waves: about PROMPT_ATTN_WGS workgroups in all; fewer than
+      // PROMPT_SPLIT_KEYS keys are walked whole
       const int G = c.n_q_heads / c.n_kv_heads;
       const int blocks = cdiv(T * G, attention_prompt_block(T, c.n_q_heads, c.n_kv_heads)) * c.n_kv_heads;
       const int kend = x->len_hi[b] + T;  // bound on the keys any row sees
-      const int ranges = std::max(1, std::min(PROMPT_MAX_RANGES, PROMPT_ATTN_WGS / blocks));
+      const int ranges = kend < PROMPT_SPLIT_KEYS
+                             ? 1 : std::max(1, std::min(PROMPT_MAX_RANGES, PROMPT_ATTN_WGS / blocks));
       a.chunk = cdiv(cdiv(kend, ranges), 64) * 64;
       a.n_chunks = a.n_launch = cdiv(kend, a.chunk);
       if (a.n_chunks > 1) a.part = at<float>(x, x->lay.p_part);

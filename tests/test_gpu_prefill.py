@@ -8,7 +8,9 @@ positions:
   hidden state against the oracle; the logits over the whole vocabulary of sampled rows against
   the oracle; every row's argmax against the GPU's own logits; the argmax of sampled rows under
   the margin rule;
-* ragged chunks (1, 100 and 300 rows, in calls that follow each other);
+* ragged chunks (1, 100 and 300 rows, in calls that follow each other; under 1024 keys the prompt
+  attention walks every key in one workgroup, the 512-row chunk above splits them into ranges
+  merged by the combine);
 * greedy decoding through the verify path after the prefill, teacher-forced against the oracle
   continuing from the same cache (the hand-over of length, hidden state and cache);
 * the host-side errors (chunk too long, capacity, no prefill configured).

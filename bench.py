@@ -210,7 +210,7 @@ def main() -> int:
     ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
                     help="skip the streaming-read ceiling measured beside the roofline")
     ap.add_argument("--prefill-tokens", type=int, default=512,
-                    help="prompt chunk of the prefill leg (0: none; dense bf16 models only)")
+                    help="prompt chunk of the prefill leg (0: none; models without experts)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling it)")
     args = ap.parse_args()
@@ -253,7 +253,7 @@ def main() -> int:
     # verify rows per sequence: a linear step (K + 1, up to KA + 1 in the adaptive leg) or a tree
     # of up to 3 branches (1 + 3K), within the 64 rows of a call
     max_rows = min(64 // B, max(16 // B, KA + 1, 1 + 3 * K))
-    PT = args.prefill_tokens if (not cfg.is_moe and args.wformat == "dense") else 0
+    PT = args.prefill_tokens if not cfg.is_moe else 0
     max_ctx = max(max_ctx, (cfg.ctx + PT + 7) // 8 * 8)
     eng = E.Engine(model, max_batch=B, max_draft=KA, max_rows=max_rows, max_ctx=max_ctx,
                    max_prefill=PT)
@@ -796,7 +796,7 @@ def q4_leg(args) -> dict:
         return {"error": f"unreadable output: {e}"}
     keep = ("value", "unit", "steps", "ms_per_step", "verify_ms", "decode_ms", "draft_ms",
             "verify_over_decode", "verify_hbm_gbs", "verify_hbm_frac", "verify_bytes",
-            "tokens_per_step", "spec_equals_greedy", "roofline")
+            "tokens_per_step", "spec_equals_greedy", "roofline", "prefill")
     out = {k: d[k] for k in keep if k in d}
     out["weights"] = "4-bit blocks: codes plus an fp16 step per 32 weights (0.5625 bytes/weight)"
     return out

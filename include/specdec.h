@@ -87,9 +87,10 @@ typedef struct {
                                specdec_pack_q4; needs dtype BF16 and every reduction width
                                (d_model, Hq*hd, the FFN widths, d_dim, d_ffn) % 128 == 0 */
   int32_t max_prefill;      /* rows of the largest specdec_prefill call, 0..1024 (0: none).  Above
-                               0 it needs dtype BF16, dense weights, no experts, d_model,
-                               Hq*hd, ffn_dim % 64 == 0 and hd in {64, 128, 256}; the workspace
-                               grows by the chunk's activations and 60 MiB of GEMM partials */
+                               0 it needs dtype BF16, no experts, d_model, Hq*hd, ffn_dim % 64
+                               == 0 and hd in {64, 128, 256}; the workspace grows by the chunk's
+                               activations and 60 MiB of GEMM partials.  With 4-bit weights the
+                               prompt GEMM rounds each weight d * (q - 8) to bf16 */
 } specdec_config;
 
 /* Per-layer tensor slots of specdec_weights.layers (n_layers * SPECDEC_N_LAYER_TENSORS). */

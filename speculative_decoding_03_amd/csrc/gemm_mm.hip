@@ -31,7 +31,19 @@ __device__ __forceinline__ size_t mm_part_offset(int z, int nblk, int blk, int n
   return (((size_t)z * nblk + blk) * nw + w) * (16 * 64 * 4);
 }
 
-template <int EPI, int WM, int WN, int KS, int D, bool SPLIT>
+// One lane's weight fragment (8 consecutive k of one row) of a 4-bit block matrix as bf16: the
+// lane's code word c (element e at bit (e % 2) * 16 + (e / 2) * 4) and the block's fp16 step h;
+// each weight d * (q - 8) is exact in fp32 and rounded to bf16 (nearest even) for the MFMA.
+__device__ __forceinline__ u32x4 q4_fragment_bf16(uint32_t c, uint32_t h) {
+  const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  const float o = -8.0f * d;
+  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;  // bytes e0 e4 e1 e5 / e2 e6 e3 e7
+  auto w = [&](uint32_t x, int byte) { return __builtin_fmaf(d, (float)((x >> (8 * byte)) & 0xFFu), o); };
+  return u32x4{f32x2_to_bf16x2(w(lo, 0), w(lo, 2)), f32x2_to_bf16x2(w(hi, 0), w(hi, 2)),
+               f32x2_to_bf16x2(w(lo, 1), w(lo, 3)), f32x2_to_bf16x2(w(hi, 1), w(hi, 3))};
+}
+
+template <int EPI, int WM, int WN, int KS, int D, bool SPLIT, bool Q4W = false>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4 > 2 ? WM * WN / 4 : 2))) mm_kernel(GemmArgs a) {
   constexpr int MM_KS = KS;               // k-blocks per LDS stage
   constexpr int NTH = WM * WN * 64;
@@ -77,13 +89,21 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
     adst[j] = fr * 64 + ln;
   }
   const bf16_t* wsrc[B_RUNS];
+  const uint8_t* qsrc[B_RUNS];  // 4-bit weights: the run's code word in its tile's first block
   int bdst[B_RUNS];
 #pragma unroll
   for (int j = 0; j < B_RUNS; ++j) {
     const int i = tid + j * NTH;
     const int fr = i / 64, ln = i % 64;
     const int kb = fr % MM_KS, t = fr / MM_KS;
-    wsrc[j] = W + ((size_t)min(t_blk + t, a.n_tiles - 1) * nkb + kb) * TILE_ELEMS + ln * LANE_ELEMS;
+    const size_t tt = (size_t)min(t_blk + t, a.n_tiles - 1);
+    if constexpr (Q4W) {
+      qsrc[j] = reinterpret_cast<const uint8_t*>(a.W) + tt * (size_t)(nkb >> 2) * Q4_BLOCK_BYTES + ln * 16;
+      wsrc[j] = nullptr;
+    } else {
+      wsrc[j] = W + (tt * nkb + kb) * TILE_ELEMS + ln * LANE_ELEMS;
+      qsrc[j] = nullptr;
+    }
     bdst[j] = (kb * BNT + t) * 64 + ln;
   }
   f32x4 acc[4][4];
@@ -94,20 +114,35 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
 
   // D stages in flight in a register ring (slot = stage % D); a stage past the last one reads the
   // last one again and is never stored
-  u32x4 ra[D][A_RUNS], rb[D][B_RUNS];
+  u32x4 ra[D][A_RUNS], rb[D][Q4W ? 1 : B_RUNS];
+  uint32_t rq[D][Q4W ? B_RUNS : 1], rh[D][Q4W ? B_RUNS : 1];  // 4-bit: code word and step
   auto load_stage = [&](int slot, int st) {
     const int s = st0 + min(st, n_st - 1);
 #pragma unroll
     for (int j = 0; j < A_RUNS; ++j) ra[slot][j] = *reinterpret_cast<const u32x4*>(xsrc[j] + s * MM_KS * TILE_K);
 #pragma unroll
-    for (int j = 0; j < B_RUNS; ++j)
-      rb[slot][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)s * MM_KS * TILE_ELEMS));
+    for (int j = 0; j < B_RUNS; ++j) {
+      if constexpr (Q4W) {
+        // k-block kbg of the stage: word kbg % 4 of the lane's 16 bytes in block kbg / 4, and
+        // the step of the lane's row there
+        const int i = tid + j * NTH, ln = i % 64;
+        const int kbg = s * MM_KS + (i / 64) % MM_KS;
+        const uint8_t* blk = qsrc[j] - ln * 16 + (size_t)(kbg >> 2) * Q4_BLOCK_BYTES;
+        rq[slot][j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(blk + ln * 16 + (kbg & 3) * 4));
+        rh[slot][j] = *reinterpret_cast<const uint16_t*>(blk + Q4_CODE_BYTES + (ln & 15) * 8 + (kbg & 3) * 2);
+      } else {
+        rb[slot][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[j] + (size_t)s * MM_KS * TILE_ELEMS));
+      }
+    }
   };
   auto store_stage = [&](int slot, int buf) {
 #pragma unroll
     for (int j = 0; j < A_RUNS; ++j) sa[buf][adst[j]] = ra[slot][j];
 #pragma unroll
-    for (int j = 0; j < B_RUNS; ++j) sb[buf][bdst[j]] = rb[slot][j];
+    for (int j = 0; j < B_RUNS; ++j) {
+      if constexpr (Q4W) sb[buf][bdst[j]] = q4_fragment_bf16(rq[slot][j], rh[slot][j]);
+      else sb[buf][bdst[j]] = rb[slot][j];
+    }
   };
   auto compute = [&](int buf) {
 #pragma unroll
@@ -248,7 +283,7 @@ __device__ void mm_finish(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int til
   }
 }
 
-template <int EPI, int WM, int WN, int KS = 2, int D = 1>
+template <int EPI, int WM, int WN, int KS = 2, int D = 1, bool Q4W = false>
 hipError_t launch_mm_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   if (a.nkb % KS) return hipErrorInvalidValue;
   dim3 grid((a.n_tiles + 4 * WN - 1) / (4 * WN), (a.M + 64 * WM - 1) / (64 * WM)), block(WM * WN * 64);
@@ -256,7 +291,7 @@ hipError_t launch_mm_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm
     if (a.kpart_n > 1) {
       // the reduction split over kpart_n workgroups per block, partials summed by a second launch
       dim3 sgrid(grid.x, grid.y, a.kpart_n), rgrid(grid.x, grid.y, WM * WN / 4);
-      hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, true>), sgrid, block, 0, st, a);
+      hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, true, Q4W>), sgrid, block, 0, st, a);
       if (tm)
         hipExtLaunchKernelGGL((mm_reduce_kernel<EPI, WM, WN>), rgrid, dim3(256), 0, st, tm->start,
                               tm->stop, 0, a);
@@ -267,9 +302,9 @@ hipError_t launch_mm_t(const GemmArgs& a, hipStream_t st, const LaunchTiming* tm
   }
   if (a.kpart_n > 1) return hipErrorInvalidValue;
   if (tm)
-    hipExtLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, false>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+    hipExtLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, false, Q4W>), grid, block, 0, st, tm->start, tm->stop, 0, a);
   else
-    hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((mm_kernel<EPI, WM, WN, KS, D, false, Q4W>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -280,19 +315,18 @@ size_t launch_mm_partial_floats(int n_tiles, int M, int kpart_n) {
   return kpart_n > 1 ? (size_t)kpart_n * ((n_tiles + 15) / 16) * ((M + 255) / 256) * 16 * 16 * 64 * 4 : 0;
 }
 
-hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
-  using namespace gemm_detail;
-  if (a.M <= 0 || a.n_tiles <= 0) return hipSuccess;
-  if (a.nkb % 2 || a.wq4) return hipErrorInvalidValue;
+namespace gemm_detail {
+template <bool Q4W>
+hipError_t launch_mm_w(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
   if (a.kpart_n > 1) {
     // a projection too narrow for 256 x 256 blocks to fill the CUs: the same blocks with the
     // reduction split kpart_n ways (at least one stage each), partials summed by a second launch
     if (!a.kpart || a.kpart_n > a.nkb / 2) return hipErrorInvalidValue;
     switch (epi) {
-      case EPI_STORE: return launch_mm_t<EPI_STORE, 4, 4>(a, st, tm);
-      case EPI_ROPE: return launch_mm_t<EPI_ROPE, 4, 4>(a, st, tm);
-      case EPI_SILU: return launch_mm_t<EPI_SILU, 4, 4>(a, st, tm);
-      case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 4, 4>(a, st, tm);
+      case EPI_STORE: return launch_mm_t<EPI_STORE, 4, 4, 2, 1, Q4W>(a, st, tm);
+      case EPI_ROPE: return launch_mm_t<EPI_ROPE, 4, 4, 2, 1, Q4W>(a, st, tm);
+      case EPI_SILU: return launch_mm_t<EPI_SILU, 4, 4, 2, 1, Q4W>(a, st, tm);
+      case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 4, 4, 2, 1, Q4W>(a, st, tm);
       default: return hipErrorInvalidValue;
     }
   }
@@ -304,16 +338,26 @@ hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTim
   const bool narrow = blocks < 256;
   switch (epi) {
     case EPI_STORE:
-      return narrow ? launch_mm_t<EPI_STORE, 1, 2>(a, st, tm) : launch_mm_t<EPI_STORE, 2, 2>(a, st, tm);
+      return narrow ? launch_mm_t<EPI_STORE, 1, 2, 2, 1, Q4W>(a, st, tm)
+                    : launch_mm_t<EPI_STORE, 2, 2, 2, 1, Q4W>(a, st, tm);
     case EPI_ROPE:
-      return narrow ? launch_mm_t<EPI_ROPE, 1, 2>(a, st, tm) : launch_mm_t<EPI_ROPE, 2, 2>(a, st, tm);
+      return narrow ? launch_mm_t<EPI_ROPE, 1, 2, 2, 1, Q4W>(a, st, tm)
+                    : launch_mm_t<EPI_ROPE, 2, 2, 2, 1, Q4W>(a, st, tm);
     // the wide projections (gate/up, LM head): 256 x 256 blocks of 16 waves, half the LDS and L2
     // bytes per product of 128 x 128 blocks (31B, 512 rows: prefill 303 -> 374 TFLOP/s; a
     // register ring of 2 to 4 stages in flight instead of one gained nothing)
-    case EPI_SILU: return launch_mm_t<EPI_SILU, 4, 4>(a, st, tm);
-    case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 4, 4>(a, st, tm);
+    case EPI_SILU: return launch_mm_t<EPI_SILU, 4, 4, 2, 1, Q4W>(a, st, tm);
+    case EPI_ARGMAX: return launch_mm_t<EPI_ARGMAX, 4, 4, 2, 1, Q4W>(a, st, tm);
     default: return hipErrorInvalidValue;
   }
+}
+}  // namespace gemm_detail
+
+hipError_t launch_mm(int epi, const GemmArgs& a, hipStream_t st, const LaunchTiming* tm) {
+  using namespace gemm_detail;
+  if (a.M <= 0 || a.n_tiles <= 0) return hipSuccess;
+  if (a.nkb % 2 || (a.wq4 && a.nkb % 4)) return hipErrorInvalidValue;
+  return a.wq4 ? launch_mm_w<true>(epi, a, st, tm) : launch_mm_w<false>(epi, a, st, tm);
 }
 
 }  // namespace specdec

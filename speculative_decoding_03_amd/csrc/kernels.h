@@ -119,7 +119,8 @@ struct LaunchTiming {
 hipError_t launch_gemm(int dtype, int MT, int NU, int epi, const GemmArgs& a, hipStream_t st,
                        const LaunchTiming* tm = nullptr);
 
-// Compute-bound GEMM of a prompt chunk (gemm_mm.hip): bf16 weights in the packed tile layout,
+// Compute-bound GEMM of a prompt chunk (gemm_mm.hip): bf16 weights in the packed tile layout
+// (or, with wq4, 4-bit blocks expanded to bf16 as they are staged; nkb % 4 == 0),
 // row-major bf16 X of a.M rows (any count), nkb % 2 == 0; epilogues EPI_STORE, EPI_ROPE (one
 // sequence: rows at positions len[0] + pos_off + row), EPI_SILU and EPI_ARGMAX (units of 64
 // columns, slot row * ld_amax + unit) as in launch_gemm.  The unit fields (nu, n_units, KW, NW,

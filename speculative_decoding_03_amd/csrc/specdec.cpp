@@ -228,8 +228,7 @@ bool valid_config(const specdec_config* c) {
   if (c->max_prefill > 0) {
     // the prompt GEMM: bf16 weights of a dense model, reduction widths in stages of 64
     const int qd = c->n_q_heads * c->head_dim;
-    if (c->dtype != SPECDEC_BF16 || c->weight_format != SPECDEC_WF_DENSE || c->n_experts > 0)
-      return false;
+    if (c->dtype != SPECDEC_BF16 || c->n_experts > 0) return false;
     if (c->d_model % 64 || qd % 64 || c->ffn_dim % 64) return false;
     // the prompt attention's head sizes
     if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return false;
@@ -822,6 +821,7 @@ GemmArgs mm_args(specdec_ctx* x, const Gemm& g, int M, int epi) {
   a.M = M;
   a.err = at<int>(x, x->lay.err);
   a.eps = x->cfg.rms_eps;
+  a.wq4 = x->cfg.weight_format == SPECDEC_WF_Q4;
   a.kpart_n = mm_split(g, M, epi);
   if (a.kpart_n > 1) a.kpart = at<float>(x, x->lay.p_part);
   return a;
@@ -841,7 +841,8 @@ int prefill_impl(specdec_ctx* x, int b, int T, const int32_t* tokens, float* log
   int* len = x->len + b;
   auto lw = [&](int l, int slot) { return (const float*)x->lw[(size_t)l * SPECDEC_N_LAYER_TENSORS + slot]; };
   HIP_TRY(launch_embed(DT_BF16, x->w.embed, x->g_head.nkb, d, tokens, T, X, ssq, XW, 0,
-                       lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st));
+                       lw(0, SPECDEC_LW_ATTN_NORM), c.vocab, err, st,
+                       c.weight_format == SPECDEC_WF_Q4));
   const size_t per_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_ctx * c.head_dim;
   const size_t seq = (size_t)b * c.n_kv_heads * c.max_ctx * c.head_dim;  // sequence b's cache
   for (int l = 0; l < c.n_layers; ++l) {

@@ -71,9 +71,10 @@ def test_workspace_sizing_and_config_checks(lib):
     bad += [dict(weight_format=2), dict(weight_format=F.WF_Q4),
             dict(weight_format=F.WF_Q4, dtype=F.BF16, d_dim=96),
             dict(weight_format=F.WF_Q4, dtype=F.BF16, d_model=288)]
-    # the prompt GEMM needs bf16, dense weights and no experts; at most 1024 rows
+    # the prompt GEMM needs bf16 and no experts, the prompt attention a head size of 64, 128 or
+    # 256; at most 1024 rows
     bad += [dict(max_prefill=64), dict(max_prefill=-1), dict(max_prefill=1025, dtype=F.BF16),
-            dict(max_prefill=64, dtype=F.BF16, weight_format=F.WF_Q4),
+            dict(max_prefill=64, dtype=F.BF16, head_dim=176),
             dict(max_prefill=64, dtype=F.BF16, n_experts=16, top_k=4, expert_ffn=128,
                  shared_ffn=256, ffn_dim=0)]
     for kw in bad:
@@ -81,6 +82,10 @@ def test_workspace_sizing_and_config_checks(lib):
     assert lib.specdec_workspace_bytes(C.byref(_config(weight_format=F.WF_Q4, dtype=F.BF16))) > 0
     bf = lib.specdec_workspace_bytes(C.byref(_config(dtype=F.BF16)))
     assert lib.specdec_workspace_bytes(C.byref(_config(dtype=F.BF16, max_prefill=512))) > bf
+    # 4-bit weights prefill too (the prompt GEMM expands their blocks to bf16)
+    q4 = lib.specdec_workspace_bytes(C.byref(_config(dtype=F.BF16, weight_format=F.WF_Q4)))
+    assert lib.specdec_workspace_bytes(C.byref(_config(dtype=F.BF16, weight_format=F.WF_Q4,
+                                                       max_prefill=512))) > q4
     # the 4-bit block format's size: n*kd/2 code bytes plus an fp16 step per 32 weights
     assert lib.specdec_q4_bytes(16, 128) == 1152
     assert lib.specdec_q4_bytes(5120, 25600) == 5120 * 25600 * 9 // 16

@@ -14,7 +14,9 @@ positions:
 * greedy decoding through the verify path after the prefill, teacher-forced against the oracle
   continuing from the same cache (the hand-over of length, hidden state and cache);
 * the host-side errors (chunk too long, capacity, no prefill configured).
-The 31B-class width runs one 256-row chunk (40 query heads over 8 KV heads of 128).
+The 31B-class width runs one 256-row chunk (40 query heads over 8 KV heads of 128).  The 512-row
+and the 256-row chunks also run with every matrix in 4-bit blocks (the prompt GEMM rounds each
+weight d * (q - 8) to bf16; the oracle takes the exact weights).
 Tolerances are the bf16 path's: relative error 2e-2, margin 0.05."""
 
 import numpy as np
@@ -83,8 +85,9 @@ def argmax_is_first_max(lg: torch.Tensor, am: torch.Tensor) -> bool:
     return not bool(lower_equal.any())
 
 
-def test_prefill_512_rows_at_e2b_width():
-    cfg = truncated("e2b", 1, ctx=530, norm_jitter=0.1, d_layers=2)
+@pytest.mark.parametrize("wformat", ["dense", "q4"])
+def test_prefill_512_rows_at_e2b_width(wformat):
+    cfg = truncated("e2b", 1, ctx=530, norm_jitter=0.1, d_layers=2, weight_format=wformat)
     T = 512
     eng, W, cache, _ = setup(cfg, T)
     try:
@@ -160,8 +163,9 @@ def test_ragged_chunks_and_greedy_after_prefill():
         eng.close()
 
 
-def test_prefill_31b_width_256_rows():
-    cfg = truncated("31b", 1, ctx=700, norm_jitter=0.1, d_layers=2)
+@pytest.mark.parametrize("wformat", ["dense", "q4"])
+def test_prefill_31b_width_256_rows(wformat):
+    cfg = truncated("31b", 1, ctx=700, norm_jitter=0.1, d_layers=2, weight_format=wformat)
     T = 256
     eng, W, cache, _ = setup(cfg, T)
     try:

@@ -2,9 +2,11 @@
 // the new rows, full over the committed prefix) and for the drafter's cross-attention into the
 // target's cache (keys [0, len), no cache of its own).
 //
-// Split over keys (flash-decoding): grid (chunk, kv head, sequence); a workgroup of four waves
-// takes one chunk of CH keys, each wave a contiguous quarter, and serves every query vector
-// that reads that KV head (all rows x the group's query heads).  K is stored [pos][hd] and V
+// Split over keys (flash-decoding): grid (chunk, kv head, sequence x query tiles); a workgroup of
+// NW waves (four, or two for models with few KV heads) takes one chunk of CH = 32 NW keys, each wave
+// a contiguous 32-key block, and serves every query vector that reads that KV head (all rows x the
+// group's query heads), or one 16-vector tile of them when the call splits its tiles over
+// workgroups.  K is stored [pos][hd] and V
 // transposed [hd][pos], so both MFMA operands stream as 16-byte loads.  Per chunk the kernel
 // leaves (row max in base-2 units, sum of exponentials, unnormalised value sum); attn_combine
 // merges the chunks in chunk order.  The value sums are kept in the storage type (bf16 rounds
@@ -23,13 +25,11 @@ namespace specdec {
 
 namespace {
 
-constexpr int NWAVE = 4;
-
 // Keys per wave: one 32-key block (measured on MI355X at the 31B shape: more workgroups and
 // two waves per SIMD beat two blocks per wave at one wave per SIMD).
-template <int HD> struct AttnShape {
+template <int HD, int NW> struct AttnShape {
   static constexpr int KPW = 32;  // keys per wave (one block: registers for 2 waves per SIMD)
-  static constexpr int CH = KPW * NWAVE;            // keys per workgroup = one partial
+  static constexpr int CH = KPW * NW;               // keys per workgroup = one partial
   static constexpr int NB = KPW / 32;               // 32-key blocks per wave
   static constexpr int DS = (HD + 31) / 32;         // 32-wide head-dim steps (scores)
   static constexpr int DT = HD / 16;                // 16-row head-dim tiles (value sum)
@@ -100,23 +100,26 @@ __device__ __forceinline__ void store_part_o(float* row, int d0, const f32x4& y)
 //   exponentials; lanes combined by a fixed butterfly);
 //   O^T = V^T P^T on MFMA with P^T taken straight from the score registers (bf16) and V^T read
 //   from the transposed cache as 16-byte runs of the same eight keys.
-// The four waves then merge through LDS (common max, rescale, sum in wave order), each wave
-// writing a quarter of the chunk's partial (o, m, l).  Exponentials are 2^x on the hardware
+// The NW waves then merge through LDS (common max, rescale, sum in wave order), each wave
+// writing 1/NW of the chunk's partial (o, m, l).  Exponentials are 2^x on the hardware
 // instruction, with scores scaled by scale * log2 e.  Keys that no row may see are never loaded.
-template <typename T, int HD, bool TREE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_occupancy<T, HD>())))
+template <typename T, int HD, int NW, bool TREE>
+__global__ void __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(attn_occupancy<T, HD>())))
 attn_kernel(AttnArgs a) {
-  using SH = AttnShape<HD>;
+  using SH = AttnShape<HD, NW>;
   constexpr int NB = SH::NB, DS = SH::DS, DT = SH::DT, KPW = SH::KPW, CH = SH::CH;
-  __shared__ __align__(16) float xch[NWAVE][16][SH::PST];
-  __shared__ float mw[NWAVE][16], lw[NWAVE][16];
+  __shared__ __align__(16) float xch[NW][16][SH::PST];
+  __shared__ float mw[NW][16], lw[NW][16];
   const int chunk = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
   const int Rall = a.R * G;
-  const int b = blockIdx.z;
-  const int q_begin = 0, q_end = Rall;  // every query vector of the group
+  // query vectors [q_begin, q_end) of the group: all of them, or tile blockIdx.z % nqt
+  const int nqt = a.q_split ? (Rall + 15) / 16 : 1;
+  const int b = blockIdx.z / nqt;
+  const int q_begin = (blockIdx.z - b * nqt) * 16;
+  const int q_end = a.q_split ? min(Rall, q_begin + 16) : Rall;
   const float scale2 = a.scale * 1.44269504088896341f;  // softmax scale times log2 e
 
   // The committed length is requested first but waited for only after every cache and query
@@ -271,9 +274,9 @@ attn_kernel(AttnArgs a) {
       o[dt] = acc;
     }
 
-    // ---- merge the four waves: common max, rescale, sum in wave order ----
+    // ---- merge the NW waves: common max, rescale, sum in wave order ----
     // Every wave parks its statistics and unscaled sums in LDS; after one barrier wave w
-    // rescales and adds up head-dim tiles w, w+4, ... over the four waves (in wave order) and
+    // rescales and adds up head-dim tiles w, w+NW, ... over the NW waves (in wave order) and
     // writes them to the partial.
     if (grp == 0) {
       mw[w][c16] = m;
@@ -282,27 +285,27 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(&xch[w][c16][dt * 16 + 4 * grp]) = o[dt];
     __syncthreads();
-    float mu[NWAVE], fu[NWAVE];
+    float mu[NW], fu[NW];
 #pragma unroll
-    for (int u = 0; u < NWAVE; ++u) mu[u] = mw[u][c16];
+    for (int u = 0; u < NW; ++u) mu[u] = mw[u][c16];
     float M = mu[0];
 #pragma unroll
-    for (int u = 1; u < NWAVE; ++u) M = fmaxf(M, mu[u]);
+    for (int u = 1; u < NW; ++u) M = fmaxf(M, mu[u]);
     const float Ms = M == -INFINITY ? 0.f : M;
 #pragma unroll
-    for (int u = 0; u < NWAVE; ++u) fu[u] = exp2_hw(mu[u] - Ms);  // 0 for a wave with no key
+    for (int u = 0; u < NW; ++u) fu[u] = exp2_hw(mu[u] - Ms);  // 0 for a wave with no key
 #pragma unroll
-    for (int dt = w; dt < DT; dt += NWAVE) {
+    for (int dt = w; dt < DT; dt += NW) {
       f32x4 y = *reinterpret_cast<const f32x4*>(&xch[0][c16][dt * 16 + 4 * grp]) * fu[0];
 #pragma unroll
-      for (int u = 1; u < NWAVE; ++u)
+      for (int u = 1; u < NW; ++u)
         y += *reinterpret_cast<const f32x4*>(&xch[u][c16][dt * 16 + 4 * grp]) * fu[u];
       if (qv < Rall) store_part_o<T>(pbase + (size_t)qv * SH::PST, dt * 16 + 4 * grp, y);
     }
     if (w == 0 && grp == 0 && qv < Rall) {
       float L = 0.f;
 #pragma unroll
-      for (int u = 0; u < NWAVE; ++u) L += lw[u][c16] * fu[u];
+      for (int u = 0; u < NW; ++u) L += lw[u][c16] * fu[u];
       pbase[(size_t)qv * SH::PST + HD] = M;
       pbase[(size_t)qv * SH::PST + HD + 1] = L;
     }
@@ -656,17 +659,23 @@ __global__ void __launch_bounds__(NWQ * 64) attn_prompt_kernel(AttnArgs a) {
   }
 }
 
+template <typename T, int HD, int NW>
+void launch_nw(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  if (a.vis == VIS_TREE)
+    hipLaunchKernelGGL((attn_kernel<T, HD, NW, true>), grid, dim3(NW * WAVE), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, HD, NW, false>), grid, dim3(NW * WAVE), 0, st, a);
+}
+
 template <typename T, int HD>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
-  if (a.chunk != AttnShape<HD>::CH) return hipErrorInvalidValue;
+  if (a.vis == VIS_TREE && !a.tree_mask) return hipErrorInvalidValue;
   const int Rall = a.R * (a.hq / a.hkv);
-  dim3 grid(a.n_launch, a.hkv, a.B), block(NWAVE * WAVE);
-  if (a.vis == VIS_TREE) {
-    if (!a.tree_mask) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_kernel<T, HD, true>), grid, block, 0, st, a);
-  } else {
-    hipLaunchKernelGGL((attn_kernel<T, HD, false>), grid, block, 0, st, a);
-  }
+  const int nqt = a.q_split ? (Rall + 15) / 16 : 1;
+  dim3 grid(a.n_launch, a.hkv, a.B * nqt);
+  if (a.chunk == AttnShape<HD, 4>::CH) launch_nw<T, HD, 4>(a, grid, st);
+  else if (a.chunk == AttnShape<HD, 2>::CH) launch_nw<T, HD, 2>(a, grid, st);
+  else return hipErrorInvalidValue;
   dim3 cgrid(Rall, a.hkv, a.B), cblock(WAVE);
   hipLaunchKernelGGL((attn_combine_kernel<T, HD>), cgrid, cblock, 0, st, a);
   return hipGetLastError();
@@ -685,7 +694,21 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int attention_chunk(int head_dim) { return head_dim <= 128 ? AttnShape<128>::CH : AttnShape<256>::CH; }
+int attention_chunk(int n_kv_heads, int max_ctx) {
+  // 64-key chunks (two-wave workgroups) when 128-key ones give fewer than 64 workgroups even at the
+  // longest context.  Measured on MI355X (attention + combine, one sequence): a single KV head of
+  // 256 at 2K context, 4 rows 14.4 -> 11.9 us and 1 row 11.3 -> 9.6 us; two KV heads at 4K no
+  // change; four KV heads of 176 at 4K and eight of 128 at 8K 1.5-2.3 us slower.
+  return n_kv_heads * ((max_ctx + 127) / 128) < 64 ? AttnShape<128, 2>::CH : AttnShape<128, 4>::CH;
+}
+
+bool attention_q_split(int n_launch, int hkv, int B, int R, int G) {
+  // one query tile per workgroup when a launch has more than one tile and fewer than 128
+  // workgroups.  Measured on MI355X: 4-5 rows x 8 query heads of a single KV head at 2K context
+  // (33 workgroups) 11.9 -> 10.0 us, two KV heads at 4K (66) 14.3 -> 12.2 us; with 132 or more
+  // workgroups (four KV heads at 4K, eight at 8K) it is 0.6-2 us slower.
+  return R * G > 16 && n_launch * hkv * B < 128;
+}
 
 bool attention_supported(int head_dim) {
   return head_dim == 64 || head_dim == 128 || head_dim == 176 || head_dim == 256;

@@ -164,6 +164,9 @@ struct AttnArgs {
   // node i sees its ancestors and itself, each at slot len + node index).
   int vis = 0;
   const uint64_t* tree_mask = nullptr;  // VIS_TREE: [R] device (launch_tree_desc)
+  // 1: each workgroup takes one 16-vector tile of the query vectors instead of all of them (more
+  // workgroups for launches that would not fill the chip; every vector's arithmetic is unchanged)
+  int q_split = 0;
 };
 enum { VIS_CAUSAL = 0, VIS_FLAT = 1, VIS_TREE = 2 };
 enum { POS_LINEAR = 0, POS_FLAT = 1, POS_TREE = 2 };
@@ -183,7 +186,10 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attention_prompt(const AttnArgs& a, hipStream_t st);
 int attention_prompt_nwq(int R, int hq, int hkv);    // waves per prompt-attention workgroup
 int attention_prompt_block(int R, int hq, int hkv);  // query vectors per workgroup
-int attention_chunk(int head_dim);          // keys per chunk (fixed per head size)
+int attention_chunk(int n_kv_heads, int max_ctx);  // keys per chunk (fixed per model and context)
+// whether a launch of n_launch chunks x hkv heads x B sequences of R rows x G query heads splits
+// its query tiles over workgroups (AttnArgs::q_split)
+bool attention_q_split(int n_launch, int hkv, int B, int R, int G);
 bool attention_supported(int head_dim);     // head sizes the attention kernel is built for
 
 // Misc kernels (misc.hip).

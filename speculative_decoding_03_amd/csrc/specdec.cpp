@@ -223,7 +223,7 @@ bool valid_config(const specdec_config* c) {
   if (c->max_batch * c->max_rows > 64) return false;
   if (c->max_draft < 1 || c->max_draft + 1 > c->max_rows) return false;
   if (c->max_ctx < c->max_rows + 1 || c->max_ctx > (1 << 20) || c->max_ctx % 8) return false;
-  if (c->max_ctx / attention_chunk(c->head_dim) > 4096) return false;
+  if (c->max_ctx / attention_chunk(c->n_kv_heads, c->max_ctx) > 4096) return false;
   if (c->max_prefill < 0 || c->max_prefill > 1024) return false;
   if (c->max_prefill > 0) {
     // the prompt GEMM: bf16 weights of a dense model, reduction widths in stages of 64
@@ -243,7 +243,7 @@ Dims make_dims(const specdec_config* c) {
   d.Bx = c->max_batch;
   d.Mx = c->max_batch * c->max_rows;
   d.Rall_max = c->max_rows * (c->n_q_heads / c->n_kv_heads);
-  d.chunk = attention_chunk(c->head_dim);
+  d.chunk = attention_chunk(c->n_kv_heads, c->max_ctx);
   d.n_chunks = cdiv(c->max_ctx, d.chunk);
   d.esz = c->dtype == SPECDEC_BF16 ? 2 : 4;
   d.parts = c->vocab / 64;
@@ -571,6 +571,7 @@ int attention(specdec_ctx* x, int layer, int B, int R, int key_off, int cls, hip
                                                          x->dm.chunk)));
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
   a.vis = vis;
+  a.q_split = attention_q_split(a.n_launch, a.hkv, B, R, c.n_q_heads / c.n_kv_heads);
   if (tree) a.tree_mask = at<uint64_t>(x, x->lay.tree_mask);
   ProfScope ps(x, cls, st);
   HIP_TRY(launch_attention(dt_of(x), a, st));

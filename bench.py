@@ -748,11 +748,13 @@ def main() -> int:
             "launch_timing": f"HIP events attached to the dispatches; the gate/up launches of {P} "
                              f"speculative steps run after the timed region",
         }
+    ceil = {}
     if gate_ms and args.ceiling:
         # a plain streaming read of the dominant launch's bytes beside its roofline: the bandwidth
         # a weight stream of that size reaches on this GPU with no arithmetic at all
         from workloads import device as WD
         ceil = WD.stream_read_ceiling(int(res["roofline"]["algorithmic_bytes_per_launch"]))
+    if ceil:
         best = max(ceil.values(), key=lambda r: r["gbs"])
         res["streaming_ceiling"] = {
             "what": "non-temporal 16-byte loads, one contiguous run per wave, 8 in flight per lane, "

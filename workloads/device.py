@@ -63,7 +63,8 @@ def synth_lib():
 def stream_read_ceiling(nbytes: int, n_wgs=(160, 256, 1600), reps: int = 7) -> dict:
     """Read bandwidth of a plain streaming kernel (non-temporal 16-byte loads, one contiguous run
     per wave, 8 loads in flight per lane) over a buffer of about nbytes, for a few workgroup
-    counts: the ceiling a weight-streaming GEMM of that size can reach.  Median of reps timed
+    counts (those that give every wave at least 512 loads): the ceiling a weight-streaming GEMM
+    of that size can reach.  Median of reps timed
     launches each, a 1 GiB read of another buffer between them (so nothing is served from the
     caches)."""
     dev = torch.device("cuda")
@@ -74,6 +75,8 @@ def stream_read_ceiling(nbytes: int, n_wgs=(160, 256, 1600), reps: int = 7) -> d
     out = {}
     for nwg in n_wgs:
         per = (nbytes // 16) // (nwg * 8) // 512 * 512
+        if per < 512:  # under one 512-load granule per wave: too many workgroups for the size
+            continue
         fper = ((1 << 30) // 16) // (2048 * 8) // 512 * 512
         ms = []
         for _ in range(reps):

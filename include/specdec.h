@@ -379,8 +379,8 @@ int specdec_query_split(specdec_ctx* ctx, int32_t kernel_class, int32_t* splits,
                         int32_t* waves, int32_t* groups);
 
 /* The same for a call of `rows` rows in all (1 <= rows <= max_batch * max_rows), which may take
-   wider work units than the context's default; also returns the 16-column tiles per unit.  A
-   unit's split-K never depends on `rows`.  Errors: SPECDEC_E_INVAL for a bad class, row count or
+   wider work units than the context's default (one per workgroup); also returns the 16-column
+   tiles per unit.  A unit's split-K never depends on `rows`.  Errors: SPECDEC_E_INVAL for a bad class, row count or
    null pointer. */
 int specdec_query_launch(specdec_ctx* ctx, int32_t kernel_class, int32_t rows, int32_t* splits,
                          int32_t* tiles_per_unit, int32_t* units, int32_t* waves, int32_t* groups);

@@ -1009,8 +1009,10 @@ hipError_t dispatch_epi(int NU, int epi, const GemmArgs& a, hipStream_t st,
   if (epi == EPI_ROPE && NU == 2) return launch_nw<T, MT, 2, EPI_ROPE, Q4>(a, st, tm);
   if (epi == EPI_SILU && NU == 2) return launch_nw<T, MT, 2, EPI_SILU, Q4>(a, st, tm);
   // gated units of four gate/up pairs: bf16 calls of 17..32 rows
-  if constexpr (MT == 2 && !Q4 && sizeof(T) == 2)
+  if constexpr (MT == 2 && !Q4 && sizeof(T) == 2) {
     if (epi == EPI_SILU && NU == 8) return launch_nw<T, MT, 8, EPI_SILU, Q4>(a, st, tm);
+    if (epi == EPI_SILU && NU == 4) return launch_nw<T, MT, 4, EPI_SILU, Q4>(a, st, tm);
+  }
   if (epi == EPI_SILU_G && NU == 2) return launch_nw<T, MT, 2, EPI_SILU_G, Q4>(a, st, tm);
   if (epi == EPI_STORE_G && NU == 1) return launch_nw<T, MT, 1, EPI_STORE_G, Q4>(a, st, tm);
   if (epi == EPI_ARGMAX && NU == 4) return launch_nw<T, MT, 4, EPI_ARGMAX, Q4>(a, st, tm);

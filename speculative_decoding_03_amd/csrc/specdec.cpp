@@ -41,6 +41,7 @@ constexpr int PROMPT_ATTN_WGS = 1024;
 constexpr int PROMPT_MAX_RANGES = 4;
 constexpr int PROMPT_SPLIT_KEYS = 1024;
 constexpr int WIDE_MIN_UNITS = 400;   // ... when that leaves at least this many units
+constexpr int WIDE4_MIN_UNITS = 128;  // else units of four tiles when that leaves this many
 // 4-bit weights carry 3.6x fewer bytes per k-block: each wave streams at least 16 (measured on
 // MI355X at the 31B shapes: 16 beats 8 and 32; wide gated projections split at most 4 ways)
 constexpr int MIN_KB_PER_WAVE_Q4 = 16;
@@ -111,6 +112,8 @@ Gemm make_gemm(const void* W, int N, int Kd, int NU, bool q4, bool allow_split =
   g.kbps = round_up4(cdiv(g.nkb, g.KW));
   if (gated && !q4 && NU == 2 && g.n_tiles % WIDE_NU == 0 && g.n_tiles / WIDE_NU >= WIDE_MIN_UNITS)
     g.nu_wide = WIDE_NU;
+  else if (gated && !q4 && NU == 2 && g.n_tiles % 4 == 0 && g.n_tiles / 4 >= WIDE4_MIN_UNITS)
+    g.nu_wide = 4;
   return g;
 }
 
@@ -121,12 +124,15 @@ int mt_for(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 // as many bytes as the unit's two weight tiles.  A wide gated projection then takes units of
 // WIDE_NU tiles (four gate/up pairs), which share each activation load over four times the
 // weight bytes.  The split-K stays the same, so each column's sum is formed in the same order
-// as in any other call.  Measured on MI355X at the 31B gate/up shape, 32 rows: 154 -> 123 us;
-// at 16 rows and fewer, and with fewer than WIDE_MIN_UNITS units, the two-tile units are faster.
+// as in any other call, and each workgroup takes one unit.  Measured on MI355X at 32 rows: the
+// 31B gate/up 154 -> 123 us (units of four tiles: 128 us); the MoE shared FFN's gate/up (704
+// tiles, too few for 8-tile units) with 4-tile units 27.6 -> 24.1 us (35.7 us with two units per
+// 8-wave workgroup).  At 16 rows and fewer the two-tile units are faster.
 void wide_units(GemmArgs& a, const Gemm& g, int M) {
   if (g.nu_wide && mt_for(M) == 2) {
     a.nu = g.nu_wide;
     a.n_units = g.n_tiles / g.nu_wide;
+    a.NW = std::max(4, g.KW);
   }
 }
 
@@ -1405,10 +1411,12 @@ int specdec_query_launch(specdec_ctx* x, int32_t cls, int32_t rows, int32_t* spl
   GemmArgs a;
   a.nu = g->NU;
   a.n_units = g->n_units;
+  a.NW = g->NW;
   if (cls == 0) wide_units(a, *g, rows);
   *tiles_per_unit = a.nu;
   *units = a.n_units;
-  *groups = cdiv(a.n_units, g->NW / g->KW);
+  *waves = a.NW;
+  *groups = cdiv(a.n_units, a.NW / g->KW);
   return SPECDEC_OK;
 }
 

@@ -153,18 +153,27 @@ def test_batched_spec_equals_batched_greedy(bcase):
 
 
 def test_gated_units_of_the_batched_call(bcase):
-    """A call of 17..32 rows of the wide dense gate/up projection (31B width) takes units of four
-    gate/up pairs (so the verify test above runs them); calls of 16 rows or fewer, 4-bit weights
-    and the narrower shared FFN of the mixture-of-experts model keep units of one pair.  The
-    split-K is the same for every call size."""
+    """A call of 17..32 rows of a dense gate/up projection takes wider units, one per workgroup:
+    four gate/up pairs at the 31B width (3200 tiles), two for the narrower shared FFN of the
+    mixture-of-experts model (704 tiles), so the verify tests above run both; calls of 16 rows or
+    fewer and 4-bit weights keep units of one pair.  The split-K is the same for every call
+    size."""
     cfg, eng = bcase["cfg"], bcase["eng"]
     M = cfg.batch * (cfg.draft_k + 1)
     kw, nu, units, nw, groups = eng.query_launch(0, M)
     kw1, nu1, units1, nw1, groups1 = eng.query_launch(0, cfg.batch)
     assert kw == kw1 and nu1 == 2
-    wide = 16 < M <= 32 and cfg.weight_format == "dense" and not cfg.is_moe
-    assert nu == (8 if wide else 2)
+    tiles = 2 * (cfg.shared_ffn if cfg.is_moe else cfg.ffn_dim) // 16
+    wide = 16 < M <= 32 and cfg.weight_format == "dense"
+    expect = 2
+    if wide and tiles % 8 == 0 and tiles // 8 >= 400:
+        expect = 8
+    elif wide and tiles % 4 == 0 and tiles // 4 >= 128:
+        expect = 4
+    assert nu == expect
     assert units * nu == units1 * nu1 and groups == units * kw // nw
+    if expect > 2:
+        assert nw == max(4, kw)  # one unit per workgroup
 
 
 @pytest.mark.parametrize("wformat", ["dense", "q4"])

@@ -32,6 +32,7 @@ WORKLOAD_TEXT = {
     "31b": "31B-class dense: 64 layers, d 5120, 40 q / 8 kv heads of 128, gated FFN 25600, vocab 262144, bf16 random-init (30.5B params, tied head); drafter 4 layers x 256 over the 5120-d backbone state, 2048 centroids x 128 tokens; ctx 8192, K=3, drafts injected at p=0.7",
     "e2b": "E2B-shaped: 24 layers, d 1536, 8 q / 1 kv heads of 256, gated FFN 6144, vocab 262144, bf16; drafter 4 x 256, 2048 centroids x 128; ctx 2048, K=3, p=0.7",
     "e4b": "E4B-shaped: 34 layers, d 2560, 8 q / 2 kv heads of 256, gated FFN 10240, vocab 262144, bf16; drafter 4 x 256, 2048 centroids; ctx 4096, K=4, p=0.7",
+    "31b-tp8": "one GPU's share of the 31B-class model under 8-way tensor parallelism (no collectives): 64 layers, d 5120, 5 q / 1 kv head of 128, gated FFN 3200 (q/k/v 896x5120, o 5120x640, gate/up 6400x5120, down 5120x3200), vocabulary slice 32768 (LM head 32768x5120), bf16; drafter 4 x 256 over the slice, 512 centroids x 64 tokens; ctx 8192, K=3, p=0.7",
     "moe": "26B-class MoE: 30 layers, d 2816, 16 q / 4 kv heads of 176, 128 experts top-8 of FFN 1408 + shared FFN 5632, vocab 262144, bf16 (48.45B params as listed); drafter 4 x 256, 2048 centroids; ctx 4096, K=3, p=0.7",
 }
 
@@ -169,10 +170,17 @@ def cpu_baseline(cfg, tokens_per_step: float, K: int, B: int) -> dict:
     t_draft = time.perf_counter() - t
     step_s = t_layers + t_head + t_draft
     timed = t_layers + t_head_slice + t_draft
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": round(B * tokens_per_step / (B * step_s), 4),
         "unit": "tokens/s",
         "cores": int(cores),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": (f"float64 numpy oracle on {int(cores)} threads, one sequence: the {K + 1} verify "
                    f"rows through all {cfg.n_layers} layers at full width over the {ctx}-position "

@@ -133,6 +133,14 @@ PRESETS = {
     "31b": ModelConfig(
         name="31b", n_layers=64, d_model=5120, n_q_heads=40, n_kv_heads=8, head_dim=128,
         ffn_dim=25600, vocab=262144, seed=3, ctx=8192, draft_k=3, kv_seed=103),
+    # One GPU's share of the 31B-class model under 8-way tensor parallelism: q/k/v and gate/up
+    # split by output columns (5 of 40 query heads, 1 of 8 KV heads, 3200 of 25600 FFN columns),
+    # o and down by input rows (the residual stream keeps its full width), the tied LM head by
+    # vocabulary (32768 of 262144 rows).  The drafter covers the same vocabulary slice with 512
+    # centroids of 64 tokens (the sharded design replicates the full drafter instead).
+    "31b-tp8": ModelConfig(
+        name="31b-tp8", n_layers=64, d_model=5120, n_q_heads=5, n_kv_heads=1, head_dim=128,
+        ffn_dim=3200, vocab=32768, n_centroids=512, seed=5, ctx=8192, draft_k=3, kv_seed=105),
     # 26B-class MoE
     "moe": ModelConfig(
         name="moe", n_layers=30, d_model=2816, n_q_heads=16, n_kv_heads=4, head_dim=176,

@@ -101,9 +101,13 @@ __global__ void __launch_bounds__(1024) accept_kernel(
   __shared__ float rv[RG][NWV];
   __shared__ int ri[RG][NWV];
   __shared__ int G[64];
+  __shared__ int T[64];
   __shared__ int m_sh;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x >> 6;
+  // the verify rows' tokens, requested with the first partials so that the acceptance scan
+  // below reads them from LDS instead of one dependent memory round trip per accepted draft
+  const int tok = tokens && (int)threadIdx.x < R ? tokens[b * R + threadIdx.x] : 0;
   for (int i0 = 0; i0 < R; i0 += RG) {
     float v[RG];
     int idx[RG];
@@ -163,14 +167,16 @@ __global__ void __launch_bounds__(1024) accept_kernel(
     }
     __syncthreads();
   }
+  if ((int)threadIdx.x < R) T[threadIdx.x] = tok;
+  __syncthreads();
   if (threadIdx.x == 0) {
     const int K = R - 1;
     int m = 0;
     if (tokens) {
-      while (m < K && tokens[b * R + m + 1] == G[m]) ++m;
+      while (m < K && T[m + 1] == G[m]) ++m;
     }
     if (out_tokens) {
-      for (int j = 0; j < m; ++j) out_tokens[b * R + j] = tokens[b * R + j + 1];
+      for (int j = 0; j < m; ++j) out_tokens[b * R + j] = T[j + 1];
       out_tokens[b * R + m] = G[m];
       for (int j = m + 1; j < R; ++j) out_tokens[b * R + j] = -1;
     }
@@ -874,6 +880,7 @@ hipError_t launch_accept(const float* amax_val, const int* amax_idx, int n_parts
                          int B, int R, const int* tokens, int* out_tokens, int* n_emit,
                          int* next_tok, int commit, int* len, float* hid, const float* X, int d,
                          int* argmax_out, int* err, hipStream_t st) {
+  if (R < 1 || R > 64) return hipErrorInvalidValue;  // the kernel's row arrays hold 64
   hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(1024), 0, st, amax_val, amax_idx, n_parts,
                      ld_amax, R, tokens, out_tokens, n_emit, next_tok, commit, len, hid, X, d,
                      argmax_out, err);

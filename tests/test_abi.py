@@ -9,6 +9,7 @@ import re
 import pytest
 
 from speculative_decoding_03_amd import _ffi as F
+from workloads import PRESETS, preset
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "specdec.h")
@@ -94,6 +95,25 @@ def test_workspace_sizing_and_config_checks(lib):
     # a mixture-of-experts configuration is valid and needs its routing buffers
     moe = _config(n_experts=16, top_k=4, expert_ffn=128, shared_ffn=256, ffn_dim=0)
     assert lib.specdec_workspace_bytes(C.byref(moe)) > 0
+
+
+@pytest.mark.parametrize("name", sorted(PRESETS))
+def test_every_workload_preset_is_a_valid_configuration(lib, name):
+    """Each workload, set up as the benchmark sets it up (batch 1, up to 6 drafts, 16 rows, its
+    context plus headroom, a 512-row prefill for dense bf16 models), in dense and, for bf16
+    models, 4-bit weights, passes the library's configuration check."""
+    m = preset(name)
+    shape = {k: int(getattr(m, k)) for k in (
+        "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
+        "n_experts", "top_k", "expert_ffn", "shared_ffn", "d_layers", "d_dim", "d_ffn",
+        "n_centroids", "kv_src_layer")}
+    bf16 = m.dtype == "bf16"
+    ctx = (max(m.ctx, m.prompt_len) + 64 + 512 + 7) // 8 * 8
+    for wf in ((F.WF_DENSE, F.WF_Q4) if bf16 else (F.WF_DENSE,)):
+        cfg = _config(**shape, dtype=F.BF16 if bf16 else F.F32, weight_format=wf, max_batch=1,
+                      max_draft=6, max_rows=16, max_ctx=ctx,
+                      max_prefill=512 if bf16 and not m.is_moe else 0)
+        assert lib.specdec_workspace_bytes(C.byref(cfg)) > 0, (name, wf)
 
 
 def test_error_strings(lib):

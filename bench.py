@@ -138,7 +138,7 @@ def cpu_baseline(cfg, tokens_per_step: float, K: int, B: int) -> dict:
     for g in range(cfg.n_kv_heads):
         Kl[g, :ctx] = S.kv_rows(cfg, "k", 0, 0, g, 0, ctx)
         Vl[g, :ctx] = S.kv_rows(cfg, "v", 0, 0, g, 0, ctx)
-    slice_rows = 32768
+    slice_rows = min(32768, cfg.vocab)
     E_slice = S.gen_rows(cfg, "embed", 0, cfg.d_model, 0, slice_rows).astype(np.float64)
     fnorm = S.norm_weight(cfg, "final_norm", 0, cfg.d_model).astype(np.float64)
     hid, t0 = S.state_init(cfg)
@@ -182,13 +182,14 @@ def cpu_baseline(cfg, tokens_per_step: float, K: int, B: int) -> dict:
         "cores": int(cores),
         "cpu_model": cpu_model,
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle on {int(cores)} threads, one sequence: the {K + 1} verify "
+        "sample": (f"float64 numpy oracle on {int(cores)} thread{'s' if int(cores) != 1 else ''}, "
+                   f"one sequence: the {K + 1} verify "
                    f"rows through all {cfg.n_layers} layers at full width over the {ctx}-position "
-                   f"KV, each layer with layer 0's weights ({t_layers:.1f} s); the tied LM head on "
-                   f"{slice_rows} of {cfg.vocab} vocabulary rows ({t_head_slice:.1f} s, scaled to "
-                   f"{t_head:.1f} s); {K} drafter sub-steps ({t_draft:.1f} s).  {timed:.1f} s timed, "
-                   f"one step = {step_s:.1f} s at {tokens_per_step:.2f} tokens/step; input "
-                   f"generation {gen_s:.1f} s not timed"),
+                   f"KV, each layer with layer 0's weights ({t_layers:.3g} s); the tied LM head on "
+                   f"{slice_rows} of {cfg.vocab} vocabulary rows ({t_head_slice:.3g} s, scaled to "
+                   f"{t_head:.3g} s); {K} drafter sub-steps ({t_draft:.3g} s).  {timed:.3g} s timed, "
+                   f"one step = {step_s:.3g} s at {tokens_per_step:.2f} tokens/step; input "
+                   f"generation {gen_s:.3g} s not timed"),
     }
 
 
@@ -777,6 +778,16 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores, bounded sample)")
         res["cpu_baseline"] = cpu_baseline(cfg, emitted / (N * B), K, B)
+        # the tiny configuration's shapes on one BLAS thread, same step structure (64 committed
+        # positions; counter-hash weights, which the sample generators need)
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                tiny = cpu_baseline(preset("tiny", ctx=64, init="hash"), emitted / (N * B), K, 1)
+            res["cpu_baseline"]["tiny_one_thread"] = {k: tiny[k] for k in ("value", "unit", "cores",
+                                                                             "sample")}
+        except ImportError:
+            pass
     eng.close()
     del eng, model
     torch.cuda.empty_cache()

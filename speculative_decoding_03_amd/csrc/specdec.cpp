@@ -33,6 +33,10 @@ constexpr int MIN_KB_PER_WAVE = 8;   // k-blocks each wave streams at least
 // q/k/v 7.8 -> 6.6 us, o + down 14.1 -> 13.3 us, verify 1.164 -> 1.137 ms, draft 0.438 -> 0.425 ms)
 constexpr int MIN_KB_PER_WAVE_SMALL = 4;
 constexpr int SMALL_UNITS = 256;
+// ... and in the argmax projections (the LM head: measured on MI355X, E2B 146.7 -> 131.7 us with
+// one wave over all 48 k-blocks instead of four, E4B 235.3 -> 224.9 us with two instead of eight,
+// 31B 412.9 -> 407.5 us with four instead of eight)
+constexpr int MIN_KB_PER_WAVE_ARGMAX = 40;
 constexpr int WIDE_NU = 8;            // tiles per gated unit in calls of 17..32 rows
 constexpr int MM_SPLIT_WGS = 240;     // workgroups of a prompt GEMM whose reduction is split
 // prompt attention: workgroups the key ranges aim at, and the most ranges (measured on MI355X,
@@ -78,9 +82,12 @@ struct Gemm {
 // Split-K factor of a projection with `units` work units of NU tiles over nkb k-blocks.  Measured
 // on MI355X at the 31B shapes (M = 4): about TARGET_WAVES waves per launch, each streaming at
 // least MIN_KB_PER_WAVE k-blocks (MIN_KB_PER_WAVE_SMALL in small projections), is best for
-// one-tile units; the 4-tile argmax units (LM head, drafter table) stream best split 8 ways.
+// one-tile units; the 4-tile argmax units (LM head, drafter table) of bf16 weights stream best
+// with at least MIN_KB_PER_WAVE_ARGMAX k-blocks per wave, split at most 8 ways.
 int split_for(int units, int nkb, int NU, bool q4) {
-  const int mkb = q4 ? MIN_KB_PER_WAVE_Q4 : (units < SMALL_UNITS ? MIN_KB_PER_WAVE_SMALL : MIN_KB_PER_WAVE);
+  const int mkb = q4 ? MIN_KB_PER_WAVE_Q4
+                     : (NU >= 4 ? MIN_KB_PER_WAVE_ARGMAX
+                                : (units < SMALL_UNITS ? MIN_KB_PER_WAVE_SMALL : MIN_KB_PER_WAVE));
   int KW = NU >= 4 ? 8 : cdiv(TARGET_WAVES, units);
   KW = std::min({KW, 16, std::max(1, nkb / mkb)});
   return pow2_floor(std::max(1, KW));

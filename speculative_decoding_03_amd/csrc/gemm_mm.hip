@@ -23,6 +23,35 @@ namespace gemm_detail {
 
 template <int EPI>
 __device__ void mm_finish(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int tile0, int lane);
+__device__ void mm_rope_store(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int tile0, int lane,
+                              bool act, uint16_t* lds);
+
+// The RMSNorm scale 1/sqrt(sum_t yssq[t][m] / yscale_n + eps) of row m = m0 + lane: the row's
+// per-tile partials (contiguous across the lanes for each t) are added into RS running sums, sum
+// j taking tiles j, j + RS, ..., with RS loads in flight at a time, and the sums added in j order.
+__device__ __forceinline__ float prompt_row_scale(const GemmArgs& a, int m0, int lane) {
+  constexpr int RS = 16;
+  const int m = min(m0 + lane, a.M - 1);
+  const float* y = a.yssq + m;
+  float s[RS];
+#pragma unroll
+  for (int j = 0; j < RS; ++j) s[j] = 0.f;
+  int t = 0;
+  for (; t + RS <= a.n_yssq; t += RS) {
+    float v[RS];
+#pragma unroll
+    for (int j = 0; j < RS; ++j) v[j] = y[(size_t)(t + j) * a.M];
+#pragma unroll
+    for (int j = 0; j < RS; ++j) s[j] += v[j];
+  }
+#pragma unroll
+  for (int j = 0; j < RS; ++j)
+    if (t + j < a.n_yssq) s[j] += y[(size_t)(t + j) * a.M];
+  float ss = s[0];
+#pragma unroll
+  for (int j = 1; j < RS; ++j) ss += s[j];
+  return 1.0f / sqrtf(ss / (float)a.yscale_n + a.eps);
+}
 
 // The partial block of split z (k-range z of kpart_n) in MFMA accumulator order: wave w of block
 // (bx, by) holds 16 fragments (tile, M-tile) of 64 lanes x 4 floats, each a contiguous 1 KB.
@@ -190,6 +219,16 @@ __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_
         *reinterpret_cast<f32x4*>(dst + ((t * 4 + mt) * 64 + lane) * 4) = acc[t][mt];
     return;
   }
+  if constexpr (EPI == EPI_ROPE && WM * WN <= 4) {
+    // every wave is done with the stage buffers; each takes 8 KB of the weight buffers for its
+    // sub-block's outputs (two more barriers inside, reached by every wave)
+    static_assert(sizeof(sb) >= (size_t)WM * WN * 64 * 64 * 2, "LDS for the rotary outputs");
+    __syncthreads();
+    const int m0 = m_blk + wm * 64, tile0 = t_blk + wn * 4;
+    mm_rope_store(a, acc, m0, tile0, lane, m0 < a.M && tile0 < a.n_tiles,
+                  reinterpret_cast<uint16_t*>(&sb[0][0]) + w * 64 * 64);
+    return;
+  }
   mm_finish<EPI>(a, acc, m_blk + wm * 64, t_blk + wn * 4, lane);
 }
 
@@ -213,7 +252,13 @@ __global__ void __launch_bounds__(256) mm_reduce_kernel(GemmArgs a) {
         acc[t][mt] = z == 0 ? v : acc[t][mt] + v;
       }
   }
-  mm_finish<EPI>(a, acc, blockIdx.y * 64 * WM + wm * 64, blockIdx.x * 4 * WN + wn * 4, lane);
+  const int m0 = blockIdx.y * 64 * WM + wm * 64, tile0 = blockIdx.x * 4 * WN + wn * 4;
+  if constexpr (EPI == EPI_ROPE) {
+    __shared__ __align__(16) uint16_t rl[4][64 * 64];  // each wave's rotary outputs
+    mm_rope_store(a, acc, m0, tile0, lane, m0 < a.M && tile0 < a.n_tiles, rl[threadIdx.x >> 6]);
+    return;
+  }
+  mm_finish<EPI>(a, acc, m0, tile0, lane);
 }
 
 // ---- the skinny kernel's epilogue on one wave's 64 x 64 sub-block (rows m0.., tiles tile0..) ----
@@ -224,12 +269,8 @@ __device__ void mm_finish(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int til
   e.M = min(64, a.M - m0);
   e.x_qx = e.out_qx = 0;
   if (a.yssq) {
-    // RMSNorm row scales of the 64 rows, one row per lane: the partials [t][M] of a row are
-    // summed in t order with loads that are contiguous across the lanes
-    const int m = min(m0 + lane, a.M - 1);
-    float ss = 0.f;
-    for (int t = 0; t < a.n_yssq; ++t) ss += a.yssq[(size_t)t * a.M + m];
-    const float mine = 1.0f / sqrtf(ss / (float)a.yscale_n + a.eps);
+    // RMSNorm row scales of the 64 rows, one row per lane (prompt_row_scale)
+    const float mine = prompt_row_scale(a, m0, lane);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -279,6 +320,103 @@ __device__ void mm_finish(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int til
       epi_prefetch<4, 2, EPI>(e, t0, lane, pre);
       epilogue<bf16_t, 4, 2, EPI, false>(e, part, t0 >> 1, t0, 0, xr, 1.f, pre, lane);
       __builtin_amdgcn_sched_barrier(0);  // the halves' registers do not overlap
+    }
+  }
+}
+
+// ---- q/k/v + RoPE + K/V append of one wave's 64 x 64 sub-block of a prompt chunk (rows m0.., tiles
+// tile0 .. tile0 + 3: 64 columns of one head, as heads are multiples of 64 columns; one sequence,
+// positions len[0] + pos_off + row).  The rotated values go to the wave's 8 KB of LDS in output
+// order, then out as contiguous runs: q and K rows ([row][hd], [pos][hd]) 16 bytes per lane, each
+// V^T row ([hd][pos]) 64 consecutive positions per instruction (the chunk's first position has any
+// alignment).  The rotary pairs are adjacent columns (2i, 2i + 1) and land at dims i and
+// i + hd / 2, as in the skinny kernel's epilogue.  Every wave of the workgroup calls this (one
+// barrier inside); `act`: the sub-block holds rows and columns.  A row whose position falls
+// outside the cache raises the capacity bit and its K and V are not written.  LDS element (r, j) of a 64 x 64
+// array sits at r * 64 + ((j / 8) ^ (r % 8)) * 8 + j % 8, so that neither the column writes nor
+// the row reads meet in a bank. ----
+__device__ __forceinline__ int rope_lds(int r, int j) { return r * 64 + ((((j >> 3) ^ r) & 7) << 3) + (j & 7); }
+
+__device__ void mm_rope_store(const GemmArgs& a, f32x4 (&acc)[4][4], int m0, int tile0, int lane,
+                              bool act, uint16_t* lds) {
+  const int c16 = lane & 15, grp = lane >> 4;
+  const int hd = a.hd, half = hd >> 1;
+  const int col0 = tile0 * TILE_N;
+  const int hh = col0 / hd, p0 = col0 - hh * hd;  // head, and its first column here (even)
+  const bool isq = hh < a.hq, isk = !isq && hh < a.hq + a.hkv;
+  const int rows = min(64, a.M - m0);
+  const int pos0 = act ? a.len[0] + a.pos_off + m0 : 0;  // position of row m0
+  const bool in_cache = pos0 >= 0 && pos0 + rows <= a.max_ctx;
+  if (act) {
+    if (a.yssq) {
+      // RMSNorm row scales of the 64 rows, one row per lane
+      const float mine = prompt_row_scale(a, m0, lane);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float sc = __shfl(mine, mt * 16 + (grp << 2) + v, WAVE);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[t][mt][v] *= sc;
+        }
+    }
+    // a position outside the cache takes a clamped rotary angle: flagged, and its row's K and V are
+    // not written
+    if (!in_cache && lane == 0) raise_error(a.err, ERRBIT_CAPACITY);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = t * 16 + c16;                     // column within the sub-block
+      const int j = (c & 1) * 32 + (c >> 1);          // its dim among the sub-block's 64
+      const int ip = (p0 + c) >> 1;                   // rotary pair index
+      float2 cs[4][4];
+      if (isq || isk) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int pc = min(max(pos0 + mt * 16 + (grp << 2) + v, 0), a.max_ctx - 1);
+            cs[mt][v] = a.rope_cs[(size_t)pc * half + ip];
+          }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = mt * 16 + (grp << 2) + v;
+          const float val = acc[t][mt][v];
+          const float partner = dpp_f32<DPP_XOR1>(val);
+          float y = val;
+          if (isq || isk) {
+            const bool second = c & 1;
+            const float x1 = second ? partner : val, x2 = second ? val : partner;
+            y = second ? (x2 * cs[mt][v].x + x1 * cs[mt][v].y) : (x1 * cs[mt][v].x - x2 * cs[mt][v].y);
+          }
+          lds[isq || isk ? rope_lds(r, j) : rope_lds(j, r)] = f32_to_bf16(y);
+        }
+    }
+  }
+  __syncthreads();
+  if (!act) return;
+  auto slot_ok = [&](int r) { return isq || (pos0 + r >= 0 && pos0 + r < a.max_ctx); };
+  if (isq || isk) {
+    // 64 rows x 8 runs of 8 dims, one 16-byte run per lane at a time
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int sidx = jj * 64 + lane, r = sidx >> 3, q = sidx & 7;
+      if (r >= rows || !slot_ok(r)) continue;
+      const int d0 = (q >> 2) * half + (p0 >> 1) + (q & 3) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + rope_lds(r, q * 8));
+      bf16_t* dst = isq ? reinterpret_cast<bf16_t*>(a.qout) + ((size_t)(m0 + r) * a.hq + hh) * hd + d0
+                        : reinterpret_cast<bf16_t*>(a.kcache) +
+                              ((size_t)(hh - a.hq) * a.max_ctx + pos0 + r) * hd + d0;
+      *reinterpret_cast<u32x4*>(dst) = v;
+    }
+  } else {
+    const int g = hh - a.hq - a.hkv;
+    uint16_t* vt = reinterpret_cast<uint16_t*>(a.vcache);
+    for (int j = 0; j < 64; ++j) {
+      const int dim = (j >> 5) * half + (p0 >> 1) + (j & 31);
+      if (lane < rows && slot_ok(lane)) vt[((size_t)g * hd + dim) * a.max_ctx + pos0 + lane] = lds[rope_lds(j, lane)];
     }
   }
 }

@@ -819,12 +819,11 @@ int verify_impl(specdec_ctx* x, int B, int R, const int32_t* tokens, float* logi
 // Ways the reduction of a prompt GEMM is split.  A projection whose 256 x 256 blocks leave most
 // CUs idle takes up to MM_SPLIT_WGS workgroups, each at least 8 k-blocks of the reduction, with
 // the fp32 partials (4 bytes per split and output) at most the weight bytes.  Measured on MI355X
-// at the 31B shapes, 512 rows: o + down 500 -> 231 us per layer including the summing launches.
-// The q/k/v projection is not split: the summing launch's rotary + K/V append epilogue, on few
-// waves, took as long as the split saved.
+// at the 31B shapes, 512 rows: o + down 500 -> 231 us per layer including the summing launches;
+// q/k/v 158 -> 82 us (its summing launch stores the rotary outputs through LDS).
 int mm_split(const Gemm& g, int M, int epi) {
   const int blocks = cdiv(g.n_tiles, 16) * cdiv(M, 256);
-  if (epi == EPI_ROPE || blocks >= MM_SPLIT_WGS / 4) return 1;
+  if (blocks >= MM_SPLIT_WGS / 4) return 1;
   const int kn = std::min({MM_SPLIT_WGS / blocks, g.nkb / 8, 16 * g.nkb / M});
   return kn >= 2 ? kn : 1;
 }

@@ -408,7 +408,16 @@ __device__ __forceinline__ void rowpart_sum(const GemmArgs& a, int lane, const R
 #pragma unroll
     for (int i = 0; i < RSL; ++i)
       if (p.t0 + (lane >> 4) + 4 * i < p.t1) s += p.v[g][i];
-    for (int t = p.t0 + (lane >> 4) + 4 * RSL; t < p.t1; t += 4) s += a.yssq[(size_t)t * ld + row];
+    // the slice's tiles past the prefetched ones, requested eight at a time and added in order
+    int t = p.t0 + (lane >> 4) + 4 * RSL;
+    for (; t + 28 < p.t1; t += 32) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = a.yssq[(size_t)(t + 4 * j) * ld + row];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; t < p.t1; t += 4) s += a.yssq[(size_t)t * ld + row];
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
     s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);

@@ -722,6 +722,65 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
 // query tiles per wave (measured on MI355X, 31B and E2B prompts of 512 rows: two tiles, which
 // share each LDS fragment read but need 223 registers, are 4-6% slower than one)
 constexpr int PROMPT_QT = 1;
+// Combines the key-range partials of a prompt's query vectors (at most PROMPT_COMBINE_RANGES
+// ranges, B = 1): HD / 8 lanes per vector, each a 16-byte run of the head dimension, read the
+// vector's ranges that hold a key its row sees (later ranges may hold no partial) and form
+// o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c, M = max_c m_c, with no exchange between lanes.
+constexpr int PROMPT_COMBINE_RANGES = 4;
+template <int HD>
+__global__ void __launch_bounds__(256) attn_combine_few_kernel(AttnArgs a) {
+  constexpr int SUB = HD / 8;     // lanes per query vector
+  constexpr int VPB = 256 / SUB;  // query vectors per workgroup
+  constexpr int NR = PROMPT_COMBINE_RANGES;
+  const int G = a.hq / a.hkv, Rall = a.R * G;
+  const int qv = blockIdx.x * VPB + (int)threadIdx.x / SUB, r = threadIdx.x % SUB, g = blockIdx.y;
+  if (qv >= Rall) return;
+  const int len = a.len[0];
+  const int row = qv / G, h = g * G + (qv - row * G);
+  const int row_end = len + row + a.key_off;  // the row sees keys [0, row_end)
+  if (len < 0 || row_end > a.max_ctx) return;  // flagged by the attention launch
+  const int n_act = min(a.n_chunks, (row_end + a.chunk - 1) / a.chunk);
+  const size_t pst = HD + 4, cstride = (size_t)Rall * pst;
+  const float* pbase = a.part + (size_t)g * a.n_chunks * cstride + (size_t)qv * pst;
+  u32x4 ov[NR];
+  float m[NR], l[NR];
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    if (c < n_act) {
+      const float* rowp = pbase + (size_t)c * cstride;
+      ov[c] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(rowp) + r * 16);
+      const float2 ml = *reinterpret_cast<const float2*>(rowp + HD);
+      m[c] = ml.x;
+      l[c] = ml.y;
+    } else {
+      ov[c] = u32x4{0, 0, 0, 0};
+      m[c] = -INFINITY;
+      l[c] = 0.f;
+    }
+  }
+  float M = m[0];
+#pragma unroll
+  for (int c = 1; c < NR; ++c) M = fmaxf(M, m[c]);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, L = 0.f;
+#pragma unroll
+  for (int c = 0; c < NR; ++c) {
+    const float w = exp2_hw(m[c] - Ms);  // a range the row does not see: 2^-inf = 0
+    L += w * l[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += w * __uint_as_float(ov[c][i] << 16);
+      acc[2 * i + 1] += w * __uint_as_float(ov[c][i] & 0xffff0000u);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;  // no visible key: a zero output
+  u32x4 pk;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk[i] = f32x2_to_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
+  *reinterpret_cast<u32x4*>(out + x_offset(a.out_qx, row, h * HD + r * 8, a.hq * HD)) = pk;
+}
+
 template <int HD>
 hipError_t launch_prompt_hd(const AttnArgs& a, int nwq, hipStream_t st) {
   constexpr int QT = PROMPT_QT;
@@ -730,7 +789,11 @@ hipError_t launch_prompt_hd(const AttnArgs& a, int nwq, hipStream_t st) {
   if (nwq == 4) hipLaunchKernelGGL((attn_prompt_kernel<HD, 4, QT>), grid, dim3(256), 0, st, a);
   else if (nwq == 2) hipLaunchKernelGGL((attn_prompt_kernel<HD, 2, QT>), grid, dim3(128), 0, st, a);
   else return hipErrorInvalidValue;
-  if (a.n_chunks > 1) {
+  if (a.n_chunks > 1 && a.n_chunks <= PROMPT_COMBINE_RANGES && !a.out_qx) {
+    constexpr int VPB = 256 / (HD / 8);
+    hipLaunchKernelGGL((attn_combine_few_kernel<HD>), dim3((Rall + VPB - 1) / VPB, a.hkv), dim3(256), 0,
+                       st, a);
+  } else if (a.n_chunks > 1) {
     dim3 cgrid(Rall, a.hkv, 1);
     hipLaunchKernelGGL((attn_combine_kernel<bf16_t, HD>), cgrid, dim3(WAVE), 0, st, a);
   }

@@ -550,6 +550,11 @@ __global__ void __launch_bounds__(NWQ * 64) attn_prompt_kernel(AttnArgs a) {
     }
   };
 
+  // the fewest keys any query vector of the wave sees: a step below it needs no causal mask
+  int kend_min = kend[0];
+#pragma unroll
+  for (int t = 1; t < QT; ++t) kend_min = min(kend_min, kend[t]);
+  kend_min = (int)-wave_max(-(float)kend_min);  // key counts are exact in fp32
   float m_run[QT], l_lane[QT];
   f32x4 o[QT][DT];
 #pragma unroll
@@ -560,6 +565,7 @@ __global__ void __launch_bounds__(NWQ * 64) attn_prompt_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   auto compute = [&](int buf, int k0) {
+    const bool full = k0 + KS <= kend_min;  // every key of the step is visible (wave-uniform)
     float sc[QT][NB][8];
     float mb[QT];
 #pragma unroll
@@ -583,7 +589,7 @@ __global__ void __launch_bounds__(NWQ * 64) attn_prompt_kernel(AttnArgs a) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int key = k0 + nb * 32 + 8 * grp + 4 * h + v;
-            const float val = key < kend[t] ? acc[t][v] * scale2 : -INFINITY;
+            const float val = (full || key < kend[t]) ? acc[t][v] * scale2 : -INFINITY;
             sc[t][nb][4 * h + v] = val;
             mb[t] = fmaxf(mb[t], val);
           }
@@ -594,9 +600,12 @@ __global__ void __launch_bounds__(NWQ * 64) attn_prompt_kernel(AttnArgs a) {
       const float mn = fmaxf(m_run[t], rows_max(mb[t]));
       ms[t] = mn == -INFINITY ? 0.f : mn;
       const float alpha = exp2_hw(m_run[t] - ms[t]);  // m_run = -inf: 0 (nothing summed yet)
-      l_lane[t] *= alpha;
+      // a factor of exactly 1 (no column's maximum grew) leaves the sums as they are
+      if (__ballot(alpha != 1.0f) != 0ull) {
+        l_lane[t] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
+      }
       m_run[t] = mn;
     }
 #pragma unroll

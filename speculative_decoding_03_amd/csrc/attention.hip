@@ -3,13 +3,12 @@
 // target's cache (keys [0, len), no cache of its own).
 //
 // Split over keys (flash-decoding): grid (chunk, kv head, sequence x query tiles); a workgroup of
-// NW waves (four, or two for models with few KV heads) takes one chunk of CH = 32 NW keys, each wave
-// a contiguous 32-key block, and serves every query vector that reads that KV head (all rows x the
-// group's query heads), or one 16-vector tile of them when the call splits its tiles over
-// workgroups.  K is stored [pos][hd] and V
-// transposed [hd][pos], so both MFMA operands stream as 16-byte loads.  Per chunk the kernel
-// leaves (row max in base-2 units, sum of exponentials, unnormalised value sum); attn_combine
-// merges the chunks in chunk order.  The value sums are kept in the storage type (bf16 rounds
+// NW waves (four, or two for models with few KV heads) takes one chunk of CH = 32 NW keys, each
+// wave a contiguous 32-key block, and serves every query vector that reads that KV head (all rows
+// x the group's query heads), or one 16-vector tile of them when the call splits its tiles over
+// workgroups.  K is stored [pos][hd] and V transposed [hd][pos], so both MFMA operands stream as
+// 16-byte loads.  Per chunk the kernel leaves (row max in base-2 units, sum of exponentials,
+// unnormalised value sum); attn_combine merges the chunks in chunk order.  The value sums are kept in the storage type (bf16 rounds
 // each chunk's sum once, well inside the bf16 path's error budget, and halves the partial
 // traffic); the maxima and sums of exponentials stay fp32.  Chunk boundaries sit at fixed
 // absolute positions and every reduction has a fixed order, so a row's output does not depend
@@ -331,7 +330,7 @@ __global__ void __launch_bounds__(WAVE) attn_combine_kernel(AttnArgs a) {
   constexpr int EPR = 16 / (int)sizeof(T);  // elements per 16-byte run
   constexpr int RN = HD / EPR;              // runs per partial row
   constexpr int QN = WAVE / RN;             // chunk groups
-  // chunks per lane per batch: 96 chunks of 128 keys (12K context at head size 128) in one batch
+  // chunks per lane per batch: at head size 128, 96 chunks (12K keys in 128-key chunks) in one batch
   constexpr int CB = 24;
   static_assert(HD % EPR == 0 && RN <= WAVE && QN >= 1, "partial row does not fit a wave");
   __shared__ __align__(16) float red[QN][HD];
